@@ -1,0 +1,108 @@
+"""Pins for oracle/gemm.py: brute force with exact rational arithmetic.
+
+Every dequantized element e2m1 * scale is a dyadic rational, so the exact
+GEMM is computable with fractions.Fraction.  The oracle's fp64 result must
+equal it rounded to fp32 whenever no fp64 rounding happens, and be within
+2^-52 * sum|a b| otherwise.  The per-block form of App. B.3 (partial dot
+products times the two local decode scales, then the two global decode
+scales) is checked to be the same number.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import formats as F
+from oracle import gemm as G
+from oracle import quantize as Q
+from fp4_block_scaled_x16_amd import inputs
+
+
+def _operand(bits_, fmt, block="1d"):
+    R, K = bits_.shape
+    q = Q.quantize(bits_, fmt, block=block)
+    vals = Q.operand_values(q["codes"], q["scales"], fmt, block, R, K)
+    return q, vals
+
+
+def _exact_gemm(a_codes, a_sc, b_codes, b_sc, sA, sB, bs):
+    """Per-block exact form: sum_blk sA_blk * sB_blk * sum_k e2m1 * e2m1."""
+    M, K = a_codes.shape
+    N = b_codes.shape[0]
+    out = [[Fraction(0)] * N for _ in range(M)]
+    ea = [[Fraction(float(v)) for v in row] for row in F.e2m1_value(a_codes)]
+    eb = [[Fraction(float(v)) for v in row] for row in F.e2m1_value(b_codes)]
+    for m in range(M):
+        for n in range(N):
+            acc = Fraction(0)
+            for blk in range(K // bs):
+                part = sum(ea[m][k] * eb[n][k] for k in range(blk * bs, (blk + 1) * bs))
+                acc += part * Fraction(float(a_sc[m, blk])) * Fraction(float(b_sc[n, blk]))
+            out[m][n] = acc * Fraction(float(sA)) * Fraction(float(sB))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K,fmt", [(16, 16, 16, "nvfp4"), (16, 24, 48, "nvfp4"),
+                                       (8, 12, 32, "ue5m3"), (12, 8, 64, "mxfp4")])
+def test_gemm_matches_exact_rational(M, N, K, fmt):
+    a_bits = inputs.activations((M, K), cfg_seed=21, outliers=False)
+    b_bits = inputs.weights((N, K), cfg_seed=21)
+    qa, a = _operand(a_bits, fmt)
+    qb, b = _operand(b_bits, fmt)
+    bs = Q.BLOCK[fmt]
+    sA = 1.0 if fmt == "mxfp4" else qa["s_dec"]
+    sB = 1.0 if fmt == "mxfp4" else qb["s_dec"]
+    a_sc = Q.scale_values(qa["scales"], fmt).reshape(M, K // bs)
+    b_sc = Q.scale_values(qb["scales"], fmt).reshape(N, K // bs)
+    exact = _exact_gemm(qa["codes_unpacked"], a_sc, qb["codes_unpacked"], b_sc, sA, sB, bs)
+    D = G.gemm_ref(a, b, sA, sB)
+    bound = G.gemm_abs_bound(a, b, sA, sB)
+    assert D.shape == (M, N) and D.dtype == np.float32
+    acc = a @ b.T                                               # the oracle's fp64 sum
+    s = Fraction(float(sA)) * Fraction(float(sB))
+    for m in range(M):
+        for n in range(N):
+            # fp64 sum within 2^-52 * sum|ab| of the exact value
+            ex_unscaled = exact[m][n] / s
+            assert abs(Fraction(float(acc[m, n])) - ex_unscaled) <= \
+                Fraction(float(bound[m, n])) / s * Fraction(1, 2 ** 52)
+            # and the fp32 output is the exact value rounded (1 ulp slack for
+            # an fp64 error that straddles an fp32 rounding boundary)
+            want32 = np.float32(float(exact[m][n]))
+            assert abs(float(D[m, n]) - float(want32)) <= abs(float(np.spacing(want32)))
+
+
+def test_gemm_bitexact_when_products_span_few_binades():
+    # tiny config data: products of e2m1 (2 sig. bits) and E4M3 scales
+    # (4 sig. bits) per operand; fp64 sums of 16 such terms are exact
+    a_bits = inputs.normal((16, 16), 1.0, cfg_seed=0, tensor_id=0)
+    b_bits = inputs.normal((16, 16), 0.02, cfg_seed=0, tensor_id=1)
+    qa, a = _operand(a_bits, "nvfp4")
+    qb, b = _operand(b_bits, "nvfp4", block="2d")
+    exact = (np.array([[sum(Fraction(float(x)) * Fraction(float(y)) for x, y in zip(ra, rb))
+                        for rb in b] for ra in a], dtype=object))
+    acc = a @ b.T
+    assert all(Fraction(float(acc[i, j])) == exact[i, j] for i in range(16) for j in range(16))
+    D = G.gemm_ref(a, b, qa["s_dec"], qb["s_dec"])
+    s = Fraction(float(qa["s_dec"])) * Fraction(float(qb["s_dec"]))
+    want = np.array([[np.float32(float(exact[i, j] * s)) for j in range(16)] for i in range(16)])
+    assert np.array_equal(D, want)
+
+
+def test_gemm_layout_is_tn():
+    # D[m, n] = sum_k A[m, k] B[n, k]: a rank-one check catches transposes
+    a = np.zeros((3, 32)); a[1, 5] = 2.0
+    b = np.zeros((4, 32)); b[2, 5] = 3.0
+    D = G.gemm_ref(a, b, 0.5, 4.0)
+    want = np.zeros((3, 4), np.float32); want[1, 2] = 12.0
+    assert np.array_equal(D, want)
+    rows, cols = np.array([1, 0]), np.array([2, 2])
+    d, bound = G.gemm_ref_entries(a, b, rows, cols, 0.5, 4.0)
+    assert d.tolist() == [12.0, 0.0] and bound.tolist() == [12.0, 0.0]
+
+
+def test_abs_bound_dominates():
+    rng = np.random.default_rng(3)
+    a = rng.standard_normal((20, 64)); b = rng.standard_normal((30, 64))
+    D = G.gemm_ref(a, b, 1.0, 1.0).astype(np.float64)
+    assert np.all(np.abs(D) <= G.gemm_abs_bound(a, b) * (1 + 1e-7))

@@ -1,0 +1,350 @@
+"""Pins for oracle/quantize.py against what the pages fix.
+
+  * a hand-derived NVFP4 example (App. B.1-B.3 with exact powers of two)
+  * the MXFP4 worked example of App. B.4 (amax = 3 + eps)
+  * block amax maps to the FP4 maximum 6 (§3, App. B.2) for RNE blocks with
+    a normal scale, and is recovered to within E4M3 precision (§3: the block
+    amax is kept at near-FP8 precision)
+  * idempotence: quantize(dequantize(q)) == q
+  * 2D scaling is transposition invariant (§4.3; 2D-block FP4 abstract)
+  * stochastic rounding is unbiased (§4.4) and never moves on-grid values
+  * event counters on crafted blocks whose counts follow from the rules
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import formats as F
+from oracle import quantize as Q
+from oracle.rht import rht16_cols
+from oracle.philox import rht_signs
+from fp4_block_scaled_x16_amd import inputs
+from conftest import GOLDEN
+
+
+def bits(a):
+    return inputs.to_bf16_bits(np.asarray(a, np.float32))
+
+
+def test_hand_example_nvfp4():
+    # Block 0 has amax 6, block 1 has amax 10.5 = the tensor amax.
+    # Eq. 1: s_enc = 2688 / 10.5 = 256 exactly, s_dec = 2^-8.
+    # Block 0: Eq. 2 s_dec_L = 1, Eq. 3 t = 256 -> E4M3 256 (code 0x78),
+    # s_enc_L = 1 / (256 * 2^-8) = 1, so y = x and codes are plain RNE of x.
+    b0 = [6, -0.5, 1, 1.5, 2, 3, 4, -6, 0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5]
+    want0 = [7, 9, 2, 3, 4, 5, 6, 15, 0, 0, 2, 2, 4, 4, 6, 6]
+    # Block 1: t = 10.5 / 6 * 256 = 448 -> code 0x7E; s_enc_L = fp32(1 / 1.75)
+    # which rounds up (4/7 = 0.100100...b), so y(10.5) = 6 + tiny > 6:
+    # saturated, code 7.  Other entries: 1.75 * 4/7 = 1 -> code 2.
+    b1 = [10.5] + [1.75] * 15
+    q = Q.quantize(bits([b0 + b1]), "nvfp4")
+    assert q["amax"] == np.float32(10.5)
+    assert q["s_dec"] == np.float32(2.0 ** -8)
+    assert q["scales"].tolist() == [[0x78, 0x7E]]
+    assert q["codes_unpacked"][0, :16].tolist() == want0
+    assert q["codes_unpacked"][0, 16:].tolist() == [7] + [2] * 15
+    # packing: even element in the low nibble
+    assert q["codes"][0, 0] == (want0[0] | want0[1] << 4)
+    c = q["counters"]
+    assert c["elem_saturated"] == 1
+    assert c["elem_underflow"] == 1          # 0.25 -> 0; the exact 0 is not an event
+    assert c["scale_saturated"] == c["scale_underflow"] == c["scale_subnormal"] == 0
+
+
+def test_mxfp4_worked_example():
+    with open(os.path.join(GOLDEN, "mxfp4_amax_3_plus_eps.json")) as f:
+        g = json.load(f)
+    rng = np.random.default_rng(1)
+    eps = np.float32(2.0 ** -6)
+    blk = rng.uniform(-3, 3, 32).astype(np.float32)
+    blk[5] = 3 + eps
+    q = Q.quantize(bits([blk]), "mxfp4")
+    assert q["scales"].tolist() == [[g["ue8m0_code"]]]
+    assert F.ue8m0_value(q["scales"][0, 0]) == g["decode_scale"]
+    mags = q["codes_unpacked"][0] & 7
+    assert mags[5] == g["amax_element_code_magnitude"]
+    assert F.E2M1_MAG[mags[5]] == g["amax_element_value"]
+    used = set(F.E2M1_MAG[mags].tolist())
+    assert not used & set(g["unused_magnitudes"])
+    assert np.isclose(np.log2(3 / 0.5), g["binades_used"])
+    assert np.isclose(np.log2(6 / 0.5), g["binades_full"])
+
+
+def test_mx_scale_is_smallest_nonsaturating_power_of_two():
+    rng = np.random.default_rng(2)
+    a = (rng.uniform(0.5, 1, 5000) * 2.0 ** rng.integers(-120, 120, 5000)).astype(np.float32)
+    a = np.concatenate([a, np.float32(6.0) * np.float32(2.0) ** np.arange(-20, 20, dtype=np.float32)])
+    code, s_enc, _ = Q.block_scales_mx(a)
+    e = code.astype(np.int64) - 127
+    for ai, ei in zip(a.tolist(), e.tolist()):
+        from fractions import Fraction
+        A = Fraction(ai)
+        assert 6 * Fraction(2) ** ei >= A > 6 * Fraction(2) ** (ei - 1)
+    assert np.array_equal(s_enc, np.ldexp(1.0, -e).astype(np.float32))
+
+
+def _blocks_with_normal_scale(q, fmt, bs):
+    codes = q["codes_unpacked"]
+    R, C = codes.shape
+    sc = q["scales"].reshape(R, C // bs)
+    return codes.reshape(R, C // bs, bs), sc, sc >= 8
+
+
+@pytest.mark.parametrize("fmt,target", [("nvfp4", 448.0), ("ue5m3", 448.0), ("ue5m3", 2048.0)])
+def test_block_amax_maps_to_six(fmt, target):
+    x = inputs.activations((64, 1024), cfg_seed=3)
+    dy = inputs.gradients((64, 1024), cfg_seed=3)
+    for t in (x, dy):
+        q = Q.quantize(t, fmt, target=target)
+        cb, sc, normal = _blocks_with_normal_scale(q, fmt, 16)
+        xf = F.bf16_bits_to_f32(t).reshape(cb.shape)
+        arg = np.abs(xf).argmax(axis=2)
+        amax_code = np.take_along_axis(cb, arg[..., None], axis=2)[..., 0] & 7
+        assert normal.sum() > 0.9 * normal.size
+        assert np.all(amax_code[normal] == 7)
+
+
+def test_block_amax_near_fp8_precision():
+    x = inputs.activations((64, 2048), cfg_seed=4)
+    q = Q.quantize(x, "nvfp4")
+    cb, sc, normal = _blocks_with_normal_scale(q, "nvfp4", 16)
+    xf = F.bf16_bits_to_f32(x).reshape(cb.shape).astype(np.float64)
+    amax_b = np.abs(xf).max(axis=2)
+    dq_amax = 6.0 * F.e4m3_value(sc) * np.float64(q["s_dec"])
+    ok = normal & (sc < 0x7E)
+    rel = np.abs(dq_amax - amax_b) / amax_b
+    assert np.all(rel[ok] <= 2.0 ** -4 * (1 + 1e-6))
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "ue5m3", "mxfp4"])
+def test_idempotent(fmt):
+    # q(dq(q(x))) == q(x) on every block whose largest code is the format
+    # maximum; dequantized values are rounded to bf16 (the quantizer input)
+    x = inputs.activations((32, 1024), cfg_seed=5)
+    R, C = x.shape
+    bs = Q.BLOCK[fmt]
+    q1 = Q.quantize(x, fmt)
+    dq = Q.dequantize(q1["codes"], q1["scales"], fmt, "1d", q1["s_dec"], R, C, out="bf16")
+    q2 = Q.quantize(dq, fmt)
+    c1 = q1["codes_unpacked"].reshape(R, C // bs, bs)
+    c2 = q2["codes_unpacked"].reshape(R, C // bs, bs)
+    maxmag = (c1 & 7).max(axis=2)
+    full = maxmag >= (6 if fmt == "mxfp4" else 7)
+    if fmt != "mxfp4":
+        full &= q1["scales"] >= 8
+    assert full.mean() > (0.75 if fmt == "mxfp4" else 0.9)
+    assert np.array_equal(c1[full], c2[full])
+    assert np.array_equal(q1["scales"][full], q2["scales"][full])
+    if fmt != "mxfp4":
+        # s_dec passed through (the amax given) also reproduces the codes
+        q3 = Q.quantize(dq, fmt, amax=q1["amax"])
+        c3 = q3["codes_unpacked"].reshape(R, C // bs, bs)
+        assert np.array_equal(c1[full], c3[full])
+
+
+def test_mx_max_code_three_is_value_preserving():
+    # App. B.4 case: requantizing halves the scale and doubles the codes
+    blk = np.zeros((1, 32), np.float32)
+    blk[0, :4] = [3.125, 1.0, -0.5, 2.0]
+    q1 = Q.quantize(bits(blk), "mxfp4")
+    dq = Q.dequantize(q1["codes"], q1["scales"], "mxfp4", "1d", 1.0, 1, 32)
+    q2 = Q.quantize(bits(dq), "mxfp4")
+    dq2 = Q.dequantize(q2["codes"], q2["scales"], "mxfp4", "1d", 1.0, 1, 32)
+    assert np.array_equal(dq, dq2)
+    assert q2["scales"][0, 0] == q1["scales"][0, 0] - 1
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "ue5m3"])
+def test_2d_transposition_invariant(fmt):
+    w = inputs.weights((96, 160), cfg_seed=6)
+    q = Q.quantize(w, fmt, block="2d", emit_transpose=True)
+    qt = Q.quantize(np.ascontiguousarray(w.T), fmt, block="2d", emit_transpose=True)
+    assert np.array_equal(q["codes_unpacked"].T, qt["codes_unpacked"])
+    assert np.array_equal(q["scales"].T, qt["scales"])
+    assert np.array_equal(q["codes_t"], qt["codes"])
+    assert np.array_equal(qt["codes_t"], q["codes"])
+    assert q["scales"].shape == (6, 10)
+
+
+def test_colwise_is_rowwise_of_transpose():
+    x = inputs.gradients((64, 96), cfg_seed=7)
+    for rnd in ("rne", "sr"):
+        a = Q.quantize(x, "nvfp4", orient="col", rnd=rnd, seed=1, offset=1)
+        b = Q.quantize(np.ascontiguousarray(x.T), "nvfp4", orient="row", rnd=rnd, seed=1, offset=1)
+        for k in ("codes", "scales", "amax", "s_dec"):
+            assert np.array_equal(a[k], b[k])
+        assert a["counters"] == b["counters"]
+
+
+def test_rht_amax_after_rotation():
+    x = inputs.activations((64, 48), cfg_seed=8)
+    s = rht_signs(7)
+    q = Q.quantize(x, "nvfp4", orient="col", rht=True, signs=s)
+    rot = rht16_cols(F.bf16_bits_to_f32(x), s)
+    assert q["amax"] == np.float32(np.abs(rot).max())
+    assert q["amax"] != np.float32(np.abs(F.bf16_bits_to_f32(x)).max())
+
+
+def _sr_codes_and_y(x_bits, reps, seed=1):
+    """Codes for reps SR repetitions (offset = repetition) and y = x * s_enc_L."""
+    xf = F.bf16_bits_to_f32(x_bits)
+    R, C = xf.shape
+    amax = Q.tensor_amax(xf)
+    s_enc, s_dec = Q.global_scales(amax)
+    amax_b = np.abs(xf.reshape(R, C // 16, 16)).max(axis=2)
+    _, s_enc_l, _ = Q.block_scales_two_level(amax_b, s_enc, s_dec, "nvfp4")
+    y = (xf * np.repeat(s_enc_l, 16, axis=1)).astype(np.float32).astype(np.float64)
+    codes = [Q.quantize(x_bits, "nvfp4", rnd="sr", seed=seed, offset=r)["codes_unpacked"]
+             for r in range(reps)]
+    return np.stack(codes), y
+
+
+def test_sr_unbiased_config1():
+    # Tiny workload: A = 256 x 256 ~ N(0, 1), seed 0; SR with Philox seed 1,
+    # 100 repetitions -> 6.5M draws.  Over unclipped elements the mean of
+    # (value(code) - y) must be within 3 standard errors of 0.
+    a = inputs.linear_tensors(1)["X"]
+    codes, y = _sr_codes_and_y(a, 100)
+    vals = F.e2m1_value(codes)                        # [reps, R, C]
+    keep = np.abs(y) <= 6.0
+    err = (vals - y[None])[:, keep].ravel()
+    n = err.size
+    assert n >= 10 ** 6
+    se = err.std() / np.sqrt(n)
+    assert abs(err.mean()) < 3 * se
+    # RNE on the same data is biased well beyond that (sanity of the test)
+    rne = F.e2m1_value(Q.quantize(a, "nvfp4")["codes_unpacked"])
+    assert abs((rne - y)[keep].mean()) > 3 * se
+
+
+def test_sr_matches_exact_expectation_and_keeps_grid_values():
+    a = inputs.linear_tensors(1)["X"][:64]
+    codes, y = _sr_codes_and_y(a, 40)
+    m = np.abs(y)
+    vals = np.abs(F.e2m1_value(codes))
+    keep = m <= 6
+    lo = F.E2M1_MAG[np.minimum(F.e2m1_floor_code(np.minimum(m, 6)), 6)]
+    hi = F.E2M1_MAG[np.minimum(F.e2m1_floor_code(np.minimum(m, 6)), 6) + 1]
+    # every draw lands on one of the two neighbours
+    assert np.all((vals[:, keep] == lo[keep]) | (vals[:, keep] == hi[keep]) | (m[keep] == 6))
+    # aggregate of (empirical mean - exact expectation) is ~ N(0, se)
+    frac = (m - lo) / (hi - lo)
+    p_up = np.ceil(frac * 65536) / 65536
+    expect = lo + (hi - lo) * p_up
+    var = (hi - lo) ** 2 * p_up * (1 - p_up)
+    d = (vals[:, keep].mean(axis=0) - expect[keep])
+    z = d.sum() / np.sqrt((var[keep] / codes.shape[0]).sum())
+    assert abs(z) < 4
+
+
+def test_sr_keeps_on_grid_values():
+    # s_enc = 256, s_dec = 2^-8 and block scale 256 give s_enc_L = 1, so
+    # y = x: on-grid values (including 0) must never be moved by SR
+    grid = [6, 4, 3, 2, 1.5, 1, 0.5, 0, -0.5, -1, -1.5, -2, -3, -4, -6, 0]
+    x = bits([grid + [10.5] + [0.0] * 15])
+    for r in range(200):
+        q = Q.quantize(x, "nvfp4", rnd="sr", seed=1, offset=r)
+        assert np.array_equal(F.e2m1_value(q["codes_unpacked"][0, :16]), np.array(grid, float))
+
+
+def test_sr_reproducible():
+    dy = inputs.gradients((32, 256), cfg_seed=9)
+    a = Q.quantize(dy, "nvfp4", rnd="sr", seed=1, offset=0)
+    b = Q.quantize(dy, "nvfp4", rnd="sr", seed=1, offset=0)
+    c = Q.quantize(dy, "nvfp4", rnd="sr", seed=1, offset=1)
+    assert np.array_equal(a["codes"], b["codes"])
+    assert not np.array_equal(a["codes"], c["codes"])
+
+
+def test_counters_outlier_underflow():
+    # one 1e30 element: s_enc = 2688 / 1e30, so a block with amax ~1e-10 has
+    # t ~ 4e-38 -> E4M3 code 0: every other nonzero block underflows, and all
+    # its nonzero elements become +-0.
+    x = np.full((4, 64), 1e-10, np.float32)
+    x[1, 3] = 1e30
+    x[2, 16:32] = 0.0
+    q = Q.quantize(bits(x), "nvfp4")
+    c = q["counters"]
+    nonzero_blocks = 16 - 1 - 1
+    assert c["scale_underflow"] == nonzero_blocks
+    assert c["elem_underflow"] == nonzero_blocks * 16 + 15
+    assert c["scale_saturated"] == 0
+    assert np.all(q["codes_unpacked"][0] == 0)
+
+
+def test_counters_zero_tensor_and_signed_zero():
+    x = np.zeros((2, 32), np.float32)
+    x[1, 5] = -0.0
+    q = Q.quantize(bits(x), "nvfp4")
+    assert q["amax"] == 0 and q["s_dec"] == 1.0
+    assert np.all(q["scales"] == 0)
+    assert q["codes_unpacked"][1, 5] == 8 and q["codes_unpacked"][0, 5] == 0
+    assert q["counters"] == Q.zero_counters()
+
+
+def test_counters_stale_amax_saturation():
+    # With a stale amax a_s, block scale t = amax_B / a_s * T saturates
+    # E4M3 exactly when amax_B / a_s * 448 > 448 (up to fp32 rounding).
+    x = inputs.activations((64, 512), cfg_seed=10)
+    xf = F.bf16_bits_to_f32(x)
+    amax_b = np.abs(xf.reshape(64, 32, 16)).max(axis=2).astype(np.float64)
+    a_s = np.float32(np.abs(xf).max() / 8.0)
+    q = Q.quantize(x, "nvfp4", amax=a_s)
+    ratio = amax_b / np.float64(a_s)
+    clear_sat = (ratio > 1 + 1e-6).sum()
+    clear_ok = (ratio < 1 - 1e-6).sum()
+    assert clear_sat <= q["counters"]["scale_saturated"] <= amax_b.size - clear_ok
+    # the same data under UE5M3 (max 122880) does not saturate its scales
+    q5 = Q.quantize(x, "ue5m3", amax=a_s, target=2048.0)
+    assert q5["counters"]["scale_saturated"] == 0
+    # with E4M3 saturated at 448, y = x * 6 / a_s: every |x| > a_s clips
+    n_big = int((np.abs(xf) > a_s * (1 + 1e-6)).sum())
+    assert n_big > 0 and q["counters"]["elem_saturated"] >= n_big
+
+
+def test_ue5m3_larger_target_avoids_scale_underflow():
+    # t = T * amax_B / amax.  With amax = 1 and a block of amax 2^-27:
+    # T = 448 gives t = 0.875 * 2^-18, below half the smallest UE5M3 value
+    # (2^-17), so the scale underflows to 0; T = 2048 gives t = 2^-16, a
+    # subnormal scale (code 2).  (UE5M3 abstract: larger T, fewer underflows.)
+    x = np.zeros((1, 32), np.float32)
+    x[0, 0] = 1.0
+    x[0, 16:] = 2.0 ** -27
+    a = Q.quantize(bits(x), "ue5m3", target=448.0)
+    b = Q.quantize(bits(x), "ue5m3", target=2048.0)
+    assert a["scales"][0, 1] == 0 and a["counters"]["scale_underflow"] == 1
+    assert a["counters"]["elem_underflow"] == 16
+    assert b["scales"][0, 1] == 2 and b["counters"]["scale_underflow"] == 0
+    assert b["counters"]["scale_subnormal"] == 1
+
+
+def test_format_error_ordering():
+    # §3: NVFP4 (16-blocks, E4M3 scales) is more accurate than MXFP4
+    x = inputs.activations((64, 1024), cfg_seed=12)
+    xf = F.bf16_bits_to_f32(x).astype(np.float64)
+    errs = {}
+    for fmt in ("nvfp4", "mxfp4"):
+        q = Q.quantize(x, fmt)
+        dq = Q.dequantize(q["codes"], q["scales"], fmt, "1d", q["s_dec"] if q["s_dec"] else 1.0, 64, 1024)
+        errs[fmt] = np.linalg.norm(dq - xf) / np.linalg.norm(xf)
+    assert errs["nvfp4"] < errs["mxfp4"]
+    assert 0.05 < errs["nvfp4"] < 0.2
+
+
+def test_dequantize_bf16_is_rounded_f32():
+    import torch
+    dy = inputs.gradients((16, 256), cfg_seed=13)
+    q = Q.quantize(dy, "ue5m3", rnd="sr", seed=1)
+    f = Q.dequantize(q["codes"], q["scales"], "ue5m3", "1d", q["s_dec"], 16, 256)
+    b = Q.dequantize(q["codes"], q["scales"], "ue5m3", "1d", q["s_dec"], 16, 256, out="bf16")
+    want = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(b, want)
+
+
+def test_empty_tensor():
+    x = np.zeros((0, 32), np.uint16)
+    q = Q.quantize(x, "nvfp4")
+    assert q["codes"].shape == (0, 16) and q["scales"].shape == (0, 2)
+    assert q["amax"] == 0 and q["s_dec"] == 1

@@ -1,0 +1,68 @@
+"""Pins for oracle/rht.py: the 16-point randomized Hadamard transform.
+
+Checked against scipy.linalg.hadamard (Sylvester construction, a library
+routine), the orthogonality the NVFP4 paper relies on (App. C: the rotation
+of each operand cancels in the product), closed forms, and an fp64 error
+bound for the fp32 butterflies.
+"""
+import numpy as np
+import scipy.linalg
+
+from oracle import rht as R
+from oracle.philox import rht_signs
+
+H16 = scipy.linalg.hadamard(16).astype(np.float64)
+
+
+def test_fwht_of_one_hot_is_hadamard_column():
+    eye = np.eye(16, dtype=np.float32)
+    got = R.fwht16_f32(eye)                 # row j = transform of e_j
+    assert np.array_equal(got.astype(np.float64), H16.T)
+    assert np.array_equal(H16 @ H16.T, 16 * np.eye(16))
+
+
+def test_signs_flip_output_rows():
+    # H_r = D_r H: bit i of the mask negates OUTPUT entry i (a row of H)
+    signs = 0b1010000000000101
+    d = np.array([-1.0 if (signs >> i) & 1 else 1.0 for i in range(16)])
+    got = R.rht16_vec(np.eye(16, dtype=np.float32), signs).astype(np.float64)
+    want = (0.25 * np.diag(d) @ H16).T       # row j = (1/4) D H e_j
+    assert np.array_equal(got, want)
+    # orthonormal: M M^T = I exactly
+    M = got.T
+    assert np.array_equal(M @ M.T, np.eye(16))
+
+
+def test_constant_vector_concentrates():
+    c = np.float32(3.25)
+    for signs in (0, 1, rht_signs(7)):
+        y = R.rht16_vec(np.full(16, c, np.float32), signs)
+        want = np.zeros(16, np.float32)
+        want[0] = -4 * c if signs & 1 else 4 * c
+        assert np.array_equal(y, want)
+
+
+def test_fp32_error_bound_against_fp64():
+    rng = np.random.default_rng(5)
+    v = (rng.standard_normal((20000, 16)) * 10.0 ** rng.uniform(-6, 6, (20000, 1))).astype(np.float32)
+    signs = rht_signs(7)
+    d = np.array([-1.0 if (signs >> i) & 1 else 1.0 for i in range(16)])
+    exact = (v.astype(np.float64) @ H16.T) * 0.25 * d
+    got = R.rht16_vec(v, signs).astype(np.float64)
+    bound = 4 * 2.0 ** -24 * 0.25 * np.abs(v.astype(np.float64)).sum(axis=1, keepdims=True)
+    assert np.all(np.abs(got - exact) <= bound)
+
+
+def test_cols_layout_and_cancellation():
+    rng = np.random.default_rng(9)
+    T, a, b = 64, 5, 7
+    x = rng.standard_normal((T, a)).astype(np.float32)
+    dy = rng.standard_normal((T, b)).astype(np.float32)
+    s = rht_signs(7)
+    rx, rdy = R.rht16_cols(x, s), R.rht16_cols(dy, s)
+    # each 16-row group of each column is transformed independently
+    assert np.array_equal(rx[16:32, 3], R.rht16_vec(x[16:32, 3], s))
+    # Wgrad with both operands rotated equals the unrotated product (App. C)
+    lhs = rdy.astype(np.float64).T @ rx.astype(np.float64)
+    rhs = dy.astype(np.float64).T @ x.astype(np.float64)
+    assert np.allclose(lhs, rhs, rtol=1e-5, atol=1e-5)
