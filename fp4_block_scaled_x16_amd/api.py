@@ -1,0 +1,222 @@
+"""ctypes binding of libfp4_mi355x.so (include/fp4.h).
+
+Argument marshalling only: torch tensors provide device memory, the current
+torch stream is passed as the hipStream_t, and every computation runs in the
+library's HIP kernels.  The library is loaded on first use; if it is missing
+(not built) every call raises -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfp4_mi355x.so")
+
+NVFP4, UE5M3, MXFP4 = 0, 1, 2
+FORMATS = {"nvfp4": NVFP4, "ue5m3": UE5M3, "mxfp4": MXFP4}
+BLOCK_LEN = {NVFP4: 16, UE5M3: 16, MXFP4: 32}
+RNE, SR = 0, 1
+BLOCK_1D, BLOCK_2D16 = 0, 1
+ROWWISE, COLWISE = 0, 1
+COUNTER_NAMES = ("scale_saturated", "scale_underflow", "scale_subnormal",
+                 "elem_saturated", "elem_underflow")
+
+
+class Fp4Error(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(msg)
+        self.status = status
+
+
+class QuantDesc(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int), ("block", ctypes.c_int), ("orient", ctypes.c_int),
+                ("round", ctypes.c_int), ("seed", ctypes.c_uint64), ("offset", ctypes.c_uint64),
+                ("rht", ctypes.c_int), ("rht_signs", ctypes.c_uint32), ("target", ctypes.c_float),
+                ("amax_given", ctypes.c_int), ("emit_transpose", ctypes.c_int)]
+
+
+class Operand(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int), ("codes", ctypes.c_void_p), ("ld_codes", ctypes.c_int64),
+                ("scales", ctypes.c_void_p), ("scale_stride_row", ctypes.c_int64),
+                ("scale_stride_kblk", ctypes.c_int64), ("scale_row_group", ctypes.c_int32),
+                ("s_dec", ctypes.c_void_p)]
+
+
+_lib = None
+EXPORTS = ("fp4_amax", "fp4_quantize", "fp4_dequantize", "fp4_rht16", "fp4_gemm",
+           "fp4_status_string", "fp4_last_error")
+
+
+def load_library(path=LIB_PATH):
+    """Load (once) and return the ctypes library; raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise Fp4Error(-1, "%s is missing: build it with __graft_entry__.build() "
+                           "(python fp4_block_scaled_x16_amd/build.py)" % path)
+    lib = ctypes.CDLL(path)
+    i64, vp, u32, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_int
+    lib.fp4_amax.argtypes = [vp, i64, i64, i64, i32, u32, vp, vp]
+    lib.fp4_quantize.argtypes = [ctypes.POINTER(QuantDesc), vp, i64, i64, i64, vp, vp, vp, vp,
+                                 vp, vp, vp]
+    lib.fp4_dequantize.argtypes = [i32, i32, vp, vp, vp, i64, i64, vp, i32, vp]
+    lib.fp4_rht16.argtypes = [vp, i64, i64, i64, u32, vp, vp]
+    lib.fp4_gemm.argtypes = [ctypes.POINTER(Operand), ctypes.POINTER(Operand), i64, i64, i64, vp,
+                             i64, i32, vp]
+    for f in ("fp4_amax", "fp4_quantize", "fp4_dequantize", "fp4_rht16", "fp4_gemm"):
+        getattr(lib, f).restype = ctypes.c_int
+    lib.fp4_status_string.argtypes = [ctypes.c_int]
+    lib.fp4_status_string.restype = ctypes.c_char_p
+    lib.fp4_last_error.argtypes = []
+    lib.fp4_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status, what):
+    if status != 0:
+        lib = load_library()
+        raise Fp4Error(status, "%s: %s (%s)" % (what, lib.fp4_status_string(status).decode(),
+                                               lib.fp4_last_error().decode()))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device=None):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _as_bf16_bits(x):
+    if x.dtype == torch.bfloat16:
+        x = x.view(torch.int16)
+    if x.dtype not in (torch.int16, torch.uint16):
+        raise TypeError("x must be bfloat16 (or its int16 bit view)")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a 2-D row-major tensor")
+    return x
+
+
+def _fmt(fmt):
+    return FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+# ------------------------------------------------------------------ amax --
+def amax(x, rht=False, signs=0, out=None):
+    """Tensor amax (optionally of the column-RHT-rotated tensor) -> device fp32 [1]."""
+    x = _as_bf16_bits(x)
+    out = torch.empty(1, dtype=torch.float32, device=x.device) if out is None else out
+    lib = load_library()
+    _check(lib.fp4_amax(_ptr(x), x.shape[0], x.shape[1], x.stride(0), int(bool(rht)), int(signs),
+                        _ptr(out), _stream(x.device)), "fp4_amax")
+    return out
+
+
+# -------------------------------------------------------------- quantize --
+@dataclass
+class Quantized:
+    """Codes and scales of one quantized matrix, plus what a GEMM needs."""
+    fmt: int
+    block: int
+    rows: int               # rows of the code matrix
+    cols: int               # cols of the code matrix (the blocked axis for 1D)
+    codes: torch.Tensor     # uint8 [rows, cols/2]
+    scales: torch.Tensor    # uint8 1D: [rows, cols/BS]; 2D: [rows/16, cols/16]
+    s_dec: torch.Tensor     # fp32 [1]
+    amax: torch.Tensor      # fp32 [1] (two-level formats)
+    codes_t: torch.Tensor = None   # 2D with emit_transpose: [cols, rows/2]
+
+    def operand(self, transposed=False):
+        """GEMM operand over the K-major code matrix (K = cols), or for 2D
+        weights with transposed=True over the codes of the transpose."""
+        bs = BLOCK_LEN[self.fmt]
+        if self.block == BLOCK_1D:
+            assert not transposed
+            return Operand(self.fmt, self.codes.data_ptr(), self.cols // 2, self.scales.data_ptr(),
+                           self.cols // bs, 1, 1, self.s_dec.data_ptr())
+        if not transposed:
+            return Operand(self.fmt, self.codes.data_ptr(), self.cols // 2, self.scales.data_ptr(),
+                           self.cols // 16, 1, 16, self.s_dec.data_ptr())
+        assert self.codes_t is not None
+        return Operand(self.fmt, self.codes_t.data_ptr(), self.rows // 2, self.scales.data_ptr(),
+                       1, self.cols // 16, 16, self.s_dec.data_ptr())
+
+
+def quantize(x, fmt="nvfp4", block="1d", orient="row", rnd="rne", seed=0, offset=0, rht=False,
+             signs=0, target=448.0, amax_in=None, emit_transpose=False, counters=None):
+    """Quantize a bf16 [R, C] matrix.  orient="col" quantizes X^T ([C, R]).
+
+    amax_in: None -> computed on the device; else a device fp32 [1] tensor read
+    as the (possibly stale) tensor amax.  counters: optional device uint64 [5]
+    tensor, accumulated.
+    """
+    x = _as_bf16_bits(x)
+    f = _fmt(fmt)
+    R, C = x.shape
+    blk = BLOCK_2D16 if block == "2d" else BLOCK_1D
+    col = orient == "col"
+    rows, cols = (C, R) if col else (R, C)
+    bs = 16 if blk == BLOCK_2D16 else BLOCK_LEN[f]
+    dev = x.device
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    if blk == BLOCK_2D16:
+        scales = torch.empty((rows // 16, cols // 16), dtype=torch.uint8, device=dev)
+    else:
+        scales = torch.empty((rows, cols // bs), dtype=torch.uint8, device=dev)
+    codes_t = (torch.empty((cols, rows // 2), dtype=torch.uint8, device=dev)
+               if emit_transpose else None)
+    s_dec = torch.empty(1, dtype=torch.float32, device=dev)
+    am = amax_in if amax_in is not None else torch.empty(1, dtype=torch.float32, device=dev)
+    desc = QuantDesc(f, blk, COLWISE if col else ROWWISE, SR if rnd == "sr" else RNE,
+                     int(seed), int(offset), int(bool(rht)), int(signs), float(target),
+                     int(amax_in is not None), int(bool(emit_transpose)))
+    lib = load_library()
+    _check(lib.fp4_quantize(ctypes.byref(desc), _ptr(x), R, C, x.stride(0), _ptr(codes),
+                            _ptr(scales), _ptr(codes_t), _ptr(am), _ptr(s_dec), _ptr(counters),
+                            _stream(dev)), "fp4_quantize")
+    return Quantized(f, blk, rows, cols, codes, scales, s_dec, am, codes_t)
+
+
+def new_counters(device="cuda"):
+    return torch.zeros(5, dtype=torch.int64, device=device)
+
+
+def counters_dict(c):
+    return dict(zip(COUNTER_NAMES, [int(v) for v in c.cpu().tolist()]))
+
+
+# ------------------------------------------------------------ dequantize --
+def dequantize(q: Quantized, out_dtype=torch.float32):
+    out = torch.empty((q.rows, q.cols), dtype=out_dtype, device=q.codes.device)
+    lib = load_library()
+    _check(lib.fp4_dequantize(q.fmt, q.block, _ptr(q.codes), _ptr(q.scales), _ptr(q.s_dec),
+                              q.rows, q.cols, _ptr(out), int(out_dtype == torch.float32),
+                              _stream(out.device)), "fp4_dequantize")
+    return out
+
+
+# ------------------------------------------------------------------- RHT --
+def rht16(x, signs):
+    x = _as_bf16_bits(x)
+    y = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    lib = load_library()
+    _check(lib.fp4_rht16(_ptr(x), x.shape[0], x.shape[1], x.stride(0), int(signs), _ptr(y),
+                         _stream(x.device)), "fp4_rht16")
+    return y
+
+
+# ------------------------------------------------------------------ GEMM --
+def gemm(a: Operand, b: Operand, M, N, K, out=None, accumulate=False, device=None):
+    """D[M, N] (+)= s_A s_B sum_k a[m, k] b[n, k] (fp32)."""
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=device or "cuda")
+    lib = load_library()
+    _check(lib.fp4_gemm(ctypes.byref(a), ctypes.byref(b), M, N, K, _ptr(out), out.stride(0),
+                        int(bool(accumulate)), _stream(out.device)), "fp4_gemm")
+    return out

@@ -1,0 +1,234 @@
+// C ABI of libfp4_mi355x.so (declared in include/fp4.h): host-side argument
+// validation, then kernel launches on the caller's stream.  Validation
+// touches no HIP API, so rejected calls work without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/fp4.h"
+#include "fp4_internal.hpp"
+
+#define FP4_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fp4_status fail(fp4_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+fp4_status ok() {
+  g_last_error.clear();
+  return FP4_OK;
+}
+
+fp4_status device_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(FP4_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int block_len(fp4_format f) { return f == FP4_MXFP4 ? 32 : 16; }
+
+bool valid_format(int f) { return f == FP4_NVFP4 || f == FP4_UE5M3 || f == FP4_MXFP4; }
+
+fp4_status check_bf16_input(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld) {
+  if (rows < 0 || cols < 0) return fail(FP4_ERR_SHAPE, "negative size rows=%lld cols=%lld",
+                                        (long long)rows, (long long)cols);
+  if (ld < cols) return fail(FP4_ERR_ARG, "ld=%lld < cols=%lld", (long long)ld, (long long)cols);
+  if (rows > 0 && cols > 0) {
+    if (!x) return fail(FP4_ERR_ARG, "x is null");
+    if (!aligned16(x)) return fail(FP4_ERR_ARG, "x must be 16-byte aligned");
+    if (ld % 8) return fail(FP4_ERR_ARG, "ld=%lld must be a multiple of 8", (long long)ld);
+    if (cols % 8) return fail(FP4_ERR_SHAPE, "cols=%lld must be a multiple of 8", (long long)cols);
+  }
+  return ok();
+}
+
+}  // namespace
+
+FP4_EXPORT const char* fp4_status_string(fp4_status s) {
+  switch (s) {
+    case FP4_OK: return "ok";
+    case FP4_ERR_ARG: return "invalid argument";
+    case FP4_ERR_SHAPE: return "invalid shape";
+    case FP4_ERR_UNSUPPORTED: return "unsupported combination";
+    case FP4_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+FP4_EXPORT const char* fp4_last_error(void) { return g_last_error.c_str(); }
+
+FP4_EXPORT fp4_status fp4_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int rht,
+                               uint32_t rht_signs, float* amax, void* stream) {
+  fp4_status st = check_bf16_input(x, rows, cols, ld);
+  if (st) return st;
+  if (!amax) return fail(FP4_ERR_ARG, "amax is null");
+  if (rht && rows % 16) return fail(FP4_ERR_SHAPE, "rht needs rows %% 16 == 0 (rows=%lld)",
+                                    (long long)rows);
+  if (rht_signs > 0xFFFFu) return fail(FP4_ERR_ARG, "rht_signs must fit in 16 bits");
+  return device_status(fp4lib::launch_amax(x, rows, cols, ld, rht, rht_signs, amax,
+                                           static_cast<hipStream_t>(stream)),
+                       "fp4_amax launch");
+}
+
+FP4_EXPORT fp4_status fp4_quantize(const fp4_quant_desc* d, const uint16_t* x, int64_t rows,
+                                   int64_t cols, int64_t ld, uint8_t* codes, uint8_t* scales,
+                                   uint8_t* codes_t, float* amax, float* s_dec,
+                                   fp4_counters* counters, void* stream) {
+  if (!d) return fail(FP4_ERR_ARG, "desc is null");
+  if (!valid_format(d->format)) return fail(FP4_ERR_ARG, "bad format %d", (int)d->format);
+  if (d->block != FP4_BLOCK_1D && d->block != FP4_BLOCK_2D16)
+    return fail(FP4_ERR_ARG, "bad block %d", (int)d->block);
+  if (d->orient != FP4_ROWWISE && d->orient != FP4_COLWISE)
+    return fail(FP4_ERR_ARG, "bad orient %d", (int)d->orient);
+  if (d->round != FP4_RNE && d->round != FP4_SR) return fail(FP4_ERR_ARG, "bad round %d", (int)d->round);
+  fp4_status st = check_bf16_input(x, rows, cols, ld);
+  if (st) return st;
+  const bool two_level = d->format != FP4_MXFP4;
+  const bool is2d = d->block == FP4_BLOCK_2D16;
+  const int bs = block_len(d->format);
+  if (is2d && d->format == FP4_MXFP4) return fail(FP4_ERR_UNSUPPORTED, "2D16 blocks need NVFP4 or UE5M3");
+  if (is2d && d->orient != FP4_ROWWISE) return fail(FP4_ERR_UNSUPPORTED, "2D16 blocks are ROWWISE only");
+  if (is2d && d->round != FP4_RNE) return fail(FP4_ERR_UNSUPPORTED, "2D16 blocks are RNE only");
+  if (d->rht && d->orient != FP4_COLWISE) return fail(FP4_ERR_UNSUPPORTED, "RHT needs COLWISE");
+  if (d->rht && d->format == FP4_MXFP4) return fail(FP4_ERR_UNSUPPORTED, "RHT needs NVFP4 or UE5M3");
+  if (d->rht && d->rht_signs > 0xFFFFu) return fail(FP4_ERR_ARG, "rht_signs must fit in 16 bits");
+  if (d->amax_given && !two_level) return fail(FP4_ERR_UNSUPPORTED, "MXFP4 has no tensor amax");
+  if (!is2d && d->emit_transpose) return fail(FP4_ERR_UNSUPPORTED, "emit_transpose needs 2D16");
+  if (two_level && !(std::isfinite(d->target) && d->target > 0.0f))
+    return fail(FP4_ERR_ARG, "target must be finite and > 0");
+  if (is2d) {
+    if (rows % 16 || cols % 16)
+      return fail(FP4_ERR_SHAPE, "2D16 needs rows, cols multiples of 16 (%lld x %lld)",
+                  (long long)rows, (long long)cols);
+  } else if (d->orient == FP4_ROWWISE) {
+    if (cols % bs) return fail(FP4_ERR_SHAPE, "cols=%lld must be a multiple of %d", (long long)cols, bs);
+  } else {
+    if (rows % bs) return fail(FP4_ERR_SHAPE, "rows=%lld must be a multiple of %d", (long long)rows, bs);
+  }
+  const bool empty = rows == 0 || cols == 0;
+  if (!empty) {
+    if (!codes || !scales) return fail(FP4_ERR_ARG, "codes/scales are null");
+    if (!aligned16(codes)) return fail(FP4_ERR_ARG, "codes must be 16-byte aligned");
+    if (d->emit_transpose && (!codes_t || !aligned16(codes_t)))
+      return fail(FP4_ERR_ARG, "codes_t must be non-null and 16-byte aligned");
+  }
+  if (two_level && !amax) return fail(FP4_ERR_ARG, "amax is null");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (two_level && !d->amax_given) {
+    hipError_t e = fp4lib::launch_amax(x, rows, cols, ld, d->rht, d->rht_signs, amax, s);
+    if (e != hipSuccess) return device_status(e, "fp4_quantize amax launch");
+  }
+  fp4lib::QuantArgs a{};
+  a.x = x;
+  a.rows = rows;
+  a.cols = cols;
+  a.ld = ld;
+  a.codes = codes;
+  a.scales = scales;
+  a.codes_t = codes_t;
+  a.amax = amax;
+  a.s_dec = s_dec;
+  a.counters = counters;
+  a.target = d->target;
+  a.seed = d->seed;
+  a.offset = d->offset;
+  a.rht_signs = d->rht_signs;
+  a.format = d->format;
+  a.round = d->round;
+  a.rht = d->rht;
+  a.emit_transpose = d->emit_transpose;
+  hipError_t e;
+  if (is2d) e = fp4lib::launch_quant_2d(a, s);
+  else if (d->orient == FP4_ROWWISE) e = fp4lib::launch_quant_row(a, s);
+  else e = fp4lib::launch_quant_col(a, s);
+  return device_status(e, "fp4_quantize launch");
+}
+
+FP4_EXPORT fp4_status fp4_dequantize(fp4_format format, fp4_block block, const uint8_t* codes,
+                                     const uint8_t* scales, const float* s_dec, int64_t rows,
+                                     int64_t cols, void* out, int out_fp32, void* stream) {
+  if (!valid_format(format)) return fail(FP4_ERR_ARG, "bad format %d", (int)format);
+  if (block != FP4_BLOCK_1D && block != FP4_BLOCK_2D16) return fail(FP4_ERR_ARG, "bad block %d", (int)block);
+  if (block == FP4_BLOCK_2D16 && format == FP4_MXFP4)
+    return fail(FP4_ERR_UNSUPPORTED, "2D16 blocks need NVFP4 or UE5M3");
+  if (rows < 0 || cols < 0) return fail(FP4_ERR_SHAPE, "negative size");
+  const int bs = block_len(format);
+  if (cols % bs) return fail(FP4_ERR_SHAPE, "cols=%lld must be a multiple of %d", (long long)cols, bs);
+  if (block == FP4_BLOCK_2D16 && rows % 16) return fail(FP4_ERR_SHAPE, "2D16 needs rows %% 16 == 0");
+  if (rows > 0 && cols > 0) {
+    if (!codes || !scales || !out) return fail(FP4_ERR_ARG, "null pointer");
+    if (!aligned16(codes) || !aligned16(out)) return fail(FP4_ERR_ARG, "codes/out must be 16-byte aligned");
+    if (format != FP4_MXFP4 && !s_dec) return fail(FP4_ERR_ARG, "s_dec is null");
+  }
+  if (rows == 0 || cols == 0) return ok();
+  return device_status(fp4lib::launch_dequant(format, block == FP4_BLOCK_2D16, codes, scales, s_dec,
+                                              rows, cols, out, out_fp32,
+                                              static_cast<hipStream_t>(stream)),
+                       "fp4_dequantize launch");
+}
+
+FP4_EXPORT fp4_status fp4_rht16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                                uint32_t rht_signs, float* y, void* stream) {
+  fp4_status st = check_bf16_input(x, rows, cols, ld);
+  if (st) return st;
+  if (rows % 16) return fail(FP4_ERR_SHAPE, "rows=%lld must be a multiple of 16", (long long)rows);
+  if (rht_signs > 0xFFFFu) return fail(FP4_ERR_ARG, "rht_signs must fit in 16 bits");
+  if (rows > 0 && cols > 0 && (!y || (reinterpret_cast<uintptr_t>(y) & 7u)))
+    return fail(FP4_ERR_ARG, "y must be non-null and 8-byte aligned");
+  if (rows == 0 || cols == 0) return ok();
+  return device_status(fp4lib::launch_rht16(x, rows, cols, ld, rht_signs, y,
+                                            static_cast<hipStream_t>(stream)),
+                       "fp4_rht16 launch");
+}
+
+FP4_EXPORT fp4_status fp4_gemm(const fp4_operand* A, const fp4_operand* B, int64_t M, int64_t N,
+                               int64_t K, float* D, int64_t ldd, int accumulate, void* stream) {
+  if (!A || !B) return fail(FP4_ERR_ARG, "operand descriptor is null");
+  if (!valid_format(A->format) || !valid_format(B->format)) return fail(FP4_ERR_ARG, "bad format");
+  if (A->format != B->format) return fail(FP4_ERR_UNSUPPORTED, "A and B formats differ");
+  if (M < 0 || N < 0 || K < 0) return fail(FP4_ERR_SHAPE, "negative size");
+  const int bs = block_len(A->format);
+  if (K % bs) return fail(FP4_ERR_SHAPE, "K=%lld must be a multiple of %d", (long long)K, bs);
+  if (ldd < N) return fail(FP4_ERR_ARG, "ldd=%lld < N=%lld", (long long)ldd, (long long)N);
+  const fp4_operand* ops[2] = {A, B};
+  for (int i = 0; i < 2; ++i) {
+    const fp4_operand* o = ops[i];
+    if (o->scale_row_group != 1 && o->scale_row_group != 16)
+      return fail(FP4_ERR_ARG, "scale_row_group must be 1 or 16");
+    if (o->scale_row_group == 16 && A->format == FP4_MXFP4)
+      return fail(FP4_ERR_UNSUPPORTED, "2D16 scales need NVFP4 or UE5M3");
+    if (M > 0 && N > 0 && K > 0) {
+      if (!o->codes || !o->scales) return fail(FP4_ERR_ARG, "operand %c has a null pointer", "AB"[i]);
+      if (o->ld_codes < K / 2) return fail(FP4_ERR_ARG, "operand %c ld_codes < K/2", "AB"[i]);
+      if (!aligned16(o->codes) || o->ld_codes % 16)
+        return fail(FP4_ERR_ARG, "operand %c codes must be 16-byte aligned with ld_codes %% 16 == 0",
+                    "AB"[i]);
+      if (o->scale_stride_row < 0 || o->scale_stride_kblk < 0)
+        return fail(FP4_ERR_ARG, "negative scale stride");
+    }
+  }
+  if (M > 0 && N > 0 && !D) return fail(FP4_ERR_ARG, "D is null");
+  if (M == 0 || N == 0) return ok();
+  fp4lib::GemmOperand a{A->codes, A->ld_codes, A->scales, A->scale_stride_row,
+                        A->scale_stride_kblk, A->scale_row_group, A->s_dec};
+  fp4lib::GemmOperand b{B->codes, B->ld_codes, B->scales, B->scale_stride_row,
+                        B->scale_stride_kblk, B->scale_row_group, B->s_dec};
+  return device_status(fp4lib::launch_gemm(A->format, a, b, M, N, K, D, ldd, accumulate,
+                                           static_cast<hipStream_t>(stream)),
+                       "fp4_gemm launch");
+}

@@ -1,0 +1,242 @@
+// Device arithmetic shared by the gfx950 quantizer kernels.
+//
+// Every function is written for bit-exact, order-fixed fp32 evaluation: the
+// library is compiled with -ffp-contract=off, fp32 denormals preserved and
+// correctly rounded fp32 division, so each '*', '/' and '+' below is one
+// IEEE operation in the order written.
+//
+// Method (NVFP4 pretraining paper, arXiv:2509.25149):
+//   App. B.1 Eq. 1  s_enc_G = 6 T / amax_X, s_dec_G = 1 / s_enc_G
+//   App. B.2 Eq. 2  s_dec_L = amax_B / 6;  Eq. 3: scale = RNE(s_dec_L s_enc_G)
+//                   s_enc_L = 1 / (scale * s_dec_G)
+//   App. B.3 Eq. 4  code = Q(x * s_enc_L)
+//   App. B.4 / §3   MXFP4: power-of-two scale rounded up, no tensor scale
+//   §4.4            stochastic rounding for gradients
+//   App. C          16-point Hadamard rotation, H_r = D_r H
+// Conventions the pages leave open (clamps, tie handling, sign of zero, the
+// random-bit layout) are fixed in include/fp4.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4dev {
+
+constexpr float kFltMax = 3.40282346638528859812e+38f;
+
+enum Fmt : int { kNV = 0, kUE = 1, kMX = 2 };
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// ---------------------------------------------------------------- scales --
+// 8-bit scale with a 3-bit mantissa and exponent bias BIAS (E4M3: 7, max
+// 448 = code 0x7E; UE5M3: 15, max 122880 = code 0xFF), round to nearest
+// even, saturating at the maximum.  t >= 0 and finite.
+template <int BIAS>
+__device__ __forceinline__ uint32_t scale_m3_encode(float t, float tmax, uint32_t maxcode) {
+  if (t >= tmax) return maxcode;
+  constexpr float kMinNormal = (BIAS == 7) ? 0x1p-6f : 0x1p-14f;
+  constexpr float kInvSubStep = (BIAS == 7) ? 0x1p9f : 0x1p17f;   // 1 / subnormal spacing
+  if (t < kMinNormal) {
+    // subnormal range: a multiple of the spacing, rint = half to even
+    return static_cast<uint32_t>(__builtin_rintf(t * kInvSubStep));
+  }
+  const uint32_t b = __float_as_uint(t);
+  // keep 3 mantissa bits, nearest-even on the 20 dropped bits; a carry
+  // moves into the exponent field as it should
+  const uint32_t r = b + 0x7FFFFu + ((b >> 20) & 1u);
+  return (r >> 20) - ((127u - BIAS) << 3);
+}
+
+template <int BIAS>
+__device__ __forceinline__ float scale_m3_decode(uint32_t code) {
+  constexpr float kSubStep = (BIAS == 7) ? 0x1p-9f : 0x1p-17f;
+  if (code < 8u) return static_cast<float>(code) * kSubStep;        // exact
+  return __uint_as_float((code + ((127u - BIAS) << 3)) << 20);
+}
+
+__device__ __forceinline__ float ue8m0_decode(uint32_t code) {
+  return code ? __uint_as_float(code << 23) : __uint_as_float(0x00400000u);  // 2^-127
+}
+
+// Tensor-level scales (Eq. 1).  amax = 0 -> s_enc = 1; overflow -> FLT_MAX.
+__device__ __forceinline__ void global_scales(float amax, float target, float& s_enc,
+                                              float& s_dec) {
+  const float six_t = 6.0f * target;
+  float e = 1.0f;
+  if (amax != 0.0f) {
+    e = six_t / amax;
+    if (!(e <= kFltMax)) e = kFltMax;
+  }
+  s_enc = e;
+  s_dec = 1.0f / e;
+}
+
+struct ScaleEvents {
+  uint32_t sat, under, sub;
+};
+
+// Two-level block scale (Eqs. 2-3) -> scale code; s_enc_l receives the
+// local encode scale (0 for a zero code, reciprocal clamped to FLT_MAX).
+template <int FMT>
+__device__ __forceinline__ uint32_t block_scale_two_level(float amax_b, float s_enc_g,
+                                                          float s_dec_g, float& s_enc_l,
+                                                          ScaleEvents& ev) {
+  const float s_dec_l = amax_b / 6.0f;
+  float t = s_dec_l * s_enc_g;
+  if (!(t <= kFltMax)) t = kFltMax;
+  uint32_t code;
+  float s_hat;
+  if constexpr (FMT == kNV) {
+    ev.sat += (t > 448.0f);
+    code = scale_m3_encode<7>(t, 448.0f, 0x7Eu);
+    s_hat = scale_m3_decode<7>(code);
+  } else {
+    ev.sat += (t > 122880.0f);
+    code = scale_m3_encode<15>(t, 122880.0f, 0xFFu);
+    s_hat = scale_m3_decode<15>(code);
+  }
+  const float p = s_hat * s_dec_g;
+  const float inv = fminf(1.0f / p, kFltMax);
+  s_enc_l = code ? inv : 0.0f;
+  ev.under += (amax_b > 0.0f) & (code == 0u);
+  ev.sub += (code >= 1u) & (code <= 7u);
+  return code;
+}
+
+// MXFP4 block scale (App. B.4): the smallest e with 6 * 2^e >= amax_B,
+// clamped to [-127, 127]; a zero block takes -127.  Returns e + 127 and the
+// exact encode scale 2^-e.
+__device__ __forceinline__ uint32_t block_scale_mx(float amax_b, float& s_enc_l) {
+  int e = -127;
+  if (amax_b > 0.0f) {
+    const uint32_t b = __float_as_uint(amax_b);
+    const int E = static_cast<int>(b >> 23);
+    const uint32_t man = b & 0x7FFFFFu;
+    int k;        // floor(log2(amax))
+    bool le;      // amax <= 1.5 * 2^k
+    if (E == 0) {  // fp32 subnormal: amax = man * 2^-149
+      const int lead_pos = 31 - __clz(man);
+      k = lead_pos - 149;
+      const uint32_t lead = 1u << lead_pos;
+      le = man <= lead + (lead >> 1);
+    } else {
+      k = E - 127;
+      le = man <= 0x400000u;
+    }
+    // 6 * 2^(k-2) = 1.5 * 2^k covers amax iff le; otherwise 6 * 2^(k-1) does
+    e = le ? k - 2 : k - 1;
+    e = e < -127 ? -127 : (e > 127 ? 127 : e);
+  }
+  const int ne = -e;   // encode exponent in [-127, 127]
+  s_enc_l = ne >= -126 ? __uint_as_float(static_cast<uint32_t>(ne + 127) << 23)
+                       : __uint_as_float(0x00400000u);
+  return static_cast<uint32_t>(e + 127);
+}
+
+// ------------------------------------------------------------ elements --
+// E2M1 round to nearest even of y (Eq. 4), |y| > 6 saturates to 6; the
+// sign bit copies y's.  Returns the 4-bit code.
+__device__ __forceinline__ uint32_t e2m1_rne(float y) {
+  const uint32_t yb = __float_as_uint(y);
+  const uint32_t sign = (yb >> 28) & 8u;
+  const uint32_t b = yb & 0x7FFFFFFFu;
+  const float m = __uint_as_float(b);
+  // below 1 the grid is {0, 0.5, 1} with ties 0.25 -> 0 and 0.75 -> 1
+  const uint32_t small = static_cast<uint32_t>(m > 0.25f) + static_cast<uint32_t>(m >= 0.75f);
+  // in [1, 6) E2M1 is a float with one mantissa bit and fp32's binades:
+  // round the fp32 mantissa to one bit, nearest-even, read exponent|bit
+  const uint32_t r = b + 0x1FFFFFu + ((b >> 22) & 1u);
+  const uint32_t big = (r >> 22) - 252u;
+  uint32_t mag = m < 1.0f ? small : big;
+  mag = m < 6.0f ? mag : 7u;
+  return sign | mag;
+}
+
+// Stochastic E2M1 rounding (§4.4): lo = largest magnitude <= |y|, hi the
+// next; round up iff r16 < 65536 (|y| - lo) / (hi - lo), computed exactly
+// as (|y| - lo) * (65536 / (hi - lo)).  |y| >= 6 gives 6.
+__device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t r16) {
+  const uint32_t yb = __float_as_uint(y);
+  const uint32_t sign = (yb >> 28) & 8u;
+  const uint32_t b = yb & 0x7FFFFFFFu;
+  const float m = __uint_as_float(b);
+  uint32_t lo;
+  float lo_v, inv_gap;
+  if (m < 1.0f) {
+    lo = m >= 0.5f ? 1u : 0u;
+    lo_v = m >= 0.5f ? 0.5f : 0.0f;
+    inv_gap = 131072.0f;                             // 65536 / 0.5
+  } else {
+    lo = (b >> 22) - 252u;                          // truncation to one mantissa bit
+    lo_v = __uint_as_float(b & 0xFFC00000u);
+    const uint32_t E = b >> 23;                     // 127, 128 or 129 here
+    inv_gap = __uint_as_float((271u - E) << 23);    // 65536 / 2^(E - 128)
+  }
+  const float frac_s = (m - lo_v) * inv_gap;        // exact
+  uint32_t mag = lo + static_cast<uint32_t>(static_cast<float>(r16) < frac_s);
+  mag = m < 6.0f ? mag : 7u;
+  return sign | mag;
+}
+
+// -------------------------------------------------------------- Philox --
+// Philox4x32-10 (Salmon et al., SC'11): ten rounds of two 32x32->64
+// multiplies, key advanced by the Weyl constants between rounds.
+struct U4 {
+  uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ U4 philox4x32_10(U4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    if (i) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = static_cast<uint64_t>(0xD2511F53u) * c.x;
+    const uint64_t p1 = static_cast<uint64_t>(0xCD9E8D57u) * c.z;
+    const uint32_t hi0 = static_cast<uint32_t>(p0 >> 32), lo0 = static_cast<uint32_t>(p0);
+    const uint32_t hi1 = static_cast<uint32_t>(p1 >> 32), lo1 = static_cast<uint32_t>(p1);
+    c = U4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+  }
+  return c;
+}
+
+// 16 random bits for 8 consecutive output indices 8g .. 8g+7.
+__device__ __forceinline__ U4 sr_words(uint64_t g, uint64_t seed, uint64_t offset) {
+  return philox4x32_10(U4{static_cast<uint32_t>(g), static_cast<uint32_t>(g >> 32),
+                          static_cast<uint32_t>(offset), static_cast<uint32_t>(offset >> 32)},
+                       static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32));
+}
+
+__device__ __forceinline__ uint32_t sr_bits(const U4& w, int j) {   // j = index & 7
+  const uint32_t word = (j >> 1) == 0 ? w.x : (j >> 1) == 1 ? w.y : (j >> 1) == 2 ? w.z : w.w;
+  return (j & 1) ? (word >> 16) : (word & 0xFFFFu);
+}
+
+// ----------------------------------------------------------------- RHT --
+// (1/4) D_r H16 v: Walsh-Hadamard butterflies with strides 1, 2, 4, 8
+// (each (a, b) -> (a + b, a - b)), exact 1/4, then output i negated when bit
+// i of `signs` is set (H_r = D_r H flips rows of H, App. C).
+__device__ __forceinline__ void rht16(float (&v)[16], uint32_t signs) {
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if ((i & h) == 0) {
+        const float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float q = v[i] * 0.25f;
+    v[i] = ((signs >> i) & 1u) ? -q : q;
+  }
+}
+
+}  // namespace fp4dev

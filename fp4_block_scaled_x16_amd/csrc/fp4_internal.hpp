@@ -1,0 +1,52 @@
+// Internal launch interface between the C ABI (fp4_api.cpp) and the kernel
+// translation units.  Arguments have been validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/fp4.h"
+
+namespace fp4lib {
+
+struct QuantArgs {
+  const uint16_t* x;
+  int64_t rows, cols, ld;
+  uint8_t* codes;
+  uint8_t* scales;
+  uint8_t* codes_t;
+  const float* amax;     // device; read by the quantize kernel (MXFP4: unused)
+  float* s_dec;          // device or null
+  fp4_counters* counters;
+  float target;
+  uint64_t seed, offset;
+  uint32_t rht_signs;
+  int format, round, rht, emit_transpose;
+};
+
+struct GemmOperand {
+  const uint8_t* codes;
+  int64_t ld_codes;
+  const uint8_t* scales;
+  int64_t s_row, s_kblk;
+  int row_group;
+  const float* s_dec;
+};
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int rht,
+                       uint32_t signs, float* amax, hipStream_t s);
+hipError_t launch_quant_row(const QuantArgs& a, hipStream_t s);
+hipError_t launch_quant_col(const QuantArgs& a, hipStream_t s);
+hipError_t launch_quant_2d(const QuantArgs& a, hipStream_t s);
+hipError_t launch_dequant(int format, int block2d, const uint8_t* codes, const uint8_t* scales,
+                          const float* s_dec, int64_t rows, int64_t cols, void* out, int out_fp32,
+                          hipStream_t s);
+hipError_t launch_rht16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, uint32_t signs,
+                        float* y, hipStream_t s);
+hipError_t launch_gemm(int format, const GemmOperand& A, const GemmOperand& B, int64_t M, int64_t N,
+                       int64_t K, float* D, int64_t ldd, int accumulate, hipStream_t s);
+
+}  // namespace fp4lib

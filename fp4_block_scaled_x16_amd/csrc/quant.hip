@@ -1,0 +1,667 @@
+// gfx950 kernels for the quantization side of FP4 block scaling:
+//   tensor amax (plain and in the RHT-rotated space), rowwise 1D quantizer,
+//   colwise (transposing) 1D quantizer with optional fused 16-point RHT,
+//   16x16 2D quantizer emitting W and W^T codes, dequantizer, standalone RHT.
+//
+// All of these are HBM-bound streams: every kernel reads its bf16 input
+// once with 16-byte vector loads, keeps the block in registers (and LDS
+// where a transpose is needed), and writes codes/scales with the widest
+// contiguous stores the layout allows.  Grids are capped at a few
+// workgroups per CU and walk the work with grid-stride loops, so the
+// tensor-scale prologue and the counter flush are paid once per workgroup.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp4_device.hpp"
+#include "fp4_internal.hpp"
+
+using namespace fp4dev;
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// ----------------------------------------------------------- counters --
+// Reduce five per-thread event counts over the workgroup and add the
+// nonzero totals to the caller's device counters (one atomic each).
+__device__ __forceinline__ void flush_counters(uint32_t (&c)[5], fp4_counters* out) {
+  __shared__ uint32_t red[kThreads / 64][5];
+#pragma unroll
+  for (int k = 0; k < 5; ++k) {
+    uint32_t v = c[k];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    c[k] = v;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+#pragma unroll
+    for (int k = 0; k < 5; ++k) red[wave][k] = c[k];
+  }
+  __syncthreads();
+  if (threadIdx.x < 5) {
+    uint32_t t = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) t += red[w][threadIdx.x];
+    if (t) {
+      unsigned long long* dst = reinterpret_cast<unsigned long long*>(out) + threadIdx.x;
+      atomicAdd(dst, static_cast<unsigned long long>(t));
+    }
+  }
+}
+
+__device__ __forceinline__ void unpack8(const uint4& q, float* v) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+    v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+  }
+}
+
+// Quantize BS values (already in fp32, in block order) with the encode
+// scale; returns BS/8 packed code words (element i at bits 4 (i % 8) of
+// word i / 8).  `idx0` is the output-layout index of element 0 (SR only).
+template <int BS, int RND, bool CNT>
+__device__ __forceinline__ void encode_block(const float* v, float s_enc_l, uint64_t idx0,
+                                             uint64_t seed, uint64_t offset, uint32_t* words,
+                                             uint32_t (&cnt)[5]) {
+#pragma unroll
+  for (int q = 0; q < BS / 8; ++q) {
+    U4 rw{0, 0, 0, 0};
+    if constexpr (RND == FP4_SR) rw = sr_words((idx0 >> 3) + q, seed, offset);
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float xv = v[q * 8 + i];
+      const float y = xv * s_enc_l;
+      uint32_t c;
+      if constexpr (RND == FP4_SR) c = e2m1_sr(y, sr_bits(rw, i));
+      else c = e2m1_rne(y);
+      word |= c << (4 * i);
+      if constexpr (CNT) {
+        cnt[3] += fabsf(y) > 6.0f;
+        cnt[4] += (xv != 0.0f) & ((c & 7u) == 0u);
+      }
+    }
+    words[q] = word;
+  }
+}
+
+template <int FMT>
+__device__ __forceinline__ uint32_t scale_for_block(float amax_b, float s_enc_g, float s_dec_g,
+                                                    float& s_enc_l, uint32_t (&cnt)[5]) {
+  if constexpr (FMT == kMX) {
+    return block_scale_mx(amax_b, s_enc_l);
+  } else {
+    ScaleEvents ev{0, 0, 0};
+    const uint32_t sc = block_scale_two_level<FMT>(amax_b, s_enc_g, s_dec_g, s_enc_l, ev);
+    cnt[0] += ev.sat;
+    cnt[1] += ev.under;
+    cnt[2] += ev.sub;
+    return sc;
+  }
+}
+
+// ---------------------------------------------------------------- amax --
+__global__ void k_fill_u32(uint32_t* p, uint32_t v) { *p = v; }
+
+// max |x| over a [rows, cols] bf16 matrix, cols % 8 == 0.  |x| as fp32 bits
+// is monotone in the value, so an unsigned atomic max is exact.
+__global__ __launch_bounds__(kThreads) void k_amax(const uint16_t* __restrict__ x, int64_t rows,
+                                                   int64_t cols, int64_t ld,
+                                                   uint32_t* __restrict__ out) {
+  const uint64_t cpr = static_cast<uint64_t>(cols) >> 3;      // 16-byte chunks per row
+  const uint64_t n = static_cast<uint64_t>(rows) * cpr;
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
+  uint64_t i = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  uint64_t r = cpr ? i / cpr : 0, j = cpr ? i - r * cpr : 0;
+  const uint64_t sr = cpr ? stride / cpr : 0, sj = cpr ? stride - sr * cpr : 0;
+  uint32_t m = 0;
+  for (; i < n; i += stride) {
+    const uint4 q = *reinterpret_cast<const uint4*>(x + r * ld + j * 8);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      // bf16 -> |fp32| bits: the sign is dropped, the rest widened
+      m = max(m, (w[k] << 16) & 0x7FFF0000u);
+      m = max(m, w[k] & 0x7FFF0000u);
+    }
+    r += sr;
+    j += sj;
+    if (j >= cpr) {
+      j -= cpr;
+      ++r;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(m, o, 64)));
+  if ((threadIdx.x & 63) == 0 && m) atomicMax(out, m);
+}
+
+// max |(1/4) D_r H16 v| over every 16-row group v of every column.
+// One thread per (column pair, group); rows % 16 == 0, cols % 8 == 0.
+__global__ __launch_bounds__(kThreads) void k_amax_rht(const uint16_t* __restrict__ x,
+                                                       int64_t rows, int64_t cols, int64_t ld,
+                                                       uint32_t signs, uint32_t* __restrict__ out) {
+  const uint64_t pairs = static_cast<uint64_t>(cols) >> 1;
+  const uint64_t n = (static_cast<uint64_t>(rows) >> 4) * pairs;
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
+  float m = 0.0f;
+  for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n;
+       i += stride) {
+    const uint64_t g = i / pairs, p = i - g * pairs;
+    const uint16_t* src = x + g * 16 * ld + p * 2;
+    float a[16], b[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(src + k * ld);
+      a[k] = bf16_to_f32(w & 0xFFFFu);
+      b[k] = bf16_to_f32(w >> 16);
+    }
+    rht16(a, signs);
+    rht16(b, signs);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) m = fmaxf(m, fmaxf(fabsf(a[k]), fabsf(b[k])));
+  }
+  uint32_t mb = __float_as_uint(m);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mb = max(mb, static_cast<uint32_t>(__shfl_xor(mb, o, 64)));
+  if ((threadIdx.x & 63) == 0 && mb) atomicMax(out, mb);
+}
+
+// ------------------------------------------------------ rowwise 1D ------
+// One thread per block of BS consecutive elements of a row.
+template <int FMT, int RND, bool CNT>
+__global__ __launch_bounds__(kThreads) void k_quant_row(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, const float* __restrict__ amax,
+    float target, float* __restrict__ s_dec_out, uint64_t seed, uint64_t offset,
+    fp4_counters* __restrict__ counters) {
+  constexpr int BS = FMT == kMX ? 32 : 16;
+  float s_enc_g = 1.0f, s_dec_g = 1.0f;
+  if constexpr (FMT != kMX) global_scales(*amax, target, s_enc_g, s_dec_g);
+  if (s_dec_out && blockIdx.x == 0 && threadIdx.x == 0) *s_dec_out = s_dec_g;
+
+  const uint64_t bpr = static_cast<uint64_t>(cols) / BS;
+  const uint64_t n = static_cast<uint64_t>(rows) * bpr;
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
+  uint64_t i = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  uint64_t r = bpr ? i / bpr : 0, j = bpr ? i - r * bpr : 0;
+  const uint64_t sr = bpr ? stride / bpr : 0, sj = bpr ? stride - sr * bpr : 0;
+  uint32_t cnt[5] = {0, 0, 0, 0, 0};
+  for (; i < n; i += stride) {
+    const uint4* src = reinterpret_cast<const uint4*>(x + r * ld + j * BS);
+    uint4 q[BS / 8];
+#pragma unroll
+    for (int k = 0; k < BS / 8; ++k) q[k] = src[k];
+    float v[BS];
+#pragma unroll
+    for (int k = 0; k < BS / 8; ++k) unpack8(q[k], v + 8 * k);
+    float amax_b = 0.0f;
+#pragma unroll
+    for (int k = 0; k < BS; ++k) amax_b = fmaxf(amax_b, fabsf(v[k]));
+    float s_enc_l;
+    const uint32_t sc = scale_for_block<FMT>(amax_b, s_enc_g, s_dec_g, s_enc_l, cnt);
+    uint32_t words[BS / 8];
+    encode_block<BS, RND, CNT>(v, s_enc_l, r * static_cast<uint64_t>(cols) + j * BS, seed,
+                               offset, words, cnt);
+    uint8_t* dst = codes + r * (static_cast<uint64_t>(cols) >> 1) + j * (BS / 2);
+    if constexpr (BS == 16) {
+      *reinterpret_cast<uint2*>(dst) = make_uint2(words[0], words[1]);
+    } else {
+      *reinterpret_cast<uint4*>(dst) = make_uint4(words[0], words[1], words[2], words[3]);
+    }
+    scales[r * bpr + j] = static_cast<uint8_t>(sc);
+    r += sr;
+    j += sj;
+    if (j >= bpr) {
+      j -= bpr;
+      ++r;
+    }
+  }
+  if constexpr (CNT) flush_counters(cnt, counters);
+}
+
+// ------------------------------------------------------ colwise 1D ------
+// Quantizes X^T: blocks are BS consecutive rows of one column.  A workgroup
+// stages a (8 BS) x 64 tile of X in LDS (coalesced 16-byte row loads), then
+// each thread takes one column pair and one row group, optionally rotates
+// each 16-row group by the RHT, and writes the codes of X^T so that the 8
+// lanes of a column cover 8 consecutive groups (64 or 128 contiguous bytes).
+template <int FMT, int RND, bool RHT, bool CNT>
+__global__ __launch_bounds__(kThreads) void k_quant_col(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, const float* __restrict__ amax,
+    float target, float* __restrict__ s_dec_out, uint64_t seed, uint64_t offset,
+    uint32_t signs, fp4_counters* __restrict__ counters) {
+  constexpr int BS = FMT == kMX ? 32 : 16;
+  constexpr int TR = 8 * BS;        // tile rows (8 groups)
+  constexpr int TC = 64;            // tile columns
+  constexpr int LDW = TC / 2 + 1;   // LDS row pitch in 32-bit words (odd: spreads banks)
+  __shared__ uint32_t tile[TR * LDW];
+
+  float s_enc_g = 1.0f, s_dec_g = 1.0f;
+  if constexpr (FMT != kMX) global_scales(*amax, target, s_enc_g, s_dec_g);
+  if (s_dec_out && blockIdx.x == 0 && threadIdx.x == 0) *s_dec_out = s_dec_g;
+
+  const int64_t tiles_c = (cols + TC - 1) / TC;
+  const int64_t tiles_r = (rows + TR - 1) / TR;
+  const int64_t ntiles = tiles_c * tiles_r;
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int grp = lane & 7;                  // row group handled in the compute phase
+  const int pair = wave * 8 + (lane >> 3);   // column pair (0..31)
+  uint32_t cnt[5] = {0, 0, 0, 0, 0};
+
+  for (int64_t tile_id = blockIdx.x; tile_id < ntiles; tile_id += gridDim.x) {
+    const int64_t tr = tile_id / tiles_c, tc = tile_id - tr * tiles_c;
+    const int64_t r0 = tr * TR, c0 = tc * TC;
+    // load: TR rows x 8 chunks of 16 bytes
+#pragma unroll
+    for (int k = 0; k < TR * 8 / kThreads; ++k) {
+      const int chunk = t + k * kThreads;
+      const int lr = chunk >> 3, lc = (chunk & 7) * 8;
+      uint4 q = make_uint4(0, 0, 0, 0);
+      if (r0 + lr < rows && c0 + lc < cols)
+        q = *reinterpret_cast<const uint4*>(x + (r0 + lr) * ld + c0 + lc);
+      uint32_t* d = tile + lr * LDW + (lc >> 1);
+      d[0] = q.x;
+      d[1] = q.y;
+      d[2] = q.z;
+      d[3] = q.w;
+    }
+    __syncthreads();
+    const int64_t col = c0 + 2 * pair;
+    const int64_t row = r0 + grp * BS;
+    if (col < cols && row < rows) {
+      float a[BS], b[BS];
+#pragma unroll
+      for (int k = 0; k < BS; ++k) {
+        const uint32_t w = tile[(grp * BS + k) * LDW + pair];
+        a[k] = bf16_to_f32(w & 0xFFFFu);
+        b[k] = bf16_to_f32(w >> 16);
+      }
+      if constexpr (RHT) {
+        rht16(*reinterpret_cast<float(*)[16]>(a), signs);
+        rht16(*reinterpret_cast<float(*)[16]>(b), signs);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float* v = h ? b : a;
+        const int64_t c = col + h;
+        float amax_b = 0.0f;
+#pragma unroll
+        for (int k = 0; k < BS; ++k) amax_b = fmaxf(amax_b, fabsf(v[k]));
+        float s_enc_l;
+        const uint32_t sc = scale_for_block<FMT>(amax_b, s_enc_g, s_dec_g, s_enc_l, cnt);
+        uint32_t words[BS / 8];
+        encode_block<BS, RND, CNT>(v, s_enc_l, static_cast<uint64_t>(c) * rows + row, seed,
+                                   offset, words, cnt);
+        uint8_t* dst = codes + c * (rows >> 1) + (row >> 1);
+        if constexpr (BS == 16) {
+          *reinterpret_cast<uint2*>(dst) = make_uint2(words[0], words[1]);
+        } else {
+          *reinterpret_cast<uint4*>(dst) = make_uint4(words[0], words[1], words[2], words[3]);
+        }
+        scales[c * (rows / BS) + row / BS] = static_cast<uint8_t>(sc);
+      }
+    }
+    __syncthreads();
+  }
+  if constexpr (CNT) flush_counters(cnt, counters);
+}
+
+// ------------------------------------------------------------ 2D 16x16 --
+// A workgroup covers a 64 x 64 region (4 x 4 tiles).  Thread t owns the
+// 16 elements of row t/4 in tile column t%4; the 16 threads of a tile are
+// lanes {c, c+4, ..., c+60} of one wave, so the tile amax is four xor
+// shuffles.  Codes of W go straight out; codes of W^T go through a byte
+// transpose in LDS.
+template <int FMT, bool CNT>
+__global__ __launch_bounds__(kThreads) void k_quant_2d(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, uint8_t* __restrict__ codes_t,
+    const float* __restrict__ amax, float target, float* __restrict__ s_dec_out,
+    fp4_counters* __restrict__ counters) {
+  __shared__ uint8_t tr_buf[64][64 + 4];
+  float s_enc_g, s_dec_g;
+  global_scales(*amax, target, s_enc_g, s_dec_g);
+  if (s_dec_out && blockIdx.x == 0 && threadIdx.x == 0) *s_dec_out = s_dec_g;
+
+  const int64_t reg_c = (cols + 63) / 64, reg_r = (rows + 63) / 64;
+  const int64_t nreg = reg_c * reg_r;
+  const int t = threadIdx.x;
+  const int lr = t >> 2, tcol = t & 3;
+  uint32_t cnt[5] = {0, 0, 0, 0, 0};
+  for (int64_t reg = blockIdx.x; reg < nreg; reg += gridDim.x) {
+    const int64_t rr = reg / reg_c, rc = reg - rr * reg_c;
+    const int64_t r0 = rr * 64, c0 = rc * 64;
+    const int64_t row = r0 + lr, col = c0 + tcol * 16;
+    const bool valid = row < rows && col < cols;   // whole 16x16 tiles are in or out
+    float v[16];
+    if (valid) {
+      const uint4* src = reinterpret_cast<const uint4*>(x + row * ld + col);
+      unpack8(src[0], v);
+      unpack8(src[1], v + 8);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) v[k] = 0.0f;
+    }
+    float am = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) am = fmaxf(am, fabsf(v[k]));
+    uint32_t amb = __float_as_uint(am);
+#pragma unroll
+    for (int o = 4; o < 64; o <<= 1) amb = max(amb, static_cast<uint32_t>(__shfl_xor(amb, o, 64)));
+    const float amax_t = __uint_as_float(amb);
+    float s_enc_l;
+    uint32_t tc5[5] = {0, 0, 0, 0, 0};
+    const uint32_t sc = scale_for_block<FMT>(amax_t, s_enc_g, s_dec_g, s_enc_l, tc5);
+    uint32_t words[2];
+    encode_block<16, FP4_RNE, CNT>(v, s_enc_l, 0, 0, 0, words, cnt);
+    if (valid) {
+      *reinterpret_cast<uint2*>(codes + row * (cols >> 1) + (col >> 1)) =
+          make_uint2(words[0], words[1]);
+      if ((lr & 15) == 0) {
+        scales[(row >> 4) * (cols >> 4) + (col >> 4)] = static_cast<uint8_t>(sc);
+        if constexpr (CNT) {
+          cnt[0] += tc5[0];
+          cnt[1] += tc5[1];
+          cnt[2] += tc5[2];
+        }
+      }
+    } else if constexpr (CNT) {
+      // padding lanes quantized zeros: they contribute no events
+    }
+    if (codes_t) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        tr_buf[tcol * 16 + k][lr] = static_cast<uint8_t>((words[k >> 3] >> (4 * (k & 7))) & 0xFu);
+      __syncthreads();
+      const int lc = t >> 2, rseg = (t & 3) * 16;
+      const int64_t ocol = c0 + lc, orow = r0 + rseg;
+      if (ocol < cols && orow < rows) {
+        uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          w0 |= static_cast<uint32_t>(tr_buf[lc][rseg + k]) << (4 * k);
+          w1 |= static_cast<uint32_t>(tr_buf[lc][rseg + 8 + k]) << (4 * k);
+        }
+        *reinterpret_cast<uint2*>(codes_t + ocol * (rows >> 1) + (orow >> 1)) = make_uint2(w0, w1);
+      }
+      __syncthreads();
+    }
+  }
+  if constexpr (CNT) flush_counters(cnt, counters);
+}
+
+// ---------------------------------------------------------- dequantize --
+// One thread per block of BS codes of a [rows, cols] code matrix.
+template <int FMT, bool B2D, bool F32>
+__global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* __restrict__ codes,
+                                                      const uint8_t* __restrict__ scales,
+                                                      const float* __restrict__ s_dec,
+                                                      int64_t rows, int64_t cols,
+                                                      void* __restrict__ out) {
+  constexpr int BS = FMT == kMX ? 32 : 16;
+  const float sd = (FMT == kMX) ? 1.0f : *s_dec;
+  const uint64_t bpr = static_cast<uint64_t>(cols) / BS;
+  const uint64_t n = static_cast<uint64_t>(rows) * bpr;
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
+  for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n;
+       i += stride) {
+    const uint64_t r = i / bpr, j = i - r * bpr;
+    const uint32_t sc = B2D ? scales[(r >> 4) * bpr + j] : scales[i];
+    float s_hat;
+    if constexpr (FMT == kNV) s_hat = scale_m3_decode<7>(sc);
+    else if constexpr (FMT == kUE) s_hat = scale_m3_decode<15>(sc);
+    else s_hat = ue8m0_decode(sc);
+    uint32_t words[BS / 8];
+    const uint8_t* src = codes + i * (BS / 2);
+    if constexpr (BS == 16) {
+      const uint2 q = *reinterpret_cast<const uint2*>(src);
+      words[0] = q.x;
+      words[1] = q.y;
+    } else {
+      const uint4 q = *reinterpret_cast<const uint4*>(src);
+      words[0] = q.x;
+      words[1] = q.y;
+      words[2] = q.z;
+      words[3] = q.w;
+    }
+    float v[BS];
+#pragma unroll
+    for (int k = 0; k < BS; ++k) {
+      const uint32_t c = (words[k >> 3] >> (4 * (k & 7))) & 0xFu;
+      const uint32_t m = c & 7u;
+      // E2M1 magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6
+      const float mag = m < 4u ? 0.5f * static_cast<float>(m)
+                               : static_cast<float>((m & 1u) ? 3u << ((m - 4u) >> 1)
+                                                             : 2u << ((m - 4u) >> 1));
+      const float e = (c & 8u) ? -mag : mag;
+      v[k] = (e * s_hat) * sd;
+    }
+    if constexpr (F32) {
+      float4* dst = reinterpret_cast<float4*>(static_cast<float*>(out) + i * BS);
+#pragma unroll
+      for (int k = 0; k < BS / 4; ++k)
+        dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+    } else {
+      uint32_t h[BS / 2];
+#pragma unroll
+      for (int k = 0; k < BS / 2; ++k) {
+        uint32_t lo = __float_as_uint(v[2 * k]), hi = __float_as_uint(v[2 * k + 1]);
+        lo = (lo + 0x7FFFu + ((lo >> 16) & 1u)) >> 16;
+        hi = (hi + 0x7FFFu + ((hi >> 16) & 1u)) >> 16;
+        h[k] = (lo & 0xFFFFu) | (hi << 16);
+      }
+      uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + i * BS);
+#pragma unroll
+      for (int k = 0; k < BS / 8; ++k)
+        dst[k] = make_uint4(h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]);
+    }
+  }
+}
+
+// ------------------------------------------------------- standalone RHT --
+__global__ __launch_bounds__(kThreads) void k_rht16(const uint16_t* __restrict__ x, int64_t rows,
+                                                    int64_t cols, int64_t ld, uint32_t signs,
+                                                    float* __restrict__ y) {
+  const uint64_t pairs = static_cast<uint64_t>(cols) >> 1;
+  const uint64_t n = (static_cast<uint64_t>(rows) >> 4) * pairs;
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
+  for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n;
+       i += stride) {
+    const uint64_t g = i / pairs, p = i - g * pairs;
+    const uint16_t* src = x + g * 16 * ld + p * 2;
+    float a[16], b[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(src + k * ld);
+      a[k] = bf16_to_f32(w & 0xFFFFu);
+      b[k] = bf16_to_f32(w >> 16);
+    }
+    rht16(a, signs);
+    rht16(b, signs);
+    float* dst = y + g * 16 * static_cast<uint64_t>(cols) + p * 2;
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      *reinterpret_cast<float2*>(dst + k * static_cast<uint64_t>(cols)) = make_float2(a[k], b[k]);
+  }
+}
+
+int grid_for(uint64_t work_items, int per_cu) {
+  const uint64_t want = (work_items + kThreads - 1) / kThreads;
+  const uint64_t cap = static_cast<uint64_t>(fp4lib::device_cu_count()) * per_cu;
+  const uint64_t g = want < cap ? want : cap;
+  return static_cast<int>(g ? g : 1);
+}
+
+}  // namespace
+
+namespace fp4lib {
+
+int device_cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cache[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int rht,
+                       uint32_t signs, float* amax, hipStream_t s) {
+  uint32_t* out = reinterpret_cast<uint32_t*>(amax);
+  hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(1), 0, s, out, 0u);
+  if (rows > 0 && cols > 0) {
+    if (rht) {
+      const uint64_t n = static_cast<uint64_t>(rows / 16) * static_cast<uint64_t>(cols / 2);
+      hipLaunchKernelGGL(k_amax_rht, dim3(grid_for(n, 8)), dim3(kThreads), 0, s, x, rows, cols,
+                         ld, signs, out);
+    } else {
+      const uint64_t n = static_cast<uint64_t>(rows) * static_cast<uint64_t>(cols / 8);
+      hipLaunchKernelGGL(k_amax, dim3(grid_for(n, 8)), dim3(kThreads), 0, s, x, rows, cols, ld,
+                         out);
+    }
+  }
+  return hipGetLastError();
+}
+
+template <int FMT, int RND, bool CNT>
+static void row_launch(const QuantArgs& a, hipStream_t s) {
+  constexpr int BS = FMT == kMX ? 32 : 16;
+  const uint64_t n = static_cast<uint64_t>(a.rows) * static_cast<uint64_t>(a.cols / BS);
+  hipLaunchKernelGGL((k_quant_row<FMT, RND, CNT>), dim3(grid_for(n, 8)), dim3(kThreads), 0, s,
+                     a.x, a.rows, a.cols, a.ld, a.codes, a.scales, a.amax, a.target, a.s_dec,
+                     a.seed, a.offset, a.counters);
+}
+
+template <int FMT, int RND>
+static void row_dispatch_cnt(const QuantArgs& a, hipStream_t s) {
+  if (a.counters) row_launch<FMT, RND, true>(a, s);
+  else row_launch<FMT, RND, false>(a, s);
+}
+
+template <int FMT>
+static void row_dispatch_rnd(const QuantArgs& a, hipStream_t s) {
+  if (a.round == FP4_SR) row_dispatch_cnt<FMT, FP4_SR>(a, s);
+  else row_dispatch_cnt<FMT, FP4_RNE>(a, s);
+}
+
+hipError_t launch_quant_row(const QuantArgs& a, hipStream_t s) {
+  if (a.format == FP4_NVFP4) row_dispatch_rnd<kNV>(a, s);
+  else if (a.format == FP4_UE5M3) row_dispatch_rnd<kUE>(a, s);
+  else row_dispatch_rnd<kMX>(a, s);
+  return hipGetLastError();
+}
+
+template <int FMT, int RND, bool RHT, bool CNT>
+static void col_launch(const QuantArgs& a, hipStream_t s) {
+  constexpr int BS = FMT == kMX ? 32 : 16;
+  const int64_t tiles = ((a.rows + 8 * BS - 1) / (8 * BS)) * ((a.cols + 63) / 64);
+  const int64_t cap = static_cast<int64_t>(device_cu_count()) * 4;
+  const int grid = static_cast<int>(tiles < cap ? (tiles > 0 ? tiles : 1) : cap);
+  hipLaunchKernelGGL((k_quant_col<FMT, RND, RHT, CNT>), dim3(grid), dim3(kThreads), 0, s, a.x,
+                     a.rows, a.cols, a.ld, a.codes, a.scales, a.amax, a.target, a.s_dec, a.seed,
+                     a.offset, a.rht_signs, a.counters);
+}
+
+template <int FMT, int RND, bool RHT>
+static void col_dispatch_cnt(const QuantArgs& a, hipStream_t s) {
+  if (a.counters) col_launch<FMT, RND, RHT, true>(a, s);
+  else col_launch<FMT, RND, RHT, false>(a, s);
+}
+
+template <int FMT, int RND>
+static void col_dispatch_rht(const QuantArgs& a, hipStream_t s) {
+  if constexpr (FMT == kMX) {
+    col_dispatch_cnt<FMT, RND, false>(a, s);   // RHT with MXFP4 is rejected by validation
+  } else {
+    if (a.rht) col_dispatch_cnt<FMT, RND, true>(a, s);
+    else col_dispatch_cnt<FMT, RND, false>(a, s);
+  }
+}
+
+template <int FMT>
+static void col_dispatch_rnd(const QuantArgs& a, hipStream_t s) {
+  if (a.round == FP4_SR) col_dispatch_rht<FMT, FP4_SR>(a, s);
+  else col_dispatch_rht<FMT, FP4_RNE>(a, s);
+}
+
+hipError_t launch_quant_col(const QuantArgs& a, hipStream_t s) {
+  if (a.format == FP4_NVFP4) col_dispatch_rnd<kNV>(a, s);
+  else if (a.format == FP4_UE5M3) col_dispatch_rnd<kUE>(a, s);
+  else col_dispatch_rnd<kMX>(a, s);
+  return hipGetLastError();
+}
+
+template <int FMT, bool CNT>
+static void q2d_launch(const QuantArgs& a, hipStream_t s) {
+  const int64_t regions = ((a.rows + 63) / 64) * ((a.cols + 63) / 64);
+  const int64_t cap = static_cast<int64_t>(device_cu_count()) * 8;
+  const int grid = static_cast<int>(regions < cap ? (regions > 0 ? regions : 1) : cap);
+  hipLaunchKernelGGL((k_quant_2d<FMT, CNT>), dim3(grid), dim3(kThreads), 0, s, a.x, a.rows,
+                     a.cols, a.ld, a.codes, a.scales, a.emit_transpose ? a.codes_t : nullptr,
+                     a.amax, a.target, a.s_dec, a.counters);
+}
+
+hipError_t launch_quant_2d(const QuantArgs& a, hipStream_t s) {
+  if (a.format == FP4_NVFP4) {
+    if (a.counters) q2d_launch<kNV, true>(a, s);
+    else q2d_launch<kNV, false>(a, s);
+  } else {
+    if (a.counters) q2d_launch<kUE, true>(a, s);
+    else q2d_launch<kUE, false>(a, s);
+  }
+  return hipGetLastError();
+}
+
+template <int FMT, bool B2D>
+static void dq_launch(const uint8_t* codes, const uint8_t* scales, const float* s_dec,
+                      int64_t rows, int64_t cols, void* out, int out_fp32, hipStream_t s) {
+  constexpr int BS = FMT == kMX ? 32 : 16;
+  const uint64_t n = static_cast<uint64_t>(rows) * static_cast<uint64_t>(cols / BS);
+  const int grid = grid_for(n, 8);
+  if (out_fp32)
+    hipLaunchKernelGGL((k_dequant<FMT, B2D, true>), dim3(grid), dim3(kThreads), 0, s, codes,
+                       scales, s_dec, rows, cols, out);
+  else
+    hipLaunchKernelGGL((k_dequant<FMT, B2D, false>), dim3(grid), dim3(kThreads), 0, s, codes,
+                       scales, s_dec, rows, cols, out);
+}
+
+hipError_t launch_dequant(int format, int block2d, const uint8_t* codes, const uint8_t* scales,
+                          const float* s_dec, int64_t rows, int64_t cols, void* out, int out_fp32,
+                          hipStream_t s) {
+  if (rows > 0 && cols > 0) {
+    if (format == FP4_NVFP4) {
+      if (block2d) dq_launch<kNV, true>(codes, scales, s_dec, rows, cols, out, out_fp32, s);
+      else dq_launch<kNV, false>(codes, scales, s_dec, rows, cols, out, out_fp32, s);
+    } else if (format == FP4_UE5M3) {
+      if (block2d) dq_launch<kUE, true>(codes, scales, s_dec, rows, cols, out, out_fp32, s);
+      else dq_launch<kUE, false>(codes, scales, s_dec, rows, cols, out, out_fp32, s);
+    } else {
+      dq_launch<kMX, false>(codes, scales, s_dec, rows, cols, out, out_fp32, s);
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rht16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, uint32_t signs,
+                        float* y, hipStream_t s) {
+  if (rows > 0 && cols > 0) {
+    const uint64_t n = static_cast<uint64_t>(rows / 16) * static_cast<uint64_t>(cols / 2);
+    hipLaunchKernelGGL(k_rht16, dim3(grid_for(n, 8)), dim3(kThreads), 0, s, x, rows, cols, ld,
+                       signs, y);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fp4lib

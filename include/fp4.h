@@ -1,0 +1,217 @@
+/*
+ * fp4.h -- C ABI of libfp4_mi355x.so: FP4 (E2M1) block-scaled quantization
+ * and the block-scaled GEMMs that consume it, hand-written HIP for gfx950.
+ *
+ * Method: "Pretraining Large Language Models with NVFP4" (arXiv:2509.25149),
+ * App. B (two-level scaling, Eqs. 1-5), §4.2 and App. C (16-point random
+ * Hadamard transform on the Wgrad inputs), §4.3 (16x16 2D weight scales),
+ * §4.4 (stochastic rounding of gradients), §3 (MXFP4 and NVFP4 formats);
+ * the UE5M3 block-scale recipe (arXiv 2609.02846, abstract: unsigned E5M3
+ * scales, target T, periodic tensor amax); the 2D-block FP4 recipe
+ * (arXiv 2607.24953, abstract: transposition-invariant scales).
+ *
+ * Conventions shared by every entry point
+ *  - Device pointers are HIP device memory of the current device; host
+ *    pointers are marked "host".  The caller owns every buffer; the library
+ *    allocates nothing and keeps no state between calls.
+ *  - bf16 inputs are uint16 bit patterns, row-major with leading dimension
+ *    `ld` (elements): the pointer must be 16-byte aligned and ld a multiple
+ *    of 8.
+ *  - `stream` is a hipStream_t (NULL: the null stream).  Every call only
+ *    enqueues work on it; nothing synchronizes with the host, and device
+ *    results (amax, s_dec, counters) stay on the device.
+ *  - Arguments are validated on the host before any HIP call; a rejected
+ *    call returns a nonzero fp4_status, enqueues nothing, and
+ *    fp4_last_error() (thread-local) describes why.  A launch failure
+ *    returns FP4_ERR_DEVICE.
+ *  - Inputs must be finite; rows == 0 or cols == 0 is a valid empty call.
+ *  - Calls that write the same output buffers on one stream are ordered by
+ *    the stream; concurrent calls on different streams must not share
+ *    output buffers.
+ */
+#ifndef FP4_MI355X_H
+#define FP4_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element payload is always E2M1 (NVFP4 paper §3: values +-{0,.5,1,1.5,2,3,4,6}).
+ * The block-scale format and block length differ:
+ *   FP4_NVFP4  1x16 blocks, E4M3 scale (max 448), fp32 tensor scale  (§3, App. B)
+ *   FP4_UE5M3  1x16 blocks, unsigned E5M3 scale (bias 15, all codes finite,
+ *              max 122880), fp32 tensor scale with target T          (UE5M3 abstract)
+ *   FP4_MXFP4  1x32 blocks, UE8M0 power-of-two scale rounded up, no tensor
+ *              scale                                                  (§3, App. B.4) */
+typedef enum { FP4_NVFP4 = 0, FP4_UE5M3 = 1, FP4_MXFP4 = 2 } fp4_format;
+
+/* Element rounding: nearest-even, or stochastic (NVFP4 paper §4.4). */
+typedef enum { FP4_RNE = 0, FP4_SR = 1 } fp4_round;
+
+/* 1D blocks along the blocked axis, or 16x16 tiles (NVFP4 paper §4.3). */
+typedef enum { FP4_BLOCK_1D = 0, FP4_BLOCK_2D16 = 1 } fp4_block;
+
+/* ROWWISE: blocks run along cols of X; output is [rows, cols] codes.
+ * COLWISE: the matrix quantized is X^T; blocks run along rows of X and the
+ * output is the [cols, rows] code matrix of X^T (Wgrad operands, §4.1). */
+typedef enum { FP4_ROWWISE = 0, FP4_COLWISE = 1 } fp4_orient;
+
+typedef enum {
+  FP4_OK = 0,
+  FP4_ERR_ARG = 1,          /* null pointer, bad enum, misaligned or bad stride  */
+  FP4_ERR_SHAPE = 2,        /* negative size, blocked axis not a block multiple  */
+  FP4_ERR_UNSUPPORTED = 3,  /* valid values, combination not defined            */
+  FP4_ERR_DEVICE = 4        /* a HIP launch failed                               */
+} fp4_status;
+
+/* Quantization events (device memory, accumulated with atomics; the caller
+ * zeroes it).  Definitions (block B, y = x * local encode scale):
+ *   scale_saturated  the block scale before conversion exceeds the format max
+ *   scale_underflow  amax_B > 0 but the block-scale code is 0
+ *   scale_subnormal  the block-scale code is a nonzero subnormal
+ *   elem_saturated   |y| > 6
+ *   elem_underflow   x != 0 but its code is +-0
+ * MXFP4 scales are never saturated, underflowed or subnormal. */
+typedef struct {
+  uint64_t scale_saturated;
+  uint64_t scale_underflow;
+  uint64_t scale_subnormal;
+  uint64_t elem_saturated;
+  uint64_t elem_underflow;
+} fp4_counters;
+
+/* How to quantize (host struct). */
+typedef struct {
+  fp4_format format;
+  fp4_block block;        /* 2D16: NVFP4/UE5M3, ROWWISE, RNE only               */
+  fp4_orient orient;
+  fp4_round round;        /* SR: 1D only                                       */
+  uint64_t seed;          /* SR: Philox4x32-10 key                             */
+  uint64_t offset;        /* SR: Philox counter words 2-3 (e.g. a step number) */
+  int rht;                /* COLWISE only: rotate every 16-row group of each
+                             column by (1/4) D_r H16 first (App. C)            */
+  uint32_t rht_signs;     /* D_r: bit i set negates output row i of H16        */
+  float target;           /* T in s_enc = 6 T / amax: 448 for NVFP4; 448 or
+                             2048 for UE5M3; ignored for MXFP4; finite, > 0    */
+  int amax_given;         /* 0: compute the tensor amax into *amax first;
+                             1: read *amax (e.g. a stale, periodically
+                             refreshed amax); NVFP4/UE5M3 only                 */
+  int emit_transpose;     /* 2D16 only: also write the codes of X^T           */
+} fp4_quant_desc;
+
+/*
+ * fp4_amax -- tensor amax (NVFP4 paper App. B.1: amax_X = max |x_i|).
+ *   x [rows, cols] bf16 (ld), device.  If rht != 0 the amax is taken over
+ *   the column-rotated tensor ((1/4) D_r H16 on each 16-row group of each
+ *   column, App. C: the scale is computed in the rotated space); then rows
+ *   must be a multiple of 16.
+ *   amax: device float, overwritten (0 for an empty tensor).
+ */
+fp4_status fp4_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                    int rht, uint32_t rht_signs, float* amax, void* stream);
+
+/*
+ * fp4_quantize -- quantize a bf16 matrix to E2M1 codes with block scales
+ * (NVFP4 paper App. B.1-B.4, Eqs. 1-4; §4.3 2D; §4.4 SR; App. C RHT).
+ *
+ *   x       [rows, cols] bf16 (ld), device.
+ *   codes   device, packed two codes per byte, element 2j in the low nibble
+ *           of byte j.  ROWWISE: [rows, cols/2] bytes; COLWISE: [cols, rows/2].
+ *   scales  device, one byte per block.  1D ROWWISE: [rows, cols/BS];
+ *           1D COLWISE: [cols, rows/BS]; 2D16: [rows/16, cols/16]
+ *           (BS = 16, or 32 for MXFP4).
+ *   codes_t device, 2D16 with emit_transpose only: [cols, rows/2] codes of
+ *           X^T quantized with the same tile scales (NULL otherwise).
+ *   amax    device float.  NVFP4/UE5M3: written (amax_given = 0) or read
+ *           (amax_given = 1).  MXFP4: unused, may be NULL.
+ *   s_dec   device float or NULL: receives s_dec_G = 1 / s_enc_G (1 for
+ *           MXFP4), the global decode scale the GEMM applies (App. B.3).
+ *   counters device fp4_counters or NULL (events not counted).
+ *   Shapes: the blocked axis (cols for ROWWISE, rows for COLWISE) must be a
+ *   multiple of BS; 2D16 needs rows and cols multiples of 16; RHT needs
+ *   COLWISE (rows % 16 == 0 follows).
+ *   SR random bits: element index i in the output code matrix ([R_out,
+ *   C_out], i = r * C_out + c) takes 16 bits of Philox4x32-10(key = seed,
+ *   counter = (i >> 3, offset)), half (i & 1) of output word (i & 7) >> 1.
+ */
+fp4_status fp4_quantize(const fp4_quant_desc* desc /* host */,
+                        const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                        uint8_t* codes, uint8_t* scales, uint8_t* codes_t,
+                        float* amax, float* s_dec, fp4_counters* counters,
+                        void* stream);
+
+/*
+ * fp4_dequantize -- decode codes and scales: v = fp32(fp32(e2m1 * scale) *
+ * s_dec_G) (NVFP4 paper App. B.2-B.3: the decode scales undo the encode
+ * scales).  The codes/scales layouts are those fp4_quantize writes for a
+ * ROWWISE (or 2D16) [rows, cols] code matrix.
+ *   s_dec   device float (NVFP4/UE5M3); ignored (may be NULL) for MXFP4.
+ *   out     device, [rows, cols] row-major: fp32 if out_fp32, else bf16
+ *           (v rounded to nearest even).
+ */
+fp4_status fp4_dequantize(fp4_format format, fp4_block block,
+                          const uint8_t* codes, const uint8_t* scales, const float* s_dec,
+                          int64_t rows, int64_t cols, void* out, int out_fp32, void* stream);
+
+/*
+ * fp4_rht16 -- the 16-point random Hadamard transform alone (NVFP4 paper
+ * §4.2, App. C): y = (1/4) D_r H16 v for v = each 16-row group of each
+ * column of x.  fp32 arithmetic as a Walsh-Hadamard butterfly network with
+ * strides 1, 2, 4, 8 (each butterfly (a, b) -> (a + b, a - b)), then the
+ * exact 1/4, then the sign flips; these are the values fp4_quantize with
+ * rht = 1 quantizes.
+ *   x [rows, cols] bf16 (ld), device; rows % 16 == 0.
+ *   y [rows, cols] fp32 row-major (leading dimension cols), device.
+ */
+fp4_status fp4_rht16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                     uint32_t rht_signs, float* y, void* stream);
+
+/* One GEMM operand: a [rows, K] code matrix, K-major (host struct of device
+ * pointers).  The scale of (row r, K-block j) is
+ *   scales[(r / scale_row_group) * scale_stride_row + j * scale_stride_kblk]
+ * so 1D scales are (row_group 1, stride_row K/BS, stride_kblk 1); 2D16
+ * scales of W are (16, K/16, 1); the 2D16 scales of W used for the codes_t
+ * matrix W^T are (16, 1, rows_of_W/16) -- the same bytes (§4.3: the tile
+ * scale is replicated per 1x16 block). */
+typedef struct {
+  fp4_format format;
+  const uint8_t* codes;       /* device; ld_codes bytes per row, ld_codes >= K/2 */
+  int64_t ld_codes;
+  const uint8_t* scales;      /* device */
+  int64_t scale_stride_row;
+  int64_t scale_stride_kblk;
+  int32_t scale_row_group;    /* 1 or 16 */
+  const float* s_dec;         /* device s_dec_G; NULL means 1 (MXFP4 ignores it) */
+} fp4_operand;
+
+/*
+ * fp4_gemm -- D[M, N] (+)= s_dec_A * s_dec_B * sum_k a[m, k] * b[n, k],
+ * a = e2m1 * scale of A [M, K], b likewise of B [N, K] ("TN": both K-major).
+ * This is the block-scaled product of NVFP4 paper App. B.3 (per-block
+ * partial products scaled by both local decode scales, fp32 accumulation,
+ * global decode scales applied to the output) used for Fprop, Dgrad and
+ * Wgrad (§4.1, Fig. 5).  A and B must have the same format; K must be a
+ * multiple of the format's block length.
+ *   D  device fp32, row-major with leading dimension ldd >= N.
+ *   accumulate  0: D = result; 1: D += result (e.g. Wgrad accumulation).
+ * Accuracy: |D - exact| <= 1e-5 * s_dec_A * s_dec_B * sum_k |a b| per element.
+ * K == 0 writes zeros (or leaves D unchanged when accumulating).
+ */
+fp4_status fp4_gemm(const fp4_operand* A /* host */, const fp4_operand* B /* host */,
+                    int64_t M, int64_t N, int64_t K, float* D, int64_t ldd,
+                    int accumulate, void* stream);
+
+/* Static description of a status code. */
+const char* fp4_status_string(fp4_status status);
+
+/* Thread-local detail of the last rejected or failed call on this thread
+ * ("" if none). */
+const char* fp4_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4_MI355X_H */

@@ -202,7 +202,7 @@ def unpack_codes(packed):
 # ------------------------------------------------------ full quantize ----
 def quantize(x_bits, fmt="nvfp4", block="1d", orient="row", rnd="rne",
              seed=0, offset=0, rht=False, signs=0, target=448.0,
-             amax=None, emit_transpose=False):
+             amax=None, emit_transpose=False, index_base=0):
     """Quantize a bf16 matrix (uint16 bit patterns, [R, C]).
 
     orient="row": blocks run along C; output codes [R, C/2], scales
@@ -213,6 +213,8 @@ def quantize(x_bits, fmt="nvfp4", block="1d", orient="row", rnd="rne",
     (rowwise only, RNE only); scales [R/16, C/16]; emit_transpose also
     returns the codes of X^T ([C, R/2]) quantized with the same tile scales.
     amax: None to compute it, or a given (possibly stale) fp32 amax.
+    index_base: output-layout index of element (0, 0), so that a slab of
+    output rows of a larger matrix draws the same random bits (SR only).
 
     Returns a dict: codes, scales, codes_t (2D only), amax, s_dec, counters.
     """
@@ -263,7 +265,7 @@ def quantize(x_bits, fmt="nvfp4", block="1d", orient="row", rnd="rne",
 
     r16 = None
     if rnd == "sr":
-        idx = (np.arange(Ro, dtype=np.int64)[:, None] * Co
+        idx = (int(index_base) + np.arange(Ro, dtype=np.int64)[:, None] * Co
                + np.arange(Co, dtype=np.int64)[None, :])
         r16 = sr_random16(idx, seed, offset)
     codes, esat, eund = encode_elements(v, s_el, rnd, r16)

@@ -1,0 +1,145 @@
+"""The C-ABI library: it loads, exports every function include/*.h declares,
+and rejects invalid arguments on the host (no GPU is touched: these calls
+return before any HIP API call)."""
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+from fp4_block_scaled_x16_amd import api
+from conftest import ROOT
+
+HEADERS = glob.glob(os.path.join(ROOT, "include", "*.h"))
+DECL = re.compile(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(fp4_[a-z0-9_]+)\s*\(", re.M)
+
+
+def declared():
+    names = set()
+    for h in HEADERS:
+        names |= set(DECL.findall(open(h).read()))
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(api.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return api.load_library()
+
+
+def test_header_declares_the_boundary():
+    assert {"fp4_amax", "fp4_quantize", "fp4_dequantize", "fp4_rht16", "fp4_gemm",
+            "fp4_status_string", "fp4_last_error"} <= declared()
+
+
+def test_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for name in declared():
+        assert name in exported, name
+        assert hasattr(lib, name)
+    # nothing but the declared API is exported
+    assert {e for e in exported if e.startswith("fp4")} == declared()
+
+
+def _err(lib):
+    return lib.fp4_last_error().decode()
+
+
+def desc(**kw):
+    d = dict(format=0, block=0, orient=0, round=0, seed=0, offset=0, rht=0, rht_signs=0,
+             target=448.0, amax_given=0, emit_transpose=0)
+    d.update(kw)
+    return api.QuantDesc(**d)
+
+
+FAKE = ctypes.c_void_p(0x10000)          # 16-byte aligned, never dereferenced
+
+
+def quant(lib, d, rows=32, cols=64, ld=None, x=FAKE, codes=FAKE, scales=FAKE, codes_t=None,
+          amax=FAKE):
+    return lib.fp4_quantize(ctypes.byref(d), x, rows, cols, cols if ld is None else ld, codes,
+                            scales, codes_t, amax, None, None, None)
+
+
+@pytest.mark.parametrize("kw,rows,cols,status", [
+    (dict(format=7), 32, 64, 1),
+    (dict(block=3), 32, 64, 1),
+    (dict(round=2), 32, 64, 1),
+    (dict(format=2, block=1), 32, 64, 3),            # 2D needs NVFP4/UE5M3
+    (dict(block=1, orient=1), 32, 64, 3),            # 2D is rowwise only
+    (dict(block=1, round=1), 32, 64, 3),             # 2D is RNE only
+    (dict(rht=1), 32, 64, 3),                        # RHT needs colwise
+    (dict(rht=1, orient=1, format=2), 32, 64, 3),    # RHT needs two-level formats
+    (dict(format=2, amax_given=1), 32, 64, 3),       # MXFP4 has no tensor amax
+    (dict(emit_transpose=1), 32, 64, 3),             # emit_transpose needs 2D
+    (dict(target=0.0), 32, 64, 1),
+    (dict(target=float("inf")), 32, 64, 1),
+    (dict(), 32, 40, 2),                             # cols % 16
+    (dict(format=2), 32, 48, 2),                     # cols % 32
+    (dict(orient=1), 24, 64, 2),                     # rows % 16 (colwise)
+    (dict(block=1), 40, 64, 2),                      # 2D rows % 16
+    (dict(), -1, 64, 2),
+])
+def test_quantize_rejects(lib, kw, rows, cols, status):
+    assert quant(lib, desc(**kw), rows, cols) == status
+    assert _err(lib)
+
+
+def test_quantize_rejects_pointers(lib):
+    assert quant(lib, desc(), x=None) == 1
+    assert quant(lib, desc(), x=ctypes.c_void_p(0x10008)) == 1      # misaligned
+    assert quant(lib, desc(), ld=60) == 1                           # ld < cols
+    assert quant(lib, desc(), ld=68) == 1                           # ld % 8
+    assert quant(lib, desc(), codes=None) == 1
+    assert quant(lib, desc(), amax=None) == 1
+    assert quant(lib, desc(block=1, emit_transpose=1)) == 1         # codes_t null
+    assert lib.fp4_quantize(None, FAKE, 32, 64, 64, FAKE, FAKE, None, FAKE, None, None, None) == 1
+
+
+def test_other_entry_points_reject(lib):
+    assert lib.fp4_amax(FAKE, 32, 64, 64, 1, 0, None, None) == 1
+    assert lib.fp4_amax(FAKE, 24, 64, 64, 1, 0, FAKE, None) == 2
+    assert lib.fp4_amax(FAKE, 32, 64, 64, 1, 1 << 16, FAKE, None) == 1
+    assert lib.fp4_dequantize(0, 0, FAKE, FAKE, FAKE, 32, 40, FAKE, 1, None) == 2
+    assert lib.fp4_dequantize(2, 1, FAKE, FAKE, FAKE, 32, 64, FAKE, 1, None) == 3
+    assert lib.fp4_dequantize(0, 0, FAKE, FAKE, None, 32, 64, FAKE, 1, None) == 1
+    assert lib.fp4_rht16(FAKE, 40, 64, 64, 0, FAKE, None) == 2
+    assert lib.fp4_rht16(FAKE, 32, 64, 64, 0, None, None) == 1
+
+
+def op(fmt=0, codes=0x10000, ld=32, rg=1):
+    return api.Operand(fmt, codes, ld, 0x20000, 4, 1, rg, 0x30000)
+
+
+@pytest.mark.parametrize("a,b,M,N,K,status", [
+    (op(0), op(2), 16, 16, 64, 3),          # formats differ
+    (op(0), op(0), 16, 16, 40, 2),          # K % 16
+    (op(2), op(2), 16, 16, 48, 2),          # K % 32
+    (op(0), op(0), -1, 16, 64, 2),
+    (op(0, rg=3), op(0), 16, 16, 64, 1),
+    (op(2, rg=16), op(2), 16, 16, 64, 3),   # 2D scales with MXFP4
+    (op(0, ld=16), op(0), 16, 16, 64, 1),   # ld_codes < K/2
+    (op(0, codes=0x10004), op(0), 16, 16, 64, 1),
+    (op(0, codes=0), op(0), 16, 16, 64, 1),
+])
+def test_gemm_rejects(lib, a, b, M, N, K, status):
+    assert lib.fp4_gemm(ctypes.byref(a), ctypes.byref(b), M, N, K, FAKE, N, 0, None) == status
+    assert _err(lib)
+
+
+def test_empty_calls_are_noops(lib):
+    # nothing to do: accepted without any device work
+    a, b = op(0), op(0)
+    assert lib.fp4_gemm(ctypes.byref(a), ctypes.byref(b), 0, 16, 64, None, 16, 0, None) == 0
+    assert lib.fp4_dequantize(0, 0, None, None, None, 0, 64, None, 1, None) == 0
+
+
+def test_status_strings(lib):
+    assert lib.fp4_status_string(0) == b"ok"
+    assert lib.fp4_status_string(3) == b"unsupported combination"
