@@ -215,9 +215,10 @@ FP4_EXPORT fp4_status fp4_gemm(const fp4_operand* A, const fp4_operand* B, int64
     if (M > 0 && N > 0 && K > 0) {
       if (!o->codes || !o->scales) return fail(FP4_ERR_ARG, "operand %c has a null pointer", "AB"[i]);
       if (o->ld_codes < K / 2) return fail(FP4_ERR_ARG, "operand %c ld_codes < K/2", "AB"[i]);
-      if (!aligned16(o->codes) || o->ld_codes % 16)
-        return fail(FP4_ERR_ARG, "operand %c codes must be 16-byte aligned with ld_codes %% 16 == 0",
-                    "AB"[i]);
+      const int ld_align = A->format == FP4_MXFP4 ? 16 : 8;
+      if (!aligned16(o->codes) || o->ld_codes % ld_align)
+        return fail(FP4_ERR_ARG, "operand %c codes must be 16-byte aligned with ld_codes %% %d == 0",
+                    "AB"[i], ld_align);
       if (o->scale_stride_row < 0 || o->scale_stride_kblk < 0)
         return fail(FP4_ERR_ARG, "negative scale stride");
     }

@@ -1,13 +1,461 @@
-// Block-scaled GEMM kernels (see launch_gemm).
+// Block-scaled FP4 GEMMs for gfx950 (NVFP4 pretraining paper, App. B.3:
+// per-block partial products scaled by both local decode scales, fp32
+// accumulation, the two global decode scales applied to the output; §4.1 /
+// Fig. 5: Fprop, Dgrad and Wgrad all run this product on FP4 operands).
+//
+//   D[M, N] (+)= s_A s_B sum_k a[m, k] b[n, k],   a = e2m1 * scale ("TN")
+//
+// Two kernels share one skeleton: a 256 x 256 output tile per workgroup,
+// four waves in a 2 x 2 arrangement (128 x 128 each, 4 x 4 MFMA tiles of
+// 32 x 32), FP4 codes and scales staged through double-buffered LDS with one
+// barrier per K step, the next K step's global loads in flight while the
+// current one is multiplied.
+//
+// * NVFP4 / UE5M3 (k_gemm_two_level): e2m1 * scale is exact in fp16 (E4M3
+//   products lie in [2^-10, 2688]; UE5M3 scales are pre-multiplied by 2^-5
+//   so products lie in [2^-23, 23040] on fp16's 2^-24 grid), so every lane
+//   dequantizes its own MFMA fragment in registers -- a hardware FP4->fp16
+//   convert and a packed fp16 multiply by the block scale -- and feeds
+//   v_mfma_f32_32x32x16_f16 with fp32 accumulation.  The 2^-5 shifts and
+//   the tensor scales are applied to the fp32 result.
+// * MXFP4 (k_gemm_mx): gfx950's scaled MFMA takes FP4 operands and one E8M0
+//   scale per 32 K-values per lane, which is exactly an MXFP4 block, so the
+//   codes go from LDS to v_mfma_scale_f32_32x32x64_f8f6f4 untouched.
+//
+// The order of K inside one K step is free as long as A and B agree: lane
+// half h of a wave owns a contiguous half of the step's K range for both
+// operands, so each lane's codes are one contiguous run in LDS.
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 
+#include "fp4_device.hpp"
 #include "fp4_internal.hpp"
+
+using namespace fp4dev;
+
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef int int8v __attribute__((ext_vector_type(8)));
+
+constexpr int kBM = 256, kBN = 256, kThreads = 256;
+
+struct Params {
+  const uint8_t* codes[2];
+  int64_t ld[2];
+  const uint8_t* scales[2];
+  int64_t s_row[2], s_kblk[2];
+  int rg_shift[2];      // log2 of the scale row group (0 or 4)
+  const float* s_dec[2];
+  float* D;
+  int64_t ldd;
+  int64_t M, N, K;
+  int accumulate;
+  int tiles_m, tiles_n;
+  int vec16[2];         // code rows are 16-byte aligned
+};
+
+// Tile order: consecutive workgroup ids go round-robin over the 8 XCDs, so
+// first give each XCD a contiguous range of tiles, then walk that range in
+// groups of 8 tile-rows so neighbouring tiles share A rows and B columns in
+// the XCD's L2.
+__device__ __forceinline__ void tile_coords(const Params& p, int& tm, int& tn) {
+  const int T = p.tiles_m * p.tiles_n;
+  int id = blockIdx.x;
+  if ((T & 7) == 0) id = (id & 7) * (T >> 3) + (id >> 3);
+  constexpr int G = 8;
+  const int per_group = G * p.tiles_n;
+  const int g = id / per_group;
+  const int first = g * G;
+  const int gm = min(p.tiles_m - first, G);
+  const int r = id - g * per_group;
+  tm = first + r % gm;
+  tn = r / gm;
+}
+
+// 16 bytes of codes at byte offset `off` of a row of `row_bytes` valid
+// bytes; K is a multiple of 16 so a chunk is full, half (8 bytes) or empty.
+// Rows whose stride is only 8-byte aligned are read as two 8-byte halves.
+__device__ __forceinline__ uint4 load_codes16(const uint8_t* row, int64_t off, int64_t row_bytes,
+                                              bool vec16) {
+  const int64_t left = row_bytes - off;
+  if (vec16 && left >= 16) return *reinterpret_cast<const uint4*>(row + off);
+  uint2 lo = make_uint2(0u, 0u), hi = make_uint2(0u, 0u);
+  if (left >= 8) lo = *reinterpret_cast<const uint2*>(row + off);
+  if (left >= 16) hi = *reinterpret_cast<const uint2*>(row + off + 8);
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
+__device__ __forceinline__ void epilogue(const Params& p, floatx16 (&acc)[4][4], float scale,
+                                         int64_t m0, int64_t n0, int wm, int wn, int lane) {
+  const int i = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      const int64_t col = n0 + wn * 128 + ni * 32 + i;
+      if (col >= p.N) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t row = m0 + wm * 128 + mi * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (row < p.M) {
+          float* dst = p.D + row * p.ldd + col;
+          const float r = acc[mi][ni][v] * scale;
+          *dst = p.accumulate ? *dst + r : r;
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------- NVFP4 / UE5M3 --
+constexpr int kBK2 = 128;   // K per step: 64 code bytes and 8 scales per row
+
+// fp16 copy of a block scale, replicated in both halves for v_pk_mul_f16.
+template <int FMT>
+__device__ __forceinline__ uint32_t scale_half2(uint32_t code) {
+  float s;
+  if constexpr (FMT == kNV) s = scale_m3_decode<7>(code);
+  else s = scale_m3_decode<15>(code) * 0x1p-5f;      // exact: keeps products in fp16 range
+  const _Float16 hs = static_cast<_Float16>(s);        // exact
+  const uint32_t b = __builtin_bit_cast(uint16_t, hs);
+  return b | (b << 16);
+}
+
+__device__ __forceinline__ half8 dequant8(uint32_t codes, uint32_t sc2) {
+  const half2v s = __builtin_bit_cast(half2v, sc2);
+  half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0);
+  half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1);
+  half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2);
+  half2v p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3);
+  p0 *= s;
+  p1 *= s;
+  p2 *= s;
+  p3 *= s;
+  return half8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+struct Stage2 {
+  // codes: [operand][chunk q 0..3][row slot][16 B], slot = row ^ (q << 2)
+  uint4 codes[2][4][256];
+  // scales: [operand][half h][row][4 x half2] for the 8 blocks of the step
+  uint4 scales[2][2][256];
+};
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level(Params p) {
+  extern __shared__ uint4 smem_raw[];
+  Stage2* st = reinterpret_cast<Stage2*>(smem_raw);
+  int tm, tn;
+  tile_coords(p, tm, tn);
+  const int64_t m0 = static_cast<int64_t>(tm) * kBM, n0 = static_cast<int64_t>(tn) * kBN;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t row_bytes = p.K >> 1;
+  const int64_t kblocks = p.K >> 4;
+  const int nsteps = static_cast<int>((p.K + kBK2 - 1) / kBK2);
+  const int64_t lim[2] = {p.M, p.N};
+  const int64_t base[2] = {m0, n0};
+
+  uint4 rc[2][4];        // staged codes: 4 chunks per operand per thread
+  uint32_t rs[2][8];     // staged scales (fp16 pairs): 8 per operand per thread
+
+  auto load_step = [&](int s) {
+    const int64_t k0b = static_cast<int64_t>(s) * (kBK2 / 2);
+#pragma unroll
+    for (int o = 0; o < 2; ++o) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = t + kThreads * j;
+        const int row = c >> 2, q = c & 3;
+        const int64_t gr = base[o] + row;
+        rc[o][j] = gr < lim[o] ? load_codes16(p.codes[o] + gr * p.ld[o], k0b + q * 16, row_bytes,
+                                              p.vec16[o])
+                               : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int c = t + kThreads * j;
+        const int row = c >> 3, kb = c & 7;
+        const int64_t gr = base[o] + row, gk = static_cast<int64_t>(s) * 8 + kb;
+        uint32_t code = 0;
+        if (gr < lim[o] && gk < kblocks)
+          code = p.scales[o][(gr >> p.rg_shift[o]) * p.s_row[o] + gk * p.s_kblk[o]];
+        rs[o][j] = scale_half2<FMT>(code);
+      }
+    }
+  };
+  auto store_step = [&](Stage2& S) {
+#pragma unroll
+    for (int o = 0; o < 2; ++o) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = t + kThreads * j;
+        const int row = c >> 2, q = c & 3;
+        S.codes[o][q][row ^ (q << 2)] = rc[o][j];
+      }
+      uint32_t* sc = reinterpret_cast<uint32_t*>(&S.scales[o][0][0]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int c = t + kThreads * j;
+        const int row = c >> 3, kb = c & 7;
+        sc[((kb >> 2) * 256 + row) * 4 + (kb & 3)] = rs[o][j];
+      }
+    }
+  };
+
+  floatx16 acc[4][4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = floatx16{};
+
+  const int i = lane & 31, h = lane >> 5;
+  if (nsteps > 0) {
+    load_step(0);
+    store_step(st[0]);
+    __syncthreads();
+  }
+  for (int s = 0; s < nsteps; ++s) {
+    const bool more = s + 1 < nsteps;
+    if (more) load_step(s + 1);
+    const Stage2& S = st[s & 1];
+    uint32_t a_raw[4][8], b_raw[4][8];
+    uint4 a_sc[4], b_sc[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      const int row = wm * 128 + mi * 32 + i;
+      const uint4 c0 = S.codes[0][2 * h][row ^ ((2 * h) << 2)];
+      const uint4 c1 = S.codes[0][2 * h + 1][row ^ ((2 * h + 1) << 2)];
+      a_raw[mi][0] = c0.x; a_raw[mi][1] = c0.y; a_raw[mi][2] = c0.z; a_raw[mi][3] = c0.w;
+      a_raw[mi][4] = c1.x; a_raw[mi][5] = c1.y; a_raw[mi][6] = c1.z; a_raw[mi][7] = c1.w;
+      a_sc[mi] = S.scales[0][h][row];
+    }
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      const int row = wn * 128 + ni * 32 + i;
+      const uint4 c0 = S.codes[1][2 * h][row ^ ((2 * h) << 2)];
+      const uint4 c1 = S.codes[1][2 * h + 1][row ^ ((2 * h + 1) << 2)];
+      b_raw[ni][0] = c0.x; b_raw[ni][1] = c0.y; b_raw[ni][2] = c0.z; b_raw[ni][3] = c0.w;
+      b_raw[ni][4] = c1.x; b_raw[ni][5] = c1.y; b_raw[ni][6] = c1.z; b_raw[ni][7] = c1.w;
+      b_sc[ni] = S.scales[1][h][row];
+    }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {     // 16 K-values per MFMA, one scale per 2 slices
+      half8 a_op[4], b_op[4];
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) {
+        const uint32_t sc = (ks >> 1) == 0 ? a_sc[mi].x : (ks >> 1) == 1 ? a_sc[mi].y
+                          : (ks >> 1) == 2 ? a_sc[mi].z : a_sc[mi].w;
+        a_op[mi] = dequant8(a_raw[mi][ks], sc);
+      }
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+        const uint32_t sc = (ks >> 1) == 0 ? b_sc[ni].x : (ks >> 1) == 1 ? b_sc[ni].y
+                          : (ks >> 1) == 2 ? b_sc[ni].z : b_sc[ni].w;
+        b_op[ni] = dequant8(b_raw[ni][ks], sc);
+      }
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_op[mi], b_op[ni], acc[mi][ni],
+                                                               0, 0, 0);
+    }
+    if (more) store_step(st[(s + 1) & 1]);
+    __syncthreads();
+  }
+
+  float scale = FMT == kUE ? 1024.0f : 1.0f;   // undo the two 2^-5 scale shifts
+  if (p.s_dec[0]) scale *= *p.s_dec[0];
+  // s_B is applied as a second multiply so that s_A * s_B never under/overflows alone
+  const float sb = p.s_dec[1] ? *p.s_dec[1] : 1.0f;
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] *= scale;
+  epilogue(p, acc, sb, m0, n0, wm, wn, lane);
+}
+
+// -------------------------------------------------------------- MXFP4 ---
+constexpr int kBKX = 128;   // K per step: 64 code bytes and 4 E8M0 scales per row
+
+struct StageX {
+  // codes: [operand][chunk q 0..3][row slot][16 B], slot = row ^ (q << 2)
+  uint4 codes[2][4][256];
+  // scales: [operand][row] -> the 4 E8M0 bytes of the step's blocks
+  uint32_t scales[2][256];
+};
+
+// One 64-K slice: lane half h owns the 32 K-values of chunk 2h + KS (one
+// MXFP4 block); its E8M0 scale is byte KS of the lane's (pre-shifted) word.
+template <int KS>
+__device__ __forceinline__ void mx_slice(const StageX& S, floatx16 (&acc)[4][4],
+                                         const uint32_t (&a_sc)[4], const uint32_t (&b_sc)[4],
+                                         int wm, int wn, int i, int h) {
+  const int q = 2 * h + KS;
+  int8v a_op[4], b_op[4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+    const int row = wm * 128 + mi * 32 + i;
+    const uint4 c = S.codes[0][q][row ^ (q << 2)];
+    a_op[mi] = int8v{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) {
+    const int row = wn * 128 + ni * 32 + i;
+    const uint4 c = S.codes[1][q][row ^ (q << 2)];
+    b_op[ni] = int8v{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+      acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          a_op[mi], b_op[ni], acc[mi][ni], 4, 4, KS, static_cast<int>(a_sc[mi]), KS,
+          static_cast<int>(b_sc[ni]));
+}
+
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(Params p) {
+  extern __shared__ uint4 smem_raw[];
+  StageX* st = reinterpret_cast<StageX*>(smem_raw);
+  int tm, tn;
+  tile_coords(p, tm, tn);
+  const int64_t m0 = static_cast<int64_t>(tm) * kBM, n0 = static_cast<int64_t>(tn) * kBN;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t kblocks = p.K >> 5;
+  const int nsteps = static_cast<int>((p.K + kBKX - 1) / kBKX);
+  const int64_t lim[2] = {p.M, p.N};
+  const int64_t base[2] = {m0, n0};
+
+  uint4 rc[2][4];        // staged codes: 4 chunks (one MXFP4 block each) per operand
+  uint32_t rs[2][4];     // their E8M0 scales
+
+  auto load_step = [&](int s) {
+    const int64_t k0b = static_cast<int64_t>(s) * (kBKX / 2);
+#pragma unroll
+    for (int o = 0; o < 2; ++o) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = t + kThreads * j;
+        const int row = c >> 2, q = c & 3;
+        const int64_t gr = base[o] + row, gk = static_cast<int64_t>(s) * 4 + q;
+        const bool ok = gr < lim[o] && gk < kblocks;   // K % 32 == 0: a chunk is all or nothing
+        rc[o][j] = ok ? *reinterpret_cast<const uint4*>(p.codes[o] + gr * p.ld[o] + k0b + q * 16)
+                      : make_uint4(0u, 0u, 0u, 0u);
+        rs[o][j] = ok ? p.scales[o][gr * p.s_row[o] + gk * p.s_kblk[o]] : 0u;
+      }
+    }
+  };
+  auto store_step = [&](StageX& S) {
+#pragma unroll
+    for (int o = 0; o < 2; ++o) {
+      uint8_t* sc = reinterpret_cast<uint8_t*>(&S.scales[o][0]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = t + kThreads * j;
+        const int row = c >> 2, q = c & 3;
+        S.codes[o][q][row ^ (q << 2)] = rc[o][j];
+        sc[row * 4 + q] = static_cast<uint8_t>(rs[o][j]);
+      }
+    }
+  };
+
+  floatx16 acc[4][4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = floatx16{};
+
+  const int i = lane & 31, h = lane >> 5;
+  if (nsteps > 0) {
+    load_step(0);
+    store_step(st[0]);
+    __syncthreads();
+  }
+  for (int s = 0; s < nsteps; ++s) {
+    const bool more = s + 1 < nsteps;
+    if (more) load_step(s + 1);
+    const StageX& S = st[s & 1];
+    // lane half h uses blocks 2h and 2h+1: shift them down to bytes 0 and 1
+    uint32_t a_sc[4], b_sc[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) a_sc[mi] = S.scales[0][wm * 128 + mi * 32 + i] >> (16 * h);
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) b_sc[ni] = S.scales[1][wn * 128 + ni * 32 + i] >> (16 * h);
+    mx_slice<0>(S, acc, a_sc, b_sc, wm, wn, i, h);
+    mx_slice<1>(S, acc, a_sc, b_sc, wm, wn, i, h);
+    if (more) store_step(st[(s + 1) & 1]);
+    __syncthreads();
+  }
+  epilogue(p, acc, 1.0f, m0, n0, wm, wn, lane);
+}
+
+}  // namespace
 
 namespace fp4lib {
 
-hipError_t launch_gemm(int, const GemmOperand&, const GemmOperand&, int64_t, int64_t, int64_t,
-                       float*, int64_t, int, hipStream_t) {
-  return hipErrorNotSupported;
+hipError_t launch_gemm(int format, const GemmOperand& A, const GemmOperand& B, int64_t M,
+                       int64_t N, int64_t K, float* D, int64_t ldd, int accumulate,
+                       hipStream_t s) {
+  Params p{};
+  const GemmOperand* ops[2] = {&A, &B};
+  for (int o = 0; o < 2; ++o) {
+    p.codes[o] = ops[o]->codes;
+    p.ld[o] = ops[o]->ld_codes;
+    p.scales[o] = ops[o]->scales;
+    p.s_row[o] = ops[o]->s_row;
+    p.s_kblk[o] = ops[o]->s_kblk;
+    p.rg_shift[o] = ops[o]->row_group == 16 ? 4 : 0;
+    p.vec16[o] = (ops[o]->ld_codes % 16 == 0) &&
+                 (reinterpret_cast<uintptr_t>(ops[o]->codes) % 16 == 0);
+    p.s_dec[o] = format == FP4_MXFP4 ? nullptr : ops[o]->s_dec;
+  }
+  p.D = D;
+  p.ldd = ldd;
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.accumulate = accumulate;
+  p.tiles_m = static_cast<int>((M + kBM - 1) / kBM);
+  p.tiles_n = static_cast<int>((N + kBN - 1) / kBN);
+  const int grid = p.tiles_m * p.tiles_n;
+  if (grid == 0) return hipSuccess;
+  // LDS beyond the default 64 KiB must be opted into once per kernel
+  static bool lds_set[3] = {false, false, false};
+  hipError_t e = hipSuccess;
+  if (format == FP4_MXFP4) {
+    const size_t lds = 2 * sizeof(StageX);
+    if (!lds_set[2]) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_mx),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+      lds_set[2] = e == hipSuccess;
+    }
+    if (e == hipSuccess) hipLaunchKernelGGL(k_gemm_mx, dim3(grid), dim3(kThreads), lds, s, p);
+  } else if (format == FP4_NVFP4) {
+    const size_t lds = 2 * sizeof(Stage2);
+    if (!lds_set[0]) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_two_level<kNV>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+      lds_set[0] = e == hipSuccess;
+    }
+    if (e == hipSuccess)
+      hipLaunchKernelGGL(k_gemm_two_level<kNV>, dim3(grid), dim3(kThreads), lds, s, p);
+  } else {
+    const size_t lds = 2 * sizeof(Stage2);
+    if (!lds_set[1]) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_two_level<kUE>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+      lds_set[1] = e == hipSuccess;
+    }
+    if (e == hipSuccess)
+      hipLaunchKernelGGL(k_gemm_two_level<kUE>, dim3(grid), dim3(kThreads), lds, s, p);
+  }
+  if (e != hipSuccess) return e;
+  return hipGetLastError();
 }
 
 }  // namespace fp4lib

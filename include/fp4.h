@@ -177,7 +177,8 @@ fp4_status fp4_rht16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
  * scale is replicated per 1x16 block). */
 typedef struct {
   fp4_format format;
-  const uint8_t* codes;       /* device; ld_codes bytes per row, ld_codes >= K/2 */
+  const uint8_t* codes;       /* device, 16-byte aligned; ld_codes bytes per row,
+                                 ld_codes >= K/2 and a multiple of 8 (16 for MXFP4) */
   int64_t ld_codes;
   const uint8_t* scales;      /* device */
   int64_t scale_stride_row;

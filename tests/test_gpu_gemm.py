@@ -1,0 +1,286 @@
+"""GPU parity of fp4_gemm against the CPU oracle.
+
+Bar: |D_gpu - D_ref| <= 1e-5 * s_A * s_B * sum_k |a b| per element, where
+D_ref is the oracle's fp64 GEMM of the oracle's own quantized operands.
+Small cases cover several 256 x 256 output tiles, ragged M and N, K steps
+with partial tails, every operand layout (1D, 2D weights, transposed 2D
+weights), accumulation and K = 0.  Full-size cases run each workload's
+Fprop / Dgrad / Wgrad at its real shape and check a grid of sampled entries,
+for which the oracle quantizes only the rows the entries need.
+"""
+import numpy as np
+import pytest
+import torch
+
+from fp4_block_scaled_x16_amd import api, inputs
+from oracle import formats as F
+from oracle import gemm as G
+from oracle import quantize as Q
+from oracle.philox import rht_signs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL = 1e-5
+SIGNS = rht_signs(7)
+
+
+def dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV)
+
+
+def check(d_gpu, ref, bound):
+    d = d_gpu.astype(np.float64)
+    err = np.abs(d - ref.astype(np.float64))
+    bad = err > TOL * bound
+    assert not bad.any(), "max err/bound %.3g at %s" % (
+        float((err / np.maximum(bound, 1e-300)).max()), np.argwhere(bad)[:5].tolist())
+
+
+def oracle_operand(bits, fmt, layout, **kw):
+    """Oracle values (float64, no tensor scale) of a GEMM operand and its s_dec.
+
+    layout: "row" (1D, K along cols), "col" (1D of X^T), "2d" (W), "2dT" (W^T).
+    """
+    if layout in ("row", "col"):
+        q = Q.quantize(bits, fmt, orient=layout, **kw)
+        R, Cc = q["codes"].shape
+        return Q.operand_values(q["codes"], q["scales"], fmt, "1d", R, 2 * Cc), q["s_dec"]
+    q = Q.quantize(bits, fmt, block="2d", emit_transpose=True, **kw)
+    R, C = bits.shape
+    vals = Q.operand_values(q["codes"], q["scales"], fmt, "2d", R, C)
+    return (vals if layout == "2d" else vals.T.copy()), q["s_dec"]
+
+
+def gpu_operand(q, layout):
+    return q.operand(transposed=(layout == "2dT"))
+
+
+def gpu_quant(bits, fmt, layout, **kw):
+    if layout in ("row", "col"):
+        return api.quantize(dev(bits), fmt, orient=layout, **kw)
+    return api.quantize(dev(bits), fmt, block="2d", emit_transpose=True, **kw)
+
+
+CASES = [
+    # fmt, A layout, B layout, M, N, K
+    ("nvfp4", "row", "row", 600, 520, 208),
+    ("nvfp4", "row", "2d", 300, 528, 400),
+    ("nvfp4", "row", "2dT", 272, 336, 528),
+    ("ue5m3", "row", "2d", 520, 272, 272),
+    ("ue5m3", "row", "2dT", 256, 256, 256),
+    ("ue5m3", "row", "row", 130, 70, 48),
+    ("mxfp4", "row", "row", 600, 520, 224),
+    ("mxfp4", "row", "row", 33, 17, 32),
+    ("nvfp4", "col", "col", 512, 264, 304),
+]
+
+
+@pytest.mark.parametrize("fmt,la,lb,M,N,K", CASES)
+def test_gemm_small(fmt, la, lb, M, N, K):
+    # A operand [M, K]; B operand [N, K] (for 2dT, W is [K, N])
+    a_shape = (M, K) if la == "row" else (K, M)
+    a_bits = inputs.activations(a_shape, cfg_seed=50)
+    if lb == "row":
+        b_bits = inputs.weights((N, K), cfg_seed=50)
+    elif lb == "col":
+        b_bits = inputs.gradients((K, N), cfg_seed=50)
+    elif lb == "2d":
+        b_bits = inputs.weights((N, K), cfg_seed=50)
+    else:
+        b_bits = inputs.weights((K, N), cfg_seed=50)
+    qa = gpu_quant(a_bits, fmt, la)
+    qb = gpu_quant(b_bits, fmt, lb)
+    d = api.gemm(gpu_operand(qa, la), gpu_operand(qb, lb), M, N, K, device=DEV)
+    torch.cuda.synchronize()
+    av, sa = oracle_operand(a_bits, fmt, la)
+    bv, sb = oracle_operand(b_bits, fmt, lb)
+    if fmt == "mxfp4":
+        sa = sb = 1.0
+    assert av.shape == (M, K) and bv.shape == (N, K)
+    check(d.cpu().numpy(), G.gemm_ref(av, bv, sa, sb), G.gemm_abs_bound(av, bv, sa, sb))
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+def test_gemm_accumulate_and_ldd(fmt):
+    M, N, K = 280, 300, 256
+    a_bits = inputs.activations((M, K), cfg_seed=51)
+    b_bits = inputs.weights((N, K), cfg_seed=51)
+    qa, qb = gpu_quant(a_bits, fmt, "row"), gpu_quant(b_bits, fmt, "row")
+    big = torch.randn((M, N + 24), dtype=torch.float32, device=DEV)
+    init = big.clone()
+    out = big[:, 8:8 + N]                       # ldd = N + 24, offset view
+    api.gemm(qa.operand(), qb.operand(), M, N, K, out=out, accumulate=True)
+    torch.cuda.synchronize()
+    av, sa = oracle_operand(a_bits, fmt, "row")
+    bv, sb = oracle_operand(b_bits, fmt, "row")
+    if fmt == "mxfp4":
+        sa = sb = 1.0
+    ref = G.gemm_ref(av, bv, sa, sb).astype(np.float64) + init[:, 8:8 + N].cpu().numpy()
+    bound = G.gemm_abs_bound(av, bv, sa, sb) + np.abs(init[:, 8:8 + N].cpu().numpy())
+    got = big.cpu().numpy()
+    check(got[:, 8:8 + N], ref, bound)
+    # columns outside the view are untouched
+    assert torch.equal(big[:, :8].cpu(), init[:, :8].cpu())
+    assert torch.equal(big[:, 8 + N:].cpu(), init[:, 8 + N:].cpu())
+
+
+def test_gemm_k_zero():
+    a = api.quantize(dev(inputs.activations((64, 32), cfg_seed=52)), "nvfp4")
+    b = api.quantize(dev(inputs.weights((48, 32), cfg_seed=52)), "nvfp4")
+    d = torch.full((64, 48), 7.0, device=DEV)
+    api.gemm(a.operand(), b.operand(), 64, 48, 0, out=d)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(d).item() == 0
+    d.fill_(7.0)
+    api.gemm(a.operand(), b.operand(), 64, 48, 0, out=d, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.all(d == 7.0).item()
+
+
+def test_gemm_zero_operand():
+    a_bits = np.zeros((64, 128), np.uint16)
+    b_bits = inputs.weights((64, 128), cfg_seed=53)
+    qa, qb = gpu_quant(a_bits, "nvfp4", "row"), gpu_quant(b_bits, "nvfp4", "row")
+    d = api.gemm(qa.operand(), qb.operand(), 64, 64, 128, device=DEV)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(d).item() == 0
+
+
+def test_gemm_ue5m3_tiny_scales():
+    # Blocks 2^-23 below the tensor amax get UE5M3 scales near 2^-17; with the
+    # 2^-5 shift their fp16 operands are subnormal.  The MFMA must use them.
+    rng = np.random.default_rng(54)
+    a = (rng.standard_normal((64, 256)) * 2.0 ** -23).astype(np.float32)
+    a[0, 0] = 1.0
+    b = (rng.standard_normal((64, 256)) * 2.0 ** -23).astype(np.float32)
+    b[0, 0] = 1.0
+    a_bits, b_bits = inputs.to_bf16_bits(a), inputs.to_bf16_bits(b)
+    qa, qb = gpu_quant(a_bits, "ue5m3", "row"), gpu_quant(b_bits, "ue5m3", "row")
+    d = api.gemm(qa.operand(), qb.operand(), 64, 64, 256, device=DEV)
+    torch.cuda.synchronize()
+    av, sa = oracle_operand(a_bits, "ue5m3", "row")
+    bv, sb = oracle_operand(b_bits, "ue5m3", "row")
+    # premise: many fp16 operands are subnormal, i.e. |e2m1 * scale| * 2^-5 < 2^-14
+    assert np.count_nonzero((av != 0) & (np.abs(av) * 2.0 ** -5 < 2.0 ** -14)) > 10000
+    check(d.cpu().numpy(), G.gemm_ref(av, bv, sa, sb), G.gemm_abs_bound(av, bv, sa, sb))
+
+
+def test_gemm_tiny_workload_config1():
+    # 256 x 256 x 256 Fprop of the tiny workload: A 1x16, W 16x16 2D
+    t = inputs.linear_tensors(1)
+    qa, qw = gpu_quant(t["X"], "nvfp4", "row"), gpu_quant(t["W"], "nvfp4", "2d")
+    d = api.gemm(qa.operand(), qw.operand(), 256, 256, 256, device=DEV)
+    torch.cuda.synchronize()
+    av, sa = oracle_operand(t["X"], "nvfp4", "row")
+    wv, sw = oracle_operand(t["W"], "nvfp4", "2d")
+    check(d.cpu().numpy(), G.gemm_ref(av, wv, sa, sw), G.gemm_abs_bound(av, wv, sa, sw))
+
+
+# ------------------------------------------------- full-size workloads ----
+def _stale(name, shape):
+    gen = {"X": inputs.activations, "W": inputs.weights, "dY": inputs.gradients}[name]
+    b = gen(shape, cfg_seed=inputs.STALE_SEED_OFFSET)
+    return np.float32(Q.tensor_amax(F.bf16_bits_to_f32(b)) / np.float32(1.5))
+
+
+def _recipe(cfg, name, layout):
+    """quantize() keyword arguments of one operand of a workload."""
+    fmt = {2: "nvfp4", 3: "nvfp4", 4: "ue5m3", 5: "mxfp4"}[cfg]
+    kw = {}
+    if name == "dY":
+        kw.update(rnd="sr", seed=1, offset=0 if layout == "row" else 1)
+    if cfg == 3 and layout == "col":
+        kw.update(rht=True, signs=SIGNS)
+    if fmt == "ue5m3":
+        kw["target"] = 2048.0 if name == "dY" else 448.0
+    return fmt, kw
+
+
+def _oracle_rows(bits, fmt, layout, sel, kw, amax):
+    """Oracle operand values of rows `sel` of the [rows, K] code matrix."""
+    out = []
+    for r in sel:
+        if layout == "row":
+            q = Q.quantize(bits[r:r + 1], fmt, amax=amax, index_base=r * bits.shape[1], **kw)
+            R, K = 1, bits.shape[1]
+            out.append(Q.operand_values(q["codes"], q["scales"], fmt, "1d", R, K)[0])
+        elif layout == "col":
+            q = Q.quantize(bits[:, r:r + 1], fmt, orient="col", amax=amax,
+                           index_base=r * bits.shape[0], **kw)
+            out.append(Q.operand_values(q["codes"], q["scales"], fmt, "1d", 1, bits.shape[0])[0])
+        elif layout == "2d":
+            g = r // 16 * 16
+            q = Q.quantize(bits[g:g + 16], fmt, block="2d", amax=amax, **kw)
+            out.append(Q.operand_values(q["codes"], q["scales"], fmt, "2d", 16, bits.shape[1])[r - g])
+        else:  # 2dT: row r of W^T is column r of W
+            g = r // 16 * 16
+            q = Q.quantize(bits[:, g:g + 16], fmt, block="2d", amax=amax, **kw)
+            vals = Q.operand_values(q["codes"], q["scales"], fmt, "2d", bits.shape[0], 16)
+            out.append(vals[:, r - g])
+    return np.stack(out)
+
+
+def _amax_for(bits, fmt, kw, stale):
+    if fmt == "mxfp4":
+        return None
+    if stale is not None:
+        return stale
+    xf = F.bf16_bits_to_f32(bits)
+    if kw.get("rht"):
+        from oracle.rht import rht16_cols
+        xf = rht16_cols(xf, SIGNS)
+    return Q.tensor_amax(xf)
+
+
+GEMMS = {
+    # name: (A tensor, A layout, B tensor, B layout)
+    "fprop": ("X", "row", "W", "2d"),
+    "dgrad": ("dY", "row", "W", "2dT"),
+    "wgrad": ("dY", "col", "X", "col"),
+}
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+@pytest.mark.parametrize("gemm", ["fprop", "dgrad", "wgrad"])
+def test_workload_gemm(cfg, gemm):
+    an, la, bn, lb = GEMMS[gemm]
+    fmt = {2: "nvfp4", 3: "nvfp4", 4: "ue5m3", 5: "mxfp4"}[cfg]
+    if fmt == "mxfp4":   # MXFP4 weights are 1D: rowwise for Fprop, colwise for Dgrad
+        lb = {"2d": "row", "2dT": "col"}.get(lb, lb)
+    t = inputs.linear_tensors(cfg, which=(an, bn))
+    a_bits, b_bits = t[an], t[bn]
+    fa, kwa = _recipe(cfg, an, la)
+    fb, kwb = _recipe(cfg, bn, lb)
+    sa_stale = _stale(an, a_bits.shape) if fmt == "ue5m3" else None
+    sb_stale = _stale(bn, b_bits.shape) if fmt == "ue5m3" else None
+
+    def gq(bits, layout, kw, stale):
+        amax_in = None if stale is None else torch.tensor([stale], dtype=torch.float32, device=DEV)
+        x = dev(bits)
+        if layout in ("2d", "2dT"):
+            return api.quantize(x, fmt, block="2d", emit_transpose=True, amax_in=amax_in,
+                                target=kw.get("target", 448.0))
+        return api.quantize(x, fmt, orient=layout, amax_in=amax_in, **kw)
+
+    qa, qb = gq(a_bits, la, kwa, sa_stale), gq(b_bits, lb, kwb, sb_stale)
+    M, K = qa.rows, qa.cols
+    N = qb.cols if lb == "2dT" else qb.rows
+    d = api.gemm(gpu_operand(qa, la), gpu_operand(qb, lb), M, N, K, device=DEV)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(100 + cfg)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 10)]))
+    cols = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 10)]))
+    amax_a = _amax_for(a_bits, fmt, kwa, sa_stale)
+    amax_b = _amax_for(b_bits, fmt, kwb, sb_stale)
+    kwb2 = {k: v for k, v in kwb.items() if k == "target"} if lb in ("2d", "2dT") else kwb
+    av = _oracle_rows(a_bits, fmt, la, rows, kwa, amax_a)
+    bv = _oracle_rows(b_bits, fmt, lb, cols, kwb2, amax_b)
+    if fmt == "mxfp4":
+        sa = sb = 1.0
+    else:
+        sa = Q.global_scales(amax_a, kwa.get("target", 448.0))[1]
+        sb = Q.global_scales(amax_b, kwb.get("target", 448.0))[1]
+    ref = G.gemm_ref(av, bv, sa, sb)
+    bound = G.gemm_abs_bound(av, bv, sa, sb)
+    got = d[torch.from_numpy(rows).to(DEV)][:, torch.from_numpy(cols).to(DEV)].cpu().numpy()
+    check(got, ref, bound)
