@@ -1,0 +1,368 @@
+"""Benchmark: one step = the whole FP4 hot path of one linear layer.
+
+Default workload: the 1.2B Transformer FFN up-projection (X [8192, 2048],
+W [6144, 2048], dY [8192, 6144]) in NVFP4, on synthetic seeded tensors
+already resident in HBM.  A step runs, on one stream:
+
+  tensor amax of X, W, dY
+  quantize X rowwise (RNE)         -> Fprop A
+  quantize W 16x16 2D (+ W^T)      -> Fprop B, Dgrad B
+  quantize dY rowwise (SR)         -> Dgrad A
+  quantize dY colwise (SR)         -> Wgrad A
+  quantize X colwise (RNE)         -> Wgrad B
+  GEMMs Fprop, Dgrad, Wgrad        (fp32 outputs)
+
+with event counters on every quantization.  The step is captured once as a
+HIP graph and replayed (after a bitwise check of replays against the eager
+step); per-kernel durations come from graphs of repeated launches of each
+op, timed with events on the launch stream.  Printed: one JSON line whose
+`value` is the step's GEMM throughput (3 x 2MNK / step time, TFLOP/s),
+per-kernel timings and rates (`parts`), the roofline of the dominant kernel
+and the CPU oracle timed on a bounded slab of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--config 2|3|4|5] [--no-cpu]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "quantize GB/s (% HBM peak); FP4 block-scaled GEMM TFLOP/s (% MFMA peak)"
+HBM_PEAK_GBS = 8000.0
+PEAK_TFLOPS = {"fp16": 2500.0, "fp4": 10100.0}   # dense MFMA, MI355X
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_gemm_nvfp4_1.2b_ffn.txt")
+
+# algorithmic bytes per element
+B_AMAX = 2.0
+B_Q1D = {"nvfp4": 2.0 + 0.5 + 1.0 / 16, "ue5m3": 2.0 + 0.5 + 1.0 / 16, "mxfp4": 2.0 + 0.5 + 1.0 / 32}
+B_Q2D_T = 2.0 + 0.5 + 0.5 + 1.0 / 256
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, choices=(2, 3, 4, 5))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    return ap.parse_args()
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "fp4_block_scaled_x16_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel_hash):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source."""
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None
+    vals = {}
+    with open(PROFILE_TRAFFIC) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_hash:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def build_step(cfg, dev):
+    """Inputs on the device and the list of (name, kind, units, fn) ops."""
+    import torch
+    from fp4_block_scaled_x16_amd import api, inputs
+    
+    c = inputs.CONFIGS[cfg]
+    fmt = c["fmt"]
+    T, din, dout = c["tokens"], c["d_in"], c["d_out"]
+    t = inputs.linear_tensors(cfg)
+    X = torch.from_numpy(t["X"].view(np.int16)).to(dev)
+    W = torch.from_numpy(t["W"].view(np.int16)).to(dev)
+    dY = torch.from_numpy(t["dY"].view(np.int16)).to(dev)
+    cnt = api.new_counters(dev)
+    rht = cfg == 3
+    target_x = target_w = target_dy = 448.0
+    stale = {}
+    if fmt == "ue5m3":
+        target_dy = 2048.0
+        for name, gen, shape in (("X", inputs.activations, X.shape), ("W", inputs.weights, W.shape),
+                                 ("dY", inputs.gradients, dY.shape)):
+            b = torch.from_numpy(gen(tuple(shape), cfg_seed=inputs.STALE_SEED_OFFSET).view(np.int16)).to(dev)
+            stale[name] = (api.amax(b) / 1.5).contiguous()
+            del b
+    D_f = torch.empty((T, dout), dtype=torch.float32, device=dev)
+    D_d = torch.empty((T, din), dtype=torch.float32, device=dev)
+    D_w = torch.empty((dout, din), dtype=torch.float32, device=dev)
+    st = {}
+    sig = inputs.rht_sign_mask()
+
+    def amax_op(name, x):
+        def f():
+            if name in stale:
+                st["amax_" + name] = stale[name]
+            else:
+                st["amax_" + name] = api.amax(x)
+        return f
+
+    def amax_rot_op(name, x):
+        def f():
+            st["amax_rot_" + name] = api.amax(x, rht=True, signs=sig)
+        return f
+
+    ops = []
+    two_level = fmt != "mxfp4"
+    if two_level:
+        ops += [("amax X", "hbm", B_AMAX * X.numel(), amax_op("X", X)),
+                ("amax W", "hbm", B_AMAX * W.numel(), amax_op("W", W)),
+                ("amax dY", "hbm", B_AMAX * dY.numel(), amax_op("dY", dY))]
+        if fmt == "ue5m3":     # stale amax given: nothing to compute
+            ops = [(n, k, 0.0, f) for (n, k, _, f) in ops]
+        if rht:
+            ops += [("amax rot X", "hbm", B_AMAX * X.numel(), amax_rot_op("X", X)),
+                    ("amax rot dY", "hbm", B_AMAX * dY.numel(), amax_rot_op("dY", dY))]
+    b1 = B_Q1D[fmt]
+
+    def q(name, x, out, **kw):
+        def f():
+            if two_level:
+                key = ("amax_rot_" if kw.get("rht") else "amax_") + name
+                kw2 = dict(kw, amax_in=st[key])
+            else:
+                kw2 = kw
+            st[out] = api.quantize(x, fmt, counters=cnt, **kw2)
+        return f
+
+    ops.append(("quant X row", "hbm", b1 * X.numel(), q("X", X, "qx", target=target_x)))
+    if two_level:
+        ops.append(("quant W 2d+T", "hbm", B_Q2D_T * W.numel(),
+                    q("W", W, "qw", block="2d", emit_transpose=True, target=target_w)))
+    else:
+        ops.append(("quant W row", "hbm", b1 * W.numel(), q("W", W, "qw")))
+        ops.append(("quant W col", "hbm", b1 * W.numel(), q("W", W, "qwc", orient="col")))
+    ops.append(("quant dY row SR", "hbm", b1 * dY.numel(),
+                q("dY", dY, "qdy", rnd="sr", seed=1, offset=0, target=target_dy)))
+    ops.append(("quant dY col SR", "hbm", b1 * dY.numel(),
+                q("dY", dY, "qdyc", orient="col", rnd="sr", seed=1, offset=1, rht=rht,
+                  signs=sig if rht else 0, target=target_dy)))
+    ops.append(("quant X col", "hbm", b1 * X.numel(),
+                q("X", X, "qxc", orient="col", rht=rht, signs=sig if rht else 0, target=target_x)))
+
+    def g(a, la, b, lb, M, N, K, out):
+        def f():
+            A = st[a].operand()
+            B = st[b].operand(transposed=(lb == "T")) if two_level else st[b].operand()
+            api.gemm(A, B, M, N, K, out=out)
+        return f
+
+    fl = lambda M, N, K: 2.0 * M * N * K
+    ops.append(("gemm fprop", "mfma", fl(T, dout, din), g("qx", "r", "qw", "r", T, dout, din, D_f)))
+    ops.append(("gemm dgrad", "mfma", fl(T, din, dout),
+                g("qdy", "r", "qw" if two_level else "qwc", "T", T, din, dout, D_d)))
+    ops.append(("gemm wgrad", "mfma", fl(dout, din, T), g("qdyc", "r", "qxc", "r", dout, din, T, D_w)))
+    return ops, cnt, dict(X=t["X"], W=t["W"], dY=t["dY"], gpu_outputs=(D_f, D_d, D_w)), fmt
+
+
+def cpu_baseline(cfg, host, fmt, tokens):
+    """The CPU oracle on a token slab of the same step (W quantized in full)."""
+    from threadpoolctl import threadpool_info
+    from oracle import quantize as Q
+    from oracle import gemm as G
+    from fp4_block_scaled_x16_amd import inputs
+
+    X, W, dY = host["X"][:tokens], host["W"], host["dY"][:tokens]
+    rht = cfg == 3
+    sig = inputs.rht_sign_mask()
+    t0 = time.perf_counter()
+    kw_dy = dict(rnd="sr", seed=1)
+    tgt_dy = 2048.0 if fmt == "ue5m3" else 448.0
+    if fmt == "mxfp4":
+        qx = Q.quantize(X, fmt)
+        qw = Q.quantize(W, fmt)
+        qwc = Q.quantize(W, fmt, orient="col")
+        qdy = Q.quantize(dY, fmt, offset=0, **kw_dy)
+        qdyc = Q.quantize(dY, fmt, orient="col", offset=1, **kw_dy)
+        qxc = Q.quantize(X, fmt, orient="col")
+        s = lambda q: 1.0
+        av = lambda q, blk="1d": Q.operand_values(q["codes"], q["scales"], fmt, blk,
+                                                  q["codes"].shape[0], 2 * q["codes"].shape[1])
+        wv, wtv = av(qw), av(qwc)
+    else:
+        qx = Q.quantize(X, fmt)
+        qw = Q.quantize(W, fmt, block="2d", emit_transpose=True)
+        qdy = Q.quantize(dY, fmt, offset=0, target=tgt_dy, **kw_dy)
+        qdyc = Q.quantize(dY, fmt, orient="col", offset=1, rht=rht, signs=sig, target=tgt_dy, **kw_dy)
+        qxc = Q.quantize(X, fmt, orient="col", rht=rht, signs=sig)
+        s = lambda q: q["s_dec"]
+        av = lambda q, blk="1d": Q.operand_values(q["codes"], q["scales"], fmt, blk,
+                                                  q["codes"].shape[0], 2 * q["codes"].shape[1])
+        wv = av(qw, "2d")
+        wtv = wv.T.copy()
+    d_f = G.gemm_ref(av(qx), wv, s(qx), s(qw))
+    d_d = G.gemm_ref(av(qdy), wtv, s(qdy), s(qw))
+    d_w = G.gemm_ref(av(qdyc), av(qxc), s(qdyc), s(qxc))
+    dt = time.perf_counter() - t0
+    T = tokens
+    din, dout = X.shape[1], W.shape[0]
+    flops = 2.0 * T * dout * din * 3
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    del d_f, d_d, d_w
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": "the same step on %d of %d tokens (W quantized in full), %.1f s; "
+                      "GEMMs in fp64 BLAS, quantizers single-threaded NumPy" % (
+                          tokens, host["X"].shape[0], dt),
+            "seconds": round(dt, 3)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only (--gpus 1); the multi-GPU "
+              "sharding of this path is described in DESIGN.md, not run.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from fp4_block_scaled_x16_amd import api, inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    api.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = args.config
+    ops, cnt, host, fmt = build_step(cfg, dev)
+
+    def run_step():
+        for (_, _, _, f) in ops:
+            f()
+
+    # eager warmup (also performs the library's one-time kernel attribute setup)
+    for _ in range(max(1, args.warmup)):
+        run_step()
+    torch.cuda.synchronize()
+    outs = [t for t in host["gpu_outputs"]]
+    eager = [t.clone() for t in outs]
+
+    # the step as one HIP graph: no host launch gaps inside the timed region
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run_step()
+    for _ in range(2):
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, eager):
+            if not torch.equal(a, b):
+                raise RuntimeError("graph replay differs from the eager step")
+    for _ in range(args.warmup):
+        graph.replay()
+    cnt.zero_()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    counters = api.counters_dict(cnt)
+
+    # per-kernel durations: each op repeated R times in its own graph, timed
+    # with events on the stream the kernels run on
+    R = 10
+    op_ms = []
+    for (_, _, _, f) in ops:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(R):
+                f()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(3):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        op_ms.append(a.elapsed_time(b) / (3 * R))
+        del g
+
+    parts = {}
+    for i, (name, kind, units, _) in enumerate(ops):
+        ms = op_ms[i]
+        p = {"ms": round(ms, 4)}
+        if kind == "hbm" and units > 0:
+            gbs = units / (ms * 1e-3) / 1e9
+            p.update(GBps=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
+        elif kind == "mfma":
+            tf = units / (ms * 1e-3) / 1e12
+            peak = PEAK_TFLOPS["fp4" if fmt == "mxfp4" else "fp16"]
+            p.update(TFLOPs=round(tf, 1), frac_peak=round(tf / peak, 4))
+        parts[name] = p
+    q_bytes = sum(u for (_, k, u, _) in ops if k == "hbm")
+    q_ms = sum(parts[n]["ms"] for (n, k, u, _) in ops if k == "hbm" and u > 0)
+    g_flops = sum(u for (_, k, u, _) in ops if k == "mfma")
+    g_ms = sum(parts[n]["ms"] for (n, k, _, _) in ops if k == "mfma")
+    value = g_flops / (ms_step * 1e-3) / 1e12
+
+    # dominant kernel: the block-scaled GEMM (all three launches run the same kernel)
+    gemm_names = [n for (n, k, _, _) in ops if k == "mfma"]
+    avg_ms = float(np.mean([parts[n]["ms"] for n in gemm_names]))
+    per_launch = g_flops / len(gemm_names)
+    achieved = per_launch / (avg_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS["fp4" if fmt == "mxfp4" else "fp16"]
+    khash = source_hash("gemm.hip", "fp4_device.hpp")
+    traffic = read_traffic(khash) if cfg == 2 else None
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": traffic,
+                "kernel": "k_gemm_two_level<NVFP4>" if fmt == "nvfp4" else
+                          ("k_gemm_two_level<UE5M3>" if fmt == "ue5m3" else "k_gemm_mx"),
+                "flops_per_launch": per_launch, "avg_launch_ms": round(avg_ms, 4),
+                "kernel_source_sha256_16": khash}
+
+    c = inputs.CONFIGS[cfg]
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp4(e2m1)+%s scales; %s MFMA, fp32 accumulate" % (
+            {"nvfp4": "e4m3", "ue5m3": "ue5m3", "mxfp4": "ue8m0"}[fmt],
+            "fp4 scaled" if fmt == "mxfp4" else "fp16 (exact dequant)"),
+        "data": "synthetic (seeded PCG64, bf16 inputs resident in HBM)",
+        "config": {"workload": c["name"], "format": fmt, "tokens": c["tokens"], "d_in": c["d_in"],
+                   "d_out": c["d_out"], "gemms": "fprop, dgrad, wgrad",
+                   "quantizations": len([1 for (n, k, u, _) in ops if n.startswith("quant")])},
+        "quantize": {"GBps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
+                     "frac_hbm": round(q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "ms": round(q_ms, 4)},
+        "gemm": {"TFLOPs": round(g_flops / (g_ms * 1e-3) / 1e12, 1),
+                 "frac_peak": round(g_flops / (g_ms * 1e-3) / 1e12 / peak, 4), "ms": round(g_ms, 4)},
+        "roofline": roofline,
+        "parts": parts,
+        "counters": counters,
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(cfg, host, fmt, args.cpu_tokens)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

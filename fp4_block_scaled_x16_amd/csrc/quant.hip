@@ -19,13 +19,20 @@ using namespace fp4dev;
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;       // tiled kernels (colwise, 2D)
+constexpr int kStream = 512;        // streaming kernels (amax, rowwise, dequant, RHT)
+
+// Same-address global atomics serialize (about 12 ns each on MI355X once
+// more than a few hundred arrive), so every kernel runs a persistent grid
+// of one or two workgroups per CU, reduces in LDS, and issues at most one
+// atomic per workgroup and counter.
 
 // ----------------------------------------------------------- counters --
 // Reduce five per-thread event counts over the workgroup and add the
 // nonzero totals to the caller's device counters (one atomic each).
+template <int NT>
 __device__ __forceinline__ void flush_counters(uint32_t (&c)[5], fp4_counters* out) {
-  __shared__ uint32_t red[kThreads / 64][5];
+  __shared__ uint32_t red[NT / 64][5];
 #pragma unroll
   for (int k = 0; k < 5; ++k) {
     uint32_t v = c[k];
@@ -42,7 +49,7 @@ __device__ __forceinline__ void flush_counters(uint32_t (&c)[5], fp4_counters* o
   if (threadIdx.x < 5) {
     uint32_t t = 0;
 #pragma unroll
-    for (int w = 0; w < kThreads / 64; ++w) t += red[w][threadIdx.x];
+    for (int w = 0; w < NT / 64; ++w) t += red[w][threadIdx.x];
     if (t) {
       unsigned long long* dst = reinterpret_cast<unsigned long long*>(out) + threadIdx.x;
       atomicAdd(dst, static_cast<unsigned long long>(t));
@@ -106,15 +113,31 @@ __device__ __forceinline__ uint32_t scale_for_block(float amax_b, float s_enc_g,
 // ---------------------------------------------------------------- amax --
 __global__ void k_fill_u32(uint32_t* p, uint32_t v) { *p = v; }
 
+// Workgroup max of a per-thread value (fp32 bits of a magnitude), then one
+// atomic max -- skipped when the current value is already as large.
+template <int NT>
+__device__ __forceinline__ void flush_max(uint32_t m, uint32_t* out) {
+  __shared__ uint32_t red[NT / 64];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(m, o, 64)));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) m = max(m, red[w]);
+    if (m > __hip_atomic_load(out, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(out, m);
+  }
+}
+
 // max |x| over a [rows, cols] bf16 matrix, cols % 8 == 0.  |x| as fp32 bits
 // is monotone in the value, so an unsigned atomic max is exact.
-__global__ __launch_bounds__(kThreads) void k_amax(const uint16_t* __restrict__ x, int64_t rows,
-                                                   int64_t cols, int64_t ld,
-                                                   uint32_t* __restrict__ out) {
+__global__ __launch_bounds__(kStream) void k_amax(const uint16_t* __restrict__ x, int64_t rows,
+                                                  int64_t cols, int64_t ld,
+                                                  uint32_t* __restrict__ out) {
   const uint64_t cpr = static_cast<uint64_t>(cols) >> 3;      // 16-byte chunks per row
   const uint64_t n = static_cast<uint64_t>(rows) * cpr;
-  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
-  uint64_t i = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kStream;
+  uint64_t i = static_cast<uint64_t>(blockIdx.x) * kStream + threadIdx.x;
   uint64_t r = cpr ? i / cpr : 0, j = cpr ? i - r * cpr : 0;
   const uint64_t sr = cpr ? stride / cpr : 0, sj = cpr ? stride - sr * cpr : 0;
   uint32_t m = 0;
@@ -134,21 +157,19 @@ __global__ __launch_bounds__(kThreads) void k_amax(const uint16_t* __restrict__ 
       ++r;
     }
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(m, o, 64)));
-  if ((threadIdx.x & 63) == 0 && m) atomicMax(out, m);
+  flush_max<kStream>(m, out);
 }
 
 // max |(1/4) D_r H16 v| over every 16-row group v of every column.
 // One thread per (column pair, group); rows % 16 == 0, cols % 8 == 0.
-__global__ __launch_bounds__(kThreads) void k_amax_rht(const uint16_t* __restrict__ x,
-                                                       int64_t rows, int64_t cols, int64_t ld,
-                                                       uint32_t signs, uint32_t* __restrict__ out) {
+__global__ __launch_bounds__(kStream) void k_amax_rht(const uint16_t* __restrict__ x,
+                                                      int64_t rows, int64_t cols, int64_t ld,
+                                                      uint32_t signs, uint32_t* __restrict__ out) {
   const uint64_t pairs = static_cast<uint64_t>(cols) >> 1;
   const uint64_t n = (static_cast<uint64_t>(rows) >> 4) * pairs;
-  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kStream;
   float m = 0.0f;
-  for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n;
+  for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kStream + threadIdx.x; i < n;
        i += stride) {
     const uint64_t g = i / pairs, p = i - g * pairs;
     const uint16_t* src = x + g * 16 * ld + p * 2;
@@ -164,16 +185,13 @@ __global__ __launch_bounds__(kThreads) void k_amax_rht(const uint16_t* __restric
 #pragma unroll
     for (int k = 0; k < 16; ++k) m = fmaxf(m, fmaxf(fabsf(a[k]), fabsf(b[k])));
   }
-  uint32_t mb = __float_as_uint(m);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mb = max(mb, static_cast<uint32_t>(__shfl_xor(mb, o, 64)));
-  if ((threadIdx.x & 63) == 0 && mb) atomicMax(out, mb);
+  flush_max<kStream>(__float_as_uint(m), out);
 }
 
 // ------------------------------------------------------ rowwise 1D ------
 // One thread per block of BS consecutive elements of a row.
 template <int FMT, int RND, bool CNT>
-__global__ __launch_bounds__(kThreads) void k_quant_row(
+__global__ __launch_bounds__(kStream) void k_quant_row(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, const float* __restrict__ amax,
     float target, float* __restrict__ s_dec_out, uint64_t seed, uint64_t offset,
@@ -185,8 +203,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_row(
 
   const uint64_t bpr = static_cast<uint64_t>(cols) / BS;
   const uint64_t n = static_cast<uint64_t>(rows) * bpr;
-  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
-  uint64_t i = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kStream;
+  uint64_t i = static_cast<uint64_t>(blockIdx.x) * kStream + threadIdx.x;
   uint64_t r = bpr ? i / bpr : 0, j = bpr ? i - r * bpr : 0;
   const uint64_t sr = bpr ? stride / bpr : 0, sj = bpr ? stride - sr * bpr : 0;
   uint32_t cnt[5] = {0, 0, 0, 0, 0};
@@ -220,7 +238,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_row(
       ++r;
     }
   }
-  if constexpr (CNT) flush_counters(cnt, counters);
+  if constexpr (CNT) flush_counters<kStream>(cnt, counters);
 }
 
 // ------------------------------------------------------ colwise 1D ------
@@ -309,7 +327,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
     }
     __syncthreads();
   }
-  if constexpr (CNT) flush_counters(cnt, counters);
+  if constexpr (CNT) flush_counters<kThreads>(cnt, counters);
 }
 
 // ------------------------------------------------------------ 2D 16x16 --
@@ -393,13 +411,13 @@ __global__ __launch_bounds__(kThreads) void k_quant_2d(
       __syncthreads();
     }
   }
-  if constexpr (CNT) flush_counters(cnt, counters);
+  if constexpr (CNT) flush_counters<kThreads>(cnt, counters);
 }
 
 // ---------------------------------------------------------- dequantize --
 // One thread per block of BS codes of a [rows, cols] code matrix.
 template <int FMT, bool B2D, bool F32>
-__global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* __restrict__ codes,
+__global__ __launch_bounds__(kStream) void k_dequant(const uint8_t* __restrict__ codes,
                                                       const uint8_t* __restrict__ scales,
                                                       const float* __restrict__ s_dec,
                                                       int64_t rows, int64_t cols,
@@ -408,8 +426,8 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* __restrict_
   const float sd = (FMT == kMX) ? 1.0f : *s_dec;
   const uint64_t bpr = static_cast<uint64_t>(cols) / BS;
   const uint64_t n = static_cast<uint64_t>(rows) * bpr;
-  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
-  for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n;
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kStream;
+  for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kStream + threadIdx.x; i < n;
        i += stride) {
     const uint64_t r = i / bpr, j = i - r * bpr;
     const uint32_t sc = B2D ? scales[(r >> 4) * bpr + j] : scales[i];
@@ -465,13 +483,13 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* __restrict_
 }
 
 // ------------------------------------------------------- standalone RHT --
-__global__ __launch_bounds__(kThreads) void k_rht16(const uint16_t* __restrict__ x, int64_t rows,
-                                                    int64_t cols, int64_t ld, uint32_t signs,
-                                                    float* __restrict__ y) {
+__global__ __launch_bounds__(kStream) void k_rht16(const uint16_t* __restrict__ x, int64_t rows,
+                                                   int64_t cols, int64_t ld, uint32_t signs,
+                                                   float* __restrict__ y) {
   const uint64_t pairs = static_cast<uint64_t>(cols) >> 1;
   const uint64_t n = (static_cast<uint64_t>(rows) >> 4) * pairs;
-  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kThreads;
-  for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n;
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kStream;
+  for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kStream + threadIdx.x; i < n;
        i += stride) {
     const uint64_t g = i / pairs, p = i - g * pairs;
     const uint16_t* src = x + g * 16 * ld + p * 2;
@@ -491,8 +509,10 @@ __global__ __launch_bounds__(kThreads) void k_rht16(const uint16_t* __restrict__
   }
 }
 
-int grid_for(uint64_t work_items, int per_cu) {
-  const uint64_t want = (work_items + kThreads - 1) / kThreads;
+// Persistent grid: enough workgroups of `threads` for the work, at most
+// per_cu per CU.
+int grid_for(uint64_t work_items, int per_cu, int threads = kStream) {
+  const uint64_t want = (work_items + threads - 1) / threads;
   const uint64_t cap = static_cast<uint64_t>(fp4lib::device_cu_count()) * per_cu;
   const uint64_t g = want < cap ? want : cap;
   return static_cast<int>(g ? g : 1);
@@ -523,11 +543,11 @@ hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld
   if (rows > 0 && cols > 0) {
     if (rht) {
       const uint64_t n = static_cast<uint64_t>(rows / 16) * static_cast<uint64_t>(cols / 2);
-      hipLaunchKernelGGL(k_amax_rht, dim3(grid_for(n, 8)), dim3(kThreads), 0, s, x, rows, cols,
+      hipLaunchKernelGGL(k_amax_rht, dim3(grid_for(n, 1)), dim3(kStream), 0, s, x, rows, cols,
                          ld, signs, out);
     } else {
       const uint64_t n = static_cast<uint64_t>(rows) * static_cast<uint64_t>(cols / 8);
-      hipLaunchKernelGGL(k_amax, dim3(grid_for(n, 8)), dim3(kThreads), 0, s, x, rows, cols, ld,
+      hipLaunchKernelGGL(k_amax, dim3(grid_for(n, 1)), dim3(kStream), 0, s, x, rows, cols, ld,
                          out);
     }
   }
@@ -538,7 +558,7 @@ template <int FMT, int RND, bool CNT>
 static void row_launch(const QuantArgs& a, hipStream_t s) {
   constexpr int BS = FMT == kMX ? 32 : 16;
   const uint64_t n = static_cast<uint64_t>(a.rows) * static_cast<uint64_t>(a.cols / BS);
-  hipLaunchKernelGGL((k_quant_row<FMT, RND, CNT>), dim3(grid_for(n, 8)), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((k_quant_row<FMT, RND, CNT>), dim3(grid_for(n, 1)), dim3(kStream), 0, s,
                      a.x, a.rows, a.cols, a.ld, a.codes, a.scales, a.amax, a.target, a.s_dec,
                      a.seed, a.offset, a.counters);
 }
@@ -566,7 +586,7 @@ template <int FMT, int RND, bool RHT, bool CNT>
 static void col_launch(const QuantArgs& a, hipStream_t s) {
   constexpr int BS = FMT == kMX ? 32 : 16;
   const int64_t tiles = ((a.rows + 8 * BS - 1) / (8 * BS)) * ((a.cols + 63) / 64);
-  const int64_t cap = static_cast<int64_t>(device_cu_count()) * 4;
+  const int64_t cap = static_cast<int64_t>(device_cu_count()) * 2;
   const int grid = static_cast<int>(tiles < cap ? (tiles > 0 ? tiles : 1) : cap);
   hipLaunchKernelGGL((k_quant_col<FMT, RND, RHT, CNT>), dim3(grid), dim3(kThreads), 0, s, a.x,
                      a.rows, a.cols, a.ld, a.codes, a.scales, a.amax, a.target, a.s_dec, a.seed,
@@ -605,7 +625,7 @@ hipError_t launch_quant_col(const QuantArgs& a, hipStream_t s) {
 template <int FMT, bool CNT>
 static void q2d_launch(const QuantArgs& a, hipStream_t s) {
   const int64_t regions = ((a.rows + 63) / 64) * ((a.cols + 63) / 64);
-  const int64_t cap = static_cast<int64_t>(device_cu_count()) * 8;
+  const int64_t cap = static_cast<int64_t>(device_cu_count()) * 2;
   const int grid = static_cast<int>(regions < cap ? (regions > 0 ? regions : 1) : cap);
   hipLaunchKernelGGL((k_quant_2d<FMT, CNT>), dim3(grid), dim3(kThreads), 0, s, a.x, a.rows,
                      a.cols, a.ld, a.codes, a.scales, a.emit_transpose ? a.codes_t : nullptr,
@@ -628,12 +648,12 @@ static void dq_launch(const uint8_t* codes, const uint8_t* scales, const float* 
                       int64_t rows, int64_t cols, void* out, int out_fp32, hipStream_t s) {
   constexpr int BS = FMT == kMX ? 32 : 16;
   const uint64_t n = static_cast<uint64_t>(rows) * static_cast<uint64_t>(cols / BS);
-  const int grid = grid_for(n, 8);
+  const int grid = grid_for(n, 2);
   if (out_fp32)
-    hipLaunchKernelGGL((k_dequant<FMT, B2D, true>), dim3(grid), dim3(kThreads), 0, s, codes,
+    hipLaunchKernelGGL((k_dequant<FMT, B2D, true>), dim3(grid), dim3(kStream), 0, s, codes,
                        scales, s_dec, rows, cols, out);
   else
-    hipLaunchKernelGGL((k_dequant<FMT, B2D, false>), dim3(grid), dim3(kThreads), 0, s, codes,
+    hipLaunchKernelGGL((k_dequant<FMT, B2D, false>), dim3(grid), dim3(kStream), 0, s, codes,
                        scales, s_dec, rows, cols, out);
 }
 
@@ -658,7 +678,7 @@ hipError_t launch_rht16(const uint16_t* x, int64_t rows, int64_t cols, int64_t l
                         float* y, hipStream_t s) {
   if (rows > 0 && cols > 0) {
     const uint64_t n = static_cast<uint64_t>(rows / 16) * static_cast<uint64_t>(cols / 2);
-    hipLaunchKernelGGL(k_rht16, dim3(grid_for(n, 8)), dim3(kThreads), 0, s, x, rows, cols, ld,
+    hipLaunchKernelGGL(k_rht16, dim3(grid_for(n, 2)), dim3(kStream), 0, s, x, rows, cols, ld,
                        signs, y);
   }
   return hipGetLastError();

@@ -20,8 +20,9 @@ from __future__ import annotations
 
 import numpy as np
 
-X_ID, W_ID, DY_ID = 0, 1, 2
+X_ID, W_ID, DY_ID, SIGNS_ID = 0, 1, 2, 3
 STALE_SEED_OFFSET = 50
+RHT_SEED = 7
 
 #: tokens x in, out x in, tokens x out for each workload
 CONFIGS = {
@@ -71,6 +72,14 @@ def gradients(shape, cfg_seed=0, tensor_id=DY_ID, lo_exp=-8.0, hi_exp=-2.0):
     sign = rng.integers(0, 2, n, dtype=np.uint8)
     mag[sign == 1] *= np.float32(-1.0)
     return to_bf16_bits(mag).reshape(shape)
+
+
+def rht_sign_mask(seed=RHT_SEED):
+    """The random diagonal D_r of the 16-point RHT as a 16-bit mask (bit i set:
+    output row i is negated).  One vector is shared by all layers and both
+    Wgrad operands; it is drawn here, from the seed, and passed to both the
+    kernels and the oracle."""
+    return int(_rng(seed, SIGNS_ID).integers(0, 1 << 16))
 
 
 def normal(shape, sigma=1.0, cfg_seed=0, tensor_id=X_ID):

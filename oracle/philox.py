@@ -67,14 +67,3 @@ def sr_random16(idx, seed, offset):
     word = np.take_along_axis(w.reshape(-1, 4), (j >> 1).reshape(-1, 1), axis=1).reshape(idx.shape)
     return ((word >> ((j & 1) * 16).astype(np.uint32)) & 0xFFFF).astype(np.uint16)
 
-
-def rht_signs(seed=7):
-    """The shared random sign vector D_r of the 16-point RHT, as a 16-bit mask.
-
-    The NVFP4 paper (§4.2, App. C) uses one random diagonal sign vector for
-    all layers; how it is drawn is not stated.  Reading: the low 16 bits of
-    word 0 of Philox4x32-10 with key (seed, 0) and counter 0; bit i set means
-    output row i of the Hadamard transform is negated.
-    """
-    w0, _, _, _ = philox4x32_10(0, 0, 0, 0, seed, 0)
-    return int(w0) & 0xFFFF

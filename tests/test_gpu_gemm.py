@@ -16,12 +16,11 @@ from fp4_block_scaled_x16_amd import api, inputs
 from oracle import formats as F
 from oracle import gemm as G
 from oracle import quantize as Q
-from oracle.philox import rht_signs
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 TOL = 1e-5
-SIGNS = rht_signs(7)
+SIGNS = inputs.rht_sign_mask()
 
 
 def dev(bits):

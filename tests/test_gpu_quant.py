@@ -13,12 +13,11 @@ import torch
 from fp4_block_scaled_x16_amd import api, inputs
 from oracle import formats as F
 from oracle import quantize as Q
-from oracle.philox import rht_signs
 from oracle.rht import rht16_cols
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-SIGNS = rht_signs(7)
+SIGNS = inputs.rht_sign_mask()
 
 
 def dev(bits):

@@ -70,8 +70,8 @@ def test_sr_stream_uniform_and_seeded():
     assert np.array_equal(r[1000:3000], P.sr_random16(idx[1000:3000], 1, 0))
 
 
-def test_rht_signs_deterministic():
-    s = P.rht_signs(7)
+def test_rht_sign_mask_is_seeded_input():
+    from fp4_block_scaled_x16_amd import inputs
+    s = inputs.rht_sign_mask()
     assert 0 <= s < 1 << 16
-    assert s == P.rht_signs(7)
-    assert s == int(P.philox4x32_10(0, 0, 0, 0, 7, 0)[0]) & 0xFFFF
+    assert s == inputs.rht_sign_mask() != inputs.rht_sign_mask(8)

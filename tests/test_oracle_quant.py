@@ -19,7 +19,6 @@ import pytest
 from oracle import formats as F
 from oracle import quantize as Q
 from oracle.rht import rht16_cols
-from oracle.philox import rht_signs
 from fp4_block_scaled_x16_amd import inputs
 from conftest import GOLDEN
 
@@ -180,7 +179,7 @@ def test_colwise_is_rowwise_of_transpose():
 
 def test_rht_amax_after_rotation():
     x = inputs.activations((64, 48), cfg_seed=8)
-    s = rht_signs(7)
+    s = inputs.rht_sign_mask()
     q = Q.quantize(x, "nvfp4", orient="col", rht=True, signs=s)
     rot = rht16_cols(F.bf16_bits_to_f32(x), s)
     assert q["amax"] == np.float32(np.abs(rot).max())

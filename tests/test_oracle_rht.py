@@ -9,7 +9,7 @@ import numpy as np
 import scipy.linalg
 
 from oracle import rht as R
-from oracle.philox import rht_signs
+from fp4_block_scaled_x16_amd import inputs
 
 H16 = scipy.linalg.hadamard(16).astype(np.float64)
 
@@ -35,7 +35,7 @@ def test_signs_flip_output_rows():
 
 def test_constant_vector_concentrates():
     c = np.float32(3.25)
-    for signs in (0, 1, rht_signs(7)):
+    for signs in (0, 1, inputs.rht_sign_mask()):
         y = R.rht16_vec(np.full(16, c, np.float32), signs)
         want = np.zeros(16, np.float32)
         want[0] = -4 * c if signs & 1 else 4 * c
@@ -45,7 +45,7 @@ def test_constant_vector_concentrates():
 def test_fp32_error_bound_against_fp64():
     rng = np.random.default_rng(5)
     v = (rng.standard_normal((20000, 16)) * 10.0 ** rng.uniform(-6, 6, (20000, 1))).astype(np.float32)
-    signs = rht_signs(7)
+    signs = inputs.rht_sign_mask()
     d = np.array([-1.0 if (signs >> i) & 1 else 1.0 for i in range(16)])
     exact = (v.astype(np.float64) @ H16.T) * 0.25 * d
     got = R.rht16_vec(v, signs).astype(np.float64)
@@ -58,7 +58,7 @@ def test_cols_layout_and_cancellation():
     T, a, b = 64, 5, 7
     x = rng.standard_normal((T, a)).astype(np.float32)
     dy = rng.standard_normal((T, b)).astype(np.float32)
-    s = rht_signs(7)
+    s = inputs.rht_sign_mask()
     rx, rdy = R.rht16_cols(x, s), R.rht16_cols(dy, s)
     # each 16-row group of each column is transformed independently
     assert np.array_equal(rx[16:32, 3], R.rht16_vec(x[16:32, 3], s))
