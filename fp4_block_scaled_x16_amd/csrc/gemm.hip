@@ -55,6 +55,7 @@ struct Params {
   int accumulate;
   int tiles_m, tiles_n;
   int vec16[2];         // code rows are 16-byte aligned
+  int sc_vec[2];        // the scales of one row and K step are contiguous and aligned
 };
 
 // Tile order: consecutive workgroup ids go round-robin over the 8 XCDs, so
@@ -144,7 +145,38 @@ struct Stage2 {
   uint4 scales[2][2][256];
 };
 
-template <int FMT>
+// One MFMA K slice (16 K-values) of the wave's 4 x 4 tiles: dequantize the
+// lane's A and B fragments for slice KS, then 16 MFMAs.
+template <int KS>
+__device__ __forceinline__ void two_level_slice(floatx16 (&acc)[4][4], const uint32_t (&a_raw)[4][8],
+                                                const uint32_t (&b_raw)[4][8], const uint4 (&a_sc)[4],
+                                                const uint4 (&b_sc)[4]) {
+  constexpr int W = KS >> 1;     // scale word: one 16-element block per two slices
+  half8 a_op[4], b_op[4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+    const uint32_t sc = W == 0 ? a_sc[mi].x : W == 1 ? a_sc[mi].y : W == 2 ? a_sc[mi].z : a_sc[mi].w;
+    a_op[mi] = dequant8(a_raw[mi][KS], sc);
+  }
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) {
+    const uint32_t sc = W == 0 ? b_sc[ni].x : W == 1 ? b_sc[ni].y : W == 2 ? b_sc[ni].z : b_sc[ni].w;
+    b_op[ni] = dequant8(b_raw[ni][KS], sc);
+  }
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_op[mi], b_op[ni], acc[mi][ni], 0, 0, 0);
+}
+
+// FAST: M, N multiples of 256, K a multiple of 128 and code rows 16-byte
+// aligned -- no bounds checks, straight-line loads (the compiler then keeps
+// them in flight across the MFMAs).  Otherwise every access is checked.
+// SCV (FAST only): bit o set when operand o's 8 scale bytes of a row and K
+// step are contiguous (one 8-byte load); else they are 8 strided byte loads
+// (the W^T operand of 2D-scaled weights).
+template <int FMT, bool FAST, int SCV>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level(Params p) {
   extern __shared__ uint4 smem_raw[];
   Stage2* st = reinterpret_cast<Stage2*>(smem_raw);
@@ -159,49 +191,108 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level(Params p) {
   const int64_t lim[2] = {p.M, p.N};
   const int64_t base[2] = {m0, n0};
 
-  uint4 rc[2][4];        // staged codes: 4 chunks per operand per thread
-  uint32_t rs[2][8];     // staged scales (fp16 pairs): 8 per operand per thread
+  // Staging registers for the next K step.  Loaded values are kept raw and
+  // only masked/decoded when written to LDS, so no load has to be waited for
+  // before the MFMAs of the current step are issued.
+  uint4 rc[2][4];        // codes: 4 chunks per operand per thread
+  uint2 rs[2];           // scale bytes of row t: the step's 8 K-blocks
+  uint32_t valid[2];     // bit j: chunk j's row is inside the matrix; bit 4: row t is
 
   auto load_step = [&](int s) {
     const int64_t k0b = static_cast<int64_t>(s) * (kBK2 / 2);
+    if constexpr (FAST) {
+#pragma unroll
+      for (int o = 0; o < 2; ++o) {
+        const uint8_t* sp = p.scales[o] + ((base[o] + t) >> p.rg_shift[o]) * p.s_row[o] +
+                            static_cast<int64_t>(s) * 8 * p.s_kblk[o];
+        if ((SCV >> o) & 1) {
+          rs[o] = *reinterpret_cast<const uint2*>(sp);
+        } else {
+          const int64_t st = p.s_kblk[o];
+          rs[o] = make_uint2(sp[0] | (sp[st] << 8) | (sp[2 * st] << 16) | (sp[3 * st] << 24),
+                             sp[4 * st] | (sp[5 * st] << 8) | (sp[6 * st] << 16) |
+                                 (sp[7 * st] << 24));
+        }
+        valid[o] = 31u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c = t + kThreads * j;
+          rc[o][j] = *reinterpret_cast<const uint4*>(p.codes[o] + (base[o] + (c >> 2)) * p.ld[o] +
+                                                     k0b + (c & 3) * 16);
+        }
+      }
+      return;
+    }
+    const bool kfull = k0b + kBK2 / 2 <= row_bytes;
 #pragma unroll
     for (int o = 0; o < 2; ++o) {
+      // scales first: they are consumed first
+      const int64_t gr = base[o] + t;
+      const bool rv = gr < lim[o];
+      const uint8_t* sp = p.scales[o] + ((rv ? gr : lim[o] - 1) >> p.rg_shift[o]) * p.s_row[o] +
+                          static_cast<int64_t>(s) * 8 * p.s_kblk[o];
+      if (kfull && p.sc_vec[o]) {
+        rs[o] = *reinterpret_cast<const uint2*>(sp);
+      } else {
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) {
+          const uint32_t v =
+              (static_cast<int64_t>(s) * 8 + kb < kblocks) ? sp[kb * p.s_kblk[o]] : 0u;
+          if (kb < 4) lo |= v << (8 * kb);
+          else hi |= v << (8 * (kb - 4));
+        }
+        rs[o] = make_uint2(lo, hi);
+      }
+      uint32_t vb = rv ? 16u : 0u;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int c = t + kThreads * j;
-        const int row = c >> 2, q = c & 3;
-        const int64_t gr = base[o] + row;
-        rc[o][j] = gr < lim[o] ? load_codes16(p.codes[o] + gr * p.ld[o], k0b + q * 16, row_bytes,
-                                              p.vec16[o])
-                               : make_uint4(0u, 0u, 0u, 0u);
+        const int64_t r = base[o] + (c >> 2);
+        vb |= (r < lim[o] ? 1u : 0u) << j;
       }
+      valid[o] = vb;
+      if (kfull && p.vec16[o]) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int c = t + kThreads * j;
-        const int row = c >> 3, kb = c & 7;
-        const int64_t gr = base[o] + row, gk = static_cast<int64_t>(s) * 8 + kb;
-        uint32_t code = 0;
-        if (gr < lim[o] && gk < kblocks)
-          code = p.scales[o][(gr >> p.rg_shift[o]) * p.s_row[o] + gk * p.s_kblk[o]];
-        rs[o][j] = scale_half2<FMT>(code);
+        for (int j = 0; j < 4; ++j) {
+          const int c = t + kThreads * j;
+          const int64_t r = base[o] + (c >> 2);
+          const uint8_t* src = p.codes[o] + (r < lim[o] ? r : lim[o] - 1) * p.ld[o];
+          rc[o][j] = *reinterpret_cast<const uint4*>(src + k0b + (c & 3) * 16);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c = t + kThreads * j;
+          const int64_t r = base[o] + (c >> 2);
+          const uint8_t* src = p.codes[o] + (r < lim[o] ? r : lim[o] - 1) * p.ld[o];
+          rc[o][j] = load_codes16(src, k0b + (c & 3) * 16, row_bytes, p.vec16[o]);
+        }
       }
     }
   };
-  auto store_step = [&](Stage2& S) {
+  auto store_scales = [&](Stage2& S) {
+#pragma unroll
+    for (int o = 0; o < 2; ++o) {
+      const bool rv = valid[o] & 16u;
+      uint32_t h[8];
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) {
+        const uint32_t code = ((kb < 4 ? rs[o].x : rs[o].y) >> (8 * (kb & 3))) & 0xFFu;
+        h[kb] = rv ? scale_half2<FMT>(code) : 0u;
+      }
+      S.scales[o][0][t] = make_uint4(h[0], h[1], h[2], h[3]);
+      S.scales[o][1][t] = make_uint4(h[4], h[5], h[6], h[7]);
+    }
+  };
+  auto store_codes = [&](Stage2& S) {
 #pragma unroll
     for (int o = 0; o < 2; ++o) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int c = t + kThreads * j;
         const int row = c >> 2, q = c & 3;
-        S.codes[o][q][row ^ (q << 2)] = rc[o][j];
-      }
-      uint32_t* sc = reinterpret_cast<uint32_t*>(&S.scales[o][0][0]);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int c = t + kThreads * j;
-        const int row = c >> 3, kb = c & 7;
-        sc[((kb >> 2) * 256 + row) * 4 + (kb & 3)] = rs[o][j];
+        S.codes[o][q][row ^ (q << 2)] = (valid[o] >> j) & 1u ? rc[o][j] : make_uint4(0u, 0u, 0u, 0u);
       }
     }
   };
@@ -215,7 +306,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level(Params p) {
   const int i = lane & 31, h = lane >> 5;
   if (nsteps > 0) {
     load_step(0);
-    store_step(st[0]);
+    store_scales(st[0]);
+    store_codes(st[0]);
     __syncthreads();
   }
   for (int s = 0; s < nsteps; ++s) {
@@ -242,29 +334,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level(Params p) {
       b_raw[ni][4] = c1.x; b_raw[ni][5] = c1.y; b_raw[ni][6] = c1.z; b_raw[ni][7] = c1.w;
       b_sc[ni] = S.scales[1][h][row];
     }
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {     // 16 K-values per MFMA, one scale per 2 slices
-      half8 a_op[4], b_op[4];
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        const uint32_t sc = (ks >> 1) == 0 ? a_sc[mi].x : (ks >> 1) == 1 ? a_sc[mi].y
-                          : (ks >> 1) == 2 ? a_sc[mi].z : a_sc[mi].w;
-        a_op[mi] = dequant8(a_raw[mi][ks], sc);
-      }
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        const uint32_t sc = (ks >> 1) == 0 ? b_sc[ni].x : (ks >> 1) == 1 ? b_sc[ni].y
-                          : (ks >> 1) == 2 ? b_sc[ni].z : b_sc[ni].w;
-        b_op[ni] = dequant8(b_raw[ni][ks], sc);
-      }
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_op[mi], b_op[ni], acc[mi][ni],
-                                                               0, 0, 0);
-    }
-    if (more) store_step(st[(s + 1) & 1]);
+    two_level_slice<0>(acc, a_raw, b_raw, a_sc, b_sc);
+    two_level_slice<1>(acc, a_raw, b_raw, a_sc, b_sc);
+    two_level_slice<2>(acc, a_raw, b_raw, a_sc, b_sc);
+    two_level_slice<3>(acc, a_raw, b_raw, a_sc, b_sc);
+    if (more) store_scales(st[(s + 1) & 1]);
+    two_level_slice<4>(acc, a_raw, b_raw, a_sc, b_sc);
+    two_level_slice<5>(acc, a_raw, b_raw, a_sc, b_sc);
+    two_level_slice<6>(acc, a_raw, b_raw, a_sc, b_sc);
+    two_level_slice<7>(acc, a_raw, b_raw, a_sc, b_sc);
+    if (more) store_codes(st[(s + 1) & 1]);
     __syncthreads();
   }
 
@@ -318,6 +397,7 @@ __device__ __forceinline__ void mx_slice(const StageX& S, floatx16 (&acc)[4][4],
           static_cast<int>(b_sc[ni]));
 }
 
+template <bool FAST, int SCV>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(Params p) {
   extern __shared__ uint4 smem_raw[];
   StageX* st = reinterpret_cast<StageX*>(smem_raw);
@@ -332,35 +412,80 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(Params p) {
   const int64_t base[2] = {m0, n0};
 
   uint4 rc[2][4];        // staged codes: 4 chunks (one MXFP4 block each) per operand
-  uint32_t rs[2][4];     // their E8M0 scales
+  uint32_t rs[2];        // E8M0 scales of row t for the step's 4 blocks
+  uint32_t valid[2];     // bit j: chunk j's row is inside the matrix; bit 4: row t is
 
   auto load_step = [&](int s) {
     const int64_t k0b = static_cast<int64_t>(s) * (kBKX / 2);
+    if constexpr (FAST) {
+#pragma unroll
+      for (int o = 0; o < 2; ++o) {
+        const uint8_t* sp = p.scales[o] + (base[o] + t) * p.s_row[o] +
+                            static_cast<int64_t>(s) * 4 * p.s_kblk[o];
+        if ((SCV >> o) & 1) {
+          rs[o] = *reinterpret_cast<const uint32_t*>(sp);
+        } else {
+          const int64_t st = p.s_kblk[o];
+          rs[o] = sp[0] | (sp[st] << 8) | (sp[2 * st] << 16) | (sp[3 * st] << 24);
+        }
+        valid[o] = 31u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c = t + kThreads * j;
+          rc[o][j] = *reinterpret_cast<const uint4*>(p.codes[o] + (base[o] + (c >> 2)) * p.ld[o] +
+                                                     k0b + (c & 3) * 16);
+        }
+      }
+      return;
+    }
+    const bool kfull = (static_cast<int64_t>(s) + 1) * 4 <= kblocks;
 #pragma unroll
     for (int o = 0; o < 2; ++o) {
+      const int64_t gr = base[o] + t;
+      const bool rv = gr < lim[o];
+      const uint8_t* sp = p.scales[o] + (rv ? gr : lim[o] - 1) * p.s_row[o] +
+                          static_cast<int64_t>(s) * 4 * p.s_kblk[o];
+      if (kfull && p.sc_vec[o]) {
+        rs[o] = *reinterpret_cast<const uint32_t*>(sp);
+      } else {
+        uint32_t w = 0;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+          if (static_cast<int64_t>(s) * 4 + kb < kblocks)
+            w |= static_cast<uint32_t>(sp[kb * p.s_kblk[o]]) << (8 * kb);
+        rs[o] = w;
+      }
+      uint32_t vb = rv ? 16u : 0u;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int c = t + kThreads * j;
-        const int row = c >> 2, q = c & 3;
-        const int64_t gr = base[o] + row, gk = static_cast<int64_t>(s) * 4 + q;
-        const bool ok = gr < lim[o] && gk < kblocks;   // K % 32 == 0: a chunk is all or nothing
-        rc[o][j] = ok ? *reinterpret_cast<const uint4*>(p.codes[o] + gr * p.ld[o] + k0b + q * 16)
-                      : make_uint4(0u, 0u, 0u, 0u);
-        rs[o][j] = ok ? p.scales[o][gr * p.s_row[o] + gk * p.s_kblk[o]] : 0u;
+        const int64_t r = base[o] + (c >> 2);
+        vb |= (r < lim[o] ? 1u : 0u) << j;
+      }
+      valid[o] = vb;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = t + kThreads * j;
+        const int64_t r = base[o] + (c >> 2);
+        const int q = c & 3;
+        const uint8_t* src = p.codes[o] + (r < lim[o] ? r : lim[o] - 1) * p.ld[o] + k0b + q * 16;
+        // K % 32 == 0: a 16-byte chunk is one whole MXFP4 block or absent
+        if (kfull) rc[o][j] = *reinterpret_cast<const uint4*>(src);
+        else rc[o][j] = (static_cast<int64_t>(s) * 4 + q < kblocks)
+                            ? *reinterpret_cast<const uint4*>(src) : make_uint4(0u, 0u, 0u, 0u);
       }
     }
   };
   auto store_step = [&](StageX& S) {
 #pragma unroll
     for (int o = 0; o < 2; ++o) {
-      uint8_t* sc = reinterpret_cast<uint8_t*>(&S.scales[o][0]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int c = t + kThreads * j;
         const int row = c >> 2, q = c & 3;
-        S.codes[o][q][row ^ (q << 2)] = rc[o][j];
-        sc[row * 4 + q] = static_cast<uint8_t>(rs[o][j]);
+        S.codes[o][q][row ^ (q << 2)] = (valid[o] >> j) & 1u ? rc[o][j] : make_uint4(0u, 0u, 0u, 0u);
       }
+      S.scales[o][t] = (valid[o] & 16u) ? rs[o] : 0u;
     }
   };
 
@@ -398,6 +523,35 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx(Params p) {
 
 namespace fp4lib {
 
+// LDS beyond the default 64 KiB must be opted into once per kernel and
+// device; remember which (device, kernel) pairs are done (setting it twice
+// is harmless, so a racing first call is too).
+static hipError_t launch_kernel(void (*kernel)(Params), size_t lds, int grid, hipStream_t s,
+                                const Params& p) {
+  constexpr int kSlots = 64;
+  static const void* done_fn[kSlots];
+  static int done_dev[kSlots];
+  static int n_done = 0;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  bool found = false;
+  for (int i = 0; i < n_done && !found; ++i)
+    found = done_fn[i] == reinterpret_cast<const void*>(kernel) && done_dev[i] == dev;
+  if (!found) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    if (n_done < kSlots) {
+      done_fn[n_done] = reinterpret_cast<const void*>(kernel);
+      done_dev[n_done] = dev;
+      ++n_done;
+    }
+  }
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), lds, s, p);
+  return hipSuccess;
+}
+
 hipError_t launch_gemm(int format, const GemmOperand& A, const GemmOperand& B, int64_t M,
                        int64_t N, int64_t K, float* D, int64_t ldd, int accumulate,
                        hipStream_t s) {
@@ -412,6 +566,10 @@ hipError_t launch_gemm(int format, const GemmOperand& A, const GemmOperand& B, i
     p.rg_shift[o] = ops[o]->row_group == 16 ? 4 : 0;
     p.vec16[o] = (ops[o]->ld_codes % 16 == 0) &&
                  (reinterpret_cast<uintptr_t>(ops[o]->codes) % 16 == 0);
+    // 8 (two-level) or 4 (MXFP4) scale bytes per row and K step
+    const int sv = format == FP4_MXFP4 ? 4 : 8;
+    p.sc_vec[o] = ops[o]->s_kblk == 1 && ops[o]->s_row % sv == 0 &&
+                  reinterpret_cast<uintptr_t>(ops[o]->scales) % sv == 0;
     p.s_dec[o] = format == FP4_MXFP4 ? nullptr : ops[o]->s_dec;
   }
   p.D = D;
@@ -424,36 +582,28 @@ hipError_t launch_gemm(int format, const GemmOperand& A, const GemmOperand& B, i
   p.tiles_n = static_cast<int>((N + kBN - 1) / kBN);
   const int grid = p.tiles_m * p.tiles_n;
   if (grid == 0) return hipSuccess;
-  // LDS beyond the default 64 KiB must be opted into once per kernel
-  static bool lds_set[3] = {false, false, false};
-  hipError_t e = hipSuccess;
+  const bool fast = M % kBM == 0 && N % kBN == 0 && p.vec16[0] && p.vec16[1] &&
+                    K % (format == FP4_MXFP4 ? kBKX : kBK2) == 0;
+  const int scv = (p.sc_vec[0] ? 1 : 0) | (p.sc_vec[1] ? 2 : 0);
+  void (*kern)(Params) = nullptr;
+  size_t lds;
   if (format == FP4_MXFP4) {
-    const size_t lds = 2 * sizeof(StageX);
-    if (!lds_set[2]) {
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_mx),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-      lds_set[2] = e == hipSuccess;
-    }
-    if (e == hipSuccess) hipLaunchKernelGGL(k_gemm_mx, dim3(grid), dim3(kThreads), lds, s, p);
+    lds = 2 * sizeof(StageX);
+    constexpr void (*mx[4])(Params) = {k_gemm_mx<true, 0>, k_gemm_mx<true, 1>,
+                                       k_gemm_mx<true, 2>, k_gemm_mx<true, 3>};
+    kern = fast ? mx[scv] : k_gemm_mx<false, 0>;
   } else if (format == FP4_NVFP4) {
-    const size_t lds = 2 * sizeof(Stage2);
-    if (!lds_set[0]) {
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_two_level<kNV>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-      lds_set[0] = e == hipSuccess;
-    }
-    if (e == hipSuccess)
-      hipLaunchKernelGGL(k_gemm_two_level<kNV>, dim3(grid), dim3(kThreads), lds, s, p);
+    lds = 2 * sizeof(Stage2);
+    constexpr void (*nv[4])(Params) = {k_gemm_two_level<kNV, true, 0>, k_gemm_two_level<kNV, true, 1>,
+                                       k_gemm_two_level<kNV, true, 2>, k_gemm_two_level<kNV, true, 3>};
+    kern = fast ? nv[scv] : k_gemm_two_level<kNV, false, 0>;
   } else {
-    const size_t lds = 2 * sizeof(Stage2);
-    if (!lds_set[1]) {
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_two_level<kUE>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-      lds_set[1] = e == hipSuccess;
-    }
-    if (e == hipSuccess)
-      hipLaunchKernelGGL(k_gemm_two_level<kUE>, dim3(grid), dim3(kThreads), lds, s, p);
+    lds = 2 * sizeof(Stage2);
+    constexpr void (*ue[4])(Params) = {k_gemm_two_level<kUE, true, 0>, k_gemm_two_level<kUE, true, 1>,
+                                       k_gemm_two_level<kUE, true, 2>, k_gemm_two_level<kUE, true, 3>};
+    kern = fast ? ue[scv] : k_gemm_two_level<kUE, false, 0>;
   }
+  const hipError_t e = launch_kernel(kern, lds, grid, s, p);
   if (e != hipSuccess) return e;
   return hipGetLastError();
 }
