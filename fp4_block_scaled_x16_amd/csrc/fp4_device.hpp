@@ -155,6 +155,21 @@ __device__ __forceinline__ uint32_t e2m1_rne(float y) {
   return sign | mag;
 }
 
+// Two E2M1 codes by round to nearest even, saturating at 6, written into
+// byte SEL of `word` (y0 in the low nibble).  gfx950's FP4 conversion with a
+// unit scale computes exactly e2m1_rne: checked on all 2^32 - 2^24 + 2
+// non-NaN fp32 inputs.
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1_rne_pair(uint32_t word, float y0, float y1) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, y0, y1, 1.0f, SEL);
+}
+
+// Number of nonzero magnitudes among the 8 codes of a packed word: adding 7
+// to a nonzero 3-bit magnitude carries into the nibble's sign position.
+__device__ __forceinline__ uint32_t nonzero_codes(uint32_t word) {
+  return __builtin_popcount(((word & 0x77777777u) + 0x77777777u) & 0x88888888u);
+}
+
 // Stochastic E2M1 rounding (§4.4): lo = largest magnitude <= |y|, hi the
 // next; round up iff r16 < 65536 (|y| - lo) / (hi - lo), computed exactly
 // as (|y| - lo) * (65536 / (hi - lo)).  |y| >= 6 gives 6.

@@ -89,22 +89,45 @@ __device__ __forceinline__ uint4 load_codes16(const uint8_t* row, int64_t off, i
   return make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
+// The MFMAs are issued as C^T = B A^T (B fragment in the "A" slot), so the
+// 16 accumulators of a lane hold one output row m and, for each group g of
+// 4, the 4 consecutive columns 8g + 4h .. +3 of a 32 x 32 tile: the
+// epilogue writes 16 bytes per store.
 __device__ __forceinline__ void epilogue(const Params& p, floatx16 (&acc)[4][4], float scale,
                                          int64_t m0, int64_t n0, int wm, int wn, int lane) {
   const int i = lane & 31, h = lane >> 5;
+  const bool vec = (p.ldd & 3) == 0 && (reinterpret_cast<uintptr_t>(p.D) & 15) == 0;
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
+    const int64_t row = m0 + wm * 128 + mi * 32 + i;
+    if (row >= p.M) continue;
+    float* drow = p.D + row * p.ldd;
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) {
-      const int64_t col = n0 + wn * 128 + ni * 32 + i;
-      if (col >= p.N) continue;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = m0 + wm * 128 + mi * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-        if (row < p.M) {
-          float* dst = p.D + row * p.ldd + col;
-          const float r = acc[mi][ni][v] * scale;
-          *dst = p.accumulate ? *dst + r : r;
+      for (int g = 0; g < 4; ++g) {
+        const int64_t col = n0 + wn * 128 + ni * 32 + 8 * g + 4 * h;
+        float r[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = acc[mi][ni][4 * g + e] * scale;
+        if (vec && col + 3 < p.N) {
+          float4* dst = reinterpret_cast<float4*>(drow + col);
+          if (p.accumulate) {
+            const float4 o = *dst;
+            r[0] += o.x;
+            r[1] += o.y;
+            r[2] += o.z;
+            r[3] += o.w;
+          }
+          *dst = make_float4(r[0], r[1], r[2], r[3]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (col + e < p.N) {
+              float* d = drow + col + e;
+              *d = p.accumulate ? *d + r[e] : r[e];
+            }
+          }
         }
       }
     }
@@ -115,11 +138,13 @@ __device__ __forceinline__ void epilogue(const Params& p, floatx16 (&acc)[4][4],
 constexpr int kBK2 = 128;   // K per step: 64 code bytes and 8 scales per row
 
 // fp16 copy of a block scale, replicated in both halves for v_pk_mul_f16.
+// E4M3 decodes with the hardware FP8 convert (exact, subnormals included);
+// UE5M3 is decoded arithmetically and pre-multiplied by 2^-5 (exact).
 template <int FMT>
 __device__ __forceinline__ uint32_t scale_half2(uint32_t code) {
   float s;
-  if constexpr (FMT == kNV) s = scale_m3_decode<7>(code);
-  else s = scale_m3_decode<15>(code) * 0x1p-5f;      // exact: keeps products in fp16 range
+  if constexpr (FMT == kNV) s = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(code), 0);
+  else s = scale_m3_decode<15>(code) * 0x1p-5f;
   const _Float16 hs = static_cast<_Float16>(s);        // exact
   const uint32_t b = __builtin_bit_cast(uint16_t, hs);
   return b | (b << 16);
@@ -145,37 +170,58 @@ struct Stage2 {
   uint4 scales[2][2][256];
 };
 
-// One MFMA K slice (16 K-values) of the wave's 4 x 4 tiles: dequantize the
-// lane's A and B fragments for slice KS, then 16 MFMAs.
+// Fragments of one MFMA K slice (16 K-values): lane half h holds the slice's
+// 8 K-values of its row for each of the wave's 4 A and 4 B tiles.
+struct Frag {
+  half8 a[4], b[4];
+};
+
 template <int KS>
-__device__ __forceinline__ void two_level_slice(floatx16 (&acc)[4][4], const uint32_t (&a_raw)[4][8],
-                                                const uint32_t (&b_raw)[4][8], const uint4 (&a_sc)[4],
-                                                const uint4 (&b_sc)[4]) {
+__device__ __forceinline__ void dequant_slice(Frag& f, const uint32_t (&a_raw)[4][8],
+                                              const uint32_t (&b_raw)[4][8], const uint4 (&a_sc)[4],
+                                              const uint4 (&b_sc)[4]) {
   constexpr int W = KS >> 1;     // scale word: one 16-element block per two slices
-  half8 a_op[4], b_op[4];
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
     const uint32_t sc = W == 0 ? a_sc[mi].x : W == 1 ? a_sc[mi].y : W == 2 ? a_sc[mi].z : a_sc[mi].w;
-    a_op[mi] = dequant8(a_raw[mi][KS], sc);
+    f.a[mi] = dequant8(a_raw[mi][KS], sc);
   }
 #pragma unroll
   for (int ni = 0; ni < 4; ++ni) {
     const uint32_t sc = W == 0 ? b_sc[ni].x : W == 1 ? b_sc[ni].y : W == 2 ? b_sc[ni].z : b_sc[ni].w;
-    b_op[ni] = dequant8(b_raw[ni][KS], sc);
+    f.b[ni] = dequant8(b_raw[ni][KS], sc);
   }
+}
+
+__device__ __forceinline__ void mfma_slice(floatx16 (&acc)[4][4], const Frag& f) {
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni)
-      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_op[mi], b_op[ni], acc[mi][ni], 0, 0, 0);
+      acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[ni], f.a[mi], acc[mi][ni], 0, 0, 0);
 }
 
-// FAST: M, N multiples of 256, K a multiple of 128 and code rows 16-byte
-// aligned -- no bounds checks, straight-line loads (the compiler then keeps
-// them in flight across the MFMAs).  Otherwise every access is checked.
-// SCV (FAST only): bit o set when operand o's 8 scale bytes of a row and K
-// step are contiguous (one 8-byte load); else they are 8 strided byte loads
-// (the W^T operand of 2D-scaled weights).
+// Scheduling hint for one slice: alternate one MFMA with four VALU ops so
+// the next slice's dequantization issues while this slice's MFMAs run.
+__device__ __forceinline__ void interleave_slice() {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
+  }
+}
+
+// Slice KS of a step: MFMAs on `cur` while dequantizing slice KS+1 into `nxt`.
+template <int KS>
+__device__ __forceinline__ void pipelined_slice(floatx16 (&acc)[4][4], const Frag& cur, Frag& nxt,
+                                                const uint32_t (&a_raw)[4][8],
+                                                const uint32_t (&b_raw)[4][8],
+                                                const uint4 (&a_sc)[4], const uint4 (&b_sc)[4]) {
+  if constexpr (KS + 1 < 8) dequant_slice<KS + 1>(nxt, a_raw, b_raw, a_sc, b_sc);
+  mfma_slice(acc, cur);
+  interleave_slice();
+}
+
 template <int FMT, bool FAST, int SCV>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level(Params p) {
   extern __shared__ uint4 smem_raw[];
@@ -195,7 +241,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level(Params p) {
   // only masked/decoded when written to LDS, so no load has to be waited for
   // before the MFMAs of the current step are issued.
   uint4 rc[2][4];        // codes: 4 chunks per operand per thread
-  uint2 rs[2];           // scale bytes of row t: the step's 8 K-blocks
+  uint2 rs[2];           // scale bytes of row t: the step's 8 K-blocks (packed)
+  uint32_t rsb[2][8];    // the same as 8 separate bytes (strided scale rows)
   uint32_t valid[2];     // bit j: chunk j's row is inside the matrix; bit 4: row t is
 
   auto load_step = [&](int s) {
@@ -208,10 +255,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level(Params p) {
         if ((SCV >> o) & 1) {
           rs[o] = *reinterpret_cast<const uint2*>(sp);
         } else {
+          // 8 independent byte loads, used only when the scales are stored
           const int64_t st = p.s_kblk[o];
-          rs[o] = make_uint2(sp[0] | (sp[st] << 8) | (sp[2 * st] << 16) | (sp[3 * st] << 24),
-                             sp[4 * st] | (sp[5 * st] << 8) | (sp[6 * st] << 16) |
-                                 (sp[7 * st] << 24));
+#pragma unroll
+          for (int kb = 0; kb < 8; ++kb) rsb[o][kb] = sp[kb * st];
         }
         valid[o] = 31u;
 #pragma unroll
@@ -275,10 +322,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level(Params p) {
 #pragma unroll
     for (int o = 0; o < 2; ++o) {
       const bool rv = valid[o] & 16u;
+      const bool bytes = FAST && !((SCV >> o) & 1);
       uint32_t h[8];
 #pragma unroll
       for (int kb = 0; kb < 8; ++kb) {
-        const uint32_t code = ((kb < 4 ? rs[o].x : rs[o].y) >> (8 * (kb & 3))) & 0xFFu;
+        const uint32_t code = bytes ? rsb[o][kb]
+                                    : ((kb < 4 ? rs[o].x : rs[o].y) >> (8 * (kb & 3))) & 0xFFu;
         h[kb] = rv ? scale_half2<FMT>(code) : 0u;
       }
       S.scales[o][0][t] = make_uint4(h[0], h[1], h[2], h[3]);
@@ -334,15 +383,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level(Params p) {
       b_raw[ni][4] = c1.x; b_raw[ni][5] = c1.y; b_raw[ni][6] = c1.z; b_raw[ni][7] = c1.w;
       b_sc[ni] = S.scales[1][h][row];
     }
-    two_level_slice<0>(acc, a_raw, b_raw, a_sc, b_sc);
-    two_level_slice<1>(acc, a_raw, b_raw, a_sc, b_sc);
-    two_level_slice<2>(acc, a_raw, b_raw, a_sc, b_sc);
-    two_level_slice<3>(acc, a_raw, b_raw, a_sc, b_sc);
+    Frag f0, f1;
+    dequant_slice<0>(f0, a_raw, b_raw, a_sc, b_sc);
+    pipelined_slice<0>(acc, f0, f1, a_raw, b_raw, a_sc, b_sc);
+    pipelined_slice<1>(acc, f1, f0, a_raw, b_raw, a_sc, b_sc);
+    pipelined_slice<2>(acc, f0, f1, a_raw, b_raw, a_sc, b_sc);
+    pipelined_slice<3>(acc, f1, f0, a_raw, b_raw, a_sc, b_sc);
     if (more) store_scales(st[(s + 1) & 1]);
-    two_level_slice<4>(acc, a_raw, b_raw, a_sc, b_sc);
-    two_level_slice<5>(acc, a_raw, b_raw, a_sc, b_sc);
-    two_level_slice<6>(acc, a_raw, b_raw, a_sc, b_sc);
-    two_level_slice<7>(acc, a_raw, b_raw, a_sc, b_sc);
+    pipelined_slice<4>(acc, f0, f1, a_raw, b_raw, a_sc, b_sc);
+    pipelined_slice<5>(acc, f1, f0, a_raw, b_raw, a_sc, b_sc);
+    pipelined_slice<6>(acc, f0, f1, a_raw, b_raw, a_sc, b_sc);
+    pipelined_slice<7>(acc, f1, f0, a_raw, b_raw, a_sc, b_sc);
     if (more) store_codes(st[(s + 1) & 1]);
     __syncthreads();
   }
@@ -393,8 +444,8 @@ __device__ __forceinline__ void mx_slice(const StageX& S, floatx16 (&acc)[4][4],
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni)
       acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          a_op[mi], b_op[ni], acc[mi][ni], 4, 4, KS, static_cast<int>(a_sc[mi]), KS,
-          static_cast<int>(b_sc[ni]));
+          b_op[ni], a_op[mi], acc[mi][ni], 4, 4, KS, static_cast<int>(b_sc[ni]), KS,
+          static_cast<int>(a_sc[mi]));
 }
 
 template <bool FAST, int SCV>

@@ -21,6 +21,12 @@ namespace {
 
 constexpr int kThreads = 256;       // tiled kernels (colwise, 2D)
 constexpr int kStream = 512;        // streaming kernels (amax, rowwise, dequant, RHT)
+#ifndef FP4_ROW_WG_PER_CU
+#define FP4_ROW_WG_PER_CU 1
+#endif
+#ifndef FP4_TILE_WG_PER_CU
+#define FP4_TILE_WG_PER_CU 2
+#endif
 
 // Same-address global atomics serialize (about 12 ns each on MI355X once
 // more than a few hundred arrive), so every kernel runs a persistent grid
@@ -69,29 +75,47 @@ __device__ __forceinline__ void unpack8(const uint4& q, float* v) {
 // Quantize BS values (already in fp32, in block order) with the encode
 // scale; returns BS/8 packed code words (element i at bits 4 (i % 8) of
 // word i / 8).  `idx0` is the output-layout index of element 0 (SR only).
+// Counters: cnt[3] += #(|y| > 6); cnt[4] += #(x != 0) - #(code != 0), which
+// is the number of nonzero inputs coded as zero (a zero input always codes
+// to zero).  The element tests are wave ballots counted on the scalar unit,
+// so they are accumulated per wave (in lane 0's cnt) rather than per lane.
 template <int BS, int RND, bool CNT>
 __device__ __forceinline__ void encode_block(const float* v, float s_enc_l, uint64_t idx0,
                                              uint64_t seed, uint64_t offset, uint32_t* words,
                                              uint32_t (&cnt)[5]) {
-#pragma unroll
+  uint32_t sat = 0, nzx = 0, nzc = 0;
+  // SR on 32-element blocks: one Philox group at a time keeps registers low
+  constexpr int kGroupUnroll = (RND == FP4_SR && BS > 16) ? 1 : BS / 8;
+#pragma unroll kGroupUnroll
   for (int q = 0; q < BS / 8; ++q) {
-    U4 rw{0, 0, 0, 0};
-    if constexpr (RND == FP4_SR) rw = sr_words((idx0 >> 3) + q, seed, offset);
-    uint32_t word = 0;
+    float y[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float xv = v[q * 8 + i];
-      const float y = xv * s_enc_l;
-      uint32_t c;
-      if constexpr (RND == FP4_SR) c = e2m1_sr(y, sr_bits(rw, i));
-      else c = e2m1_rne(y);
-      word |= c << (4 * i);
-      if constexpr (CNT) {
-        cnt[3] += fabsf(y) > 6.0f;
-        cnt[4] += (xv != 0.0f) & ((c & 7u) == 0u);
-      }
+    for (int i = 0; i < 8; ++i) y[i] = v[q * 8 + i] * s_enc_l;
+    uint32_t word = 0;
+    if constexpr (RND == FP4_SR) {
+      const U4 rw = sr_words((idx0 >> 3) + q, seed, offset);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) word |= e2m1_sr(y[i], sr_bits(rw, i)) << (4 * i);
+    } else {
+      word = e2m1_rne_pair<0>(word, y[0], y[1]);
+      word = e2m1_rne_pair<1>(word, y[2], y[3]);
+      word = e2m1_rne_pair<2>(word, y[4], y[5]);
+      word = e2m1_rne_pair<3>(word, y[6], y[7]);
     }
     words[q] = word;
+    if constexpr (CNT) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        sat += __builtin_popcountll(__builtin_amdgcn_ballot_w64(fabsf(y[i]) > 6.0f));
+        nzx += __builtin_popcountll(__builtin_amdgcn_ballot_w64(v[q * 8 + i] != 0.0f));
+      }
+      nzc += nonzero_codes(word);
+    }
+  }
+  if constexpr (CNT) {
+    const bool lead = (threadIdx.x & 63) == 0;
+    cnt[3] += lead ? sat : 0u;
+    cnt[4] += (lead ? nzx : 0u) - nzc;
   }
 }
 
@@ -140,23 +164,34 @@ __global__ __launch_bounds__(kStream) void k_amax(const uint16_t* __restrict__ x
   uint64_t i = static_cast<uint64_t>(blockIdx.x) * kStream + threadIdx.x;
   uint64_t r = cpr ? i / cpr : 0, j = cpr ? i - r * cpr : 0;
   const uint64_t sr = cpr ? stride / cpr : 0, sj = cpr ? stride - sr * cpr : 0;
+  // two 16-byte chunks per thread and iteration, loads issued together
   uint32_t m = 0;
-  for (; i < n; i += stride) {
-    const uint4 q = *reinterpret_cast<const uint4*>(x + r * ld + j * 8);
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      // bf16 -> |fp32| bits: the sign is dropped, the rest widened
-      m = max(m, (w[k] << 16) & 0x7FFF0000u);
-      m = max(m, w[k] & 0x7FFF0000u);
-    }
+  for (; i < n; i += 2 * stride) {
+    const uint64_t r1 = r, j1 = j;
     r += sr;
     j += sj;
     if (j >= cpr) {
       j -= cpr;
       ++r;
     }
+    const bool two = i + stride < n;
+    const uint4 q0 = *reinterpret_cast<const uint4*>(x + r1 * ld + j1 * 8);
+    const uint4 q1 = *reinterpret_cast<const uint4*>(x + (two ? r : r1) * ld + (two ? j : j1) * 8);
+    r += sr;
+    j += sj;
+    if (j >= cpr) {
+      j -= cpr;
+      ++r;
+    }
+    // |bf16| as unsigned 16-bit halves; the max of magnitudes is monotone
+    const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t a = w[k] & 0x7FFF7FFFu;
+      m = max(m, max(a & 0xFFFFu, a >> 16));
+    }
   }
+  m <<= 16;   // fp32 bits of the largest magnitude
   flush_max<kStream>(m, out);
 }
 
@@ -208,11 +243,29 @@ __global__ __launch_bounds__(kStream) void k_quant_row(
   uint64_t r = bpr ? i / bpr : 0, j = bpr ? i - r * bpr : 0;
   const uint64_t sr = bpr ? stride / bpr : 0, sj = bpr ? stride - sr * bpr : 0;
   uint32_t cnt[5] = {0, 0, 0, 0, 0};
-  for (; i < n; i += stride) {
+  // The next block's loads are issued before the current block is encoded;
+  // past the end they re-read a valid block, so no branch guards them.
+  uint4 q[BS / 8];
+  if (i < n) {
     const uint4* src = reinterpret_cast<const uint4*>(x + r * ld + j * BS);
-    uint4 q[BS / 8];
 #pragma unroll
     for (int k = 0; k < BS / 8; ++k) q[k] = src[k];
+  }
+  for (; i < n; i += stride) {
+    const uint64_t r_cur = r, j_cur = j;
+    r += sr;
+    j += sj;
+    if (j >= bpr) {
+      j -= bpr;
+      ++r;
+    }
+    const bool has_next = i + stride < n;
+    const uint4* nsrc = reinterpret_cast<const uint4*>(x + (has_next ? r : r_cur) * ld +
+                                                       (has_next ? j : j_cur) * BS);
+    uint4 nq[BS / 8];
+#pragma unroll
+    for (int k = 0; k < BS / 8; ++k) nq[k] = nsrc[k];
+
     float v[BS];
 #pragma unroll
     for (int k = 0; k < BS / 8; ++k) unpack8(q[k], v + 8 * k);
@@ -222,21 +275,17 @@ __global__ __launch_bounds__(kStream) void k_quant_row(
     float s_enc_l;
     const uint32_t sc = scale_for_block<FMT>(amax_b, s_enc_g, s_dec_g, s_enc_l, cnt);
     uint32_t words[BS / 8];
-    encode_block<BS, RND, CNT>(v, s_enc_l, r * static_cast<uint64_t>(cols) + j * BS, seed,
+    encode_block<BS, RND, CNT>(v, s_enc_l, r_cur * static_cast<uint64_t>(cols) + j_cur * BS, seed,
                                offset, words, cnt);
-    uint8_t* dst = codes + r * (static_cast<uint64_t>(cols) >> 1) + j * (BS / 2);
+    uint8_t* dst = codes + r_cur * (static_cast<uint64_t>(cols) >> 1) + j_cur * (BS / 2);
     if constexpr (BS == 16) {
       *reinterpret_cast<uint2*>(dst) = make_uint2(words[0], words[1]);
     } else {
       *reinterpret_cast<uint4*>(dst) = make_uint4(words[0], words[1], words[2], words[3]);
     }
-    scales[r * bpr + j] = static_cast<uint8_t>(sc);
-    r += sr;
-    j += sj;
-    if (j >= bpr) {
-      j -= bpr;
-      ++r;
-    }
+    scales[r_cur * bpr + j_cur] = static_cast<uint8_t>(sc);
+#pragma unroll
+    for (int k = 0; k < BS / 8; ++k) q[k] = nq[k];
   }
   if constexpr (CNT) flush_counters<kStream>(cnt, counters);
 }
@@ -293,20 +342,16 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
     const int64_t col = c0 + 2 * pair;
     const int64_t row = r0 + grp * BS;
     if (col < cols && row < rows) {
-      float a[BS], b[BS];
-#pragma unroll
-      for (int k = 0; k < BS; ++k) {
-        const uint32_t w = tile[(grp * BS + k) * LDW + pair];
-        a[k] = bf16_to_f32(w & 0xFFFFu);
-        b[k] = bf16_to_f32(w >> 16);
-      }
-      if constexpr (RHT) {
-        rht16(*reinterpret_cast<float(*)[16]>(a), signs);
-        rht16(*reinterpret_cast<float(*)[16]>(b), signs);
-      }
-#pragma unroll
+      // the two columns one after the other: half the live registers
+#pragma unroll 1
       for (int h = 0; h < 2; ++h) {
-        const float* v = h ? b : a;
+        float v[BS];
+#pragma unroll
+        for (int k = 0; k < BS; ++k) {
+          const uint32_t w = tile[(grp * BS + k) * LDW + pair];
+          v[k] = bf16_to_f32(h ? (w >> 16) : (w & 0xFFFFu));
+        }
+        if constexpr (RHT) rht16(*reinterpret_cast<float(*)[16]>(v), signs);
         const int64_t c = col + h;
         float amax_b = 0.0f;
 #pragma unroll
@@ -558,7 +603,8 @@ template <int FMT, int RND, bool CNT>
 static void row_launch(const QuantArgs& a, hipStream_t s) {
   constexpr int BS = FMT == kMX ? 32 : 16;
   const uint64_t n = static_cast<uint64_t>(a.rows) * static_cast<uint64_t>(a.cols / BS);
-  hipLaunchKernelGGL((k_quant_row<FMT, RND, CNT>), dim3(grid_for(n, 1)), dim3(kStream), 0, s,
+  hipLaunchKernelGGL((k_quant_row<FMT, RND, CNT>), dim3(grid_for(n, FP4_ROW_WG_PER_CU)),
+                     dim3(kStream), 0, s,
                      a.x, a.rows, a.cols, a.ld, a.codes, a.scales, a.amax, a.target, a.s_dec,
                      a.seed, a.offset, a.counters);
 }
@@ -586,7 +632,7 @@ template <int FMT, int RND, bool RHT, bool CNT>
 static void col_launch(const QuantArgs& a, hipStream_t s) {
   constexpr int BS = FMT == kMX ? 32 : 16;
   const int64_t tiles = ((a.rows + 8 * BS - 1) / (8 * BS)) * ((a.cols + 63) / 64);
-  const int64_t cap = static_cast<int64_t>(device_cu_count()) * 2;
+  const int64_t cap = static_cast<int64_t>(device_cu_count()) * FP4_TILE_WG_PER_CU;
   const int grid = static_cast<int>(tiles < cap ? (tiles > 0 ? tiles : 1) : cap);
   hipLaunchKernelGGL((k_quant_col<FMT, RND, RHT, CNT>), dim3(grid), dim3(kThreads), 0, s, a.x,
                      a.rows, a.cols, a.ld, a.codes, a.scales, a.amax, a.target, a.s_dec, a.seed,
@@ -625,7 +671,7 @@ hipError_t launch_quant_col(const QuantArgs& a, hipStream_t s) {
 template <int FMT, bool CNT>
 static void q2d_launch(const QuantArgs& a, hipStream_t s) {
   const int64_t regions = ((a.rows + 63) / 64) * ((a.cols + 63) / 64);
-  const int64_t cap = static_cast<int64_t>(device_cu_count()) * 2;
+  const int64_t cap = static_cast<int64_t>(device_cu_count()) * FP4_TILE_WG_PER_CU;
   const int grid = static_cast<int>(regions < cap ? (regions > 0 ? regions : 1) : cap);
   hipLaunchKernelGGL((k_quant_2d<FMT, CNT>), dim3(grid), dim3(kThreads), 0, s, a.x, a.rows,
                      a.cols, a.ld, a.codes, a.scales, a.emit_transpose ? a.codes_t : nullptr,

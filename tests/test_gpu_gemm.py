@@ -145,22 +145,29 @@ def test_gemm_zero_operand():
     assert torch.count_nonzero(d).item() == 0
 
 
-def test_gemm_ue5m3_tiny_scales():
-    # Blocks 2^-23 below the tensor amax get UE5M3 scales near 2^-17; with the
-    # 2^-5 shift their fp16 operands are subnormal.  The MFMA must use them.
+@pytest.mark.parametrize("fmt,rel", [("ue5m3", 2.0 ** -23), ("nvfp4", 2.0 ** -17)])
+def test_gemm_tiny_scales(fmt, rel):
+    # Blocks far below the tensor amax get the smallest scales: UE5M3 scales
+    # near 2^-17, whose 2^-5-shifted fp16 operands are subnormal; E4M3
+    # subnormal scale codes (exponent field 0).  Both must be used exactly.
     rng = np.random.default_rng(54)
-    a = (rng.standard_normal((64, 256)) * 2.0 ** -23).astype(np.float32)
+    a = (rng.standard_normal((64, 256)) * rel).astype(np.float32)
     a[0, 0] = 1.0
-    b = (rng.standard_normal((64, 256)) * 2.0 ** -23).astype(np.float32)
+    b = (rng.standard_normal((64, 256)) * rel).astype(np.float32)
     b[0, 0] = 1.0
     a_bits, b_bits = inputs.to_bf16_bits(a), inputs.to_bf16_bits(b)
-    qa, qb = gpu_quant(a_bits, "ue5m3", "row"), gpu_quant(b_bits, "ue5m3", "row")
+    qa, qb = gpu_quant(a_bits, fmt, "row"), gpu_quant(b_bits, fmt, "row")
     d = api.gemm(qa.operand(), qb.operand(), 64, 64, 256, device=DEV)
     torch.cuda.synchronize()
-    av, sa = oracle_operand(a_bits, "ue5m3", "row")
-    bv, sb = oracle_operand(b_bits, "ue5m3", "row")
-    # premise: many fp16 operands are subnormal, i.e. |e2m1 * scale| * 2^-5 < 2^-14
-    assert np.count_nonzero((av != 0) & (np.abs(av) * 2.0 ** -5 < 2.0 ** -14)) > 10000
+    av, sa = oracle_operand(a_bits, fmt, "row")
+    bv, sb = oracle_operand(b_bits, fmt, "row")
+    if fmt == "ue5m3":
+        # premise: many fp16 operands are subnormal, |e2m1 * scale| * 2^-5 < 2^-14
+        assert np.count_nonzero((av != 0) & (np.abs(av) * 2.0 ** -5 < 2.0 ** -14)) > 10000
+    else:
+        # premise: many E4M3 scale codes are subnormal (1..7)
+        sc = Q.quantize(a_bits, fmt)["scales"]
+        assert np.count_nonzero((sc >= 1) & (sc <= 7)) > 100
     check(d.cpu().numpy(), G.gemm_ref(av, bv, sa, sb), G.gemm_abs_bound(av, bv, sa, sb))
 
 
