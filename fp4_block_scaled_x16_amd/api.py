@@ -22,6 +22,8 @@ BLOCK_LEN = {NVFP4: 16, UE5M3: 16, MXFP4: 32}
 RNE, SR = 0, 1
 BLOCK_1D, BLOCK_2D16 = 0, 1
 ROWWISE, COLWISE = 0, 1
+SCALES_ROWMAJOR, SCALES_TILED = 0, 1
+SCALE_LAYOUTS = {"rowmajor": SCALES_ROWMAJOR, "tiled": SCALES_TILED}
 COUNTER_NAMES = ("scale_saturated", "scale_underflow", "scale_subnormal",
                  "elem_saturated", "elem_underflow")
 
@@ -36,14 +38,15 @@ class QuantDesc(ctypes.Structure):
     _fields_ = [("format", ctypes.c_int), ("block", ctypes.c_int), ("orient", ctypes.c_int),
                 ("round", ctypes.c_int), ("seed", ctypes.c_uint64), ("offset", ctypes.c_uint64),
                 ("rht", ctypes.c_int), ("rht_signs", ctypes.c_uint32), ("target", ctypes.c_float),
-                ("amax_given", ctypes.c_int), ("emit_transpose", ctypes.c_int)]
+                ("amax_given", ctypes.c_int), ("emit_transpose", ctypes.c_int),
+                ("scale_layout", ctypes.c_int)]
 
 
 class Operand(ctypes.Structure):
     _fields_ = [("format", ctypes.c_int), ("codes", ctypes.c_void_p), ("ld_codes", ctypes.c_int64),
                 ("scales", ctypes.c_void_p), ("scale_stride_row", ctypes.c_int64),
                 ("scale_stride_kblk", ctypes.c_int64), ("scale_row_group", ctypes.c_int32),
-                ("s_dec", ctypes.c_void_p)]
+                ("s_dec", ctypes.c_void_p), ("scale_layout", ctypes.c_int)]
 
 
 _lib = None
@@ -64,7 +67,7 @@ def load_library(path=LIB_PATH):
     lib.fp4_amax.argtypes = [vp, i64, i64, i64, i32, u32, vp, vp]
     lib.fp4_quantize.argtypes = [ctypes.POINTER(QuantDesc), vp, i64, i64, i64, vp, vp, vp, vp,
                                  vp, vp, vp]
-    lib.fp4_dequantize.argtypes = [i32, i32, vp, vp, vp, i64, i64, vp, i32, vp]
+    lib.fp4_dequantize.argtypes = [i32, i32, i32, vp, vp, vp, i64, i64, vp, i32, vp]
     lib.fp4_rht16.argtypes = [vp, i64, i64, i64, u32, vp, vp]
     lib.fp4_gemm.argtypes = [ctypes.POINTER(Operand), ctypes.POINTER(Operand), i64, i64, i64, vp,
                              i64, i32, vp]
@@ -127,30 +130,47 @@ class Quantized:
     rows: int               # rows of the code matrix
     cols: int               # cols of the code matrix (the blocked axis for 1D)
     codes: torch.Tensor     # uint8 [rows, cols/2]
-    scales: torch.Tensor    # uint8 1D: [rows, cols/BS]; 2D: [rows/16, cols/16]
+    scales: torch.Tensor    # uint8 1D: [rows, cols/BS] (TILED: flat, tiled_scale_bytes);
+                            # 2D: [rows/16, cols/16]
     s_dec: torch.Tensor     # fp32 [1]
     amax: torch.Tensor      # fp32 [1] (two-level formats)
     codes_t: torch.Tensor = None   # 2D with emit_transpose: [cols, rows/2]
+    scale_layout: int = SCALES_ROWMAJOR
 
     def operand(self, transposed=False):
         """GEMM operand over the K-major code matrix (K = cols), or for 2D
-        weights with transposed=True over the codes of the transpose."""
+        weights with transposed=True over the codes of the transpose.
+
+        The operand holds raw device pointers; it keeps this object (and so
+        its tensors) alive for as long as the operand itself is referenced.
+        """
         bs = BLOCK_LEN[self.fmt]
         if self.block == BLOCK_1D:
             assert not transposed
-            return Operand(self.fmt, self.codes.data_ptr(), self.cols // 2, self.scales.data_ptr(),
-                           self.cols // bs, 1, 1, self.s_dec.data_ptr())
-        if not transposed:
-            return Operand(self.fmt, self.codes.data_ptr(), self.cols // 2, self.scales.data_ptr(),
-                           self.cols // 16, 1, 16, self.s_dec.data_ptr())
-        assert self.codes_t is not None
-        return Operand(self.fmt, self.codes_t.data_ptr(), self.rows // 2, self.scales.data_ptr(),
-                       1, self.cols // 16, 16, self.s_dec.data_ptr())
+            op = Operand(self.fmt, self.codes.data_ptr(), self.cols // 2, self.scales.data_ptr(),
+                         self.cols // bs, 1, 1, self.s_dec.data_ptr(), self.scale_layout)
+        elif not transposed:
+            op = Operand(self.fmt, self.codes.data_ptr(), self.cols // 2, self.scales.data_ptr(),
+                         self.cols // 16, 1, 16, self.s_dec.data_ptr(), SCALES_ROWMAJOR)
+        else:
+            assert self.codes_t is not None
+            op = Operand(self.fmt, self.codes_t.data_ptr(), self.rows // 2, self.scales.data_ptr(),
+                         1, self.cols // 16, 16, self.s_dec.data_ptr(), SCALES_ROWMAJOR)
+        op._owner = self
+        return op
+
+
+def tiled_scale_bytes(rows, blocks_per_row):
+    """Size of the TILED scale buffer of a [rows, blocks_per_row] scale matrix:
+    2 KiB atoms of 256 rows x 8 blocks."""
+    return -(-rows // 256) * -(-blocks_per_row // 8) * 2048
 
 
 def quantize(x, fmt="nvfp4", block="1d", orient="row", rnd="rne", seed=0, offset=0, rht=False,
-             signs=0, target=448.0, amax_in=None, emit_transpose=False, counters=None):
+             signs=0, target=448.0, amax_in=None, emit_transpose=False, counters=None,
+             scale_layout="rowmajor"):
     """Quantize a bf16 [R, C] matrix.  orient="col" quantizes X^T ([C, R]).
+    scale_layout: "rowmajor" or "tiled" (1D blocks only).
 
     amax_in: None -> computed on the device; else a device fp32 [1] tensor read
     as the (possibly stale) tensor amax.  counters: optional device uint64 [5]
@@ -165,8 +185,11 @@ def quantize(x, fmt="nvfp4", block="1d", orient="row", rnd="rne", seed=0, offset
     bs = 16 if blk == BLOCK_2D16 else BLOCK_LEN[f]
     dev = x.device
     codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    layout = SCALE_LAYOUTS[scale_layout] if isinstance(scale_layout, str) else int(scale_layout)
     if blk == BLOCK_2D16:
         scales = torch.empty((rows // 16, cols // 16), dtype=torch.uint8, device=dev)
+    elif layout == SCALES_TILED:
+        scales = torch.empty(tiled_scale_bytes(rows, cols // bs), dtype=torch.uint8, device=dev)
     else:
         scales = torch.empty((rows, cols // bs), dtype=torch.uint8, device=dev)
     codes_t = (torch.empty((cols, rows // 2), dtype=torch.uint8, device=dev)
@@ -175,12 +198,12 @@ def quantize(x, fmt="nvfp4", block="1d", orient="row", rnd="rne", seed=0, offset
     am = amax_in if amax_in is not None else torch.empty(1, dtype=torch.float32, device=dev)
     desc = QuantDesc(f, blk, COLWISE if col else ROWWISE, SR if rnd == "sr" else RNE,
                      int(seed), int(offset), int(bool(rht)), int(signs), float(target),
-                     int(amax_in is not None), int(bool(emit_transpose)))
+                     int(amax_in is not None), int(bool(emit_transpose)), layout)
     lib = load_library()
     _check(lib.fp4_quantize(ctypes.byref(desc), _ptr(x), R, C, x.stride(0), _ptr(codes),
                             _ptr(scales), _ptr(codes_t), _ptr(am), _ptr(s_dec), _ptr(counters),
                             _stream(dev)), "fp4_quantize")
-    return Quantized(f, blk, rows, cols, codes, scales, s_dec, am, codes_t)
+    return Quantized(f, blk, rows, cols, codes, scales, s_dec, am, codes_t, layout)
 
 
 def new_counters(device="cuda"):
@@ -195,7 +218,8 @@ def counters_dict(c):
 def dequantize(q: Quantized, out_dtype=torch.float32):
     out = torch.empty((q.rows, q.cols), dtype=out_dtype, device=q.codes.device)
     lib = load_library()
-    _check(lib.fp4_dequantize(q.fmt, q.block, _ptr(q.codes), _ptr(q.scales), _ptr(q.s_dec),
+    _check(lib.fp4_dequantize(q.fmt, q.block, q.scale_layout, _ptr(q.codes), _ptr(q.scales),
+                              _ptr(q.s_dec),
                               q.rows, q.cols, _ptr(out), int(out_dtype == torch.float32),
                               _stream(out.device)), "fp4_dequantize")
     return out

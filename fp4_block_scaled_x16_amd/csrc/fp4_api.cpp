@@ -108,6 +108,10 @@ FP4_EXPORT fp4_status fp4_quantize(const fp4_quant_desc* d, const uint16_t* x, i
   if (d->rht && d->rht_signs > 0xFFFFu) return fail(FP4_ERR_ARG, "rht_signs must fit in 16 bits");
   if (d->amax_given && !two_level) return fail(FP4_ERR_UNSUPPORTED, "MXFP4 has no tensor amax");
   if (!is2d && d->emit_transpose) return fail(FP4_ERR_UNSUPPORTED, "emit_transpose needs 2D16");
+  if (d->scale_layout != FP4_SCALES_ROWMAJOR && d->scale_layout != FP4_SCALES_TILED)
+    return fail(FP4_ERR_ARG, "bad scale_layout %d", (int)d->scale_layout);
+  const bool tiled = d->scale_layout == FP4_SCALES_TILED;
+  if (tiled && is2d) return fail(FP4_ERR_UNSUPPORTED, "TILED scales are for 1D blocks");
   if (two_level && !(std::isfinite(d->target) && d->target > 0.0f))
     return fail(FP4_ERR_ARG, "target must be finite and > 0");
   if (is2d) {
@@ -123,6 +127,7 @@ FP4_EXPORT fp4_status fp4_quantize(const fp4_quant_desc* d, const uint16_t* x, i
   if (!empty) {
     if (!codes || !scales) return fail(FP4_ERR_ARG, "codes/scales are null");
     if (!aligned16(codes)) return fail(FP4_ERR_ARG, "codes must be 16-byte aligned");
+    if (tiled && !aligned16(scales)) return fail(FP4_ERR_ARG, "TILED scales must be 16-byte aligned");
     if (d->emit_transpose && (!codes_t || !aligned16(codes_t)))
       return fail(FP4_ERR_ARG, "codes_t must be non-null and 16-byte aligned");
   }
@@ -152,6 +157,7 @@ FP4_EXPORT fp4_status fp4_quantize(const fp4_quant_desc* d, const uint16_t* x, i
   a.round = d->round;
   a.rht = d->rht;
   a.emit_transpose = d->emit_transpose;
+  a.tiled = tiled ? 1 : 0;
   hipError_t e;
   if (is2d) e = fp4lib::launch_quant_2d(a, s);
   else if (d->orient == FP4_ROWWISE) e = fp4lib::launch_quant_row(a, s);
@@ -159,11 +165,16 @@ FP4_EXPORT fp4_status fp4_quantize(const fp4_quant_desc* d, const uint16_t* x, i
   return device_status(e, "fp4_quantize launch");
 }
 
-FP4_EXPORT fp4_status fp4_dequantize(fp4_format format, fp4_block block, const uint8_t* codes,
+FP4_EXPORT fp4_status fp4_dequantize(fp4_format format, fp4_block block,
+                                     fp4_scale_layout scale_layout, const uint8_t* codes,
                                      const uint8_t* scales, const float* s_dec, int64_t rows,
                                      int64_t cols, void* out, int out_fp32, void* stream) {
   if (!valid_format(format)) return fail(FP4_ERR_ARG, "bad format %d", (int)format);
   if (block != FP4_BLOCK_1D && block != FP4_BLOCK_2D16) return fail(FP4_ERR_ARG, "bad block %d", (int)block);
+  if (scale_layout != FP4_SCALES_ROWMAJOR && scale_layout != FP4_SCALES_TILED)
+    return fail(FP4_ERR_ARG, "bad scale_layout %d", (int)scale_layout);
+  const bool tiled = scale_layout == FP4_SCALES_TILED;
+  if (tiled && block == FP4_BLOCK_2D16) return fail(FP4_ERR_UNSUPPORTED, "TILED scales are for 1D blocks");
   if (block == FP4_BLOCK_2D16 && format == FP4_MXFP4)
     return fail(FP4_ERR_UNSUPPORTED, "2D16 blocks need NVFP4 or UE5M3");
   if (rows < 0 || cols < 0) return fail(FP4_ERR_SHAPE, "negative size");
@@ -173,11 +184,12 @@ FP4_EXPORT fp4_status fp4_dequantize(fp4_format format, fp4_block block, const u
   if (rows > 0 && cols > 0) {
     if (!codes || !scales || !out) return fail(FP4_ERR_ARG, "null pointer");
     if (!aligned16(codes) || !aligned16(out)) return fail(FP4_ERR_ARG, "codes/out must be 16-byte aligned");
+    if (tiled && !aligned16(scales)) return fail(FP4_ERR_ARG, "TILED scales must be 16-byte aligned");
     if (format != FP4_MXFP4 && !s_dec) return fail(FP4_ERR_ARG, "s_dec is null");
   }
   if (rows == 0 || cols == 0) return ok();
-  return device_status(fp4lib::launch_dequant(format, block == FP4_BLOCK_2D16, codes, scales, s_dec,
-                                              rows, cols, out, out_fp32,
+  return device_status(fp4lib::launch_dequant(format, block == FP4_BLOCK_2D16, tiled, codes, scales,
+                                              s_dec, rows, cols, out, out_fp32,
                                               static_cast<hipStream_t>(stream)),
                        "fp4_dequantize launch");
 }
@@ -210,6 +222,10 @@ FP4_EXPORT fp4_status fp4_gemm(const fp4_operand* A, const fp4_operand* B, int64
     const fp4_operand* o = ops[i];
     if (o->scale_row_group != 1 && o->scale_row_group != 16)
       return fail(FP4_ERR_ARG, "scale_row_group must be 1 or 16");
+    if (o->scale_layout != FP4_SCALES_ROWMAJOR && o->scale_layout != FP4_SCALES_TILED)
+      return fail(FP4_ERR_ARG, "operand %c: bad scale_layout %d", "AB"[i], (int)o->scale_layout);
+    if (o->scale_layout == FP4_SCALES_TILED && o->scale_row_group != 1)
+      return fail(FP4_ERR_UNSUPPORTED, "operand %c: TILED scales need scale_row_group 1", "AB"[i]);
     if (o->scale_row_group == 16 && A->format == FP4_MXFP4)
       return fail(FP4_ERR_UNSUPPORTED, "2D16 scales need NVFP4 or UE5M3");
     if (M > 0 && N > 0 && K > 0) {
@@ -221,14 +237,18 @@ FP4_EXPORT fp4_status fp4_gemm(const fp4_operand* A, const fp4_operand* B, int64
                     "AB"[i], ld_align);
       if (o->scale_stride_row < 0 || o->scale_stride_kblk < 0)
         return fail(FP4_ERR_ARG, "negative scale stride");
+      if (o->scale_layout == FP4_SCALES_TILED && !aligned16(o->scales))
+        return fail(FP4_ERR_ARG, "operand %c: TILED scales must be 16-byte aligned", "AB"[i]);
     }
   }
   if (M > 0 && N > 0 && !D) return fail(FP4_ERR_ARG, "D is null");
   if (M == 0 || N == 0) return ok();
   fp4lib::GemmOperand a{A->codes, A->ld_codes, A->scales, A->scale_stride_row,
-                        A->scale_stride_kblk, A->scale_row_group, A->s_dec};
+                        A->scale_stride_kblk, A->scale_row_group, A->s_dec,
+                        A->scale_layout == FP4_SCALES_TILED};
   fp4lib::GemmOperand b{B->codes, B->ld_codes, B->scales, B->scale_stride_row,
-                        B->scale_stride_kblk, B->scale_row_group, B->s_dec};
+                        B->scale_stride_kblk, B->scale_row_group, B->s_dec,
+                        B->scale_layout == FP4_SCALES_TILED};
   return device_status(fp4lib::launch_gemm(A->format, a, b, M, N, K, D, ldd, accumulate,
                                            static_cast<hipStream_t>(stream)),
                        "fp4_gemm launch");

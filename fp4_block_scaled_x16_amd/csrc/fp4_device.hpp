@@ -254,4 +254,12 @@ __device__ __forceinline__ void rht16(float (&v)[16], uint32_t signs) {
   }
 }
 
+// Byte offset of the scale of (row r, block j) in the TILED scale layout:
+// 2 KiB atoms of 8 consecutive blocks x 256 consecutive rows, row by row,
+// kg = ceil(blocks per row / 8) atoms per 256-row band.
+__host__ __device__ __forceinline__ uint64_t tiled_scale_offset(uint64_t r, uint64_t j,
+                                                                uint64_t kg) {
+  return (((r >> 8) * kg + (j >> 3)) << 11) + ((r & 255u) << 3) + (j & 7u);
+}
+
 }  // namespace fp4dev

@@ -22,6 +22,7 @@ struct QuantArgs {
   uint64_t seed, offset;
   uint32_t rht_signs;
   int format, round, rht, emit_transpose;
+  int tiled;             // 1D scales in the TILED layout (2 KiB atoms of 256 rows x 8 blocks)
 };
 
 struct GemmOperand {
@@ -31,6 +32,7 @@ struct GemmOperand {
   int64_t s_row, s_kblk;
   int row_group;
   const float* s_dec;
+  bool tiled;            // scales in the TILED layout (strides unused)
 };
 
 // Number of compute units of the current device (cached per device).
@@ -41,9 +43,9 @@ hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld
 hipError_t launch_quant_row(const QuantArgs& a, hipStream_t s);
 hipError_t launch_quant_col(const QuantArgs& a, hipStream_t s);
 hipError_t launch_quant_2d(const QuantArgs& a, hipStream_t s);
-hipError_t launch_dequant(int format, int block2d, const uint8_t* codes, const uint8_t* scales,
-                          const float* s_dec, int64_t rows, int64_t cols, void* out, int out_fp32,
-                          hipStream_t s);
+hipError_t launch_dequant(int format, int block2d, int tiled, const uint8_t* codes,
+                          const uint8_t* scales, const float* s_dec, int64_t rows, int64_t cols,
+                          void* out, int out_fp32, hipStream_t s);
 hipError_t launch_rht16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, uint32_t signs,
                         float* y, hipStream_t s);
 hipError_t launch_gemm(int format, const GemmOperand& A, const GemmOperand& B, int64_t M, int64_t N,

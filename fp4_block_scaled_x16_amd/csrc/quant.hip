@@ -230,7 +230,7 @@ __global__ __launch_bounds__(kStream) void k_quant_row(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, const float* __restrict__ amax,
     float target, float* __restrict__ s_dec_out, uint64_t seed, uint64_t offset,
-    fp4_counters* __restrict__ counters) {
+    fp4_counters* __restrict__ counters, int tiled) {
   constexpr int BS = FMT == kMX ? 32 : 16;
   float s_enc_g = 1.0f, s_dec_g = 1.0f;
   if constexpr (FMT != kMX) global_scales(*amax, target, s_enc_g, s_dec_g);
@@ -283,7 +283,8 @@ __global__ __launch_bounds__(kStream) void k_quant_row(
     } else {
       *reinterpret_cast<uint4*>(dst) = make_uint4(words[0], words[1], words[2], words[3]);
     }
-    scales[r_cur * bpr + j_cur] = static_cast<uint8_t>(sc);
+    scales[tiled ? tiled_scale_offset(r_cur, j_cur, (bpr + 7) >> 3) : r_cur * bpr + j_cur] =
+        static_cast<uint8_t>(sc);
 #pragma unroll
     for (int k = 0; k < BS / 8; ++k) q[k] = nq[k];
   }
@@ -301,7 +302,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, const float* __restrict__ amax,
     float target, float* __restrict__ s_dec_out, uint64_t seed, uint64_t offset,
-    uint32_t signs, fp4_counters* __restrict__ counters) {
+    uint32_t signs, fp4_counters* __restrict__ counters, int tiled) {
   constexpr int BS = FMT == kMX ? 32 : 16;
   constexpr int TR = 8 * BS;        // tile rows (8 groups)
   constexpr int TC = 64;            // tile columns
@@ -367,7 +368,9 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
         } else {
           *reinterpret_cast<uint4*>(dst) = make_uint4(words[0], words[1], words[2], words[3]);
         }
-        scales[c * (rows / BS) + row / BS] = static_cast<uint8_t>(sc);
+        const uint64_t kb = static_cast<uint64_t>(rows / BS);
+        scales[tiled ? tiled_scale_offset(c, row / BS, (kb + 7) >> 3) : c * kb + row / BS] =
+            static_cast<uint8_t>(sc);
       }
     }
     __syncthreads();
@@ -466,7 +469,7 @@ __global__ __launch_bounds__(kStream) void k_dequant(const uint8_t* __restrict__
                                                       const uint8_t* __restrict__ scales,
                                                       const float* __restrict__ s_dec,
                                                       int64_t rows, int64_t cols,
-                                                      void* __restrict__ out) {
+                                                      void* __restrict__ out, int tiled) {
   constexpr int BS = FMT == kMX ? 32 : 16;
   const float sd = (FMT == kMX) ? 1.0f : *s_dec;
   const uint64_t bpr = static_cast<uint64_t>(cols) / BS;
@@ -475,7 +478,9 @@ __global__ __launch_bounds__(kStream) void k_dequant(const uint8_t* __restrict__
   for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kStream + threadIdx.x; i < n;
        i += stride) {
     const uint64_t r = i / bpr, j = i - r * bpr;
-    const uint32_t sc = B2D ? scales[(r >> 4) * bpr + j] : scales[i];
+    const uint32_t sc = B2D     ? scales[(r >> 4) * bpr + j]
+                        : tiled ? scales[tiled_scale_offset(r, j, (bpr + 7) >> 3)]
+                                : scales[i];
     float s_hat;
     if constexpr (FMT == kNV) s_hat = scale_m3_decode<7>(sc);
     else if constexpr (FMT == kUE) s_hat = scale_m3_decode<15>(sc);
@@ -606,7 +611,7 @@ static void row_launch(const QuantArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((k_quant_row<FMT, RND, CNT>), dim3(grid_for(n, FP4_ROW_WG_PER_CU)),
                      dim3(kStream), 0, s,
                      a.x, a.rows, a.cols, a.ld, a.codes, a.scales, a.amax, a.target, a.s_dec,
-                     a.seed, a.offset, a.counters);
+                     a.seed, a.offset, a.counters, a.tiled);
 }
 
 template <int FMT, int RND>
@@ -636,7 +641,7 @@ static void col_launch(const QuantArgs& a, hipStream_t s) {
   const int grid = static_cast<int>(tiles < cap ? (tiles > 0 ? tiles : 1) : cap);
   hipLaunchKernelGGL((k_quant_col<FMT, RND, RHT, CNT>), dim3(grid), dim3(kThreads), 0, s, a.x,
                      a.rows, a.cols, a.ld, a.codes, a.scales, a.amax, a.target, a.s_dec, a.seed,
-                     a.offset, a.rht_signs, a.counters);
+                     a.offset, a.rht_signs, a.counters, a.tiled);
 }
 
 template <int FMT, int RND, bool RHT>
@@ -690,31 +695,31 @@ hipError_t launch_quant_2d(const QuantArgs& a, hipStream_t s) {
 }
 
 template <int FMT, bool B2D>
-static void dq_launch(const uint8_t* codes, const uint8_t* scales, const float* s_dec,
+static void dq_launch(int tiled, const uint8_t* codes, const uint8_t* scales, const float* s_dec,
                       int64_t rows, int64_t cols, void* out, int out_fp32, hipStream_t s) {
   constexpr int BS = FMT == kMX ? 32 : 16;
   const uint64_t n = static_cast<uint64_t>(rows) * static_cast<uint64_t>(cols / BS);
   const int grid = grid_for(n, 2);
   if (out_fp32)
     hipLaunchKernelGGL((k_dequant<FMT, B2D, true>), dim3(grid), dim3(kStream), 0, s, codes,
-                       scales, s_dec, rows, cols, out);
+                       scales, s_dec, rows, cols, out, tiled);
   else
     hipLaunchKernelGGL((k_dequant<FMT, B2D, false>), dim3(grid), dim3(kStream), 0, s, codes,
-                       scales, s_dec, rows, cols, out);
+                       scales, s_dec, rows, cols, out, tiled);
 }
 
-hipError_t launch_dequant(int format, int block2d, const uint8_t* codes, const uint8_t* scales,
-                          const float* s_dec, int64_t rows, int64_t cols, void* out, int out_fp32,
-                          hipStream_t s) {
+hipError_t launch_dequant(int format, int block2d, int tiled, const uint8_t* codes,
+                          const uint8_t* scales, const float* s_dec, int64_t rows, int64_t cols,
+                          void* out, int out_fp32, hipStream_t s) {
   if (rows > 0 && cols > 0) {
     if (format == FP4_NVFP4) {
-      if (block2d) dq_launch<kNV, true>(codes, scales, s_dec, rows, cols, out, out_fp32, s);
-      else dq_launch<kNV, false>(codes, scales, s_dec, rows, cols, out, out_fp32, s);
+      if (block2d) dq_launch<kNV, true>(tiled, codes, scales, s_dec, rows, cols, out, out_fp32, s);
+      else dq_launch<kNV, false>(tiled, codes, scales, s_dec, rows, cols, out, out_fp32, s);
     } else if (format == FP4_UE5M3) {
-      if (block2d) dq_launch<kUE, true>(codes, scales, s_dec, rows, cols, out, out_fp32, s);
-      else dq_launch<kUE, false>(codes, scales, s_dec, rows, cols, out, out_fp32, s);
+      if (block2d) dq_launch<kUE, true>(tiled, codes, scales, s_dec, rows, cols, out, out_fp32, s);
+      else dq_launch<kUE, false>(tiled, codes, scales, s_dec, rows, cols, out, out_fp32, s);
     } else {
-      dq_launch<kMX, false>(codes, scales, s_dec, rows, cols, out, out_fp32, s);
+      dq_launch<kMX, false>(tiled, codes, scales, s_dec, rows, cols, out, out_fp32, s);
     }
   }
   return hipGetLastError();

@@ -53,6 +53,20 @@ typedef enum { FP4_RNE = 0, FP4_SR = 1 } fp4_round;
 /* 1D blocks along the blocked axis, or 16x16 tiles (NVFP4 paper §4.3). */
 typedef enum { FP4_BLOCK_1D = 0, FP4_BLOCK_2D16 = 1 } fp4_block;
 
+/* Where the block scales of a 1D code matrix [R, C] (KB = C / BS blocks per
+ * row) are stored.
+ *   FP4_SCALES_ROWMAJOR  scale of (row r, block j) at r * KB + j; R * KB bytes.
+ *   FP4_SCALES_TILED     at ((r / 256) * KG + j / 8) * 2048 + (r % 256) * 8 + j % 8
+ *                        with KG = ceil(KB / 8): 2 KiB atoms, each holding 8
+ *                        consecutive blocks of 256 consecutive rows, row by row.
+ *                        The buffer is ceil(R / 256) * KG * 2048 bytes and
+ *                        16-byte aligned; bytes of rows >= R or blocks >= KB
+ *                        are padding, never written and never used.
+ * TILED is a storage layout chosen for the GEMM: one 256-row output tile
+ * reads the scales of 8 K-blocks as one contiguous 2 KiB run instead of 256
+ * scattered pieces.  The scale values are the same in both layouts. */
+typedef enum { FP4_SCALES_ROWMAJOR = 0, FP4_SCALES_TILED = 1 } fp4_scale_layout;
+
 /* ROWWISE: blocks run along cols of X; output is [rows, cols] codes.
  * COLWISE: the matrix quantized is X^T; blocks run along rows of X and the
  * output is the [cols, rows] code matrix of X^T (Wgrad operands, §4.1). */
@@ -99,6 +113,9 @@ typedef struct {
                              1: read *amax (e.g. a stale, periodically
                              refreshed amax); NVFP4/UE5M3 only                 */
   int emit_transpose;     /* 2D16 only: also write the codes of X^T           */
+  fp4_scale_layout scale_layout;  /* 1D only: layout of `scales` (TILED: of
+                             the output code matrix, [rows, cols] for ROWWISE,
+                             [cols, rows] for COLWISE)                         */
 } fp4_quant_desc;
 
 /*
@@ -121,7 +138,8 @@ fp4_status fp4_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
  *           of byte j.  ROWWISE: [rows, cols/2] bytes; COLWISE: [cols, rows/2].
  *   scales  device, one byte per block.  1D ROWWISE: [rows, cols/BS];
  *           1D COLWISE: [cols, rows/BS]; 2D16: [rows/16, cols/16]
- *           (BS = 16, or 32 for MXFP4).
+ *           (BS = 16, or 32 for MXFP4).  1D scales follow desc->scale_layout
+ *           (TILED: 16-byte aligned, size as given with fp4_scale_layout).
  *   codes_t device, 2D16 with emit_transpose only: [cols, rows/2] codes of
  *           X^T quantized with the same tile scales (NULL otherwise).
  *   amax    device float.  NVFP4/UE5M3: written (amax_given = 0) or read
@@ -146,12 +164,13 @@ fp4_status fp4_quantize(const fp4_quant_desc* desc /* host */,
  * fp4_dequantize -- decode codes and scales: v = fp32(fp32(e2m1 * scale) *
  * s_dec_G) (NVFP4 paper App. B.2-B.3: the decode scales undo the encode
  * scales).  The codes/scales layouts are those fp4_quantize writes for a
- * ROWWISE (or 2D16) [rows, cols] code matrix.
+ * ROWWISE (or 2D16) [rows, cols] code matrix; 1D scales in scale_layout
+ * (2D16 scales are always [rows/16, cols/16]).
  *   s_dec   device float (NVFP4/UE5M3); ignored (may be NULL) for MXFP4.
  *   out     device, [rows, cols] row-major: fp32 if out_fp32, else bf16
  *           (v rounded to nearest even).
  */
-fp4_status fp4_dequantize(fp4_format format, fp4_block block,
+fp4_status fp4_dequantize(fp4_format format, fp4_block block, fp4_scale_layout scale_layout,
                           const uint8_t* codes, const uint8_t* scales, const float* s_dec,
                           int64_t rows, int64_t cols, void* out, int out_fp32, void* stream);
 
@@ -169,12 +188,15 @@ fp4_status fp4_rht16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
                      uint32_t rht_signs, float* y, void* stream);
 
 /* One GEMM operand: a [rows, K] code matrix, K-major (host struct of device
- * pointers).  The scale of (row r, K-block j) is
+ * pointers).  With scale_layout ROWMAJOR the scale of (row r, K-block j) is
  *   scales[(r / scale_row_group) * scale_stride_row + j * scale_stride_kblk]
  * so 1D scales are (row_group 1, stride_row K/BS, stride_kblk 1); 2D16
  * scales of W are (16, K/16, 1); the 2D16 scales of W used for the codes_t
  * matrix W^T are (16, 1, rows_of_W/16) -- the same bytes (§4.3: the tile
- * scale is replicated per 1x16 block). */
+ * scale is replicated per 1x16 block).  With scale_layout TILED the scales
+ * are the TILED layout of the [rows, K] code matrix (KB = K / BS); the
+ * strides are ignored, scale_row_group must be 1 and `scales` 16-byte
+ * aligned. */
 typedef struct {
   fp4_format format;
   const uint8_t* codes;       /* device, 16-byte aligned; ld_codes bytes per row,
@@ -185,6 +207,7 @@ typedef struct {
   int64_t scale_stride_kblk;
   int32_t scale_row_group;    /* 1 or 16 */
   const float* s_dec;         /* device s_dec_G; NULL means 1 (MXFP4 ignores it) */
+  fp4_scale_layout scale_layout;
 } fp4_operand;
 
 /*

@@ -53,7 +53,7 @@ def _err(lib):
 
 def desc(**kw):
     d = dict(format=0, block=0, orient=0, round=0, seed=0, offset=0, rht=0, rht_signs=0,
-             target=448.0, amax_given=0, emit_transpose=0)
+             target=448.0, amax_given=0, emit_transpose=0, scale_layout=0)
     d.update(kw)
     return api.QuantDesc(**d)
 
@@ -85,6 +85,8 @@ def quant(lib, d, rows=32, cols=64, ld=None, x=FAKE, codes=FAKE, scales=FAKE, co
     (dict(orient=1), 24, 64, 2),                     # rows % 16 (colwise)
     (dict(block=1), 40, 64, 2),                      # 2D rows % 16
     (dict(), -1, 64, 2),
+    (dict(scale_layout=2), 32, 64, 1),
+    (dict(block=1, scale_layout=1), 32, 64, 3),      # TILED scales are 1D only
 ])
 def test_quantize_rejects(lib, kw, rows, cols, status):
     assert quant(lib, desc(**kw), rows, cols) == status
@@ -100,21 +102,27 @@ def test_quantize_rejects_pointers(lib):
     assert quant(lib, desc(), amax=None) == 1
     assert quant(lib, desc(block=1, emit_transpose=1)) == 1         # codes_t null
     assert lib.fp4_quantize(None, FAKE, 32, 64, 64, FAKE, FAKE, None, FAKE, None, None, None) == 1
+    # TILED scales must be 16-byte aligned (row-major ones need not be)
+    assert quant(lib, desc(scale_layout=1), scales=ctypes.c_void_p(0x10004)) == 1
 
 
 def test_other_entry_points_reject(lib):
     assert lib.fp4_amax(FAKE, 32, 64, 64, 1, 0, None, None) == 1
     assert lib.fp4_amax(FAKE, 24, 64, 64, 1, 0, FAKE, None) == 2
     assert lib.fp4_amax(FAKE, 32, 64, 64, 1, 1 << 16, FAKE, None) == 1
-    assert lib.fp4_dequantize(0, 0, FAKE, FAKE, FAKE, 32, 40, FAKE, 1, None) == 2
-    assert lib.fp4_dequantize(2, 1, FAKE, FAKE, FAKE, 32, 64, FAKE, 1, None) == 3
-    assert lib.fp4_dequantize(0, 0, FAKE, FAKE, None, 32, 64, FAKE, 1, None) == 1
+    assert lib.fp4_dequantize(0, 0, 0, FAKE, FAKE, FAKE, 32, 40, FAKE, 1, None) == 2
+    assert lib.fp4_dequantize(2, 1, 0, FAKE, FAKE, FAKE, 32, 64, FAKE, 1, None) == 3
+    assert lib.fp4_dequantize(0, 0, 0, FAKE, FAKE, None, 32, 64, FAKE, 1, None) == 1
+    assert lib.fp4_dequantize(0, 0, 5, FAKE, FAKE, FAKE, 32, 64, FAKE, 1, None) == 1
+    assert lib.fp4_dequantize(0, 1, 1, FAKE, FAKE, FAKE, 32, 64, FAKE, 1, None) == 3
+    assert lib.fp4_dequantize(0, 0, 1, FAKE, ctypes.c_void_p(0x10008), FAKE, 32, 64, FAKE, 1,
+                              None) == 1
     assert lib.fp4_rht16(FAKE, 40, 64, 64, 0, FAKE, None) == 2
     assert lib.fp4_rht16(FAKE, 32, 64, 64, 0, None, None) == 1
 
 
-def op(fmt=0, codes=0x10000, ld=32, rg=1):
-    return api.Operand(fmt, codes, ld, 0x20000, 4, 1, rg, 0x30000)
+def op(fmt=0, codes=0x10000, ld=32, rg=1, layout=0, scales=0x20000):
+    return api.Operand(fmt, codes, ld, scales, 4, 1, rg, 0x30000, layout)
 
 
 @pytest.mark.parametrize("a,b,M,N,K,status", [
@@ -127,6 +135,9 @@ def op(fmt=0, codes=0x10000, ld=32, rg=1):
     (op(0, ld=16), op(0), 16, 16, 64, 1),   # ld_codes < K/2
     (op(0, codes=0x10004), op(0), 16, 16, 64, 1),
     (op(0, codes=0), op(0), 16, 16, 64, 1),
+    (op(0, layout=3), op(0), 16, 16, 64, 1),
+    (op(0, layout=1, rg=16), op(0), 16, 16, 64, 3),          # TILED scales are 1D
+    (op(2, layout=1, scales=0x20008), op(2), 16, 16, 64, 1),  # TILED misaligned
 ])
 def test_gemm_rejects(lib, a, b, M, N, K, status):
     assert lib.fp4_gemm(ctypes.byref(a), ctypes.byref(b), M, N, K, FAKE, N, 0, None) == status
@@ -137,9 +148,31 @@ def test_empty_calls_are_noops(lib):
     # nothing to do: accepted without any device work
     a, b = op(0), op(0)
     assert lib.fp4_gemm(ctypes.byref(a), ctypes.byref(b), 0, 16, 64, None, 16, 0, None) == 0
-    assert lib.fp4_dequantize(0, 0, None, None, None, 0, 64, None, 1, None) == 0
+    assert lib.fp4_dequantize(0, 0, 0, None, None, None, 0, 64, None, 1, None) == 0
 
 
 def test_status_strings(lib):
     assert lib.fp4_status_string(0) == b"ok"
     assert lib.fp4_status_string(3) == b"unsupported combination"
+
+
+def test_operand_keeps_its_storage_alive():
+    """A GEMM operand carries raw device pointers, so it must keep the
+    quantized tensors it points into alive: dropping the Quantized object
+    right after .operand() must not free them (a later allocator flush would
+    unmap memory the GEMM still reads)."""
+    import gc
+    import weakref
+    import torch
+    codes = torch.zeros((32, 16), dtype=torch.uint8)
+    scales = torch.zeros((32, 2), dtype=torch.uint8)
+    s_dec = torch.ones(1)
+    q = api.Quantized(api.NVFP4, api.BLOCK_1D, 32, 32, codes, scales, s_dec, s_dec.clone())
+    ref = weakref.ref(codes)
+    op = q.operand()
+    del q, codes, scales
+    gc.collect()
+    assert ref() is not None and op.codes == ref().data_ptr()
+    del op
+    gc.collect()
+    assert ref() is None

@@ -54,9 +54,9 @@ def gpu_operand(q, layout):
     return q.operand(transposed=(layout == "2dT"))
 
 
-def gpu_quant(bits, fmt, layout, **kw):
+def gpu_quant(bits, fmt, layout, scales="rowmajor", **kw):
     if layout in ("row", "col"):
-        return api.quantize(dev(bits), fmt, orient=layout, **kw)
+        return api.quantize(dev(bits), fmt, orient=layout, scale_layout=scales, **kw)
     return api.quantize(dev(bits), fmt, block="2d", emit_transpose=True, **kw)
 
 
@@ -71,7 +71,42 @@ CASES = [
     ("mxfp4", "row", "row", 600, 520, 224),
     ("mxfp4", "row", "row", 33, 17, 32),
     ("nvfp4", "col", "col", 512, 264, 304),
+    # MXFP4 with K a multiple of 512: the LDS-DMA ring kernel (one turn of
+    # the ring only, ragged tiles with clamped rows, several turns)
+    ("mxfp4", "row", "row", 300, 264, 512),
+    ("mxfp4", "col", "col", 520, 264, 1024),
+    ("mxfp4", "row", "row", 256, 512, 2048),
 ]
+
+
+TILED_CASES = [
+    # fmt, A layout, B layout, M, N, K, A scales, B scales
+    ("nvfp4", "row", "row", 600, 520, 208, "tiled", "tiled"),     # ragged, partial K step
+    ("nvfp4", "row", "2d", 512, 512, 512, "tiled", "rowmajor"),   # tile-aligned loader
+    ("ue5m3", "row", "row", 256, 512, 1024, "tiled", "tiled"),
+    ("mxfp4", "row", "row", 600, 520, 224, "tiled", "tiled"),     # register-staged MXFP4
+    ("mxfp4", "row", "col", 300, 264, 512, "tiled", "rowmajor"),  # DMA ring, mixed layouts
+    ("mxfp4", "row", "row", 300, 264, 512, "tiled", "tiled"),     # K-256 kernel, 2 steps
+    ("mxfp4", "col", "col", 520, 264, 1024, "tiled", "tiled"),    # ... one loop turn
+    ("mxfp4", "row", "row", 256, 512, 2048, "tiled", "tiled"),    # ... several turns
+]
+
+
+@pytest.mark.parametrize("fmt,la,lb,M,N,K,sa_layout,sb_layout", TILED_CASES)
+def test_gemm_tiled_scales(fmt, la, lb, M, N, K, sa_layout, sb_layout):
+    a_shape = (M, K) if la == "row" else (K, M)
+    a_bits = inputs.activations(a_shape, cfg_seed=53)
+    b_bits = inputs.weights((N, K), cfg_seed=53) if lb in ("row", "2d") else \
+        inputs.gradients((K, N), cfg_seed=53)
+    qa = gpu_quant(a_bits, fmt, la, scales=sa_layout)
+    qb = gpu_quant(b_bits, fmt, lb, scales=sb_layout)
+    d = api.gemm(gpu_operand(qa, la), gpu_operand(qb, lb), M, N, K, device=DEV)
+    torch.cuda.synchronize()
+    av, sa = oracle_operand(a_bits, fmt, la)
+    bv, sb = oracle_operand(b_bits, fmt, lb)
+    if fmt == "mxfp4":
+        sa = sb = 1.0
+    check(d.cpu().numpy(), G.gemm_ref(av, bv, sa, sb), G.gemm_abs_bound(av, bv, sa, sb))
 
 
 @pytest.mark.parametrize("fmt,la,lb,M,N,K", CASES)
@@ -99,9 +134,9 @@ def test_gemm_small(fmt, la, lb, M, N, K):
     check(d.cpu().numpy(), G.gemm_ref(av, bv, sa, sb), G.gemm_abs_bound(av, bv, sa, sb))
 
 
-@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
-def test_gemm_accumulate_and_ldd(fmt):
-    M, N, K = 280, 300, 256
+@pytest.mark.parametrize("fmt,K", [("nvfp4", 256), ("mxfp4", 256), ("mxfp4", 512)])
+def test_gemm_accumulate_and_ldd(fmt, K):
+    M, N = 280, 300
     a_bits = inputs.activations((M, K), cfg_seed=51)
     b_bits = inputs.weights((N, K), cfg_seed=51)
     qa, qb = gpu_quant(a_bits, fmt, "row"), gpu_quant(b_bits, fmt, "row")
@@ -246,9 +281,10 @@ GEMMS = {
 }
 
 
+@pytest.mark.parametrize("scales", ["rowmajor", "tiled"])
 @pytest.mark.parametrize("cfg", [2, 3, 4, 5])
 @pytest.mark.parametrize("gemm", ["fprop", "dgrad", "wgrad"])
-def test_workload_gemm(cfg, gemm):
+def test_workload_gemm(cfg, gemm, scales):
     an, la, bn, lb = GEMMS[gemm]
     fmt = {2: "nvfp4", 3: "nvfp4", 4: "ue5m3", 5: "mxfp4"}[cfg]
     if fmt == "mxfp4":   # MXFP4 weights are 1D: rowwise for Fprop, colwise for Dgrad
@@ -266,7 +302,7 @@ def test_workload_gemm(cfg, gemm):
         if layout in ("2d", "2dT"):
             return api.quantize(x, fmt, block="2d", emit_transpose=True, amax_in=amax_in,
                                 target=kw.get("target", 448.0))
-        return api.quantize(x, fmt, orient=layout, amax_in=amax_in, **kw)
+        return api.quantize(x, fmt, orient=layout, amax_in=amax_in, scale_layout=scales, **kw)
 
     qa, qb = gq(a_bits, la, kwa, sa_stale), gq(b_bits, lb, kwb, sb_stale)
     M, K = qa.rows, qa.cols

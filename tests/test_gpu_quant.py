@@ -14,6 +14,7 @@ from fp4_block_scaled_x16_amd import api, inputs
 from oracle import formats as F
 from oracle import quantize as Q
 from oracle.rht import rht16_cols
+from scale_layout import untile
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -29,13 +30,13 @@ def f32_bits(v):
 
 
 def run_both(x_bits, fmt, block="1d", orient="row", rnd="rne", seed=1, offset=0, rht=False,
-             target=448.0, stale=None, emit_transpose=False):
+             target=448.0, stale=None, emit_transpose=False, scale_layout="rowmajor"):
     x = dev(x_bits)
     cnt = api.new_counters()
     amax_in = None if stale is None else torch.tensor([stale], dtype=torch.float32, device=DEV)
     q = api.quantize(x, fmt, block=block, orient=orient, rnd=rnd, seed=seed, offset=offset,
                      rht=rht, signs=SIGNS if rht else 0, target=target, amax_in=amax_in,
-                     emit_transpose=emit_transpose, counters=cnt)
+                     emit_transpose=emit_transpose, counters=cnt, scale_layout=scale_layout)
     torch.cuda.synchronize()
     r = Q.quantize(x_bits, fmt, block=block, orient=orient, rnd=rnd, seed=seed, offset=offset,
                    rht=rht, signs=SIGNS if rht else 0, target=target,
@@ -44,9 +45,17 @@ def run_both(x_bits, fmt, block="1d", orient="row", rnd="rne", seed=1, offset=0,
     return q, r, api.counters_dict(cnt)
 
 
+def gpu_scales(q):
+    """Row-major scale matrix of a quantized result, whatever its layout."""
+    s = q.scales.cpu().numpy()
+    if q.scale_layout == api.SCALES_TILED:
+        return untile(s, q.rows, q.cols // api.BLOCK_LEN[q.fmt])
+    return s
+
+
 def assert_same(q, r, cnt):
     assert np.array_equal(q.codes.cpu().numpy(), r["codes"]), "codes differ"
-    assert np.array_equal(q.scales.cpu().numpy(), r["scales"]), "scales differ"
+    assert np.array_equal(gpu_scales(q), r["scales"]), "scales differ"
     if r.get("codes_t") is not None:
         assert np.array_equal(q.codes_t.cpu().numpy(), r["codes_t"]), "codes_t differ"
     if r["amax"] is not None:
@@ -71,6 +80,24 @@ def test_rowwise(fmt, rnd, dist):
     x = GEN[dist]((1037, cols), 31)
     q, r, c = run_both(x, fmt, rnd=rnd, offset=3)
     assert_same(q, r, c)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "ue5m3", "mxfp4"])
+@pytest.mark.parametrize("orient", ["row", "col"])
+def test_tiled_scale_layout(fmt, orient):
+    """TILED scales hold the same values as row-major ones: output code
+    matrices of 300 / 264 rows (a partial 256-row band) and 38 / 19 blocks
+    per row (a partial group of 8), SR on gradients."""
+    shape = (300, 608) if orient == "row" else (608, 264)
+    x = inputs.gradients(shape, cfg_seed=33)
+    q, r, c = run_both(x, fmt, orient=orient, rnd="sr", offset=2, scale_layout="tiled")
+    assert q.scales.dim() == 1 and q.scales.numel() == api.tiled_scale_bytes(
+        q.rows, q.cols // api.BLOCK_LEN[q.fmt])
+    assert_same(q, r, c)
+    d = api.dequantize(q)
+    torch.cuda.synchronize()
+    want = Q.dequantize(r["codes"], r["scales"], fmt, "1d", r["s_dec"], q.rows, q.cols, out="f32")
+    assert np.array_equal(d.cpu().numpy().view(np.uint32), want.view(np.uint32))
 
 
 @pytest.mark.parametrize("fmt,target", [("nvfp4", 448.0), ("ue5m3", 448.0), ("ue5m3", 2048.0)])
@@ -258,7 +285,14 @@ def test_workload_1d(cfg, name):
         amax_dev = None if amax is None else torch.tensor([amax], dtype=torch.float32, device=DEV)
         q = api.quantize(xd, fmt, orient=orient, rnd=rnd, seed=1, offset=offset, rht=rht,
                          signs=SIGNS if rht else 0, target=target, amax_in=amax_dev)
+        # the same quantization with TILED scales: identical codes, same scale values
+        qt = api.quantize(xd, fmt, orient=orient, rnd=rnd, seed=1, offset=offset, rht=rht,
+                          signs=SIGNS if rht else 0, target=target, amax_in=amax_dev,
+                          scale_layout="tiled")
         torch.cuda.synchronize()
+        assert torch.equal(q.codes, qt.codes), (name, orient)
+        assert np.array_equal(gpu_scales(qt), q.scales.cpu().numpy()), (name, orient)
+        del qt
         want = None
         if fmt != "mxfp4":
             want = amax if amax is not None else Q.tensor_amax(rht16_cols(xf, SIGNS) if rht else xf)
