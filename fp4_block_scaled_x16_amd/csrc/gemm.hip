@@ -367,9 +367,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level(Params p) {
     store_codes(st[0]);
     __syncthreads();
   }
+  // Every step loads and stores a next step (the last one re-reads itself
+  // into the buffer nobody reads again): with no branch around them the
+  // loads and LDS writes share one scheduling region with the MFMAs instead
+  // of stalling the wave at the top and bottom of each step.
   for (int s = 0; s < nsteps; ++s) {
-    const bool more = s + 1 < nsteps;
-    if (more) load_step(s + 1);
+    load_step(s + 1 < nsteps ? s + 1 : s);
     const Stage2& S = st[s & 1];
     uint32_t a_raw[4][8], b_raw[4][8];
     uint4 a_sc[4], b_sc[4];
@@ -397,12 +400,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level(Params p) {
     pipelined_slice<1>(acc, f1, f0, a_raw, b_raw, a_sc, b_sc);
     pipelined_slice<2>(acc, f0, f1, a_raw, b_raw, a_sc, b_sc);
     pipelined_slice<3>(acc, f1, f0, a_raw, b_raw, a_sc, b_sc);
-    if (more) store_scales(st[(s + 1) & 1]);
+    store_scales(st[(s + 1) & 1]);
     pipelined_slice<4>(acc, f0, f1, a_raw, b_raw, a_sc, b_sc);
     pipelined_slice<5>(acc, f1, f0, a_raw, b_raw, a_sc, b_sc);
     pipelined_slice<6>(acc, f0, f1, a_raw, b_raw, a_sc, b_sc);
     pipelined_slice<7>(acc, f1, f0, a_raw, b_raw, a_sc, b_sc);
-    if (more) store_codes(st[(s + 1) & 1]);
+    store_codes(st[(s + 1) & 1]);
     __syncthreads();
   }
 
@@ -843,6 +846,35 @@ __device__ __forceinline__ void v_scales(const StageV& S, uint32_t (&a_sc)[4], u
   for (int ni = 0; ni < 4; ++ni) b_sc[ni] = sb[(wn * 128 + ni * 32 + i) * 2 + h];
 }
 
+// Slice 3 of a step with the refill of stage C (K step `refill`) woven in:
+// one 16-byte code DMA after each of the 16 MFMAs, then the scale atom.
+// Issued in one burst, the 68 DMA instructions of the workgroup would queue
+// behind each other in the memory pipeline and hold back the MFMAs of every
+// wave; left to the scheduler, they sink to the next barrier and do not
+// overlap at all.  sched_barrier(0) pins each pair in place.
+__device__ __forceinline__ void ring_mfma3_refill(floatx16 (&acc)[4][4], const MxFrag& f,
+                                                  const uint32_t (&a_sc)[4],
+                                                  const uint32_t (&b_sc)[4], StageV& C,
+                                                  const DmaSrcV& src, int refill, int wave) {
+  const int64_t cb = static_cast<int64_t>(refill) * (kBKV / 2);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          f.b[ni], f.a[mi], acc[mi][ni], 4, 4, 3, static_cast<int>(b_sc[ni]), 3,
+          static_cast<int>(a_sc[mi]));
+      const int x = mi * 4 + ni, o = x >> 3, j = x & 7;
+      __builtin_amdgcn_global_load_lds(src.codes[o][j] + cb, &C.codes[o][wave * 512 + j * 64], 16,
+                                       0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  __builtin_amdgcn_global_load_lds(src.scales + (static_cast<int64_t>(refill) << 11),
+                                   &C.scales[wave >> 1][(wave & 1) * 128], 16, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // One K step on stage C, slice-0 operands (fa) and scales in registers.
 template <bool LAST, bool DMA>
 __device__ __forceinline__ void v_step(StageV& C, const StageV& Nx, floatx16 (&acc)[4][4],
@@ -860,11 +892,11 @@ __device__ __forceinline__ void v_step(StageV& C, const StageV& Nx, floatx16 (&a
   } else {
     wait_vmcnt<0>();          // this wave's DMA of Nx (the only one in flight)
     ring_barrier();           // ... and every other wave's; C fully read
-    if constexpr (DMA) dma_v(C, src, refill, wave);
     uint32_t na[4], nb[4];
     v_scales(Nx, na, nb, wm, wn, i, h);
     v_operands<0>(Nx, fa, wm, wn, i, h);
-    ring_mfma<3>(acc, fb, a_sc, b_sc);
+    if constexpr (DMA) ring_mfma3_refill(acc, fb, a_sc, b_sc, C, src, refill, wave);
+    else ring_mfma<3>(acc, fb, a_sc, b_sc);
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       a_sc[x] = na[x];

@@ -21,12 +21,12 @@ namespace {
 
 constexpr int kThreads = 256;       // tiled kernels (colwise, 2D)
 constexpr int kStream = 512;        // streaming kernels (amax, rowwise, dequant, RHT)
-#ifndef FP4_ROW_WG_PER_CU
-#define FP4_ROW_WG_PER_CU 1
-#endif
-#ifndef FP4_TILE_WG_PER_CU
-#define FP4_TILE_WG_PER_CU 2
-#endif
+// Resident workgroups per CU of the persistent quantizer grids (measured on
+// MI355X: more waves let the VALU-heavy stochastic-rounding kernels overlap
+// their LDS and memory latency; the RNE tile kernels prefer fewer).
+constexpr int kRowWgPerCu = 2;      // rowwise, RNE and SR
+constexpr int kColWgPerCuSR = 4;    // colwise with stochastic rounding
+constexpr int kTileWgPerCu = 2;     // colwise RNE, 2D
 
 // Same-address global atomics serialize (about 12 ns each on MI355X once
 // more than a few hundred arrive), so every kernel runs a persistent grid
@@ -608,7 +608,7 @@ template <int FMT, int RND, bool CNT>
 static void row_launch(const QuantArgs& a, hipStream_t s) {
   constexpr int BS = FMT == kMX ? 32 : 16;
   const uint64_t n = static_cast<uint64_t>(a.rows) * static_cast<uint64_t>(a.cols / BS);
-  hipLaunchKernelGGL((k_quant_row<FMT, RND, CNT>), dim3(grid_for(n, FP4_ROW_WG_PER_CU)),
+  hipLaunchKernelGGL((k_quant_row<FMT, RND, CNT>), dim3(grid_for(n, kRowWgPerCu)),
                      dim3(kStream), 0, s,
                      a.x, a.rows, a.cols, a.ld, a.codes, a.scales, a.amax, a.target, a.s_dec,
                      a.seed, a.offset, a.counters, a.tiled);
@@ -637,7 +637,8 @@ template <int FMT, int RND, bool RHT, bool CNT>
 static void col_launch(const QuantArgs& a, hipStream_t s) {
   constexpr int BS = FMT == kMX ? 32 : 16;
   const int64_t tiles = ((a.rows + 8 * BS - 1) / (8 * BS)) * ((a.cols + 63) / 64);
-  const int64_t cap = static_cast<int64_t>(device_cu_count()) * FP4_TILE_WG_PER_CU;
+  const int64_t cap = static_cast<int64_t>(device_cu_count()) *
+                      (RND == FP4_SR ? kColWgPerCuSR : kTileWgPerCu);
   const int grid = static_cast<int>(tiles < cap ? (tiles > 0 ? tiles : 1) : cap);
   hipLaunchKernelGGL((k_quant_col<FMT, RND, RHT, CNT>), dim3(grid), dim3(kThreads), 0, s, a.x,
                      a.rows, a.cols, a.ld, a.codes, a.scales, a.amax, a.target, a.s_dec, a.seed,
@@ -676,7 +677,7 @@ hipError_t launch_quant_col(const QuantArgs& a, hipStream_t s) {
 template <int FMT, bool CNT>
 static void q2d_launch(const QuantArgs& a, hipStream_t s) {
   const int64_t regions = ((a.rows + 63) / 64) * ((a.cols + 63) / 64);
-  const int64_t cap = static_cast<int64_t>(device_cu_count()) * FP4_TILE_WG_PER_CU;
+  const int64_t cap = static_cast<int64_t>(device_cu_count()) * kTileWgPerCu;
   const int grid = static_cast<int>(regions < cap ? (regions > 0 ? regions : 1) : cap);
   hipLaunchKernelGGL((k_quant_2d<FMT, CNT>), dim3(grid), dim3(kThreads), 0, s, a.x, a.rows,
                      a.cols, a.ld, a.codes, a.scales, a.emit_transpose ? a.codes_t : nullptr,
