@@ -52,8 +52,70 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2, choices=(2, 3, 4, 5))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--counters-run", action="store_true",
+                    help="run each op of the step once, eagerly, then a 512 MiB calibration "
+                         "kernel, for rocprofv3 --pmc; prints nothing else")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn the counter CSVs of two --counters-run passes (FETCH_SIZE, "
+                         "WRITE_SIZE) into the GEMM traffic summary")
     return ap.parse_args()
+
+
+CAL_BYTES = 512 << 20       # calibration kernel: reads and writes this many bytes
+
+
+def counters_run(ops):
+    """One eager pass of the step's ops, then y = 2 x on CAL_BYTES of fp32
+    (a plain streaming kernel of known traffic) to calibrate the counters."""
+    import torch
+    for (_, _, _, f) in ops:
+        f()
+    x = torch.ones(CAL_BYTES // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(2):
+        torch.mul(x, 2.0, out=y)
+    torch.cuda.synchronize()
+
+
+def summarize_pmc(fetch_csv, write_csv, cfg):
+    """Per-launch HBM bytes of the GEMM kernel from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled by what the same counter reads for the
+    calibration kernel of known size."""
+    import csv
+
+    def per_dispatch(path, counter):
+        rows = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = int(r["Dispatch_Id"])
+                rows[key] = (r["Kernel_Name"], rows.get(key, ("", 0.0))[1] + float(r["Counter_Value"]))
+        return [rows[k] for k in sorted(rows)]
+
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        d = per_dispatch(path, counter)
+        gemm = [v for (n, v) in d if "k_gemm" in n]
+        cal = [v for (n, v) in d if "elementwise" in n.lower() and "mul" in n.lower()]
+        if not gemm or not cal:
+            raise SystemExit("no GEMM or calibration dispatches in %s" % path)
+        factor = CAL_BYTES / (np.mean(cal[-2:]) * 1024.0)     # bytes per counted byte
+        out[counter] = (gemm, factor)
+    fetch, f_fac = out["FETCH_SIZE"]
+    write, w_fac = out["WRITE_SIZE"]
+    names = ["fprop", "dgrad", "wgrad"][:len(fetch)]
+    lines = ["kernel_source_sha256_16=%s" % source_hash("gemm.hip", "fp4_device.hpp"),
+             "calibration_fetch_factor=%.4f" % f_fac, "calibration_write_factor=%.4f" % w_fac]
+    tot = []
+    for i, n in enumerate(names):
+        fb, wb = fetch[i] * 1024.0 * f_fac, write[i] * 1024.0 * w_fac
+        tot.append(fb + wb)
+        lines.append("%s_fetch_bytes=%.0f" % (n, fb))
+        lines.append("%s_write_bytes=%.0f" % (n, wb))
+    lines.append("hbm_bytes_per_launch=%.0f" % float(np.mean(tot)))
+    print("\n".join(lines))
 
 
 def source_hash(*names):
@@ -145,6 +207,8 @@ def build_step(cfg, dev):
                 kw2 = dict(kw, amax_in=st[key])
             else:
                 kw2 = kw
+            if kw2.get("block") != "2d":
+                kw2 = dict(kw2, scale_layout="tiled")   # the GEMM-friendly 1D scale layout
             st[out] = api.quantize(x, fmt, counters=cnt, **kw2)
         return f
 
@@ -231,9 +295,12 @@ def cpu_baseline(cfg, host, fmt, tokens):
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.config)
+        return
     if args.gpus != 1:
-        print("bench.py: this build measures one GPU only (--gpus 1); the multi-GPU "
-              "sharding of this path is described in DESIGN.md, not run.", file=sys.stderr)
+        print("bench.py measures one GPU (--gpus 1); runs on several GPUs are not "
+              "part of this benchmark.", file=sys.stderr)
         sys.exit(2)
     import torch
     from fp4_block_scaled_x16_amd import api, inputs
@@ -246,6 +313,9 @@ def main():
     torch.cuda.set_device(dev)
     cfg = args.config
     ops, cnt, host, fmt = build_step(cfg, dev)
+    if args.counters_run:
+        counters_run(ops)
+        return
 
     def run_step():
         for (_, _, _, f) in ops:
@@ -333,7 +403,7 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic,
                 "kernel": "k_gemm_two_level<NVFP4>" if fmt == "nvfp4" else
-                          ("k_gemm_two_level<UE5M3>" if fmt == "ue5m3" else "k_gemm_mx"),
+                          ("k_gemm_two_level<UE5M3>" if fmt == "ue5m3" else "k_gemm_mx_tiled"),
                 "flops_per_launch": per_launch, "avg_launch_ms": round(avg_ms, 4),
                 "kernel_source_sha256_16": khash}
 
@@ -347,7 +417,7 @@ def main():
             "fp4 scaled" if fmt == "mxfp4" else "fp16 (exact dequant)"),
         "data": "synthetic (seeded PCG64, bf16 inputs resident in HBM)",
         "config": {"workload": c["name"], "format": fmt, "tokens": c["tokens"], "d_in": c["d_in"],
-                   "d_out": c["d_out"], "gemms": "fprop, dgrad, wgrad",
+                   "d_out": c["d_out"], "gemms": "fprop, dgrad, wgrad", "scales_1d": "tiled",
                    "quantizations": len([1 for (n, k, u, _) in ops if n.startswith("quant")])},
         "quantize": {"GBps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
                      "frac_hbm": round(q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
