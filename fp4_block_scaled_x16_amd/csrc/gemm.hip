@@ -361,21 +361,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level(Params p) {
     for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = floatx16{};
 
   const int i = lane & 31, h = lane >> 5;
-  if (nsteps > 0) {
-    load_step(0);
-    store_scales(st[0]);
-    store_codes(st[0]);
-    __syncthreads();
-  }
-  // Every step loads and stores a next step (the last one re-reads itself
-  // into the buffer nobody reads again): with no branch around them the
-  // loads and LDS writes share one scheduling region with the MFMAs instead
-  // of stalling the wave at the top and bottom of each step.
-  for (int s = 0; s < nsteps; ++s) {
-    load_step(s + 1 < nsteps ? s + 1 : s);
-    const Stage2& S = st[s & 1];
-    uint32_t a_raw[4][8], b_raw[4][8];
-    uint4 a_sc[4], b_sc[4];
+  uint32_t a_raw[4][8], b_raw[4][8];
+  uint4 a_sc[4], b_sc[4];
+  // this lane's raw codes (its K half of the step) and decoded scales
+  auto read_stage = [&](const Stage2& S) {
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
       const int row = wm * 128 + mi * 32 + i;
@@ -394,6 +383,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level(Params p) {
       b_raw[ni][4] = c1.x; b_raw[ni][5] = c1.y; b_raw[ni][6] = c1.z; b_raw[ni][7] = c1.w;
       b_sc[ni] = S.scales[1][h][row];
     }
+  };
+  if (nsteps > 0) {
+    load_step(0);
+    store_scales(st[0]);
+    store_codes(st[0]);
+    __syncthreads();
+    read_stage(st[0]);
+  }
+  // Step s: the raw codes and scales of stage s & 1 are already in
+  // registers.  The next step's stage is loaded and stored during slices
+  // 0..5; its raw registers are dead once slice 7 has been dequantized
+  // (during slice 6), so the barrier comes before slice 7 and the next
+  // stage's LDS reads overlap slice 7's MFMAs instead of stalling the top of
+  // the next step.  The stage written during step s + 1 (= s & 1) was last
+  // read before this barrier.  Every step loads and stores a next step (the
+  // last one re-reads itself into the buffer nobody reads again): with no
+  // branch around them the loads and LDS writes share one scheduling region
+  // with the MFMAs.
+  for (int s = 0; s < nsteps; ++s) {
+    load_step(s + 1 < nsteps ? s + 1 : s);
     Frag f0, f1;
     dequant_slice<0>(f0, a_raw, b_raw, a_sc, b_sc);
     pipelined_slice<0>(acc, f0, f1, a_raw, b_raw, a_sc, b_sc);
@@ -403,10 +412,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level(Params p) {
     store_scales(st[(s + 1) & 1]);
     pipelined_slice<4>(acc, f0, f1, a_raw, b_raw, a_sc, b_sc);
     pipelined_slice<5>(acc, f1, f0, a_raw, b_raw, a_sc, b_sc);
-    pipelined_slice<6>(acc, f0, f1, a_raw, b_raw, a_sc, b_sc);
-    pipelined_slice<7>(acc, f1, f0, a_raw, b_raw, a_sc, b_sc);
     store_codes(st[(s + 1) & 1]);
+    pipelined_slice<6>(acc, f0, f1, a_raw, b_raw, a_sc, b_sc);
     __syncthreads();
+    read_stage(st[(s + 1) & 1]);
+    pipelined_slice<7>(acc, f1, f0, a_raw, b_raw, a_sc, b_sc);
   }
 
   float scale = FMT == kUE ? 1024.0f : 1.0f;   // undo the two 2^-5 scale shifts
