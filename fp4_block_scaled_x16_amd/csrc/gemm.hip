@@ -147,21 +147,30 @@ __device__ __forceinline__ void epilogue(const Params& p, floatx16 (&acc)[4][4],
 // ------------------------------------------------------- NVFP4 / UE5M3 --
 constexpr int kBK2 = 128;   // K per step: 64 code bytes and 8 scales per row
 
-// fp16 copy of a block scale, replicated in both halves for v_pk_mul_f16.
-// E4M3 decodes with the hardware FP8 convert (exact, subnormals included);
-// UE5M3 is decoded arithmetically and pre-multiplied by 2^-5 (exact).
+// Two consecutive block scales (codes in bits 0-7 and 8-15) as an fp16
+// pair, block 2k in the low half.  E4M3 uses the packed hardware FP8 -> fp16
+// convert with a unit scale (exact: every E4M3 value, subnormals included,
+// is an fp16 value); UE5M3 is decoded arithmetically and pre-multiplied by
+// 2^-5 (exact).
 template <int FMT>
-__device__ __forceinline__ uint32_t scale_half2(uint32_t code) {
-  float s;
-  if constexpr (FMT == kNV) s = __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(code), 0);
-  else s = scale_m3_decode<15>(code) * 0x1p-5f;
-  const _Float16 hs = static_cast<_Float16>(s);        // exact
-  const uint32_t b = __builtin_bit_cast(uint16_t, hs);
-  return b | (b << 16);
+__device__ __forceinline__ uint32_t scale_pair_f16(uint32_t two_codes) {
+  if constexpr (FMT == kNV) {
+    return __builtin_bit_cast(uint32_t,
+                              __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(two_codes, 1.0f, false));
+  } else {
+    const _Float16 lo = static_cast<_Float16>(scale_m3_decode<15>(two_codes & 0xFFu) * 0x1p-5f);
+    const _Float16 hi =
+        static_cast<_Float16>(scale_m3_decode<15>((two_codes >> 8) & 0xFFu) * 0x1p-5f);
+    return __builtin_bit_cast(uint32_t, half2v{lo, hi});
+  }
 }
 
-__device__ __forceinline__ half8 dequant8(uint32_t codes, uint32_t sc2) {
-  const half2v s = __builtin_bit_cast(half2v, sc2);
+// Eight E2M1 codes times one block scale (exact in fp16): the scale is one
+// half of an fp16 pair, broadcast by the packed multiply's operand select.
+template <int HALF>
+__device__ __forceinline__ half8 dequant8(uint32_t codes, uint32_t pair) {
+  const half2v sp = __builtin_bit_cast(half2v, pair);
+  const half2v s = HALF ? half2v{sp[1], sp[1]} : half2v{sp[0], sp[0]};
   half2v p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0);
   half2v p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1);
   half2v p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2);
@@ -176,8 +185,8 @@ __device__ __forceinline__ half8 dequant8(uint32_t codes, uint32_t sc2) {
 struct Stage2 {
   // codes: [operand][chunk q 0..3][row slot][16 B], slot = row ^ (q << 2)
   uint4 codes[2][4][256];
-  // scales: [operand][half h][row][4 x half2] for the 8 blocks of the step
-  uint4 scales[2][2][256];
+  // scales: [operand][half h][row] -> fp16 pairs of blocks 4h..4h+3 of the step
+  uint2 scales[2][2][256];
 };
 
 // Fragments of one MFMA K slice (16 K-values): lane half h holds the slice's
@@ -188,19 +197,15 @@ struct Frag {
 
 template <int KS>
 __device__ __forceinline__ void dequant_slice(Frag& f, const uint32_t (&a_raw)[4][8],
-                                              const uint32_t (&b_raw)[4][8], const uint4 (&a_sc)[4],
-                                              const uint4 (&b_sc)[4]) {
-  constexpr int W = KS >> 1;     // scale word: one 16-element block per two slices
+                                              const uint32_t (&b_raw)[4][8], const uint2 (&a_sc)[4],
+                                              const uint2 (&b_sc)[4]) {
+  constexpr int W = KS >> 1;     // block of the lane's 4: one 16-element block per two slices
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
-    const uint32_t sc = W == 0 ? a_sc[mi].x : W == 1 ? a_sc[mi].y : W == 2 ? a_sc[mi].z : a_sc[mi].w;
-    f.a[mi] = dequant8(a_raw[mi][KS], sc);
-  }
+  for (int mi = 0; mi < 4; ++mi)
+    f.a[mi] = dequant8<W & 1>(a_raw[mi][KS], (W >> 1) ? a_sc[mi].y : a_sc[mi].x);
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
-    const uint32_t sc = W == 0 ? b_sc[ni].x : W == 1 ? b_sc[ni].y : W == 2 ? b_sc[ni].z : b_sc[ni].w;
-    f.b[ni] = dequant8(b_raw[ni][KS], sc);
-  }
+  for (int ni = 0; ni < 4; ++ni)
+    f.b[ni] = dequant8<W & 1>(b_raw[ni][KS], (W >> 1) ? b_sc[ni].y : b_sc[ni].x);
 }
 
 __device__ __forceinline__ void mfma_slice(floatx16 (&acc)[4][4], const Frag& f) {
@@ -226,7 +231,7 @@ template <int KS>
 __device__ __forceinline__ void pipelined_slice(floatx16 (&acc)[4][4], const Frag& cur, Frag& nxt,
                                                 const uint32_t (&a_raw)[4][8],
                                                 const uint32_t (&b_raw)[4][8],
-                                                const uint4 (&a_sc)[4], const uint4 (&b_sc)[4]) {
+                                                const uint2 (&a_sc)[4], const uint2 (&b_sc)[4]) {
   if constexpr (KS + 1 < 8) dequant_slice<KS + 1>(nxt, a_raw, b_raw, a_sc, b_sc);
   mfma_slice(acc, cur);
   interleave_slice();
@@ -331,15 +336,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level(Params p) {
     for (int o = 0; o < 2; ++o) {
       const bool rv = valid[o] & 16u;
       const bool bytes = FAST && !((SCV >> o) & 1);
-      uint32_t h[8];
+      // fp16 pairs of the step's 8 scale codes (pair k: blocks 2k, 2k + 1);
+      // strided scales arrive as separate bytes, each pair needs only its two
+      uint32_t pr[4];
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb) {
-        const uint32_t code = bytes ? rsb[o][kb]
-                                    : ((kb < 4 ? rs[o].x : rs[o].y) >> (8 * (kb & 3))) & 0xFFu;
-        h[kb] = rv ? scale_half2<FMT>(code) : 0u;
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t two = bytes ? rsb[o][2 * k] | (rsb[o][2 * k + 1] << 8)
+                                   : (k < 2 ? rs[o].x : rs[o].y) >> (16 * (k & 1));
+        pr[k] = scale_pair_f16<FMT>(two);
       }
-      S.scales[o][0][t] = make_uint4(h[0], h[1], h[2], h[3]);
-      S.scales[o][1][t] = make_uint4(h[4], h[5], h[6], h[7]);
+      S.scales[o][0][t] = rv ? make_uint2(pr[0], pr[1]) : make_uint2(0u, 0u);
+      S.scales[o][1][t] = rv ? make_uint2(pr[2], pr[3]) : make_uint2(0u, 0u);
     }
   };
   auto store_codes = [&](Stage2& S) {
@@ -362,7 +369,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level(Params p) {
 
   const int i = lane & 31, h = lane >> 5;
   uint32_t a_raw[4][8], b_raw[4][8];
-  uint4 a_sc[4], b_sc[4];
+  uint2 a_sc[4], b_sc[4];
   // this lane's raw codes (its K half of the step) and decoded scales
   auto read_stage = [&](const Stage2& S) {
 #pragma unroll
