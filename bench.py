@@ -52,7 +52,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2, choices=(2, 3, 4, 5))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--cpu-tokens", type=int, default=8192)
     ap.add_argument("--counters-run", action="store_true",
                     help="run each op of the step once, eagerly, then a 512 MiB calibration "
                          "kernel, for rocprofv3 --pmc; prints nothing else")
@@ -402,7 +402,7 @@ def main():
     traffic = read_traffic(khash) if cfg == 2 else None
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic,
-                "kernel": "k_gemm_two_level<NVFP4>" if fmt == "nvfp4" else
+                "kernel": "k_gemm_two_level_dma<NVFP4>" if fmt == "nvfp4" else
                           ("k_gemm_two_level<UE5M3>" if fmt == "ue5m3" else "k_gemm_mx_tiled"),
                 "flops_per_launch": per_launch, "avg_launch_ms": round(avg_ms, 4),
                 "kernel_source_sha256_16": khash}
