@@ -5,22 +5,30 @@
 //
 //   D[M, N] (+)= s_A s_B sum_k a[m, k] b[n, k],   a = e2m1 * scale ("TN")
 //
-// Two kernels share one skeleton: a 256 x 256 output tile per workgroup,
+// Every kernel uses one skeleton: a 256 x 256 output tile per workgroup,
 // four waves in a 2 x 2 arrangement (128 x 128 each, 4 x 4 MFMA tiles of
-// 32 x 32), FP4 codes and scales staged through double-buffered LDS with one
-// barrier per K step, the next K step's global loads in flight while the
-// current one is multiplied.
+// 32 x 32), FP4 codes and scales staged through LDS, one barrier per K step,
+// the next K step's loads in flight while the current one is multiplied,
+// and an XCD-aware grouped tile order.
 //
-// * NVFP4 / UE5M3 (k_gemm_two_level): e2m1 * scale is exact in fp16 (E4M3
-//   products lie in [2^-10, 2688]; UE5M3 scales are pre-multiplied by 2^-5
-//   so products lie in [2^-23, 23040] on fp16's 2^-24 grid), so every lane
-//   dequantizes its own MFMA fragment in registers -- a hardware FP4->fp16
-//   convert and a packed fp16 multiply by the block scale -- and feeds
+// * NVFP4 / UE5M3: e2m1 * scale is exact in fp16 (E4M3 products lie in
+//   [2^-10, 2688]; UE5M3 scales are pre-multiplied by 2^-5 so products lie
+//   in [2^-23, 23040] on fp16's 2^-24 grid), so every lane dequantizes its
+//   own MFMA fragment in registers -- a hardware FP4->fp16 convert and a
+//   packed fp16 multiply by the block scale -- and feeds
 //   v_mfma_f32_32x32x16_f16 with fp32 accumulation.  The 2^-5 shifts and
 //   the tensor scales are applied to the fp32 result.
-// * MXFP4 (k_gemm_mx): gfx950's scaled MFMA takes FP4 operands and one E8M0
-//   scale per 32 K-values per lane, which is exactly an MXFP4 block, so the
-//   codes go from LDS to v_mfma_scale_f32_32x32x64_f8f6f4 untouched.
+//     k_gemm_two_level_dma  NVFP4, K % 256 == 0, 16-byte code rows: codes
+//                           go to LDS by DMA (global_load_lds).
+//     k_gemm_two_level      every other shape (and UE5M3): codes staged
+//                           through registers, ragged edges masked.
+// * MXFP4: gfx950's scaled MFMA takes FP4 operands and one E8M0 scale per 32
+//   K-values per lane, which is exactly an MXFP4 block, so the codes go from
+//   LDS to v_mfma_scale_f32_32x32x64_f8f6f4 untouched.
+//     k_gemm_mx_tiled  TILED scales, K % 512 == 0: K step 256, codes and
+//                      scales by DMA in whole 128-byte lines.
+//     k_gemm_mx_ring   K % 512 == 0, other scale layouts: 4-stage K-128 DMA ring.
+//     k_gemm_mx        every other shape: register-staged, edges masked.
 //
 // The order of K inside one K step is free as long as A and B agree: lane
 // half h of a wave owns a contiguous half of the step's K range for both
