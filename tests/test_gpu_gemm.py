@@ -71,6 +71,12 @@ CASES = [
     ("mxfp4", "row", "row", 600, 520, 224),
     ("mxfp4", "row", "row", 33, 17, 32),
     ("nvfp4", "col", "col", 512, 264, 304),
+    # NVFP4 with K a multiple of 256: codes by DMA, ragged tiles with clamped
+    # rows, every scale-loader variant (contiguous / strided for A and B)
+    ("nvfp4", "row", "row", 300, 264, 512),
+    ("nvfp4", "row", "2dT", 272, 336, 512),
+    ("nvfp4", "2dT", "row", 336, 280, 768),
+    ("nvfp4", "2dT", "2dT", 272, 304, 256),
     # MXFP4 with K a multiple of 512: the LDS-DMA ring kernel (one turn of
     # the ring only, ragged tiles with clamped rows, several turns)
     ("mxfp4", "row", "row", 300, 264, 512),
@@ -113,7 +119,8 @@ def test_gemm_tiled_scales(fmt, la, lb, M, N, K, sa_layout, sb_layout):
 def test_gemm_small(fmt, la, lb, M, N, K):
     # A operand [M, K]; B operand [N, K] (for 2dT, W is [K, N])
     a_shape = (M, K) if la == "row" else (K, M)
-    a_bits = inputs.activations(a_shape, cfg_seed=50)
+    a_bits = (inputs.weights(a_shape, cfg_seed=50) if la.startswith("2d")
+              else inputs.activations(a_shape, cfg_seed=50))
     if lb == "row":
         b_bits = inputs.weights((N, K), cfg_seed=50)
     elif lb == "col":
