@@ -106,7 +106,7 @@ def summarize_pmc(fetch_csv, write_csv, cfg):
     fetch, f_fac = out["FETCH_SIZE"]
     write, w_fac = out["WRITE_SIZE"]
     names = ["fprop", "dgrad", "wgrad"][:len(fetch)]
-    lines = ["kernel_source_sha256_16=%s" % source_hash("gemm.hip", "fp4_device.hpp"),
+    lines = ["kernel_source_sha256_16=%s" % source_hash(*GEMM_SOURCES),
              "calibration_fetch_factor=%.4f" % f_fac, "calibration_write_factor=%.4f" % w_fac]
     tot = []
     for i, n in enumerate(names):
@@ -116,6 +116,11 @@ def summarize_pmc(fetch_csv, write_csv, cfg):
         lines.append("%s_write_bytes=%.0f" % (n, wb))
     lines.append("hbm_bytes_per_launch=%.0f" % float(np.mean(tot)))
     print("\n".join(lines))
+
+
+# every source the GEMM kernels are built from
+GEMM_SOURCES = ("gemm.hip", "gemm_common.hpp", "gemm_nv.hip", "gemm_nv_dma.hpp", "gemm_nv_dma256.hip",
+                "gemm_nv_dma192.hip", "gemm_mx.hip", "gemm_mx_dma.hip", "fp4_device.hpp")
 
 
 def source_hash(*names):
@@ -398,7 +403,7 @@ def main():
     per_launch = g_flops / len(gemm_names)
     achieved = per_launch / (avg_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS["fp4" if fmt == "mxfp4" else "fp16"]
-    khash = source_hash("gemm.hip", "fp4_device.hpp")
+    khash = source_hash(*GEMM_SOURCES)
     traffic = read_traffic(khash) if cfg == 2 else None
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic,

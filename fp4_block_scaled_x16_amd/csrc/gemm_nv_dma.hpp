@@ -1,0 +1,213 @@
+// NVFP4 block-scaled GEMM with the codes moved into LDS by DMA (K a
+// multiple of 256, 16-byte-aligned code rows).  The kernel template is
+// instantiated per tile height in gemm_nv_dma256.hip and gemm_nv_dma192.hip
+// (two translation units, so the two sets compile in parallel).
+#pragma once
+
+#include "gemm_common.hpp"
+
+namespace fp4gemm {
+namespace {
+
+// ------------------------------------------- NVFP4 / UE5M3, codes by DMA ---
+// The two-level product for K a multiple of 256 and 16-byte-aligned code
+// rows: the same per-lane dequantization and slice pipeline as
+// k_gemm_two_level, but the codes go from global memory straight into LDS
+// (global_load_lds, 16 bytes per lane) instead of through registers and LDS
+// stores, and ragged M / N read the last valid row (never stored).  Block
+// scales are still loaded to registers and decoded once per K step by the
+// loading thread.  Codes and scales of each of the two stages are separate
+// __shared__ variables named with compile-time indices, so the compiler can
+// tell the DMA targets from the LDS the waves read and write.
+//
+// MI is the number of 32-row MFMA tiles per wave in M: 4 gives the usual
+// 256 x 256 tile, 3 a 192 x 256 tile (each wave 96 x 128), for shapes where
+// 256-row tiles would leave part of the chip idle in the last round (e.g.
+// 6144 output rows: 192 tiles of 256 rows on 256 CUs, but 256 of 192 rows).
+struct DmaSrcNv {
+  const uint8_t* base[2];       // operand code matrices (uniform)
+  uint32_t off[2][4];           // this lane's 16 bytes of rows wave*(16 J) + 16j + lane/4
+};                              // (the host keeps every offset below 2^31)
+
+// Operand o's tile has 64 J rows (J = MI for A, 4 for B); wave w loads rows
+// 16 J w .. 16 J w + 16 J - 1, 16 rows per instruction.
+template <int MI>
+__device__ __forceinline__ void dma_codes_nv(uint4 (&dst)[2][1024], const DmaSrcNv& src,
+                                             int64_t step, int wave) {
+  const int64_t cb = step * (kBK2 / 2);
+#pragma unroll
+  for (int o = 0; o < 2; ++o) {
+    constexpr int J[2] = {MI, 4};
+#pragma unroll
+    for (int j = 0; j < J[o]; ++j)
+      __builtin_amdgcn_global_load_lds(src.base[o] + cb + src.off[o][j],
+                                       &dst[o][wave * (64 * J[o]) + j * 64], 16, 0, 0);
+  }
+}
+
+template <int FMT, int SCV, int MI>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level_dma(Params p) {
+  constexpr int BM = 64 * MI;
+  __shared__ uint4 cst0[2][1024], cst1[2][1024];   // [operand][row * 4 + (chunk ^ swizzle)]
+  __shared__ uint2 sst0[2][2][256], sst1[2][2][256];  // [operand][half][row] fp16 scale pairs
+  int tm, tn;
+  tile_coords(p, tm, tn);
+  const int64_t m0 = static_cast<int64_t>(tm) * BM, n0 = static_cast<int64_t>(tn) * kBN;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nsteps = static_cast<int>(p.K / kBK2);
+  const int64_t lim[2] = {p.M, p.N};
+  const int64_t base[2] = {m0, n0};
+
+  DmaSrcNv src;
+#pragma unroll
+  for (int o = 0; o < 2; ++o) {
+    src.base[o] = p.codes[o];
+    const int J = o == 0 ? MI : 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = wave * (16 * J) + j * 16 + (lane >> 2);
+      const int q = (lane & 3) ^ dma_swizzle(row);
+      const int64_t r = min(base[o] + row, lim[o] - 1);
+      src.off[o][j] = static_cast<uint32_t>(r * p.ld[o] + q * 16);
+    }
+  }
+  // scales of row t (clamped), K step s: a per-lane offset plus a uniform
+  // per-step stride (one 2 KiB atom TILED, 8 K-blocks otherwise).  With
+  // BM < 256, threads t >= BM load and store A scales that are never read.
+  uint32_t soff[2];
+  int64_t sstep[2];
+#pragma unroll
+  for (int o = 0; o < 2; ++o) {
+    soff[o] = static_cast<uint32_t>(scale_ptr(p, o, min(base[o] + t, lim[o] - 1), 0) - p.scales[o]);
+    sstep[o] = p.tiled[o] ? 2048 : 8 * p.s_kblk[o];
+  }
+
+  uint2 rs[2];
+  uint32_t rsb[2][8];
+  auto load_scales = [&](int s) {
+#pragma unroll
+    for (int o = 0; o < 2; ++o) {
+      const uint8_t* sp = p.scales[o] + s * sstep[o] + soff[o];
+      if ((SCV >> o) & 1) {
+        rs[o] = *reinterpret_cast<const uint2*>(sp);
+      } else {
+        const int64_t st = p.s_kblk[o];
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) rsb[o][kb] = sp[kb * st];
+      }
+    }
+  };
+  auto store_scales = [&](uint2 (&S)[2][2][256]) {
+#pragma unroll
+    for (int o = 0; o < 2; ++o) {
+      const bool bytes = !((SCV >> o) & 1);
+      uint32_t pr[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t two = bytes ? rsb[o][2 * k] | (rsb[o][2 * k + 1] << 8)
+                                   : (k < 2 ? rs[o].x : rs[o].y) >> (16 * (k & 1));
+        pr[k] = scale_pair_f16<FMT>(two);
+      }
+      S[o][0][t] = make_uint2(pr[0], pr[1]);
+      S[o][1][t] = make_uint2(pr[2], pr[3]);
+    }
+  };
+
+  floatx16 acc[MI][4];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = floatx16{};
+
+  const int i = lane & 31, h = lane >> 5;
+  uint32_t a_raw[MI][8], b_raw[4][8];
+  uint2 a_sc[MI], b_sc[4];
+  auto read_stage = [&](const uint4 (&C)[2][1024], const uint2 (&S)[2][2][256]) {
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int row = wm * (MI * 32) + mi * 32 + i;
+      const int sw = dma_swizzle(row);
+      const uint4 c0 = C[0][row * 4 + ((2 * h) ^ sw)];
+      const uint4 c1 = C[0][row * 4 + ((2 * h + 1) ^ sw)];
+      a_raw[mi][0] = c0.x; a_raw[mi][1] = c0.y; a_raw[mi][2] = c0.z; a_raw[mi][3] = c0.w;
+      a_raw[mi][4] = c1.x; a_raw[mi][5] = c1.y; a_raw[mi][6] = c1.z; a_raw[mi][7] = c1.w;
+      a_sc[mi] = S[0][h][row];
+    }
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      const int row = wn * 128 + ni * 32 + i;
+      const int sw = dma_swizzle(row);
+      const uint4 c0 = C[1][row * 4 + ((2 * h) ^ sw)];
+      const uint4 c1 = C[1][row * 4 + ((2 * h + 1) ^ sw)];
+      b_raw[ni][0] = c0.x; b_raw[ni][1] = c0.y; b_raw[ni][2] = c0.z; b_raw[ni][3] = c0.w;
+      b_raw[ni][4] = c1.x; b_raw[ni][5] = c1.y; b_raw[ni][6] = c1.z; b_raw[ni][7] = c1.w;
+      b_sc[ni] = S[1][h][row];
+    }
+  };
+
+  // Step s on stage C (raw codes and scales already in registers) while the
+  // next step (s + 1, or s again on the last step: the other stage is not
+  // read afterwards) fills stage N: its scale loads and code DMA are issued
+  // at the top; after slice 6 the DMA has landed and the decoded scales are
+  // stored (one wait for both), then the barrier, and the next stage's LDS
+  // reads overlap slice 7.  N was last read before the previous barrier.
+  auto step = [&](uint4 (&Nc)[2][1024], uint2 (&Ns)[2][2][256], int s) {
+    const int nxt = s + 1 < nsteps ? s + 1 : s;
+    load_scales(nxt);
+    dma_codes_nv<MI>(Nc, src, nxt, wave);
+    __builtin_amdgcn_sched_barrier(0);     // keep the loads at the top of the step
+    FragT<MI> f0, f1;
+    dequant_slice<0>(f0, a_raw, b_raw, a_sc, b_sc);
+    pipelined_slice<0>(acc, f0, f1, a_raw, b_raw, a_sc, b_sc);
+    pipelined_slice<1>(acc, f1, f0, a_raw, b_raw, a_sc, b_sc);
+    pipelined_slice<2>(acc, f0, f1, a_raw, b_raw, a_sc, b_sc);
+    pipelined_slice<3>(acc, f1, f0, a_raw, b_raw, a_sc, b_sc);
+    pipelined_slice<4>(acc, f0, f1, a_raw, b_raw, a_sc, b_sc);
+    pipelined_slice<5>(acc, f1, f0, a_raw, b_raw, a_sc, b_sc);
+    pipelined_slice<6>(acc, f0, f1, a_raw, b_raw, a_sc, b_sc);
+    wait_vmcnt<0>();
+    store_scales(Ns);
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // this wave's LDS stores done
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    read_stage(Nc, Ns);
+    pipelined_slice<7>(acc, f1, f0, a_raw, b_raw, a_sc, b_sc);
+  };
+
+  load_scales(0);
+  dma_codes_nv<MI>(cst0, src, 0, wave);
+  store_scales(sst0);
+  wait_vmcnt<0>();
+  ring_barrier();
+  read_stage(cst0, sst0);
+  for (int s = 0; s < nsteps; s += 2) {
+    step(cst1, sst1, s);
+    step(cst0, sst0, s + 1);
+  }
+
+  float scale = FMT == kUE ? 1024.0f : 1.0f;   // undo the two 2^-5 scale shifts
+  if (p.s_dec[0]) scale *= *p.s_dec[0];
+  const float sb = p.s_dec[1] ? *p.s_dec[1] : 1.0f;
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] *= scale;
+  epilogue(p, acc, sb, m0, n0, wm, wn, lane);
+}
+
+}  // namespace
+
+// Launch the MI-variant for scale-loader variant `scv` (bit o: operand o's
+// scales of one row and K step are one aligned 8-byte word).
+template <int MI>
+hipError_t launch_two_level_dma_mi(int scv, const Params& p, hipStream_t s) {
+  constexpr void (*dnv[4])(Params) = {k_gemm_two_level_dma<kNV, 0, MI>, k_gemm_two_level_dma<kNV, 1, MI>,
+                                      k_gemm_two_level_dma<kNV, 2, MI>, k_gemm_two_level_dma<kNV, 3, MI>};
+  hipLaunchKernelGGL(dnv[scv], dim3(p.tiles_m * p.tiles_n), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace fp4gemm

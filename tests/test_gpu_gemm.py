@@ -77,6 +77,10 @@ CASES = [
     ("nvfp4", "row", "2dT", 272, 336, 512),
     ("nvfp4", "2dT", "row", 336, 280, 768),
     ("nvfp4", "2dT", "2dT", 272, 304, 256),
+    # ... tile height: shapes that fill at most one round of the CUs take
+    # 192-row tiles (all of the above); this one has 192 256-row tiles but
+    # 264 192-row tiles, so on a 256-CU device it takes 256-row tiles
+    ("nvfp4", "row", "row", 2048, 6144, 256),
     # MXFP4 with K a multiple of 512: the LDS-DMA ring kernel (one turn of
     # the ring only, ragged tiles with clamped rows, several turns)
     ("mxfp4", "row", "row", 300, 264, 512),
