@@ -5,13 +5,13 @@ W [6144, 2048], dY [8192, 6144]) in NVFP4, on synthetic seeded tensors
 already resident in HBM.  A step runs, on one stream:
 
   tensor amax of X, W, dY
-  quantize X rowwise (RNE)         -> Fprop A
-  quantize W 16x16 2D (+ W^T)      -> Fprop B, Dgrad B
-  quantize dY rowwise (SR)         -> Dgrad A
-  quantize dY colwise (SR)         -> Wgrad A
-  quantize X colwise (RNE)         -> Wgrad B
-  GEMMs Fprop, Dgrad, Wgrad        (fp32 outputs)
+  quantize X rowwise + colwise (RNE, one read)   -> Fprop A, Wgrad B
+  quantize W 16x16 2D (+ W^T)                    -> Fprop B, Dgrad B
+  quantize dY rowwise + colwise (SR, one read)   -> Dgrad A, Wgrad A
+  GEMMs Fprop, Dgrad, Wgrad                      (fp32 outputs)
 
+(--separate-quant: the rowwise and colwise quantizations of X and dY as
+four kernels, each reading its tensor.)
 with event counters on every quantization.  The step is captured once as a
 HIP graph and replayed (after a bitwise check of replays against the eager
 step); per-kernel durations come from graphs of repeated launches of each
@@ -20,7 +20,7 @@ op, timed with events on the launch stream.  Printed: one JSON line whose
 per-kernel timings and rates (`parts`), the roofline of the dominant kernel
 and the CPU oracle timed on a bounded slab of the same workload.
 
-  python bench.py [--steps K] [--warmup W] [--config 2|3|4|5] [--no-cpu]
+  python bench.py [--steps K] [--warmup W] [--config 2|3|4|5] [--no-cpu] [--separate-quant]
 """
 import argparse
 import hashlib
@@ -43,6 +43,9 @@ PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_gemm_nvfp4_1.2b_ffn.tx
 B_AMAX = 2.0
 B_Q1D = {"nvfp4": 2.0 + 0.5 + 1.0 / 16, "ue5m3": 2.0 + 0.5 + 1.0 / 16, "mxfp4": 2.0 + 0.5 + 1.0 / 32}
 B_Q2D_T = 2.0 + 0.5 + 0.5 + 1.0 / 256
+# one read, rowwise and colwise codes + scales written
+B_DUAL = {"nvfp4": 2.0 + 2 * (0.5 + 1.0 / 16), "ue5m3": 2.0 + 2 * (0.5 + 1.0 / 16),
+          "mxfp4": 2.0 + 2 * (0.5 + 1.0 / 32)}
 
 
 def parse():
@@ -53,6 +56,9 @@ def parse():
     ap.add_argument("--config", type=int, default=2, choices=(2, 3, 4, 5))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=8192)
+    ap.add_argument("--separate-quant", action="store_true",
+                    help="quantize X and dY rowwise and colwise in separate kernels (two reads "
+                         "each) instead of one dual kernel per tensor")
     ap.add_argument("--counters-run", action="store_true",
                     help="run each op of the step once, eagerly, then a 512 MiB calibration "
                          "kernel, for rocprofv3 --pmc; prints nothing else")
@@ -150,7 +156,7 @@ def read_traffic(kernel_hash):
         return None
 
 
-def build_step(cfg, dev):
+def build_step(cfg, dev, dual=True):
     """Inputs on the device and the list of (name, kind, units, fn) ops."""
     import torch
     from fp4_block_scaled_x16_amd import api, inputs
@@ -217,20 +223,43 @@ def build_step(cfg, dev):
             st[out] = api.quantize(x, fmt, counters=cnt, **kw2)
         return f
 
-    ops.append(("quant X row", "hbm", b1 * X.numel(), q("X", X, "qx", target=target_x)))
+    def qd(name, x, out_r, out_c, **kw):
+        """Rowwise and colwise codes of x from one read (RHT on the colwise side)."""
+        def f():
+            kw2 = dict(kw, scale_layout="tiled")
+            if two_level:
+                kw2["amax_in"] = st["amax_" + name]
+                kw2["amax_t_in"] = st[("amax_rot_" if kw.get("rht") else "amax_") + name]
+            st[out_r], st[out_c] = api.quantize_dual(x, fmt, counters=cnt, **kw2)
+        return f
+
+    bd = B_DUAL[fmt]
+    if dual:
+        ops.append(("quant X row+col", "hbm", bd * X.numel(),
+                    qd("X", X, "qx", "qxc", rht=rht, signs=sig if rht else 0, target=target_x)))
+    else:
+        ops.append(("quant X row", "hbm", b1 * X.numel(), q("X", X, "qx", target=target_x)))
     if two_level:
         ops.append(("quant W 2d+T", "hbm", B_Q2D_T * W.numel(),
                     q("W", W, "qw", block="2d", emit_transpose=True, target=target_w)))
+    elif dual:
+        ops.append(("quant W row+col", "hbm", bd * W.numel(), qd("W", W, "qw", "qwc")))
     else:
         ops.append(("quant W row", "hbm", b1 * W.numel(), q("W", W, "qw")))
         ops.append(("quant W col", "hbm", b1 * W.numel(), q("W", W, "qwc", orient="col")))
-    ops.append(("quant dY row SR", "hbm", b1 * dY.numel(),
-                q("dY", dY, "qdy", rnd="sr", seed=1, offset=0, target=target_dy)))
-    ops.append(("quant dY col SR", "hbm", b1 * dY.numel(),
-                q("dY", dY, "qdyc", orient="col", rnd="sr", seed=1, offset=1, rht=rht,
-                  signs=sig if rht else 0, target=target_dy)))
-    ops.append(("quant X col", "hbm", b1 * X.numel(),
-                q("X", X, "qxc", orient="col", rht=rht, signs=sig if rht else 0, target=target_x)))
+    if dual:
+        ops.append(("quant dY row+col SR", "hbm", bd * dY.numel(),
+                    qd("dY", dY, "qdy", "qdyc", rnd="sr", seed=1, offset=0, offset_t=1, rht=rht,
+                       signs=sig if rht else 0, target=target_dy)))
+    else:
+        ops.append(("quant dY row SR", "hbm", b1 * dY.numel(),
+                    q("dY", dY, "qdy", rnd="sr", seed=1, offset=0, target=target_dy)))
+        ops.append(("quant dY col SR", "hbm", b1 * dY.numel(),
+                    q("dY", dY, "qdyc", orient="col", rnd="sr", seed=1, offset=1, rht=rht,
+                      signs=sig if rht else 0, target=target_dy)))
+        ops.append(("quant X col", "hbm", b1 * X.numel(),
+                    q("X", X, "qxc", orient="col", rht=rht, signs=sig if rht else 0,
+                      target=target_x)))
 
     def g(a, la, b, lb, M, N, K, out):
         def f():
@@ -317,7 +346,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cfg = args.config
-    ops, cnt, host, fmt = build_step(cfg, dev)
+    ops, cnt, host, fmt = build_step(cfg, dev, dual=not args.separate_quant)
     if args.counters_run:
         counters_run(ops)
         return
@@ -423,7 +452,8 @@ def main():
         "data": "synthetic (seeded PCG64, bf16 inputs resident in HBM)",
         "config": {"workload": c["name"], "format": fmt, "tokens": c["tokens"], "d_in": c["d_in"],
                    "d_out": c["d_out"], "gemms": "fprop, dgrad, wgrad", "scales_1d": "tiled",
-                   "quantizations": len([1 for (n, k, u, _) in ops if n.startswith("quant")])},
+                   "quantize_kernels": len([1 for (n, k, u, _) in ops if n.startswith("quant")]),
+                   "dual_quantize": not args.separate_quant},
         "quantize": {"GBps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
                      "frac_hbm": round(q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "ms": round(q_ms, 4)},

@@ -67,11 +67,14 @@ def load_library(path=LIB_PATH):
     lib.fp4_amax.argtypes = [vp, i64, i64, i64, i32, u32, vp, vp]
     lib.fp4_quantize.argtypes = [ctypes.POINTER(QuantDesc), vp, i64, i64, i64, vp, vp, vp, vp,
                                  vp, vp, vp]
+    lib.fp4_quantize_dual.argtypes = [ctypes.POINTER(QuantDesc), ctypes.POINTER(QuantDesc), vp, i64,
+                                      i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.fp4_dequantize.argtypes = [i32, i32, i32, vp, vp, vp, i64, i64, vp, i32, vp]
     lib.fp4_rht16.argtypes = [vp, i64, i64, i64, u32, vp, vp]
     lib.fp4_gemm.argtypes = [ctypes.POINTER(Operand), ctypes.POINTER(Operand), i64, i64, i64, vp,
                              i64, i32, vp]
-    for f in ("fp4_amax", "fp4_quantize", "fp4_dequantize", "fp4_rht16", "fp4_gemm"):
+    for f in ("fp4_amax", "fp4_quantize", "fp4_quantize_dual", "fp4_dequantize", "fp4_rht16",
+              "fp4_gemm"):
         getattr(lib, f).restype = ctypes.c_int
     lib.fp4_status_string.argtypes = [ctypes.c_int]
     lib.fp4_status_string.restype = ctypes.c_char_p
@@ -204,6 +207,55 @@ def quantize(x, fmt="nvfp4", block="1d", orient="row", rnd="rne", seed=0, offset
                             _ptr(scales), _ptr(codes_t), _ptr(am), _ptr(s_dec), _ptr(counters),
                             _stream(dev)), "fp4_quantize")
     return Quantized(f, blk, rows, cols, codes, scales, s_dec, am, codes_t, layout)
+
+
+def _scales_1d(rows, blocks, layout, dev):
+    if layout == SCALES_TILED:
+        return torch.empty(tiled_scale_bytes(rows, blocks), dtype=torch.uint8, device=dev)
+    return torch.empty((rows, blocks), dtype=torch.uint8, device=dev)
+
+
+def quantize_dual(x, fmt="nvfp4", rnd="rne", seed=0, offset=0, offset_t=None, rht=False, signs=0,
+                  target=448.0, amax_in=None, amax_t_in=None, counters=None,
+                  scale_layout="rowmajor", scale_layout_t=None):
+    """Rowwise and colwise 1D quantization of a bf16 [R, C] matrix from one
+    read: returns (rowwise Quantized [R, C], colwise Quantized of X^T [C, R]).
+
+    Both sides use `rnd` and `seed`; the colwise side uses offset_t (default
+    offset + 1), the RHT (rht/signs) and scale_layout_t (default
+    scale_layout).  amax_in / amax_t_in: None -> computed on the device, else
+    device fp32 [1] tensors read as the given amax of each side.
+    """
+    x = _as_bf16_bits(x)
+    f = _fmt(fmt)
+    R, C = x.shape
+    bs = BLOCK_LEN[f]
+    dev = x.device
+    lay = SCALE_LAYOUTS[scale_layout] if isinstance(scale_layout, str) else int(scale_layout)
+    lay_t = lay if scale_layout_t is None else (
+        SCALE_LAYOUTS[scale_layout_t] if isinstance(scale_layout_t, str) else int(scale_layout_t))
+    if offset_t is None:
+        offset_t = offset + 1
+    codes = torch.empty((R, C // 2), dtype=torch.uint8, device=dev)
+    codes_t = torch.empty((C, R // 2), dtype=torch.uint8, device=dev)
+    scales = _scales_1d(R, C // bs, lay, dev)
+    scales_t = _scales_1d(C, R // bs, lay_t, dev)
+    s_dec = torch.empty(1, dtype=torch.float32, device=dev)
+    s_dec_t = torch.empty(1, dtype=torch.float32, device=dev)
+    am = amax_in if amax_in is not None else torch.empty(1, dtype=torch.float32, device=dev)
+    am_t = amax_t_in if amax_t_in is not None else torch.empty(1, dtype=torch.float32, device=dev)
+    r = SR if rnd == "sr" else RNE
+    d_row = QuantDesc(f, BLOCK_1D, ROWWISE, r, int(seed), int(offset), 0, 0, float(target),
+                      int(amax_in is not None), 0, lay)
+    d_col = QuantDesc(f, BLOCK_1D, COLWISE, r, int(seed), int(offset_t), int(bool(rht)), int(signs),
+                      float(target), int(amax_t_in is not None), 0, lay_t)
+    lib = load_library()
+    _check(lib.fp4_quantize_dual(ctypes.byref(d_row), ctypes.byref(d_col), _ptr(x), R, C,
+                                 x.stride(0), _ptr(codes), _ptr(scales), _ptr(codes_t),
+                                 _ptr(scales_t), _ptr(am), _ptr(am_t), _ptr(s_dec), _ptr(s_dec_t),
+                                 _ptr(counters), _stream(dev)), "fp4_quantize_dual")
+    return (Quantized(f, BLOCK_1D, R, C, codes, scales, s_dec, am, None, lay),
+            Quantized(f, BLOCK_1D, C, R, codes_t, scales_t, s_dec_t, am_t, None, lay_t))
 
 
 def new_counters(device="cuda"):

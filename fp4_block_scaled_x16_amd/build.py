@@ -41,14 +41,28 @@ def _run(cmd):
     return err
 
 
-def build(verbose=False):
+def _stale(obj, src):
+    """True if obj is missing or older than its source or any header."""
+    if not os.path.exists(obj):
+        return True
+    deps = [src] + [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hpp", ".h"))]
+    deps += [os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))]
+    t = os.path.getmtime(obj)
+    return any(os.path.getmtime(d) > t for d in deps)
+
+
+def build(verbose=False, incremental=False):
+    """Compile every source (incremental=True: only those whose object is
+    older than the source or any header) and link the library."""
     os.makedirs(BUILD, exist_ok=True)
     objs, cmds = [], []
     for src in SOURCES:
         obj = os.path.join(BUILD, src + ".o")
         objs.append(obj)
+        if incremental and not _stale(obj, os.path.join(CSRC, src)):
+            continue
         cmds.append([HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj])
-    with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+    with ThreadPoolExecutor(max_workers=max(1, len(cmds))) as ex:
         for err in ex.map(_run, cmds):
             if verbose and err.strip():
                 print(err, file=sys.stderr)
@@ -59,4 +73,4 @@ def build(verbose=False):
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, incremental="--incremental" in sys.argv))

@@ -165,6 +165,99 @@ FP4_EXPORT fp4_status fp4_quantize(const fp4_quant_desc* d, const uint16_t* x, i
   return device_status(e, "fp4_quantize launch");
 }
 
+FP4_EXPORT fp4_status fp4_quantize_dual(const fp4_quant_desc* rd, const fp4_quant_desc* cd,
+                                        const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                                        uint8_t* codes, uint8_t* scales, uint8_t* codes_t,
+                                        uint8_t* scales_t, float* amax, float* amax_t,
+                                        float* s_dec, float* s_dec_t, fp4_counters* counters,
+                                        void* stream) {
+  if (!rd || !cd) return fail(FP4_ERR_ARG, "desc is null");
+  const fp4_quant_desc* ds[2] = {rd, cd};
+  for (int i = 0; i < 2; ++i) {
+    const fp4_quant_desc* d = ds[i];
+    const char* side = i ? "colwise" : "rowwise";
+    if (!valid_format(d->format)) return fail(FP4_ERR_ARG, "%s: bad format %d", side, (int)d->format);
+    if (d->block != FP4_BLOCK_1D && d->block != FP4_BLOCK_2D16)
+      return fail(FP4_ERR_ARG, "%s: bad block %d", side, (int)d->block);
+    if (d->orient != FP4_ROWWISE && d->orient != FP4_COLWISE)
+      return fail(FP4_ERR_ARG, "%s: bad orient %d", side, (int)d->orient);
+    if (d->round != FP4_RNE && d->round != FP4_SR)
+      return fail(FP4_ERR_ARG, "%s: bad round %d", side, (int)d->round);
+    if (d->scale_layout != FP4_SCALES_ROWMAJOR && d->scale_layout != FP4_SCALES_TILED)
+      return fail(FP4_ERR_ARG, "%s: bad scale_layout %d", side, (int)d->scale_layout);
+    if (d->block != FP4_BLOCK_1D) return fail(FP4_ERR_UNSUPPORTED, "%s: dual quantization is 1D", side);
+    if (d->emit_transpose) return fail(FP4_ERR_UNSUPPORTED, "%s: emit_transpose needs 2D16", side);
+    if (d->format != FP4_MXFP4 && !(std::isfinite(d->target) && d->target > 0.0f))
+      return fail(FP4_ERR_ARG, "%s: target must be finite and > 0", side);
+    if (d->amax_given && d->format == FP4_MXFP4)
+      return fail(FP4_ERR_UNSUPPORTED, "%s: MXFP4 has no tensor amax", side);
+  }
+  if (rd->orient != FP4_ROWWISE || cd->orient != FP4_COLWISE)
+    return fail(FP4_ERR_UNSUPPORTED, "descs must be ROWWISE then COLWISE");
+  if (rd->format != cd->format) return fail(FP4_ERR_UNSUPPORTED, "the two formats differ");
+  if (rd->round != cd->round) return fail(FP4_ERR_UNSUPPORTED, "the two rounding modes differ");
+  if (rd->rht) return fail(FP4_ERR_UNSUPPORTED, "RHT needs COLWISE");
+  if (cd->rht && cd->format == FP4_MXFP4) return fail(FP4_ERR_UNSUPPORTED, "RHT needs NVFP4 or UE5M3");
+  if (cd->rht && cd->rht_signs > 0xFFFFu) return fail(FP4_ERR_ARG, "rht_signs must fit in 16 bits");
+  fp4_status st = check_bf16_input(x, rows, cols, ld);
+  if (st) return st;
+  const int bs = block_len(rd->format);
+  if (cols % bs || rows % bs)
+    return fail(FP4_ERR_SHAPE, "rows=%lld and cols=%lld must be multiples of %d", (long long)rows,
+                (long long)cols, bs);
+  const bool two_level = rd->format != FP4_MXFP4;
+  const bool empty = rows == 0 || cols == 0;
+  if (!empty) {
+    if (!codes || !scales || !codes_t || !scales_t) return fail(FP4_ERR_ARG, "codes/scales are null");
+    if (!aligned16(codes) || !aligned16(codes_t))
+      return fail(FP4_ERR_ARG, "codes and codes_t must be 16-byte aligned");
+    if ((rd->scale_layout == FP4_SCALES_TILED && !aligned16(scales)) ||
+        (cd->scale_layout == FP4_SCALES_TILED && !aligned16(scales_t)))
+      return fail(FP4_ERR_ARG, "TILED scales must be 16-byte aligned");
+  }
+  if (two_level) {
+    if (!amax || !amax_t) return fail(FP4_ERR_ARG, "amax/amax_t is null");
+    if (amax == amax_t && (rd->amax_given != cd->amax_given || cd->rht))
+      return fail(FP4_ERR_ARG, "amax and amax_t may share a buffer only without RHT and with "
+                               "the same amax_given");
+  }
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (two_level && !rd->amax_given) {
+    hipError_t e = fp4lib::launch_amax(x, rows, cols, ld, 0, 0, amax, s);
+    if (e != hipSuccess) return device_status(e, "fp4_quantize_dual amax launch");
+  }
+  if (two_level && !cd->amax_given && !(amax_t == amax && !rd->amax_given)) {
+    hipError_t e = fp4lib::launch_amax(x, rows, cols, ld, cd->rht, cd->rht_signs, amax_t, s);
+    if (e != hipSuccess) return device_status(e, "fp4_quantize_dual amax launch");
+  }
+  fp4lib::QuantArgs a[2]{};
+  uint8_t* cs[2] = {codes, codes_t};
+  uint8_t* ss[2] = {scales, scales_t};
+  float* am[2] = {amax, amax_t};
+  float* sd[2] = {s_dec, s_dec_t};
+  for (int i = 0; i < 2; ++i) {
+    a[i].x = x;
+    a[i].rows = rows;
+    a[i].cols = cols;
+    a[i].ld = ld;
+    a[i].codes = cs[i];
+    a[i].scales = ss[i];
+    a[i].amax = am[i];
+    a[i].s_dec = sd[i];
+    a[i].counters = counters;
+    a[i].target = ds[i]->target;
+    a[i].seed = ds[i]->seed;
+    a[i].offset = ds[i]->offset;
+    a[i].rht_signs = ds[i]->rht_signs;
+    a[i].format = ds[i]->format;
+    a[i].round = ds[i]->round;
+    a[i].rht = ds[i]->rht;
+    a[i].tiled = ds[i]->scale_layout == FP4_SCALES_TILED ? 1 : 0;
+  }
+  return device_status(fp4lib::launch_quant_dual(a[0], a[1], s), "fp4_quantize_dual launch");
+}
+
 FP4_EXPORT fp4_status fp4_dequantize(fp4_format format, fp4_block block,
                                      fp4_scale_layout scale_layout, const uint8_t* codes,
                                      const uint8_t* scales, const float* s_dec, int64_t rows,

@@ -43,6 +43,9 @@ hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld
 hipError_t launch_quant_row(const QuantArgs& a, hipStream_t s);
 hipError_t launch_quant_col(const QuantArgs& a, hipStream_t s);
 hipError_t launch_quant_2d(const QuantArgs& a, hipStream_t s);
+// Rowwise (`row`) and colwise (`col`) 1D quantization of the same input in
+// one kernel: same format and rounding mode; RHT only on the colwise side.
+hipError_t launch_quant_dual(const QuantArgs& row, const QuantArgs& col, hipStream_t s);
 hipError_t launch_dequant(int format, int block2d, int tiled, const uint8_t* codes,
                           const uint8_t* scales, const float* s_dec, int64_t rows, int64_t cols,
                           void* out, int out_fp32, hipStream_t s);

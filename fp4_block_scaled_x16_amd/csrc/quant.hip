@@ -1,7 +1,8 @@
 // gfx950 kernels for the quantization side of FP4 block scaling:
 //   tensor amax (plain and in the RHT-rotated space), rowwise 1D quantizer,
 //   colwise (transposing) 1D quantizer with optional fused 16-point RHT,
-//   16x16 2D quantizer emitting W and W^T codes, dequantizer, standalone RHT.
+//   the two together from one read of X (dual), 16x16 2D quantizer emitting
+//   W and W^T codes, dequantizer, standalone RHT.
 //
 // All of these are HBM-bound streams: every kernel reads its bf16 input
 // once with 16-byte vector loads, keeps the block in registers (and LDS
@@ -378,6 +379,165 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
   if constexpr (CNT) flush_counters<kThreads>(cnt, counters);
 }
 
+// ------------------------------------------------ dual: rowwise + colwise --
+// One read of X for both code matrices a linear layer takes from it: the
+// rowwise codes (blocks along cols: the Fprop / Dgrad operand) and the codes
+// of X^T (blocks along rows, optionally RHT-rotated: the Wgrad operand,
+// NVFP4 paper §4.1 and §4.2).  A workgroup walks (8 BS) x 64 tiles of X as
+// k_quant_col does.  Each thread loads two whole rowwise blocks of the tile
+// (BS consecutive elements of a row each), encodes them from registers as
+// k_quant_row does, and stores them into the LDS tile; the colwise half
+// then runs from LDS exactly as k_quant_col.  The next tile's loads are
+// issued before the current tile is encoded.  Both halves use the same
+// rounding mode, each with its own tensor scale, Philox key and counter
+// offset, and output layout.
+template <int FMT, int RND, bool RHT, bool CNT>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(FMT == kMX ? 1 : 3))) void k_quant_dual(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, uint8_t* __restrict__ codes_t,
+    uint8_t* __restrict__ scales_t, const float* __restrict__ amax,
+    const float* __restrict__ amax_t, float target, float target_t,
+    float* __restrict__ s_dec_out, float* __restrict__ s_dec_t_out, uint64_t seed,
+    uint64_t offset, uint64_t seed_t, uint64_t offset_t, uint32_t signs,
+    fp4_counters* __restrict__ counters, int tiled, int tiled_t) {
+  constexpr int BS = FMT == kMX ? 32 : 16;
+  constexpr int TR = 8 * BS;        // tile rows (8 groups)
+  constexpr int TC = 64;            // tile columns
+  constexpr int LDW = TC / 2 + 1;   // LDS row pitch in 32-bit words (odd: spreads banks)
+  constexpr int BPR = TC / BS;      // rowwise blocks per tile row
+  constexpr int NB = TR * BPR / kThreads;   // rowwise blocks per thread and tile (2)
+  static_assert(NB * kThreads == TR * BPR, "tile must split evenly into blocks");
+  __shared__ uint32_t tile[TR * LDW];
+
+  float s_enc_g = 1.0f, s_dec_g = 1.0f, s_enc_gt = 1.0f, s_dec_gt = 1.0f;
+  if constexpr (FMT != kMX) {
+    global_scales(*amax, target, s_enc_g, s_dec_g);
+    global_scales(*amax_t, target_t, s_enc_gt, s_dec_gt);
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    if (s_dec_out) *s_dec_out = s_dec_g;
+    if (s_dec_t_out) *s_dec_t_out = s_dec_gt;
+  }
+
+  const int64_t tiles_c = (cols + TC - 1) / TC;
+  const int64_t tiles_r = (rows + TR - 1) / TR;
+  const int64_t ntiles = tiles_c * tiles_r;
+  const uint64_t bpr = static_cast<uint64_t>(cols) / BS;   // rowwise blocks per row of X
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int grp = lane & 7;                  // row group handled in the colwise phase
+  const int pair = wave * 8 + (lane >> 3);   // column pair (0..31)
+  uint32_t cnt[5] = {0, 0, 0, 0, 0};
+
+  // rowwise block b = t + k * kThreads of a tile: tile row b / BPR, columns
+  // (b % BPR) * BS ..; blocks outside X load zeros and write nothing
+  auto load = [&](int64_t tile_id, uint4 (&q)[NB][BS / 8]) {
+    const int64_t tr = tile_id / tiles_c, tc = tile_id - tr * tiles_c;
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int b = t + k * kThreads;
+      const int64_t r = tr * TR + b / BPR, c = tc * TC + (b % BPR) * BS;
+      const bool in = tile_id < ntiles && r < rows && c < cols;
+#pragma unroll
+      for (int e = 0; e < BS / 8; ++e)
+        q[k][e] = in ? *reinterpret_cast<const uint4*>(x + r * ld + c + 8 * e)
+                     : make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  uint4 q[NB][BS / 8];
+  load(blockIdx.x, q);
+  for (int64_t tile_id = blockIdx.x; tile_id < ntiles; tile_id += gridDim.x) {
+    const int64_t tr = tile_id / tiles_c, tc = tile_id - tr * tiles_c;
+    const int64_t r0 = tr * TR, c0 = tc * TC;
+    uint4 nq[NB][BS / 8];
+    load(tile_id + gridDim.x, nq);
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      const int b = t + k * kThreads;
+      const int lr = b / BPR, lc = (b % BPR) * BS;
+      const int64_t r = r0 + lr, c = c0 + lc;
+      uint32_t* d = tile + lr * LDW + (lc >> 1);
+#pragma unroll
+      for (int e = 0; e < BS / 8; ++e) {
+        d[4 * e] = q[k][e].x;
+        d[4 * e + 1] = q[k][e].y;
+        d[4 * e + 2] = q[k][e].z;
+        d[4 * e + 3] = q[k][e].w;
+      }
+      float v[BS];
+#pragma unroll
+      for (int e = 0; e < BS / 8; ++e) unpack8(q[k][e], v + 8 * e);
+      float amax_b = 0.0f;
+#pragma unroll
+      for (int e = 0; e < BS; ++e) amax_b = fmaxf(amax_b, fabsf(v[e]));
+      float s_enc_l;
+      const bool in = r < rows && c < cols;
+      uint32_t sc_cnt[5] = {0, 0, 0, 0, 0};
+      const uint32_t sc = scale_for_block<FMT>(amax_b, s_enc_g, s_dec_g, s_enc_l, sc_cnt);
+      if (in) {
+        cnt[0] += sc_cnt[0];
+        cnt[1] += sc_cnt[1];
+        cnt[2] += sc_cnt[2];
+      }
+      uint32_t words[BS / 8];
+      encode_block<BS, RND, CNT>(v, s_enc_l, static_cast<uint64_t>(r) * cols + c, seed, offset,
+                                 words, cnt);
+      if (in) {
+        uint8_t* dst = codes + r * (cols >> 1) + (c >> 1);
+        if constexpr (BS == 16) {
+          *reinterpret_cast<uint2*>(dst) = make_uint2(words[0], words[1]);
+        } else {
+          *reinterpret_cast<uint4*>(dst) = make_uint4(words[0], words[1], words[2], words[3]);
+        }
+        const uint64_t j = static_cast<uint64_t>(c) / BS;
+        scales[tiled ? tiled_scale_offset(r, j, (bpr + 7) >> 3) : r * bpr + j] =
+            static_cast<uint8_t>(sc);
+      }
+    }
+    __syncthreads();
+    const int64_t col = c0 + 2 * pair;
+    const int64_t row = r0 + grp * BS;
+    if (col < cols && row < rows) {
+#pragma unroll 1
+      for (int h = 0; h < 2; ++h) {
+        float v[BS];
+#pragma unroll
+        for (int k = 0; k < BS; ++k) {
+          const uint32_t w = tile[(grp * BS + k) * LDW + pair];
+          v[k] = bf16_to_f32(h ? (w >> 16) : (w & 0xFFFFu));
+        }
+        if constexpr (RHT) rht16(*reinterpret_cast<float(*)[16]>(v), signs);
+        const int64_t c = col + h;
+        float amax_b = 0.0f;
+#pragma unroll
+        for (int k = 0; k < BS; ++k) amax_b = fmaxf(amax_b, fabsf(v[k]));
+        float s_enc_l;
+        const uint32_t sc = scale_for_block<FMT>(amax_b, s_enc_gt, s_dec_gt, s_enc_l, cnt);
+        uint32_t words[BS / 8];
+        encode_block<BS, RND, CNT>(v, s_enc_l, static_cast<uint64_t>(c) * rows + row, seed_t,
+                                   offset_t, words, cnt);
+        uint8_t* dst = codes_t + c * (rows >> 1) + (row >> 1);
+        if constexpr (BS == 16) {
+          *reinterpret_cast<uint2*>(dst) = make_uint2(words[0], words[1]);
+        } else {
+          *reinterpret_cast<uint4*>(dst) = make_uint4(words[0], words[1], words[2], words[3]);
+        }
+        const uint64_t kb = static_cast<uint64_t>(rows / BS);
+        scales_t[tiled_t ? tiled_scale_offset(c, row / BS, (kb + 7) >> 3) : c * kb + row / BS] =
+            static_cast<uint8_t>(sc);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NB; ++k)
+#pragma unroll
+      for (int e = 0; e < BS / 8; ++e) q[k][e] = nq[k][e];
+  }
+  if constexpr (CNT) flush_counters<kThreads>(cnt, counters);
+}
+
 // ------------------------------------------------------------ 2D 16x16 --
 // A workgroup covers a 64 x 64 region (4 x 4 tiles).  Thread t owns the
 // 16 elements of row t/4 in tile column t%4; the 16 threads of a tile are
@@ -671,6 +831,48 @@ hipError_t launch_quant_col(const QuantArgs& a, hipStream_t s) {
   if (a.format == FP4_NVFP4) col_dispatch_rnd<kNV>(a, s);
   else if (a.format == FP4_UE5M3) col_dispatch_rnd<kUE>(a, s);
   else col_dispatch_rnd<kMX>(a, s);
+  return hipGetLastError();
+}
+
+template <int FMT, int RND, bool RHT, bool CNT>
+static void dual_launch(const QuantArgs& a, const QuantArgs& b, hipStream_t s) {
+  constexpr int BS = FMT == kMX ? 32 : 16;
+  const int64_t tiles = ((a.rows + 8 * BS - 1) / (8 * BS)) * ((a.cols + 63) / 64);
+  const int64_t cap = static_cast<int64_t>(device_cu_count()) *
+                      (RND == FP4_SR ? kColWgPerCuSR : kTileWgPerCu);
+  const int grid = static_cast<int>(tiles < cap ? (tiles > 0 ? tiles : 1) : cap);
+  hipLaunchKernelGGL((k_quant_dual<FMT, RND, RHT, CNT>), dim3(grid), dim3(kThreads), 0, s, a.x,
+                     a.rows, a.cols, a.ld, a.codes, a.scales, b.codes, b.scales, a.amax, b.amax,
+                     a.target, b.target, a.s_dec, b.s_dec, a.seed, a.offset, b.seed, b.offset,
+                     b.rht_signs, a.counters, a.tiled, b.tiled);
+}
+
+template <int FMT, int RND, bool RHT>
+static void dual_dispatch_cnt(const QuantArgs& a, const QuantArgs& b, hipStream_t s) {
+  if (a.counters) dual_launch<FMT, RND, RHT, true>(a, b, s);
+  else dual_launch<FMT, RND, RHT, false>(a, b, s);
+}
+
+template <int FMT, int RND>
+static void dual_dispatch_rht(const QuantArgs& a, const QuantArgs& b, hipStream_t s) {
+  if constexpr (FMT == kMX) {
+    dual_dispatch_cnt<FMT, RND, false>(a, b, s);   // RHT with MXFP4 is rejected by validation
+  } else {
+    if (b.rht) dual_dispatch_cnt<FMT, RND, true>(a, b, s);
+    else dual_dispatch_cnt<FMT, RND, false>(a, b, s);
+  }
+}
+
+template <int FMT>
+static void dual_dispatch_rnd(const QuantArgs& a, const QuantArgs& b, hipStream_t s) {
+  if (a.round == FP4_SR) dual_dispatch_rht<FMT, FP4_SR>(a, b, s);
+  else dual_dispatch_rht<FMT, FP4_RNE>(a, b, s);
+}
+
+hipError_t launch_quant_dual(const QuantArgs& row, const QuantArgs& col, hipStream_t s) {
+  if (row.format == FP4_NVFP4) dual_dispatch_rnd<kNV>(row, col, s);
+  else if (row.format == FP4_UE5M3) dual_dispatch_rnd<kUE>(row, col, s);
+  else dual_dispatch_rnd<kMX>(row, col, s);
   return hipGetLastError();
 }
 

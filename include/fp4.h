@@ -161,6 +161,36 @@ fp4_status fp4_quantize(const fp4_quant_desc* desc /* host */,
                         void* stream);
 
 /*
+ * fp4_quantize_dual -- both 1D quantizations of one bf16 matrix from a
+ * single read of it: the ROWWISE code matrix [rows, cols] and the COLWISE
+ * code matrix of X^T [cols, rows].  A linear layer needs both of X (Fprop
+ * uses the rows, Wgrad the columns) and both of dY (Dgrad, Wgrad)
+ * (NVFP4 paper §4.1, Fig. 5); the colwise side may carry the RHT of the
+ * Wgrad inputs (§4.2, App. C).  Each output is bit-identical to what
+ * fp4_quantize writes with the same descriptor.
+ *
+ *   row_desc  ROWWISE, 1D, no RHT.      col_desc  COLWISE, 1D.
+ *   Both: the same format and the same rounding mode (seed, offset, target,
+ *   amax_given and scale_layout are per side).
+ *   x [rows, cols] bf16 (ld), device; rows and cols multiples of BS.
+ *   codes, scales     rowwise outputs, as fp4_quantize with row_desc.
+ *   codes_t, scales_t colwise outputs, as fp4_quantize with col_desc.
+ *   amax, amax_t      device floats, NVFP4/UE5M3 (MXFP4: unused, may be
+ *           NULL): each written (amax_given = 0; amax_t in the rotated space
+ *           when col_desc->rht) or read (amax_given = 1).  They may be the
+ *           same buffer only when col_desc has no RHT and both sides have
+ *           the same amax_given (the amax is then computed once).
+ *   s_dec, s_dec_t    device floats or NULL: the two global decode scales.
+ *   counters  device fp4_counters or NULL: events of both sides, summed.
+ */
+fp4_status fp4_quantize_dual(const fp4_quant_desc* row_desc /* host */,
+                             const fp4_quant_desc* col_desc /* host */,
+                             const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
+                             uint8_t* codes, uint8_t* scales, uint8_t* codes_t, uint8_t* scales_t,
+                             float* amax, float* amax_t, float* s_dec, float* s_dec_t,
+                             fp4_counters* counters, void* stream);
+
+/*
  * fp4_dequantize -- decode codes and scales: v = fp32(fp32(e2m1 * scale) *
  * s_dec_G) (NVFP4 paper App. B.2-B.3: the decode scales undo the encode
  * scales).  The codes/scales layouts are those fp4_quantize writes for a

@@ -32,8 +32,8 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert {"fp4_amax", "fp4_quantize", "fp4_dequantize", "fp4_rht16", "fp4_gemm",
-            "fp4_status_string", "fp4_last_error"} <= declared()
+    assert {"fp4_amax", "fp4_quantize", "fp4_quantize_dual", "fp4_dequantize", "fp4_rht16",
+            "fp4_gemm", "fp4_status_string", "fp4_last_error"} <= declared()
 
 
 def test_exports_every_declared_symbol(lib):
@@ -104,6 +104,50 @@ def test_quantize_rejects_pointers(lib):
     assert lib.fp4_quantize(None, FAKE, 32, 64, 64, FAKE, FAKE, None, FAKE, None, None, None) == 1
     # TILED scales must be 16-byte aligned (row-major ones need not be)
     assert quant(lib, desc(scale_layout=1), scales=ctypes.c_void_p(0x10004)) == 1
+
+
+def dual(lib, rd, cd, rows=32, cols=64, x=FAKE, codes=FAKE, scales=FAKE, codes_t=FAKE,
+         scales_t=FAKE, amax=FAKE, amax_t=ctypes.c_void_p(0x10010)):
+    return lib.fp4_quantize_dual(ctypes.byref(rd), ctypes.byref(cd), x, rows, cols, cols, codes,
+                                 scales, codes_t, scales_t, amax, amax_t, None, None, None, None)
+
+
+@pytest.mark.parametrize("rkw,ckw,rows,cols,status", [
+    (dict(format=7), dict(orient=1), 32, 64, 1),
+    (dict(), dict(orient=1, round=2), 32, 64, 1),
+    (dict(orient=1), dict(orient=1), 32, 64, 3),              # first desc must be ROWWISE
+    (dict(), dict(), 32, 64, 3),                              # second desc must be COLWISE
+    (dict(), dict(orient=1, format=1), 32, 64, 3),            # formats differ
+    (dict(), dict(orient=1, round=1), 32, 64, 3),             # rounding modes differ
+    (dict(rht=1), dict(orient=1), 32, 64, 3),                 # RHT on the rowwise side
+    (dict(format=2), dict(orient=1, format=2, rht=1), 64, 64, 3),   # RHT with MXFP4
+    (dict(block=1), dict(orient=1), 32, 64, 3),               # 2D
+    (dict(), dict(orient=1, emit_transpose=1), 32, 64, 3),
+    (dict(format=2, amax_given=1), dict(orient=1, format=2), 64, 64, 3),
+    (dict(target=-1.0), dict(orient=1), 32, 64, 1),
+    (dict(), dict(orient=1, scale_layout=4), 32, 64, 1),
+    (dict(), dict(orient=1), 24, 64, 2),                      # rows % 16
+    (dict(), dict(orient=1), 32, 40, 2),                      # cols % 16
+    (dict(format=2), dict(orient=1, format=2), 48, 64, 2),    # rows % 32
+])
+def test_quantize_dual_rejects(lib, rkw, ckw, rows, cols, status):
+    assert dual(lib, desc(**rkw), desc(**ckw), rows, cols) == status
+    assert _err(lib)
+
+
+def test_quantize_dual_rejects_pointers(lib):
+    r, c = desc(), desc(orient=1)
+    assert dual(lib, r, c, x=None) == 1
+    assert dual(lib, r, c, codes_t=None) == 1
+    assert dual(lib, r, c, scales_t=None) == 1
+    assert dual(lib, r, c, codes_t=ctypes.c_void_p(0x10008)) == 1       # misaligned
+    assert dual(lib, r, c, amax_t=None) == 1
+    # a shared amax buffer is only allowed without RHT and with equal amax_given
+    assert dual(lib, r, desc(orient=1, rht=1), amax_t=FAKE) == 1
+    assert dual(lib, r, desc(orient=1, amax_given=1), amax_t=FAKE) == 1
+    assert dual(lib, r, desc(orient=1, scale_layout=1), scales_t=ctypes.c_void_p(0x10004)) == 1
+    assert lib.fp4_quantize_dual(None, ctypes.byref(c), FAKE, 32, 64, 64, FAKE, FAKE, FAKE, FAKE,
+                                 FAKE, FAKE, None, None, None, None) == 1
 
 
 def test_other_entry_points_reject(lib):
