@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--config", type=int, default=2, choices=(2, 3, 4, 5))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=8192)
+    ap.add_argument("--serial", action="store_true",
+                    help="run the step's kernels one after another on one stream")
     ap.add_argument("--separate-quant", action="store_true",
                     help="quantize X and dY rowwise and colwise in separate kernels (two reads "
                          "each) instead of one dual kernel per tensor")
@@ -355,6 +357,42 @@ def main():
         for (_, _, _, f) in ops:
             f()
 
+    # The amax + quantize work of X, W and dY is independent: each tensor's
+    # runs on its own stream (default priority), Fprop starts as soon as X
+    # and W are quantized (beside dY's VALU-bound stochastic rounding), and
+    # Dgrad / Wgrad follow on the main stream once everything has joined.
+    # Every side stream first waits for the main stream, so memory the
+    # previous step's GEMMs read is not reused before they finish.
+    side = [torch.cuda.Stream(dev) for _ in range(3)]
+
+    def tensor_of(name):
+        if name.startswith("gemm"):
+            return name
+        return next(t for t in ("dY", "X", "W") if (" " + t + " ") in (name + " "))
+
+    def run_step_concurrent():
+        main = torch.cuda.current_stream(dev)
+        ev = {}
+        for i, t in enumerate(("X", "W", "dY")):
+            side[i].wait_stream(main)
+            with torch.cuda.stream(side[i]):
+                for (n, _, _, f) in ops:
+                    if tensor_of(n) == t:
+                        f()
+                ev[t] = torch.cuda.Event()
+                ev[t].record(side[i])
+        with torch.cuda.stream(side[0]):
+            side[0].wait_event(ev["W"])
+            next(f for (n, _, _, f) in ops if n == "gemm fprop")()
+        for s_ in side:
+            main.wait_stream(s_)
+        for (n, _, _, f) in ops:
+            if n in ("gemm dgrad", "gemm wgrad"):
+                f()
+
+    if not args.serial:
+        run_step = run_step_concurrent  # noqa: F811
+
     # eager warmup (also performs the library's one-time kernel attribute setup)
     for _ in range(max(1, args.warmup)):
         run_step()
@@ -453,6 +491,7 @@ def main():
         "config": {"workload": c["name"], "format": fmt, "tokens": c["tokens"], "d_in": c["d_in"],
                    "d_out": c["d_out"], "gemms": "fprop, dgrad, wgrad", "scales_1d": "tiled",
                    "quantize_kernels": len([1 for (n, k, u, _) in ops if n.startswith("quant")]),
+                   "streams": 1 if args.serial else 4,
                    "dual_quantize": not args.separate_quant},
         "quantize": {"GBps": round(q_bytes / (q_ms * 1e-3) / 1e9, 1),
                      "frac_hbm": round(q_bytes / (q_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
