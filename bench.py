@@ -56,6 +56,11 @@ def parse():
     ap.add_argument("--config", type=int, default=2, choices=(2, 3, 4, 5))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-tokens", type=int, default=8192)
+    ap.add_argument("--layer", action="store_true",
+                    help="time QuantizedLinear.forward + backward (the layer a user calls) "
+                         "instead of the step's kernel list")
+    ap.add_argument("--no-rht", action="store_true",
+                    help="--layer on the 12B workload: leave out the RHT of the Wgrad operands")
     ap.add_argument("--serial", action="store_true",
                     help="run the step's kernels one after another on one stream")
     ap.add_argument("--separate-quant", action="store_true",
@@ -329,6 +334,61 @@ def cpu_baseline(cfg, host, fmt, tokens):
             "seconds": round(dt, 3)}
 
 
+def layer_main(args, dev):
+    """Forward + backward of QuantizedLinear on a workload's tensors, captured
+    as one graph: the end-to-end time of the FP4 layer (amax, quantization,
+    three GEMMs, fp32 Wgrad accumulation)."""
+    import torch
+    from fp4_block_scaled_x16_amd import inputs
+    from fp4_block_scaled_x16_amd.linear import QuantizedLinear, Recipe
+
+    cfg = args.config
+    c = inputs.CONFIGS[cfg]
+    fmt = c["fmt"]
+    t = inputs.linear_tensors(cfg)
+    X, W, dY = (torch.from_numpy(t[n].view(np.int16)).to(dev) for n in ("X", "W", "dY"))
+    rht = cfg == 3 and not args.no_rht
+    r = Recipe(fmt, target_dy=2048.0 if fmt == "ue5m3" else 448.0, rht=rht,
+               rht_signs=inputs.rht_sign_mask() if rht else 0)
+    layer = QuantizedLinear(W, r)
+
+    def step():
+        layer.forward(X)
+        layer.backward(dY)
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    flops = 3 * 2.0 * c["tokens"] * c["d_in"] * c["d_out"]
+    print(json.dumps({
+        "metric": METRIC, "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "data": "synthetic (seeded PCG64, bf16 inputs resident in HBM)",
+        "config": {"workload": c["name"].replace("-rht", "") + ("-rht" if rht else "") + "-layer",
+                   "format": fmt, "rht": rht,
+                   "tokens": c["tokens"], "d_in": c["d_in"], "d_out": c["d_out"],
+                   "amax": "current (recomputed every step)", "wgrad": "fp32 accumulate"},
+        "counters_all_runs": {k: int(v) for k, v in zip(("scale_saturated", "scale_underflow",
+                                                 "scale_subnormal", "elem_saturated",
+                                                 "elem_underflow"),
+                                                layer.counters.cpu().tolist())},
+    }))
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
@@ -347,6 +407,9 @@ def main():
     api.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.layer:
+        layer_main(args, dev)
+        return
     cfg = args.config
     ops, cnt, host, fmt = build_step(cfg, dev, dual=not args.separate_quant)
     if args.counters_run:

@@ -1,0 +1,136 @@
+"""A linear layer whose three GEMMs run on FP4 operands.
+
+NVFP4 paper §4.1 and Fig. 5: in a linear layer Y = X W^T, the forward
+product (Fprop) and both backward products -- Dgrad (dX = dY W) and Wgrad
+(dW = dY^T X) -- consume FP4-quantized operands and accumulate in fp32.
+This class composes the library's entry points into that layer:
+
+  forward(X)    X  -> rowwise codes (Fprop A) and colwise codes of X^T
+                      (Wgrad B) from one read; RHT on the colwise side when
+                      the recipe asks for it (§4.2, App. C)
+                W  -> 16x16 2D codes of W and W^T with one scale per tile
+                      (§4.3; MXFP4: 1D rowwise and colwise codes)
+                Y  = Fprop(X, W)                          fp32 [tokens, out]
+  backward(dY)  dY -> rowwise codes (Dgrad A) and colwise codes of dY^T
+                      (Wgrad A) with stochastic rounding (§4.4)
+                dX = Dgrad(dY, W^T)                       fp32 [tokens, in]
+                main_grad += Wgrad(dY^T, X^T)             fp32 [out, in]
+
+Tensor amax: current scaling (recomputed every step, the NVFP4 recipe) or,
+with amax_interval = N > 1, recomputed every N-th step and reused in
+between (the periodic tensor scaling of the UE5M3 recipe).  The SR random
+stream of step s uses Philox counter offsets 2s (rowwise dY) and 2s + 1
+(colwise dY), so no two steps or orientations share random bits.
+
+Every computation runs in the library's kernels; this module only
+allocates outputs and passes pointers (through `api`).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import api
+
+
+@dataclass
+class Recipe:
+    fmt: str = "nvfp4"            # "nvfp4", "ue5m3" or "mxfp4"
+    target_x: float = 448.0       # T of s_enc = 6 T / amax, per tensor
+    target_w: float = 448.0
+    target_dy: float = 448.0
+    rht: bool = False             # RHT on the Wgrad operands (colwise X and dY)
+    rht_signs: int = 0            # 16-bit sign mask D_r
+    sr_seed: int = 1              # Philox key of the stochastic rounding of dY
+    amax_interval: int = 1        # recompute each tensor amax every this many steps
+    scale_layout: str = "tiled"   # storage of the 1D block scales
+
+    @property
+    def two_level(self):
+        return self.fmt != "mxfp4"
+
+
+class QuantizedLinear:
+    """Y = X W^T with FP4 Fprop / Dgrad / Wgrad (see the module docstring).
+
+    weight: bf16 [out, in] device tensor (the master copy stays in bf16);
+    main_grad: fp32 [out, in], accumulated by every backward (zero it
+    between optimizer steps).
+    """
+
+    def __init__(self, weight: torch.Tensor, recipe: Recipe = Recipe()):
+        if weight.dim() != 2:
+            raise ValueError("weight must be [out, in]")
+        self.weight = weight
+        self.recipe = recipe
+        self.out_features, self.in_features = weight.shape
+        dev = weight.device
+        self.main_grad = torch.zeros((self.out_features, self.in_features), dtype=torch.float32,
+                                     device=dev)
+        names = ("x", "x_t", "w", "dy", "dy_t")
+        self.amax = {n: torch.zeros(1, dtype=torch.float32, device=dev) for n in names}
+        self.step = 0
+        self.counters = api.new_counters(dev)
+        self._saved = None
+
+    def _refresh(self):
+        r = self.recipe
+        return r.two_level and (r.amax_interval <= 1 or self.step % r.amax_interval == 0)
+
+    def _amax_args(self, x, name, rht):
+        """amax buffers (rowwise, colwise) for a dual quantization of x,
+        refreshed on this step if due; without RHT both sides share one
+        buffer.  MXFP4 has none."""
+        r = self.recipe
+        if not r.two_level:
+            return None, None
+        if self._refresh():
+            api.amax(x, out=self.amax[name])
+            if rht:
+                api.amax(x, rht=True, signs=r.rht_signs, out=self.amax[name + "_t"])
+        return self.amax[name], self.amax[name + "_t" if rht else name]
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        r = self.recipe
+        if x.dim() != 2 or x.shape[1] != self.in_features:
+            raise ValueError("x must be [tokens, in_features]")
+        am, am_t = self._amax_args(x, "x", r.rht)
+        qx, qx_t = api.quantize_dual(x, r.fmt, rht=r.rht, signs=r.rht_signs, target=r.target_x,
+                                     amax_in=am, amax_t_in=am_t, counters=self.counters,
+                                     scale_layout=r.scale_layout)
+        if r.two_level:
+            if self._refresh():
+                api.amax(self.weight, out=self.amax["w"])
+            qw = api.quantize(self.weight, r.fmt, block="2d", emit_transpose=True,
+                              target=r.target_w, amax_in=self.amax["w"], counters=self.counters)
+            w_op, wt_op = qw.operand(), qw.operand(transposed=True)
+        else:
+            qw, qw_t = api.quantize_dual(self.weight, r.fmt, counters=self.counters,
+                                         scale_layout=r.scale_layout)
+            w_op, wt_op = qw.operand(), qw_t.operand()
+        tokens = x.shape[0]
+        y = api.gemm(qx.operand(), w_op, tokens, self.out_features, self.in_features,
+                     device=x.device)
+        self._saved = (qx_t, wt_op, tokens)
+        return y
+
+    def backward(self, dy: torch.Tensor) -> torch.Tensor:
+        r = self.recipe
+        if self._saved is None:
+            raise RuntimeError("backward() needs a preceding forward()")
+        qx_t, wt_op, tokens = self._saved
+        if dy.dim() != 2 or tuple(dy.shape) != (tokens, self.out_features):
+            raise ValueError("dy must be [tokens, out_features]")
+        am, am_t = self._amax_args(dy, "dy", r.rht)
+        qdy, qdy_t = api.quantize_dual(dy, r.fmt, rnd="sr", seed=r.sr_seed, offset=2 * self.step,
+                                       offset_t=2 * self.step + 1, rht=r.rht, signs=r.rht_signs,
+                                       target=r.target_dy, amax_in=am, amax_t_in=am_t,
+                                       counters=self.counters, scale_layout=r.scale_layout)
+        dx = api.gemm(qdy.operand(), wt_op, tokens, self.in_features, self.out_features,
+                      device=dy.device)
+        api.gemm(qdy_t.operand(), qx_t.operand(), self.out_features, self.in_features, tokens,
+                 out=self.main_grad, accumulate=True)
+        self._saved = None
+        self.step += 1
+        return dx
