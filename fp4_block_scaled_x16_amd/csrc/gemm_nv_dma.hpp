@@ -45,6 +45,25 @@ __device__ __forceinline__ void dma_codes_nv(uint4 (&dst)[2][1024], const DmaSrc
   }
 }
 
+// Scheduling hint for the last slice of a step: the stage's LDS reads go
+// first, then a quarter of the slice's MFMAs alone (the reads land
+// meanwhile), then the rest each followed by its share of the next step's
+// slice-0 dequantization.
+template <int MI>
+__device__ __forceinline__ void interleave_tail() {
+  constexpr int kReads = 2 * (MI + 4) + (MI + 4);   // 16-byte code reads + scale reads
+  constexpr int kFirst = MI;
+  constexpr int kRest = 4 * MI - kFirst;
+  constexpr int kValu = (8 * (MI + 4) + kRest - 1) / kRest;
+  __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);   // DS read
+  __builtin_amdgcn_sched_group_barrier(0x008, kFirst, 0);   // MFMA
+#pragma unroll
+  for (int i = 0; i < kRest; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);  // VALU
+  }
+}
+
 template <int FMT, int SCV, int MI>
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level_dma(Params p) {
   constexpr int BM = 64 * MI;
@@ -124,27 +143,32 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level_dma(Params p) {
   const int i = lane & 31, h = lane >> 5;
   uint32_t a_raw[MI][8], b_raw[4][8];
   uint2 a_sc[MI], b_sc[4];
+  // LDS reads of a stage into the raw-code and scale registers, in the
+  // order the slices need them: the first 16 bytes of every row (slices
+  // 0-3) and the scales first, the second 16 bytes (slices 4-7) last.
   auto read_stage = [&](const uint4 (&C)[2][1024], const uint2 (&S)[2][2][256]) {
+    auto read_half = [&](int q) {
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      const int row = wm * (MI * 32) + mi * 32 + i;
-      const int sw = dma_swizzle(row);
-      const uint4 c0 = C[0][row * 4 + ((2 * h) ^ sw)];
-      const uint4 c1 = C[0][row * 4 + ((2 * h + 1) ^ sw)];
-      a_raw[mi][0] = c0.x; a_raw[mi][1] = c0.y; a_raw[mi][2] = c0.z; a_raw[mi][3] = c0.w;
-      a_raw[mi][4] = c1.x; a_raw[mi][5] = c1.y; a_raw[mi][6] = c1.z; a_raw[mi][7] = c1.w;
-      a_sc[mi] = S[0][h][row];
-    }
+      for (int mi = 0; mi < MI; ++mi) {
+        const int row = wm * (MI * 32) + mi * 32 + i;
+        const uint4 c = C[0][row * 4 + ((2 * h + q) ^ dma_swizzle(row))];
+        a_raw[mi][4 * q] = c.x; a_raw[mi][4 * q + 1] = c.y;
+        a_raw[mi][4 * q + 2] = c.z; a_raw[mi][4 * q + 3] = c.w;
+      }
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-      const int row = wn * 128 + ni * 32 + i;
-      const int sw = dma_swizzle(row);
-      const uint4 c0 = C[1][row * 4 + ((2 * h) ^ sw)];
-      const uint4 c1 = C[1][row * 4 + ((2 * h + 1) ^ sw)];
-      b_raw[ni][0] = c0.x; b_raw[ni][1] = c0.y; b_raw[ni][2] = c0.z; b_raw[ni][3] = c0.w;
-      b_raw[ni][4] = c1.x; b_raw[ni][5] = c1.y; b_raw[ni][6] = c1.z; b_raw[ni][7] = c1.w;
-      b_sc[ni] = S[1][h][row];
-    }
+      for (int ni = 0; ni < 4; ++ni) {
+        const int row = wn * 128 + ni * 32 + i;
+        const uint4 c = C[1][row * 4 + ((2 * h + q) ^ dma_swizzle(row))];
+        b_raw[ni][4 * q] = c.x; b_raw[ni][4 * q + 1] = c.y;
+        b_raw[ni][4 * q + 2] = c.z; b_raw[ni][4 * q + 3] = c.w;
+      }
+    };
+    read_half(0);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) a_sc[mi] = S[0][h][wm * (MI * 32) + mi * 32 + i];
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) b_sc[ni] = S[1][h][wn * 128 + ni * 32 + i];
+    read_half(1);
   };
 
   // Step s on stage C (raw codes and scales already in registers) while the
@@ -153,13 +177,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level_dma(Params p) {
   // at the top; after slice 6 the DMA has landed and the decoded scales are
   // stored (one wait for both), then the barrier, and the next stage's LDS
   // reads overlap slice 7.  N was last read before the previous barrier.
+  // Slice 0 of a step is dequantized either at the top of the step (256-row
+  // tiles) or, for 192-row tiles, under the second part of the previous
+  // step's slice 7 (kTail; measured faster there, slower with 256 rows,
+  // whose slice-7 MFMAs cannot hide the 8 extra VALU ops per MFMA).
+  constexpr bool kTail = MI != 4;
+  FragT<MI> f0, f1;
   auto step = [&](uint4 (&Nc)[2][1024], uint2 (&Ns)[2][2][256], int s) {
     const int nxt = s + 1 < nsteps ? s + 1 : s;
     load_scales(nxt);
     dma_codes_nv<MI>(Nc, src, nxt, wave);
     __builtin_amdgcn_sched_barrier(0);     // keep the loads at the top of the step
-    FragT<MI> f0, f1;
-    dequant_slice<0>(f0, a_raw, b_raw, a_sc, b_sc);
+    if constexpr (!kTail) dequant_slice<0>(f0, a_raw, b_raw, a_sc, b_sc);
     pipelined_slice<0>(acc, f0, f1, a_raw, b_raw, a_sc, b_sc);
     pipelined_slice<1>(acc, f1, f0, a_raw, b_raw, a_sc, b_sc);
     pipelined_slice<2>(acc, f0, f1, a_raw, b_raw, a_sc, b_sc);
@@ -174,7 +203,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level_dma(Params p) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     read_stage(Nc, Ns);
-    pipelined_slice<7>(acc, f1, f0, a_raw, b_raw, a_sc, b_sc);
+    if constexpr (kTail) {
+      dequant_slice<0>(f0, a_raw, b_raw, a_sc, b_sc);
+      mfma_slice(acc, f1);
+      interleave_tail<MI>();
+    } else {
+      pipelined_slice<7>(acc, f1, f0, a_raw, b_raw, a_sc, b_sc);
+    }
   };
 
   load_scales(0);
@@ -183,6 +218,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level_dma(Params p) {
   wait_vmcnt<0>();
   ring_barrier();
   read_stage(cst0, sst0);
+  if constexpr (kTail) dequant_slice<0>(f0, a_raw, b_raw, a_sc, b_sc);
   for (int s = 0; s < nsteps; s += 2) {
     step(cst1, sst1, s);
     step(cst0, sst0, s + 1);
