@@ -69,6 +69,9 @@ def parse():
     ap.add_argument("--counters-run", action="store_true",
                     help="run each op of the step once, eagerly, then a 512 MiB calibration "
                          "kernel, for rocprofv3 --pmc; prints nothing else")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
+                    help="per-kernel durations from a rocprofv3 kernel trace of a default run: "
+                         "all launches, and the isolated launches of the per-op timing graphs")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn the counter CSVs of two --counters-run passes (FETCH_SIZE, "
                          "WRITE_SIZE) into the GEMM traffic summary")
@@ -389,8 +392,37 @@ def layer_main(args, dev):
     }))
 
 
+OP_TIMING_LAUNCHES = 40     # per op: R = 10 launches per graph, replayed 1 + 3 times
+
+
+def summarize_trace(path):
+    """Average duration of each library kernel over all its launches, and
+    over its last OP_TIMING_LAUNCHES launches: those of the per-op timing
+    graphs that produce `parts` (each kernel alone on the GPU), as opposed
+    to the step replays, where independent kernels run side by side."""
+    import csv
+    import collections
+    by = collections.defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            n = r["Kernel_Name"].replace("void ", "").replace("fp4gemm::", "")
+            n = n.replace("(anonymous namespace)::", "").split("(")[0]
+            if n.startswith(("k_gemm", "k_quant", "k_amax")):
+                t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+                by[n].append((t0, (t1 - t0) / 1e3))
+    print("| kernel | calls | avg us, all | avg us, isolated (last %d) |" % OP_TIMING_LAUNCHES)
+    print("|---|---:|---:|---:|")
+    for n, v in by.items():
+        d = [x[1] for x in sorted(v)]
+        iso = d[-OP_TIMING_LAUNCHES:]
+        print("| %s | %d | %.1f | %.1f |" % (n, len(d), sum(d) / len(d), sum(iso) / len(iso)))
+
+
 def main():
     args = parse()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.config)
         return
