@@ -82,6 +82,15 @@ def rht_sign_mask(seed=RHT_SEED):
     return int(_rng(seed, SIGNS_ID).integers(0, 1 << 16))
 
 
+def rht_sign_bits(n, seed=RHT_SEED):
+    """The random diagonal D_r of the n-point RHT as an n-bit integer mask
+    (bit i set: output row i is negated); n = 16 gives rht_sign_mask()."""
+    if n == 16:
+        return rht_sign_mask(seed)
+    bits = _rng(seed, SIGNS_ID + 100 + n).integers(0, 2, size=n)
+    return sum(int(b) << i for i, b in enumerate(bits))
+
+
 def normal(shape, sigma=1.0, cfg_seed=0, tensor_id=X_ID):
     rng = _rng(cfg_seed, tensor_id)
     n = int(np.prod(shape))

@@ -54,7 +54,7 @@ import numpy as np
 
 from . import formats as F
 from .philox import sr_random16
-from .rht import rht16_cols
+from .rht import rht_cols
 
 FLT_MAX = np.float32(np.finfo(np.float32).max)
 
@@ -202,14 +202,15 @@ def unpack_codes(packed):
 # ------------------------------------------------------ full quantize ----
 def quantize(x_bits, fmt="nvfp4", block="1d", orient="row", rnd="rne",
              seed=0, offset=0, rht=False, signs=0, target=448.0,
-             amax=None, emit_transpose=False, index_base=0):
+             amax=None, emit_transpose=False, index_base=0, rht_n=16):
     """Quantize a bf16 matrix (uint16 bit patterns, [R, C]).
 
     orient="row": blocks run along C; output codes [R, C/2], scales
     [R, C/BS].  orient="col": the matrix quantized is X^T, so output codes
     are [C, R/2] and scales [C, R/BS]; with rht=True every 16-row group of
     each column is first rotated by (1/4) D_r H16 (App. C), and the tensor
-    amax is taken after the rotation.  block="2d": 16x16 tiles of X
+    amax is taken after the rotation (rht_n: the size N of the variant
+    transforms, groups of N rows, `signs` an N-bit mask).  block="2d": 16x16 tiles of X
     (rowwise only, RNE only); scales [R/16, C/16]; emit_transpose also
     returns the codes of X^T ([C, R/2]) quantized with the same tile scales.
     amax: None to compute it, or a given (possibly stale) fp32 amax.
@@ -229,8 +230,8 @@ def quantize(x_bits, fmt="nvfp4", block="1d", orient="row", rnd="rne",
         assert R % 16 == 0 and C % 16 == 0
         bs = 16
     if rht:
-        assert orient == "col" and R % 16 == 0
-        x = rht16_cols(x, signs)
+        assert orient == "col" and R % rht_n == 0
+        x = rht_cols(x, signs, rht_n)
     v = x.T.copy() if orient == "col" else x               # rows of v are blocked
     Ro, Co = v.shape
     assert Co % bs == 0, "block axis must be a multiple of the block size"
