@@ -43,6 +43,28 @@ int block_len(fp4_format f) { return f == FP4_MXFP4 ? 32 : 16; }
 
 bool valid_format(int f) { return f == FP4_NVFP4 || f == FP4_UE5M3 || f == FP4_MXFP4; }
 
+int rht_size(const fp4_quant_desc* d) { return d->rht_n ? d->rht_n : 16; }
+
+// RHT size and sign mask of a descriptor (checked only when rht is on).
+fp4_status check_rht(const fp4_quant_desc* d, const char* side) {
+  if (!d->rht) return FP4_OK;
+  const int n = rht_size(d);
+  if (n != 4 && n != 16 && n != 32 && n != 64 && n != 128)
+    return fail(FP4_ERR_ARG, "%s: rht_n=%d must be 4, 16, 32, 64 or 128", side, d->rht_n);
+  const uint32_t w[4] = {d->rht_signs, d->rht_signs_hi[0], d->rht_signs_hi[1], d->rht_signs_hi[2]};
+  for (int i = 0; i < 4; ++i) {
+    const int lo = 32 * i;                          // first bit of word i
+    const uint32_t allowed = n >= lo + 32 ? 0xFFFFFFFFu : n <= lo ? 0u : ((1u << (n - lo)) - 1u);
+    if (w[i] & ~allowed) return fail(FP4_ERR_ARG, "%s: rht sign bits at or above N=%d", side, n);
+  }
+  return FP4_OK;
+}
+
+void copy_signs(const fp4_quant_desc* d, uint32_t (&out)[4]) {
+  out[0] = d->rht_signs;
+  for (int i = 0; i < 3; ++i) out[i + 1] = d->rht_signs_hi[i];
+}
+
 fp4_status check_bf16_input(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld) {
   if (rows < 0 || cols < 0) return fail(FP4_ERR_SHAPE, "negative size rows=%lld cols=%lld",
                                         (long long)rows, (long long)cols);
@@ -79,7 +101,8 @@ FP4_EXPORT fp4_status fp4_amax(const uint16_t* x, int64_t rows, int64_t cols, in
   if (rht && rows % 16) return fail(FP4_ERR_SHAPE, "rht needs rows %% 16 == 0 (rows=%lld)",
                                     (long long)rows);
   if (rht_signs > 0xFFFFu) return fail(FP4_ERR_ARG, "rht_signs must fit in 16 bits");
-  return device_status(fp4lib::launch_amax(x, rows, cols, ld, rht, rht_signs, amax,
+  const uint32_t s4[4] = {rht_signs, 0u, 0u, 0u};
+  return device_status(fp4lib::launch_amax(x, rows, cols, ld, rht, 16, s4, amax,
                                            static_cast<hipStream_t>(stream)),
                        "fp4_amax launch");
 }
@@ -105,7 +128,8 @@ FP4_EXPORT fp4_status fp4_quantize(const fp4_quant_desc* d, const uint16_t* x, i
   if (is2d && d->round != FP4_RNE) return fail(FP4_ERR_UNSUPPORTED, "2D16 blocks are RNE only");
   if (d->rht && d->orient != FP4_COLWISE) return fail(FP4_ERR_UNSUPPORTED, "RHT needs COLWISE");
   if (d->rht && d->format == FP4_MXFP4) return fail(FP4_ERR_UNSUPPORTED, "RHT needs NVFP4 or UE5M3");
-  if (d->rht && d->rht_signs > 0xFFFFu) return fail(FP4_ERR_ARG, "rht_signs must fit in 16 bits");
+  st = check_rht(d, "desc");
+  if (st) return st;
   if (d->amax_given && !two_level) return fail(FP4_ERR_UNSUPPORTED, "MXFP4 has no tensor amax");
   if (!is2d && d->emit_transpose) return fail(FP4_ERR_UNSUPPORTED, "emit_transpose needs 2D16");
   if (d->scale_layout != FP4_SCALES_ROWMAJOR && d->scale_layout != FP4_SCALES_TILED)
@@ -122,6 +146,9 @@ FP4_EXPORT fp4_status fp4_quantize(const fp4_quant_desc* d, const uint16_t* x, i
     if (cols % bs) return fail(FP4_ERR_SHAPE, "cols=%lld must be a multiple of %d", (long long)cols, bs);
   } else {
     if (rows % bs) return fail(FP4_ERR_SHAPE, "rows=%lld must be a multiple of %d", (long long)rows, bs);
+    if (d->rht && rows % rht_size(d))
+      return fail(FP4_ERR_SHAPE, "rows=%lld must be a multiple of rht_n=%d", (long long)rows,
+                  rht_size(d));
   }
   const bool empty = rows == 0 || cols == 0;
   if (!empty) {
@@ -135,7 +162,9 @@ FP4_EXPORT fp4_status fp4_quantize(const fp4_quant_desc* d, const uint16_t* x, i
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (two_level && !d->amax_given) {
-    hipError_t e = fp4lib::launch_amax(x, rows, cols, ld, d->rht, d->rht_signs, amax, s);
+    uint32_t s4[4];
+    copy_signs(d, s4);
+    hipError_t e = fp4lib::launch_amax(x, rows, cols, ld, d->rht, rht_size(d), s4, amax, s);
     if (e != hipSuccess) return device_status(e, "fp4_quantize amax launch");
   }
   fp4lib::QuantArgs a{};
@@ -152,7 +181,8 @@ FP4_EXPORT fp4_status fp4_quantize(const fp4_quant_desc* d, const uint16_t* x, i
   a.target = d->target;
   a.seed = d->seed;
   a.offset = d->offset;
-  a.rht_signs = d->rht_signs;
+  copy_signs(d, a.rht_signs);
+  a.rht_n = rht_size(d);
   a.format = d->format;
   a.round = d->round;
   a.rht = d->rht;
@@ -198,13 +228,17 @@ FP4_EXPORT fp4_status fp4_quantize_dual(const fp4_quant_desc* rd, const fp4_quan
   if (rd->round != cd->round) return fail(FP4_ERR_UNSUPPORTED, "the two rounding modes differ");
   if (rd->rht) return fail(FP4_ERR_UNSUPPORTED, "RHT needs COLWISE");
   if (cd->rht && cd->format == FP4_MXFP4) return fail(FP4_ERR_UNSUPPORTED, "RHT needs NVFP4 or UE5M3");
-  if (cd->rht && cd->rht_signs > 0xFFFFu) return fail(FP4_ERR_ARG, "rht_signs must fit in 16 bits");
+  const fp4_status st0 = check_rht(cd, "colwise");
+  if (st0) return st0;
   fp4_status st = check_bf16_input(x, rows, cols, ld);
   if (st) return st;
   const int bs = block_len(rd->format);
   if (cols % bs || rows % bs)
     return fail(FP4_ERR_SHAPE, "rows=%lld and cols=%lld must be multiples of %d", (long long)rows,
                 (long long)cols, bs);
+  if (cd->rht && rows % rht_size(cd))
+    return fail(FP4_ERR_SHAPE, "rows=%lld must be a multiple of rht_n=%d", (long long)rows,
+                rht_size(cd));
   const bool two_level = rd->format != FP4_MXFP4;
   const bool empty = rows == 0 || cols == 0;
   if (!empty) {
@@ -224,11 +258,14 @@ FP4_EXPORT fp4_status fp4_quantize_dual(const fp4_quant_desc* rd, const fp4_quan
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (two_level && !rd->amax_given) {
-    hipError_t e = fp4lib::launch_amax(x, rows, cols, ld, 0, 0, amax, s);
+    const uint32_t none[4] = {0u, 0u, 0u, 0u};
+    hipError_t e = fp4lib::launch_amax(x, rows, cols, ld, 0, 16, none, amax, s);
     if (e != hipSuccess) return device_status(e, "fp4_quantize_dual amax launch");
   }
   if (two_level && !cd->amax_given && !(amax_t == amax && !rd->amax_given)) {
-    hipError_t e = fp4lib::launch_amax(x, rows, cols, ld, cd->rht, cd->rht_signs, amax_t, s);
+    uint32_t s4[4];
+    copy_signs(cd, s4);
+    hipError_t e = fp4lib::launch_amax(x, rows, cols, ld, cd->rht, rht_size(cd), s4, amax_t, s);
     if (e != hipSuccess) return device_status(e, "fp4_quantize_dual amax launch");
   }
   fp4lib::QuantArgs a[2]{};
@@ -249,7 +286,8 @@ FP4_EXPORT fp4_status fp4_quantize_dual(const fp4_quant_desc* rd, const fp4_quan
     a[i].target = ds[i]->target;
     a[i].seed = ds[i]->seed;
     a[i].offset = ds[i]->offset;
-    a[i].rht_signs = ds[i]->rht_signs;
+    copy_signs(ds[i], a[i].rht_signs);
+    a[i].rht_n = rht_size(ds[i]);
     a[i].format = ds[i]->format;
     a[i].round = ds[i]->round;
     a[i].rht = ds[i]->rht;

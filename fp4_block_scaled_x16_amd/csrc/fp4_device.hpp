@@ -262,4 +262,52 @@ __host__ __device__ __forceinline__ uint64_t tiled_scale_offset(uint64_t r, uint
   return (((r >> 8) * kg + (j >> 3)) << 11) + ((r & 255u) << 3) + (j & 7u);
 }
 
+
+// N-point variant (N in {4, 16, 32, 64, 128}): fl32(1/sqrt(N)) D_r H_N on
+// groups of N consecutive rows of a column.  A lane holds 16 consecutive
+// rows (one 1x16 block); for N > 16 the N / 16 lanes whose index bits 0-2
+// (`grp`) differ only below N / 16 hold the rest of the group, and the
+// butterflies with strides 16, 32, 64 run between them by xor shuffles
+// (the lane with the bit clear holds the lower entry: a + b; its partner
+// a - b).  Stride order 1, 2, 4, ... as in rht16; N = 4 runs strides 1, 2
+// only (four independent 4-point transforms).  Every lane of an N-row
+// group must be active.
+struct RhtN {
+  int n;
+  float scale;          // fl32(1 / sqrt(n))
+  uint32_t s[4];        // D_r: bit i of the 128-bit mask negates output row i
+};
+
+__device__ __forceinline__ void rht_n(float (&v)[16], const RhtN& r, int grp) {
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+    if (h >= 4 && r.n < 16) break;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if ((i & h) == 0) {
+        const float a = v[i], b = v[i + h];
+        v[i] = a + b;
+        v[i + h] = a - b;
+      }
+    }
+  }
+  for (int m = 1; 16 * m < r.n; m <<= 1) {
+    const bool upper = (grp & m) != 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float o = __shfl_xor(v[i], m, 64);
+      v[i] = upper ? o - v[i] : v[i] + o;
+    }
+  }
+  // sign bits of this lane's rows: 16 consecutive bits from `base`
+  const int base = r.n <= 16 ? 0 : ((grp & (r.n / 16 - 1)) << 4);
+  const int wsel = base >> 5;
+  const uint32_t word = wsel == 0 ? r.s[0] : wsel == 1 ? r.s[1] : wsel == 2 ? r.s[2] : r.s[3];
+  const int lmask = r.n < 16 ? r.n - 1 : 15;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const float q = v[k] * r.scale;
+    v[k] = ((word >> ((base & 31) + (k & lmask))) & 1u) ? -q : q;
+  }
+}
 }  // namespace fp4dev

@@ -20,7 +20,8 @@ struct QuantArgs {
   fp4_counters* counters;
   float target;
   uint64_t seed, offset;
-  uint32_t rht_signs;
+  uint32_t rht_signs[4];   // D_r of the RHT: bit i negates output row i (128 bits)
+  int rht_n;               // RHT size: 4, 16, 32, 64 or 128 (0 means 16)
   int format, round, rht, emit_transpose;
   int tiled;             // 1D scales in the TILED layout (2 KiB atoms of 256 rows x 8 blocks)
 };
@@ -39,7 +40,7 @@ struct GemmOperand {
 int device_cu_count();
 
 hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int rht,
-                       uint32_t signs, float* amax, hipStream_t s);
+                       int rht_n, const uint32_t (&signs)[4], float* amax, hipStream_t s);
 hipError_t launch_quant_row(const QuantArgs& a, hipStream_t s);
 hipError_t launch_quant_col(const QuantArgs& a, hipStream_t s);
 hipError_t launch_quant_2d(const QuantArgs& a, hipStream_t s);

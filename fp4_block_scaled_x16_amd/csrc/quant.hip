@@ -11,6 +11,8 @@
 // workgroups per CU and walk the work with grid-stride loops, so the
 // tensor-scale prologue and the counter flush are paid once per workgroup.
 #include <hip/hip_runtime.h>
+
+#include <cmath>
 #include <stdint.h>
 
 #include "fp4_device.hpp"
@@ -298,12 +300,16 @@ __global__ __launch_bounds__(kStream) void k_quant_row(
 // each thread takes one column pair and one row group, optionally rotates
 // each 16-row group by the RHT, and writes the codes of X^T so that the 8
 // lanes of a column cover 8 consecutive groups (64 or 128 contiguous bytes).
-template <int FMT, int RND, bool RHT, bool CNT>
+//
+// AMX (amax only): the same staging and rotation, but instead of encoding,
+// the largest |value| is reduced into *amax_out (fp32 bits, atomic max):
+// the tensor amax in the rotated space for the N-point RHT variants.
+template <int FMT, int RND, bool RHT, bool CNT, bool AMX = false>
 __global__ __launch_bounds__(kThreads) void k_quant_col(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, const float* __restrict__ amax,
     float target, float* __restrict__ s_dec_out, uint64_t seed, uint64_t offset,
-    uint32_t signs, fp4_counters* __restrict__ counters, int tiled) {
+    RhtN rht, fp4_counters* __restrict__ counters, int tiled, uint32_t* __restrict__ amax_out) {
   constexpr int BS = FMT == kMX ? 32 : 16;
   constexpr int TR = 8 * BS;        // tile rows (8 groups)
   constexpr int TC = 64;            // tile columns
@@ -311,7 +317,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
   __shared__ uint32_t tile[TR * LDW];
 
   float s_enc_g = 1.0f, s_dec_g = 1.0f;
-  if constexpr (FMT != kMX) global_scales(*amax, target, s_enc_g, s_dec_g);
+  if constexpr (FMT != kMX && !AMX) global_scales(*amax, target, s_enc_g, s_dec_g);
   if (s_dec_out && blockIdx.x == 0 && threadIdx.x == 0) *s_dec_out = s_dec_g;
 
   const int64_t tiles_c = (cols + TC - 1) / TC;
@@ -322,6 +328,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
   const int grp = lane & 7;                  // row group handled in the compute phase
   const int pair = wave * 8 + (lane >> 3);   // column pair (0..31)
   uint32_t cnt[5] = {0, 0, 0, 0, 0};
+  float vmax = 0.0f;                         // AMX
 
   for (int64_t tile_id = blockIdx.x; tile_id < ntiles; tile_id += gridDim.x) {
     const int64_t tr = tile_id / tiles_c, tc = tile_id - tr * tiles_c;
@@ -353,11 +360,15 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
           const uint32_t w = tile[(grp * BS + k) * LDW + pair];
           v[k] = bf16_to_f32(h ? (w >> 16) : (w & 0xFFFFu));
         }
-        if constexpr (RHT) rht16(*reinterpret_cast<float(*)[16]>(v), signs);
+        if constexpr (RHT) rht_n(*reinterpret_cast<float(*)[16]>(v), rht, grp);
         const int64_t c = col + h;
         float amax_b = 0.0f;
 #pragma unroll
         for (int k = 0; k < BS; ++k) amax_b = fmaxf(amax_b, fabsf(v[k]));
+        if constexpr (AMX) {
+          vmax = fmaxf(vmax, amax_b);
+          continue;
+        }
         float s_enc_l;
         const uint32_t sc = scale_for_block<FMT>(amax_b, s_enc_g, s_dec_g, s_enc_l, cnt);
         uint32_t words[BS / 8];
@@ -376,6 +387,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
     }
     __syncthreads();
   }
+  if constexpr (AMX) flush_max<kThreads>(__float_as_uint(vmax), amax_out);
   if constexpr (CNT) flush_counters<kThreads>(cnt, counters);
 }
 
@@ -399,7 +411,7 @@ __attribute__((amdgpu_waves_per_eu(FMT == kMX ? 1 : 3))) void k_quant_dual(
     uint8_t* __restrict__ scales_t, const float* __restrict__ amax,
     const float* __restrict__ amax_t, float target, float target_t,
     float* __restrict__ s_dec_out, float* __restrict__ s_dec_t_out, uint64_t seed,
-    uint64_t offset, uint64_t seed_t, uint64_t offset_t, uint32_t signs,
+    uint64_t offset, uint64_t seed_t, uint64_t offset_t, RhtN rht,
     fp4_counters* __restrict__ counters, int tiled, int tiled_t) {
   constexpr int BS = FMT == kMX ? 32 : 16;
   constexpr int TR = 8 * BS;        // tile rows (8 groups)
@@ -508,7 +520,7 @@ __attribute__((amdgpu_waves_per_eu(FMT == kMX ? 1 : 3))) void k_quant_dual(
           const uint32_t w = tile[(grp * BS + k) * LDW + pair];
           v[k] = bf16_to_f32(h ? (w >> 16) : (w & 0xFFFFu));
         }
-        if constexpr (RHT) rht16(*reinterpret_cast<float(*)[16]>(v), signs);
+        if constexpr (RHT) rht_n(*reinterpret_cast<float(*)[16]>(v), rht, grp);
         const int64_t c = col + h;
         float amax_b = 0.0f;
 #pragma unroll
@@ -746,15 +758,33 @@ int device_cu_count() {
   return cache[dev];
 }
 
+// The RHT of size n (0 means 16) with the 128-bit sign mask s4.
+static RhtN make_rht(int n, const uint32_t (&s4)[4]) {
+  RhtN r;
+  r.n = n ? n : 16;
+  r.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(r.n)));
+  for (int i = 0; i < 4; ++i) r.s[i] = s4[i];
+  return r;
+}
+
 hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int rht,
-                       uint32_t signs, float* amax, hipStream_t s) {
+                       int rht_n, const uint32_t (&signs)[4], float* amax, hipStream_t s) {
   uint32_t* out = reinterpret_cast<uint32_t*>(amax);
   hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(1), 0, s, out, 0u);
   if (rows > 0 && cols > 0) {
-    if (rht) {
+    const RhtN r = make_rht(rht_n, signs);
+    if (rht && r.n == 16) {
       const uint64_t n = static_cast<uint64_t>(rows / 16) * static_cast<uint64_t>(cols / 2);
       hipLaunchKernelGGL(k_amax_rht, dim3(grid_for(n, 1)), dim3(kStream), 0, s, x, rows, cols,
-                         ld, signs, out);
+                         ld, signs[0], out);
+    } else if (rht) {
+      // the other sizes: the colwise quantizer's staging and rotation, amax only
+      const int64_t tiles = ((rows + 127) / 128) * ((cols + 63) / 64);
+      const int64_t cap = static_cast<int64_t>(device_cu_count()) * kTileWgPerCu;
+      const int grid = static_cast<int>(tiles < cap ? tiles : cap);
+      hipLaunchKernelGGL((k_quant_col<kNV, FP4_RNE, true, false, true>), dim3(grid),
+                         dim3(kThreads), 0, s, x, rows, cols, ld, nullptr, nullptr, nullptr, 0.0f,
+                         nullptr, uint64_t(0), uint64_t(0), r, nullptr, 0, out);
     } else {
       const uint64_t n = static_cast<uint64_t>(rows) * static_cast<uint64_t>(cols / 8);
       hipLaunchKernelGGL(k_amax, dim3(grid_for(n, 1)), dim3(kStream), 0, s, x, rows, cols, ld,
@@ -802,7 +832,7 @@ static void col_launch(const QuantArgs& a, hipStream_t s) {
   const int grid = static_cast<int>(tiles < cap ? (tiles > 0 ? tiles : 1) : cap);
   hipLaunchKernelGGL((k_quant_col<FMT, RND, RHT, CNT>), dim3(grid), dim3(kThreads), 0, s, a.x,
                      a.rows, a.cols, a.ld, a.codes, a.scales, a.amax, a.target, a.s_dec, a.seed,
-                     a.offset, a.rht_signs, a.counters, a.tiled);
+                     a.offset, make_rht(a.rht_n, a.rht_signs), a.counters, a.tiled, nullptr);
 }
 
 template <int FMT, int RND, bool RHT>
@@ -844,7 +874,7 @@ static void dual_launch(const QuantArgs& a, const QuantArgs& b, hipStream_t s) {
   hipLaunchKernelGGL((k_quant_dual<FMT, RND, RHT, CNT>), dim3(grid), dim3(kThreads), 0, s, a.x,
                      a.rows, a.cols, a.ld, a.codes, a.scales, b.codes, b.scales, a.amax, b.amax,
                      a.target, b.target, a.s_dec, b.s_dec, a.seed, a.offset, b.seed, b.offset,
-                     b.rht_signs, a.counters, a.tiled, b.tiled);
+                     make_rht(b.rht_n, b.rht_signs), a.counters, a.tiled, b.tiled);
 }
 
 template <int FMT, int RND, bool RHT>

@@ -104,9 +104,10 @@ typedef struct {
   fp4_round round;        /* SR: 1D only                                       */
   uint64_t seed;          /* SR: Philox4x32-10 key                             */
   uint64_t offset;        /* SR: Philox counter words 2-3 (e.g. a step number) */
-  int rht;                /* COLWISE only: rotate every 16-row group of each
-                             column by (1/4) D_r H16 first (App. C)            */
-  uint32_t rht_signs;     /* D_r: bit i set negates output row i of H16        */
+  int rht;                /* COLWISE only: rotate every rht_n-row group of each
+                             column by fl32(1/sqrt(N)) D_r H_N first (App. C;
+                             §4.2 weighs N = 4, 16, 128 and uses 16)           */
+  uint32_t rht_signs;     /* D_r, bits 0-31: bit i set negates output row i   */
   float target;           /* T in s_enc = 6 T / amax: 448 for NVFP4; 448 or
                              2048 for UE5M3; ignored for MXFP4; finite, > 0    */
   int amax_given;         /* 0: compute the tensor amax into *amax first;
@@ -116,6 +117,12 @@ typedef struct {
   fp4_scale_layout scale_layout;  /* 1D only: layout of `scales` (TILED: of
                              the output code matrix, [rows, cols] for ROWWISE,
                              [cols, rows] for COLWISE)                         */
+  int rht_n;              /* RHT size N: 4, 16, 32, 64 or 128; 0 means 16.
+                             Arithmetic: fp32 butterflies with strides 1, 2,
+                             ..., N/2, then * fl32(1/sqrt(N)), then the signs;
+                             rows must be a multiple of N                      */
+  uint32_t rht_signs_hi[3];  /* D_r, bits 32-127 (N > 32); every bit at or
+                             above N must be 0                                  */
 } fp4_quant_desc;
 
 /*

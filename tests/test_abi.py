@@ -93,6 +93,32 @@ def test_quantize_rejects(lib, kw, rows, cols, status):
     assert _err(lib)
 
 
+def _hi(*w):
+    return (ctypes.c_uint32 * 3)(*w)
+
+
+@pytest.mark.parametrize("kw,rows,status", [
+    (dict(rht_n=8), 64, 1),                                  # not a supported size
+    (dict(rht_n=256), 256, 1),
+    (dict(rht_n=32), 48, 2),                                 # rows % N
+    (dict(rht_n=128), 192, 2),
+    (dict(rht_n=4, rht_signs=0x10), 32, 1),                  # sign bit at or above N
+    (dict(rht_n=16, rht_signs=1 << 16), 32, 1),
+    (dict(rht_n=32, rht_signs_hi=_hi(1, 0, 0)), 64, 1),
+    (dict(rht_n=64, rht_signs_hi=_hi(0, 1, 0)), 64, 1),
+])
+def test_quantize_rejects_rht_sizes(lib, kw, rows, status):
+    assert quant(lib, desc(orient=1, rht=1, **kw), rows, 64) == status
+    assert _err(lib)
+
+
+def test_quantize_rht_size_is_unchecked_without_rht(lib):
+    # rht_n and the high sign words only matter with rht on: an RNE rowwise
+    # call with them set passes validation up to the (missing) device
+    d = desc(rht_n=8, rht_signs_hi=_hi(7, 7, 7))
+    assert quant(lib, d, codes=None) == 1 and "codes" in _err(lib)
+
+
 def test_quantize_rejects_pointers(lib):
     assert quant(lib, desc(), x=None) == 1
     assert quant(lib, desc(), x=ctypes.c_void_p(0x10008)) == 1      # misaligned
@@ -118,6 +144,8 @@ def dual(lib, rd, cd, rows=32, cols=64, x=FAKE, codes=FAKE, scales=FAKE, codes_t
     (dict(orient=1), dict(orient=1), 32, 64, 3),              # first desc must be ROWWISE
     (dict(), dict(), 32, 64, 3),                              # second desc must be COLWISE
     (dict(), dict(orient=1, format=1), 32, 64, 3),            # formats differ
+    (dict(), dict(orient=1, rht=1, rht_n=64), 32, 64, 2),     # rows % rht_n
+    (dict(), dict(orient=1, rht=1, rht_n=5), 64, 64, 1),
     (dict(), dict(orient=1, round=1), 32, 64, 3),             # rounding modes differ
     (dict(rht=1), dict(orient=1), 32, 64, 3),                 # RHT on the rowwise side
     (dict(format=2), dict(orient=1, format=2, rht=1), 64, 64, 3),   # RHT with MXFP4

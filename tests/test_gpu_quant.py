@@ -330,3 +330,43 @@ def test_workload4_counters_slab(T):
         q, r, c = run_both(xb, "ue5m3", rnd=rnd, target=T, stale=amax)
         assert_same(q, r, c)
         assert c["scale_saturated"] == 0          # UE5M3 range absorbs the stale amax
+
+
+# ------------------------------------------------ RHT sizes N = 4 ... 128 --
+@pytest.mark.parametrize("n", [4, 16, 32, 64, 128])
+@pytest.mark.parametrize("fmt,rnd", [("nvfp4", "rne"), ("nvfp4", "sr"), ("ue5m3", "rne")])
+def test_colwise_rht_sizes(n, fmt, rnd):
+    """Colwise quantization with the N-point RHT, the tensor amax taken in
+    the rotated space by the library (N = 16 by its own kernel, the other
+    sizes by the colwise kernel's amax mode): everything bit-exact."""
+    rows = 384 if n == 128 else 320        # whole 128-row tiles, or 2 tiles + a 64-row tile
+    x = inputs.gradients((rows, 200), cfg_seed=44) if rnd == "sr" else \
+        inputs.activations((rows, 200), cfg_seed=44)
+    signs = inputs.rht_sign_bits(n)
+    cnt = api.new_counters()
+    q = api.quantize(dev(x), fmt, orient="col", rnd=rnd, seed=2, offset=5, rht=True, signs=signs,
+                     rht_n=n, counters=cnt)
+    torch.cuda.synchronize()
+    r = Q.quantize(x, fmt, orient="col", rnd=rnd, seed=2, offset=5, rht=True, signs=signs,
+                   rht_n=n)
+    assert_same(q, r, api.counters_dict(cnt))
+
+
+@pytest.mark.parametrize("n,rnd", [(4, "rne"), (32, "sr"), (128, "sr")])
+def test_dual_rht_sizes(n, rnd):
+    x = inputs.gradients((384, 208), cfg_seed=45)
+    signs = inputs.rht_sign_bits(n)
+    cnt = api.new_counters()
+    qr, qc = api.quantize_dual(dev(x), "nvfp4", rnd=rnd, seed=2, offset=0, offset_t=1, rht=True,
+                               signs=signs, rht_n=n, counters=cnt, scale_layout="tiled")
+    torch.cuda.synchronize()
+    rr = Q.quantize(x, "nvfp4", orient="row", rnd=rnd, seed=2, offset=0)
+    rc = Q.quantize(x, "nvfp4", orient="col", rnd=rnd, seed=2, offset=1, rht=True, signs=signs,
+                    rht_n=n)
+    for q, r in ((qr, rr), (qc, rc)):
+        assert np.array_equal(q.codes.cpu().numpy(), r["codes"])
+        assert np.array_equal(gpu_scales(q), r["scales"])
+        assert f32_bits(q.amax.item()) == f32_bits(r["amax"])
+        assert f32_bits(q.s_dec.item()) == f32_bits(r["s_dec"])
+    assert api.counters_dict(cnt) == {k: rr["counters"][k] + rc["counters"][k]
+                                      for k in rr["counters"]}
