@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--layer", action="store_true",
                     help="time QuantizedLinear.forward + backward (the layer a user calls) "
                          "instead of the step's kernel list")
+    ap.add_argument("--rht-n", type=int, default=16, choices=(4, 16, 32, 64, 128),
+                    help="--layer on the 12B workload: size of the RHT")
     ap.add_argument("--no-rht", action="store_true",
                     help="--layer on the 12B workload: leave out the RHT of the Wgrad operands")
     ap.add_argument("--serial", action="store_true",
@@ -351,8 +353,8 @@ def layer_main(args, dev):
     t = inputs.linear_tensors(cfg)
     X, W, dY = (torch.from_numpy(t[n].view(np.int16)).to(dev) for n in ("X", "W", "dY"))
     rht = cfg == 3 and not args.no_rht
-    r = Recipe(fmt, target_dy=2048.0 if fmt == "ue5m3" else 448.0, rht=rht,
-               rht_signs=inputs.rht_sign_mask() if rht else 0)
+    r = Recipe(fmt, target_dy=2048.0 if fmt == "ue5m3" else 448.0, rht=rht, rht_n=args.rht_n,
+               rht_signs=inputs.rht_sign_bits(args.rht_n) if rht else 0)
     layer = QuantizedLinear(W, r)
 
     def step():
@@ -382,7 +384,7 @@ def layer_main(args, dev):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "data": "synthetic (seeded PCG64, bf16 inputs resident in HBM)",
         "config": {"workload": c["name"].replace("-rht", "") + ("-rht" if rht else "") + "-layer",
-                   "format": fmt, "rht": rht,
+                   "format": fmt, "rht": rht, "rht_n": args.rht_n if rht else None,
                    "tokens": c["tokens"], "d_in": c["d_in"], "d_out": c["d_out"],
                    "amax": "current (recomputed every step)", "wgrad": "fp32 accumulate"},
         "counters_all_runs": {k: int(v) for k, v in zip(("scale_saturated", "scale_underflow",

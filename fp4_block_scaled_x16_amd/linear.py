@@ -41,7 +41,8 @@ class Recipe:
     target_w: float = 448.0
     target_dy: float = 448.0
     rht: bool = False             # RHT on the Wgrad operands (colwise X and dY)
-    rht_signs: int = 0            # 16-bit sign mask D_r
+    rht_n: int = 16               # RHT size N: 4, 16, 32, 64 or 128
+    rht_signs: int = 0            # N-bit sign mask D_r
     sr_seed: int = 1              # Philox key of the stochastic rounding of dY
     amax_interval: int = 1        # recompute each tensor amax every this many steps
     scale_layout: str = "tiled"   # storage of the 1D block scales
@@ -81,14 +82,18 @@ class QuantizedLinear:
     def _amax_args(self, x, name, rht):
         """amax buffers (rowwise, colwise) for a dual quantization of x,
         refreshed on this step if due; without RHT both sides share one
-        buffer.  MXFP4 has none."""
+        buffer.  MXFP4 has none.  With an RHT of size other than 16 the
+        colwise amax is left to the quantizer (None: computed in the rotated
+        space) and kept from its result."""
         r = self.recipe
         if not r.two_level:
             return None, None
         if self._refresh():
             api.amax(x, out=self.amax[name])
-            if rht:
+            if rht and r.rht_n == 16:
                 api.amax(x, rht=True, signs=r.rht_signs, out=self.amax[name + "_t"])
+            elif rht:
+                return self.amax[name], None
         return self.amax[name], self.amax[name + "_t" if rht else name]
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
@@ -96,9 +101,11 @@ class QuantizedLinear:
         if x.dim() != 2 or x.shape[1] != self.in_features:
             raise ValueError("x must be [tokens, in_features]")
         am, am_t = self._amax_args(x, "x", r.rht)
-        qx, qx_t = api.quantize_dual(x, r.fmt, rht=r.rht, signs=r.rht_signs, target=r.target_x,
-                                     amax_in=am, amax_t_in=am_t, counters=self.counters,
-                                     scale_layout=r.scale_layout)
+        qx, qx_t = api.quantize_dual(x, r.fmt, rht=r.rht, signs=r.rht_signs, rht_n=r.rht_n,
+                                     target=r.target_x, amax_in=am, amax_t_in=am_t,
+                                     counters=self.counters, scale_layout=r.scale_layout)
+        if r.rht and am_t is None and r.two_level:
+            self.amax["x_t"] = qx_t.amax
         if r.two_level:
             if self._refresh():
                 api.amax(self.weight, out=self.amax["w"])
@@ -125,8 +132,11 @@ class QuantizedLinear:
         am, am_t = self._amax_args(dy, "dy", r.rht)
         qdy, qdy_t = api.quantize_dual(dy, r.fmt, rnd="sr", seed=r.sr_seed, offset=2 * self.step,
                                        offset_t=2 * self.step + 1, rht=r.rht, signs=r.rht_signs,
-                                       target=r.target_dy, amax_in=am, amax_t_in=am_t,
-                                       counters=self.counters, scale_layout=r.scale_layout)
+                                       rht_n=r.rht_n, target=r.target_dy, amax_in=am,
+                                       amax_t_in=am_t, counters=self.counters,
+                                       scale_layout=r.scale_layout)
+        if r.rht and am_t is None and r.two_level:
+            self.amax["dy_t"] = qdy_t.amax
         dx = api.gemm(qdy.operand(), wt_op, tokens, self.in_features, self.out_features,
                       device=dy.device)
         api.gemm(qdy_t.operand(), qx_t.operand(), self.out_features, self.in_features, tokens,

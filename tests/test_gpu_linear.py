@@ -5,8 +5,9 @@ Per step: Y = Fprop, dX = Dgrad, and the fp32 main gradient accumulating
 Wgrad, each within 1e-5 * s_A s_B sum|a b| per element (summed over the
 steps for the accumulated gradient) of the oracle's fp64 GEMMs of its own
 quantized operands; event counters equal to the oracle's.  Cases: NVFP4
-with and without the RHT, UE5M3 with the tensor amax refreshed every second
-step (steps in between reuse it on new data), MXFP4.
+with and without the RHT (16-point, and 64-point with the amax refreshed
+every second step), UE5M3 with the tensor amax refreshed every second step
+(steps in between reuse it on new data), MXFP4.
 """
 import numpy as np
 import pytest
@@ -17,7 +18,7 @@ from fp4_block_scaled_x16_amd.linear import QuantizedLinear, Recipe
 from oracle import formats as F
 from oracle import gemm as G
 from oracle import quantize as Q
-from oracle.rht import rht16_cols
+from oracle.rht import rht_cols
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -44,7 +45,7 @@ def oracle_step(x, w, dy, r: Recipe, step, amax):
     fmt, cnt = r.fmt, []
     qx = Q.quantize(x, fmt, orient="row", target=r.target_x, amax=amax["x"])
     qxt = Q.quantize(x, fmt, orient="col", rht=r.rht, signs=r.rht_signs, target=r.target_x,
-                     amax=amax["x_t"])
+                     amax=amax["x_t"], rht_n=r.rht_n)
     if r.two_level:
         qw = Q.quantize(w, fmt, block="2d", emit_transpose=True, target=r.target_w,
                         amax=amax["w"])
@@ -58,7 +59,8 @@ def oracle_step(x, w, dy, r: Recipe, step, amax):
     qdy = Q.quantize(dy, fmt, orient="row", rnd="sr", seed=r.sr_seed, offset=2 * step,
                      target=r.target_dy, amax=amax["dy"])
     qdyt = Q.quantize(dy, fmt, orient="col", rnd="sr", seed=r.sr_seed, offset=2 * step + 1,
-                      rht=r.rht, signs=r.rht_signs, target=r.target_dy, amax=amax["dy_t"])
+                      rht=r.rht, signs=r.rht_signs, target=r.target_dy, amax=amax["dy_t"],
+                      rht_n=r.rht_n)
     cnt += [qx["counters"], qxt["counters"], qdy["counters"], qdyt["counters"]]
     out = {}
     for name, a, sa, b, sb in (("y", vals(qx, fmt), s_dec(qx, fmt), wv, sw),
@@ -75,8 +77,8 @@ def tensor_amaxes(x, w, dy, r):
         return dict(x=None, x_t=None, w=None, dy=None, dy_t=None)
     xf, dyf = F.bf16_bits_to_f32(x), F.bf16_bits_to_f32(dy)
     a = dict(x=Q.tensor_amax(xf), w=Q.tensor_amax(F.bf16_bits_to_f32(w)), dy=Q.tensor_amax(dyf))
-    a["x_t"] = Q.tensor_amax(rht16_cols(xf, r.rht_signs)) if r.rht else a["x"]
-    a["dy_t"] = Q.tensor_amax(rht16_cols(dyf, r.rht_signs)) if r.rht else a["dy"]
+    a["x_t"] = Q.tensor_amax(rht_cols(xf, r.rht_signs, r.rht_n)) if r.rht else a["x"]
+    a["dy_t"] = Q.tensor_amax(rht_cols(dyf, r.rht_signs, r.rht_n)) if r.rht else a["dy"]
     return a
 
 
@@ -89,6 +91,8 @@ def check(got, ref_bound):
 RECIPES = {
     "nvfp4": (Recipe("nvfp4"), 1),
     "nvfp4_rht": (Recipe("nvfp4", rht=True, rht_signs=SIGNS), 1),
+    "nvfp4_rht64_periodic": (Recipe("nvfp4", rht=True, rht_n=64, rht_signs=inputs.rht_sign_bits(64),
+                                    amax_interval=2), 3),
     "ue5m3_periodic": (Recipe("ue5m3", target_dy=2048.0, amax_interval=2), 3),
     "mxfp4": (Recipe("mxfp4"), 1),
 }
@@ -100,6 +104,8 @@ def test_linear_layer(name):
     tokens, d_in, d_out = 272, 128, 208          # 2D W tiles; two GEMM tiles in two dims
     if r.fmt == "mxfp4":
         tokens, d_in, d_out = 320, 128, 224      # 32-multiples for 1x32 blocks
+    if r.rht and r.rht_n > 16:
+        tokens = 320                             # a multiple of the RHT size
     w = inputs.weights((d_out, d_in), cfg_seed=80)
     layer = QuantizedLinear(dev(w), r)
     dw_ref = np.zeros((d_out, d_in))
