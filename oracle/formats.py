@@ -115,6 +115,28 @@ def _scale_rne_sat(t, table):
     return idx.astype(np.uint8), sat
 
 
+def _scale_up_sat(t, table):
+    """Smallest table value >= t (the code of t rounded up), saturating at
+    the largest; `table` is ascending in the code."""
+    t = np.asarray(t, dtype=np.float32)
+    assert np.all(t >= 0) and np.all(np.isfinite(t)), "scale input must be finite, >= 0"
+    mag = t.astype(np.float64)
+    sat = mag > table[-1]
+    idx = np.searchsorted(table, np.minimum(mag, table[-1]), side="left")
+    return idx.astype(np.uint8), sat
+
+
+def e4m3_up_sat(t):
+    """E4M3 code of fp32 ``t >= 0`` rounded up (never below t unless t > 448,
+    which saturates to 448)."""
+    return _scale_up_sat(t, E4M3_VALUES)
+
+
+def ue5m3_up_sat(t):
+    """UE5M3 code of fp32 ``t >= 0`` rounded up, saturating at 122880."""
+    return _scale_up_sat(t, UE5M3_VALUES)
+
+
 def e4m3_rne_sat(t):
     """E4M3 code of fp32 ``t >= 0``: RNE, saturating at 448 (never NaN).
 

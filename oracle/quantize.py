@@ -90,22 +90,26 @@ def global_scales(amax, target=448.0):
 
 
 # ------------------------------------------------------------ B.2 -------
-def block_scales_two_level(amax_b, s_enc_g, s_dec_g, fmt):
+def block_scales_two_level(amax_b, s_enc_g, s_dec_g, fmt, scale_round="rne"):
     """Scale codes and local encode scales for NVFP4 / UE5M3 blocks.
 
-    amax_b: fp32 array of block amaxes.  Returns (codes uint8, s_enc_L fp32,
-    per-block event arrays dict).
+    amax_b: fp32 array of block amaxes.  scale_round: "rne" (App. B.2: the
+    scale is rounded to nearest) or "up" (the 2D-block page's truncation-free
+    scaling, read as: the scale is rounded up, so the block amax times the
+    encode scale does not exceed 6 and no element is clipped).  Returns
+    (codes uint8, s_enc_L fp32, per-block event arrays dict).
     """
+    assert scale_round in ("rne", "up")
     amax_b = np.asarray(amax_b, dtype=np.float32)
     s_dec_l = (amax_b / np.float32(6.0)).astype(np.float32)            # Eq. 2
     with np.errstate(over="ignore"):
         t = (s_dec_l * np.float32(s_enc_g)).astype(np.float32)          # Eq. 3
     t = np.where(np.isfinite(t), t, FLT_MAX).astype(np.float32)
     if fmt == "nvfp4":
-        code, sat = F.e4m3_rne_sat(t)
+        code, sat = (F.e4m3_up_sat if scale_round == "up" else F.e4m3_rne_sat)(t)
         s_hat = F.e4m3_value(code).astype(np.float32)
     elif fmt == "ue5m3":
-        code, sat = F.ue5m3_rne_sat(t)
+        code, sat = (F.ue5m3_up_sat if scale_round == "up" else F.ue5m3_rne_sat)(t)
         s_hat = F.ue5m3_value(code).astype(np.float32)
     else:
         raise ValueError(fmt)
@@ -202,7 +206,7 @@ def unpack_codes(packed):
 # ------------------------------------------------------ full quantize ----
 def quantize(x_bits, fmt="nvfp4", block="1d", orient="row", rnd="rne",
              seed=0, offset=0, rht=False, signs=0, target=448.0,
-             amax=None, emit_transpose=False, index_base=0, rht_n=16):
+             amax=None, emit_transpose=False, index_base=0, rht_n=16, scale_round="rne"):
     """Quantize a bf16 matrix (uint16 bit patterns, [R, C]).
 
     orient="row": blocks run along C; output codes [R, C/2], scales
@@ -216,6 +220,10 @@ def quantize(x_bits, fmt="nvfp4", block="1d", orient="row", rnd="rne",
     amax: None to compute it, or a given (possibly stale) fp32 amax.
     index_base: output-layout index of element (0, 0), so that a slab of
     output rows of a larger matrix draws the same random bits (SR only).
+    scale_round: "rne" or "up" (truncation-free block scales; two-level
+    formats -- MXFP4 scales are always rounded up).  block="2d" with SR
+    draws the random bits of element (r, c) of X at index r*C + c, so the
+    codes of X^T are exactly the transposed codes of X.
 
     Returns a dict: codes, scales, codes_t (2D only), amax, s_dec, counters.
     """
@@ -226,7 +234,7 @@ def quantize(x_bits, fmt="nvfp4", block="1d", orient="row", rnd="rne",
     R, C = x.shape
     bs = BLOCK[fmt]
     if block == "2d":
-        assert fmt != "mxfp4" and orient == "row" and rnd == "rne" and not rht
+        assert fmt != "mxfp4" and orient == "row" and not rht
         assert R % 16 == 0 and C % 16 == 0
         bs = 16
     if rht:
@@ -256,7 +264,7 @@ def quantize(x_bits, fmt="nvfp4", block="1d", orient="row", rnd="rne",
     if fmt == "mxfp4":
         scode, s_enc_l, sev = block_scales_mx(amax_b)
     else:
-        scode, s_enc_l, sev = block_scales_two_level(amax_b, s_enc_g, s_dec_g, fmt)
+        scode, s_enc_l, sev = block_scales_two_level(amax_b, s_enc_g, s_dec_g, fmt, scale_round)
 
     # per-element encode scale
     if block == "1d":

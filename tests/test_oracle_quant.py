@@ -347,3 +347,70 @@ def test_empty_tensor():
     q = Q.quantize(x, "nvfp4")
     assert q["codes"].shape == (0, 16) and q["scales"].shape == (0, 2)
     assert q["amax"] == 0 and q["s_dec"] == 1
+
+
+# --------------------------------- truncation-free scales and 2D SR --------
+# (2D-block FP4 page: 2D blocks combined with truncation-free scaling and
+# stochastic rounding keep gradients unbiased)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "ue5m3"])
+def test_round_up_scale_is_smallest_value_not_below(fmt):
+    table = F.E4M3_VALUES if fmt == "nvfp4" else F.UE5M3_VALUES
+    enc = F.e4m3_up_sat if fmt == "nvfp4" else F.ue5m3_up_sat
+    rng = np.random.default_rng(21)
+    t = np.concatenate([table.astype(np.float32),                       # exactly representable
+                        (rng.uniform(0, 1, 20000) * table[-1]).astype(np.float32),
+                        np.float32(2.0) ** rng.uniform(-24, 10, 20000).astype(np.float32)])
+    t = t[t <= table[-1]]
+    code, sat = enc(t)
+    assert not sat.any()
+    v = table[code]
+    assert np.all(v >= t.astype(np.float64))                  # never below
+    below = code > 0
+    assert np.all(table[code[below] - 1] < t[below])           # and the smallest such
+    # on representable inputs it agrees with round-to-nearest
+    exact = np.isin(t.astype(np.float64), table)
+    rne = (F.e4m3_rne_sat if fmt == "nvfp4" else F.ue5m3_rne_sat)(t[exact])[0]
+    assert np.array_equal(code[exact], rne)
+    c, s = enc(np.float32([table[-1] * 2]))
+    assert c[0] == len(table) - 1 and s[0]
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "ue5m3"])
+@pytest.mark.parametrize("block", ["1d", "2d"])
+def test_round_up_scales_leave_nothing_to_clip(fmt, block):
+    x = inputs.activations((256, 256), cfg_seed=3)          # N(0,1) with x50 outliers
+    up = Q.quantize(x, fmt, block=block, scale_round="up")
+    rne = Q.quantize(x, fmt, block=block)
+    assert rne["counters"]["elem_saturated"] > 0            # nearest scales do clip
+    assert up["counters"]["elem_saturated"] == 0            # rounded-up ones do not
+    # the scale codes are the nearest ones or one above
+    d = up["scales"].astype(int) - rne["scales"].astype(int)
+    assert set(np.unique(d)) <= {0, 1}
+
+
+def test_2d_sr_is_transposition_consistent_and_unbiased():
+    w = inputs.weights((64, 48), cfg_seed=4)
+    q = Q.quantize(w, "nvfp4", block="2d", rnd="sr", seed=9, offset=0, emit_transpose=True,
+                   scale_round="up")
+    codes = Q.unpack_codes(q["codes"])
+    assert np.array_equal(Q.unpack_codes(q["codes_t"]), codes.T)
+    # transposing W and quantizing again gives the transposed result only with
+    # the same random bits; with the bits of W^T's own layout it differs
+    qt = Q.quantize(np.ascontiguousarray(w.T), "nvfp4", block="2d", rnd="sr", seed=9, offset=0,
+                    scale_round="up")
+    assert np.array_equal(qt["scales"], q["scales"].T)
+    # unbiased over 200 draws: no element is clipped, so every element's mean
+    # code value converges to y (3 sigma on the pooled mean)
+    xf = F.bf16_bits_to_f32(w).astype(np.float64)
+    vals = []
+    for r in range(200):
+        qr = Q.quantize(w, "nvfp4", block="2d", rnd="sr", seed=9, offset=r, scale_round="up")
+        vals.append(Q.operand_values(qr["codes"], qr["scales"], "nvfp4", "2d", 64, 48)
+                    * float(qr["s_dec"]))
+    err = np.stack(vals) - xf[None]
+    scale = Q.element_scales(q["scales"], "nvfp4", "2d", 64, 48) * float(q["s_dec"])
+    z = err / scale[None]                                   # in units of the element's scale
+    assert q["counters"]["elem_saturated"] == 0
+    assert abs(z.mean()) < 3 * z.std() / np.sqrt(z.size)
