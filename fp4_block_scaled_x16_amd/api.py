@@ -40,7 +40,10 @@ class QuantDesc(ctypes.Structure):
                 ("rht", ctypes.c_int), ("rht_signs", ctypes.c_uint32), ("target", ctypes.c_float),
                 ("amax_given", ctypes.c_int), ("emit_transpose", ctypes.c_int),
                 ("scale_layout", ctypes.c_int), ("rht_n", ctypes.c_int),
-                ("rht_signs_hi", ctypes.c_uint32 * 3)]
+                ("rht_signs_hi", ctypes.c_uint32 * 3), ("scale_round", ctypes.c_int)]
+
+
+SCALE_ROUND = {"rne": 0, "up": 1}
 
 
 def _sign_words(signs):
@@ -179,10 +182,11 @@ def tiled_scale_bytes(rows, blocks_per_row):
 
 def quantize(x, fmt="nvfp4", block="1d", orient="row", rnd="rne", seed=0, offset=0, rht=False,
              signs=0, target=448.0, amax_in=None, emit_transpose=False, counters=None,
-             scale_layout="rowmajor", rht_n=16):
+             scale_layout="rowmajor", rht_n=16, scale_round="rne"):
     """Quantize a bf16 [R, C] matrix.  orient="col" quantizes X^T ([C, R]).
     scale_layout: "rowmajor" or "tiled" (1D blocks only).  rht_n: size of
     the RHT (4, 16, 32, 64, 128); signs: its sign mask, up to 128 bits.
+    scale_round: "rne" or "up" (truncation-free block scales).
 
     amax_in: None -> computed on the device; else a device fp32 [1] tensor read
     as the (possibly stale) tensor amax.  counters: optional device uint64 [5]
@@ -211,7 +215,8 @@ def quantize(x, fmt="nvfp4", block="1d", orient="row", rnd="rne", seed=0, offset
     s_lo, s_hi = _sign_words(signs)
     desc = QuantDesc(f, blk, COLWISE if col else ROWWISE, SR if rnd == "sr" else RNE,
                      int(seed), int(offset), int(bool(rht)), s_lo, float(target),
-                     int(amax_in is not None), int(bool(emit_transpose)), layout, int(rht_n), s_hi)
+                     int(amax_in is not None), int(bool(emit_transpose)), layout, int(rht_n), s_hi,
+                     SCALE_ROUND[scale_round])
     lib = load_library()
     _check(lib.fp4_quantize(ctypes.byref(desc), _ptr(x), R, C, x.stride(0), _ptr(codes),
                             _ptr(scales), _ptr(codes_t), _ptr(am), _ptr(s_dec), _ptr(counters),
@@ -227,7 +232,7 @@ def _scales_1d(rows, blocks, layout, dev):
 
 def quantize_dual(x, fmt="nvfp4", rnd="rne", seed=0, offset=0, offset_t=None, rht=False, signs=0,
                   target=448.0, amax_in=None, amax_t_in=None, counters=None,
-                  scale_layout="rowmajor", scale_layout_t=None, rht_n=16):
+                  scale_layout="rowmajor", scale_layout_t=None, rht_n=16, scale_round="rne"):
     """Rowwise and colwise 1D quantization of a bf16 [R, C] matrix from one
     read: returns (rowwise Quantized [R, C], colwise Quantized of X^T [C, R]).
 
@@ -256,10 +261,12 @@ def quantize_dual(x, fmt="nvfp4", rnd="rne", seed=0, offset=0, offset_t=None, rh
     am_t = amax_t_in if amax_t_in is not None else torch.empty(1, dtype=torch.float32, device=dev)
     r = SR if rnd == "sr" else RNE
     s_lo, s_hi = _sign_words(signs)
+    sr_mode = SCALE_ROUND[scale_round]
     d_row = QuantDesc(f, BLOCK_1D, ROWWISE, r, int(seed), int(offset), 0, 0, float(target),
-                      int(amax_in is not None), 0, lay, 16)
+                      int(amax_in is not None), 0, lay, 16, (ctypes.c_uint32 * 3)(), sr_mode)
     d_col = QuantDesc(f, BLOCK_1D, COLWISE, r, int(seed), int(offset_t), int(bool(rht)), s_lo,
-                      float(target), int(amax_t_in is not None), 0, lay_t, int(rht_n), s_hi)
+                      float(target), int(amax_t_in is not None), 0, lay_t, int(rht_n), s_hi,
+                      sr_mode)
     lib = load_library()
     _check(lib.fp4_quantize_dual(ctypes.byref(d_row), ctypes.byref(d_col), _ptr(x), R, C,
                                  x.stride(0), _ptr(codes), _ptr(scales), _ptr(codes_t),

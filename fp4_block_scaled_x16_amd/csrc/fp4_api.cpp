@@ -125,7 +125,8 @@ FP4_EXPORT fp4_status fp4_quantize(const fp4_quant_desc* d, const uint16_t* x, i
   const int bs = block_len(d->format);
   if (is2d && d->format == FP4_MXFP4) return fail(FP4_ERR_UNSUPPORTED, "2D16 blocks need NVFP4 or UE5M3");
   if (is2d && d->orient != FP4_ROWWISE) return fail(FP4_ERR_UNSUPPORTED, "2D16 blocks are ROWWISE only");
-  if (is2d && d->round != FP4_RNE) return fail(FP4_ERR_UNSUPPORTED, "2D16 blocks are RNE only");
+  if (d->scale_round != FP4_SCALE_RNE && d->scale_round != FP4_SCALE_UP)
+    return fail(FP4_ERR_ARG, "bad scale_round %d", (int)d->scale_round);
   if (d->rht && d->orient != FP4_COLWISE) return fail(FP4_ERR_UNSUPPORTED, "RHT needs COLWISE");
   if (d->rht && d->format == FP4_MXFP4) return fail(FP4_ERR_UNSUPPORTED, "RHT needs NVFP4 or UE5M3");
   st = check_rht(d, "desc");
@@ -183,6 +184,7 @@ FP4_EXPORT fp4_status fp4_quantize(const fp4_quant_desc* d, const uint16_t* x, i
   a.offset = d->offset;
   copy_signs(d, a.rht_signs);
   a.rht_n = rht_size(d);
+  a.scale_up = two_level && d->scale_round == FP4_SCALE_UP;
   a.format = d->format;
   a.round = d->round;
   a.rht = d->rht;
@@ -221,6 +223,8 @@ FP4_EXPORT fp4_status fp4_quantize_dual(const fp4_quant_desc* rd, const fp4_quan
       return fail(FP4_ERR_ARG, "%s: target must be finite and > 0", side);
     if (d->amax_given && d->format == FP4_MXFP4)
       return fail(FP4_ERR_UNSUPPORTED, "%s: MXFP4 has no tensor amax", side);
+    if (d->scale_round != FP4_SCALE_RNE && d->scale_round != FP4_SCALE_UP)
+      return fail(FP4_ERR_ARG, "%s: bad scale_round %d", side, (int)d->scale_round);
   }
   if (rd->orient != FP4_ROWWISE || cd->orient != FP4_COLWISE)
     return fail(FP4_ERR_UNSUPPORTED, "descs must be ROWWISE then COLWISE");
@@ -288,6 +292,7 @@ FP4_EXPORT fp4_status fp4_quantize_dual(const fp4_quant_desc* rd, const fp4_quan
     a[i].offset = ds[i]->offset;
     copy_signs(ds[i], a[i].rht_signs);
     a[i].rht_n = rht_size(ds[i]);
+    a[i].scale_up = ds[i]->format != FP4_MXFP4 && ds[i]->scale_round == FP4_SCALE_UP;
     a[i].format = ds[i]->format;
     a[i].round = ds[i]->round;
     a[i].rht = ds[i]->rht;

@@ -81,9 +81,12 @@ struct ScaleEvents {
 // Two-level block scale (Eqs. 2-3) -> scale code; s_enc_l receives the
 // local encode scale (0 for a zero code, reciprocal clamped to FLT_MAX).
 template <int FMT>
+// up: round the scale up instead of to nearest (truncation-free scaling,
+// 2D-block FP4 page): the nearest code, moved one code up when its value is
+// below t (the codes of both formats are ascending in value).
 __device__ __forceinline__ uint32_t block_scale_two_level(float amax_b, float s_enc_g,
                                                           float s_dec_g, float& s_enc_l,
-                                                          ScaleEvents& ev) {
+                                                          ScaleEvents& ev, bool up = false) {
   const float s_dec_l = amax_b / 6.0f;
   float t = s_dec_l * s_enc_g;
   if (!(t <= kFltMax)) t = kFltMax;
@@ -93,10 +96,12 @@ __device__ __forceinline__ uint32_t block_scale_two_level(float amax_b, float s_
     ev.sat += (t > 448.0f);
     code = scale_m3_encode<7>(t, 448.0f, 0x7Eu);
     s_hat = scale_m3_decode<7>(code);
+    if (up && code < 0x7Eu && s_hat < t) s_hat = scale_m3_decode<7>(++code);
   } else {
     ev.sat += (t > 122880.0f);
     code = scale_m3_encode<15>(t, 122880.0f, 0xFFu);
     s_hat = scale_m3_decode<15>(code);
+    if (up && code < 0xFFu && s_hat < t) s_hat = scale_m3_decode<15>(++code);
   }
   const float p = s_hat * s_dec_g;
   const float inv = fminf(1.0f / p, kFltMax);

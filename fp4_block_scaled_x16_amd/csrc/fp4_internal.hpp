@@ -24,6 +24,7 @@ struct QuantArgs {
   int rht_n;               // RHT size: 4, 16, 32, 64 or 128 (0 means 16)
   int format, round, rht, emit_transpose;
   int tiled;             // 1D scales in the TILED layout (2 KiB atoms of 256 rows x 8 blocks)
+  int scale_up;          // block scales rounded up (truncation-free), two-level formats
 };
 
 struct GemmOperand {

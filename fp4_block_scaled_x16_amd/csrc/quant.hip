@@ -124,12 +124,13 @@ __device__ __forceinline__ void encode_block(const float* v, float s_enc_l, uint
 
 template <int FMT>
 __device__ __forceinline__ uint32_t scale_for_block(float amax_b, float s_enc_g, float s_dec_g,
-                                                    float& s_enc_l, uint32_t (&cnt)[5]) {
+                                                    float& s_enc_l, uint32_t (&cnt)[5],
+                                                    bool up) {
   if constexpr (FMT == kMX) {
     return block_scale_mx(amax_b, s_enc_l);
   } else {
     ScaleEvents ev{0, 0, 0};
-    const uint32_t sc = block_scale_two_level<FMT>(amax_b, s_enc_g, s_dec_g, s_enc_l, ev);
+    const uint32_t sc = block_scale_two_level<FMT>(amax_b, s_enc_g, s_dec_g, s_enc_l, ev, up);
     cnt[0] += ev.sat;
     cnt[1] += ev.under;
     cnt[2] += ev.sub;
@@ -233,7 +234,7 @@ __global__ __launch_bounds__(kStream) void k_quant_row(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, const float* __restrict__ amax,
     float target, float* __restrict__ s_dec_out, uint64_t seed, uint64_t offset,
-    fp4_counters* __restrict__ counters, int tiled) {
+    fp4_counters* __restrict__ counters, int tiled, int scale_up) {
   constexpr int BS = FMT == kMX ? 32 : 16;
   float s_enc_g = 1.0f, s_dec_g = 1.0f;
   if constexpr (FMT != kMX) global_scales(*amax, target, s_enc_g, s_dec_g);
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(kStream) void k_quant_row(
 #pragma unroll
     for (int k = 0; k < BS; ++k) amax_b = fmaxf(amax_b, fabsf(v[k]));
     float s_enc_l;
-    const uint32_t sc = scale_for_block<FMT>(amax_b, s_enc_g, s_dec_g, s_enc_l, cnt);
+    const uint32_t sc = scale_for_block<FMT>(amax_b, s_enc_g, s_dec_g, s_enc_l, cnt, scale_up);
     uint32_t words[BS / 8];
     encode_block<BS, RND, CNT>(v, s_enc_l, r_cur * static_cast<uint64_t>(cols) + j_cur * BS, seed,
                                offset, words, cnt);
@@ -309,7 +310,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, const float* __restrict__ amax,
     float target, float* __restrict__ s_dec_out, uint64_t seed, uint64_t offset,
-    RhtN rht, fp4_counters* __restrict__ counters, int tiled, uint32_t* __restrict__ amax_out) {
+    RhtN rht, fp4_counters* __restrict__ counters, int tiled, uint32_t* __restrict__ amax_out,
+    int scale_up) {
   constexpr int BS = FMT == kMX ? 32 : 16;
   constexpr int TR = 8 * BS;        // tile rows (8 groups)
   constexpr int TC = 64;            // tile columns
@@ -370,7 +372,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
           continue;
         }
         float s_enc_l;
-        const uint32_t sc = scale_for_block<FMT>(amax_b, s_enc_g, s_dec_g, s_enc_l, cnt);
+        const uint32_t sc = scale_for_block<FMT>(amax_b, s_enc_g, s_dec_g, s_enc_l, cnt, scale_up);
         uint32_t words[BS / 8];
         encode_block<BS, RND, CNT>(v, s_enc_l, static_cast<uint64_t>(c) * rows + row, seed,
                                    offset, words, cnt);
@@ -412,7 +414,7 @@ __attribute__((amdgpu_waves_per_eu(FMT == kMX ? 1 : 3))) void k_quant_dual(
     const float* __restrict__ amax_t, float target, float target_t,
     float* __restrict__ s_dec_out, float* __restrict__ s_dec_t_out, uint64_t seed,
     uint64_t offset, uint64_t seed_t, uint64_t offset_t, RhtN rht,
-    fp4_counters* __restrict__ counters, int tiled, int tiled_t) {
+    fp4_counters* __restrict__ counters, int tiled, int tiled_t, int scale_up, int scale_up_t) {
   constexpr int BS = FMT == kMX ? 32 : 16;
   constexpr int TR = 8 * BS;        // tile rows (8 groups)
   constexpr int TC = 64;            // tile columns
@@ -487,7 +489,8 @@ __attribute__((amdgpu_waves_per_eu(FMT == kMX ? 1 : 3))) void k_quant_dual(
       float s_enc_l;
       const bool in = r < rows && c < cols;
       uint32_t sc_cnt[5] = {0, 0, 0, 0, 0};
-      const uint32_t sc = scale_for_block<FMT>(amax_b, s_enc_g, s_dec_g, s_enc_l, sc_cnt);
+      const uint32_t sc =
+          scale_for_block<FMT>(amax_b, s_enc_g, s_dec_g, s_enc_l, sc_cnt, scale_up);
       if (in) {
         cnt[0] += sc_cnt[0];
         cnt[1] += sc_cnt[1];
@@ -526,7 +529,8 @@ __attribute__((amdgpu_waves_per_eu(FMT == kMX ? 1 : 3))) void k_quant_dual(
 #pragma unroll
         for (int k = 0; k < BS; ++k) amax_b = fmaxf(amax_b, fabsf(v[k]));
         float s_enc_l;
-        const uint32_t sc = scale_for_block<FMT>(amax_b, s_enc_gt, s_dec_gt, s_enc_l, cnt);
+        const uint32_t sc =
+            scale_for_block<FMT>(amax_b, s_enc_gt, s_dec_gt, s_enc_l, cnt, scale_up_t);
         uint32_t words[BS / 8];
         encode_block<BS, RND, CNT>(v, s_enc_l, static_cast<uint64_t>(c) * rows + row, seed_t,
                                    offset_t, words, cnt);
@@ -556,12 +560,16 @@ __attribute__((amdgpu_waves_per_eu(FMT == kMX ? 1 : 3))) void k_quant_dual(
 // lanes {c, c+4, ..., c+60} of one wave, so the tile amax is four xor
 // shuffles.  Codes of W go straight out; codes of W^T go through a byte
 // transpose in LDS.
-template <int FMT, bool CNT>
+// With stochastic rounding the random bits of element (r, c) are drawn at
+// index r * cols + c, and the codes of W^T are the transposed codes of W,
+// so both orientations hold the same rounded values (the 2D-block FP4
+// page's transposition consistency, kept under SR).
+template <int FMT, int RND, bool CNT>
 __global__ __launch_bounds__(kThreads) void k_quant_2d(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, uint8_t* __restrict__ codes_t,
     const float* __restrict__ amax, float target, float* __restrict__ s_dec_out,
-    fp4_counters* __restrict__ counters) {
+    fp4_counters* __restrict__ counters, uint64_t seed, uint64_t offset, int scale_up) {
   __shared__ uint8_t tr_buf[64][64 + 4];
   float s_enc_g, s_dec_g;
   global_scales(*amax, target, s_enc_g, s_dec_g);
@@ -595,9 +603,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_2d(
     const float amax_t = __uint_as_float(amb);
     float s_enc_l;
     uint32_t tc5[5] = {0, 0, 0, 0, 0};
-    const uint32_t sc = scale_for_block<FMT>(amax_t, s_enc_g, s_dec_g, s_enc_l, tc5);
+    const uint32_t sc = scale_for_block<FMT>(amax_t, s_enc_g, s_dec_g, s_enc_l, tc5, scale_up);
     uint32_t words[2];
-    encode_block<16, FP4_RNE, CNT>(v, s_enc_l, 0, 0, 0, words, cnt);
+    encode_block<16, RND, CNT>(v, s_enc_l, static_cast<uint64_t>(row) * cols + col, seed, offset,
+                               words, cnt);
     if (valid) {
       *reinterpret_cast<uint2*>(codes + row * (cols >> 1) + (col >> 1)) =
           make_uint2(words[0], words[1]);
@@ -784,7 +793,7 @@ hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld
       const int grid = static_cast<int>(tiles < cap ? tiles : cap);
       hipLaunchKernelGGL((k_quant_col<kNV, FP4_RNE, true, false, true>), dim3(grid),
                          dim3(kThreads), 0, s, x, rows, cols, ld, nullptr, nullptr, nullptr, 0.0f,
-                         nullptr, uint64_t(0), uint64_t(0), r, nullptr, 0, out);
+                         nullptr, uint64_t(0), uint64_t(0), r, nullptr, 0, out, 0);
     } else {
       const uint64_t n = static_cast<uint64_t>(rows) * static_cast<uint64_t>(cols / 8);
       hipLaunchKernelGGL(k_amax, dim3(grid_for(n, 1)), dim3(kStream), 0, s, x, rows, cols, ld,
@@ -801,7 +810,7 @@ static void row_launch(const QuantArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((k_quant_row<FMT, RND, CNT>), dim3(grid_for(n, kRowWgPerCu)),
                      dim3(kStream), 0, s,
                      a.x, a.rows, a.cols, a.ld, a.codes, a.scales, a.amax, a.target, a.s_dec,
-                     a.seed, a.offset, a.counters, a.tiled);
+                     a.seed, a.offset, a.counters, a.tiled, a.scale_up);
 }
 
 template <int FMT, int RND>
@@ -832,7 +841,8 @@ static void col_launch(const QuantArgs& a, hipStream_t s) {
   const int grid = static_cast<int>(tiles < cap ? (tiles > 0 ? tiles : 1) : cap);
   hipLaunchKernelGGL((k_quant_col<FMT, RND, RHT, CNT>), dim3(grid), dim3(kThreads), 0, s, a.x,
                      a.rows, a.cols, a.ld, a.codes, a.scales, a.amax, a.target, a.s_dec, a.seed,
-                     a.offset, make_rht(a.rht_n, a.rht_signs), a.counters, a.tiled, nullptr);
+                     a.offset, make_rht(a.rht_n, a.rht_signs), a.counters, a.tiled, nullptr,
+                     a.scale_up);
 }
 
 template <int FMT, int RND, bool RHT>
@@ -874,7 +884,8 @@ static void dual_launch(const QuantArgs& a, const QuantArgs& b, hipStream_t s) {
   hipLaunchKernelGGL((k_quant_dual<FMT, RND, RHT, CNT>), dim3(grid), dim3(kThreads), 0, s, a.x,
                      a.rows, a.cols, a.ld, a.codes, a.scales, b.codes, b.scales, a.amax, b.amax,
                      a.target, b.target, a.s_dec, b.s_dec, a.seed, a.offset, b.seed, b.offset,
-                     make_rht(b.rht_n, b.rht_signs), a.counters, a.tiled, b.tiled);
+                     make_rht(b.rht_n, b.rht_signs), a.counters, a.tiled, b.tiled, a.scale_up,
+                     b.scale_up);
 }
 
 template <int FMT, int RND, bool RHT>
@@ -906,24 +917,30 @@ hipError_t launch_quant_dual(const QuantArgs& row, const QuantArgs& col, hipStre
   return hipGetLastError();
 }
 
-template <int FMT, bool CNT>
+template <int FMT, int RND, bool CNT>
 static void q2d_launch(const QuantArgs& a, hipStream_t s) {
   const int64_t regions = ((a.rows + 63) / 64) * ((a.cols + 63) / 64);
   const int64_t cap = static_cast<int64_t>(device_cu_count()) * kTileWgPerCu;
   const int grid = static_cast<int>(regions < cap ? (regions > 0 ? regions : 1) : cap);
-  hipLaunchKernelGGL((k_quant_2d<FMT, CNT>), dim3(grid), dim3(kThreads), 0, s, a.x, a.rows,
+  hipLaunchKernelGGL((k_quant_2d<FMT, RND, CNT>), dim3(grid), dim3(kThreads), 0, s, a.x, a.rows,
                      a.cols, a.ld, a.codes, a.scales, a.emit_transpose ? a.codes_t : nullptr,
-                     a.amax, a.target, a.s_dec, a.counters);
+                     a.amax, a.target, a.s_dec, a.counters, a.seed, a.offset, a.scale_up);
+}
+
+template <int FMT>
+static void q2d_dispatch(const QuantArgs& a, hipStream_t s) {
+  if (a.round == FP4_SR) {
+    if (a.counters) q2d_launch<FMT, FP4_SR, true>(a, s);
+    else q2d_launch<FMT, FP4_SR, false>(a, s);
+  } else {
+    if (a.counters) q2d_launch<FMT, FP4_RNE, true>(a, s);
+    else q2d_launch<FMT, FP4_RNE, false>(a, s);
+  }
 }
 
 hipError_t launch_quant_2d(const QuantArgs& a, hipStream_t s) {
-  if (a.format == FP4_NVFP4) {
-    if (a.counters) q2d_launch<kNV, true>(a, s);
-    else q2d_launch<kNV, false>(a, s);
-  } else {
-    if (a.counters) q2d_launch<kUE, true>(a, s);
-    else q2d_launch<kUE, false>(a, s);
-  }
+  if (a.format == FP4_NVFP4) q2d_dispatch<kNV>(a, s);
+  else q2d_dispatch<kUE>(a, s);
   return hipGetLastError();
 }
 

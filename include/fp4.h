@@ -50,6 +50,13 @@ typedef enum { FP4_NVFP4 = 0, FP4_UE5M3 = 1, FP4_MXFP4 = 2 } fp4_format;
 /* Element rounding: nearest-even, or stochastic (NVFP4 paper §4.4). */
 typedef enum { FP4_RNE = 0, FP4_SR = 1 } fp4_round;
 
+/* Block-scale rounding for NVFP4 / UE5M3: to nearest (NVFP4 paper App. B.2),
+ * or up -- the 2D-block FP4 page's truncation-free scaling: the block amax
+ * times the encode scale then does not exceed 6, so no element is clipped
+ * (up to fp32 rounding of the scale arithmetic).  MXFP4 scales are always
+ * rounded up (App. B.4). */
+typedef enum { FP4_SCALE_RNE = 0, FP4_SCALE_UP = 1 } fp4_scale_round;
+
 /* 1D blocks along the blocked axis, or 16x16 tiles (NVFP4 paper §4.3). */
 typedef enum { FP4_BLOCK_1D = 0, FP4_BLOCK_2D16 = 1 } fp4_block;
 
@@ -99,9 +106,10 @@ typedef struct {
 /* How to quantize (host struct). */
 typedef struct {
   fp4_format format;
-  fp4_block block;        /* 2D16: NVFP4/UE5M3, ROWWISE, RNE only               */
+  fp4_block block;        /* 2D16: NVFP4/UE5M3, ROWWISE                        */
   fp4_orient orient;
-  fp4_round round;        /* SR: 1D only                                       */
+  fp4_round round;        /* SR with 2D16: element (r, c) draws at index
+                             r * cols + c, and codes_t is the transposed codes */
   uint64_t seed;          /* SR: Philox4x32-10 key                             */
   uint64_t offset;        /* SR: Philox counter words 2-3 (e.g. a step number) */
   int rht;                /* COLWISE only: rotate every rht_n-row group of each
@@ -123,6 +131,7 @@ typedef struct {
                              rows must be a multiple of N                      */
   uint32_t rht_signs_hi[3];  /* D_r, bits 32-127 (N > 32); every bit at or
                              above N must be 0                                  */
+  fp4_scale_round scale_round;  /* NVFP4/UE5M3 block scales: RNE or UP      */
 } fp4_quant_desc;
 
 /*

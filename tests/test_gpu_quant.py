@@ -370,3 +370,48 @@ def test_dual_rht_sizes(n, rnd):
         assert f32_bits(q.s_dec.item()) == f32_bits(r["s_dec"])
     assert api.counters_dict(cnt) == {k: rr["counters"][k] + rc["counters"][k]
                                       for k in rr["counters"]}
+
+
+# ------------------------- truncation-free scales, stochastic rounding in 2D --
+@pytest.mark.parametrize("fmt", ["nvfp4", "ue5m3"])
+@pytest.mark.parametrize("orient", ["row", "col"])
+@pytest.mark.parametrize("rnd", ["rne", "sr"])
+def test_scale_round_up(fmt, orient, rnd):
+    x = inputs.activations((304, 208), cfg_seed=46)      # outliers: nearest scales clip some
+    cnt = api.new_counters()
+    q = api.quantize(dev(x), fmt, orient=orient, rnd=rnd, seed=3, offset=2, counters=cnt,
+                     scale_round="up", scale_layout="tiled")
+    torch.cuda.synchronize()
+    r = Q.quantize(x, fmt, orient=orient, rnd=rnd, seed=3, offset=2, scale_round="up")
+    assert_same(q, r, api.counters_dict(cnt))
+    assert r["counters"]["elem_saturated"] == 0
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "ue5m3"])
+@pytest.mark.parametrize("scale_round", ["rne", "up"])
+def test_2d_stochastic_rounding(fmt, scale_round):
+    """16x16 blocks with SR (2D-block FP4 page): W and W^T codes are exact
+    transposes, every output bit-exact with the oracle."""
+    w = inputs.gradients((336, 208), cfg_seed=47)         # several 64 x 64 regions + a ragged one
+    cnt = api.new_counters()
+    q = api.quantize(dev(w), fmt, block="2d", rnd="sr", seed=5, offset=7, emit_transpose=True,
+                     counters=cnt, scale_round=scale_round)
+    torch.cuda.synchronize()
+    r = Q.quantize(w, fmt, block="2d", rnd="sr", seed=5, offset=7, emit_transpose=True,
+                   scale_round=scale_round)
+    assert_same(q, r, api.counters_dict(cnt))
+
+
+def test_dual_scale_round_up():
+    x = inputs.gradients((256, 192), cfg_seed=48)
+    cnt = api.new_counters()
+    qr, qc = api.quantize_dual(dev(x), "nvfp4", rnd="sr", seed=4, offset=0, offset_t=1,
+                               counters=cnt, scale_round="up")
+    torch.cuda.synchronize()
+    rr = Q.quantize(x, "nvfp4", orient="row", rnd="sr", seed=4, offset=0, scale_round="up")
+    rc = Q.quantize(x, "nvfp4", orient="col", rnd="sr", seed=4, offset=1, scale_round="up")
+    for q, r in ((qr, rr), (qc, rc)):
+        assert np.array_equal(q.codes.cpu().numpy(), r["codes"])
+        assert np.array_equal(q.scales.cpu().numpy(), r["scales"])
+    assert api.counters_dict(cnt) == {k: rr["counters"][k] + rc["counters"][k]
+                                      for k in rr["counters"]}
