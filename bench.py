@@ -61,6 +61,10 @@ def parse():
                          "instead of the step's kernel list")
     ap.add_argument("--rht-n", type=int, default=16, choices=(4, 16, 32, 64, 128),
                     help="--layer on the 12B workload: size of the RHT")
+    ap.add_argument("--act-2d", action="store_true",
+                    help="--layer: 16x16 blocks for X and dY too (the 2D-block recipe; no RHT)")
+    ap.add_argument("--scale-up", action="store_true",
+                    help="--layer: truncation-free (rounded-up) block scales")
     ap.add_argument("--no-rht", action="store_true",
                     help="--layer on the 12B workload: leave out the RHT of the Wgrad operands")
     ap.add_argument("--serial", action="store_true",
@@ -352,9 +356,11 @@ def layer_main(args, dev):
     fmt = c["fmt"]
     t = inputs.linear_tensors(cfg)
     X, W, dY = (torch.from_numpy(t[n].view(np.int16)).to(dev) for n in ("X", "W", "dY"))
-    rht = cfg == 3 and not args.no_rht
+    rht = cfg == 3 and not args.no_rht and not args.act_2d
     r = Recipe(fmt, target_dy=2048.0 if fmt == "ue5m3" else 448.0, rht=rht, rht_n=args.rht_n,
-               rht_signs=inputs.rht_sign_bits(args.rht_n) if rht else 0)
+               rht_signs=inputs.rht_sign_bits(args.rht_n) if rht else 0,
+               act_block="2d" if args.act_2d else "1d",
+               scale_round="up" if args.scale_up else "rne")
     layer = QuantizedLinear(W, r)
 
     def step():
@@ -385,6 +391,7 @@ def layer_main(args, dev):
         "data": "synthetic (seeded PCG64, bf16 inputs resident in HBM)",
         "config": {"workload": c["name"].replace("-rht", "") + ("-rht" if rht else "") + "-layer",
                    "format": fmt, "rht": rht, "rht_n": args.rht_n if rht else None,
+                   "act_block": r.act_block, "scale_round": r.scale_round,
                    "tokens": c["tokens"], "d_in": c["d_in"], "d_out": c["d_out"],
                    "amax": "current (recomputed every step)", "wgrad": "fp32 accumulate"},
         "counters_all_runs": {k: int(v) for k, v in zip(("scale_saturated", "scale_underflow",

@@ -16,6 +16,12 @@ This class composes the library's entry points into that layer:
                 dX = Dgrad(dY, W^T)                       fp32 [tokens, in]
                 main_grad += Wgrad(dY^T, X^T)             fp32 [out, in]
 
+With act_block = "2d" (the 2D-block FP4 recipe) X and dY are quantized in
+16x16 blocks as well, each once with its transpose (dY with stochastic
+rounding, the same random bits for both orientations), so every operand a
+tensor contributes holds the same values in Fprop / Dgrad and in Wgrad;
+scale_round = "up" rounds block scales up (truncation-free scaling).
+
 Tensor amax: current scaling (recomputed every step, the NVFP4 recipe) or,
 with amax_interval = N > 1, recomputed every N-th step and reused in
 between (the periodic tensor scaling of the UE5M3 recipe).  The SR random
@@ -46,6 +52,8 @@ class Recipe:
     sr_seed: int = 1              # Philox key of the stochastic rounding of dY
     amax_interval: int = 1        # recompute each tensor amax every this many steps
     scale_layout: str = "tiled"   # storage of the 1D block scales
+    act_block: str = "1d"         # "1d" (1x16 / 1x32) or "2d" (16x16) for X and dY
+    scale_round: str = "rne"      # block scales: "rne" or "up" (truncation-free)
 
     @property
     def two_level(self):
@@ -63,6 +71,8 @@ class QuantizedLinear:
     def __init__(self, weight: torch.Tensor, recipe: Recipe = Recipe()):
         if weight.dim() != 2:
             raise ValueError("weight must be [out, in]")
+        if recipe.act_block == "2d" and (recipe.rht or not recipe.two_level):
+            raise ValueError("2D activation blocks need NVFP4 or UE5M3 and no RHT")
         self.weight = weight
         self.recipe = recipe
         self.out_features, self.in_features = weight.shape
@@ -101,45 +111,59 @@ class QuantizedLinear:
         if x.dim() != 2 or x.shape[1] != self.in_features:
             raise ValueError("x must be [tokens, in_features]")
         am, am_t = self._amax_args(x, "x", r.rht)
-        qx, qx_t = api.quantize_dual(x, r.fmt, rht=r.rht, signs=r.rht_signs, rht_n=r.rht_n,
-                                     target=r.target_x, amax_in=am, amax_t_in=am_t,
-                                     counters=self.counters, scale_layout=r.scale_layout)
-        if r.rht and am_t is None and r.two_level:
-            self.amax["x_t"] = qx_t.amax
+        if r.act_block == "2d":
+            qx2 = api.quantize(x, r.fmt, block="2d", emit_transpose=True, target=r.target_x,
+                               amax_in=am, counters=self.counters, scale_round=r.scale_round)
+            x_op, xt_op = qx2.operand(), qx2.operand(transposed=True)
+        else:
+            qx, qx_t = api.quantize_dual(x, r.fmt, rht=r.rht, signs=r.rht_signs, rht_n=r.rht_n,
+                                         target=r.target_x, amax_in=am, amax_t_in=am_t,
+                                         counters=self.counters, scale_layout=r.scale_layout,
+                                         scale_round=r.scale_round)
+            if r.rht and am_t is None and r.two_level:
+                self.amax["x_t"] = qx_t.amax
+            x_op, xt_op = qx.operand(), qx_t.operand()
         if r.two_level:
             if self._refresh():
                 api.amax(self.weight, out=self.amax["w"])
             qw = api.quantize(self.weight, r.fmt, block="2d", emit_transpose=True,
-                              target=r.target_w, amax_in=self.amax["w"], counters=self.counters)
+                              target=r.target_w, amax_in=self.amax["w"], counters=self.counters,
+                              scale_round=r.scale_round)
             w_op, wt_op = qw.operand(), qw.operand(transposed=True)
         else:
             qw, qw_t = api.quantize_dual(self.weight, r.fmt, counters=self.counters,
                                          scale_layout=r.scale_layout)
             w_op, wt_op = qw.operand(), qw_t.operand()
         tokens = x.shape[0]
-        y = api.gemm(qx.operand(), w_op, tokens, self.out_features, self.in_features,
-                     device=x.device)
-        self._saved = (qx_t, wt_op, tokens)
+        y = api.gemm(x_op, w_op, tokens, self.out_features, self.in_features, device=x.device)
+        self._saved = (xt_op, wt_op, tokens)
         return y
 
     def backward(self, dy: torch.Tensor) -> torch.Tensor:
         r = self.recipe
         if self._saved is None:
             raise RuntimeError("backward() needs a preceding forward()")
-        qx_t, wt_op, tokens = self._saved
+        xt_op, wt_op, tokens = self._saved
         if dy.dim() != 2 or tuple(dy.shape) != (tokens, self.out_features):
             raise ValueError("dy must be [tokens, out_features]")
         am, am_t = self._amax_args(dy, "dy", r.rht)
-        qdy, qdy_t = api.quantize_dual(dy, r.fmt, rnd="sr", seed=r.sr_seed, offset=2 * self.step,
-                                       offset_t=2 * self.step + 1, rht=r.rht, signs=r.rht_signs,
-                                       rht_n=r.rht_n, target=r.target_dy, amax_in=am,
-                                       amax_t_in=am_t, counters=self.counters,
-                                       scale_layout=r.scale_layout)
-        if r.rht and am_t is None and r.two_level:
-            self.amax["dy_t"] = qdy_t.amax
-        dx = api.gemm(qdy.operand(), wt_op, tokens, self.in_features, self.out_features,
-                      device=dy.device)
-        api.gemm(qdy_t.operand(), qx_t.operand(), self.out_features, self.in_features, tokens,
+        if r.act_block == "2d":
+            qdy2 = api.quantize(dy, r.fmt, block="2d", rnd="sr", seed=r.sr_seed,
+                                offset=2 * self.step, emit_transpose=True, target=r.target_dy,
+                                amax_in=am, counters=self.counters, scale_round=r.scale_round)
+            dy_op, dyt_op = qdy2.operand(), qdy2.operand(transposed=True)
+        else:
+            qdy, qdy_t = api.quantize_dual(dy, r.fmt, rnd="sr", seed=r.sr_seed,
+                                           offset=2 * self.step, offset_t=2 * self.step + 1,
+                                           rht=r.rht, signs=r.rht_signs, rht_n=r.rht_n,
+                                           target=r.target_dy, amax_in=am, amax_t_in=am_t,
+                                           counters=self.counters, scale_layout=r.scale_layout,
+                                           scale_round=r.scale_round)
+            if r.rht and am_t is None and r.two_level:
+                self.amax["dy_t"] = qdy_t.amax
+            dy_op, dyt_op = qdy.operand(), qdy_t.operand()
+        dx = api.gemm(dy_op, wt_op, tokens, self.in_features, self.out_features, device=dy.device)
+        api.gemm(dyt_op, xt_op, self.out_features, self.in_features, tokens,
                  out=self.main_grad, accumulate=True)
         self._saved = None
         self.step += 1

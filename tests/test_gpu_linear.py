@@ -7,7 +7,8 @@ steps for the accumulated gradient) of the oracle's fp64 GEMMs of its own
 quantized operands; event counters equal to the oracle's.  Cases: NVFP4
 with and without the RHT (16-point, and 64-point with the amax refreshed
 every second step), UE5M3 with the tensor amax refreshed every second step
-(steps in between reuse it on new data), MXFP4.
+(steps in between reuse it on new data), MXFP4, and the 2D-block recipe
+(16x16 blocks for X and dY too, SR on dY, rounded-up scales).
 """
 import numpy as np
 import pytest
@@ -42,13 +43,25 @@ def s_dec(q, fmt):
 def oracle_step(x, w, dy, r: Recipe, step, amax):
     """Oracle Y, dX, dW (+ abs bounds) and counters of one step, with the
     tensor amax values `amax` (dict; None entries for MXFP4)."""
-    fmt, cnt = r.fmt, []
-    qx = Q.quantize(x, fmt, orient="row", target=r.target_x, amax=amax["x"])
-    qxt = Q.quantize(x, fmt, orient="col", rht=r.rht, signs=r.rht_signs, target=r.target_x,
-                     amax=amax["x_t"], rht_n=r.rht_n)
+    fmt, cnt, sr_mode = r.fmt, [], r.scale_round
+    if r.act_block == "2d":
+        # one 16x16-block quantization per tensor; the transposed operand is
+        # the same values transposed (2D-block page)
+        q2 = Q.quantize(x, fmt, block="2d", target=r.target_x, amax=amax["x"],
+                        scale_round=sr_mode)
+        xv = vals(q2, fmt, "2d")
+        x_ops = ((xv, q2["s_dec"]), (xv.T.copy(), q2["s_dec"]))
+        cnt.append(q2["counters"])
+    else:
+        qx = Q.quantize(x, fmt, orient="row", target=r.target_x, amax=amax["x"],
+                        scale_round=sr_mode)
+        qxt = Q.quantize(x, fmt, orient="col", rht=r.rht, signs=r.rht_signs, target=r.target_x,
+                         amax=amax["x_t"], rht_n=r.rht_n, scale_round=sr_mode)
+        x_ops = ((vals(qx, fmt), s_dec(qx, fmt)), (vals(qxt, fmt), s_dec(qxt, fmt)))
+        cnt += [qx["counters"], qxt["counters"]]
     if r.two_level:
         qw = Q.quantize(w, fmt, block="2d", emit_transpose=True, target=r.target_w,
-                        amax=amax["w"])
+                        amax=amax["w"], scale_round=sr_mode)
         wv = vals(qw, fmt, "2d")
         wtv, sw, swt = wv.T.copy(), qw["s_dec"], qw["s_dec"]
         cnt.append(qw["counters"])
@@ -56,17 +69,24 @@ def oracle_step(x, w, dy, r: Recipe, step, amax):
         qw, qwt = Q.quantize(w, fmt, orient="row"), Q.quantize(w, fmt, orient="col")
         wv, wtv, sw, swt = vals(qw, fmt), vals(qwt, fmt), 1.0, 1.0
         cnt += [qw["counters"], qwt["counters"]]
-    qdy = Q.quantize(dy, fmt, orient="row", rnd="sr", seed=r.sr_seed, offset=2 * step,
-                     target=r.target_dy, amax=amax["dy"])
-    qdyt = Q.quantize(dy, fmt, orient="col", rnd="sr", seed=r.sr_seed, offset=2 * step + 1,
-                      rht=r.rht, signs=r.rht_signs, target=r.target_dy, amax=amax["dy_t"],
-                      rht_n=r.rht_n)
-    cnt += [qx["counters"], qxt["counters"], qdy["counters"], qdyt["counters"]]
+    if r.act_block == "2d":
+        q2 = Q.quantize(dy, fmt, block="2d", rnd="sr", seed=r.sr_seed, offset=2 * step,
+                        target=r.target_dy, amax=amax["dy"], scale_round=sr_mode)
+        dv = vals(q2, fmt, "2d")
+        dy_ops = ((dv, q2["s_dec"]), (dv.T.copy(), q2["s_dec"]))
+        cnt.append(q2["counters"])
+    else:
+        qdy = Q.quantize(dy, fmt, orient="row", rnd="sr", seed=r.sr_seed, offset=2 * step,
+                         target=r.target_dy, amax=amax["dy"], scale_round=sr_mode)
+        qdyt = Q.quantize(dy, fmt, orient="col", rnd="sr", seed=r.sr_seed, offset=2 * step + 1,
+                          rht=r.rht, signs=r.rht_signs, target=r.target_dy, amax=amax["dy_t"],
+                          rht_n=r.rht_n, scale_round=sr_mode)
+        dy_ops = ((vals(qdy, fmt), s_dec(qdy, fmt)), (vals(qdyt, fmt), s_dec(qdyt, fmt)))
+        cnt += [qdy["counters"], qdyt["counters"]]
     out = {}
-    for name, a, sa, b, sb in (("y", vals(qx, fmt), s_dec(qx, fmt), wv, sw),
-                               ("dx", vals(qdy, fmt), s_dec(qdy, fmt), wtv, swt),
-                               ("dw", vals(qdyt, fmt), s_dec(qdyt, fmt), vals(qxt, fmt),
-                                s_dec(qxt, fmt))):
+    for name, (a, sa), (b, sb) in (("y", x_ops[0], (wv, sw)),
+                                   ("dx", dy_ops[0], (wtv, swt)),
+                                   ("dw", dy_ops[1], x_ops[1])):
         out[name] = (G.gemm_ref(a, b, sa, sb), G.gemm_abs_bound(a, b, sa, sb))
     counters = {k: sum(c[k] for c in cnt) for k in cnt[0]}
     return out, counters
@@ -95,6 +115,10 @@ RECIPES = {
                                     amax_interval=2), 3),
     "ue5m3_periodic": (Recipe("ue5m3", target_dy=2048.0, amax_interval=2), 3),
     "mxfp4": (Recipe("mxfp4"), 1),
+    "nvfp4_2d_blocks_up": (Recipe("nvfp4", act_block="2d", scale_round="up"), 2),
+    "ue5m3_2d_blocks_periodic": (Recipe("ue5m3", target_dy=2048.0, act_block="2d",
+                                        amax_interval=2), 2),
+    "nvfp4_1d_up": (Recipe("nvfp4", scale_round="up"), 1),
 }
 
 
