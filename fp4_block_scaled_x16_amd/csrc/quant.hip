@@ -30,6 +30,7 @@ constexpr int kStream = 512;        // streaming kernels (amax, rowwise, dequant
 constexpr int kRowWgPerCu = 2;      // rowwise, RNE and SR
 constexpr int kColWgPerCuSR = 4;    // colwise with stochastic rounding
 constexpr int kTileWgPerCu = 2;     // colwise RNE, 2D
+constexpr int kAmaxWgPerCu = 1;     // tensor amax (plain and 16-point RHT)
 
 // Same-address global atomics serialize (about 12 ns each on MI355X once
 // more than a few hundred arrive), so every kernel runs a persistent grid
@@ -784,7 +785,7 @@ hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld
     const RhtN r = make_rht(rht_n, signs);
     if (rht && r.n == 16) {
       const uint64_t n = static_cast<uint64_t>(rows / 16) * static_cast<uint64_t>(cols / 2);
-      hipLaunchKernelGGL(k_amax_rht, dim3(grid_for(n, 1)), dim3(kStream), 0, s, x, rows, cols,
+      hipLaunchKernelGGL(k_amax_rht, dim3(grid_for(n, kAmaxWgPerCu)), dim3(kStream), 0, s, x, rows, cols,
                          ld, signs[0], out);
     } else if (rht) {
       // the other sizes: the colwise quantizer's staging and rotation, amax only
@@ -796,7 +797,7 @@ hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld
                          nullptr, uint64_t(0), uint64_t(0), r, nullptr, 0, out, 0);
     } else {
       const uint64_t n = static_cast<uint64_t>(rows) * static_cast<uint64_t>(cols / 8);
-      hipLaunchKernelGGL(k_amax, dim3(grid_for(n, 1)), dim3(kStream), 0, s, x, rows, cols, ld,
+      hipLaunchKernelGGL(k_amax, dim3(grid_for(n, kAmaxWgPerCu)), dim3(kStream), 0, s, x, rows, cols, ld,
                          out);
     }
   }
