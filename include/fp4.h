@@ -165,7 +165,7 @@ fp4_status fp4_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
  *   counters device fp4_counters or NULL (events not counted).
  *   Shapes: the blocked axis (cols for ROWWISE, rows for COLWISE) must be a
  *   multiple of BS; 2D16 needs rows and cols multiples of 16; RHT needs
- *   COLWISE (rows % 16 == 0 follows).
+ *   COLWISE and rows a multiple of its size N (rht_n).
  *   SR random bits: element index i in the output code matrix ([R_out,
  *   C_out], i = r * C_out + c) takes 16 bits of Philox4x32-10(key = seed,
  *   counter = (i >> 3, offset)), half (i & 1) of output word (i & 7) >> 1.

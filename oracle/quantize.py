@@ -214,9 +214,10 @@ def quantize(x_bits, fmt="nvfp4", block="1d", orient="row", rnd="rne",
     are [C, R/2] and scales [C, R/BS]; with rht=True every 16-row group of
     each column is first rotated by (1/4) D_r H16 (App. C), and the tensor
     amax is taken after the rotation (rht_n: the size N of the variant
-    transforms, groups of N rows, `signs` an N-bit mask).  block="2d": 16x16 tiles of X
-    (rowwise only, RNE only); scales [R/16, C/16]; emit_transpose also
-    returns the codes of X^T ([C, R/2]) quantized with the same tile scales.
+    transforms, groups of N rows, `signs` an N-bit mask).  block="2d":
+    16x16 tiles of X (rowwise only); scales [R/16, C/16]; emit_transpose
+    also returns the codes of X^T ([C, R/2]) quantized with the same tile
+    scales.
     amax: None to compute it, or a given (possibly stale) fp32 amax.
     index_base: output-layout index of element (0, 0), so that a slab of
     output rows of a larger matrix draws the same random bits (SR only).
