@@ -248,3 +248,21 @@ def test_operand_keeps_its_storage_alive():
     del op
     gc.collect()
     assert ref() is None
+
+
+def test_struct_layouts_match_header(tmp_path):
+    """The ctypes mirrors of the ABI structs have the C header's size and
+    field offsets (compiled with the host C compiler)."""
+    exe = tmp_path / "abi_layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"),
+                    os.path.join(ROOT, "tests", "abi_layout.c"), "-o", str(exe)], check=True)
+    c = {}
+    for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                               check=True).stdout.splitlines():
+        k, v = line.split()
+        c[k] = int(v)
+    for name, cls in (("fp4_quant_desc", api.QuantDesc), ("fp4_operand", api.Operand)):
+        assert ctypes.sizeof(cls) == c[name + ".__size__"], name
+        for field, _ in cls._fields_:
+            assert getattr(cls, field).offset == c["%s.%s" % (name, field)], (name, field)
+    assert c["fp4_counters.__size__"] == 5 * 8
