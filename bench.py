@@ -427,6 +427,62 @@ def summarize_trace(path):
         print("| %s | %d | %.1f | %.1f |" % (n, len(d), sum(d) / len(d), sum(iso) / len(iso)))
 
 
+def format_comparison(dev):
+    """MXFP4 against NVFP4 on the 8B workload's identical tensors, every
+    operand 1D in both formats (W rowwise for Fprop, colwise for Dgrad), RNE
+    for X and W, SR for dY: each format's relative Frobenius quantization
+    error ||dq(q(x)) - x||_F / ||x||_F per tensor, and its three GEMMs'
+    durations (graphs of 10 launches on the launch stream)."""
+    import torch
+    from fp4_block_scaled_x16_amd import api, inputs
+
+    c = inputs.CONFIGS[5]
+    T, din, dout = c["tokens"], c["d_in"], c["d_out"]
+    t = inputs.linear_tensors(5)
+    ten = {n: torch.from_numpy(t[n].view(np.int16)).to(dev) for n in ("X", "W", "dY")}
+    del t
+    out = {}
+    for fmt in ("mxfp4", "nvfp4"):
+        qx, qxc = api.quantize_dual(ten["X"], fmt, scale_layout="tiled")
+        qw, qwc = api.quantize_dual(ten["W"], fmt, scale_layout="tiled")
+        qdy, qdyc = api.quantize_dual(ten["dY"], fmt, rnd="sr", seed=1, offset=0, offset_t=1,
+                                      scale_layout="tiled")
+        err = {}
+        for name, q in (("X", qx), ("W", qw), ("dY", qdy)):
+            xf = ten[name].view(torch.bfloat16).double()
+            dq = api.dequantize(q).double()
+            err[name] = float(torch.linalg.vector_norm(dq - xf) / torch.linalg.vector_norm(xf))
+            del xf, dq
+        gemms = {"fprop": (qx, qw, T, dout, din), "dgrad": (qdy, qwc, T, din, dout),
+                 "wgrad": (qdyc, qxc, dout, din, T)}
+        ms, tf = {}, {}
+        for name, (qa, qb, M, N, K) in gemms.items():
+            a, b = qa.operand(), qb.operand()
+            D = torch.empty((M, N), dtype=torch.float32, device=dev)
+            api.gemm(a, b, M, N, K, out=D)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(10):
+                    api.gemm(a, b, M, N, K, out=D)
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(3):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ms[name] = round(e0.elapsed_time(e1) / 30, 4)
+            tf[name] = round(2.0 * M * N * K / (ms[name] * 1e-3) / 1e12, 1)
+            del g, D
+        peak = PEAK_TFLOPS["fp4" if fmt == "mxfp4" else "fp16"]
+        out[fmt] = {"frobenius_rel_error": {k: round(v, 6) for k, v in err.items()},
+                    "gemm_ms": ms, "gemm_TFLOPs": tf,
+                    "gemm_frac_peak": {k: round(v / peak, 4) for k, v in tf.items()}}
+        del qx, qxc, qw, qwc, qdy, qdyc
+    return out
+
+
 def main():
     args = parse()
     if args.summarize_trace:
@@ -607,6 +663,8 @@ def main():
         "counters": counters,
         "wall_s_timed": round(wall, 3),
     }
+    if cfg == 5:
+        out["format_comparison"] = format_comparison(dev)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(cfg, host, fmt, args.cpu_tokens)
     print(json.dumps(out))

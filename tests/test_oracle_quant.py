@@ -414,3 +414,23 @@ def test_2d_sr_is_transposition_consistent_and_unbiased():
     z = err / scale[None]                                   # in units of the element's scale
     assert q["counters"]["elem_saturated"] == 0
     assert abs(z.mean()) < 3 * z.std() / np.sqrt(z.size)
+
+
+def test_format_error_ordering():
+    """NVFP4 paper §3 (App. B.4 worked example): 16-element blocks with
+    E4M3 scales represent values more accurately than 32-element blocks
+    with power-of-two scales.  On rows drawn like the format-comparison
+    workload's X, W and dY (1D blocks, SR on dY), NVFP4's relative
+    Frobenius quantization error is below MXFP4's for every tensor."""
+    shapes = {"X": (128, 4096), "W": (128, 4096), "dY": (64, 21504)}
+    gens = {"X": inputs.activations, "W": inputs.weights, "dY": inputs.gradients}
+    for name, shape in shapes.items():
+        x = gens[name](shape, cfg_seed=0)
+        xf = F.bf16_bits_to_f32(x).astype(np.float64)
+        kw = dict(rnd="sr", seed=1) if name == "dY" else {}
+        err = {}
+        for fmt in ("nvfp4", "mxfp4"):
+            q = Q.quantize(x, fmt, **kw)
+            dq = Q.dequantize(q["codes"], q["scales"], fmt, "1d", q["s_dec"], *shape)
+            err[fmt] = np.linalg.norm(dq.astype(np.float64) - xf) / np.linalg.norm(xf)
+        assert err["nvfp4"] < err["mxfp4"], (name, err)
