@@ -14,7 +14,8 @@ pages it follows:
 * The UE5M3 block-scale FP4 pretraining abstract (arXiv 2609.02846):
   unsigned E5M3 block scales, target T, periodic (stale) tensor amax.
 * The 2D-block FP4 training abstract (arXiv 2607.24953): transposition-
-  invariant scaling.
+  invariant scaling, truncation-free scaling, stochastic rounding on 2D
+  blocks.
 
 Floating-point decisions that pick an integer code are taken in fp32, the
 precision the NVFP4 paper fixes for the tensor scale (App. B.1) and that its
@@ -22,9 +23,10 @@ precision the NVFP4 paper fixes for the tensor scale (App. B.1) and that its
 sums are taken in fp64.
 
 Modules:
-  formats  - E2M1 / E4M3 / UE5M3 / UE8M0 tables and round-to-nearest-even
+  formats  - E2M1 / E4M3 / UE5M3 / UE8M0 tables; round-to-nearest-even and
+             rounded-up scale encoders
   philox   - Philox4x32-10 counter-based generator (Salmon et al., SC'11)
-  rht      - 16-point randomized Hadamard transform
+  rht      - randomized Hadamard transform, 16-point and N = 4 ... 128
   quantize - tensor amax, two-level scales, 1D/2D/colwise quantize,
              stochastic rounding, counters, dequantize
   gemm     - block-scaled GEMM reference in fp64 and its error bound
