@@ -261,12 +261,21 @@ FP4_EXPORT fp4_status fp4_quantize_dual(const fp4_quant_desc* rd, const fp4_quan
   }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (two_level && !rd->amax_given) {
+  // both amaxes wanted with the 16-point RHT on the colwise side: one read
+  const bool fused = two_level && !rd->amax_given && !cd->amax_given && cd->rht &&
+                     rht_size(cd) == 16 && amax != amax_t;
+  if (fused) {
+    uint32_t s4[4];
+    copy_signs(cd, s4);
+    hipError_t e = fp4lib::launch_amax(x, rows, cols, ld, 1, 16, s4, amax_t, s, amax);
+    if (e != hipSuccess) return device_status(e, "fp4_quantize_dual amax launch");
+  }
+  if (two_level && !rd->amax_given && !fused) {
     const uint32_t none[4] = {0u, 0u, 0u, 0u};
     hipError_t e = fp4lib::launch_amax(x, rows, cols, ld, 0, 16, none, amax, s);
     if (e != hipSuccess) return device_status(e, "fp4_quantize_dual amax launch");
   }
-  if (two_level && !cd->amax_given && !(amax_t == amax && !rd->amax_given)) {
+  if (two_level && !cd->amax_given && !fused && !(amax_t == amax && !rd->amax_given)) {
     uint32_t s4[4];
     copy_signs(cd, s4);
     hipError_t e = fp4lib::launch_amax(x, rows, cols, ld, cd->rht, rht_size(cd), s4, amax_t, s);

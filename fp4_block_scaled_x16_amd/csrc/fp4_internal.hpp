@@ -40,8 +40,10 @@ struct GemmOperand {
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 
+// amax_plain (optional, rht with N = 16 only): also max |x| from the same read.
 hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int rht,
-                       int rht_n, const uint32_t (&signs)[4], float* amax, hipStream_t s);
+                       int rht_n, const uint32_t (&signs)[4], float* amax, hipStream_t s,
+                       float* amax_plain = nullptr);
 hipError_t launch_quant_row(const QuantArgs& a, hipStream_t s);
 hipError_t launch_quant_col(const QuantArgs& a, hipStream_t s);
 hipError_t launch_quant_2d(const QuantArgs& a, hipStream_t s);

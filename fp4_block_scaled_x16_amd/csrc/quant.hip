@@ -158,6 +158,33 @@ __device__ __forceinline__ void flush_max(uint32_t m, uint32_t* out) {
   }
 }
 
+// Two maxima at once (one barrier): a -> *out_a, and b -> *out_b if out_b.
+template <int NT>
+__device__ __forceinline__ void flush_max2(uint32_t a, uint32_t b, uint32_t* out_a,
+                                           uint32_t* out_b) {
+  __shared__ uint32_t red[NT / 64][2];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    a = max(a, static_cast<uint32_t>(__shfl_xor(a, o, 64)));
+    b = max(b, static_cast<uint32_t>(__shfl_xor(b, o, 64)));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    red[threadIdx.x >> 6][0] = a;
+    red[threadIdx.x >> 6][1] = b;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) {
+      a = max(a, red[w][0]);
+      b = max(b, red[w][1]);
+    }
+    if (a > __hip_atomic_load(out_a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(out_a, a);
+    if (out_b && b > __hip_atomic_load(out_b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+      atomicMax(out_b, b);
+  }
+}
+
 // max |x| over a [rows, cols] bf16 matrix, cols % 8 == 0.  |x| as fp32 bits
 // is monotone in the value, so an unsigned atomic max is exact.
 __global__ __launch_bounds__(kStream) void k_amax(const uint16_t* __restrict__ x, int64_t rows,
@@ -200,15 +227,18 @@ __global__ __launch_bounds__(kStream) void k_amax(const uint16_t* __restrict__ x
   flush_max<kStream>(m, out);
 }
 
-// max |(1/4) D_r H16 v| over every 16-row group v of every column.
-// One thread per (column pair, group); rows % 16 == 0, cols % 8 == 0.
+// max |(1/4) D_r H16 v| over every 16-row group v of every column, and (if
+// out_plain) max |x| over the same values before the rotation, from the
+// same read.  One thread per (column pair, group); rows % 16 == 0,
+// cols % 8 == 0.
 __global__ __launch_bounds__(kStream) void k_amax_rht(const uint16_t* __restrict__ x,
                                                       int64_t rows, int64_t cols, int64_t ld,
-                                                      uint32_t signs, uint32_t* __restrict__ out) {
+                                                      uint32_t signs, uint32_t* __restrict__ out,
+                                                      uint32_t* __restrict__ out_plain) {
   const uint64_t pairs = static_cast<uint64_t>(cols) >> 1;
   const uint64_t n = (static_cast<uint64_t>(rows) >> 4) * pairs;
   const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kStream;
-  float m = 0.0f;
+  float m = 0.0f, mp = 0.0f;
   for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kStream + threadIdx.x; i < n;
        i += stride) {
     const uint64_t g = i / pairs, p = i - g * pairs;
@@ -219,13 +249,14 @@ __global__ __launch_bounds__(kStream) void k_amax_rht(const uint16_t* __restrict
       const uint32_t w = *reinterpret_cast<const uint32_t*>(src + k * ld);
       a[k] = bf16_to_f32(w & 0xFFFFu);
       b[k] = bf16_to_f32(w >> 16);
+      mp = fmaxf(mp, fmaxf(fabsf(a[k]), fabsf(b[k])));
     }
     rht16(a, signs);
     rht16(b, signs);
 #pragma unroll
     for (int k = 0; k < 16; ++k) m = fmaxf(m, fmaxf(fabsf(a[k]), fabsf(b[k])));
   }
-  flush_max<kStream>(__float_as_uint(m), out);
+  flush_max2<kStream>(__float_as_uint(m), __float_as_uint(mp), out, out_plain);
 }
 
 // ------------------------------------------------------ rowwise 1D ------
@@ -778,15 +809,18 @@ static RhtN make_rht(int n, const uint32_t (&s4)[4]) {
 }
 
 hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int rht,
-                       int rht_n, const uint32_t (&signs)[4], float* amax, hipStream_t s) {
+                       int rht_n, const uint32_t (&signs)[4], float* amax, hipStream_t s,
+                       float* amax_plain) {
   uint32_t* out = reinterpret_cast<uint32_t*>(amax);
+  uint32_t* out_plain = reinterpret_cast<uint32_t*>(amax_plain);
   hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(1), 0, s, out, 0u);
+  if (out_plain) hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(1), 0, s, out_plain, 0u);
   if (rows > 0 && cols > 0) {
     const RhtN r = make_rht(rht_n, signs);
     if (rht && r.n == 16) {
       const uint64_t n = static_cast<uint64_t>(rows / 16) * static_cast<uint64_t>(cols / 2);
       hipLaunchKernelGGL(k_amax_rht, dim3(grid_for(n, kAmaxWgPerCu)), dim3(kStream), 0, s, x, rows, cols,
-                         ld, signs[0], out);
+                         ld, signs[0], out, out_plain);
     } else if (rht) {
       // the other sizes: the colwise quantizer's staging and rotation, amax only
       const int64_t tiles = ((rows + 127) / 128) * ((cols + 63) / 64);

@@ -92,19 +92,21 @@ class QuantizedLinear:
     def _amax_args(self, x, name, rht):
         """amax buffers (rowwise, colwise) for a dual quantization of x,
         refreshed on this step if due; without RHT both sides share one
-        buffer.  MXFP4 has none.  With an RHT of size other than 16 the
-        colwise amax is left to the quantizer (None: computed in the rotated
-        space) and kept from its result."""
+        buffer.  MXFP4 has none.  With the RHT a refresh leaves both to the
+        quantizer (None, None: the plain and the rotated amax, from one read
+        for N = 16), and `_keep_amax` keeps what it computed."""
         r = self.recipe
         if not r.two_level:
             return None, None
         if self._refresh():
+            if rht:
+                return None, None
             api.amax(x, out=self.amax[name])
-            if rht and r.rht_n == 16:
-                api.amax(x, rht=True, signs=r.rht_signs, out=self.amax[name + "_t"])
-            elif rht:
-                return self.amax[name], None
         return self.amax[name], self.amax[name + "_t" if rht else name]
+
+    def _keep_amax(self, name, q, q_t, given):
+        if self.recipe.two_level and given is None:
+            self.amax[name], self.amax[name + "_t"] = q.amax, q_t.amax
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         r = self.recipe
@@ -120,8 +122,7 @@ class QuantizedLinear:
                                          target=r.target_x, amax_in=am, amax_t_in=am_t,
                                          counters=self.counters, scale_layout=r.scale_layout,
                                          scale_round=r.scale_round)
-            if r.rht and am_t is None and r.two_level:
-                self.amax["x_t"] = qx_t.amax
+            self._keep_amax("x", qx, qx_t, am)
             x_op, xt_op = qx.operand(), qx_t.operand()
         if r.two_level:
             if self._refresh():
@@ -159,8 +160,7 @@ class QuantizedLinear:
                                            target=r.target_dy, amax_in=am, amax_t_in=am_t,
                                            counters=self.counters, scale_layout=r.scale_layout,
                                            scale_round=r.scale_round)
-            if r.rht and am_t is None and r.two_level:
-                self.amax["dy_t"] = qdy_t.amax
+            self._keep_amax("dy", qdy, qdy_t, am)
             dy_op, dyt_op = qdy.operand(), qdy_t.operand()
         dx = api.gemm(dy_op, wt_op, tokens, self.in_features, self.out_features, device=dy.device)
         api.gemm(dyt_op, xt_op, self.out_features, self.in_features, tokens,
