@@ -187,7 +187,9 @@ fp4_status fp4_quantize(const fp4_quant_desc* desc /* host */,
  *
  *   row_desc  ROWWISE, 1D, no RHT.      col_desc  COLWISE, 1D.
  *   Both: the same format and the same rounding mode (seed, offset, target,
- *   amax_given and scale_layout are per side).
+ *   amax_given, scale_layout and scale_round are per side; the RHT fields
+ *   apply to the colwise side).  When both amaxes are computed here with a
+ *   16-point RHT, one read of x yields the plain and the rotated amax.
  *   x [rows, cols] bf16 (ld), device; rows and cols multiples of BS.
  *   codes, scales     rowwise outputs, as fp4_quantize with row_desc.
  *   codes_t, scales_t colwise outputs, as fp4_quantize with col_desc.
