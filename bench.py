@@ -216,13 +216,17 @@ def build_step(cfg, dev, dual=True):
 
     ops = []
     two_level = fmt != "mxfp4"
+    # With the RHT and dual quantization, X's and dY's plain and rotated
+    # amax come from one read inside the dual quantizer (no separate ops).
+    fused_amax = rht and dual
     if two_level:
-        ops += [("amax X", "hbm", B_AMAX * X.numel(), amax_op("X", X)),
-                ("amax W", "hbm", B_AMAX * W.numel(), amax_op("W", W)),
-                ("amax dY", "hbm", B_AMAX * dY.numel(), amax_op("dY", dY))]
+        ops += [("amax W", "hbm", B_AMAX * W.numel(), amax_op("W", W))]
+        if not fused_amax:
+            ops += [("amax X", "hbm", B_AMAX * X.numel(), amax_op("X", X)),
+                    ("amax dY", "hbm", B_AMAX * dY.numel(), amax_op("dY", dY))]
         if fmt == "ue5m3":     # stale amax given: nothing to compute
             ops = [(n, k, 0.0, f) for (n, k, _, f) in ops]
-        if rht:
+        if rht and not fused_amax:
             ops += [("amax rot X", "hbm", B_AMAX * X.numel(), amax_rot_op("X", X)),
                     ("amax rot dY", "hbm", B_AMAX * dY.numel(), amax_rot_op("dY", dY))]
     b1 = B_Q1D[fmt]
@@ -243,13 +247,13 @@ def build_step(cfg, dev, dual=True):
         """Rowwise and colwise codes of x from one read (RHT on the colwise side)."""
         def f():
             kw2 = dict(kw, scale_layout="tiled")
-            if two_level:
+            if two_level and not fused_amax:
                 kw2["amax_in"] = st["amax_" + name]
                 kw2["amax_t_in"] = st[("amax_rot_" if kw.get("rht") else "amax_") + name]
             st[out_r], st[out_c] = api.quantize_dual(x, fmt, counters=cnt, **kw2)
         return f
 
-    bd = B_DUAL[fmt]
+    bd = B_DUAL[fmt] + (B_AMAX if fused_amax else 0.0)   # + the amax read when fused
     if dual:
         ops.append(("quant X row+col", "hbm", bd * X.numel(),
                     qd("X", X, "qx", "qxc", rht=rht, signs=sig if rht else 0, target=target_x)))
