@@ -84,8 +84,10 @@ def load_library(path=LIB_PATH):
     lib.fp4_rht16.argtypes = [vp, i64, i64, i64, u32, vp, vp]
     lib.fp4_gemm.argtypes = [ctypes.POINTER(Operand), ctypes.POINTER(Operand), i64, i64, i64, vp,
                              i64, i32, vp]
+    lib.fp4_selftest_sweep.argtypes = [i32, vp, i32, vp, vp]
+    lib.fp4_selftest_gemm_decode.argtypes = [i32, vp, vp]
     for f in ("fp4_amax", "fp4_quantize", "fp4_quantize_dual", "fp4_dequantize", "fp4_rht16",
-              "fp4_gemm"):
+              "fp4_gemm", "fp4_selftest_sweep", "fp4_selftest_gemm_decode"):
         getattr(lib, f).restype = ctypes.c_int
     lib.fp4_status_string.argtypes = [ctypes.c_int]
     lib.fp4_status_string.restype = ctypes.c_char_p
@@ -314,3 +316,33 @@ def gemm(a: Operand, b: Operand, M, N, K, out=None, accumulate=False, device=Non
     _check(lib.fp4_gemm(ctypes.byref(a), ctypes.byref(b), M, N, K, _ptr(out), out.stride(0),
                         int(bool(accumulate)), _stream(out.device)), "fp4_gemm")
     return out
+
+
+# ------------------------------------------------------------- self-test --
+SWEEPS = {"e2m1_rne": 0, "e4m3_scale": 1, "ue5m3_scale": 2}
+
+
+def selftest_sweep(kind, thresholds, device="cuda"):
+    """Run one of the library's conversions over its whole input domain
+    against the step function `thresholds` (ascending fp32 bit patterns,
+    uint32): returns (mismatches, smallest mismatching pattern or None,
+    inputs checked)."""
+    if len(thresholds) and int(max(thresholds)) >= 2 ** 31:
+        raise ValueError("thresholds are magnitudes: patterns below 2^31")
+    thr = torch.tensor([int(t) for t in thresholds], dtype=torch.int32).to(device)
+    res = torch.empty(3, dtype=torch.int64, device=device)
+    lib = load_library()
+    _check(lib.fp4_selftest_sweep(SWEEPS[kind], _ptr(thr), thr.numel(), _ptr(res),
+                                  _stream(res.device)), "fp4_selftest_sweep")
+    bad, first, checked = (int(v) & (2 ** 64 - 1) for v in res.cpu().tolist())
+    return bad, (None if bad == 0 else first), checked
+
+
+def selftest_gemm_decode(fmt, device="cuda"):
+    """The GEMM's operand decode of every (scale code, E2M1 code) pair:
+    uint16 fp16 patterns [256, 2, 16] (see fp4_selftest_gemm_decode)."""
+    out = torch.empty((256, 2, 16), dtype=torch.int16, device=device)
+    lib = load_library()
+    _check(lib.fp4_selftest_gemm_decode(_fmt(fmt), _ptr(out), _stream(out.device)),
+           "fp4_selftest_gemm_decode")
+    return out.cpu().numpy().view("uint16")

@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 SOURCES = ["quant.hip", "gemm.hip", "gemm_nv.hip", "gemm_nv_dma256.hip",
            "gemm_nv_dma192.hip", "gemm_mx.hip",
-           "gemm_mx_dma.hip", "fp4_api.cpp"]
+           "gemm_mx_dma.hip", "selftest.hip", "fp4_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-x", "hip", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-fvisibility=hidden", "-ffp-contract=off",

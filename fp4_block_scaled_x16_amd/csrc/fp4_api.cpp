@@ -9,6 +9,7 @@
 #include <string>
 
 #include "../../include/fp4.h"
+#include "../../include/fp4_selftest.h"
 #include "fp4_internal.hpp"
 
 #define FP4_EXPORT extern "C" __attribute__((visibility("default")))
@@ -397,4 +398,27 @@ FP4_EXPORT fp4_status fp4_gemm(const fp4_operand* A, const fp4_operand* B, int64
   return device_status(fp4lib::launch_gemm(A->format, a, b, M, N, K, D, ldd, accumulate,
                                            static_cast<hipStream_t>(stream)),
                        "fp4_gemm launch");
+}
+
+FP4_EXPORT fp4_status fp4_selftest_sweep(int kind, const uint32_t* thresholds, int n,
+                                         uint64_t* result, void* stream) {
+  static const int kLen[3] = {7, 126, 255};
+  if (kind < FP4_SWEEP_E2M1_RNE || kind > FP4_SWEEP_UE5M3_SCALE)
+    return fail(FP4_ERR_ARG, "bad sweep kind %d", kind);
+  if (n != kLen[kind])
+    return fail(FP4_ERR_ARG, "sweep kind %d needs %d thresholds (got %d)", kind, kLen[kind], n);
+  if (!thresholds || !result) return fail(FP4_ERR_ARG, "thresholds/result is null");
+  if (reinterpret_cast<uintptr_t>(result) & 7u) return fail(FP4_ERR_ARG, "result must be 8-byte aligned");
+  return device_status(fp4lib::launch_selftest_sweep(kind, thresholds, n, result,
+                                                     static_cast<hipStream_t>(stream)),
+                       "fp4_selftest_sweep launch");
+}
+
+FP4_EXPORT fp4_status fp4_selftest_gemm_decode(fp4_format format, uint16_t* out, void* stream) {
+  if (format != FP4_NVFP4 && format != FP4_UE5M3)
+    return fail(FP4_ERR_ARG, "gemm decode needs NVFP4 or UE5M3 (format %d)", (int)format);
+  if (!out || (reinterpret_cast<uintptr_t>(out) & 1u)) return fail(FP4_ERR_ARG, "out is null or misaligned");
+  return device_status(fp4lib::launch_selftest_gemm_decode(format, out,
+                                                           static_cast<hipStream_t>(stream)),
+                       "fp4_selftest_gemm_decode launch");
 }

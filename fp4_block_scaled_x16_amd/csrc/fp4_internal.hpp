@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "../../include/fp4.h"
+#include "../../include/fp4_selftest.h"
 
 namespace fp4lib {
 
@@ -57,5 +58,9 @@ hipError_t launch_rht16(const uint16_t* x, int64_t rows, int64_t cols, int64_t l
                         float* y, hipStream_t s);
 hipError_t launch_gemm(int format, const GemmOperand& A, const GemmOperand& B, int64_t M, int64_t N,
                        int64_t K, float* D, int64_t ldd, int accumulate, hipStream_t s);
+// Exhaustive conversion checks (selftest.hip).
+hipError_t launch_selftest_sweep(int kind, const uint32_t* thresholds, int n, uint64_t* result,
+                                 hipStream_t s);
+hipError_t launch_selftest_gemm_decode(int format, uint16_t* out, hipStream_t s);
 
 }  // namespace fp4lib

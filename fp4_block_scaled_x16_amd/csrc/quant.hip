@@ -238,7 +238,8 @@ __global__ __launch_bounds__(kStream) void k_amax_rht(const uint16_t* __restrict
   const uint64_t pairs = static_cast<uint64_t>(cols) >> 1;
   const uint64_t n = (static_cast<uint64_t>(rows) >> 4) * pairs;
   const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kStream;
-  float m = 0.0f, mp = 0.0f;
+  float m = 0.0f;
+  uint32_t mp = 0;   // largest |x| as bf16 magnitude bits, as k_amax takes it
   for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kStream + threadIdx.x; i < n;
        i += stride) {
     const uint64_t g = i / pairs, p = i - g * pairs;
@@ -249,14 +250,15 @@ __global__ __launch_bounds__(kStream) void k_amax_rht(const uint16_t* __restrict
       const uint32_t w = *reinterpret_cast<const uint32_t*>(src + k * ld);
       a[k] = bf16_to_f32(w & 0xFFFFu);
       b[k] = bf16_to_f32(w >> 16);
-      mp = fmaxf(mp, fmaxf(fabsf(a[k]), fabsf(b[k])));
+      const uint32_t mag = w & 0x7FFF7FFFu;
+      mp = max(mp, max(mag & 0xFFFFu, mag >> 16));
     }
     rht16(a, signs);
     rht16(b, signs);
 #pragma unroll
     for (int k = 0; k < 16; ++k) m = fmaxf(m, fmaxf(fabsf(a[k]), fabsf(b[k])));
   }
-  flush_max2<kStream>(__float_as_uint(m), __float_as_uint(mp), out, out_plain);
+  flush_max2<kStream>(__float_as_uint(m), mp << 16, out, out_plain);
 }
 
 // ------------------------------------------------------ rowwise 1D ------

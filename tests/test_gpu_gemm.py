@@ -291,11 +291,50 @@ GEMMS = {
     "wgrad": ("dY", "col", "X", "col"),
 }
 
+_W2D = {}
+
+
+def _oracle_w2d(cfg, bits, fmt, amax, target):
+    """The oracle's 16x16 quantization of a workload's whole W (cached: the
+    Fprop and Dgrad cases of both scale layouts read it)."""
+    if cfg not in _W2D:
+        _W2D.clear()
+        _W2D[cfg] = Q.quantize(bits, fmt, block="2d", emit_transpose=True, amax=amax,
+                               target=target)
+    return _W2D[cfg]
+
+
+def _oracle_w_rows(q, fmt, layout, sel, R, C):
+    """Operand values of rows `sel` of W [R, C] (layout "2d") or of W^T
+    (layout "2dT") from the oracle's whole-tensor 2D quantization `q`."""
+    out = []
+    for r in sel:
+        g = r // 16 * 16
+        if layout == "2d":
+            v = Q.operand_values(q["codes"][g:g + 16], q["scales"][g // 16:g // 16 + 1], fmt,
+                                 "2d", 16, C)
+        else:   # W^T rows g..g+15 are W's columns; their tile scales are a column of W's
+            v = Q.operand_values(q["codes_t"][g:g + 16], q["scales"][:, g // 16:g // 16 + 1].T,
+                                 fmt, "2d", 16, R)
+        out.append(v[r - g])
+    return np.stack(out)
+
+
+def _one_per_32(n, rng):
+    """One index in every group of 32 (every 32 x 32 output sub-tile is
+    sampled once rows and columns both come from this), plus both ends."""
+    idx = np.arange(0, n, 32) + rng.integers(0, 32, (n + 31) // 32)
+    return np.unique(np.concatenate([[0, n - 1], np.minimum(idx, n - 1)]))
+
 
 @pytest.mark.parametrize("scales", ["rowmajor", "tiled"])
 @pytest.mark.parametrize("cfg", [2, 3, 4, 5])
 @pytest.mark.parametrize("gemm", ["fprop", "dgrad", "wgrad"])
 def test_workload_gemm(cfg, gemm, scales):
+    """A full-size GEMM of a workload, in the launch configuration the
+    benchmark uses: D starts as NaN and must be finite everywhere afterwards
+    (every output tile written), and one entry in every 32 x 32 sub-tile is
+    checked against the oracle."""
     an, la, bn, lb = GEMMS[gemm]
     fmt = {2: "nvfp4", 3: "nvfp4", 4: "ue5m3", 5: "mxfp4"}[cfg]
     if fmt == "mxfp4":   # MXFP4 weights are 1D: rowwise for Fprop, colwise for Dgrad
@@ -318,16 +357,21 @@ def test_workload_gemm(cfg, gemm, scales):
     qa, qb = gq(a_bits, la, kwa, sa_stale), gq(b_bits, lb, kwb, sb_stale)
     M, K = qa.rows, qa.cols
     N = qb.cols if lb == "2dT" else qb.rows
-    d = api.gemm(gpu_operand(qa, la), gpu_operand(qb, lb), M, N, K, device=DEV)
+    d = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+    api.gemm(gpu_operand(qa, la), gpu_operand(qb, lb), M, N, K, out=d)
     torch.cuda.synchronize()
+    del qa, qb
+    assert bool(torch.isfinite(d).all()), "output entries left unwritten"
     rng = np.random.default_rng(100 + cfg)
-    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 10)]))
-    cols = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 10)]))
+    rows, cols = _one_per_32(M, rng), _one_per_32(N, rng)
     amax_a = _amax_for(a_bits, fmt, kwa, sa_stale)
     amax_b = _amax_for(b_bits, fmt, kwb, sb_stale)
-    kwb2 = {k: v for k, v in kwb.items() if k == "target"} if lb in ("2d", "2dT") else kwb
     av = _oracle_rows(a_bits, fmt, la, rows, kwa, amax_a)
-    bv = _oracle_rows(b_bits, fmt, lb, cols, kwb2, amax_b)
+    if lb in ("2d", "2dT"):
+        qw = _oracle_w2d(cfg, b_bits, fmt, amax_b, kwb.get("target", 448.0))
+        bv = _oracle_w_rows(qw, fmt, lb, cols, *b_bits.shape)
+    else:
+        bv = _oracle_rows(b_bits, fmt, lb, cols, kwb, amax_b)
     if fmt == "mxfp4":
         sa = sb = 1.0
     else:

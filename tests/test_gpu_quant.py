@@ -415,3 +415,44 @@ def test_dual_scale_round_up():
         assert np.array_equal(q.scales.cpu().numpy(), r["scales"])
     assert api.counters_dict(cnt) == {k: rr["counters"][k] + rc["counters"][k]
                                       for k in rr["counters"]}
+
+
+# -------------------------------------- whole tensors at full size ----
+@pytest.mark.parametrize("cfg,name", [(2, "dY"), (4, "X"), (5, "X")])
+def test_workload_whole_tensor(cfg, name):
+    """One full-size rowwise quantization per format, compared whole: every
+    code, every scale and the five event counters (NVFP4: the 1.2B dY with
+    stochastic rounding; UE5M3: the 8B X with its stale amax; MXFP4: the 8B
+    X), in the TILED scale layout the GEMMs read."""
+    fmt = FMT[cfg]
+    xb = inputs.linear_tensors(cfg, which=(name,))[name]
+    rnd = "sr" if name == "dY" else "rne"
+    amax = _stale_amax(name, xb.shape) if fmt == "ue5m3" else None
+    amax_dev = None if amax is None else torch.tensor([amax], dtype=torch.float32, device=DEV)
+    cnt = api.new_counters()
+    q = api.quantize(dev(xb), fmt, rnd=rnd, seed=1, offset=0, amax_in=amax_dev, counters=cnt,
+                     scale_layout="tiled")
+    torch.cuda.synchronize()
+    r = Q.quantize(xb, fmt, rnd=rnd, seed=1, offset=0, amax=amax)
+    assert np.array_equal(q.codes.cpu().numpy(), r["codes"])
+    assert np.array_equal(gpu_scales(q), r["scales"])
+    assert api.counters_dict(cnt) == r["counters"]
+    if fmt != "mxfp4":
+        assert f32_bits(q.s_dec.item()) == f32_bits(r["s_dec"])
+
+
+def test_workload_dual_whole_tensor():
+    """The dual quantizer on the whole 1.2B X (both code matrices, scales and
+    the summed counters), as the benchmark step runs it."""
+    xb = inputs.linear_tensors(2, which=("X",))["X"]
+    cnt = api.new_counters()
+    qr, qc = api.quantize_dual(dev(xb), "nvfp4", counters=cnt, scale_layout="tiled")
+    torch.cuda.synchronize()
+    rr = Q.quantize(xb, "nvfp4", orient="row")
+    rc = Q.quantize(xb, "nvfp4", orient="col")
+    for q, r in ((qr, rr), (qc, rc)):
+        assert np.array_equal(q.codes.cpu().numpy(), r["codes"])
+        assert np.array_equal(gpu_scales(q), r["scales"])
+        assert f32_bits(q.amax.item()) == f32_bits(r["amax"])
+    assert api.counters_dict(cnt) == {k: rr["counters"][k] + rc["counters"][k]
+                                      for k in rr["counters"]}

@@ -160,3 +160,19 @@ def test_dual_workload(cfg, name):
                            target=target, amax=want, index_base=a * q.cols)
             assert np.array_equal(q.codes[a:b].cpu().numpy(), r["codes"]), (orient, a)
             assert np.array_equal(full[a:b], r["scales"]), (orient, a)
+
+
+def test_dual_fused_amax_keeps_nan_like_k_amax():
+    """With the 16-point RHT on the colwise side and both amaxes computed,
+    the plain amax comes from the rotated-amax kernel's read.  Its rowwise
+    amax must equal what the plain amax kernel (the unfused path) returns,
+    also for a tensor holding a NaN (outside the value contract, but the two
+    paths must not differ)."""
+    x = inputs.activations((64, 128), cfg_seed=49)
+    x[5, 17] = 0x7FC0                                   # bf16 quiet NaN
+    xd = dev(x)
+    qr, _ = api.quantize_dual(xd, "nvfp4", rht=True, signs=SIGNS)       # fused amax pass
+    plain = api.amax(xd)                                                 # k_amax
+    torch.cuda.synchronize()
+    assert f32_bits(qr.amax.item()) == f32_bits(plain.item())
+    assert np.isnan(plain.item())
