@@ -1,24 +1,25 @@
 """Benchmark: one step = the whole FP4 hot path of one linear layer.
 
-Default workload: the 1.2B Transformer FFN up-projection (X [8192, 2048],
-W [6144, 2048], dY [8192, 6144]) in NVFP4, on synthetic seeded tensors
-already resident in HBM.  A step runs, on one stream:
+Default workload: the 8B hybrid model's FFN up-projection (X [8192, 4096],
+W [21504, 4096], dY [8192, 21504]) with UE5M3 block scales and stale tensor
+amaxes (T = 448 for X and W, 2048 for dY), on synthetic seeded tensors
+already resident in HBM.  A step runs:
 
-  tensor amax of X, W, dY
   quantize X rowwise + colwise (RNE, one read)   -> Fprop A, Wgrad B
   quantize W 16x16 2D (+ W^T)                    -> Fprop B, Dgrad B
   quantize dY rowwise + colwise (SR, one read)   -> Dgrad A, Wgrad A
   GEMMs Fprop, Dgrad, Wgrad                      (fp32 outputs)
 
-(--separate-quant: the rowwise and colwise quantizations of X and dY as
-four kernels, each reading its tensor.)
-with event counters on every quantization.  The step is captured once as a
-HIP graph and replayed (after a bitwise check of replays against the eager
-step); per-kernel durations come from graphs of repeated launches of each
-op, timed with events on the launch stream.  Printed: one JSON line whose
+(NVFP4 workloads, --config 2|3|5, add the tensor amax passes; --separate-quant
+quantizes each orientation with its own read.)  Event counters are kept on
+every quantization.  The step is captured once as a HIP graph and replayed
+(after a bitwise check of replays against the eager step).  Per-kernel
+durations come from graphs that run each op after a 512 MiB write (which
+evicts the 256 MB Infinity Cache), minus the same graph without the op,
+timed with events on the launch stream.  Printed: one JSON line whose
 `value` is the step's GEMM throughput (3 x 2MNK / step time, TFLOP/s),
 per-kernel timings and rates (`parts`), the roofline of the dominant kernel
-and the CPU oracle timed on a bounded slab of the same workload.
+and the CPU oracle timed on a bounded sample of the same workload.
 
   python bench.py [--steps K] [--warmup W] [--config 2|3|4|5] [--no-cpu] [--separate-quant]
 """
@@ -37,7 +38,10 @@ sys.path.insert(0, ROOT)
 METRIC = "quantize GB/s (% HBM peak); FP4 block-scaled GEMM TFLOP/s (% MFMA peak)"
 HBM_PEAK_GBS = 8000.0
 PEAK_TFLOPS = {"fp16": 2500.0, "fp4": 10100.0}   # dense MFMA, MI355X
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_gemm_nvfp4_1.2b_ffn.txt")
+# rocprofv3 counter summaries of the dominant (GEMM) kernel, per workload
+PROFILE_TRAFFIC = {2: os.path.join(ROOT, "profiles", "traffic_gemm_nvfp4_1.2b_ffn.txt"),
+                   4: os.path.join(ROOT, "profiles", "traffic_gemm_ue5m3_8b_ffn.txt")}
+FLUSH_BYTES = 512 << 20     # written before each timed op: more than the 256 MB Infinity Cache
 
 # algorithmic bytes per element
 B_AMAX = 2.0
@@ -53,9 +57,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2, choices=(2, 3, 4, 5))
+    ap.add_argument("--config", type=int, default=4, choices=(2, 3, 4, 5))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-tokens", type=int, default=8192)
+    ap.add_argument("--cpu-tokens", type=int, default=4096,
+                    help="tokens of the CPU oracle's sample (W is quantized in full)")
     ap.add_argument("--layer", action="store_true",
                     help="time QuantizedLinear.forward + backward (the layer a user calls) "
                          "instead of the step's kernel list")
@@ -141,8 +146,8 @@ def summarize_pmc(fetch_csv, write_csv, cfg):
 
 
 # every source the GEMM kernels are built from
-GEMM_SOURCES = ("gemm.hip", "gemm_common.hpp", "gemm_nv.hip", "gemm_nv_dma.hpp", "gemm_nv_dma256.hip",
-                "gemm_nv_dma192.hip", "gemm_mx.hip", "gemm_mx_dma.hip", "fp4_device.hpp")
+GEMM_SOURCES = ("gemm.hip", "gemm_common.hpp", "gemm_nv.hip", "gemm_nv_dma.hip", "gemm_mx.hip",
+                "gemm_mx_dma.hip", "fp4_device.hpp")
 
 
 def source_hash(*names):
@@ -153,13 +158,15 @@ def source_hash(*names):
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel_hash):
+def read_traffic(cfg, kernel_hash):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3
-    counter summary, if it was taken on the current kernel source."""
-    if not os.path.exists(PROFILE_TRAFFIC):
+    counter summary of this workload, if it was taken on the current kernel
+    source."""
+    path = PROFILE_TRAFFIC.get(cfg)
+    if path is None or not os.path.exists(path):
         return None
     vals = {}
-    with open(PROFILE_TRAFFIC) as f:
+    with open(path) as f:
         for line in f:
             if "=" in line and not line.startswith("#"):
                 k, v = line.split("=", 1)
@@ -187,12 +194,15 @@ def build_step(cfg, dev, dual=True):
     cnt = api.new_counters(dev)
     rht = cfg == 3
     target_x = target_w = target_dy = 448.0
-    stale = {}
+    stale, host_stale = {}, {}
     if fmt == "ue5m3":
+        # the stale amax: from the same distribution drawn 50 steps earlier
+        # (seed offset 50), divided by 1.5 so the current tensors overshoot it
         target_dy = 2048.0
         for name, gen, shape in (("X", inputs.activations, X.shape), ("W", inputs.weights, W.shape),
                                  ("dY", inputs.gradients, dY.shape)):
-            b = torch.from_numpy(gen(tuple(shape), cfg_seed=inputs.STALE_SEED_OFFSET).view(np.int16)).to(dev)
+            host_stale["stale_" + name] = gen(tuple(shape), cfg_seed=inputs.STALE_SEED_OFFSET)
+            b = torch.from_numpy(host_stale["stale_" + name].view(np.int16)).to(dev)
             stale[name] = (api.amax(b) / 1.5).contiguous()
             del b
     D_f = torch.empty((T, dout), dtype=torch.float32, device=dev)
@@ -224,8 +234,10 @@ def build_step(cfg, dev, dual=True):
         if not fused_amax:
             ops += [("amax X", "hbm", B_AMAX * X.numel(), amax_op("X", X)),
                     ("amax dY", "hbm", B_AMAX * dY.numel(), amax_op("dY", dY))]
-        if fmt == "ue5m3":     # stale amax given: nothing to compute
-            ops = [(n, k, 0.0, f) for (n, k, _, f) in ops]
+        if fmt == "ue5m3":     # stale amaxes given: nothing to compute in the step
+            for name in ("X", "W", "dY"):
+                st["amax_" + name] = stale[name]
+            ops = []
         if rht and not fused_amax:
             ops += [("amax rot X", "hbm", B_AMAX * X.numel(), amax_rot_op("X", X)),
                     ("amax rot dY", "hbm", B_AMAX * dY.numel(), amax_rot_op("dY", dY))]
@@ -293,58 +305,141 @@ def build_step(cfg, dev, dual=True):
     ops.append(("gemm dgrad", "mfma", fl(T, din, dout),
                 g("qdy", "r", "qw" if two_level else "qwc", "T", T, din, dout, D_d)))
     ops.append(("gemm wgrad", "mfma", fl(dout, din, T), g("qdyc", "r", "qxc", "r", dout, din, T, D_w)))
-    return ops, cnt, dict(X=t["X"], W=t["W"], dY=t["dY"], gpu_outputs=(D_f, D_d, D_w)), fmt
+    return ops, cnt, dict(X=t["X"], W=t["W"], dY=t["dY"], gpu_outputs=(D_f, D_d, D_w),
+                          **host_stale), fmt
 
 
-def cpu_baseline(cfg, host, fmt, tokens):
-    """The CPU oracle on a token slab of the same step (W quantized in full)."""
-    from threadpoolctl import threadpool_info
+def cpu_cores():
+    """Host cores this process may run on (at most 16, the host share of one GPU)."""
+    return max(1, min(len(os.sched_getaffinity(0)), 16))
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_chunk(task):
+    """Pool worker: the oracle's quantization of one chunk and its exactly
+    dequantized GEMM operand values (fp64) -> (values, s_dec)."""
+    from oracle import quantize as Q
+    bits, fmt, layout, kw = task
+    if layout == "2d":
+        q = Q.quantize(bits, fmt, block="2d", emit_transpose=True, **kw)
+        R, C = bits.shape
+        return Q.operand_values(q["codes"], q["scales"], fmt, "2d", R, C), q["s_dec"]
+    q = Q.quantize(bits, fmt, orient=layout, **kw)
+    R, Cc = q["codes"].shape
+    return Q.operand_values(q["codes"], q["scales"], fmt, "1d", R, 2 * Cc), q["s_dec"]
+
+
+def _oracle_amax_chunk(task):
+    from oracle import formats as F
+    from oracle import quantize as Q
+    bits, rht, signs = task
+    xf = F.bf16_bits_to_f32(bits)
+    if rht:
+        from oracle.rht import rht16_cols
+        xf = rht16_cols(xf, signs)
+    return float(Q.tensor_amax(xf))
+
+
+def _pooled_quantize(pool, n, bits, fmt, layout, **kw):
+    """Operand values of one quantized operand, chunked over the pool: rows
+    for rowwise and 2D (16-row groups), columns for colwise (each chunk
+    keeps its Philox indices through index_base)."""
+    if fmt != "mxfp4" and "amax" not in kw:
+        raise ValueError("chunks of a two-level quantization need the tensor amax")
+    R, C = bits.shape
+    tasks = []
+    if layout == "col":
+        step = -(-C // n)
+        for c0 in range(0, C, step):
+            tasks.append((np.ascontiguousarray(bits[:, c0:c0 + step]), fmt, "col",
+                          dict(kw, index_base=c0 * R)))
+        parts = pool.map(_oracle_chunk, tasks)
+        return np.concatenate([p[0] for p in parts], axis=0), parts[0][1]
+    unit = 16 if layout == "2d" else 1
+    step = -(-R // (n * unit)) * unit
+    for r0 in range(0, R, step):
+        k = dict(kw) if layout == "2d" else dict(kw, index_base=r0 * C)
+        tasks.append((bits[r0:r0 + step], fmt, layout, k))
+    parts = pool.map(_oracle_chunk, tasks)
+    return np.concatenate([p[0] for p in parts], axis=0), parts[0][1]
+
+
+def cpu_baseline(cfg, host, fmt, tokens, pool):
+    """The CPU oracle on a token slab of the same step (W quantized in full):
+    quantizers over a process pool of the host's cores, fp64 BLAS GEMMs on
+    the same number of threads."""
+    from threadpoolctl import threadpool_limits
+    from oracle import formats as F
     from oracle import quantize as Q
     from oracle import gemm as G
     from fp4_block_scaled_x16_amd import inputs
 
+    n = cpu_cores()
     X, W, dY = host["X"][:tokens], host["W"], host["dY"][:tokens]
     rht = cfg == 3
     sig = inputs.rht_sign_mask()
-    t0 = time.perf_counter()
-    kw_dy = dict(rnd="sr", seed=1)
+    two_level = fmt != "mxfp4"
     tgt_dy = 2048.0 if fmt == "ue5m3" else 448.0
-    if fmt == "mxfp4":
-        qx = Q.quantize(X, fmt)
-        qw = Q.quantize(W, fmt)
-        qwc = Q.quantize(W, fmt, orient="col")
-        qdy = Q.quantize(dY, fmt, offset=0, **kw_dy)
-        qdyc = Q.quantize(dY, fmt, orient="col", offset=1, **kw_dy)
-        qxc = Q.quantize(X, fmt, orient="col")
-        s = lambda q: 1.0
-        av = lambda q, blk="1d": Q.operand_values(q["codes"], q["scales"], fmt, blk,
-                                                  q["codes"].shape[0], 2 * q["codes"].shape[1])
-        wv, wtv = av(qw), av(qwc)
+    # stale amaxes (UE5M3) are inputs of the step, not part of it
+    stale = {}
+    if fmt == "ue5m3":
+        for name in ("X", "W", "dY"):
+            stale[name] = np.float32(Q.tensor_amax(F.bf16_bits_to_f32(host["stale_" + name]))
+                                     / np.float32(1.5))
+
+    def amax(name, bits, rot=False):
+        if not two_level:
+            return {}
+        if name in stale:
+            return {"amax": stale[name]}
+        step = -(-bits.shape[0] // (16 * n)) * 16
+        parts = pool.map(_oracle_amax_chunk, [(bits[r:r + step], rot, sig)
+                                              for r in range(0, bits.shape[0], step)])
+        return {"amax": np.float32(max(parts))}
+
+    t0 = time.perf_counter()
+    kx = dict(amax("X", X))
+    kxc = dict(amax("X", X, rht), rht=rht, signs=sig) if rht else kx
+    kdy = dict(amax("dY", dY), rnd="sr", seed=1, target=tgt_dy)
+    kdyc = dict(amax("dY", dY, rht), rnd="sr", seed=1, target=tgt_dy, rht=rht, signs=sig) \
+        if rht else kdy
+    kw_ = dict(amax("W", W))
+    xv, sx = _pooled_quantize(pool, n, X, fmt, "row", **kx)
+    xcv, sxc = _pooled_quantize(pool, n, X, fmt, "col", **kxc)
+    dyv, sdy = _pooled_quantize(pool, n, dY, fmt, "row", offset=0, **kdy)
+    dycv, sdyc = _pooled_quantize(pool, n, dY, fmt, "col", **dict(kdyc, offset=1))
+    if two_level:
+        wv, sw = _pooled_quantize(pool, n, W, fmt, "2d", **kw_)
+        wtv = wv.T
     else:
-        qx = Q.quantize(X, fmt)
-        qw = Q.quantize(W, fmt, block="2d", emit_transpose=True)
-        qdy = Q.quantize(dY, fmt, offset=0, target=tgt_dy, **kw_dy)
-        qdyc = Q.quantize(dY, fmt, orient="col", offset=1, rht=rht, signs=sig, target=tgt_dy, **kw_dy)
-        qxc = Q.quantize(X, fmt, orient="col", rht=rht, signs=sig)
-        s = lambda q: q["s_dec"]
-        av = lambda q, blk="1d": Q.operand_values(q["codes"], q["scales"], fmt, blk,
-                                                  q["codes"].shape[0], 2 * q["codes"].shape[1])
-        wv = av(qw, "2d")
-        wtv = wv.T.copy()
-    d_f = G.gemm_ref(av(qx), wv, s(qx), s(qw))
-    d_d = G.gemm_ref(av(qdy), wtv, s(qdy), s(qw))
-    d_w = G.gemm_ref(av(qdyc), av(qxc), s(qdyc), s(qxc))
+        wv, sw = _pooled_quantize(pool, n, W, fmt, "row")
+        wtv, _ = _pooled_quantize(pool, n, W, fmt, "col")
+    t_q = time.perf_counter() - t0
+    s = (lambda v: v) if two_level else (lambda v: 1.0)
+    with threadpool_limits(limits=n, user_api="blas"):
+        d_f = G.gemm_ref(xv, wv, s(sx), s(sw))
+        d_d = G.gemm_ref(dyv, np.ascontiguousarray(wtv), s(sdy), s(sw))
+        d_w = G.gemm_ref(np.ascontiguousarray(dycv), np.ascontiguousarray(xcv), s(sdyc), s(sxc))
     dt = time.perf_counter() - t0
     T = tokens
     din, dout = X.shape[1], W.shape[0]
     flops = 2.0 * T * dout * din * 3
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     del d_f, d_d, d_w
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": "the same step on %d of %d tokens (W quantized in full), %.1f s; "
-                      "GEMMs in fp64 BLAS, quantizers single-threaded NumPy" % (
-                          tokens, host["X"].shape[0], dt),
-            "seconds": round(dt, 3)}
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": n, "kind": "oracle",
+            "sample": "the same step on %d of %d tokens (W quantized in full), %.1f s: "
+                      "quantizers %.1f s over a pool of %d processes, GEMMs %.1f s in fp64 BLAS "
+                      "on %d threads" % (tokens, host["X"].shape[0], dt, t_q, n, dt - t_q, n),
+            "seconds": round(dt, 3), "cpu_model": cpu_model()}
 
 
 def layer_main(args, dev):
@@ -499,6 +594,11 @@ def main():
         print("bench.py measures one GPU (--gpus 1); runs on several GPUs are not "
               "part of this benchmark.", file=sys.stderr)
         sys.exit(2)
+    # the CPU oracle's worker processes are forked before anything touches the GPU
+    pool = None
+    if not (args.no_cpu or args.layer or args.counters_run):
+        import multiprocessing
+        pool = multiprocessing.get_context("fork").Pool(cpu_cores())
     import torch
     from fp4_block_scaled_x16_amd import api, inputs
 
@@ -590,38 +690,62 @@ def main():
     ms_step = e0.elapsed_time(e1) / args.steps
     counters = api.counters_dict(cnt)
 
-    # per-kernel durations: each op repeated R times in its own graph, timed
-    # with events on the stream the kernels run on
+    # Per-kernel durations, timed with events on the stream the kernels run
+    # on: a graph of R x (512 MiB write, op) minus a graph of R x (512 MiB
+    # write), so every op starts with the Infinity Cache holding none of its
+    # inputs; and (`parts_warm`) a graph of R back-to-back launches.
     R = 10
-    op_ms = []
-    for (_, _, _, f) in ops:
+    flush_buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+
+    def graph_ms(body, reps=3):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for _ in range(R):
-                f()
+            body()
         g.replay()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
-        for _ in range(3):
+        for _ in range(reps):
             g.replay()
         b.record()
         torch.cuda.synchronize()
-        op_ms.append(a.elapsed_time(b) / (3 * R))
         del g
+        return a.elapsed_time(b) / reps
 
-    parts = {}
-    for i, (name, kind, units, _) in enumerate(ops):
-        ms = op_ms[i]
-        p = {"ms": round(ms, 4)}
-        if kind == "hbm" and units > 0:
-            gbs = units / (ms * 1e-3) / 1e9
-            p.update(GBps=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
-        elif kind == "mfma":
-            tf = units / (ms * 1e-3) / 1e12
-            peak = PEAK_TFLOPS["fp4" if fmt == "mxfp4" else "fp16"]
-            p.update(TFLOPs=round(tf, 1), frac_peak=round(tf / peak, 4))
-        parts[name] = p
+    def flushes():
+        for _ in range(R):
+            flush_buf.fill_(1.0)
+
+    op_ms, op_ms_warm = [], []
+    for (_, _, _, f) in ops:
+        def cold():
+            for _ in range(R):
+                flush_buf.fill_(1.0)
+                f()
+
+        def warm():
+            for _ in range(R):
+                f()
+        t_flush = graph_ms(flushes)
+        op_ms.append(max(graph_ms(cold) - t_flush, 0.0) / R)
+        op_ms_warm.append(graph_ms(warm) / R)
+    del flush_buf
+
+    def rates(times):
+        out = {}
+        for i, (name, kind, units, _) in enumerate(ops):
+            ms = times[i]
+            p = {"ms": round(ms, 4)}
+            if kind == "hbm" and units > 0:
+                gbs = units / (ms * 1e-3) / 1e9
+                p.update(GBps=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
+            elif kind == "mfma":
+                tf = units / (ms * 1e-3) / 1e12
+                peak = PEAK_TFLOPS["fp4" if fmt == "mxfp4" else "fp16"]
+                p.update(TFLOPs=round(tf, 1), frac_peak=round(tf / peak, 4))
+            out[name] = p
+        return out
+    parts, parts_warm = rates(op_ms), rates(op_ms_warm)
     q_bytes = sum(u for (_, k, u, _) in ops if k == "hbm")
     q_ms = sum(parts[n]["ms"] for (n, k, u, _) in ops if k == "hbm" and u > 0)
     g_flops = sum(u for (_, k, u, _) in ops if k == "mfma")
@@ -635,11 +759,11 @@ def main():
     achieved = per_launch / (avg_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS["fp4" if fmt == "mxfp4" else "fp16"]
     khash = source_hash(*GEMM_SOURCES)
-    traffic = read_traffic(khash) if cfg == 2 else None
+    traffic = read_traffic(cfg, khash)
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic,
                 "kernel": "k_gemm_two_level_dma<NVFP4>" if fmt == "nvfp4" else
-                          ("k_gemm_two_level<UE5M3>" if fmt == "ue5m3" else "k_gemm_mx_tiled"),
+                          ("k_gemm_two_level_dma<UE5M3>" if fmt == "ue5m3" else "k_gemm_mx_tiled"),
                 "flops_per_launch": per_launch, "avg_launch_ms": round(avg_ms, 4),
                 "kernel_source_sha256_16": khash}
 
@@ -664,13 +788,16 @@ def main():
                  "frac_peak": round(g_flops / (g_ms * 1e-3) / 1e12 / peak, 4), "ms": round(g_ms, 4)},
         "roofline": roofline,
         "parts": parts,
+        "parts_warm": parts_warm,
         "counters": counters,
         "wall_s_timed": round(wall, 3),
     }
     if cfg == 5:
         out["format_comparison"] = format_comparison(dev)
-    if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(cfg, host, fmt, args.cpu_tokens)
+    if pool is not None:
+        out["cpu_baseline"] = cpu_baseline(cfg, host, fmt, args.cpu_tokens, pool)
+        pool.close()
+        pool.join()
     print(json.dumps(out))
 
 

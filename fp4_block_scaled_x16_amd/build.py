@@ -21,9 +21,14 @@ BUILD = os.path.join(ROOT, "_build")
 LIB_NAME = "libfp4_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["quant.hip", "gemm.hip", "gemm_nv.hip", "gemm_nv_dma256.hip",
-           "gemm_nv_dma192.hip", "gemm_mx.hip",
-           "gemm_mx_dma.hip", "selftest.hip", "fp4_api.cpp"]
+# (source, object name, extra flags): gemm_nv_dma.hip is built once per
+# block-scale format and tile height so the four kernel families compile in
+# parallel
+SOURCES = [("quant.hip", "quant", []), ("gemm.hip", "gemm", []), ("gemm_nv.hip", "gemm_nv", [])] + [
+    ("gemm_nv_dma.hip", "gemm_nv_dma_%d_%d" % (f, mi), ["-DFP4_DMA_FMT=%d" % f, "-DFP4_DMA_MI=%d" % mi])
+    for f in (0, 1) for mi in (4, 3)] + [
+    ("gemm_mx.hip", "gemm_mx", []), ("gemm_mx_dma.hip", "gemm_mx_dma", []),
+    ("selftest.hip", "selftest", []), ("fp4_api.cpp", "fp4_api", [])]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-x", "hip", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-fvisibility=hidden", "-ffp-contract=off",
@@ -56,12 +61,12 @@ def build(verbose=False, incremental=False):
     older than the source or any header) and link the library."""
     os.makedirs(BUILD, exist_ok=True)
     objs, cmds = [], []
-    for src in SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
+    for src, name, extra in SOURCES:
+        obj = os.path.join(BUILD, name + ".o")
         objs.append(obj)
         if incremental and not _stale(obj, os.path.join(CSRC, src)):
             continue
-        cmds.append([HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC] + FLAGS + extra + ["-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=max(1, len(cmds))) as ex:
         for err in ex.map(_run, cmds):
             if verbose and err.strip():

@@ -6,7 +6,7 @@
 //   D[M, N] (+)= s_A s_B sum_k a[m, k] b[n, k],   a = e2m1 * scale ("TN")
 //
 // Every kernel uses one skeleton: a 256 x 256 output tile per workgroup
-// (192 x 256 for some NVFP4 shapes),
+// (192 x 256 for some NVFP4 / UE5M3 shapes),
 // four waves in a 2 x 2 arrangement (128 x 128 each, 4 x 4 MFMA tiles of
 // 32 x 32), FP4 codes and scales staged through LDS, one barrier per K step,
 // the next K step's loads in flight while the current one is multiplied,
@@ -19,12 +19,11 @@
 //   packed fp16 multiply by the block scale -- and feeds
 //   v_mfma_f32_32x32x16_f16 with fp32 accumulation.  The 2^-5 shifts and
 //   the tensor scales are applied to the fp32 result.
-//     k_gemm_two_level_dma  NVFP4, K % 256 == 0, 16-byte code rows: codes
-//                           go to LDS by DMA (global_load_lds); 256- or
-//                           192-row tiles (gemm_nv_dma*.hip).
-//     k_gemm_two_level      every other shape (and UE5M3): codes staged
-//                           through registers, ragged edges masked
-//                           (gemm_nv.hip).
+//     k_gemm_two_level_dma  K % 256 == 0, 16-byte code rows: codes go to
+//                           LDS by DMA (global_load_lds); 256- or 192-row
+//                           tiles (gemm_nv_dma.hip).
+//     k_gemm_two_level      every other shape: codes staged through
+//                           registers, ragged edges masked (gemm_nv.hip).
 // * MXFP4: gfx950's scaled MFMA takes FP4 operands and one E8M0 scale per 32
 //   K-values per lane, which is exactly an MXFP4 block, so the codes go from
 //   LDS to v_mfma_scale_f32_32x32x64_f8f6f4 untouched.
@@ -133,14 +132,11 @@ hipError_t launch_gemm(int format, const GemmOperand& A, const GemmOperand& B, i
     if (ring) return launch_mx_ring(p, grid, s);
     return launch_mx(fast, scv, p, grid, s);
   }
-  if (format == FP4_NVFP4 && K > 0 && K % (2 * kBK2) == 0 && p.vec16[0] && p.vec16[1] &&
+  if (K > 0 && K % (2 * kBK2) == 0 && p.vec16[0] && p.vec16[1] &&
       M * p.ld[0] < (int64_t(1) << 31) && N * p.ld[1] < (int64_t(1) << 31) &&
       scale_extent(p, 0, M) < (int64_t(1) << 31) && scale_extent(p, 1, N) < (int64_t(1) << 31)) {
-    // NVFP4 codes by DMA: whole pairs of K steps, 16-byte code rows.  (UE5M3
-    // stays on the register-staged kernel: its arithmetic scale decode sits
-    // in front of this kernel's barrier and costs more than the DMA saves.)
-    // Tile height 192 instead of 256 when that shortens the launch: its
-    // time goes as (rounds of tiles over the CUs) x (tile height), with a
+    // Codes by DMA: whole pairs of K steps, 16-byte code rows.  Tile height
+    // 192 instead of 256 when that shortens the launch: its time goes as (rounds of tiles over the CUs) x (tile height), with a
     // 5 % allowance for the smaller tile's lower MFMA share per VALU op.
     const int64_t cus = device_cu_count();
     auto cost = [&](int64_t bm) {
@@ -149,7 +145,9 @@ hipError_t launch_gemm(int format, const GemmOperand& A, const GemmOperand& B, i
     };
     const int short_tile = cost(192) * 20 < cost(256) * 19 ? 1 : 0;
     if (short_tile) p.tiles_m = static_cast<int>((M + 191) / 192);
-    return short_tile ? launch_two_level_dma_192(scv, p, s) : launch_two_level_dma_256(scv, p, s);
+    if (format == FP4_NVFP4)
+      return short_tile ? launch_two_level_dma_0_3(scv, p, s) : launch_two_level_dma_0_4(scv, p, s);
+    return short_tile ? launch_two_level_dma_1_3(scv, p, s) : launch_two_level_dma_1_4(scv, p, s);
   }
   return launch_two_level(format, fast, scv, p, grid, s);
 }

@@ -1,10 +1,9 @@
 // Shared pieces of the block-scaled FP4 GEMM kernels: the launch
 // parameters, tile order, epilogue, LDS swizzle and wait helpers, and the
 // NVFP4 / UE5M3 dequantize-and-multiply slice.  Each kernel family lives in
-// its own translation unit (gemm_nv.hip, gemm_nv_dma256.hip and
-// gemm_nv_dma192.hip, gemm_mx.hip,
-// gemm_mx_dma.hip) behind the launch functions declared at the end; the
-// dispatch between them is in gemm.hip.
+// its own translation unit (gemm_nv.hip, gemm_nv_dma.hip -- built once per
+// format and tile height --, gemm_mx.hip, gemm_mx_dma.hip) behind the launch
+// functions declared at the end; the dispatch between them is in gemm.hip.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -261,8 +260,12 @@ hipError_t launch_with_lds(void (*kernel)(Params), size_t lds, int grid, hipStre
 // Family launchers (one translation unit each).  `grid` = tiles_m * tiles_n.
 hipError_t launch_two_level(int format, bool fast, int scv, const Params& p, int grid,
                             hipStream_t s);
-hipError_t launch_two_level_dma_256(int scv, const Params& p, hipStream_t s);
-hipError_t launch_two_level_dma_192(int scv, const Params& p, hipStream_t s);
+// gemm_nv_dma.hip, one object per format (0 NVFP4, 1 UE5M3) and tile height
+// (4: 256 rows, 3: 192 rows)
+hipError_t launch_two_level_dma_0_4(int scv, const Params& p, hipStream_t s);
+hipError_t launch_two_level_dma_0_3(int scv, const Params& p, hipStream_t s);
+hipError_t launch_two_level_dma_1_4(int scv, const Params& p, hipStream_t s);
+hipError_t launch_two_level_dma_1_3(int scv, const Params& p, hipStream_t s);
 hipError_t launch_mx(bool fast, int scv, const Params& p, int grid, hipStream_t s);
 hipError_t launch_mx_ring(const Params& p, int grid, hipStream_t s);
 hipError_t launch_mx_tiled(const Params& p, int grid, hipStream_t s);

@@ -1,5 +1,5 @@
-// NVFP4 / UE5M3 block-scaled GEMM with register-staged codes: every shape
-// (ragged M, N and K tails masked) and the only kernel for UE5M3.
+// NVFP4 / UE5M3 block-scaled GEMM with register-staged codes: the shapes the
+// DMA kernel does not take (ragged M, N and K tails masked).
 
 #include "gemm_common.hpp"
 

@@ -1,8 +1,8 @@
-// NVFP4 block-scaled GEMM with the codes moved into LDS by DMA (K a
-// multiple of 256, 16-byte-aligned code rows).  The kernel template is
-// instantiated per tile height in gemm_nv_dma256.hip and gemm_nv_dma192.hip
-// (two translation units, so the two sets compile in parallel).
-#pragma once
+// NVFP4 / UE5M3 block-scaled GEMM with the codes moved into LDS by DMA (K a
+// multiple of 256, 16-byte-aligned code rows).  This source is compiled once
+// per (format, tile height) with FP4_DMA_FMT (0 NVFP4, 1 UE5M3) and
+// FP4_DMA_MI (4: 256-row tiles, 3: 192-row tiles) defined, so the four
+// kernel families build in parallel; each object defines one launcher.
 
 #include "gemm_common.hpp"
 
@@ -16,7 +16,7 @@ namespace {
 // (global_load_lds, 16 bytes per lane) instead of through registers and LDS
 // stores, and ragged M / N read the last valid row (never stored).  Block
 // scales are still loaded to registers and decoded once per K step by the
-// loading thread.  Codes and scales of each of the two stages are separate
+// loading thread, off the path to the barrier (see the step below).  Codes and scales of each of the two stages are separate
 // __shared__ variables named with compile-time indices, so the compiler can
 // tell the DMA targets from the LDS the waves read and write.
 //
@@ -69,6 +69,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level_dma(Params p) {
   constexpr int BM = 64 * MI;
   __shared__ uint4 cst0[2][1024], cst1[2][1024];   // [operand][row * 4 + (chunk ^ swizzle)]
   __shared__ uint2 sst0[2][2][256], sst1[2][2][256];  // [operand][half][row] fp16 scale pairs
+  // UE5M3: fp16 value (times 2^-5) of every scale code, so a decode is one
+  // LDS read instead of the arithmetic decode (E4M3 uses the FP8 convert)
+  __shared__ uint16_t ue_tab[FMT == kUE ? 256 : 1];
   int tm, tn;
   tile_coords(p, tm, tn);
   const int64_t m0 = static_cast<int64_t>(tm) * BM, n0 = static_cast<int64_t>(tn) * kBN;
@@ -103,34 +106,58 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level_dma(Params p) {
     sstep[o] = p.tiled[o] ? 2048 : 8 * p.s_kblk[o];
   }
 
-  uint2 rs[2];
-  uint32_t rsb[2][8];
-  auto load_scales = [&](int s) {
+  // Raw scale bytes are loaded two K steps ahead (rs[1]) and decoded one
+  // step ahead (rs[0] -> pr) during the slices, so only the LDS store of the
+  // already decoded pairs sits between the code DMA's arrival and the
+  // barrier; the decode is cheap for E4M3 (the packed FP8 convert) but
+  // arithmetic for UE5M3.
+  uint2 rs[2][2];
+  uint32_t rsb[2][2][8];
+  uint32_t pr[2][4];
+  constexpr int kScaleLoads = (SCV & 1 ? 1 : 8) + (SCV & 2 ? 1 : 8);
+  constexpr int kDmaLoads = MI + 4;
+  auto load_scales = [&](int slot, int s) {
 #pragma unroll
     for (int o = 0; o < 2; ++o) {
       const uint8_t* sp = p.scales[o] + s * sstep[o] + soff[o];
       if ((SCV >> o) & 1) {
-        rs[o] = *reinterpret_cast<const uint2*>(sp);
+        rs[slot][o] = *reinterpret_cast<const uint2*>(sp);
       } else {
         const int64_t st = p.s_kblk[o];
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb) rsb[o][kb] = sp[kb * st];
+        for (int kb = 0; kb < 8; ++kb) rsb[slot][o][kb] = sp[kb * st];
       }
+    }
+  };
+  auto decode_scales = [&]() {
+#pragma unroll
+    for (int o = 0; o < 2; ++o) {
+      const bool bytes = !((SCV >> o) & 1);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t two = bytes ? rsb[0][o][2 * k] | (rsb[0][o][2 * k + 1] << 8)
+                                   : (k < 2 ? rs[0][o].x : rs[0][o].y) >> (16 * (k & 1));
+        if constexpr (FMT == kUE)
+          pr[o][k] = static_cast<uint32_t>(ue_tab[two & 0xFFu]) |
+                     (static_cast<uint32_t>(ue_tab[(two >> 8) & 0xFFu]) << 16);
+        else
+          pr[o][k] = scale_pair_f16<FMT>(two);
+      }
+    }
+  };
+  auto shift_scales = [&]() {
+#pragma unroll
+    for (int o = 0; o < 2; ++o) {
+      rs[0][o] = rs[1][o];
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) rsb[0][o][kb] = rsb[1][o][kb];
     }
   };
   auto store_scales = [&](uint2 (&S)[2][2][256]) {
 #pragma unroll
     for (int o = 0; o < 2; ++o) {
-      const bool bytes = !((SCV >> o) & 1);
-      uint32_t pr[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t two = bytes ? rsb[o][2 * k] | (rsb[o][2 * k + 1] << 8)
-                                   : (k < 2 ? rs[o].x : rs[o].y) >> (16 * (k & 1));
-        pr[k] = scale_pair_f16<FMT>(two);
-      }
-      S[o][0][t] = make_uint2(pr[0], pr[1]);
-      S[o][1][t] = make_uint2(pr[2], pr[3]);
+      S[o][0][t] = make_uint2(pr[o][0], pr[o][1]);
+      S[o][1][t] = make_uint2(pr[o][2], pr[o][3]);
     }
   };
 
@@ -173,21 +200,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level_dma(Params p) {
 
   // Step s on stage C (raw codes and scales already in registers) while the
   // next step (s + 1, or s again on the last step: the other stage is not
-  // read afterwards) fills stage N: its scale loads and code DMA are issued
-  // at the top; after slice 6 the DMA has landed and the decoded scales are
-  // stored (one wait for both), then the barrier, and the next stage's LDS
-  // reads overlap slice 7.  N was last read before the previous barrier.
-  // Slice 0 of a step is dequantized either at the top of the step (256-row
-  // tiles) or, for 192-row tiles, under the second part of the previous
-  // step's slice 7 (kTail; measured faster there, slower with 256 rows,
-  // whose slice-7 MFMAs cannot hide the 8 extra VALU ops per MFMA).
+  // read afterwards) fills stage N.  At the top: the code DMA of step s + 1
+  // and the scale loads of step s + 2 are issued, then (their own loads,
+  // issued a step earlier, have landed) the scales of step s + 1 are decoded
+  // among the slices.  After slice 6 the DMA has landed (the younger scale
+  // loads may still be in flight), the decoded scales are stored, then the
+  // barrier, and the next stage's LDS reads overlap slice 7.  N was last
+  // read before the previous barrier.  Slice 0 of a step is dequantized
+  // either at the top of the step (256-row tiles) or, for 192-row tiles,
+  // under the second part of the previous step's slice 7 (kTail; measured
+  // faster there, slower with 256 rows, whose slice-7 MFMAs cannot hide the
+  // 8 extra VALU ops per MFMA).
   constexpr bool kTail = MI != 4;
   FragT<MI> f0, f1;
   auto step = [&](uint4 (&Nc)[2][1024], uint2 (&Ns)[2][2][256], int s) {
     const int nxt = s + 1 < nsteps ? s + 1 : s;
-    load_scales(nxt);
+    const int nxt2 = s + 2 < nsteps ? s + 2 : nsteps - 1;
     dma_codes_nv<MI>(Nc, src, nxt, wave);
+    __builtin_amdgcn_sched_barrier(0);     // the DMA is issued before (is older than) ...
+    load_scales(1, nxt2);                  // ... the scale loads: the vmcnt waits rely on it
     __builtin_amdgcn_sched_barrier(0);     // keep the loads at the top of the step
+    wait_vmcnt<kDmaLoads + kScaleLoads>();  // step s + 1's scale bytes
+    decode_scales();
     if constexpr (!kTail) dequant_slice<0>(f0, a_raw, b_raw, a_sc, b_sc);
     pipelined_slice<0>(acc, f0, f1, a_raw, b_raw, a_sc, b_sc);
     pipelined_slice<1>(acc, f1, f0, a_raw, b_raw, a_sc, b_sc);
@@ -196,8 +230,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level_dma(Params p) {
     pipelined_slice<4>(acc, f0, f1, a_raw, b_raw, a_sc, b_sc);
     pipelined_slice<5>(acc, f1, f0, a_raw, b_raw, a_sc, b_sc);
     pipelined_slice<6>(acc, f0, f1, a_raw, b_raw, a_sc, b_sc);
-    wait_vmcnt<0>();
+    wait_vmcnt<kScaleLoads>();              // the code DMA of step s + 1
     store_scales(Ns);
+    shift_scales();
     __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // this wave's LDS stores done
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -212,10 +247,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level_dma(Params p) {
     }
   };
 
-  load_scales(0);
+  if constexpr (FMT == kUE) {
+    ue_tab[t] = static_cast<uint16_t>(scale_pair_f16<kUE>(static_cast<uint32_t>(t)) & 0xFFFFu);
+  }
+  load_scales(0, 0);
   dma_codes_nv<MI>(cst0, src, 0, wave);
-  store_scales(sst0);
   wait_vmcnt<0>();
+  if constexpr (FMT == kUE) ring_barrier();   // the table is written
+  decode_scales();
+  store_scales(sst0);
+  load_scales(0, nsteps > 1 ? 1 : 0);     // step 1's scales, decoded in step 0
   ring_barrier();
   read_stage(cst0, sst0);
   if constexpr (kTail) dequant_slice<0>(f0, a_raw, b_raw, a_sc, b_sc);
@@ -223,6 +264,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level_dma(Params p) {
     step(cst1, sst1, s);
     step(cst0, sst0, s + 1);
   }
+  wait_vmcnt<0>();                         // the last (unused) scale loads
 
   float scale = FMT == kUE ? 1024.0f : 1.0f;   // undo the two 2^-5 scale shifts
   if (p.s_dec[0]) scale *= *p.s_dec[0];
@@ -236,13 +278,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level_dma(Params p) {
 
 }  // namespace
 
-// Launch the MI-variant for scale-loader variant `scv` (bit o: operand o's
-// scales of one row and K step are one aligned 8-byte word).
-template <int MI>
-hipError_t launch_two_level_dma_mi(int scv, const Params& p, hipStream_t s) {
-  constexpr void (*dnv[4])(Params) = {k_gemm_two_level_dma<kNV, 0, MI>, k_gemm_two_level_dma<kNV, 1, MI>,
-                                      k_gemm_two_level_dma<kNV, 2, MI>, k_gemm_two_level_dma<kNV, 3, MI>};
-  hipLaunchKernelGGL(dnv[scv], dim3(p.tiles_m * p.tiles_n), dim3(kThreads), 0, s, p);
+#if !defined(FP4_DMA_FMT) || !defined(FP4_DMA_MI)
+#error "compile with -DFP4_DMA_FMT=0|1 -DFP4_DMA_MI=4|3"
+#endif
+
+// This object's launcher, launch_two_level_dma_<FMT>_<MI>: scale-loader
+// variant `scv` (bit o: operand o's scales of one row and K step are one
+// aligned 8-byte word).
+#define FP4_DMA_NAME2(f, m) launch_two_level_dma_##f##_##m
+#define FP4_DMA_NAME(f, m) FP4_DMA_NAME2(f, m)
+hipError_t FP4_DMA_NAME(FP4_DMA_FMT, FP4_DMA_MI)(int scv, const Params& p, hipStream_t s) {
+  constexpr int F = FP4_DMA_FMT == 0 ? kNV : kUE;
+  constexpr void (*k[4])(Params) = {
+      k_gemm_two_level_dma<F, 0, FP4_DMA_MI>, k_gemm_two_level_dma<F, 1, FP4_DMA_MI>,
+      k_gemm_two_level_dma<F, 2, FP4_DMA_MI>, k_gemm_two_level_dma<F, 3, FP4_DMA_MI>};
+  hipLaunchKernelGGL(k[scv], dim3(p.tiles_m * p.tiles_n), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
