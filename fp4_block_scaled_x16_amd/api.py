@@ -340,8 +340,8 @@ def selftest_sweep(kind, thresholds, device="cuda"):
 
 def selftest_gemm_decode(fmt, device="cuda"):
     """The GEMM's operand decode of every (scale code, E2M1 code) pair:
-    uint16 fp16 patterns [256, 2, 16] (see fp4_selftest_gemm_decode)."""
-    out = torch.empty((256, 2, 16), dtype=torch.int16, device=device)
+    uint16 fp16 patterns [256, 4, 16] (see fp4_selftest_gemm_decode)."""
+    out = torch.empty((256, 4, 16), dtype=torch.int16, device=device)
     lib = load_library()
     _check(lib.fp4_selftest_gemm_decode(_fmt(fmt), _ptr(out), _stream(out.device)),
            "fp4_selftest_gemm_decode")

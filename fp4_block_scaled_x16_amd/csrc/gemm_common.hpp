@@ -156,21 +156,34 @@ __device__ __forceinline__ void ring_barrier() {
 // ------------------------------------------------------- NVFP4 / UE5M3 --
 constexpr int kBK2 = 128;   // K per step: 64 code bytes and 8 scales per row
 
-// Two consecutive block scales (codes in bits 0-7 and 8-15) as an fp16
-// pair, block 2k in the low half.  E4M3 uses the packed hardware FP8 -> fp16
-// convert with a unit scale (exact: every E4M3 value, subnormals included,
-// is an fp16 value); UE5M3 is decoded arithmetically and pre-multiplied by
-// 2^-5 (exact).
-template <int FMT>
-__device__ __forceinline__ uint32_t scale_pair_f16(uint32_t two_codes) {
+typedef unsigned short ushort2v __attribute__((ext_vector_type(2)));
+
+// Two consecutive block scales (codes in bytes B and B + 1 of `word`) as an
+// fp16 pair, block 2k in the low half.  E4M3 uses the packed hardware FP8 ->
+// fp16 convert with a unit scale (exact: every E4M3 value, subnormals
+// included, is an fp16 value).  UE5M3 (bias 15, like fp16) shifted left by 7
+// is bit for bit the fp16 of its value, subnormals included, for every code
+// but those with exponent field 31 (fp16 infinities / NaNs).  Times 2^-5:
+// the fp16 multiply is exact for exponent fields up to 30; the integer
+// exponent decrement max(h, 6 << 10) - (5 << 10) is exact from 6 up (31
+// included) and gives 2^-14 below, more than any product there; so the
+// unsigned minimum of the two is exact for every code (at 31 the multiply
+// gives an infinity or NaN, above 0x7C00).  Checked on all 256 codes.
+template <int FMT, int B = 0>
+__device__ __forceinline__ uint32_t scale_pair_f16(uint32_t word) {
+  static_assert(B == 0 || B == 2, "a pair starts at byte 0 or 2");
   if constexpr (FMT == kNV) {
     return __builtin_bit_cast(uint32_t,
-                              __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(two_codes, 1.0f, false));
+                              __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, B == 2));
   } else {
-    const _Float16 lo = static_cast<_Float16>(scale_m3_decode<15>(two_codes & 0xFFu) * 0x1p-5f);
-    const _Float16 hi =
-        static_cast<_Float16>(scale_m3_decode<15>((two_codes >> 8) & 0xFFu) * 0x1p-5f);
-    return __builtin_bit_cast(uint32_t, half2v{lo, hi});
+    // bytes B, B + 1 -> the low bytes of the two halves (0x0C selects zero)
+    constexpr uint32_t kSel = B == 0 ? 0x0C010C00u : 0x0C030C02u;
+    const ushort2v h = __builtin_bit_cast(ushort2v, __builtin_amdgcn_perm(0u, word, kSel)) << 7;
+    const ushort2v dec = __builtin_elementwise_max(h, ushort2v{0x1800, 0x1800}) -
+                         ushort2v{0x1400, 0x1400};
+    const half2v mul = __builtin_bit_cast(half2v, h) * half2v{0x1p-5f16, 0x1p-5f16};
+    return __builtin_bit_cast(uint32_t,
+                              __builtin_elementwise_min(dec, __builtin_bit_cast(ushort2v, mul)));
   }
 }
 

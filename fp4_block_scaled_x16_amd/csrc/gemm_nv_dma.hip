@@ -69,9 +69,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level_dma(Params p) {
   constexpr int BM = 64 * MI;
   __shared__ uint4 cst0[2][1024], cst1[2][1024];   // [operand][row * 4 + (chunk ^ swizzle)]
   __shared__ uint2 sst0[2][2][256], sst1[2][2][256];  // [operand][half][row] fp16 scale pairs
-  // UE5M3: fp16 value (times 2^-5) of every scale code, so a decode is one
-  // LDS read instead of the arithmetic decode (E4M3 uses the FP8 convert)
-  __shared__ uint16_t ue_tab[FMT == kUE ? 256 : 1];
   int tm, tn;
   tile_coords(p, tm, tn);
   const int64_t m0 = static_cast<int64_t>(tm) * BM, n0 = static_cast<int64_t>(tn) * kBN;
@@ -106,26 +103,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level_dma(Params p) {
     sstep[o] = p.tiled[o] ? 2048 : 8 * p.s_kblk[o];
   }
 
-  // Raw scale bytes are loaded two K steps ahead (rs[1]) and decoded one
-  // step ahead (rs[0] -> pr) during the slices, so only the LDS store of the
-  // already decoded pairs sits between the code DMA's arrival and the
-  // barrier; the decode is cheap for E4M3 (the packed FP8 convert) but
-  // arithmetic for UE5M3.
-  uint2 rs[2][2];
-  uint32_t rsb[2][2][8];
+  // Raw scale bytes are loaded two K steps ahead, at the top of a step, and
+  // decoded (into pr) after that step's barrier, under its last slice's
+  // MFMAs, when the loads have long landed; the decoded pairs are stored
+  // into the stage at the end of the next step.  So no step waits for loads
+  // it has just issued, and only an LDS store sits between the code DMA's
+  // arrival and the barrier.  The decode (scale_pair_f16: one instruction
+  // per pair for E4M3, five for UE5M3) fills VALU slots of the last slice.
+  uint2 rs[2];
+  uint32_t rsb[2][8];
   uint32_t pr[2][4];
   constexpr int kScaleLoads = (SCV & 1 ? 1 : 8) + (SCV & 2 ? 1 : 8);
-  constexpr int kDmaLoads = MI + 4;
-  auto load_scales = [&](int slot, int s) {
+  auto load_scales = [&](int s) {
 #pragma unroll
     for (int o = 0; o < 2; ++o) {
       const uint8_t* sp = p.scales[o] + s * sstep[o] + soff[o];
       if ((SCV >> o) & 1) {
-        rs[slot][o] = *reinterpret_cast<const uint2*>(sp);
+        rs[o] = *reinterpret_cast<const uint2*>(sp);
       } else {
         const int64_t st = p.s_kblk[o];
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb) rsb[slot][o][kb] = sp[kb * st];
+        for (int kb = 0; kb < 8; ++kb) rsb[o][kb] = sp[kb * st];
       }
     }
   };
@@ -135,22 +133,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level_dma(Params p) {
       const bool bytes = !((SCV >> o) & 1);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const uint32_t two = bytes ? rsb[0][o][2 * k] | (rsb[0][o][2 * k + 1] << 8)
-                                   : (k < 2 ? rs[0][o].x : rs[0][o].y) >> (16 * (k & 1));
-        if constexpr (FMT == kUE)
-          pr[o][k] = static_cast<uint32_t>(ue_tab[two & 0xFFu]) |
-                     (static_cast<uint32_t>(ue_tab[(two >> 8) & 0xFFu]) << 16);
+        if (bytes)
+          pr[o][k] = scale_pair_f16<FMT>(rsb[o][2 * k] | (rsb[o][2 * k + 1] << 8));
+        else if (k & 1)
+          pr[o][k] = scale_pair_f16<FMT, 2>(k < 2 ? rs[o].x : rs[o].y);
         else
-          pr[o][k] = scale_pair_f16<FMT>(two);
+          pr[o][k] = scale_pair_f16<FMT, 0>(k < 2 ? rs[o].x : rs[o].y);
       }
-    }
-  };
-  auto shift_scales = [&]() {
-#pragma unroll
-    for (int o = 0; o < 2; ++o) {
-      rs[0][o] = rs[1][o];
-#pragma unroll
-      for (int kb = 0; kb < 8; ++kb) rsb[0][o][kb] = rsb[1][o][kb];
     }
   };
   auto store_scales = [&](uint2 (&S)[2][2][256]) {
@@ -200,17 +189,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level_dma(Params p) {
 
   // Step s on stage C (raw codes and scales already in registers) while the
   // next step (s + 1, or s again on the last step: the other stage is not
-  // read afterwards) fills stage N.  At the top: the code DMA of step s + 1
-  // and the scale loads of step s + 2 are issued, then (their own loads,
-  // issued a step earlier, have landed) the scales of step s + 1 are decoded
-  // among the slices.  After slice 6 the DMA has landed (the younger scale
-  // loads may still be in flight), the decoded scales are stored, then the
-  // barrier, and the next stage's LDS reads overlap slice 7.  N was last
-  // read before the previous barrier.  Slice 0 of a step is dequantized
-  // either at the top of the step (256-row tiles) or, for 192-row tiles,
-  // under the second part of the previous step's slice 7 (kTail; measured
-  // faster there, slower with 256 rows, whose slice-7 MFMAs cannot hide the
-  // 8 extra VALU ops per MFMA).
+  // read afterwards) fills stage N.  At the top: the code DMA of step s + 1,
+  // then the scale loads of step s + 2.  After slice 6 the DMA has landed
+  // (the younger scale loads may still be in flight), the scales of step
+  // s + 1 (decoded during step s - 1) are stored, then the barrier; the next
+  // stage's LDS reads and the decode of step s + 2's scales overlap slice
+  // 7.  N was last read before the previous barrier.  Slice 0 of a step is
+  // dequantized either at the top of the step (256-row tiles) or, for
+  // 192-row tiles, under the second part of the previous step's slice 7
+  // (kTail; measured faster there, slower with 256 rows, whose slice-7
+  // MFMAs cannot hide the 8 extra VALU ops per MFMA).
   constexpr bool kTail = MI != 4;
   FragT<MI> f0, f1;
   auto step = [&](uint4 (&Nc)[2][1024], uint2 (&Ns)[2][2][256], int s) {
@@ -218,10 +206,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level_dma(Params p) {
     const int nxt2 = s + 2 < nsteps ? s + 2 : nsteps - 1;
     dma_codes_nv<MI>(Nc, src, nxt, wave);
     __builtin_amdgcn_sched_barrier(0);     // the DMA is issued before (is older than) ...
-    load_scales(1, nxt2);                  // ... the scale loads: the vmcnt waits rely on it
+    load_scales(nxt2);                     // ... the scale loads: the vmcnt wait relies on it
     __builtin_amdgcn_sched_barrier(0);     // keep the loads at the top of the step
-    wait_vmcnt<kDmaLoads + kScaleLoads>();  // step s + 1's scale bytes
-    decode_scales();
     if constexpr (!kTail) dequant_slice<0>(f0, a_raw, b_raw, a_sc, b_sc);
     pipelined_slice<0>(acc, f0, f1, a_raw, b_raw, a_sc, b_sc);
     pipelined_slice<1>(acc, f1, f0, a_raw, b_raw, a_sc, b_sc);
@@ -230,14 +216,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level_dma(Params p) {
     pipelined_slice<4>(acc, f0, f1, a_raw, b_raw, a_sc, b_sc);
     pipelined_slice<5>(acc, f1, f0, a_raw, b_raw, a_sc, b_sc);
     pipelined_slice<6>(acc, f0, f1, a_raw, b_raw, a_sc, b_sc);
+    // Nothing crosses these fences: without them the scheduler lifts the
+    // wait, the store and the barrier (which the MFMAs do not depend on)
+    // above the slices, and every step would stall on the DMA it has just
+    // issued.
+    __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<kScaleLoads>();              // the code DMA of step s + 1
     store_scales(Ns);
-    shift_scales();
     __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));   // this wave's LDS stores done
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
     read_stage(Nc, Ns);
+    wait_vmcnt<0>();                        // step s + 2's scale bytes (issued at the top)
+    decode_scales();
     if constexpr (kTail) {
       dequant_slice<0>(f0, a_raw, b_raw, a_sc, b_sc);
       mfma_slice(acc, f1);
@@ -247,16 +240,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level_dma(Params p) {
     }
   };
 
-  if constexpr (FMT == kUE) {
-    ue_tab[t] = static_cast<uint16_t>(scale_pair_f16<kUE>(static_cast<uint32_t>(t)) & 0xFFFFu);
-  }
-  load_scales(0, 0);
+  load_scales(0);
   dma_codes_nv<MI>(cst0, src, 0, wave);
   wait_vmcnt<0>();
-  if constexpr (FMT == kUE) ring_barrier();   // the table is written
   decode_scales();
   store_scales(sst0);
-  load_scales(0, nsteps > 1 ? 1 : 0);     // step 1's scales, decoded in step 0
+  load_scales(nsteps > 1 ? 1 : 0);       // step 1's scales, stored at the end of step 0
+  wait_vmcnt<0>();
+  decode_scales();
   ring_barrier();
   read_stage(cst0, sst0);
   if constexpr (kTail) dequant_slice<0>(f0, a_raw, b_raw, a_sc, b_sc);

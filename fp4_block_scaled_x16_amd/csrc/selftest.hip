@@ -130,7 +130,8 @@ __global__ __launch_bounds__(kSweepThreads) void k_sweep_scale(const uint32_t* _
 }
 
 // One thread per block-scale code s: the 16 E2M1 codes times s, with s in
-// the low and then in the high half of the scale pair.
+// the low and then in the high half of the scale pair, the pair taken from
+// bytes 0-1 and then from bytes 2-3 of a word.
 // The code words are made from `salt` (0 at run time) so that, as in the
 // GEMM, they are run-time values in vector registers; the fp16 results are
 // stored as whole 8-element vectors (element-wise stores through
@@ -141,23 +142,33 @@ __global__ __launch_bounds__(256) void k_gemm_decode(uint16_t* __restrict__ out,
   using namespace fp4gemm;
   const uint32_t s = threadIdx.x;
   constexpr uint32_t kCodes = FMT == kNV ? 0x7Fu : 256u;
-  uint16_t* o = out + s * 32;
+  uint16_t* o = out + s * 64;
   if (s >= kCodes) {
 #pragma unroll
-    for (int i = 0; i < 32; ++i) o[i] = 0;
+    for (int i = 0; i < 64; ++i) o[i] = 0;
     return;
   }
   const uint32_t other = (s + 1u + (s * 37u) % (kCodes - 1u)) % kCodes;   // != s
   const uint32_t lo = 0x76543210u ^ (salt * s), hi = 0xFEDCBA98u ^ (salt * s);
-  half8 v[4];
-  uint32_t pair = scale_pair_f16<FMT>(s | (other << 8));
+  // the scale pair from bytes 0-1 of a word (bytes 2-3 hold other codes),
+  // then from bytes 2-3
+  const uint32_t w0 = s | (other << 8) | ((other ^ 0x55u) % kCodes << 16);
+  const uint32_t w1 = other | (s << 8) | ((other ^ 0x2Au) % kCodes << 24);
+  half8 v[8];
+  uint32_t pair = scale_pair_f16<FMT, 0>(w0);
   v[0] = dequant8<0>(lo, pair);
   v[1] = dequant8<0>(hi, pair);
-  pair = scale_pair_f16<FMT>(other | (s << 8));
+  pair = scale_pair_f16<FMT, 0>(w1);
   v[2] = dequant8<1>(lo, pair);
   v[3] = dequant8<1>(hi, pair);
+  pair = scale_pair_f16<FMT, 2>((w0 << 16) | ((other ^ 0x33u) % kCodes));
+  v[4] = dequant8<0>(lo, pair);
+  v[5] = dequant8<0>(hi, pair);
+  pair = scale_pair_f16<FMT, 2>((w1 << 16) | ((other ^ 0x66u) % kCodes << 8));
+  v[6] = dequant8<1>(lo, pair);
+  v[7] = dequant8<1>(hi, pair);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) *reinterpret_cast<half8*>(o + 8 * q) = v[q];   // 16-byte aligned
+  for (int q = 0; q < 8; ++q) *reinterpret_cast<half8*>(o + 8 * q) = v[q];   // 16-byte aligned
 }
 
 }  // namespace

@@ -57,10 +57,12 @@ fp4_status fp4_selftest_sweep(int kind, const uint32_t* thresholds, int n,
  * fp4_selftest_gemm_decode -- the GEMM's exact operand decode for every
  * (block-scale code, E2M1 code) pair of a two-level format.
  *   format  FP4_NVFP4 (scale codes 0 .. 0x7E) or FP4_UE5M3 (0 .. 0xFF).
- *   out     device uint16 [256][2][16]: out[s][h][c] is the fp16 bit pattern
+ *   out     device uint16 [256][4][16]: out[s][v][c] is the fp16 bit pattern
  *           the decode gives for E2M1 code c with scale code s held in half
- *           h of the scale pair (the other half holds a different code);
- *           rows s beyond the format's codes are written as 0.
+ *           v & 1 of the scale pair (the other half holds a different code),
+ *           the pair read from bytes 0-1 (v < 2) or 2-3 (v >= 2) of a word
+ *           whose other bytes hold other codes; rows s beyond the format's
+ *           codes are written as 0.
  */
 fp4_status fp4_selftest_gemm_decode(fp4_format format, uint16_t* out, void* stream);
 

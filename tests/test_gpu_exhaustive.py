@@ -14,8 +14,9 @@ elements; the UE5M3 abstract for the unsigned E5M3 scale).
   oracle's encoders.
 * E2M1 x scale -> fp16 (the GEMM operand decode): all 16 codes times every
   E4M3 scale code (the FP4 and FP8 hardware converts, then the packed
-  multiply) and every UE5M3 scale code, with the scale in either half of the
-  pair, against the oracle's values rounded to fp16 (exact, checked).
+  multiply) and every UE5M3 scale code (its packed integer / fp16 decode),
+  with the scale in either half of a pair read from either half of a word,
+  against the oracle's values rounded to fp16 (exact, checked).
 """
 import numpy as np
 import pytest
@@ -79,13 +80,13 @@ def test_scale_encoder_exhaustive(kind, encode, n_codes, vmax):
     ("ue5m3", F.UE5M3_VALUES, 2.0 ** -5, 256),
 ])
 def test_gemm_operand_decode_exhaustive(fmt, values, shift, n_codes):
-    got = api.selftest_gemm_decode(fmt)                      # [256, 2, 16]
+    got = api.selftest_gemm_decode(fmt)                      # [256, 4, 16]
     e2m1 = F.e2m1_value(np.arange(16))                        # codes 0..15
     exact = values[:n_codes, None] * e2m1[None, :] * shift    # float64
     half = exact.astype(np.float16)
     assert np.array_equal(half.astype(np.float64), exact)     # premise: exact in fp16
     want = half.view(np.uint16)                               # code 8 gives -0
     assert want[1, 8] == 0x8000
-    for h in range(2):
-        assert np.array_equal(got[:n_codes, h], want), (fmt, h, np.argwhere(got[:n_codes, h] != want)[:5])
+    for v in range(4):      # scale in either half of a pair from bytes 0-1 or 2-3
+        assert np.array_equal(got[:n_codes, v], want), (fmt, v, np.argwhere(got[:n_codes, v] != want)[:5])
     assert not got[n_codes:].any()
