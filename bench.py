@@ -106,9 +106,10 @@ def counters_run(ops):
 
 
 def summarize_pmc(fetch_csv, write_csv, cfg):
-    """Per-launch HBM bytes of the GEMM kernel from FETCH_SIZE / WRITE_SIZE
-    (KiB per dispatch), each scaled by what the same counter reads for the
-    calibration kernel of known size."""
+    """Per-launch HBM bytes of every library kernel of the step from
+    FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each scaled by what the same
+    counter reads for the calibration kernel of known size; the GEMM line
+    (mean over its launches) is what the roofline's `traffic` reports."""
     import csv
 
     def per_dispatch(path, counter):
@@ -121,27 +122,32 @@ def summarize_pmc(fetch_csv, write_csv, cfg):
                 rows[key] = (r["Kernel_Name"], rows.get(key, ("", 0.0))[1] + float(r["Counter_Value"]))
         return [rows[k] for k in sorted(rows)]
 
+    def short(n):
+        n = n.replace("void ", "").replace("fp4gemm::", "").replace("(anonymous namespace)::", "")
+        return n.split("(")[0]
+
     out = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         d = per_dispatch(path, counter)
-        gemm = [v for (n, v) in d if "k_gemm" in n]
+        lib = [(short(n), v) for (n, v) in d if "k_gemm" in n or "k_quant" in n or "k_amax" in n]
         cal = [v for (n, v) in d if "elementwise" in n.lower() and "mul" in n.lower()]
-        if not gemm or not cal:
-            raise SystemExit("no GEMM or calibration dispatches in %s" % path)
+        if not lib or not cal:
+            raise SystemExit("no library or calibration dispatches in %s" % path)
         factor = CAL_BYTES / (np.mean(cal[-2:]) * 1024.0)     # bytes per counted byte
-        out[counter] = (gemm, factor)
+        out[counter] = (lib, factor)
     fetch, f_fac = out["FETCH_SIZE"]
     write, w_fac = out["WRITE_SIZE"]
-    names = ["fprop", "dgrad", "wgrad"][:len(fetch)]
     lines = ["kernel_source_sha256_16=%s" % source_hash(*GEMM_SOURCES),
              "calibration_fetch_factor=%.4f" % f_fac, "calibration_write_factor=%.4f" % w_fac]
-    tot = []
-    for i, n in enumerate(names):
-        fb, wb = fetch[i] * 1024.0 * f_fac, write[i] * 1024.0 * w_fac
-        tot.append(fb + wb)
-        lines.append("%s_fetch_bytes=%.0f" % (n, fb))
-        lines.append("%s_write_bytes=%.0f" % (n, wb))
-    lines.append("hbm_bytes_per_launch=%.0f" % float(np.mean(tot)))
+    gemm_tot = []
+    gnames = iter(["fprop", "dgrad", "wgrad"])
+    for (n, fv), (_, wv) in zip(fetch, write):
+        fb, wb = fv * 1024.0 * f_fac, wv * 1024.0 * w_fac
+        tag = next(gnames) if "k_gemm" in n else "quant"
+        if "k_gemm" in n:
+            gemm_tot.append(fb + wb)
+        lines.append("%s %s fetch_bytes=%.0f write_bytes=%.0f" % (tag, n, fb, wb))
+    lines.append("hbm_bytes_per_launch=%.0f" % float(np.mean(gemm_tot)))
     print("\n".join(lines))
 
 
@@ -168,7 +174,7 @@ def read_traffic(cfg, kernel_hash):
     vals = {}
     with open(path) as f:
         for line in f:
-            if "=" in line and not line.startswith("#"):
+            if "=" in line and " " not in line.split("=", 1)[0] and not line.startswith("#"):
                 k, v = line.split("=", 1)
                 vals[k.strip()] = v.strip()
     if vals.get("kernel_source_sha256_16") != kernel_hash:
@@ -500,14 +506,15 @@ def layer_main(args, dev):
     }))
 
 
-OP_TIMING_LAUNCHES = 40     # per op: R = 10 launches per graph, replayed 1 + 3 times
+OP_TIMING_LAUNCHES = 40     # per op and graph: R = 10 launches, replayed 1 + 3 times
 
 
 def summarize_trace(path):
     """Average duration of each library kernel over all its launches, and
-    over its last OP_TIMING_LAUNCHES launches: those of the per-op timing
-    graphs that produce `parts` (each kernel alone on the GPU), as opposed
-    to the step replays, where independent kernels run side by side."""
+    over its last 2 x OP_TIMING_LAUNCHES launches: those of the per-op timing
+    graphs (each kernel alone on the GPU; first after a cache-evicting write,
+    `parts`, then back to back, `parts_warm`), as opposed to the step
+    replays, where independent kernels run side by side."""
     import csv
     import collections
     by = collections.defaultdict(list)
@@ -518,12 +525,15 @@ def summarize_trace(path):
             if n.startswith(("k_gemm", "k_quant", "k_amax")):
                 t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
                 by[n].append((t0, (t1 - t0) / 1e3))
-    print("| kernel | calls | avg us, all | avg us, isolated (last %d) |" % OP_TIMING_LAUNCHES)
-    print("|---|---:|---:|---:|")
+    L = OP_TIMING_LAUNCHES
+    print("| kernel | calls | avg us, all | avg us, alone after a cache flush | avg us, alone back to back |")
+    print("|---|---:|---:|---:|---:|")
     for n, v in by.items():
         d = [x[1] for x in sorted(v)]
-        iso = d[-OP_TIMING_LAUNCHES:]
-        print("| %s | %d | %.1f | %.1f |" % (n, len(d), sum(d) / len(d), sum(iso) / len(iso)))
+        cold, warm = d[-2 * L:-L], d[-L:]
+        print("| %s | %d | %.1f | %.1f | %.1f |" % (n, len(d), sum(d) / len(d),
+                                                   sum(cold) / max(len(cold), 1),
+                                                   sum(warm) / max(len(warm), 1)))
 
 
 def format_comparison(dev):
