@@ -69,6 +69,9 @@ void copy_signs(const fp4_quant_desc* d, uint32_t (&out)[4]) {
 fp4_status check_bf16_input(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld) {
   if (rows < 0 || cols < 0) return fail(FP4_ERR_SHAPE, "negative size rows=%lld cols=%lld",
                                         (long long)rows, (long long)cols);
+  if (rows >= (int64_t(1) << 31) || cols >= (int64_t(1) << 31))
+    return fail(FP4_ERR_SHAPE, "rows=%lld and cols=%lld must be below 2^31", (long long)rows,
+                (long long)cols);
   if (ld < cols) return fail(FP4_ERR_ARG, "ld=%lld < cols=%lld", (long long)ld, (long long)cols);
   if (rows > 0 && cols > 0) {
     if (!x) return fail(FP4_ERR_ARG, "x is null");

@@ -29,7 +29,7 @@ constexpr int kStream = 512;        // streaming kernels (amax, rowwise, dequant
 // their LDS and memory latency; the RNE tile kernels prefer fewer).
 constexpr int kRowWgPerCu = 2;      // rowwise, RNE and SR
 constexpr int kColWgPerCuSR = 4;    // colwise with stochastic rounding
-constexpr int kTileWgPerCu = 2;     // colwise RNE, 2D
+constexpr int kTileWgPerCu = 3;     // colwise / dual RNE, 2D
 constexpr int kAmaxWgPerCu = 1;     // tensor amax (plain and 16-point RHT)
 
 // Same-address global atomics serialize (about 12 ns each on MI355X once
@@ -79,15 +79,16 @@ __device__ __forceinline__ void unpack8(const uint4& q, float* v) {
 // Quantize BS values (already in fp32, in block order) with the encode
 // scale; returns BS/8 packed code words (element i at bits 4 (i % 8) of
 // word i / 8).  `idx0` is the output-layout index of element 0 (SR only).
-// Counters: cnt[3] += #(|y| > 6); cnt[4] += #(x != 0) - #(code != 0), which
-// is the number of nonzero inputs coded as zero (a zero input always codes
-// to zero).  The element tests are wave ballots counted on the scalar unit,
-// so they are accumulated per wave (in lane 0's cnt) rather than per lane.
-template <int BS, int RND, bool CNT>
+// Counters, per lane: cnt[3] += #(|y| > 6); cnt[4] += NZX * #(x != 0) -
+// #(code != 0), the number of nonzero inputs coded as zero (a zero input
+// always codes to zero).  NZX = 2 lets one side of the dual quantizer count
+// the nonzero inputs for both sides (NZX = 0 on the other).  Per-lane
+// counts keep the tests on the vector unit; wave ballots would hold one
+// 64-bit mask per test in scalar registers, which spill.
+template <int BS, int RND, bool CNT, int NZX = 1>
 __device__ __forceinline__ void encode_block(const float* v, float s_enc_l, uint64_t idx0,
                                              uint64_t seed, uint64_t offset, uint32_t* words,
                                              uint32_t (&cnt)[5]) {
-  uint32_t sat = 0, nzx = 0, nzc = 0;
   // SR on 32-element blocks: one Philox group at a time keeps registers low
   constexpr int kGroupUnroll = (RND == FP4_SR && BS > 16) ? 1 : BS / 8;
 #pragma unroll kGroupUnroll
@@ -110,16 +111,11 @@ __device__ __forceinline__ void encode_block(const float* v, float s_enc_l, uint
     if constexpr (CNT) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        sat += __builtin_popcountll(__builtin_amdgcn_ballot_w64(fabsf(y[i]) > 6.0f));
-        nzx += __builtin_popcountll(__builtin_amdgcn_ballot_w64(v[q * 8 + i] != 0.0f));
+        cnt[3] += fabsf(y[i]) > 6.0f ? 1u : 0u;
+        if constexpr (NZX > 0) cnt[4] += v[q * 8 + i] != 0.0f ? static_cast<uint32_t>(NZX) : 0u;
       }
-      nzc += nonzero_codes(word);
+      cnt[4] -= nonzero_codes(word);
     }
-  }
-  if constexpr (CNT) {
-    const bool lead = (threadIdx.x & 63) == 0;
-    cnt[3] += lead ? sat : 0u;
-    cnt[4] += (lead ? nzx : 0u) - nzc;
   }
 }
 
@@ -356,9 +352,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
   if constexpr (FMT != kMX && !AMX) global_scales(*amax, target, s_enc_g, s_dec_g);
   if (s_dec_out && blockIdx.x == 0 && threadIdx.x == 0) *s_dec_out = s_dec_g;
 
-  const int64_t tiles_c = (cols + TC - 1) / TC;
-  const int64_t tiles_r = (rows + TR - 1) / TR;
-  const int64_t ntiles = tiles_c * tiles_r;
+  // tile counts fit in 32 bits (the host keeps rows, cols below 2^31)
+  const uint32_t tiles_c = static_cast<uint32_t>((cols + TC - 1) / TC);
+  const uint32_t tiles_r = static_cast<uint32_t>((rows + TR - 1) / TR);
+  const uint32_t ntiles = tiles_c * tiles_r;
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int grp = lane & 7;                  // row group handled in the compute phase
@@ -366,9 +363,9 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
   uint32_t cnt[5] = {0, 0, 0, 0, 0};
   float vmax = 0.0f;                         // AMX
 
-  for (int64_t tile_id = blockIdx.x; tile_id < ntiles; tile_id += gridDim.x) {
-    const int64_t tr = tile_id / tiles_c, tc = tile_id - tr * tiles_c;
-    const int64_t r0 = tr * TR, c0 = tc * TC;
+  for (uint32_t tile_id = blockIdx.x; tile_id < ntiles; tile_id += gridDim.x) {
+    const uint32_t tr = tile_id / tiles_c, tc = tile_id - tr * tiles_c;
+    const int64_t r0 = static_cast<int64_t>(tr) * TR, c0 = static_cast<int64_t>(tc) * TC;
     // load: TR rows x 8 chunks of 16 bytes
 #pragma unroll
     for (int k = 0; k < TR * 8 / kThreads; ++k) {
@@ -468,9 +465,10 @@ __attribute__((amdgpu_waves_per_eu(FMT == kMX ? 1 : 3))) void k_quant_dual(
     if (s_dec_t_out) *s_dec_t_out = s_dec_gt;
   }
 
-  const int64_t tiles_c = (cols + TC - 1) / TC;
-  const int64_t tiles_r = (rows + TR - 1) / TR;
-  const int64_t ntiles = tiles_c * tiles_r;
+  // tile counts fit in 32 bits (the host keeps rows, cols below 2^31)
+  const uint32_t tiles_c = static_cast<uint32_t>((cols + TC - 1) / TC);
+  const uint32_t tiles_r = static_cast<uint32_t>((rows + TR - 1) / TR);
+  const uint32_t ntiles = tiles_c * tiles_r;
   const uint64_t bpr = static_cast<uint64_t>(cols) / BS;   // rowwise blocks per row of X
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
@@ -480,12 +478,13 @@ __attribute__((amdgpu_waves_per_eu(FMT == kMX ? 1 : 3))) void k_quant_dual(
 
   // rowwise block b = t + k * kThreads of a tile: tile row b / BPR, columns
   // (b % BPR) * BS ..; blocks outside X load zeros and write nothing
-  auto load = [&](int64_t tile_id, uint4 (&q)[NB][BS / 8]) {
-    const int64_t tr = tile_id / tiles_c, tc = tile_id - tr * tiles_c;
+  auto load = [&](uint32_t tile_id, uint4 (&q)[NB][BS / 8]) {
+    const uint32_t tr = tile_id / tiles_c, tc = tile_id - tr * tiles_c;
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
       const int b = t + k * kThreads;
-      const int64_t r = tr * TR + b / BPR, c = tc * TC + (b % BPR) * BS;
+      const int64_t r = static_cast<int64_t>(tr) * TR + b / BPR;
+      const int64_t c = static_cast<int64_t>(tc) * TC + (b % BPR) * BS;
       const bool in = tile_id < ntiles && r < rows && c < cols;
 #pragma unroll
       for (int e = 0; e < BS / 8; ++e)
@@ -496,9 +495,9 @@ __attribute__((amdgpu_waves_per_eu(FMT == kMX ? 1 : 3))) void k_quant_dual(
 
   uint4 q[NB][BS / 8];
   load(blockIdx.x, q);
-  for (int64_t tile_id = blockIdx.x; tile_id < ntiles; tile_id += gridDim.x) {
-    const int64_t tr = tile_id / tiles_c, tc = tile_id - tr * tiles_c;
-    const int64_t r0 = tr * TR, c0 = tc * TC;
+  for (uint32_t tile_id = blockIdx.x; tile_id < ntiles; tile_id += gridDim.x) {
+    const uint32_t tr = tile_id / tiles_c, tc = tile_id - tr * tiles_c;
+    const int64_t r0 = static_cast<int64_t>(tr) * TR, c0 = static_cast<int64_t>(tc) * TC;
     uint4 nq[NB][BS / 8];
     load(tile_id + gridDim.x, nq);
 #pragma unroll
@@ -531,8 +530,10 @@ __attribute__((amdgpu_waves_per_eu(FMT == kMX ? 1 : 3))) void k_quant_dual(
         cnt[2] += sc_cnt[2];
       }
       uint32_t words[BS / 8];
-      encode_block<BS, RND, CNT>(v, s_enc_l, static_cast<uint64_t>(r) * cols + c, seed, offset,
-                                 words, cnt);
+      // without the RHT both sides quantize the same values: the nonzero
+      // inputs are counted here for both; the rotated side counts its own
+      encode_block<BS, RND, CNT, RHT ? 1 : 2>(v, s_enc_l, static_cast<uint64_t>(r) * cols + c,
+                                              seed, offset, words, cnt);
       if (in) {
         uint8_t* dst = codes + r * (cols >> 1) + (c >> 1);
         if constexpr (BS == 16) {
@@ -566,8 +567,8 @@ __attribute__((amdgpu_waves_per_eu(FMT == kMX ? 1 : 3))) void k_quant_dual(
         const uint32_t sc =
             scale_for_block<FMT>(amax_b, s_enc_gt, s_dec_gt, s_enc_l, cnt, scale_up_t);
         uint32_t words[BS / 8];
-        encode_block<BS, RND, CNT>(v, s_enc_l, static_cast<uint64_t>(c) * rows + row, seed_t,
-                                   offset_t, words, cnt);
+        encode_block<BS, RND, CNT, RHT ? 1 : 0>(v, s_enc_l, static_cast<uint64_t>(c) * rows + row,
+                                                seed_t, offset_t, words, cnt);
         uint8_t* dst = codes_t + c * (rows >> 1) + (row >> 1);
         if constexpr (BS == 16) {
           *reinterpret_cast<uint2*>(dst) = make_uint2(words[0], words[1]);
@@ -609,14 +610,16 @@ __global__ __launch_bounds__(kThreads) void k_quant_2d(
   global_scales(*amax, target, s_enc_g, s_dec_g);
   if (s_dec_out && blockIdx.x == 0 && threadIdx.x == 0) *s_dec_out = s_dec_g;
 
-  const int64_t reg_c = (cols + 63) / 64, reg_r = (rows + 63) / 64;
-  const int64_t nreg = reg_c * reg_r;
+  // region counts fit in 32 bits (the host keeps rows, cols below 2^31)
+  const uint32_t reg_c = static_cast<uint32_t>((cols + 63) / 64);
+  const uint32_t reg_r = static_cast<uint32_t>((rows + 63) / 64);
+  const uint32_t nreg = reg_c * reg_r;
   const int t = threadIdx.x;
   const int lr = t >> 2, tcol = t & 3;
   uint32_t cnt[5] = {0, 0, 0, 0, 0};
-  for (int64_t reg = blockIdx.x; reg < nreg; reg += gridDim.x) {
-    const int64_t rr = reg / reg_c, rc = reg - rr * reg_c;
-    const int64_t r0 = rr * 64, c0 = rc * 64;
+  for (uint32_t reg = blockIdx.x; reg < nreg; reg += gridDim.x) {
+    const uint32_t rr = reg / reg_c, rc = reg - rr * reg_c;
+    const int64_t r0 = static_cast<int64_t>(rr) * 64, c0 = static_cast<int64_t>(rc) * 64;
     const int64_t row = r0 + lr, col = c0 + tcol * 16;
     const bool valid = row < rows && col < cols;   // whole 16x16 tiles are in or out
     float v[16];

@@ -24,7 +24,8 @@
  *    call returns a nonzero fp4_status, enqueues nothing, and
  *    fp4_last_error() (thread-local) describes why.  A launch failure
  *    returns FP4_ERR_DEVICE.
- *  - Inputs must be finite; rows == 0 or cols == 0 is a valid empty call.
+ *  - Inputs must be finite; rows == 0 or cols == 0 is a valid empty call;
+ *    rows and cols of a bf16 input are below 2^31.
  *  - Calls that write the same output buffers on one stream are ordered by
  *    the stream; concurrent calls on different streams must not share
  *    output buffers.
