@@ -75,13 +75,13 @@ def load_library(path=LIB_PATH):
                            "(python fp4_block_scaled_x16_amd/build.py)" % path)
     lib = ctypes.CDLL(path)
     i64, vp, u32, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_uint32, ctypes.c_int
-    lib.fp4_amax.argtypes = [vp, i64, i64, i64, i32, u32, vp, vp]
+    lib.fp4_amax.argtypes = [ctypes.POINTER(QuantDesc), vp, i64, i64, i64, vp, vp]
     lib.fp4_quantize.argtypes = [ctypes.POINTER(QuantDesc), vp, i64, i64, i64, vp, vp, vp, vp,
                                  vp, vp, vp]
     lib.fp4_quantize_dual.argtypes = [ctypes.POINTER(QuantDesc), ctypes.POINTER(QuantDesc), vp, i64,
                                       i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.fp4_dequantize.argtypes = [i32, i32, i32, vp, vp, vp, i64, i64, vp, i32, vp]
-    lib.fp4_rht16.argtypes = [vp, i64, i64, i64, u32, vp, vp]
+    lib.fp4_rht16.argtypes = [ctypes.POINTER(QuantDesc), vp, i64, i64, i64, vp, vp]
     lib.fp4_gemm.argtypes = [ctypes.POINTER(Operand), ctypes.POINTER(Operand), i64, i64, i64, vp,
                              i64, i32, vp]
     lib.fp4_selftest_sweep.argtypes = [i32, vp, i32, vp, vp]
@@ -127,12 +127,21 @@ def _fmt(fmt):
 
 
 # ------------------------------------------------------------------ amax --
-def amax(x, rht=False, signs=0, out=None):
-    """Tensor amax (optionally of the column-RHT-rotated tensor) -> device fp32 [1]."""
+def _rht_desc(orient, rht, signs, rht_n):
+    s_lo, s_hi = _sign_words(signs)
+    return QuantDesc(NVFP4, BLOCK_1D, COLWISE if orient == "col" else ROWWISE, RNE, 0, 0,
+                     int(bool(rht)), s_lo, 448.0, 0, 0, SCALES_ROWMAJOR, int(rht_n), s_hi, 0)
+
+
+def amax(x, rht=False, signs=0, out=None, rht_n=16, orient="col"):
+    """Tensor amax -> device fp32 [1]; with rht, of the tensor rotated along
+    the blocked axis of `orient` ("col": N-row groups of each column, the
+    Wgrad operands; "row": N-column groups of each row, Fprop / Dgrad)."""
     x = _as_bf16_bits(x)
     out = torch.empty(1, dtype=torch.float32, device=x.device) if out is None else out
+    desc = _rht_desc(orient, rht, signs, rht_n)
     lib = load_library()
-    _check(lib.fp4_amax(_ptr(x), x.shape[0], x.shape[1], x.stride(0), int(bool(rht)), int(signs),
+    _check(lib.fp4_amax(ctypes.byref(desc), _ptr(x), x.shape[0], x.shape[1], x.stride(0),
                         _ptr(out), _stream(x.device)), "fp4_amax")
     return out
 
@@ -234,14 +243,17 @@ def _scales_1d(rows, blocks, layout, dev):
 
 def quantize_dual(x, fmt="nvfp4", rnd="rne", seed=0, offset=0, offset_t=None, rht=False, signs=0,
                   target=448.0, amax_in=None, amax_t_in=None, counters=None,
-                  scale_layout="rowmajor", scale_layout_t=None, rht_n=16, scale_round="rne"):
+                  scale_layout="rowmajor", scale_layout_t=None, rht_n=16, scale_round="rne",
+                  rht_row=False, signs_row=0, rht_n_row=16):
     """Rowwise and colwise 1D quantization of a bf16 [R, C] matrix from one
     read: returns (rowwise Quantized [R, C], colwise Quantized of X^T [C, R]).
 
     Both sides use `rnd` and `seed`; the colwise side uses offset_t (default
-    offset + 1), the RHT (rht/signs) and scale_layout_t (default
-    scale_layout).  amax_in / amax_t_in: None -> computed on the device, else
-    device fp32 [1] tensors read as the given amax of each side.
+    offset + 1), the RHT (rht/signs/rht_n, along the columns) and
+    scale_layout_t (default scale_layout); the rowwise side may rotate along
+    the rows (rht_row/signs_row, rht_n_row 4 or 16).  amax_in / amax_t_in:
+    None -> computed on the device, else device fp32 [1] tensors read as
+    the given amax of each side.
     """
     x = _as_bf16_bits(x)
     f = _fmt(fmt)
@@ -264,8 +276,10 @@ def quantize_dual(x, fmt="nvfp4", rnd="rne", seed=0, offset=0, offset_t=None, rh
     r = SR if rnd == "sr" else RNE
     s_lo, s_hi = _sign_words(signs)
     sr_mode = SCALE_ROUND[scale_round]
-    d_row = QuantDesc(f, BLOCK_1D, ROWWISE, r, int(seed), int(offset), 0, 0, float(target),
-                      int(amax_in is not None), 0, lay, 16, (ctypes.c_uint32 * 3)(), sr_mode)
+    r_lo, r_hi = _sign_words(signs_row)
+    d_row = QuantDesc(f, BLOCK_1D, ROWWISE, r, int(seed), int(offset), int(bool(rht_row)), r_lo,
+                      float(target), int(amax_in is not None), 0, lay, int(rht_n_row), r_hi,
+                      sr_mode)
     d_col = QuantDesc(f, BLOCK_1D, COLWISE, r, int(seed), int(offset_t), int(bool(rht)), s_lo,
                       float(target), int(amax_t_in is not None), 0, lay_t, int(rht_n), s_hi,
                       sr_mode)
@@ -298,12 +312,14 @@ def dequantize(q: Quantized, out_dtype=torch.float32):
 
 
 # ------------------------------------------------------------------- RHT --
-def rht16(x, signs):
+def rht16(x, signs, rht_n=16, orient="col"):
+    """The RHT alone (fp32 [R, C]) along the blocked axis of `orient`."""
     x = _as_bf16_bits(x)
     y = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    desc = _rht_desc(orient, True, signs, rht_n)
     lib = load_library()
-    _check(lib.fp4_rht16(_ptr(x), x.shape[0], x.shape[1], x.stride(0), int(signs), _ptr(y),
-                         _stream(x.device)), "fp4_rht16")
+    _check(lib.fp4_rht16(ctypes.byref(desc), _ptr(x), x.shape[0], x.shape[1], x.stride(0),
+                         _ptr(y), _stream(x.device)), "fp4_rht16")
     return y
 
 

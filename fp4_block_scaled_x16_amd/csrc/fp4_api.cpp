@@ -97,17 +97,24 @@ FP4_EXPORT const char* fp4_status_string(fp4_status s) {
 
 FP4_EXPORT const char* fp4_last_error(void) { return g_last_error.c_str(); }
 
-FP4_EXPORT fp4_status fp4_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int rht,
-                               uint32_t rht_signs, float* amax, void* stream) {
+FP4_EXPORT fp4_status fp4_amax(const fp4_quant_desc* d, const uint16_t* x, int64_t rows,
+                               int64_t cols, int64_t ld, float* amax, void* stream) {
+  if (!d) return fail(FP4_ERR_ARG, "desc is null");
+  if (d->orient != FP4_ROWWISE && d->orient != FP4_COLWISE)
+    return fail(FP4_ERR_ARG, "bad orient %d", (int)d->orient);
   fp4_status st = check_bf16_input(x, rows, cols, ld);
   if (st) return st;
   if (!amax) return fail(FP4_ERR_ARG, "amax is null");
-  if (rht && rows % 16) return fail(FP4_ERR_SHAPE, "rht needs rows %% 16 == 0 (rows=%lld)",
-                                    (long long)rows);
-  if (rht_signs > 0xFFFFu) return fail(FP4_ERR_ARG, "rht_signs must fit in 16 bits");
-  const uint32_t s4[4] = {rht_signs, 0u, 0u, 0u};
-  return device_status(fp4lib::launch_amax(x, rows, cols, ld, rht, 16, s4, amax,
-                                           static_cast<hipStream_t>(stream)),
+  st = check_rht(d, "desc");
+  if (st) return st;
+  const bool along_rows = d->orient == FP4_ROWWISE;
+  if (d->rht && (along_rows ? cols : rows) % rht_size(d))
+    return fail(FP4_ERR_SHAPE, "the rotated axis (%s=%lld) must be a multiple of rht_n=%d",
+                along_rows ? "cols" : "rows", (long long)(along_rows ? cols : rows), rht_size(d));
+  uint32_t s4[4];
+  copy_signs(d, s4);
+  return device_status(fp4lib::launch_amax(x, rows, cols, ld, d->rht, rht_size(d), s4, amax,
+                                           static_cast<hipStream_t>(stream), nullptr, along_rows),
                        "fp4_amax launch");
 }
 
@@ -131,7 +138,7 @@ FP4_EXPORT fp4_status fp4_quantize(const fp4_quant_desc* d, const uint16_t* x, i
   if (is2d && d->orient != FP4_ROWWISE) return fail(FP4_ERR_UNSUPPORTED, "2D16 blocks are ROWWISE only");
   if (d->scale_round != FP4_SCALE_RNE && d->scale_round != FP4_SCALE_UP)
     return fail(FP4_ERR_ARG, "bad scale_round %d", (int)d->scale_round);
-  if (d->rht && d->orient != FP4_COLWISE) return fail(FP4_ERR_UNSUPPORTED, "RHT needs COLWISE");
+  if (d->rht && is2d) return fail(FP4_ERR_UNSUPPORTED, "RHT needs 1D blocks");
   if (d->rht && d->format == FP4_MXFP4) return fail(FP4_ERR_UNSUPPORTED, "RHT needs NVFP4 or UE5M3");
   st = check_rht(d, "desc");
   if (st) return st;
@@ -149,6 +156,9 @@ FP4_EXPORT fp4_status fp4_quantize(const fp4_quant_desc* d, const uint16_t* x, i
                   (long long)rows, (long long)cols);
   } else if (d->orient == FP4_ROWWISE) {
     if (cols % bs) return fail(FP4_ERR_SHAPE, "cols=%lld must be a multiple of %d", (long long)cols, bs);
+    if (d->rht && cols % rht_size(d))
+      return fail(FP4_ERR_SHAPE, "cols=%lld must be a multiple of rht_n=%d", (long long)cols,
+                  rht_size(d));
   } else {
     if (rows % bs) return fail(FP4_ERR_SHAPE, "rows=%lld must be a multiple of %d", (long long)rows, bs);
     if (d->rht && rows % rht_size(d))
@@ -169,7 +179,8 @@ FP4_EXPORT fp4_status fp4_quantize(const fp4_quant_desc* d, const uint16_t* x, i
   if (two_level && !d->amax_given) {
     uint32_t s4[4];
     copy_signs(d, s4);
-    hipError_t e = fp4lib::launch_amax(x, rows, cols, ld, d->rht, rht_size(d), s4, amax, s);
+    hipError_t e = fp4lib::launch_amax(x, rows, cols, ld, d->rht, rht_size(d), s4, amax, s,
+                                       nullptr, d->orient == FP4_ROWWISE);
     if (e != hipSuccess) return device_status(e, "fp4_quantize amax launch");
   }
   fp4lib::QuantArgs a{};
@@ -234,9 +245,13 @@ FP4_EXPORT fp4_status fp4_quantize_dual(const fp4_quant_desc* rd, const fp4_quan
     return fail(FP4_ERR_UNSUPPORTED, "descs must be ROWWISE then COLWISE");
   if (rd->format != cd->format) return fail(FP4_ERR_UNSUPPORTED, "the two formats differ");
   if (rd->round != cd->round) return fail(FP4_ERR_UNSUPPORTED, "the two rounding modes differ");
-  if (rd->rht) return fail(FP4_ERR_UNSUPPORTED, "RHT needs COLWISE");
-  if (cd->rht && cd->format == FP4_MXFP4) return fail(FP4_ERR_UNSUPPORTED, "RHT needs NVFP4 or UE5M3");
-  const fp4_status st0 = check_rht(cd, "colwise");
+  if ((rd->rht || cd->rht) && cd->format == FP4_MXFP4)
+    return fail(FP4_ERR_UNSUPPORTED, "RHT needs NVFP4 or UE5M3");
+  if (rd->rht && rht_size(rd) != 4 && rht_size(rd) != 16)
+    return fail(FP4_ERR_UNSUPPORTED, "rowwise RHT of the dual quantizer: rht_n must be 4 or 16");
+  fp4_status st0 = check_rht(rd, "rowwise");
+  if (st0) return st0;
+  st0 = check_rht(cd, "colwise");
   if (st0) return st0;
   fp4_status st = check_bf16_input(x, rows, cols, ld);
   if (st) return st;
@@ -247,6 +262,9 @@ FP4_EXPORT fp4_status fp4_quantize_dual(const fp4_quant_desc* rd, const fp4_quan
   if (cd->rht && rows % rht_size(cd))
     return fail(FP4_ERR_SHAPE, "rows=%lld must be a multiple of rht_n=%d", (long long)rows,
                 rht_size(cd));
+  if (rd->rht && cols % rht_size(rd))
+    return fail(FP4_ERR_SHAPE, "cols=%lld must be a multiple of rht_n=%d", (long long)cols,
+                rht_size(rd));
   const bool two_level = rd->format != FP4_MXFP4;
   const bool empty = rows == 0 || cols == 0;
   if (!empty) {
@@ -259,14 +277,14 @@ FP4_EXPORT fp4_status fp4_quantize_dual(const fp4_quant_desc* rd, const fp4_quan
   }
   if (two_level) {
     if (!amax || !amax_t) return fail(FP4_ERR_ARG, "amax/amax_t is null");
-    if (amax == amax_t && (rd->amax_given != cd->amax_given || cd->rht))
+    if (amax == amax_t && (rd->amax_given != cd->amax_given || cd->rht || rd->rht))
       return fail(FP4_ERR_ARG, "amax and amax_t may share a buffer only without RHT and with "
                                "the same amax_given");
   }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   // both amaxes wanted with the 16-point RHT on the colwise side: one read
-  const bool fused = two_level && !rd->amax_given && !cd->amax_given && cd->rht &&
+  const bool fused = two_level && !rd->amax_given && !cd->amax_given && cd->rht && !rd->rht &&
                      rht_size(cd) == 16 && amax != amax_t;
   if (fused) {
     uint32_t s4[4];
@@ -275,8 +293,10 @@ FP4_EXPORT fp4_status fp4_quantize_dual(const fp4_quant_desc* rd, const fp4_quan
     if (e != hipSuccess) return device_status(e, "fp4_quantize_dual amax launch");
   }
   if (two_level && !rd->amax_given && !fused) {
-    const uint32_t none[4] = {0u, 0u, 0u, 0u};
-    hipError_t e = fp4lib::launch_amax(x, rows, cols, ld, 0, 16, none, amax, s);
+    uint32_t s4[4];
+    copy_signs(rd, s4);
+    hipError_t e = fp4lib::launch_amax(x, rows, cols, ld, rd->rht, rht_size(rd), s4, amax, s,
+                                       nullptr, true);
     if (e != hipSuccess) return device_status(e, "fp4_quantize_dual amax launch");
   }
   if (two_level && !cd->amax_given && !fused && !(amax_t == amax && !rd->amax_given)) {
@@ -343,17 +363,28 @@ FP4_EXPORT fp4_status fp4_dequantize(fp4_format format, fp4_block block,
                        "fp4_dequantize launch");
 }
 
-FP4_EXPORT fp4_status fp4_rht16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
-                                uint32_t rht_signs, float* y, void* stream) {
+FP4_EXPORT fp4_status fp4_rht16(const fp4_quant_desc* d, const uint16_t* x, int64_t rows,
+                                int64_t cols, int64_t ld, float* y, void* stream) {
+  if (!d) return fail(FP4_ERR_ARG, "desc is null");
+  if (d->orient != FP4_ROWWISE && d->orient != FP4_COLWISE)
+    return fail(FP4_ERR_ARG, "bad orient %d", (int)d->orient);
   fp4_status st = check_bf16_input(x, rows, cols, ld);
   if (st) return st;
-  if (rows % 16) return fail(FP4_ERR_SHAPE, "rows=%lld must be a multiple of 16", (long long)rows);
-  if (rht_signs > 0xFFFFu) return fail(FP4_ERR_ARG, "rht_signs must fit in 16 bits");
-  if (rows > 0 && cols > 0 && (!y || (reinterpret_cast<uintptr_t>(y) & 7u)))
-    return fail(FP4_ERR_ARG, "y must be non-null and 8-byte aligned");
+  fp4_quant_desc on = *d;
+  on.rht = 1;                                  // the transform itself is always applied
+  st = check_rht(&on, "desc");
+  if (st) return st;
+  const bool along_rows = d->orient == FP4_ROWWISE;
+  if ((along_rows ? cols : rows) % rht_size(d))
+    return fail(FP4_ERR_SHAPE, "the rotated axis (%s=%lld) must be a multiple of rht_n=%d",
+                along_rows ? "cols" : "rows", (long long)(along_rows ? cols : rows), rht_size(d));
+  if (rows > 0 && cols > 0 && (!y || (reinterpret_cast<uintptr_t>(y) & 15u)))
+    return fail(FP4_ERR_ARG, "y must be non-null and 16-byte aligned");
   if (rows == 0 || cols == 0) return ok();
-  return device_status(fp4lib::launch_rht16(x, rows, cols, ld, rht_signs, y,
-                                            static_cast<hipStream_t>(stream)),
+  uint32_t s4[4];
+  copy_signs(d, s4);
+  return device_status(fp4lib::launch_rht(x, rows, cols, ld, rht_size(d), s4, along_rows, y,
+                                          static_cast<hipStream_t>(stream)),
                        "fp4_rht16 launch");
 }
 

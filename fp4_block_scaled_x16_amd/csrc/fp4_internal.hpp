@@ -41,10 +41,12 @@ struct GemmOperand {
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 
-// amax_plain (optional, rht with N = 16 only): also max |x| from the same read.
+// amax_plain (optional, rht with N = 16 along the columns only): also max |x|
+// from the same read.  along_rows: the rotation runs along the rows of x
+// (rowwise quantization) instead of along its columns.
 hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int rht,
                        int rht_n, const uint32_t (&signs)[4], float* amax, hipStream_t s,
-                       float* amax_plain = nullptr);
+                       float* amax_plain = nullptr, bool along_rows = false);
 hipError_t launch_quant_row(const QuantArgs& a, hipStream_t s);
 hipError_t launch_quant_col(const QuantArgs& a, hipStream_t s);
 hipError_t launch_quant_2d(const QuantArgs& a, hipStream_t s);
@@ -54,8 +56,9 @@ hipError_t launch_quant_dual(const QuantArgs& row, const QuantArgs& col, hipStre
 hipError_t launch_dequant(int format, int block2d, int tiled, const uint8_t* codes,
                           const uint8_t* scales, const float* s_dec, int64_t rows, int64_t cols,
                           void* out, int out_fp32, hipStream_t s);
-hipError_t launch_rht16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, uint32_t signs,
-                        float* y, hipStream_t s);
+// The RHT of size rht_n (0 means 16) alone, along the rows or the columns.
+hipError_t launch_rht(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int rht_n,
+                      const uint32_t (&signs)[4], bool along_rows, float* y, hipStream_t s);
 hipError_t launch_gemm(int format, const GemmOperand& A, const GemmOperand& B, int64_t M, int64_t N,
                        int64_t K, float* D, int64_t ldd, int accumulate, hipStream_t s);
 // Exhaustive conversion checks (selftest.hip).

@@ -258,13 +258,18 @@ __global__ __launch_bounds__(kStream) void k_amax_rht(const uint16_t* __restrict
 }
 
 // ------------------------------------------------------ rowwise 1D ------
-// One thread per block of BS consecutive elements of a row.
-template <int FMT, int RND, bool CNT>
+// One thread per block of BS consecutive elements of a row.  With RHT
+// (16-element blocks) every N-element group of a row is rotated first
+// (NVFP4 paper §4.2: the Fprop / Dgrad operands, rotated along K): the
+// grid stride is a multiple of 64, so lane l handles blocks i = l mod 64,
+// and the N / 16 blocks of a group (cols % N == 0) sit on consecutive
+// lanes with the same bits above N / 16, which rht_n combines by shuffles.
+template <int FMT, int RND, bool CNT, bool RHT = false>
 __global__ __launch_bounds__(kStream) void k_quant_row(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, const float* __restrict__ amax,
     float target, float* __restrict__ s_dec_out, uint64_t seed, uint64_t offset,
-    fp4_counters* __restrict__ counters, int tiled, int scale_up) {
+    fp4_counters* __restrict__ counters, int tiled, int scale_up, RhtN rht) {
   constexpr int BS = FMT == kMX ? 32 : 16;
   float s_enc_g = 1.0f, s_dec_g = 1.0f;
   if constexpr (FMT != kMX) global_scales(*amax, target, s_enc_g, s_dec_g);
@@ -303,6 +308,7 @@ __global__ __launch_bounds__(kStream) void k_quant_row(
     float v[BS];
 #pragma unroll
     for (int k = 0; k < BS / 8; ++k) unpack8(q[k], v + 8 * k);
+    if constexpr (RHT && BS == 16) rht_n(v, rht, static_cast<int>(threadIdx.x & 7));
     float amax_b = 0.0f;
 #pragma unroll
     for (int k = 0; k < BS; ++k) amax_b = fmaxf(amax_b, fabsf(v[k]));
@@ -435,8 +441,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
 // then runs from LDS exactly as k_quant_col.  The next tile's loads are
 // issued before the current tile is encoded.  Both halves use the same
 // rounding mode, each with its own tensor scale, Philox key and counter
-// offset, and output layout.
-template <int FMT, int RND, bool RHT, bool CNT>
+// offset, and output layout.  RHT rotates the colwise side's N-row groups
+// (any N); RRHT rotates the rowwise side's blocks along the row (N = 4 or
+// 16, within a block: the Fprop / Dgrad operands, §4.2).
+template <int FMT, int RND, bool RHT, bool CNT, bool RRHT = false>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(FMT == kMX ? 1 : 3))) void k_quant_dual(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
@@ -445,7 +453,8 @@ __attribute__((amdgpu_waves_per_eu(FMT == kMX ? 1 : 3))) void k_quant_dual(
     const float* __restrict__ amax_t, float target, float target_t,
     float* __restrict__ s_dec_out, float* __restrict__ s_dec_t_out, uint64_t seed,
     uint64_t offset, uint64_t seed_t, uint64_t offset_t, RhtN rht,
-    fp4_counters* __restrict__ counters, int tiled, int tiled_t, int scale_up, int scale_up_t) {
+    fp4_counters* __restrict__ counters, int tiled, int tiled_t, int scale_up, int scale_up_t,
+    RhtN rht_row) {
   constexpr int BS = FMT == kMX ? 32 : 16;
   constexpr int TR = 8 * BS;        // tile rows (8 groups)
   constexpr int TC = 64;            // tile columns
@@ -516,6 +525,7 @@ __attribute__((amdgpu_waves_per_eu(FMT == kMX ? 1 : 3))) void k_quant_dual(
       float v[BS];
 #pragma unroll
       for (int e = 0; e < BS / 8; ++e) unpack8(q[k][e], v + 8 * e);
+      if constexpr (RRHT && BS == 16) rht_n(v, rht_row, 0);   // N <= 16: no shuffles
       float amax_b = 0.0f;
 #pragma unroll
       for (int e = 0; e < BS; ++e) amax_b = fmaxf(amax_b, fabsf(v[e]));
@@ -531,9 +541,9 @@ __attribute__((amdgpu_waves_per_eu(FMT == kMX ? 1 : 3))) void k_quant_dual(
       }
       uint32_t words[BS / 8];
       // without the RHT both sides quantize the same values: the nonzero
-      // inputs are counted here for both; the rotated side counts its own
-      encode_block<BS, RND, CNT, RHT ? 1 : 2>(v, s_enc_l, static_cast<uint64_t>(r) * cols + c,
-                                              seed, offset, words, cnt);
+      // inputs are counted here for both; a rotated side counts its own
+      encode_block<BS, RND, CNT, (RHT || RRHT) ? 1 : 2>(
+          v, s_enc_l, static_cast<uint64_t>(r) * cols + c, seed, offset, words, cnt);
       if (in) {
         uint8_t* dst = codes + r * (cols >> 1) + (c >> 1);
         if constexpr (BS == 16) {
@@ -567,8 +577,8 @@ __attribute__((amdgpu_waves_per_eu(FMT == kMX ? 1 : 3))) void k_quant_dual(
         const uint32_t sc =
             scale_for_block<FMT>(amax_b, s_enc_gt, s_dec_gt, s_enc_l, cnt, scale_up_t);
         uint32_t words[BS / 8];
-        encode_block<BS, RND, CNT, RHT ? 1 : 0>(v, s_enc_l, static_cast<uint64_t>(c) * rows + row,
-                                                seed_t, offset_t, words, cnt);
+        encode_block<BS, RND, CNT, (RHT || RRHT) ? 1 : 0>(
+            v, s_enc_l, static_cast<uint64_t>(c) * rows + row, seed_t, offset_t, words, cnt);
         uint8_t* dst = codes_t + c * (rows >> 1) + (row >> 1);
         if constexpr (BS == 16) {
           *reinterpret_cast<uint2*>(dst) = make_uint2(words[0], words[1]);
@@ -777,6 +787,52 @@ __global__ __launch_bounds__(kStream) void k_rht16(const uint16_t* __restrict__ 
   }
 }
 
+// ------------------------------------------------ RHT of size N, alone --
+// fl32(1/sqrt(N)) D_r H_N on every N-element group along the rows of x
+// (ROW: N consecutive columns of a row) or along its columns (COL: N
+// consecutive rows of a column), as the quantizers apply it.  One thread
+// per 16-element segment; the N / 16 segments of a group are consecutive
+// segments of one line, on consecutive lanes (segment s on lane s mod 64:
+// the grid stride is a multiple of 64), combined by rht_n's shuffles.
+// AMX: the largest |value| goes to *amax_out (fp32 bits, atomic max), else
+// the values are written to y ([rows, cols] fp32, row-major).
+template <bool ROW, bool AMX>
+__global__ __launch_bounds__(kStream) void k_rht_gen(const uint16_t* __restrict__ x, int64_t rows,
+                                                     int64_t cols, int64_t ld, RhtN rht,
+                                                     float* __restrict__ y,
+                                                     uint32_t* __restrict__ amax_out) {
+  const uint64_t seg_per_line = static_cast<uint64_t>(ROW ? cols : rows) >> 4;
+  const uint64_t nseg = seg_per_line * static_cast<uint64_t>(ROW ? rows : cols);
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kStream;
+  float m = 0.0f;
+  for (uint64_t sg = static_cast<uint64_t>(blockIdx.x) * kStream + threadIdx.x; sg < nseg;
+       sg += stride) {
+    const uint64_t line = sg / seg_per_line, j = sg - line * seg_per_line;
+    float v[16];
+    if constexpr (ROW) {
+      const uint4* src = reinterpret_cast<const uint4*>(x + line * ld + 16 * j);
+      unpack8(src[0], v);
+      unpack8(src[1], v + 8);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) v[k] = bf16_to_f32(x[(16 * j + k) * ld + line]);
+    }
+    rht_n(v, rht, static_cast<int>(threadIdx.x & 7));
+    if constexpr (AMX) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) m = fmaxf(m, fabsf(v[k]));
+    } else if constexpr (ROW) {
+      float4* dst = reinterpret_cast<float4*>(y + line * static_cast<uint64_t>(cols) + 16 * j);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) y[(16 * j + k) * static_cast<uint64_t>(cols) + line] = v[k];
+    }
+  }
+  if constexpr (AMX) flush_max<kStream>(__float_as_uint(m), amax_out);
+}
+
 // Persistent grid: enough workgroups of `threads` for the work, at most
 // per_cu per CU.
 int grid_for(uint64_t work_items, int per_cu, int threads = kStream) {
@@ -815,14 +871,19 @@ static RhtN make_rht(int n, const uint32_t (&s4)[4]) {
 
 hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int rht,
                        int rht_n, const uint32_t (&signs)[4], float* amax, hipStream_t s,
-                       float* amax_plain) {
+                       float* amax_plain, bool along_rows) {
   uint32_t* out = reinterpret_cast<uint32_t*>(amax);
   uint32_t* out_plain = reinterpret_cast<uint32_t*>(amax_plain);
   hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(1), 0, s, out, 0u);
   if (out_plain) hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(1), 0, s, out_plain, 0u);
   if (rows > 0 && cols > 0) {
     const RhtN r = make_rht(rht_n, signs);
-    if (rht && r.n == 16) {
+    if (rht && along_rows) {
+      // rotation along the rows (rowwise quantization): the generic kernel
+      const uint64_t n = static_cast<uint64_t>(rows) * static_cast<uint64_t>(cols / 16);
+      hipLaunchKernelGGL((k_rht_gen<true, true>), dim3(grid_for(n, kAmaxWgPerCu)), dim3(kStream),
+                         0, s, x, rows, cols, ld, r, nullptr, out);
+    } else if (rht && r.n == 16) {
       const uint64_t n = static_cast<uint64_t>(rows / 16) * static_cast<uint64_t>(cols / 2);
       hipLaunchKernelGGL(k_amax_rht, dim3(grid_for(n, kAmaxWgPerCu)), dim3(kStream), 0, s, x, rows, cols,
                          ld, signs[0], out, out_plain);
@@ -847,10 +908,19 @@ template <int FMT, int RND, bool CNT>
 static void row_launch(const QuantArgs& a, hipStream_t s) {
   constexpr int BS = FMT == kMX ? 32 : 16;
   const uint64_t n = static_cast<uint64_t>(a.rows) * static_cast<uint64_t>(a.cols / BS);
+  const RhtN r = make_rht(a.rht_n, a.rht_signs);
+  if constexpr (FMT != kMX) {
+    if (a.rht) {
+      hipLaunchKernelGGL((k_quant_row<FMT, RND, CNT, true>), dim3(grid_for(n, kRowWgPerCu)),
+                         dim3(kStream), 0, s, a.x, a.rows, a.cols, a.ld, a.codes, a.scales, a.amax,
+                         a.target, a.s_dec, a.seed, a.offset, a.counters, a.tiled, a.scale_up, r);
+      return;
+    }
+  }
   hipLaunchKernelGGL((k_quant_row<FMT, RND, CNT>), dim3(grid_for(n, kRowWgPerCu)),
                      dim3(kStream), 0, s,
                      a.x, a.rows, a.cols, a.ld, a.codes, a.scales, a.amax, a.target, a.s_dec,
-                     a.seed, a.offset, a.counters, a.tiled, a.scale_up);
+                     a.seed, a.offset, a.counters, a.tiled, a.scale_up, r);
 }
 
 template <int FMT, int RND>
@@ -914,24 +984,32 @@ hipError_t launch_quant_col(const QuantArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int FMT, int RND, bool RHT, bool CNT>
+template <int FMT, int RND, bool RHT, bool CNT, bool RRHT>
 static void dual_launch(const QuantArgs& a, const QuantArgs& b, hipStream_t s) {
   constexpr int BS = FMT == kMX ? 32 : 16;
   const int64_t tiles = ((a.rows + 8 * BS - 1) / (8 * BS)) * ((a.cols + 63) / 64);
   const int64_t cap = static_cast<int64_t>(device_cu_count()) *
                       (RND == FP4_SR ? kColWgPerCuSR : kTileWgPerCu);
   const int grid = static_cast<int>(tiles < cap ? (tiles > 0 ? tiles : 1) : cap);
-  hipLaunchKernelGGL((k_quant_dual<FMT, RND, RHT, CNT>), dim3(grid), dim3(kThreads), 0, s, a.x,
-                     a.rows, a.cols, a.ld, a.codes, a.scales, b.codes, b.scales, a.amax, b.amax,
-                     a.target, b.target, a.s_dec, b.s_dec, a.seed, a.offset, b.seed, b.offset,
-                     make_rht(b.rht_n, b.rht_signs), a.counters, a.tiled, b.tiled, a.scale_up,
-                     b.scale_up);
+  hipLaunchKernelGGL((k_quant_dual<FMT, RND, RHT, CNT, RRHT>), dim3(grid), dim3(kThreads), 0, s,
+                     a.x, a.rows, a.cols, a.ld, a.codes, a.scales, b.codes, b.scales, a.amax,
+                     b.amax, a.target, b.target, a.s_dec, b.s_dec, a.seed, a.offset, b.seed,
+                     b.offset, make_rht(b.rht_n, b.rht_signs), a.counters, a.tiled, b.tiled,
+                     a.scale_up, b.scale_up, make_rht(a.rht_n, a.rht_signs));
 }
 
 template <int FMT, int RND, bool RHT>
 static void dual_dispatch_cnt(const QuantArgs& a, const QuantArgs& b, hipStream_t s) {
-  if (a.counters) dual_launch<FMT, RND, RHT, true>(a, b, s);
-  else dual_launch<FMT, RND, RHT, false>(a, b, s);
+  // the rowwise side's RHT (a.rht) only with the two-level formats
+  if constexpr (FMT != kMX) {
+    if (a.rht) {
+      if (a.counters) dual_launch<FMT, RND, RHT, true, true>(a, b, s);
+      else dual_launch<FMT, RND, RHT, false, true>(a, b, s);
+      return;
+    }
+  }
+  if (a.counters) dual_launch<FMT, RND, RHT, true, false>(a, b, s);
+  else dual_launch<FMT, RND, RHT, false, false>(a, b, s);
 }
 
 template <int FMT, int RND>
@@ -1015,12 +1093,24 @@ hipError_t launch_dequant(int format, int block2d, int tiled, const uint8_t* cod
   return hipGetLastError();
 }
 
-hipError_t launch_rht16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, uint32_t signs,
-                        float* y, hipStream_t s) {
+hipError_t launch_rht(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int rht_n,
+                      const uint32_t (&signs)[4], bool along_rows, float* y, hipStream_t s) {
   if (rows > 0 && cols > 0) {
-    const uint64_t n = static_cast<uint64_t>(rows / 16) * static_cast<uint64_t>(cols / 2);
-    hipLaunchKernelGGL(k_rht16, dim3(grid_for(n, 2)), dim3(kStream), 0, s, x, rows, cols, ld,
-                       signs, y);
+    const RhtN r = make_rht(rht_n, signs);
+    if (!along_rows && r.n == 16) {
+      const uint64_t n = static_cast<uint64_t>(rows / 16) * static_cast<uint64_t>(cols / 2);
+      hipLaunchKernelGGL(k_rht16, dim3(grid_for(n, 2)), dim3(kStream), 0, s, x, rows, cols, ld,
+                         signs[0], y);
+    } else {
+      const uint64_t n = static_cast<uint64_t>(along_rows ? rows : cols) *
+                         static_cast<uint64_t>((along_rows ? cols : rows) / 16);
+      if (along_rows)
+        hipLaunchKernelGGL((k_rht_gen<true, false>), dim3(grid_for(n, 2)), dim3(kStream), 0, s, x,
+                           rows, cols, ld, r, y, nullptr);
+      else
+        hipLaunchKernelGGL((k_rht_gen<false, false>), dim3(grid_for(n, 2)), dim3(kStream), 0, s,
+                           x, rows, cols, ld, r, y, nullptr);
+    }
   }
   return hipGetLastError();
 }

@@ -16,6 +16,15 @@ This class composes the library's entry points into that layer:
                 dX = Dgrad(dY, W^T)                       fp32 [tokens, in]
                 main_grad += Wgrad(dY^T, X^T)             fp32 [out, in]
 
+With rht_kd (§4.2: Fprop and Dgrad "may also benefit" from the RHT) the
+Fprop and Dgrad operands are rotated along their K axis as well: X and W
+rowwise along the input features (Fprop), dY rowwise and W colwise along
+the output features (Dgrad), each pair with the same signs so the rotation
+cancels in the product.  W is then quantized in 1D blocks (a rowwise and a
+colwise code matrix, rotated along different axes) instead of 16x16 tiles:
+one rotated W cannot serve both products (§4.3 on keeping Fprop and Dgrad
+consistent; the rotated layer trades that consistency for the rotation).
+
 With act_block = "2d" (the 2D-block FP4 recipe) X and dY are quantized in
 16x16 blocks as well, each once with its transpose (dY with stochastic
 rounding, the same random bits for both orientations), so every operand a
@@ -54,6 +63,9 @@ class Recipe:
     scale_layout: str = "tiled"   # storage of the 1D block scales
     act_block: str = "1d"         # "1d" (1x16 / 1x32) or "2d" (16x16) for X and dY
     scale_round: str = "rne"      # block scales: "rne" or "up" (truncation-free)
+    rht_kd: bool = False          # RHT along K on the Fprop / Dgrad operands too
+    rht_kd_n: int = 16            # its size N: 4 or 16
+    rht_kd_signs: int = 0         # its N-bit sign mask
 
     @property
     def two_level(self):
@@ -71,15 +83,17 @@ class QuantizedLinear:
     def __init__(self, weight: torch.Tensor, recipe: Recipe = Recipe()):
         if weight.dim() != 2:
             raise ValueError("weight must be [out, in]")
-        if recipe.act_block == "2d" and (recipe.rht or not recipe.two_level):
+        if recipe.act_block == "2d" and (recipe.rht or recipe.rht_kd or not recipe.two_level):
             raise ValueError("2D activation blocks need NVFP4 or UE5M3 and no RHT")
+        if recipe.rht_kd and (not recipe.two_level or recipe.rht_kd_n not in (4, 16)):
+            raise ValueError("the RHT along K needs NVFP4 or UE5M3 and N = 4 or 16")
         self.weight = weight
         self.recipe = recipe
         self.out_features, self.in_features = weight.shape
         dev = weight.device
         self.main_grad = torch.zeros((self.out_features, self.in_features), dtype=torch.float32,
                                      device=dev)
-        names = ("x", "x_t", "w", "dy", "dy_t")
+        names = ("x", "x_t", "w", "w_t", "dy", "dy_t")
         self.amax = {n: torch.zeros(1, dtype=torch.float32, device=dev) for n in names}
         self.step = 0
         self.counters = api.new_counters(dev)
@@ -91,10 +105,11 @@ class QuantizedLinear:
 
     def _amax_args(self, x, name, rht):
         """amax buffers (rowwise, colwise) for a dual quantization of x,
-        refreshed on this step if due; without RHT both sides share one
-        buffer.  MXFP4 has none.  With the RHT a refresh leaves both to the
-        quantizer (None, None: the plain and the rotated amax, from one read
-        for N = 16), and `_keep_amax` keeps what it computed."""
+        refreshed on this step if due; without an RHT on either side both
+        share one buffer.  MXFP4 has none.  With an RHT a refresh leaves both
+        to the quantizer (None, None: each side's amax in its own rotated
+        space; the plain and the 16-point-rotated one from one read), and
+        `_keep_amax` keeps what it computed."""
         r = self.recipe
         if not r.two_level:
             return None, None
@@ -104,6 +119,13 @@ class QuantizedLinear:
             api.amax(x, out=self.amax[name])
         return self.amax[name], self.amax[name + "_t" if rht else name]
 
+    def _kd(self):
+        """Keyword arguments of the rowwise side's RHT along K (or none)."""
+        r = self.recipe
+        if not r.rht_kd:
+            return {}
+        return dict(rht_row=True, signs_row=r.rht_kd_signs, rht_n_row=r.rht_kd_n)
+
     def _keep_amax(self, name, q, q_t, given):
         if self.recipe.two_level and given is None:
             self.amax[name], self.amax[name + "_t"] = q.amax, q_t.amax
@@ -112,7 +134,7 @@ class QuantizedLinear:
         r = self.recipe
         if x.dim() != 2 or x.shape[1] != self.in_features:
             raise ValueError("x must be [tokens, in_features]")
-        am, am_t = self._amax_args(x, "x", r.rht)
+        am, am_t = self._amax_args(x, "x", r.rht or r.rht_kd)
         if r.act_block == "2d":
             qx2 = api.quantize(x, r.fmt, block="2d", emit_transpose=True, target=r.target_x,
                                amax_in=am, counters=self.counters, scale_round=r.scale_round)
@@ -121,10 +143,21 @@ class QuantizedLinear:
             qx, qx_t = api.quantize_dual(x, r.fmt, rht=r.rht, signs=r.rht_signs, rht_n=r.rht_n,
                                          target=r.target_x, amax_in=am, amax_t_in=am_t,
                                          counters=self.counters, scale_layout=r.scale_layout,
-                                         scale_round=r.scale_round)
+                                         scale_round=r.scale_round, **self._kd())
             self._keep_amax("x", qx, qx_t, am)
             x_op, xt_op = qx.operand(), qx_t.operand()
-        if r.two_level:
+        if r.rht_kd:
+            # 1D W: rowwise along the inputs (Fprop B), colwise along the
+            # outputs (Dgrad B), each rotated along its own K
+            am, am_t = self._amax_args(self.weight, "w", True)
+            qw, qw_t = api.quantize_dual(self.weight, r.fmt, rht=True, signs=r.rht_kd_signs,
+                                         rht_n=r.rht_kd_n, target=r.target_w, amax_in=am,
+                                         amax_t_in=am_t, counters=self.counters,
+                                         scale_layout=r.scale_layout, scale_round=r.scale_round,
+                                         **self._kd())
+            self._keep_amax("w", qw, qw_t, am)
+            w_op, wt_op = qw.operand(), qw_t.operand()
+        elif r.two_level:
             if self._refresh():
                 api.amax(self.weight, out=self.amax["w"])
             qw = api.quantize(self.weight, r.fmt, block="2d", emit_transpose=True,
@@ -147,7 +180,7 @@ class QuantizedLinear:
         xt_op, wt_op, tokens = self._saved
         if dy.dim() != 2 or tuple(dy.shape) != (tokens, self.out_features):
             raise ValueError("dy must be [tokens, out_features]")
-        am, am_t = self._amax_args(dy, "dy", r.rht)
+        am, am_t = self._amax_args(dy, "dy", r.rht or r.rht_kd)
         if r.act_block == "2d":
             qdy2 = api.quantize(dy, r.fmt, block="2d", rnd="sr", seed=r.sr_seed,
                                 offset=2 * self.step, emit_transpose=True, target=r.target_dy,
@@ -159,7 +192,7 @@ class QuantizedLinear:
                                            rht=r.rht, signs=r.rht_signs, rht_n=r.rht_n,
                                            target=r.target_dy, amax_in=am, amax_t_in=am_t,
                                            counters=self.counters, scale_layout=r.scale_layout,
-                                           scale_round=r.scale_round)
+                                           scale_round=r.scale_round, **self._kd())
             self._keep_amax("dy", qdy, qdy_t, am)
             dy_op, dyt_op = qdy.operand(), qdy_t.operand()
         dx = api.gemm(dy_op, wt_op, tokens, self.in_features, self.out_features, device=dy.device)

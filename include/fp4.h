@@ -113,9 +113,13 @@ typedef struct {
                              r * cols + c, and codes_t is the transposed codes */
   uint64_t seed;          /* SR: Philox4x32-10 key                             */
   uint64_t offset;        /* SR: Philox counter words 2-3 (e.g. a step number) */
-  int rht;                /* COLWISE only: rotate every rht_n-row group of each
-                             column by fl32(1/sqrt(N)) D_r H_N first (App. C;
-                             §4.2 weighs N = 4, 16, 128 and uses 16)           */
+  int rht;                /* 1D, NVFP4/UE5M3: rotate every rht_n-element group
+                             along the blocked axis by fl32(1/sqrt(N)) D_r H_N
+                             first -- rows of a column for COLWISE (the Wgrad
+                             operands, App. C), columns of a row for ROWWISE
+                             (the Fprop / Dgrad operands, rotated along K by
+                             the same signs on both sides, §4.2; §4.2 weighs
+                             N = 4, 16, 128 and uses 16)                       */
   uint32_t rht_signs;     /* D_r, bits 0-31: bit i set negates output row i   */
   float target;           /* T in s_enc = 6 T / amax: 448 for NVFP4; 448 or
                              2048 for UE5M3; ignored for MXFP4; finite, > 0    */
@@ -129,22 +133,26 @@ typedef struct {
   int rht_n;              /* RHT size N: 4, 16, 32, 64 or 128; 0 means 16.
                              Arithmetic: fp32 butterflies with strides 1, 2,
                              ..., N/2, then * fl32(1/sqrt(N)), then the signs;
-                             rows must be a multiple of N                      */
+                             the blocked axis must be a multiple of N          */
   uint32_t rht_signs_hi[3];  /* D_r, bits 32-127 (N > 32); every bit at or
                              above N must be 0                                  */
   fp4_scale_round scale_round;  /* NVFP4/UE5M3 block scales: RNE or UP      */
 } fp4_quant_desc;
 
 /*
- * fp4_amax -- tensor amax (NVFP4 paper App. B.1: amax_X = max |x_i|).
- *   x [rows, cols] bf16 (ld), device.  If rht != 0 the amax is taken over
- *   the column-rotated tensor ((1/4) D_r H16 on each 16-row group of each
- *   column, App. C: the scale is computed in the rotated space); then rows
- *   must be a multiple of 16.
- *   amax: device float, overwritten (0 for an empty tensor).
+ * fp4_amax -- tensor amax (NVFP4 paper App. B.1: amax_X = max |x_i|), the
+ * one fp4_quantize computes for `desc` when amax_given = 0.
+ *   desc  host; used: orient, rht, rht_n, rht_signs, rht_signs_hi.  With
+ *         rht the amax is taken over the rotated tensor (App. C: the scale
+ *         is computed in the rotated space): every rht_n-element group along
+ *         the blocked axis -- rows of a column for COLWISE, columns of a row
+ *         for ROWWISE -- rotated as fp4_quantize rotates it; that axis must
+ *         be a multiple of rht_n.
+ *   x     [rows, cols] bf16 (ld), device.
+ *   amax  device float, overwritten (0 for an empty tensor).
  */
-fp4_status fp4_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
-                    int rht, uint32_t rht_signs, float* amax, void* stream);
+fp4_status fp4_amax(const fp4_quant_desc* desc /* host */, const uint16_t* x, int64_t rows,
+                    int64_t cols, int64_t ld, float* amax, void* stream);
 
 /*
  * fp4_quantize -- quantize a bf16 matrix to E2M1 codes with block scales
@@ -165,8 +173,8 @@ fp4_status fp4_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
  *           MXFP4), the global decode scale the GEMM applies (App. B.3).
  *   counters device fp4_counters or NULL (events not counted).
  *   Shapes: the blocked axis (cols for ROWWISE, rows for COLWISE) must be a
- *   multiple of BS; 2D16 needs rows and cols multiples of 16; RHT needs
- *   COLWISE and rows a multiple of its size N (rht_n).
+ *   multiple of BS; 2D16 needs rows and cols multiples of 16; RHT needs 1D
+ *   blocks and the blocked axis a multiple of its size N (rht_n).
  *   SR random bits: element index i in the output code matrix ([R_out,
  *   C_out], i = r * C_out + c) takes 16 bits of Philox4x32-10(key = seed,
  *   counter = (i >> 3, offset)), half (i & 1) of output word (i & 7) >> 1.
@@ -186,19 +194,20 @@ fp4_status fp4_quantize(const fp4_quant_desc* desc /* host */,
  * Wgrad inputs (§4.2, App. C).  Each output is bit-identical to what
  * fp4_quantize writes with the same descriptor.
  *
- *   row_desc  ROWWISE, 1D, no RHT.      col_desc  COLWISE, 1D.
+ *   row_desc  ROWWISE, 1D; its RHT (along the rows) with rht_n 4 or 16.
+ *   col_desc  COLWISE, 1D; its RHT (along the columns) of any size.
  *   Both: the same format and the same rounding mode (seed, offset, target,
- *   amax_given, scale_layout and scale_round are per side; the RHT fields
- *   apply to the colwise side).  When both amaxes are computed here with a
- *   16-point RHT, one read of x yields the plain and the rotated amax.
+ *   amax_given, scale_layout, scale_round and the RHT fields are per
+ *   side).  When both amaxes are computed here with a 16-point RHT on the
+ *   colwise side only, one read of x yields the plain and the rotated amax.
  *   x [rows, cols] bf16 (ld), device; rows and cols multiples of BS.
  *   codes, scales     rowwise outputs, as fp4_quantize with row_desc.
  *   codes_t, scales_t colwise outputs, as fp4_quantize with col_desc.
  *   amax, amax_t      device floats, NVFP4/UE5M3 (MXFP4: unused, may be
- *           NULL): each written (amax_given = 0; amax_t in the rotated space
- *           when col_desc->rht) or read (amax_given = 1).  They may be the
- *           same buffer only when col_desc has no RHT and both sides have
- *           the same amax_given (the amax is then computed once).
+ *           NULL): each written (amax_given = 0; in the rotated space of
+ *           that side's RHT) or read (amax_given = 1).  They may be the same
+ *           buffer only when neither side has an RHT and both sides have the
+ *           same amax_given (the amax is then computed once).
  *   s_dec, s_dec_t    device floats or NULL: the two global decode scales.
  *   counters  device fp4_counters or NULL: events of both sides, summed.
  */
@@ -224,17 +233,22 @@ fp4_status fp4_dequantize(fp4_format format, fp4_block block, fp4_scale_layout s
                           int64_t rows, int64_t cols, void* out, int out_fp32, void* stream);
 
 /*
- * fp4_rht16 -- the 16-point random Hadamard transform alone (NVFP4 paper
- * §4.2, App. C): y = (1/4) D_r H16 v for v = each 16-row group of each
- * column of x.  fp32 arithmetic as a Walsh-Hadamard butterfly network with
- * strides 1, 2, 4, 8 (each butterfly (a, b) -> (a + b, a - b)), then the
- * exact 1/4, then the sign flips; these are the values fp4_quantize with
- * rht = 1 quantizes.
- *   x [rows, cols] bf16 (ld), device; rows % 16 == 0.
- *   y [rows, cols] fp32 row-major (leading dimension cols), device.
+ * fp4_rht16 -- the random Hadamard transform alone (NVFP4 paper §4.2,
+ * App. C): y = fl32(1/sqrt(N)) D_r H_N v for every N-element group v along
+ * the blocked axis of `desc` -- N consecutive rows of a column (COLWISE) or
+ * N consecutive columns of a row (ROWWISE); N = rht_n (0 means 16, the
+ * 16-point transform: scale exactly 1/4).  fp32 arithmetic as a
+ * Walsh-Hadamard butterfly network with strides 1, 2, ..., N/2 (each
+ * butterfly (a, b) -> (a + b, a - b)), then the scale, then the sign flips
+ * (bit i of rht_signs / rht_signs_hi negates entry i of each group); these
+ * are the values fp4_quantize with rht = 1 quantizes.
+ *   desc  host; used: orient, rht_n, rht_signs, rht_signs_hi (rht ignored).
+ *   x [rows, cols] bf16 (ld), device; the rotated axis a multiple of N.
+ *   y [rows, cols] fp32 row-major (leading dimension cols), device,
+ *     16-byte aligned.
  */
-fp4_status fp4_rht16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
-                     uint32_t rht_signs, float* y, void* stream);
+fp4_status fp4_rht16(const fp4_quant_desc* desc /* host */, const uint16_t* x, int64_t rows,
+                     int64_t cols, int64_t ld, float* y, void* stream);
 
 /* One GEMM operand: a [rows, K] code matrix, K-major (host struct of device
  * pointers).  With scale_layout ROWMAJOR the scale of (row r, K-block j) is

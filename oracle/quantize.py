@@ -211,10 +211,12 @@ def quantize(x_bits, fmt="nvfp4", block="1d", orient="row", rnd="rne",
 
     orient="row": blocks run along C; output codes [R, C/2], scales
     [R, C/BS].  orient="col": the matrix quantized is X^T, so output codes
-    are [C, R/2] and scales [C, R/BS]; with rht=True every 16-row group of
-    each column is first rotated by (1/4) D_r H16 (App. C), and the tensor
-    amax is taken after the rotation (rht_n: the size N of the variant
-    transforms, groups of N rows, `signs` an N-bit mask).  block="2d":
+    are [C, R/2] and scales [C, R/BS].  rht=True first rotates every group
+    of 16 consecutive elements along the blocked axis -- 16 rows of a column
+    for orient="col" (the Wgrad operands, App. C), 16 columns of a row for
+    orient="row" (the Fprop / Dgrad operands, §4.2) -- by (1/4) D_r H16, and
+    the tensor amax is taken after the rotation (rht_n: the size N of the
+    variant transforms, groups of N elements, `signs` an N-bit mask).  block="2d":
     16x16 tiles of X (rowwise only); scales [R/16, C/16]; emit_transpose
     also returns the codes of X^T ([C, R/2]) quantized with the same tile
     scales.
@@ -239,8 +241,12 @@ def quantize(x_bits, fmt="nvfp4", block="1d", orient="row", rnd="rne",
         assert R % 16 == 0 and C % 16 == 0
         bs = 16
     if rht:
-        assert orient == "col" and R % rht_n == 0
-        x = rht_cols(x, signs, rht_n)
+        if orient == "col":
+            assert R % rht_n == 0
+            x = rht_cols(x, signs, rht_n)
+        else:      # along the rows: the columns of X^T
+            assert C % rht_n == 0
+            x = rht_cols(x.T, signs, rht_n).T.copy()
     v = x.T.copy() if orient == "col" else x               # rows of v are blocked
     Ro, Co = v.shape
     assert Co % bs == 0, "block axis must be a multiple of the block size"

@@ -74,7 +74,8 @@ def quant(lib, d, rows=32, cols=64, ld=None, x=FAKE, codes=FAKE, scales=FAKE, co
     (dict(format=2, block=1), 32, 64, 3),            # 2D needs NVFP4/UE5M3
     (dict(block=1, orient=1), 32, 64, 3),            # 2D is rowwise only
     (dict(scale_round=2), 32, 64, 1),                # bad scale rounding
-    (dict(rht=1), 32, 64, 3),                        # RHT needs colwise
+    (dict(rht=1, block=1), 32, 64, 3),               # RHT needs 1D blocks
+    (dict(rht=1, rht_n=128), 32, 64, 2),             # rowwise RHT: cols % rht_n
     (dict(rht=1, orient=1, format=2), 32, 64, 3),    # RHT needs two-level formats
     (dict(format=2, amax_given=1), 32, 64, 3),       # MXFP4 has no tensor amax
     (dict(emit_transpose=1), 32, 64, 3),             # emit_transpose needs 2D
@@ -147,7 +148,9 @@ def dual(lib, rd, cd, rows=32, cols=64, x=FAKE, codes=FAKE, scales=FAKE, codes_t
     (dict(), dict(orient=1, rht=1, rht_n=64), 32, 64, 2),     # rows % rht_n
     (dict(), dict(orient=1, rht=1, rht_n=5), 64, 64, 1),
     (dict(), dict(orient=1, round=1), 32, 64, 3),             # rounding modes differ
-    (dict(rht=1), dict(orient=1), 32, 64, 3),                 # RHT on the rowwise side
+    (dict(rht=1, rht_n=32), dict(orient=1), 32, 64, 3),       # rowwise-side RHT: N 4 or 16
+    (dict(rht=1, rht_n=4, rht_signs=1 << 4), dict(orient=1), 32, 64, 1),   # bits above N
+    (dict(rht=1, format=2), dict(orient=1, format=2), 64, 64, 3),   # RHT with MXFP4
     (dict(format=2), dict(orient=1, format=2, rht=1), 64, 64, 3),   # RHT with MXFP4
     (dict(block=1), dict(orient=1), 32, 64, 3),               # 2D
     (dict(), dict(orient=1, emit_transpose=1), 32, 64, 3),
@@ -178,10 +181,24 @@ def test_quantize_dual_rejects_pointers(lib):
                                  FAKE, FAKE, None, None, None, None) == 1
 
 
+def amax_call(lib, d, rows=32, cols=64, amax=FAKE):
+    return lib.fp4_amax(None if d is None else ctypes.byref(d), FAKE, rows, cols, cols, amax, None)
+
+
+def rht_call(lib, d, rows=32, cols=64, y=FAKE):
+    return lib.fp4_rht16(None if d is None else ctypes.byref(d), FAKE, rows, cols, cols, y, None)
+
+
 def test_other_entry_points_reject(lib):
-    assert lib.fp4_amax(FAKE, 32, 64, 64, 1, 0, None, None) == 1
-    assert lib.fp4_amax(FAKE, 24, 64, 64, 1, 0, FAKE, None) == 2
-    assert lib.fp4_amax(FAKE, 32, 64, 64, 1, 1 << 16, FAKE, None) == 1
+    assert amax_call(lib, None) == 1                                          # no desc
+    assert amax_call(lib, desc(orient=1, rht=1), amax=None) == 1
+    assert amax_call(lib, desc(orient=1, rht=1), rows=24) == 2                # rows % 16
+    assert amax_call(lib, desc(orient=0, rht=1), cols=40) == 2                # cols % 16
+    assert amax_call(lib, desc(orient=0, rht=1, rht_n=128), cols=64) == 2     # cols % 128
+    assert amax_call(lib, desc(orient=1, rht=1, rht_signs=1 << 16)) == 1      # bits above N
+    assert amax_call(lib, desc(orient=1, rht=1, rht_n=8)) == 1                # bad size
+    assert amax_call(lib, desc(orient=5)) == 1
+    assert amax_call(lib, desc(orient=0), rows=1 << 31) == 2                  # too many rows
     assert lib.fp4_dequantize(0, 0, 0, FAKE, FAKE, FAKE, 32, 40, FAKE, 1, None) == 2
     assert lib.fp4_dequantize(2, 1, 0, FAKE, FAKE, FAKE, 32, 64, FAKE, 1, None) == 3
     assert lib.fp4_dequantize(0, 0, 0, FAKE, FAKE, None, 32, 64, FAKE, 1, None) == 1
@@ -189,8 +206,12 @@ def test_other_entry_points_reject(lib):
     assert lib.fp4_dequantize(0, 1, 1, FAKE, FAKE, FAKE, 32, 64, FAKE, 1, None) == 3
     assert lib.fp4_dequantize(0, 0, 1, FAKE, ctypes.c_void_p(0x10008), FAKE, 32, 64, FAKE, 1,
                               None) == 1
-    assert lib.fp4_rht16(FAKE, 40, 64, 64, 0, FAKE, None) == 2
-    assert lib.fp4_rht16(FAKE, 32, 64, 64, 0, None, None) == 1
+    assert rht_call(lib, desc(orient=1), rows=40) == 2
+    assert rht_call(lib, desc(orient=1), y=None) == 1
+    assert rht_call(lib, desc(orient=1), y=ctypes.c_void_p(0x10008)) == 1    # 16-byte aligned
+    assert rht_call(lib, desc(orient=0, rht_n=32), cols=48) == 2
+    assert rht_call(lib, desc(orient=1, rht_n=4, rht_signs=1 << 4)) == 1
+    assert rht_call(lib, None) == 1
 
 
 def op(fmt=0, codes=0x10000, ld=32, rg=1, layout=0, scales=0x20000):

@@ -5,10 +5,12 @@ Per step: Y = Fprop, dX = Dgrad, and the fp32 main gradient accumulating
 Wgrad, each within 1e-5 * s_A s_B sum|a b| per element (summed over the
 steps for the accumulated gradient) of the oracle's fp64 GEMMs of its own
 quantized operands; event counters equal to the oracle's.  Cases: NVFP4
-with and without the RHT (16-point, and 64-point with the amax refreshed
-every second step), UE5M3 with the tensor amax refreshed every second step
-(steps in between reuse it on new data), MXFP4, and the 2D-block recipe
-(16x16 blocks for X and dY too, SR on dY, rounded-up scales).
+with and without the RHT (16-point, with the amax refreshed every step and
+every second step, and 64-point refreshed every second step), the RHT
+along K on the Fprop / Dgrad operands too (16- and 4-point), UE5M3 with the
+tensor amax refreshed every second step (steps in between reuse it on new
+data), MXFP4, and the 2D-block recipe (16x16 blocks for X and dY too, SR
+on dY, rounded-up scales).
 """
 import numpy as np
 import pytest
@@ -54,12 +56,19 @@ def oracle_step(x, w, dy, r: Recipe, step, amax):
         cnt.append(q2["counters"])
     else:
         qx = Q.quantize(x, fmt, orient="row", target=r.target_x, amax=amax["x"],
-                        scale_round=sr_mode)
+                        scale_round=sr_mode, rht=r.rht_kd, signs=r.rht_kd_signs, rht_n=r.rht_kd_n)
         qxt = Q.quantize(x, fmt, orient="col", rht=r.rht, signs=r.rht_signs, target=r.target_x,
                          amax=amax["x_t"], rht_n=r.rht_n, scale_round=sr_mode)
         x_ops = ((vals(qx, fmt), s_dec(qx, fmt)), (vals(qxt, fmt), s_dec(qxt, fmt)))
         cnt += [qx["counters"], qxt["counters"]]
-    if r.two_level:
+    if r.rht_kd:
+        kd = dict(rht=True, signs=r.rht_kd_signs, rht_n=r.rht_kd_n, target=r.target_w,
+                  scale_round=sr_mode)
+        qw = Q.quantize(w, fmt, orient="row", amax=amax["w"], **kd)
+        qwt = Q.quantize(w, fmt, orient="col", amax=amax["w_t"], **kd)
+        wv, wtv, sw, swt = vals(qw, fmt), vals(qwt, fmt), qw["s_dec"], qwt["s_dec"]
+        cnt += [qw["counters"], qwt["counters"]]
+    elif r.two_level:
         qw = Q.quantize(w, fmt, block="2d", emit_transpose=True, target=r.target_w,
                         amax=amax["w"], scale_round=sr_mode)
         wv = vals(qw, fmt, "2d")
@@ -77,7 +86,8 @@ def oracle_step(x, w, dy, r: Recipe, step, amax):
         cnt.append(q2["counters"])
     else:
         qdy = Q.quantize(dy, fmt, orient="row", rnd="sr", seed=r.sr_seed, offset=2 * step,
-                         target=r.target_dy, amax=amax["dy"], scale_round=sr_mode)
+                         target=r.target_dy, amax=amax["dy"], scale_round=sr_mode,
+                         rht=r.rht_kd, signs=r.rht_kd_signs, rht_n=r.rht_kd_n)
         qdyt = Q.quantize(dy, fmt, orient="col", rnd="sr", seed=r.sr_seed, offset=2 * step + 1,
                           rht=r.rht, signs=r.rht_signs, target=r.target_dy, amax=amax["dy_t"],
                           rht_n=r.rht_n, scale_round=sr_mode)
@@ -94,11 +104,17 @@ def oracle_step(x, w, dy, r: Recipe, step, amax):
 
 def tensor_amaxes(x, w, dy, r):
     if not r.two_level:
-        return dict(x=None, x_t=None, w=None, dy=None, dy_t=None)
-    xf, dyf = F.bf16_bits_to_f32(x), F.bf16_bits_to_f32(dy)
-    a = dict(x=Q.tensor_amax(xf), w=Q.tensor_amax(F.bf16_bits_to_f32(w)), dy=Q.tensor_amax(dyf))
-    a["x_t"] = Q.tensor_amax(rht_cols(xf, r.rht_signs, r.rht_n)) if r.rht else a["x"]
-    a["dy_t"] = Q.tensor_amax(rht_cols(dyf, r.rht_signs, r.rht_n)) if r.rht else a["dy"]
+        return dict(x=None, x_t=None, w=None, w_t=None, dy=None, dy_t=None)
+    xf, wf, dyf = F.bf16_bits_to_f32(x), F.bf16_bits_to_f32(w), F.bf16_bits_to_f32(dy)
+
+    def along_k(v):     # rotated along the rows (the K axis of Fprop / Dgrad)
+        return rht_cols(v.T, r.rht_kd_signs, r.rht_kd_n).T if r.rht_kd else v
+
+    a = dict(x=Q.tensor_amax(along_k(xf)), w=Q.tensor_amax(along_k(wf)),
+             dy=Q.tensor_amax(along_k(dyf)))
+    a["x_t"] = Q.tensor_amax(rht_cols(xf, r.rht_signs, r.rht_n)) if r.rht else Q.tensor_amax(xf)
+    a["dy_t"] = Q.tensor_amax(rht_cols(dyf, r.rht_signs, r.rht_n)) if r.rht else Q.tensor_amax(dyf)
+    a["w_t"] = Q.tensor_amax(rht_cols(wf, r.rht_kd_signs, r.rht_kd_n)) if r.rht_kd else a["w"]
     return a
 
 
@@ -119,6 +135,13 @@ RECIPES = {
     "ue5m3_2d_blocks_periodic": (Recipe("ue5m3", target_dy=2048.0, act_block="2d",
                                         amax_interval=2), 2),
     "nvfp4_1d_up": (Recipe("nvfp4", scale_round="up"), 1),
+    # the fused plain + rotated amax pass on refreshes, kept for the next step
+    "nvfp4_rht16_periodic": (Recipe("nvfp4", rht=True, rht_signs=SIGNS, amax_interval=2), 3),
+    # RHT along K on the Fprop / Dgrad operands as well (1D W)
+    "nvfp4_rht_all_gemms": (Recipe("nvfp4", rht=True, rht_signs=SIGNS, rht_kd=True,
+                                   rht_kd_signs=SIGNS), 1),
+    "ue5m3_rht4_kd_periodic": (Recipe("ue5m3", target_dy=2048.0, rht_kd=True, rht_kd_n=4,
+                                      rht_kd_signs=inputs.rht_sign_bits(4), amax_interval=2), 3),
 }
 
 

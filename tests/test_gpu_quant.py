@@ -456,3 +456,69 @@ def test_workload_dual_whole_tensor():
         assert f32_bits(q.amax.item()) == f32_bits(r["amax"])
     assert api.counters_dict(cnt) == {k: rr["counters"][k] + rc["counters"][k]
                                       for k in rr["counters"]}
+
+
+# ------------------- RHT along the rows: the Fprop / Dgrad operands ----
+from oracle.rht import rht_cols
+
+
+def _rot(xf, signs, n, orient):
+    """The oracle's rotation along the blocked axis of `orient`."""
+    return rht_cols(xf, signs, n) if orient == "col" else rht_cols(xf.T, signs, n).T
+
+
+@pytest.mark.parametrize("n", [4, 16, 32, 64, 128])
+@pytest.mark.parametrize("fmt,rnd", [("nvfp4", "rne"), ("nvfp4", "sr"), ("ue5m3", "rne")])
+def test_rowwise_rht_sizes(n, fmt, rnd):
+    """Rowwise quantization with every N-column group of each row rotated
+    (the lanes of a group combine by shuffles for N > 16), the tensor amax
+    taken in the rotated space by the library: bit-exact with the oracle."""
+    x = inputs.gradients((40, 384), cfg_seed=62) if rnd == "sr" else \
+        inputs.activations((40, 384), cfg_seed=62)
+    signs = inputs.rht_sign_bits(n)
+    cnt = api.new_counters()
+    q = api.quantize(dev(x), fmt, orient="row", rnd=rnd, seed=2, offset=5, rht=True, signs=signs,
+                     rht_n=n, counters=cnt, scale_layout="tiled")
+    torch.cuda.synchronize()
+    r = Q.quantize(x, fmt, orient="row", rnd=rnd, seed=2, offset=5, rht=True, signs=signs, rht_n=n)
+    assert_same(q, r, api.counters_dict(cnt))
+
+
+@pytest.mark.parametrize("n", [4, 16, 32, 64, 128])
+@pytest.mark.parametrize("orient", ["row", "col"])
+def test_rht_alone_and_rotated_amax(n, orient):
+    """fp4_rht16 and fp4_amax with every RHT size in both orientations:
+    the rotated values bit for bit, and their amax, equal the oracle's."""
+    x = inputs.activations((256, 384), cfg_seed=63)
+    signs = inputs.rht_sign_bits(n)
+    y = api.rht16(dev(x), signs, rht_n=n, orient=orient)
+    a = api.amax(dev(x), rht=True, signs=signs, rht_n=n, orient=orient)
+    torch.cuda.synchronize()
+    want = _rot(F.bf16_bits_to_f32(x), signs, n, orient)
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), want.view(np.uint32))
+    assert f32_bits(a.item()) == f32_bits(Q.tensor_amax(want))
+
+
+@pytest.mark.parametrize("n_row,n_col,rnd", [(16, 16, "rne"), (4, 64, "sr"), (16, 128, "sr")])
+def test_dual_rht_both_sides(n_row, n_col, rnd):
+    """The dual quantizer with the rowwise side rotated along the rows and
+    the colwise side along the columns (a linear layer with the RHT on all
+    three GEMMs' operands), both amaxes computed by the library."""
+    x = inputs.gradients((384, 208), cfg_seed=64)
+    sr, sc = inputs.rht_sign_bits(n_row), inputs.rht_sign_bits(n_col)
+    cnt = api.new_counters()
+    qr, qc = api.quantize_dual(dev(x), "nvfp4", rnd=rnd, seed=2, offset=0, offset_t=1, rht=True,
+                               signs=sc, rht_n=n_col, rht_row=True, signs_row=sr,
+                               rht_n_row=n_row, counters=cnt, scale_layout="tiled")
+    torch.cuda.synchronize()
+    rr = Q.quantize(x, "nvfp4", orient="row", rnd=rnd, seed=2, offset=0, rht=True, signs=sr,
+                    rht_n=n_row)
+    rc = Q.quantize(x, "nvfp4", orient="col", rnd=rnd, seed=2, offset=1, rht=True, signs=sc,
+                    rht_n=n_col)
+    for q, r in ((qr, rr), (qc, rc)):
+        assert np.array_equal(q.codes.cpu().numpy(), r["codes"])
+        assert np.array_equal(gpu_scales(q), r["scales"])
+        assert f32_bits(q.amax.item()) == f32_bits(r["amax"])
+        assert f32_bits(q.s_dec.item()) == f32_bits(r["s_dec"])
+    assert api.counters_dict(cnt) == {k: rr["counters"][k] + rc["counters"][k]
+                                      for k in rr["counters"]}

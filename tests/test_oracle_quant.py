@@ -437,3 +437,45 @@ def test_format_error_ordering():
             dq = Q.dequantize(q["codes"], q["scales"], fmt, "1d", q["s_dec"], *shape)
             err[fmt] = np.linalg.norm(dq.astype(np.float64) - xf) / np.linalg.norm(xf)
         assert err["nvfp4"] < err["mxfp4"], (name, err)
+
+
+# ------------------------- RHT on the Fprop / Dgrad operands (along K) ----
+@pytest.mark.parametrize("n", [4, 16, 32, 64, 128])
+@pytest.mark.parametrize("fmt,rnd", [("nvfp4", "rne"), ("ue5m3", "sr")])
+def test_rowwise_rht_is_colwise_rht_of_transpose(n, fmt, rnd):
+    """NVFP4 paper §4.2 (RHT on Fprop / Dgrad inputs): rotating along the
+    rows of X (rowwise blocks) is the pinned column rotation of X^T: the
+    rowwise quantization of X with the RHT equals, code for code, the
+    colwise quantization of X^T with the same transform and signs (SR
+    indices are those of the same output code matrix)."""
+    x = inputs.activations((48, 2 * n if n >= 64 else 128), cfg_seed=60 + n)
+    s = inputs.rht_sign_bits(n)
+    a = Q.quantize(x, fmt, orient="row", rnd=rnd, seed=3, offset=1, rht=True, signs=s, rht_n=n)
+    b = Q.quantize(np.ascontiguousarray(x.T), fmt, orient="col", rnd=rnd, seed=3, offset=1,
+                   rht=True, signs=s, rht_n=n)
+    for k in ("codes", "scales", "amax", "s_dec"):
+        assert np.array_equal(a[k], b[k]), k
+    assert a["counters"] == b["counters"]
+
+
+def test_fprop_with_rotated_operands_approximates_the_product():
+    """Fprop with X and W rotated along K by the same D_r H16 (§4.2): the
+    rotation cancels in X W^T (H orthonormal), so the product of the
+    dequantized rotated operands approximates X W^T as closely as the
+    unrotated quantized product does: relative Frobenius error below 0.2 for
+    both (each operand carries an E2M1 relative RMS error near 0.085, so the
+    product's is near 0.12; a rotation that does not cancel gives an error
+    near 1), within a factor 1.5 of each other."""
+    X = inputs.activations((256, 512), cfg_seed=61)
+    W = inputs.weights((128, 512), cfg_seed=61)
+    ref = F.bf16_bits_to_f32(X).astype(np.float64) @ F.bf16_bits_to_f32(W).astype(np.float64).T
+    s = inputs.rht_sign_mask()
+    errs = []
+    for rht in (False, True):
+        qx = Q.quantize(X, "nvfp4", rht=rht, signs=s)
+        qw = Q.quantize(W, "nvfp4", rht=rht, signs=s)
+        dx = Q.dequantize(qx["codes"], qx["scales"], "nvfp4", "1d", qx["s_dec"], 256, 512)
+        dw = Q.dequantize(qw["codes"], qw["scales"], "nvfp4", "1d", qw["s_dec"], 128, 512)
+        d = dx.astype(np.float64) @ dw.astype(np.float64).T
+        errs.append(np.linalg.norm(d - ref) / np.linalg.norm(ref))
+    assert max(errs) < 0.2 and errs[1] < 1.5 * errs[0] and errs[0] < 1.5 * errs[1], errs
