@@ -15,10 +15,26 @@ to fp32.  (Scaling per block before or after the partial sums is the same
 number in exact arithmetic.)
 
 Layout: "TN" -- both operands are K-major: A is [M, K], B is [N, K].
+
+Global decode scales are either one fp32 number per operand or, for the
+per-row global scale (App. B.1, last sentence), one per operand row: s_A[m]
+per row of A and s_B[n] per row of B, so D[m, n] takes s_A[m] * s_B[n].
 """
 from __future__ import annotations
 
 import numpy as np
+
+
+def _scale(s_dec_a, s_dec_b):
+    """s_A s_B in float64, shaped to broadcast over [M, N] (a scalar, or
+    s_A as a column and s_B as a row when they are per-row vectors)."""
+    sa = np.asarray(s_dec_a, dtype=np.float32).astype(np.float64)
+    sb = np.asarray(s_dec_b, dtype=np.float32).astype(np.float64)
+    if sa.ndim:
+        sa = sa.reshape(-1, 1)
+    if sb.ndim:
+        sb = sb.reshape(1, -1)
+    return sa * sb
 
 
 def gemm_ref(a_vals, b_vals, s_dec_a=1.0, s_dec_b=1.0):
@@ -26,9 +42,8 @@ def gemm_ref(a_vals, b_vals, s_dec_a=1.0, s_dec_b=1.0):
     a = np.asarray(a_vals, dtype=np.float64)
     b = np.asarray(b_vals, dtype=np.float64)
     acc = a @ b.T
-    s = np.float64(np.float32(s_dec_a)) * np.float64(np.float32(s_dec_b))
     with np.errstate(over="ignore"):
-        return (acc * s).astype(np.float32)
+        return (acc * _scale(s_dec_a, s_dec_b)).astype(np.float32)
 
 
 def gemm_abs_bound(a_vals, b_vals, s_dec_a=1.0, s_dec_b=1.0):
@@ -36,15 +51,16 @@ def gemm_abs_bound(a_vals, b_vals, s_dec_a=1.0, s_dec_b=1.0):
     per-element tolerance |D_gpu - D_ref| <= 1e-5 * bound."""
     a = np.abs(np.asarray(a_vals, dtype=np.float64))
     b = np.abs(np.asarray(b_vals, dtype=np.float64))
-    s = np.float64(np.float32(s_dec_a)) * np.float64(np.float32(s_dec_b))
-    return (a @ b.T) * s
+    return (a @ b.T) * _scale(s_dec_a, s_dec_b)
 
 
 def gemm_ref_entries(a_vals, b_vals, rows, cols, s_dec_a=1.0, s_dec_b=1.0):
     """Reference and bound for selected entries (rows[i], cols[i]) only."""
     a = np.asarray(a_vals, dtype=np.float64)[rows]
     b = np.asarray(b_vals, dtype=np.float64)[cols]
-    s = np.float64(np.float32(s_dec_a)) * np.float64(np.float32(s_dec_b))
+    sa = np.asarray(s_dec_a, dtype=np.float32).astype(np.float64)
+    sb = np.asarray(s_dec_b, dtype=np.float32).astype(np.float64)
+    s = (sa[rows] if sa.ndim else sa) * (sb[cols] if sb.ndim else sb)
     acc = np.einsum("ik,ik->i", a, b)
     bound = np.einsum("ik,ik->i", np.abs(a), np.abs(b)) * s
     with np.errstate(over="ignore"):

@@ -16,6 +16,11 @@ page, so each is restated from its surrounding prose:
   B.3 (Eq. 4)  element code = Q(x * s_enc_L), Q = E2M1 conversion.
   B.4          MXFP4: power-of-two UE8M0 scale rounded up so the block amax
                never saturates; no tensor scale.
+  B.1 (end)    the "global" scale may cover a smaller span than the tensor,
+               a row for instance, so that no separate pass over memory is
+               needed for the amax: scope="row" gives every row of the
+               output code matrix its own amax, s_enc and s_dec (Eq. 1 per
+               row); each row is then quantized exactly as a one-row tensor.
   §4.3         2D weights: one scale per 16x16 tile (16 in x 16 out channels).
   §4.4         stochastic rounding on gradients: round to one of the two
                neighbours with probability inversely proportional to the
@@ -75,6 +80,15 @@ def tensor_amax(v):
     if v.size == 0:
         return np.float32(0.0)
     return np.float32(np.max(np.abs(v)))
+
+
+def row_amax(v):
+    """max |x| of every row (fp32 [R]): the amax of the per-row global
+    scale (App. B.1, last sentence); 0 for an empty row."""
+    v = np.asarray(v, dtype=np.float32)
+    if v.shape[1] == 0:
+        return np.zeros(v.shape[0], np.float32)
+    return np.max(np.abs(v), axis=1).astype(np.float32)
 
 
 def global_scales(amax, target=448.0):
@@ -206,7 +220,8 @@ def unpack_codes(packed):
 # ------------------------------------------------------ full quantize ----
 def quantize(x_bits, fmt="nvfp4", block="1d", orient="row", rnd="rne",
              seed=0, offset=0, rht=False, signs=0, target=448.0,
-             amax=None, emit_transpose=False, index_base=0, rht_n=16, scale_round="rne"):
+             amax=None, emit_transpose=False, index_base=0, rht_n=16, scale_round="rne",
+             scope="tensor"):
     """Quantize a bf16 matrix (uint16 bit patterns, [R, C]).
 
     orient="row": blocks run along C; output codes [R, C/2], scales
@@ -227,11 +242,15 @@ def quantize(x_bits, fmt="nvfp4", block="1d", orient="row", rnd="rne",
     formats -- MXFP4 scales are always rounded up).  block="2d" with SR
     draws the random bits of element (r, c) of X at index r*C + c, so the
     codes of X^T are exactly the transposed codes of X.
+    scope: "tensor" (one global scale) or "row" (two-level formats, 1D: one
+    global scale per row of the output code matrix; `amax`, if given, and
+    the returned amax and s_dec are then fp32 arrays with one entry per row).
 
     Returns a dict: codes, scales, codes_t (2D only), amax, s_dec, counters.
     """
     assert fmt in FORMATS and block in ("1d", "2d") and orient in ("row", "col")
-    assert rnd in ("rne", "sr")
+    assert rnd in ("rne", "sr") and scope in ("tensor", "row")
+    assert scope == "tensor" or (fmt != "mxfp4" and block == "1d")
     x = F.bf16_bits_to_f32(np.asarray(x_bits, dtype=np.uint16))
     assert x.ndim == 2
     R, C = x.shape
@@ -254,6 +273,12 @@ def quantize(x_bits, fmt="nvfp4", block="1d", orient="row", rnd="rne",
     if fmt == "mxfp4":
         assert amax is None, "MXFP4 has no tensor scale"
         amax_x, s_enc_g, s_dec_g = None, np.float32(1.0), np.float32(1.0)
+    elif scope == "row":
+        amax_x = (row_amax(v) if amax is None
+                  else np.asarray(amax, dtype=np.float32).reshape(Ro).copy())
+        pairs = [global_scales(a, target) for a in amax_x]
+        s_enc_g = np.array([p[0] for p in pairs], np.float32).reshape(Ro, 1)
+        s_dec_g = np.array([p[1] for p in pairs], np.float32).reshape(Ro, 1)
     else:
         amax_x = tensor_amax(v) if amax is None else np.float32(amax)
         s_enc_g, s_dec_g = global_scales(amax_x, target)
@@ -296,8 +321,9 @@ def quantize(x_bits, fmt="nvfp4", block="1d", orient="row", rnd="rne",
     out = {
         "codes": pack_codes(codes),
         "scales": scode.astype(np.uint8),
-        "amax": None if amax_x is None else np.float32(amax_x),
-        "s_dec": np.float32(s_dec_g),
+        "amax": (None if amax_x is None else
+                 amax_x if scope == "row" else np.float32(amax_x)),
+        "s_dec": s_dec_g.reshape(Ro) if scope == "row" else np.float32(s_dec_g),
         "counters": counters,
         "codes_unpacked": codes,
     }
@@ -330,14 +356,20 @@ def dequantize(codes_packed, scodes, fmt, block, s_dec, R, C, out="f32"):
 
     The decode follows App. B.2-B.3 of the NVFP4 paper (the decode scales
     undo the encode scales).  e2m1 * scale is exact in fp32.  MXFP4 has no
-    tensor scale (s_dec is taken as 1).
+    tensor scale (s_dec is taken as 1).  s_dec may be an array of R per-row
+    decode scales (scope="row").
     """
     codes = unpack_codes(np.asarray(codes_packed, dtype=np.uint8).reshape(R, C // 2))
     e = F.e2m1_value(codes)
     s = element_scales(scodes, fmt, block, R, C)
     with np.errstate(over="ignore"):
         prod = (e * s).astype(np.float32)
-        sd = np.float32(1.0) if fmt == "mxfp4" else np.float32(s_dec)
+        if fmt == "mxfp4":
+            sd = np.float32(1.0)
+        elif np.ndim(s_dec) == 0:
+            sd = np.float32(s_dec)
+        else:
+            sd = np.asarray(s_dec, dtype=np.float32).reshape(R, 1)
         v = (prod * sd).astype(np.float32)
     if out == "bf16":
         return F.f32_to_bf16_bits(v)

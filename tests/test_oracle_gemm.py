@@ -106,3 +106,33 @@ def test_abs_bound_dominates():
     a = rng.standard_normal((20, 64)); b = rng.standard_normal((30, 64))
     D = G.gemm_ref(a, b, 1.0, 1.0).astype(np.float64)
     assert np.all(np.abs(D) <= G.gemm_abs_bound(a, b) * (1 + 1e-7))
+
+
+def test_per_row_decode_scales_brute_force():
+    """Per-row global decode scales (App. B.1, last sentence; B.3: applied to
+    the output): D[m, n] = s_A[m] s_B[n] sum_k a[m, k] b[n, k], checked by
+    plain loops over the dequantized operands (rows of different scale, so a
+    scale applied along the wrong axis fails)."""
+    from oracle import quantize as Q
+    rng = np.random.default_rng(9)
+    M, N, K = 6, 5, 32
+    fa = (rng.standard_normal((M, K)) * np.exp2(3.0 * np.arange(M))[:, None]).astype(np.float32)
+    fb = (rng.standard_normal((N, K)) * np.exp2(-2.0 * np.arange(N))[:, None]).astype(np.float32)
+    qa = Q.quantize(inputs.to_bf16_bits(fa), "nvfp4", scope="row")
+    qb = Q.quantize(inputs.to_bf16_bits(fb), "nvfp4", scope="row")
+    da = Q.dequantize(qa["codes"], qa["scales"], "nvfp4", "1d", qa["s_dec"], M, K)
+    db = Q.dequantize(qb["codes"], qb["scales"], "nvfp4", "1d", qb["s_dec"], N, K)
+    av = Q.operand_values(qa["codes"], qa["scales"], "nvfp4", "1d", M, K)
+    bv = Q.operand_values(qb["codes"], qb["scales"], "nvfp4", "1d", N, K)
+    d = G.gemm_ref(av, bv, qa["s_dec"], qb["s_dec"])
+    bound = G.gemm_abs_bound(av, bv, qa["s_dec"], qb["s_dec"])
+    for m in range(M):
+        for n in range(N):
+            want = 0.0
+            for k in range(K):
+                want += float(da[m, k]) * float(db[n, k])
+            # the dequantized values are rounded to fp32 once each
+            assert abs(float(d[m, n]) - want) <= 1e-6 * bound[m, n] + 1e-300
+    rows, cols = np.array([0, 5, 3]), np.array([4, 0, 2])
+    e, eb = G.gemm_ref_entries(av, bv, rows, cols, qa["s_dec"], qb["s_dec"])
+    assert np.array_equal(e, d[rows, cols]) and np.allclose(eb, bound[rows, cols], rtol=1e-15)

@@ -479,3 +479,91 @@ def test_fprop_with_rotated_operands_approximates_the_product():
         d = dx.astype(np.float64) @ dw.astype(np.float64).T
         errs.append(np.linalg.norm(d - ref) / np.linalg.norm(ref))
     assert max(errs) < 0.2 and errs[1] < 1.5 * errs[0] and errs[0] < 1.5 * errs[1], errs
+
+
+# ---------------------------------------------- per-row global scale ----
+# NVFP4 paper App. B.1, last sentence: the global scale may span a row
+# instead of the whole tensor, so no separate amax pass is needed.
+
+def _rows_over_decades(R, C, cfg_seed):
+    """bf16 bits of an [R, C] matrix whose rows differ in scale by up to
+    2^40 (row r is N(0, 1) times 2^(2 (r mod 21) - 20))."""
+    v = inputs.normal((R, C), cfg_seed=cfg_seed)
+    f = np.exp2(2.0 * (np.arange(R) % 21) - 20.0).astype(np.float32)
+    return bits(F.bf16_bits_to_f32(v) * f[:, None])
+
+
+@pytest.mark.parametrize("fmt,target", [("nvfp4", 448.0), ("ue5m3", 2048.0)])
+@pytest.mark.parametrize("rnd", ["rne", "sr"])
+def test_row_scope_quantizes_each_row_as_a_one_row_tensor(fmt, target, rnd):
+    """With the global scale spanning a row, row r is quantized exactly as
+    the 1 x C tensor x[r] with its own tensor amax (the row amax); under SR
+    the row keeps its random bits (index r * C + c, passed as index_base)."""
+    R, C = 24, 64
+    x = _rows_over_decades(R, C, 11)
+    q = Q.quantize(x, fmt, rnd=rnd, seed=5, offset=2, target=target, scope="row")
+    total = Q.zero_counters()
+    for r in range(R):
+        q1 = Q.quantize(x[r:r + 1], fmt, rnd=rnd, seed=5, offset=2, target=target,
+                        index_base=r * C)
+        assert np.array_equal(q["codes"][r], q1["codes"][0])
+        assert np.array_equal(q["scales"][r], q1["scales"][0])
+        assert q["amax"][r] == q1["amax"] and q["s_dec"][r] == q1["s_dec"]
+        for k in total:
+            total[k] += q1["counters"][k]
+    assert q["counters"] == total
+    assert q["s_dec"].dtype == np.float32 and q["s_dec"].shape == (R,)
+
+
+@pytest.mark.parametrize("fmt,target,rne_sat", [("nvfp4", 448.0, F.e4m3_rne_sat),
+                                                 ("ue5m3", 2048.0, F.ue5m3_rne_sat)])
+def test_row_scope_every_row_reaches_the_target_scale(fmt, target, rne_sat):
+    """Eq. 1 per row maps each row's largest local decode scale amax_r / 6
+    to T, so every nonzero row holds a block whose scale code is the code of
+    T (448: E4M3 0x7E; 2048: UE5M3 2^11).  With one tensor scale only the
+    row holding the tensor amax does."""
+    x = _rows_over_decades(42, 64, 12)
+    want = int(rne_sat(np.array([target], np.float32))[0][0])
+    q = Q.quantize(x, fmt, target=target, scope="row")
+    assert np.all(q["scales"].max(axis=1) == want)
+    qt = Q.quantize(x, fmt, target=target)
+    assert np.count_nonzero(qt["scales"].max(axis=1) == want) < 42 // 2
+
+
+def test_row_scope_power_of_two_row_scaling():
+    """Multiplying one row by 2^k (exact in bf16 and fp32) multiplies only
+    that row's amax and s_dec by 2^k and leaves every code and block scale
+    unchanged: the row's global scale absorbs the factor exactly."""
+    x = _rows_over_decades(16, 128, 13)
+    f = F.bf16_bits_to_f32(x)
+    q = Q.quantize(x, "nvfp4", scope="row")
+    for r, k in ((3, 7), (9, -5)):
+        g = f.copy()
+        g[r] *= np.float32(2.0 ** k)
+        q2 = Q.quantize(bits(g), "nvfp4", scope="row")
+        assert np.array_equal(q2["codes"], q["codes"])
+        assert np.array_equal(q2["scales"], q["scales"])
+        want = q["s_dec"].copy()
+        want[r] = np.float32(want[r] * np.float32(2.0 ** k))
+        assert np.array_equal(q2["s_dec"], want)
+        assert q2["amax"][r] == np.float32(q["amax"][r] * np.float32(2.0 ** k))
+
+
+def test_row_scope_keeps_small_rows_that_the_tensor_scale_loses():
+    """Rows 2^40 below the tensor amax fall under the E4M3 scale range with
+    one tensor scale (their block scales underflow to 0 and the rows decode
+    to 0); with per-row scales no block underflows and every row decodes
+    within the NVFP4 error (relative Frobenius error below 0.15)."""
+    R, C = 21, 64
+    x = _rows_over_decades(R, C, 14)
+    f = F.bf16_bits_to_f32(x).astype(np.float64)
+    qr = Q.quantize(x, "nvfp4", scope="row")
+    qt = Q.quantize(x, "nvfp4")
+    assert qr["counters"]["scale_underflow"] == 0
+    assert qt["counters"]["scale_underflow"] > 0
+    vr = Q.dequantize(qr["codes"], qr["scales"], "nvfp4", "1d", qr["s_dec"], R, C)
+    vt = Q.dequantize(qt["codes"], qt["scales"], "nvfp4", "1d", qt["s_dec"], R, C)
+    err_r = np.linalg.norm(vr - f, axis=1) / np.linalg.norm(f, axis=1)
+    err_t = np.linalg.norm(vt - f, axis=1) / np.linalg.norm(f, axis=1)
+    assert np.all(err_r < 0.15), err_r
+    assert err_t[0] == 1.0          # row 0 (scale 2^-20) decodes to all zeros
