@@ -24,6 +24,8 @@ BLOCK_1D, BLOCK_2D16 = 0, 1
 ROWWISE, COLWISE = 0, 1
 SCALES_ROWMAJOR, SCALES_TILED = 0, 1
 SCALE_LAYOUTS = {"rowmajor": SCALES_ROWMAJOR, "tiled": SCALES_TILED}
+GLOBAL_TENSOR, GLOBAL_ROW = 0, 1
+GLOBAL_SCOPES = {"tensor": GLOBAL_TENSOR, "row": GLOBAL_ROW}
 COUNTER_NAMES = ("scale_saturated", "scale_underflow", "scale_subnormal",
                  "elem_saturated", "elem_underflow")
 
@@ -40,7 +42,8 @@ class QuantDesc(ctypes.Structure):
                 ("rht", ctypes.c_int), ("rht_signs", ctypes.c_uint32), ("target", ctypes.c_float),
                 ("amax_given", ctypes.c_int), ("emit_transpose", ctypes.c_int),
                 ("scale_layout", ctypes.c_int), ("rht_n", ctypes.c_int),
-                ("rht_signs_hi", ctypes.c_uint32 * 3), ("scale_round", ctypes.c_int)]
+                ("rht_signs_hi", ctypes.c_uint32 * 3), ("scale_round", ctypes.c_int),
+                ("global_scope", ctypes.c_int)]
 
 
 SCALE_ROUND = {"rne": 0, "up": 1}
@@ -57,7 +60,8 @@ class Operand(ctypes.Structure):
     _fields_ = [("format", ctypes.c_int), ("codes", ctypes.c_void_p), ("ld_codes", ctypes.c_int64),
                 ("scales", ctypes.c_void_p), ("scale_stride_row", ctypes.c_int64),
                 ("scale_stride_kblk", ctypes.c_int64), ("scale_row_group", ctypes.c_int32),
-                ("s_dec", ctypes.c_void_p), ("scale_layout", ctypes.c_int)]
+                ("s_dec", ctypes.c_void_p), ("scale_layout", ctypes.c_int),
+                ("s_dec_scope", ctypes.c_int)]
 
 
 _lib = None
@@ -80,7 +84,7 @@ def load_library(path=LIB_PATH):
                                  vp, vp, vp]
     lib.fp4_quantize_dual.argtypes = [ctypes.POINTER(QuantDesc), ctypes.POINTER(QuantDesc), vp, i64,
                                       i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
-    lib.fp4_dequantize.argtypes = [i32, i32, i32, vp, vp, vp, i64, i64, vp, i32, vp]
+    lib.fp4_dequantize.argtypes = [i32, i32, i32, vp, vp, vp, i32, i64, i64, vp, i32, vp]
     lib.fp4_rht16.argtypes = [ctypes.POINTER(QuantDesc), vp, i64, i64, i64, vp, vp]
     lib.fp4_gemm.argtypes = [ctypes.POINTER(Operand), ctypes.POINTER(Operand), i64, i64, i64, vp,
                              i64, i32, vp]
@@ -157,10 +161,11 @@ class Quantized:
     codes: torch.Tensor     # uint8 [rows, cols/2]
     scales: torch.Tensor    # uint8 1D: [rows, cols/BS] (TILED: flat, tiled_scale_bytes);
                             # 2D: [rows/16, cols/16]
-    s_dec: torch.Tensor     # fp32 [1]
-    amax: torch.Tensor      # fp32 [1] (two-level formats)
+    s_dec: torch.Tensor     # fp32 [1], or [rows] with per-row global scales
+    amax: torch.Tensor      # fp32 [1] or [rows] (two-level formats)
     codes_t: torch.Tensor = None   # 2D with emit_transpose: [cols, rows/2]
     scale_layout: int = SCALES_ROWMAJOR
+    scope: int = GLOBAL_TENSOR     # GLOBAL_ROW: one global scale per row
 
     def operand(self, transposed=False):
         """GEMM operand over the K-major code matrix (K = cols), or for 2D
@@ -173,7 +178,8 @@ class Quantized:
         if self.block == BLOCK_1D:
             assert not transposed
             op = Operand(self.fmt, self.codes.data_ptr(), self.cols // 2, self.scales.data_ptr(),
-                         self.cols // bs, 1, 1, self.s_dec.data_ptr(), self.scale_layout)
+                         self.cols // bs, 1, 1, self.s_dec.data_ptr(), self.scale_layout,
+                         self.scope)
         elif not transposed:
             op = Operand(self.fmt, self.codes.data_ptr(), self.cols // 2, self.scales.data_ptr(),
                          self.cols // 16, 1, 16, self.s_dec.data_ptr(), SCALES_ROWMAJOR)
@@ -193,15 +199,17 @@ def tiled_scale_bytes(rows, blocks_per_row):
 
 def quantize(x, fmt="nvfp4", block="1d", orient="row", rnd="rne", seed=0, offset=0, rht=False,
              signs=0, target=448.0, amax_in=None, emit_transpose=False, counters=None,
-             scale_layout="rowmajor", rht_n=16, scale_round="rne"):
+             scale_layout="rowmajor", rht_n=16, scale_round="rne", global_scope="tensor"):
     """Quantize a bf16 [R, C] matrix.  orient="col" quantizes X^T ([C, R]).
     scale_layout: "rowmajor" or "tiled" (1D blocks only).  rht_n: size of
     the RHT (4, 16, 32, 64, 128); signs: its sign mask, up to 128 bits.
     scale_round: "rne" or "up" (truncation-free block scales).
+    global_scope: "tensor" or "row" (rowwise 1D NVFP4 / UE5M3: one global
+    scale per row, amax and s_dec of R entries, no separate amax pass).
 
     amax_in: None -> computed on the device; else a device fp32 [1] tensor read
-    as the (possibly stale) tensor amax.  counters: optional device uint64 [5]
-    tensor, accumulated.
+    as the (possibly stale) tensor amax ([R] per-row amaxes with "row").
+    counters: optional device uint64 [5] tensor, accumulated.
     """
     x = _as_bf16_bits(x)
     f = _fmt(fmt)
@@ -221,18 +229,20 @@ def quantize(x, fmt="nvfp4", block="1d", orient="row", rnd="rne", seed=0, offset
         scales = torch.empty((rows, cols // bs), dtype=torch.uint8, device=dev)
     codes_t = (torch.empty((cols, rows // 2), dtype=torch.uint8, device=dev)
                if emit_transpose else None)
-    s_dec = torch.empty(1, dtype=torch.float32, device=dev)
-    am = amax_in if amax_in is not None else torch.empty(1, dtype=torch.float32, device=dev)
+    scope = GLOBAL_SCOPES[global_scope]
+    n_g = rows if scope == GLOBAL_ROW else 1
+    s_dec = torch.empty(n_g, dtype=torch.float32, device=dev)
+    am = amax_in if amax_in is not None else torch.empty(n_g, dtype=torch.float32, device=dev)
     s_lo, s_hi = _sign_words(signs)
     desc = QuantDesc(f, blk, COLWISE if col else ROWWISE, SR if rnd == "sr" else RNE,
                      int(seed), int(offset), int(bool(rht)), s_lo, float(target),
                      int(amax_in is not None), int(bool(emit_transpose)), layout, int(rht_n), s_hi,
-                     SCALE_ROUND[scale_round])
+                     SCALE_ROUND[scale_round], scope)
     lib = load_library()
     _check(lib.fp4_quantize(ctypes.byref(desc), _ptr(x), R, C, x.stride(0), _ptr(codes),
                             _ptr(scales), _ptr(codes_t), _ptr(am), _ptr(s_dec), _ptr(counters),
                             _stream(dev)), "fp4_quantize")
-    return Quantized(f, blk, rows, cols, codes, scales, s_dec, am, codes_t, layout)
+    return Quantized(f, blk, rows, cols, codes, scales, s_dec, am, codes_t, layout, scope)
 
 
 def _scales_1d(rows, blocks, layout, dev):
@@ -305,7 +315,7 @@ def dequantize(q: Quantized, out_dtype=torch.float32):
     out = torch.empty((q.rows, q.cols), dtype=out_dtype, device=q.codes.device)
     lib = load_library()
     _check(lib.fp4_dequantize(q.fmt, q.block, q.scale_layout, _ptr(q.codes), _ptr(q.scales),
-                              _ptr(q.s_dec),
+                              _ptr(q.s_dec), q.scope,
                               q.rows, q.cols, _ptr(out), int(out_dtype == torch.float32),
                               _stream(out.device)), "fp4_dequantize")
     return out

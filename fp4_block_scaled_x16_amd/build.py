@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 # (source, object name, extra flags): gemm_nv_dma.hip is built once per
 # block-scale format and tile height so the four kernel families compile in
 # parallel
-SOURCES = [("quant.hip", "quant", []), ("gemm.hip", "gemm", []), ("gemm_nv.hip", "gemm_nv", [])] + [
+SOURCES = [("quant.hip", "quant", []), ("quant_rowscope.hip", "quant_rowscope", []), ("gemm.hip", "gemm", []), ("gemm_nv.hip", "gemm_nv", [])] + [
     ("gemm_nv_dma.hip", "gemm_nv_dma_%d_%d" % (f, mi), ["-DFP4_DMA_FMT=%d" % f, "-DFP4_DMA_MI=%d" % mi])
     for f in (0, 1) for mi in (4, 3)] + [
     ("gemm_mx.hip", "gemm_mx", []), ("gemm_mx_dma.hip", "gemm_mx_dma", []),

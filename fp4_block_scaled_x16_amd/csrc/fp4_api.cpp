@@ -105,6 +105,9 @@ FP4_EXPORT fp4_status fp4_amax(const fp4_quant_desc* d, const uint16_t* x, int64
   fp4_status st = check_bf16_input(x, rows, cols, ld);
   if (st) return st;
   if (!amax) return fail(FP4_ERR_ARG, "amax is null");
+  if (d->global_scope != FP4_GLOBAL_TENSOR)
+    return fail(FP4_ERR_UNSUPPORTED, "fp4_amax computes the tensor amax only (per-row amaxes "
+                                     "come from fp4_quantize with global_scope ROW)");
   st = check_rht(d, "desc");
   if (st) return st;
   const bool along_rows = d->orient == FP4_ROWWISE;
@@ -143,6 +146,11 @@ FP4_EXPORT fp4_status fp4_quantize(const fp4_quant_desc* d, const uint16_t* x, i
   st = check_rht(d, "desc");
   if (st) return st;
   if (d->amax_given && !two_level) return fail(FP4_ERR_UNSUPPORTED, "MXFP4 has no tensor amax");
+  if (d->global_scope != FP4_GLOBAL_TENSOR && d->global_scope != FP4_GLOBAL_ROW)
+    return fail(FP4_ERR_ARG, "bad global_scope %d", (int)d->global_scope);
+  const bool row_scope = d->global_scope == FP4_GLOBAL_ROW;
+  if (row_scope && (!two_level || is2d || d->orient != FP4_ROWWISE))
+    return fail(FP4_ERR_UNSUPPORTED, "global_scope ROW needs NVFP4 or UE5M3, 1D, ROWWISE");
   if (!is2d && d->emit_transpose) return fail(FP4_ERR_UNSUPPORTED, "emit_transpose needs 2D16");
   if (d->scale_layout != FP4_SCALES_ROWMAJOR && d->scale_layout != FP4_SCALES_TILED)
     return fail(FP4_ERR_ARG, "bad scale_layout %d", (int)d->scale_layout);
@@ -176,7 +184,7 @@ FP4_EXPORT fp4_status fp4_quantize(const fp4_quant_desc* d, const uint16_t* x, i
   if (two_level && !amax) return fail(FP4_ERR_ARG, "amax is null");
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (two_level && !d->amax_given) {
+  if (two_level && !d->amax_given && !row_scope) {
     uint32_t s4[4];
     copy_signs(d, s4);
     hipError_t e = fp4lib::launch_amax(x, rows, cols, ld, d->rht, rht_size(d), s4, amax, s,
@@ -205,8 +213,10 @@ FP4_EXPORT fp4_status fp4_quantize(const fp4_quant_desc* d, const uint16_t* x, i
   a.rht = d->rht;
   a.emit_transpose = d->emit_transpose;
   a.tiled = tiled ? 1 : 0;
+  a.amax_given = d->amax_given ? 1 : 0;
   hipError_t e;
-  if (is2d) e = fp4lib::launch_quant_2d(a, s);
+  if (row_scope) e = fp4lib::launch_quant_row_scoped(a, s);
+  else if (is2d) e = fp4lib::launch_quant_2d(a, s);
   else if (d->orient == FP4_ROWWISE) e = fp4lib::launch_quant_row(a, s);
   else e = fp4lib::launch_quant_col(a, s);
   return device_status(e, "fp4_quantize launch");
@@ -240,6 +250,9 @@ FP4_EXPORT fp4_status fp4_quantize_dual(const fp4_quant_desc* rd, const fp4_quan
       return fail(FP4_ERR_UNSUPPORTED, "%s: MXFP4 has no tensor amax", side);
     if (d->scale_round != FP4_SCALE_RNE && d->scale_round != FP4_SCALE_UP)
       return fail(FP4_ERR_ARG, "%s: bad scale_round %d", side, (int)d->scale_round);
+    if (d->global_scope != FP4_GLOBAL_TENSOR)
+      return fail(FP4_ERR_UNSUPPORTED, "%s: dual quantization has tensor-scope global scales "
+                                       "(per-row scales: fp4_quantize ROWWISE)", side);
   }
   if (rd->orient != FP4_ROWWISE || cd->orient != FP4_COLWISE)
     return fail(FP4_ERR_UNSUPPORTED, "descs must be ROWWISE then COLWISE");
@@ -336,8 +349,9 @@ FP4_EXPORT fp4_status fp4_quantize_dual(const fp4_quant_desc* rd, const fp4_quan
 
 FP4_EXPORT fp4_status fp4_dequantize(fp4_format format, fp4_block block,
                                      fp4_scale_layout scale_layout, const uint8_t* codes,
-                                     const uint8_t* scales, const float* s_dec, int64_t rows,
-                                     int64_t cols, void* out, int out_fp32, void* stream) {
+                                     const uint8_t* scales, const float* s_dec,
+                                     fp4_global_scope s_dec_scope, int64_t rows, int64_t cols,
+                                     void* out, int out_fp32, void* stream) {
   if (!valid_format(format)) return fail(FP4_ERR_ARG, "bad format %d", (int)format);
   if (block != FP4_BLOCK_1D && block != FP4_BLOCK_2D16) return fail(FP4_ERR_ARG, "bad block %d", (int)block);
   if (scale_layout != FP4_SCALES_ROWMAJOR && scale_layout != FP4_SCALES_TILED)
@@ -346,6 +360,11 @@ FP4_EXPORT fp4_status fp4_dequantize(fp4_format format, fp4_block block,
   if (tiled && block == FP4_BLOCK_2D16) return fail(FP4_ERR_UNSUPPORTED, "TILED scales are for 1D blocks");
   if (block == FP4_BLOCK_2D16 && format == FP4_MXFP4)
     return fail(FP4_ERR_UNSUPPORTED, "2D16 blocks need NVFP4 or UE5M3");
+  if (s_dec_scope != FP4_GLOBAL_TENSOR && s_dec_scope != FP4_GLOBAL_ROW)
+    return fail(FP4_ERR_ARG, "bad s_dec_scope %d", (int)s_dec_scope);
+  const bool s_dec_rows = s_dec_scope == FP4_GLOBAL_ROW;
+  if (s_dec_rows && (format == FP4_MXFP4 || block != FP4_BLOCK_1D))
+    return fail(FP4_ERR_UNSUPPORTED, "per-row s_dec needs NVFP4 or UE5M3 and 1D blocks");
   if (rows < 0 || cols < 0) return fail(FP4_ERR_SHAPE, "negative size");
   const int bs = block_len(format);
   if (cols % bs) return fail(FP4_ERR_SHAPE, "cols=%lld must be a multiple of %d", (long long)cols, bs);
@@ -358,7 +377,7 @@ FP4_EXPORT fp4_status fp4_dequantize(fp4_format format, fp4_block block,
   }
   if (rows == 0 || cols == 0) return ok();
   return device_status(fp4lib::launch_dequant(format, block == FP4_BLOCK_2D16, tiled, codes, scales,
-                                              s_dec, rows, cols, out, out_fp32,
+                                              s_dec, s_dec_rows, rows, cols, out, out_fp32,
                                               static_cast<hipStream_t>(stream)),
                        "fp4_dequantize launch");
 }
@@ -408,6 +427,11 @@ FP4_EXPORT fp4_status fp4_gemm(const fp4_operand* A, const fp4_operand* B, int64
       return fail(FP4_ERR_UNSUPPORTED, "operand %c: TILED scales need scale_row_group 1", "AB"[i]);
     if (o->scale_row_group == 16 && A->format == FP4_MXFP4)
       return fail(FP4_ERR_UNSUPPORTED, "2D16 scales need NVFP4 or UE5M3");
+    if (o->s_dec_scope != FP4_GLOBAL_TENSOR && o->s_dec_scope != FP4_GLOBAL_ROW)
+      return fail(FP4_ERR_ARG, "operand %c: bad s_dec_scope %d", "AB"[i], (int)o->s_dec_scope);
+    if (o->s_dec_scope == FP4_GLOBAL_ROW && (A->format == FP4_MXFP4 || !o->s_dec))
+      return fail(FP4_ERR_UNSUPPORTED, "operand %c: per-row s_dec needs NVFP4 or UE5M3 and a "
+                                       "non-null s_dec", "AB"[i]);
     if (M > 0 && N > 0 && K > 0) {
       if (!o->codes || !o->scales) return fail(FP4_ERR_ARG, "operand %c has a null pointer", "AB"[i]);
       if (o->ld_codes < K / 2) return fail(FP4_ERR_ARG, "operand %c ld_codes < K/2", "AB"[i]);
@@ -425,10 +449,10 @@ FP4_EXPORT fp4_status fp4_gemm(const fp4_operand* A, const fp4_operand* B, int64
   if (M == 0 || N == 0) return ok();
   fp4lib::GemmOperand a{A->codes, A->ld_codes, A->scales, A->scale_stride_row,
                         A->scale_stride_kblk, A->scale_row_group, A->s_dec,
-                        A->scale_layout == FP4_SCALES_TILED};
+                        A->scale_layout == FP4_SCALES_TILED, A->s_dec_scope == FP4_GLOBAL_ROW};
   fp4lib::GemmOperand b{B->codes, B->ld_codes, B->scales, B->scale_stride_row,
                         B->scale_stride_kblk, B->scale_row_group, B->s_dec,
-                        B->scale_layout == FP4_SCALES_TILED};
+                        B->scale_layout == FP4_SCALES_TILED, B->s_dec_scope == FP4_GLOBAL_ROW};
   return device_status(fp4lib::launch_gemm(A->format, a, b, M, N, K, D, ldd, accumulate,
                                            static_cast<hipStream_t>(stream)),
                        "fp4_gemm launch");

@@ -16,7 +16,8 @@ struct QuantArgs {
   uint8_t* codes;
   uint8_t* scales;
   uint8_t* codes_t;
-  const float* amax;     // device; read by the quantize kernel (MXFP4: unused)
+  const float* amax;     // device; read by the quantize kernel (MXFP4: unused);
+                         // per-row scope: float[rows], written unless amax_given
   float* s_dec;          // device or null
   fp4_counters* counters;
   float target;
@@ -26,6 +27,7 @@ struct QuantArgs {
   int format, round, rht, emit_transpose;
   int tiled;             // 1D scales in the TILED layout (2 KiB atoms of 256 rows x 8 blocks)
   int scale_up;          // block scales rounded up (truncation-free), two-level formats
+  int amax_given;        // per-row scope: read amax[r] instead of computing it
 };
 
 struct GemmOperand {
@@ -36,6 +38,7 @@ struct GemmOperand {
   int row_group;
   const float* s_dec;
   bool tiled;            // scales in the TILED layout (strides unused)
+  bool s_dec_rows;       // s_dec holds one decode scale per operand row
 };
 
 // Number of compute units of the current device (cached per device).
@@ -48,14 +51,18 @@ hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld
                        int rht_n, const uint32_t (&signs)[4], float* amax, hipStream_t s,
                        float* amax_plain = nullptr, bool along_rows = false);
 hipError_t launch_quant_row(const QuantArgs& a, hipStream_t s);
+// Rowwise 1D with one global scale per row (two-level formats): the row
+// amaxes (a.amax, float[rows]) come from the same read that quantizes.
+hipError_t launch_quant_row_scoped(const QuantArgs& a, hipStream_t s);
 hipError_t launch_quant_col(const QuantArgs& a, hipStream_t s);
 hipError_t launch_quant_2d(const QuantArgs& a, hipStream_t s);
 // Rowwise (`row`) and colwise (`col`) 1D quantization of the same input in
 // one kernel: same format and rounding mode; RHT only on the colwise side.
 hipError_t launch_quant_dual(const QuantArgs& row, const QuantArgs& col, hipStream_t s);
+// s_dec_rows: s_dec holds one decode scale per row.
 hipError_t launch_dequant(int format, int block2d, int tiled, const uint8_t* codes,
-                          const uint8_t* scales, const float* s_dec, int64_t rows, int64_t cols,
-                          void* out, int out_fp32, hipStream_t s);
+                          const uint8_t* scales, const float* s_dec, bool s_dec_rows,
+                          int64_t rows, int64_t cols, void* out, int out_fp32, hipStream_t s);
 // The RHT of size rht_n (0 means 16) alone, along the rows or the columns.
 hipError_t launch_rht(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int rht_n,
                       const uint32_t (&signs)[4], bool along_rows, float* y, hipStream_t s);

@@ -109,6 +109,7 @@ hipError_t launch_gemm(int format, const GemmOperand& A, const GemmOperand& B, i
     p.sc_vec[o] = p.tiled[o] || (ops[o]->s_kblk == 1 && ops[o]->s_row % sv == 0 &&
                                  reinterpret_cast<uintptr_t>(ops[o]->scales) % sv == 0);
     p.s_dec[o] = format == FP4_MXFP4 ? nullptr : ops[o]->s_dec;
+    p.s_dec_rows[o] = p.s_dec[o] && ops[o]->s_dec_rows ? 1 : 0;
   }
   p.D = D;
   p.ldd = ldd;

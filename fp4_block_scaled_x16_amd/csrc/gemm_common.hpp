@@ -32,6 +32,7 @@ struct Params {
   int64_t s_row[2], s_kblk[2];
   int rg_shift[2];      // log2 of the scale row group (0 or 4)
   const float* s_dec[2];
+  int s_dec_rows[2];    // s_dec holds one decode scale per operand row (per-row global scale)
   float* D;
   int64_t ldd;
   int64_t M, N, K;
@@ -87,11 +88,55 @@ __device__ __forceinline__ uint4 load_codes16(const uint8_t* row, int64_t off, i
 // 4, the 4 consecutive columns 8g + 4h .. +3 of a 32 x 32 tile: the
 // epilogue writes 16 bytes per store.
 // MI 32-row MFMA tiles per wave in M (a wave covers MI * 32 rows).
+// `scale` is the tensor-level s_dec_B (1 when B has per-row scales).  Per-row
+// decode scales (s_dec_A[m], s_dec_B[n]) are loaded before the first store
+// and multiplied into the accumulators: a wait for a load issued between
+// stores would wait for those stores too.
 template <int MI>
 __device__ __forceinline__ void epilogue(const Params& p, floatx16 (&acc)[MI][4], float scale,
                                          int64_t m0, int64_t n0, int wm, int wn, int lane) {
   const int i = lane & 31, h = lane >> 5;
   const bool vec = (p.ldd & 3) == 0 && (reinterpret_cast<uintptr_t>(p.D) & 15) == 0;
+  if (p.s_dec_rows[0]) {
+    float sa[MI];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+      const int64_t row = m0 + wm * (MI * 32) + mi * 32 + i;
+      sa[mi] = row < p.M ? p.s_dec[0][row] : 1.0f;
+    }
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) acc[mi][ni] *= sa[mi];
+  }
+  if (p.s_dec_rows[1]) {
+    const bool vec_b = (reinterpret_cast<uintptr_t>(p.s_dec[1]) & 15) == 0;
+    float cb[4][16];
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t col = n0 + wn * 128 + ni * 32 + 8 * g + 4 * h;
+        if (vec_b && col + 3 < p.N) {
+          const float4 t = *reinterpret_cast<const float4*>(p.s_dec[1] + col);
+          cb[ni][4 * g] = t.x;
+          cb[ni][4 * g + 1] = t.y;
+          cb[ni][4 * g + 2] = t.z;
+          cb[ni][4 * g + 3] = t.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            cb[ni][4 * g + e] = col + e < p.N ? p.s_dec[1][col + e] : 1.0f;
+        }
+      }
+    }
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int k = 0; k < 16; ++k) acc[mi][ni][k] *= cb[ni][k];
+  }
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
     const int64_t row = m0 + wm * (MI * 32) + mi * 32 + i;

@@ -196,9 +196,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level(Params p) {
   }
 
   float scale = FMT == kUE ? 1024.0f : 1.0f;   // undo the two 2^-5 scale shifts
-  if (p.s_dec[0]) scale *= *p.s_dec[0];
+  if (p.s_dec[0] && !p.s_dec_rows[0]) scale *= *p.s_dec[0];
   // s_B is applied as a second multiply so that s_A * s_B never under/overflows alone
-  const float sb = p.s_dec[1] ? *p.s_dec[1] : 1.0f;
+  const float sb = p.s_dec[1] && !p.s_dec_rows[1] ? *p.s_dec[1] : 1.0f;
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll

@@ -258,8 +258,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level_dma(Params p) {
   wait_vmcnt<0>();                         // the last (unused) scale loads
 
   float scale = FMT == kUE ? 1024.0f : 1.0f;   // undo the two 2^-5 scale shifts
-  if (p.s_dec[0]) scale *= *p.s_dec[0];
-  const float sb = p.s_dec[1] ? *p.s_dec[1] : 1.0f;
+  if (p.s_dec[0] && !p.s_dec_rows[0]) scale *= *p.s_dec[0];
+  const float sb = p.s_dec[1] && !p.s_dec_rows[1] ? *p.s_dec[1] : 1.0f;
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll

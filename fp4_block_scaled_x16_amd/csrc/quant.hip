@@ -17,8 +17,10 @@
 
 #include "fp4_device.hpp"
 #include "fp4_internal.hpp"
+#include "quant_common.hpp"
 
 using namespace fp4dev;
+using namespace fp4quant;
 
 namespace {
 
@@ -31,109 +33,6 @@ constexpr int kRowWgPerCu = 2;      // rowwise, RNE and SR
 constexpr int kColWgPerCuSR = 4;    // colwise with stochastic rounding
 constexpr int kTileWgPerCu = 3;     // colwise / dual RNE, 2D
 constexpr int kAmaxWgPerCu = 1;     // tensor amax (plain and 16-point RHT)
-
-// Same-address global atomics serialize (about 12 ns each on MI355X once
-// more than a few hundred arrive), so every kernel runs a persistent grid
-// of one or two workgroups per CU, reduces in LDS, and issues at most one
-// atomic per workgroup and counter.
-
-// ----------------------------------------------------------- counters --
-// Reduce five per-thread event counts over the workgroup and add the
-// nonzero totals to the caller's device counters (one atomic each).
-template <int NT>
-__device__ __forceinline__ void flush_counters(uint32_t (&c)[5], fp4_counters* out) {
-  __shared__ uint32_t red[NT / 64][5];
-#pragma unroll
-  for (int k = 0; k < 5; ++k) {
-    uint32_t v = c[k];
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    c[k] = v;
-  }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) {
-#pragma unroll
-    for (int k = 0; k < 5; ++k) red[wave][k] = c[k];
-  }
-  __syncthreads();
-  if (threadIdx.x < 5) {
-    uint32_t t = 0;
-#pragma unroll
-    for (int w = 0; w < NT / 64; ++w) t += red[w][threadIdx.x];
-    if (t) {
-      unsigned long long* dst = reinterpret_cast<unsigned long long*>(out) + threadIdx.x;
-      atomicAdd(dst, static_cast<unsigned long long>(t));
-    }
-  }
-}
-
-__device__ __forceinline__ void unpack8(const uint4& q, float* v) {
-  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
-    v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
-  }
-}
-
-// Quantize BS values (already in fp32, in block order) with the encode
-// scale; returns BS/8 packed code words (element i at bits 4 (i % 8) of
-// word i / 8).  `idx0` is the output-layout index of element 0 (SR only).
-// Counters, per lane: cnt[3] += #(|y| > 6); cnt[4] += NZX * #(x != 0) -
-// #(code != 0), the number of nonzero inputs coded as zero (a zero input
-// always codes to zero).  NZX = 2 lets one side of the dual quantizer count
-// the nonzero inputs for both sides (NZX = 0 on the other).  Per-lane
-// counts keep the tests on the vector unit; wave ballots would hold one
-// 64-bit mask per test in scalar registers, which spill.
-template <int BS, int RND, bool CNT, int NZX = 1>
-__device__ __forceinline__ void encode_block(const float* v, float s_enc_l, uint64_t idx0,
-                                             uint64_t seed, uint64_t offset, uint32_t* words,
-                                             uint32_t (&cnt)[5]) {
-  // SR on 32-element blocks: one Philox group at a time keeps registers low
-  constexpr int kGroupUnroll = (RND == FP4_SR && BS > 16) ? 1 : BS / 8;
-#pragma unroll kGroupUnroll
-  for (int q = 0; q < BS / 8; ++q) {
-    float y[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = v[q * 8 + i] * s_enc_l;
-    uint32_t word = 0;
-    if constexpr (RND == FP4_SR) {
-      const U4 rw = sr_words((idx0 >> 3) + q, seed, offset);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) word |= e2m1_sr(y[i], sr_bits(rw, i)) << (4 * i);
-    } else {
-      word = e2m1_rne_pair<0>(word, y[0], y[1]);
-      word = e2m1_rne_pair<1>(word, y[2], y[3]);
-      word = e2m1_rne_pair<2>(word, y[4], y[5]);
-      word = e2m1_rne_pair<3>(word, y[6], y[7]);
-    }
-    words[q] = word;
-    if constexpr (CNT) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        cnt[3] += fabsf(y[i]) > 6.0f ? 1u : 0u;
-        if constexpr (NZX > 0) cnt[4] += v[q * 8 + i] != 0.0f ? static_cast<uint32_t>(NZX) : 0u;
-      }
-      cnt[4] -= nonzero_codes(word);
-    }
-  }
-}
-
-template <int FMT>
-__device__ __forceinline__ uint32_t scale_for_block(float amax_b, float s_enc_g, float s_dec_g,
-                                                    float& s_enc_l, uint32_t (&cnt)[5],
-                                                    bool up) {
-  if constexpr (FMT == kMX) {
-    return block_scale_mx(amax_b, s_enc_l);
-  } else {
-    ScaleEvents ev{0, 0, 0};
-    const uint32_t sc = block_scale_two_level<FMT>(amax_b, s_enc_g, s_dec_g, s_enc_l, ev, up);
-    cnt[0] += ev.sat;
-    cnt[1] += ev.under;
-    cnt[2] += ev.sub;
-    return sc;
-  }
-}
 
 // ---------------------------------------------------------------- amax --
 __global__ void k_fill_u32(uint32_t* p, uint32_t v) { *p = v; }
@@ -692,20 +591,22 @@ __global__ __launch_bounds__(kThreads) void k_quant_2d(
 
 // ---------------------------------------------------------- dequantize --
 // One thread per block of BS codes of a [rows, cols] code matrix.
+// sd_rows: s_dec holds one decode scale per row (per-row global scale).
 template <int FMT, bool B2D, bool F32>
 __global__ __launch_bounds__(kStream) void k_dequant(const uint8_t* __restrict__ codes,
                                                       const uint8_t* __restrict__ scales,
                                                       const float* __restrict__ s_dec,
-                                                      int64_t rows, int64_t cols,
+                                                      int sd_rows, int64_t rows, int64_t cols,
                                                       void* __restrict__ out, int tiled) {
   constexpr int BS = FMT == kMX ? 32 : 16;
-  const float sd = (FMT == kMX) ? 1.0f : *s_dec;
+  const float sd_tensor = (FMT == kMX || sd_rows) ? 1.0f : *s_dec;
   const uint64_t bpr = static_cast<uint64_t>(cols) / BS;
   const uint64_t n = static_cast<uint64_t>(rows) * bpr;
   const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kStream;
   for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kStream + threadIdx.x; i < n;
        i += stride) {
     const uint64_t r = i / bpr, j = i - r * bpr;
+    const float sd = (FMT != kMX && sd_rows) ? s_dec[r] : sd_tensor;
     const uint32_t sc = B2D     ? scales[(r >> 4) * bpr + j]
                         : tiled ? scales[tiled_scale_offset(r, j, (bpr + 7) >> 3)]
                                 : scales[i];
@@ -833,14 +734,6 @@ __global__ __launch_bounds__(kStream) void k_rht_gen(const uint16_t* __restrict_
   if constexpr (AMX) flush_max<kStream>(__float_as_uint(m), amax_out);
 }
 
-// Persistent grid: enough workgroups of `threads` for the work, at most
-// per_cu per CU.
-int grid_for(uint64_t work_items, int per_cu, int threads = kStream) {
-  const uint64_t want = (work_items + threads - 1) / threads;
-  const uint64_t cap = static_cast<uint64_t>(fp4lib::device_cu_count()) * per_cu;
-  const uint64_t g = want < cap ? want : cap;
-  return static_cast<int>(g ? g : 1);
-}
 
 }  // namespace
 
@@ -860,14 +753,6 @@ int device_cu_count() {
   return cache[dev];
 }
 
-// The RHT of size n (0 means 16) with the 128-bit sign mask s4.
-static RhtN make_rht(int n, const uint32_t (&s4)[4]) {
-  RhtN r;
-  r.n = n ? n : 16;
-  r.scale = static_cast<float>(1.0 / std::sqrt(static_cast<double>(r.n)));
-  for (int i = 0; i < 4; ++i) r.s[i] = s4[i];
-  return r;
-}
 
 hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int rht,
                        int rht_n, const uint32_t (&signs)[4], float* amax, hipStream_t s,
@@ -1064,30 +949,32 @@ hipError_t launch_quant_2d(const QuantArgs& a, hipStream_t s) {
 
 template <int FMT, bool B2D>
 static void dq_launch(int tiled, const uint8_t* codes, const uint8_t* scales, const float* s_dec,
-                      int64_t rows, int64_t cols, void* out, int out_fp32, hipStream_t s) {
+                      int sd_rows, int64_t rows, int64_t cols, void* out, int out_fp32,
+                      hipStream_t s) {
   constexpr int BS = FMT == kMX ? 32 : 16;
   const uint64_t n = static_cast<uint64_t>(rows) * static_cast<uint64_t>(cols / BS);
   const int grid = grid_for(n, 2);
   if (out_fp32)
     hipLaunchKernelGGL((k_dequant<FMT, B2D, true>), dim3(grid), dim3(kStream), 0, s, codes,
-                       scales, s_dec, rows, cols, out, tiled);
+                       scales, s_dec, sd_rows, rows, cols, out, tiled);
   else
     hipLaunchKernelGGL((k_dequant<FMT, B2D, false>), dim3(grid), dim3(kStream), 0, s, codes,
-                       scales, s_dec, rows, cols, out, tiled);
+                       scales, s_dec, sd_rows, rows, cols, out, tiled);
 }
 
 hipError_t launch_dequant(int format, int block2d, int tiled, const uint8_t* codes,
-                          const uint8_t* scales, const float* s_dec, int64_t rows, int64_t cols,
-                          void* out, int out_fp32, hipStream_t s) {
+                          const uint8_t* scales, const float* s_dec, bool s_dec_rows,
+                          int64_t rows, int64_t cols, void* out, int out_fp32, hipStream_t s) {
+  const int sr = s_dec_rows ? 1 : 0;
   if (rows > 0 && cols > 0) {
     if (format == FP4_NVFP4) {
-      if (block2d) dq_launch<kNV, true>(tiled, codes, scales, s_dec, rows, cols, out, out_fp32, s);
-      else dq_launch<kNV, false>(tiled, codes, scales, s_dec, rows, cols, out, out_fp32, s);
+      if (block2d) dq_launch<kNV, true>(tiled, codes, scales, s_dec, sr, rows, cols, out, out_fp32, s);
+      else dq_launch<kNV, false>(tiled, codes, scales, s_dec, sr, rows, cols, out, out_fp32, s);
     } else if (format == FP4_UE5M3) {
-      if (block2d) dq_launch<kUE, true>(tiled, codes, scales, s_dec, rows, cols, out, out_fp32, s);
-      else dq_launch<kUE, false>(tiled, codes, scales, s_dec, rows, cols, out, out_fp32, s);
+      if (block2d) dq_launch<kUE, true>(tiled, codes, scales, s_dec, sr, rows, cols, out, out_fp32, s);
+      else dq_launch<kUE, false>(tiled, codes, scales, s_dec, sr, rows, cols, out, out_fp32, s);
     } else {
-      dq_launch<kMX, false>(tiled, codes, scales, s_dec, rows, cols, out, out_fp32, s);
+      dq_launch<kMX, false>(tiled, codes, scales, s_dec, 0, rows, cols, out, out_fp32, s);
     }
   }
   return hipGetLastError();

@@ -80,6 +80,18 @@ typedef enum { FP4_SCALES_ROWMAJOR = 0, FP4_SCALES_TILED = 1 } fp4_scale_layout;
  * output is the [cols, rows] code matrix of X^T (Wgrad operands, §4.1). */
 typedef enum { FP4_ROWWISE = 0, FP4_COLWISE = 1 } fp4_orient;
 
+/* Span of the global (tensor-level) scale s_enc_G = 6 T / amax, s_dec_G =
+ * 1 / s_enc_G (NVFP4 paper App. B.1).  TENSOR: one amax over the whole
+ * tensor (a separate pass over x unless given).  ROW: App. B.1 closes by
+ * noting the global scale may span a row instead, so no extra round trip
+ * through device memory is needed: every row of a ROWWISE 1D code matrix
+ * gets its own amax_r = max_c |x[r, c]| (over the rotated row with an RHT),
+ * s_enc_r and s_dec_r, read in the same pass that quantizes the row; the
+ * GEMM applies s_dec_A[m] s_dec_B[n] to D[m, n].  (A COLWISE row is a
+ * column of x spanning every token, which a one-read tile pass cannot see
+ * whole before it encodes: COLWISE and 2D16 stay TENSOR.) */
+typedef enum { FP4_GLOBAL_TENSOR = 0, FP4_GLOBAL_ROW = 1 } fp4_global_scope;
+
 typedef enum {
   FP4_OK = 0,
   FP4_ERR_ARG = 1,          /* null pointer, bad enum, misaligned or bad stride  */
@@ -137,12 +149,17 @@ typedef struct {
   uint32_t rht_signs_hi[3];  /* D_r, bits 32-127 (N > 32); every bit at or
                              above N must be 0                                  */
   fp4_scale_round scale_round;  /* NVFP4/UE5M3 block scales: RNE or UP      */
+  fp4_global_scope global_scope;  /* TENSOR, or ROW (NVFP4/UE5M3, 1D ROWWISE,
+                             fp4_quantize only): amax and s_dec are then
+                             arrays of `rows` floats                          */
 } fp4_quant_desc;
 
 /*
  * fp4_amax -- tensor amax (NVFP4 paper App. B.1: amax_X = max |x_i|), the
  * one fp4_quantize computes for `desc` when amax_given = 0.
- *   desc  host; used: orient, rht, rht_n, rht_signs, rht_signs_hi.  With
+ *   desc  host; used: orient, rht, rht_n, rht_signs, rht_signs_hi,
+ *         global_scope (TENSOR only: fp4_quantize computes per-row amaxes
+ *         itself, in the pass that quantizes).  With
  *         rht the amax is taken over the rotated tensor (App. C: the scale
  *         is computed in the rotated space): every rht_n-element group along
  *         the blocked axis -- rows of a column for COLWISE, columns of a row
@@ -168,9 +185,12 @@ fp4_status fp4_amax(const fp4_quant_desc* desc /* host */, const uint16_t* x, in
  *   codes_t device, 2D16 with emit_transpose only: [cols, rows/2] codes of
  *           X^T quantized with the same tile scales (NULL otherwise).
  *   amax    device float.  NVFP4/UE5M3: written (amax_given = 0) or read
- *           (amax_given = 1).  MXFP4: unused, may be NULL.
+ *           (amax_given = 1).  MXFP4: unused, may be NULL.  global_scope
+ *           ROW: device float[rows], one amax per row, written or read
+ *           likewise (written in the quantizing pass, no separate pass).
  *   s_dec   device float or NULL: receives s_dec_G = 1 / s_enc_G (1 for
- *           MXFP4), the global decode scale the GEMM applies (App. B.3).
+ *           MXFP4), the global decode scale the GEMM applies (App. B.3);
+ *           global_scope ROW: device float[rows] or NULL, s_dec_r per row.
  *   counters device fp4_counters or NULL (events not counted).
  *   Shapes: the blocked axis (cols for ROWWISE, rows for COLWISE) must be a
  *   multiple of BS; 2D16 needs rows and cols multiples of 16; RHT needs 1D
@@ -196,6 +216,7 @@ fp4_status fp4_quantize(const fp4_quant_desc* desc /* host */,
  *
  *   row_desc  ROWWISE, 1D; its RHT (along the rows) with rht_n 4 or 16.
  *   col_desc  COLWISE, 1D; its RHT (along the columns) of any size.
+ *   Both: global_scope TENSOR (per-row scopes: fp4_quantize).
  *   Both: the same format and the same rounding mode (seed, offset, target,
  *   amax_given, scale_layout, scale_round and the RHT fields are per
  *   side).  When both amaxes are computed here with a 16-point RHT on the
@@ -225,12 +246,15 @@ fp4_status fp4_quantize_dual(const fp4_quant_desc* row_desc /* host */,
  * ROWWISE (or 2D16) [rows, cols] code matrix; 1D scales in scale_layout
  * (2D16 scales are always [rows/16, cols/16]).
  *   s_dec   device float (NVFP4/UE5M3); ignored (may be NULL) for MXFP4.
+ *   s_dec_scope  TENSOR: s_dec is one float; ROW (NVFP4/UE5M3, 1D): s_dec
+ *           is float[rows], row r decoded with s_dec[r].
  *   out     device, [rows, cols] row-major: fp32 if out_fp32, else bf16
  *           (v rounded to nearest even).
  */
 fp4_status fp4_dequantize(fp4_format format, fp4_block block, fp4_scale_layout scale_layout,
                           const uint8_t* codes, const uint8_t* scales, const float* s_dec,
-                          int64_t rows, int64_t cols, void* out, int out_fp32, void* stream);
+                          fp4_global_scope s_dec_scope, int64_t rows, int64_t cols, void* out,
+                          int out_fp32, void* stream);
 
 /*
  * fp4_rht16 -- the random Hadamard transform alone (NVFP4 paper §4.2,
@@ -271,10 +295,13 @@ typedef struct {
   int32_t scale_row_group;    /* 1 or 16 */
   const float* s_dec;         /* device s_dec_G; NULL means 1 (MXFP4 ignores it) */
   fp4_scale_layout scale_layout;
+  fp4_global_scope s_dec_scope;  /* TENSOR: s_dec is one float; ROW (NVFP4/UE5M3):
+                                 s_dec[rows], one per operand row (non-NULL) */
 } fp4_operand;
 
 /*
- * fp4_gemm -- D[M, N] (+)= s_dec_A * s_dec_B * sum_k a[m, k] * b[n, k],
+ * fp4_gemm -- D[M, N] (+)= s_dec_A * s_dec_B * sum_k a[m, k] * b[n, k]
+ * (s_dec_A[m] and s_dec_B[n] for operands with per-row global scales),
  * a = e2m1 * scale of A [M, K], b likewise of B [N, K] ("TN": both K-major).
  * This is the block-scaled product of NVFP4 paper App. B.3 (per-block
  * partial products scaled by both local decode scales, fp32 accumulation,

@@ -24,6 +24,7 @@ int main(void) {
   F(fp4_quant_desc, rht_n);
   F(fp4_quant_desc, rht_signs_hi);
   F(fp4_quant_desc, scale_round);
+  F(fp4_quant_desc, global_scope);
   printf("fp4_operand.__size__ %zu\n", sizeof(fp4_operand));
   F(fp4_operand, format);
   F(fp4_operand, codes);
@@ -34,6 +35,7 @@ int main(void) {
   F(fp4_operand, scale_row_group);
   F(fp4_operand, s_dec);
   F(fp4_operand, scale_layout);
+  F(fp4_operand, s_dec_scope);
   printf("fp4_counters.__size__ %zu\n", sizeof(fp4_counters));
   return 0;
 }

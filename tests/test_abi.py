@@ -88,6 +88,10 @@ def quant(lib, d, rows=32, cols=64, ld=None, x=FAKE, codes=FAKE, scales=FAKE, co
     (dict(), -1, 64, 2),
     (dict(scale_layout=2), 32, 64, 1),
     (dict(block=1, scale_layout=1), 32, 64, 3),      # TILED scales are 1D only
+    (dict(global_scope=2), 32, 64, 1),               # bad global scope
+    (dict(global_scope=1, format=2), 32, 64, 3),     # per-row scales: two-level formats
+    (dict(global_scope=1, orient=1), 32, 64, 3),     # per-row scales: ROWWISE only
+    (dict(global_scope=1, block=1), 32, 64, 3),      # per-row scales: 1D only
 ])
 def test_quantize_rejects(lib, kw, rows, cols, status):
     assert quant(lib, desc(**kw), rows, cols) == status
@@ -160,6 +164,8 @@ def dual(lib, rd, cd, rows=32, cols=64, x=FAKE, codes=FAKE, scales=FAKE, codes_t
     (dict(), dict(orient=1), 24, 64, 2),                      # rows % 16
     (dict(), dict(orient=1), 32, 40, 2),                      # cols % 16
     (dict(format=2), dict(orient=1, format=2), 48, 64, 2),    # rows % 32
+    (dict(global_scope=1), dict(orient=1), 32, 64, 3),        # per-row scales: fp4_quantize
+    (dict(), dict(orient=1, global_scope=1), 32, 64, 3),
 ])
 def test_quantize_dual_rejects(lib, rkw, ckw, rows, cols, status):
     assert dual(lib, desc(**rkw), desc(**ckw), rows, cols) == status
@@ -199,13 +205,17 @@ def test_other_entry_points_reject(lib):
     assert amax_call(lib, desc(orient=1, rht=1, rht_n=8)) == 1                # bad size
     assert amax_call(lib, desc(orient=5)) == 1
     assert amax_call(lib, desc(orient=0), rows=1 << 31) == 2                  # too many rows
-    assert lib.fp4_dequantize(0, 0, 0, FAKE, FAKE, FAKE, 32, 40, FAKE, 1, None) == 2
-    assert lib.fp4_dequantize(2, 1, 0, FAKE, FAKE, FAKE, 32, 64, FAKE, 1, None) == 3
-    assert lib.fp4_dequantize(0, 0, 0, FAKE, FAKE, None, 32, 64, FAKE, 1, None) == 1
-    assert lib.fp4_dequantize(0, 0, 5, FAKE, FAKE, FAKE, 32, 64, FAKE, 1, None) == 1
-    assert lib.fp4_dequantize(0, 1, 1, FAKE, FAKE, FAKE, 32, 64, FAKE, 1, None) == 3
-    assert lib.fp4_dequantize(0, 0, 1, FAKE, ctypes.c_void_p(0x10008), FAKE, 32, 64, FAKE, 1,
+    assert amax_call(lib, desc(orient=0, global_scope=1)) == 3                # tensor amax only
+    assert lib.fp4_dequantize(0, 0, 0, FAKE, FAKE, FAKE, 0, 32, 40, FAKE, 1, None) == 2
+    assert lib.fp4_dequantize(2, 1, 0, FAKE, FAKE, FAKE, 0, 32, 64, FAKE, 1, None) == 3
+    assert lib.fp4_dequantize(0, 0, 0, FAKE, FAKE, None, 0, 32, 64, FAKE, 1, None) == 1
+    assert lib.fp4_dequantize(0, 0, 5, FAKE, FAKE, FAKE, 0, 32, 64, FAKE, 1, None) == 1
+    assert lib.fp4_dequantize(0, 1, 1, FAKE, FAKE, FAKE, 0, 32, 64, FAKE, 1, None) == 3
+    assert lib.fp4_dequantize(0, 0, 1, FAKE, ctypes.c_void_p(0x10008), FAKE, 0, 32, 64, FAKE, 1,
                               None) == 1
+    assert lib.fp4_dequantize(0, 0, 0, FAKE, FAKE, FAKE, 2, 32, 64, FAKE, 1, None) == 1
+    assert lib.fp4_dequantize(2, 0, 0, FAKE, FAKE, FAKE, 1, 32, 64, FAKE, 1, None) == 3
+    assert lib.fp4_dequantize(0, 1, 0, FAKE, FAKE, FAKE, 1, 32, 64, FAKE, 1, None) == 3
     assert rht_call(lib, desc(orient=1), rows=40) == 2
     assert rht_call(lib, desc(orient=1), y=None) == 1
     assert rht_call(lib, desc(orient=1), y=ctypes.c_void_p(0x10008)) == 1    # 16-byte aligned
@@ -214,8 +224,8 @@ def test_other_entry_points_reject(lib):
     assert rht_call(lib, None) == 1
 
 
-def op(fmt=0, codes=0x10000, ld=32, rg=1, layout=0, scales=0x20000):
-    return api.Operand(fmt, codes, ld, scales, 4, 1, rg, 0x30000, layout)
+def op(fmt=0, codes=0x10000, ld=32, rg=1, layout=0, scales=0x20000, s_dec=0x30000, scope=0):
+    return api.Operand(fmt, codes, ld, scales, 4, 1, rg, s_dec, layout, scope)
 
 
 @pytest.mark.parametrize("a,b,M,N,K,status", [
@@ -231,6 +241,9 @@ def op(fmt=0, codes=0x10000, ld=32, rg=1, layout=0, scales=0x20000):
     (op(0, layout=3), op(0), 16, 16, 64, 1),
     (op(0, layout=1, rg=16), op(0), 16, 16, 64, 3),          # TILED scales are 1D
     (op(2, layout=1, scales=0x20008), op(2), 16, 16, 64, 1),  # TILED misaligned
+    (op(0, scope=2), op(0), 16, 16, 64, 1),                   # bad s_dec scope
+    (op(2, scope=1), op(2), 16, 16, 64, 3),                   # per-row s_dec with MXFP4
+    (op(0), op(0, scope=1, s_dec=0), 16, 16, 64, 3),          # per-row s_dec is required
 ])
 def test_gemm_rejects(lib, a, b, M, N, K, status):
     assert lib.fp4_gemm(ctypes.byref(a), ctypes.byref(b), M, N, K, FAKE, N, 0, None) == status
@@ -241,7 +254,7 @@ def test_empty_calls_are_noops(lib):
     # nothing to do: accepted without any device work
     a, b = op(0), op(0)
     assert lib.fp4_gemm(ctypes.byref(a), ctypes.byref(b), 0, 16, 64, None, 16, 0, None) == 0
-    assert lib.fp4_dequantize(0, 0, 0, None, None, None, 0, 64, None, 1, None) == 0
+    assert lib.fp4_dequantize(0, 0, 0, None, None, None, 0, 0, 64, None, 1, None) == 0
 
 
 def test_status_strings(lib):
