@@ -312,7 +312,8 @@ def build_step(cfg, dev, dual=True):
                 g("qdy", "r", "qw" if two_level else "qwc", "T", T, din, dout, D_d)))
     ops.append(("gemm wgrad", "mfma", fl(dout, din, T), g("qdyc", "r", "qxc", "r", dout, din, T, D_w)))
     return ops, cnt, dict(X=t["X"], W=t["W"], dY=t["dY"], gpu_outputs=(D_f, D_d, D_w),
-                          **host_stale), fmt
+                          device=dict(X=X, W=W, dY=dY), fprop_out=D_f,
+                          targets=dict(X=target_x, W=target_w, dY=target_dy), **host_stale), fmt
 
 
 def cpu_cores():
@@ -592,6 +593,62 @@ def format_comparison(dev):
     return out
 
 
+def row_scope_parts(fmt, host, graph_ms, flush_buf, R=10):
+    """The per-row global scale (NVFP4 paper App. B.1, closing remark) on the
+    rowwise operands of Fprop and Dgrad, cache-flushed like `parts`: for X,
+    W (RNE) and dY (SR), the tensor-scope route -- an amax pass, then the
+    rowwise quantizer -- against the one-pass rowwise quantizer with one
+    global scale per row; and Fprop on 1D operands with per-row decode
+    scales on both against the same with tensor scales.  (The colwise Wgrad
+    operands keep the tensor scope: a row of X^T spans every token.)"""
+    import torch
+    from fp4_block_scaled_x16_amd import api
+
+    dev_t, tg = host["device"], host["targets"]
+    cnt = api.new_counters(flush_buf.device)
+    buf = torch.empty(1, dtype=torch.float32, device=flush_buf.device)
+
+    def cold_ms(f):
+        def body():
+            for _ in range(R):
+                flush_buf.fill_(1.0)
+                f()
+
+        def flush_only():
+            for _ in range(R):
+                flush_buf.fill_(1.0)
+        return max(graph_ms(body) - graph_ms(flush_only), 0.0) / R
+
+    res = {}
+    for name, rnd in (("X", "rne"), ("W", "rne"), ("dY", "sr")):
+        x = dev_t[name]
+        kw = dict(rnd=rnd, seed=1, target=tg[name], scale_layout="tiled", counters=cnt)
+
+        def two():
+            api.amax(x, out=buf, orient="row")
+            api.quantize(x, fmt, amax_in=buf, **kw)
+
+        def one():
+            api.quantize(x, fmt, global_scope="row", **kw)
+        t2, t1 = cold_ms(two), cold_ms(one)
+        res[name] = {"amax_pass_plus_rowwise_ms": round(t2, 4), "rowwise_per_row_ms": round(t1, 4),
+                     "rowwise_per_row_GBps": round(B_Q1D[fmt] * x.numel() / (t1 * 1e-3) / 1e9, 1)}
+    X, W = dev_t["X"], dev_t["W"]
+    M, K = X.shape
+    N = W.shape[0]
+    out = host["fprop_out"]
+    for scope in ("tensor", "row"):
+        # both operands 1D with TILED scales, so only the global scope differs
+        qx = api.quantize(X, fmt, global_scope=scope, target=tg["X"], scale_layout="tiled")
+        qw = api.quantize(W, fmt, global_scope=scope, target=tg["W"], scale_layout="tiled")
+        t_g = cold_ms(lambda: api.gemm(qx.operand(), qw.operand(), M, N, K, out=out))
+        res["fprop_1d_%s_scales_ms" % scope] = round(t_g, 4)
+        del qx, qw
+    res["note"] = ("rowwise operands of Fprop/Dgrad; Wgrad's colwise operands keep the tensor "
+                   "scope")
+    return res
+
+
 def main():
     args = parse()
     if args.summarize_trace:
@@ -739,7 +796,6 @@ def main():
         t_flush = graph_ms(flushes)
         op_ms.append(max(graph_ms(cold) - t_flush, 0.0) / R)
         op_ms_warm.append(graph_ms(warm) / R)
-    del flush_buf
 
     def rates(times):
         out = {}
@@ -756,6 +812,9 @@ def main():
             out[name] = p
         return out
     parts, parts_warm = rates(op_ms), rates(op_ms_warm)
+    row_scope = None
+    if fmt != "mxfp4":
+        row_scope = row_scope_parts(fmt, host, graph_ms, flush_buf)
     q_bytes = sum(u for (_, k, u, _) in ops if k == "hbm")
     q_ms = sum(parts[n]["ms"] for (n, k, u, _) in ops if k == "hbm" and u > 0)
     g_flops = sum(u for (_, k, u, _) in ops if k == "mfma")
@@ -802,6 +861,9 @@ def main():
         "counters": counters,
         "wall_s_timed": round(wall, 3),
     }
+    if row_scope is not None:
+        out["row_scope"] = row_scope
+    del flush_buf
     if cfg == 5:
         out["format_comparison"] = format_comparison(dev)
     if pool is not None:

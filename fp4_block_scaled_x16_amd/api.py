@@ -87,7 +87,7 @@ def load_library(path=LIB_PATH):
     lib.fp4_dequantize.argtypes = [i32, i32, i32, vp, vp, vp, i32, i64, i64, vp, i32, vp]
     lib.fp4_rht16.argtypes = [ctypes.POINTER(QuantDesc), vp, i64, i64, i64, vp, vp]
     lib.fp4_gemm.argtypes = [ctypes.POINTER(Operand), ctypes.POINTER(Operand), i64, i64, i64, vp,
-                             i64, i32, vp]
+                             i32, i64, i32, vp]
     lib.fp4_selftest_sweep.argtypes = [i32, vp, i32, vp, vp]
     lib.fp4_selftest_gemm_decode.argtypes = [i32, vp, vp]
     for f in ("fp4_amax", "fp4_quantize", "fp4_quantize_dual", "fp4_dequantize", "fp4_rht16",
@@ -334,13 +334,20 @@ def rht16(x, signs, rht_n=16, orient="col"):
 
 
 # ------------------------------------------------------------------ GEMM --
-def gemm(a: Operand, b: Operand, M, N, K, out=None, accumulate=False, device=None):
-    """D[M, N] (+)= s_A s_B sum_k a[m, k] b[n, k] (fp32)."""
+OUT_TYPES = {torch.float32: 0, torch.bfloat16: 1}
+
+
+def gemm(a: Operand, b: Operand, M, N, K, out=None, accumulate=False, device=None,
+         out_dtype=torch.float32):
+    """D[M, N] (+)= s_A s_B sum_k a[m, k] b[n, k], written as fp32 or bf16
+    (the dtype of `out` when given, else out_dtype)."""
     if out is None:
-        out = torch.empty((M, N), dtype=torch.float32, device=device or "cuda")
+        out = torch.empty((M, N), dtype=out_dtype, device=device or "cuda")
+    if out.dtype not in OUT_TYPES or out.dim() != 2 or out.stride(1) != 1:
+        raise ValueError("out must be a row-major 2-D fp32 or bf16 tensor")
     lib = load_library()
-    _check(lib.fp4_gemm(ctypes.byref(a), ctypes.byref(b), M, N, K, _ptr(out), out.stride(0),
-                        int(bool(accumulate)), _stream(out.device)), "fp4_gemm")
+    _check(lib.fp4_gemm(ctypes.byref(a), ctypes.byref(b), M, N, K, _ptr(out), OUT_TYPES[out.dtype],
+                        out.stride(0), int(bool(accumulate)), _stream(out.device)), "fp4_gemm")
     return out
 
 

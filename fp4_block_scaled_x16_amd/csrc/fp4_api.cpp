@@ -408,7 +408,8 @@ FP4_EXPORT fp4_status fp4_rht16(const fp4_quant_desc* d, const uint16_t* x, int6
 }
 
 FP4_EXPORT fp4_status fp4_gemm(const fp4_operand* A, const fp4_operand* B, int64_t M, int64_t N,
-                               int64_t K, float* D, int64_t ldd, int accumulate, void* stream) {
+                               int64_t K, void* D, fp4_out_type d_type, int64_t ldd,
+                               int accumulate, void* stream) {
   if (!A || !B) return fail(FP4_ERR_ARG, "operand descriptor is null");
   if (!valid_format(A->format) || !valid_format(B->format)) return fail(FP4_ERR_ARG, "bad format");
   if (A->format != B->format) return fail(FP4_ERR_UNSUPPORTED, "A and B formats differ");
@@ -416,6 +417,8 @@ FP4_EXPORT fp4_status fp4_gemm(const fp4_operand* A, const fp4_operand* B, int64
   const int bs = block_len(A->format);
   if (K % bs) return fail(FP4_ERR_SHAPE, "K=%lld must be a multiple of %d", (long long)K, bs);
   if (ldd < N) return fail(FP4_ERR_ARG, "ldd=%lld < N=%lld", (long long)ldd, (long long)N);
+  if (d_type != FP4_OUT_F32 && d_type != FP4_OUT_BF16)
+    return fail(FP4_ERR_ARG, "bad d_type %d", (int)d_type);
   const fp4_operand* ops[2] = {A, B};
   for (int i = 0; i < 2; ++i) {
     const fp4_operand* o = ops[i];
@@ -453,7 +456,8 @@ FP4_EXPORT fp4_status fp4_gemm(const fp4_operand* A, const fp4_operand* B, int64
   fp4lib::GemmOperand b{B->codes, B->ld_codes, B->scales, B->scale_stride_row,
                         B->scale_stride_kblk, B->scale_row_group, B->s_dec,
                         B->scale_layout == FP4_SCALES_TILED, B->s_dec_scope == FP4_GLOBAL_ROW};
-  return device_status(fp4lib::launch_gemm(A->format, a, b, M, N, K, D, ldd, accumulate,
+  return device_status(fp4lib::launch_gemm(A->format, a, b, M, N, K, D, d_type == FP4_OUT_BF16,
+                                           ldd, accumulate,
                                            static_cast<hipStream_t>(stream)),
                        "fp4_gemm launch");
 }

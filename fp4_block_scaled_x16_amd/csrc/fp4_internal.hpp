@@ -67,7 +67,8 @@ hipError_t launch_dequant(int format, int block2d, int tiled, const uint8_t* cod
 hipError_t launch_rht(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int rht_n,
                       const uint32_t (&signs)[4], bool along_rows, float* y, hipStream_t s);
 hipError_t launch_gemm(int format, const GemmOperand& A, const GemmOperand& B, int64_t M, int64_t N,
-                       int64_t K, float* D, int64_t ldd, int accumulate, hipStream_t s);
+                       int64_t K, void* D, int d_bf16, int64_t ldd, int accumulate,
+                       hipStream_t s);
 // Exhaustive conversion checks (selftest.hip).
 hipError_t launch_selftest_sweep(int kind, const uint32_t* thresholds, int n, uint64_t* result,
                                  hipStream_t s);

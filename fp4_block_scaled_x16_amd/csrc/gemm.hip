@@ -88,7 +88,7 @@ static int64_t scale_extent(const Params& p, int o, int64_t rows) {
 }
 
 hipError_t launch_gemm(int format, const GemmOperand& A, const GemmOperand& B, int64_t M,
-                       int64_t N, int64_t K, float* D, int64_t ldd, int accumulate,
+                       int64_t N, int64_t K, void* D, int d_bf16, int64_t ldd, int accumulate,
                        hipStream_t s) {
   using namespace fp4gemm;
   Params p{};
@@ -111,7 +111,8 @@ hipError_t launch_gemm(int format, const GemmOperand& A, const GemmOperand& B, i
     p.s_dec[o] = format == FP4_MXFP4 ? nullptr : ops[o]->s_dec;
     p.s_dec_rows[o] = p.s_dec[o] && ops[o]->s_dec_rows ? 1 : 0;
   }
-  p.D = D;
+  p.D = static_cast<float*>(D);
+  p.d_bf16 = d_bf16;
   p.ldd = ldd;
   p.M = M;
   p.N = N;

@@ -33,7 +33,8 @@ struct Params {
   int rg_shift[2];      // log2 of the scale row group (0 or 4)
   const float* s_dec[2];
   int s_dec_rows[2];    // s_dec holds one decode scale per operand row (per-row global scale)
-  float* D;
+  float* D;             // fp32, or bf16 (d_bf16) reinterpreted; ldd in elements
+  int d_bf16;
   int64_t ldd;
   int64_t M, N, K;
   int accumulate;
@@ -88,21 +89,83 @@ __device__ __forceinline__ uint4 load_codes16(const uint8_t* row, int64_t off, i
 // 4, the 4 consecutive columns 8g + 4h .. +3 of a 32 x 32 tile: the
 // epilogue writes 16 bytes per store.
 // MI 32-row MFMA tiles per wave in M (a wave covers MI * 32 rows).
+// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float v) {
+  const uint32_t u = __float_as_uint(v);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// The store loop of `epilogue` for a bf16 D (NVFP4 paper §4.1: the GEMMs
+// may write BF16): each value is formed in fp32 exactly as for an fp32 D
+// (with accumulate: the old bf16 value widened and added in fp32), then
+// rounded once to bf16; 8 bytes per store.
+template <int MI>
+__device__ __forceinline__ void epilogue_bf16(const Params& p, floatx16 (&acc)[MI][4],
+                                              float scale, int64_t m0, int64_t n0, int wm,
+                                              int wn, int lane) {
+  const int i = lane & 31, h = lane >> 5;
+  uint16_t* d16 = reinterpret_cast<uint16_t*>(p.D);
+  const bool vec = (p.ldd & 3) == 0 && (reinterpret_cast<uintptr_t>(d16) & 7) == 0;
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+    const int64_t row = m0 + wm * (MI * 32) + mi * 32 + i;
+    if (row >= p.M) continue;
+    uint16_t* drow = d16 + row * p.ldd;
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t col = n0 + wn * 128 + ni * 32 + 8 * g + 4 * h;
+        float r[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = acc[mi][ni][4 * g + e] * scale;
+        if (vec && col + 3 < p.N) {
+          uint2* dst = reinterpret_cast<uint2*>(drow + col);
+          if (p.accumulate) {
+            const uint2 o = *dst;
+            r[0] += __uint_as_float(o.x << 16);
+            r[1] += __uint_as_float(o.x & 0xFFFF0000u);
+            r[2] += __uint_as_float(o.y << 16);
+            r[3] += __uint_as_float(o.y & 0xFFFF0000u);
+          }
+          *dst = make_uint2(f32_to_bf16_rne(r[0]) | (f32_to_bf16_rne(r[1]) << 16),
+                            f32_to_bf16_rne(r[2]) | (f32_to_bf16_rne(r[3]) << 16));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (col + e < p.N) {
+              uint16_t* d = drow + col + e;
+              const float v = p.accumulate ? r[e] + __uint_as_float(uint32_t(*d) << 16) : r[e];
+              *d = static_cast<uint16_t>(f32_to_bf16_rne(v));
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
 // `scale` is the tensor-level s_dec_B (1 when B has per-row scales).  Per-row
-// decode scales (s_dec_A[m], s_dec_B[n]) are loaded before the first store
-// and multiplied into the accumulators: a wait for a load issued between
-// stores would wait for those stores too.
+// decode scales (s_dec_A[m], s_dec_B[n]) are multiplied into the
+// accumulators before the first store: either read from LDS copies of the
+// tile's scales (lds_a / lds_b, indexed by the row or column within the
+// tile), or loaded from global memory ahead of every store (a wait for a
+// load issued between stores would wait for those stores too).
 template <int MI>
 __device__ __forceinline__ void epilogue(const Params& p, floatx16 (&acc)[MI][4], float scale,
-                                         int64_t m0, int64_t n0, int wm, int wn, int lane) {
+                                         int64_t m0, int64_t n0, int wm, int wn, int lane,
+                                         const float* lds_a = nullptr,
+                                         const float* lds_b = nullptr) {
   const int i = lane & 31, h = lane >> 5;
   const bool vec = (p.ldd & 3) == 0 && (reinterpret_cast<uintptr_t>(p.D) & 15) == 0;
   if (p.s_dec_rows[0]) {
     float sa[MI];
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
-      const int64_t row = m0 + wm * (MI * 32) + mi * 32 + i;
-      sa[mi] = row < p.M ? p.s_dec[0][row] : 1.0f;
+      const int lr = wm * (MI * 32) + mi * 32 + i;
+      const int64_t row = m0 + lr;
+      sa[mi] = lds_a ? lds_a[lr] : row < p.M ? p.s_dec[0][row] : 1.0f;
     }
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
@@ -116,8 +179,15 @@ __device__ __forceinline__ void epilogue(const Params& p, floatx16 (&acc)[MI][4]
     for (int ni = 0; ni < 4; ++ni) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int64_t col = n0 + wn * 128 + ni * 32 + 8 * g + 4 * h;
-        if (vec_b && col + 3 < p.N) {
+        const int lc = wn * 128 + ni * 32 + 8 * g + 4 * h;
+        const int64_t col = n0 + lc;
+        if (lds_b) {
+          const float4 t = *reinterpret_cast<const float4*>(lds_b + lc);
+          cb[ni][4 * g] = t.x;
+          cb[ni][4 * g + 1] = t.y;
+          cb[ni][4 * g + 2] = t.z;
+          cb[ni][4 * g + 3] = t.w;
+        } else if (vec_b && col + 3 < p.N) {
           const float4 t = *reinterpret_cast<const float4*>(p.s_dec[1] + col);
           cb[ni][4 * g] = t.x;
           cb[ni][4 * g + 1] = t.y;
@@ -136,6 +206,10 @@ __device__ __forceinline__ void epilogue(const Params& p, floatx16 (&acc)[MI][4]
       for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
         for (int k = 0; k < 16; ++k) acc[mi][ni][k] *= cb[ni][k];
+  }
+  if (p.d_bf16) {
+    epilogue_bf16(p, acc, scale, m0, n0, wm, wn, lane);
+    return;
   }
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {

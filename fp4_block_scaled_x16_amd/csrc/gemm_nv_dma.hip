@@ -69,6 +69,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level_dma(Params p) {
   constexpr int BM = 64 * MI;
   __shared__ uint4 cst0[2][1024], cst1[2][1024];   // [operand][row * 4 + (chunk ^ swizzle)]
   __shared__ uint2 sst0[2][2][256], sst1[2][2][256];  // [operand][half][row] fp16 scale pairs
+  // per-row decode scales of the tile's A rows and B rows (per-row global
+  // scales only): loaded with the first K step's scales, read by the epilogue
+  __shared__ __attribute__((aligned(16))) float srow[2][256];
   int tm, tn;
   tile_coords(p, tm, tn);
   const int64_t m0 = static_cast<int64_t>(tm) * BM, n0 = static_cast<int64_t>(tn) * kBN;
@@ -240,11 +243,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level_dma(Params p) {
     }
   };
 
+  float srow_v[2] = {1.0f, 1.0f};
+#pragma unroll
+  for (int o = 0; o < 2; ++o)
+    if (p.s_dec_rows[o]) srow_v[o] = p.s_dec[o][min(base[o] + t, lim[o] - 1)];
   load_scales(0);
   dma_codes_nv<MI>(cst0, src, 0, wave);
   wait_vmcnt<0>();
   decode_scales();
   store_scales(sst0);
+#pragma unroll
+  for (int o = 0; o < 2; ++o)
+    if (p.s_dec_rows[o]) srow[o][t] = srow_v[o];
   load_scales(nsteps > 1 ? 1 : 0);       // step 1's scales, stored at the end of step 0
   wait_vmcnt<0>();
   decode_scales();
@@ -264,7 +274,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level_dma(Params p) {
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) acc[mi][ni] *= scale;
-  epilogue(p, acc, sb, m0, n0, wm, wn, lane);
+  epilogue(p, acc, sb, m0, n0, wm, wn, lane, srow[0], srow[1]);
 }
 
 }  // namespace

@@ -37,6 +37,17 @@ between (the periodic tensor scaling of the UE5M3 recipe).  The SR random
 stream of step s uses Philox counter offsets 2s (rowwise dY) and 2s + 1
 (colwise dY), so no two steps or orientations share random bits.
 
+Outputs: Y and dX are fp32 or bf16 (out_dtype; §4.1: the GEMMs write BF16
+or FP32, rounded once from the fp32 result in the GEMM's epilogue); the
+weight gradient accumulates in fp32 (main_grad).
+
+Calling the layer (`layer(x)`) runs it under autograd: a torch.autograd.
+Function whose forward is Fprop and whose backward is Dgrad (the gradient
+of x) and Wgrad (added to main_grad; the weight gets no .grad).  Its
+gradient dY is quantized from bf16, so the autograd path takes bf16 x and
+writes bf16 Y and dX (out_dtype "bf16").  `forward` / `backward` are the
+same steps called explicitly, one backward per forward.
+
 Every computation runs in the library's kernels; this module only
 allocates outputs and passes pointers (through `api`).
 """
@@ -66,6 +77,7 @@ class Recipe:
     rht_kd: bool = False          # RHT along K on the Fprop / Dgrad operands too
     rht_kd_n: int = 16            # its size N: 4 or 16
     rht_kd_signs: int = 0         # its N-bit sign mask
+    out_dtype: str = "fp32"       # Y and dX: "fp32" or "bf16"
 
     @property
     def two_level(self):
@@ -87,6 +99,8 @@ class QuantizedLinear:
             raise ValueError("2D activation blocks need NVFP4 or UE5M3 and no RHT")
         if recipe.rht_kd and (not recipe.two_level or recipe.rht_kd_n not in (4, 16)):
             raise ValueError("the RHT along K needs NVFP4 or UE5M3 and N = 4 or 16")
+        if recipe.out_dtype not in _OUT_DTYPES:
+            raise ValueError("out_dtype must be 'fp32' or 'bf16'")
         self.weight = weight
         self.recipe = recipe
         self.out_features, self.in_features = weight.shape
@@ -130,7 +144,27 @@ class QuantizedLinear:
         if self.recipe.two_level and given is None:
             self.amax[name], self.amax[name + "_t"] = q.amax, q_t.amax
 
+    def __call__(self, x: torch.Tensor) -> torch.Tensor:
+        """Y = X W^T under autograd (bf16 x, bf16 Y; see the module docstring)."""
+        if self.recipe.out_dtype != "bf16":
+            raise ValueError("the autograd path needs Recipe(out_dtype='bf16'): its gradient "
+                             "dY is quantized from bf16")
+        return _Fp4LinearFunction.apply(x, self.weight, self)
+
     def forward(self, x: torch.Tensor) -> torch.Tensor:
+        """Fprop of one step; the operands Dgrad / Wgrad need are kept for
+        the next `backward`."""
+        y, self._saved = self._forward(x)
+        return y
+
+    def backward(self, dy: torch.Tensor) -> torch.Tensor:
+        """Dgrad (returned) and Wgrad (added to main_grad) of the last forward."""
+        if self._saved is None:
+            raise RuntimeError("backward() needs a preceding forward()")
+        saved, self._saved = self._saved, None
+        return self._backward(dy, saved)
+
+    def _forward(self, x):
         r = self.recipe
         if x.dim() != 2 or x.shape[1] != self.in_features:
             raise ValueError("x must be [tokens, in_features]")
@@ -169,15 +203,13 @@ class QuantizedLinear:
                                          scale_layout=r.scale_layout)
             w_op, wt_op = qw.operand(), qw_t.operand()
         tokens = x.shape[0]
-        y = api.gemm(x_op, w_op, tokens, self.out_features, self.in_features, device=x.device)
-        self._saved = (xt_op, wt_op, tokens)
-        return y
+        y = api.gemm(x_op, w_op, tokens, self.out_features, self.in_features, device=x.device,
+                     out_dtype=_OUT_DTYPES[r.out_dtype])
+        return y, (xt_op, wt_op, tokens)
 
-    def backward(self, dy: torch.Tensor) -> torch.Tensor:
+    def _backward(self, dy, saved):
         r = self.recipe
-        if self._saved is None:
-            raise RuntimeError("backward() needs a preceding forward()")
-        xt_op, wt_op, tokens = self._saved
+        xt_op, wt_op, tokens = saved
         if dy.dim() != 2 or tuple(dy.shape) != (tokens, self.out_features):
             raise ValueError("dy must be [tokens, out_features]")
         am, am_t = self._amax_args(dy, "dy", r.rht or r.rht_kd)
@@ -195,9 +227,31 @@ class QuantizedLinear:
                                            scale_round=r.scale_round, **self._kd())
             self._keep_amax("dy", qdy, qdy_t, am)
             dy_op, dyt_op = qdy.operand(), qdy_t.operand()
-        dx = api.gemm(dy_op, wt_op, tokens, self.in_features, self.out_features, device=dy.device)
+        dx = api.gemm(dy_op, wt_op, tokens, self.in_features, self.out_features, device=dy.device,
+                      out_dtype=_OUT_DTYPES[r.out_dtype])
         api.gemm(dyt_op, xt_op, self.out_features, self.in_features, tokens,
                  out=self.main_grad, accumulate=True)
-        self._saved = None
         self.step += 1
         return dx
+
+
+_OUT_DTYPES = {"fp32": torch.float32, "bf16": torch.bfloat16}
+
+
+class _Fp4LinearFunction(torch.autograd.Function):
+    """Autograd wrapper of one QuantizedLinear step: forward = Fprop (the
+    quantized operands for the backward GEMMs are kept on the context),
+    backward = Dgrad (the gradient of x) and Wgrad (added to the layer's
+    main_grad; no gradient is returned for the weight or the layer)."""
+
+    @staticmethod
+    def forward(ctx, x, weight, layer):
+        y, ctx.saved = layer._forward(x)
+        ctx.layer = layer
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        saved, ctx.saved = ctx.saved, None
+        dx = ctx.layer._backward(dy.contiguous(), saved)
+        return dx, None, None

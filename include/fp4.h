@@ -299,6 +299,10 @@ typedef struct {
                                  s_dec[rows], one per operand row (non-NULL) */
 } fp4_operand;
 
+/* Element type of a GEMM output (NVFP4 paper §4.1: the GEMMs take FP4
+ * inputs and write BF16 or FP32). */
+typedef enum { FP4_OUT_F32 = 0, FP4_OUT_BF16 = 1 } fp4_out_type;
+
 /*
  * fp4_gemm -- D[M, N] (+)= s_dec_A * s_dec_B * sum_k a[m, k] * b[n, k]
  * (s_dec_A[m] and s_dec_B[n] for operands with per-row global scales),
@@ -308,14 +312,18 @@ typedef struct {
  * global decode scales applied to the output) used for Fprop, Dgrad and
  * Wgrad (§4.1, Fig. 5).  A and B must have the same format; K must be a
  * multiple of the format's block length.
- *   D  device fp32, row-major with leading dimension ldd >= N.
+ *   D  device, row-major with leading dimension ldd >= N (in elements of
+ *      d_type): fp32 (FP4_OUT_F32), or bf16 bits (FP4_OUT_BF16: every value
+ *      is formed in fp32 as for an fp32 D -- with accumulate, the old bf16
+ *      value widened and added in fp32 -- then rounded once to nearest even).
  *   accumulate  0: D = result; 1: D += result (e.g. Wgrad accumulation).
- * Accuracy: |D - exact| <= 1e-5 * s_dec_A * s_dec_B * sum_k |a b| per element.
+ * Accuracy (fp32 D): |D - exact| <= 1e-5 * s_dec_A * s_dec_B * sum_k |a b|
+ * per element; a bf16 D is that fp32 value rounded to bf16.
  * K == 0 writes zeros (or leaves D unchanged when accumulating).
  */
 fp4_status fp4_gemm(const fp4_operand* A /* host */, const fp4_operand* B /* host */,
-                    int64_t M, int64_t N, int64_t K, float* D, int64_t ldd,
-                    int accumulate, void* stream);
+                    int64_t M, int64_t N, int64_t K, void* D, fp4_out_type d_type,
+                    int64_t ldd, int accumulate, void* stream);
 
 /* Static description of a status code. */
 const char* fp4_status_string(fp4_status status);

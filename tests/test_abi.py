@@ -246,15 +246,22 @@ def op(fmt=0, codes=0x10000, ld=32, rg=1, layout=0, scales=0x20000, s_dec=0x3000
     (op(0), op(0, scope=1, s_dec=0), 16, 16, 64, 3),          # per-row s_dec is required
 ])
 def test_gemm_rejects(lib, a, b, M, N, K, status):
-    assert lib.fp4_gemm(ctypes.byref(a), ctypes.byref(b), M, N, K, FAKE, N, 0, None) == status
+    assert lib.fp4_gemm(ctypes.byref(a), ctypes.byref(b), M, N, K, FAKE, 0, N, 0, None) == status
     assert _err(lib)
 
 
 def test_empty_calls_are_noops(lib):
     # nothing to do: accepted without any device work
     a, b = op(0), op(0)
-    assert lib.fp4_gemm(ctypes.byref(a), ctypes.byref(b), 0, 16, 64, None, 16, 0, None) == 0
+    assert lib.fp4_gemm(ctypes.byref(a), ctypes.byref(b), 0, 16, 64, None, 0, 16, 0, None) == 0
+    assert lib.fp4_gemm(ctypes.byref(a), ctypes.byref(b), 0, 16, 64, None, 1, 16, 0, None) == 0
     assert lib.fp4_dequantize(0, 0, 0, None, None, None, 0, 0, 64, None, 1, None) == 0
+
+
+def test_gemm_rejects_output_type(lib):
+    a, b = op(0), op(0)
+    assert lib.fp4_gemm(ctypes.byref(a), ctypes.byref(b), 16, 16, 64, FAKE, 2, 16, 0, None) == 1
+    assert "d_type" in _err(lib)
 
 
 def test_status_strings(lib):

@@ -16,6 +16,7 @@ from fp4_block_scaled_x16_amd import api, inputs
 from oracle import formats as F
 from oracle import gemm as G
 from oracle import quantize as Q
+from bf16_check import bf16_close
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -381,3 +382,38 @@ def test_workload_gemm(cfg, gemm, scales):
     bound = G.gemm_abs_bound(av, bv, sa, sb)
     got = d[torch.from_numpy(rows).to(DEV)][:, torch.from_numpy(cols).to(DEV)].cpu().numpy()
     check(got, ref, bound)
+
+
+@pytest.mark.parametrize("fmt,la,lb,M,N,K", [
+    ("nvfp4", "row", "row", 300, 264, 512),       # DMA kernel
+    ("nvfp4", "row", "row", 130, 70, 48),         # register-staged kernel, ragged N
+    ("nvfp4", "row", "2dT", 130, 80, 48),
+    ("ue5m3", "row", "2d", 520, 272, 512),
+    ("mxfp4", "row", "row", 280, 300, 512),       # scaled-MFMA kernel
+    ("mxfp4", "row", "row", 33, 17, 32),
+])
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_gemm_bf16_output(fmt, la, lb, M, N, K, accumulate):
+    """NVFP4 paper §4.1: the GEMMs may write BF16.  Each value is the fp32
+    result rounded once to bf16 (accumulation adds the old bf16 value in
+    fp32 first); ragged N exercises the element-wise stores."""
+    a_bits = inputs.activations((M, K), cfg_seed=71)
+    b_bits = (inputs.weights((K, N), cfg_seed=72) if lb == "2dT" else
+              inputs.weights((N, K), cfg_seed=72) if lb == "2d" else
+              inputs.gradients((N, K), cfg_seed=72))
+    qa, qb = gpu_quant(a_bits, fmt, la), gpu_quant(b_bits, fmt, lb)
+    av, sa = oracle_operand(a_bits, fmt, la)
+    bv, sb = oracle_operand(b_bits, fmt, lb)
+    if fmt == "mxfp4":
+        sa = sb = 1.0
+    ref = G.gemm_ref(av, bv, sa, sb).astype(np.float64)
+    bound = G.gemm_abs_bound(av, bv, sa, sb)
+    init = torch.randn((M, N), dtype=torch.float32, device=DEV).to(torch.bfloat16)
+    out = init.clone() if accumulate else torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    api.gemm(gpu_operand(qa, la), gpu_operand(qb, lb), M, N, K, out=out, accumulate=accumulate)
+    torch.cuda.synchronize()
+    if accumulate:
+        d0 = F.bf16_bits_to_f32(init.view(torch.int16).cpu().numpy().view(np.uint16))
+        ref = ref + d0.astype(np.float64)
+        bound = bound + np.abs(d0)
+    bf16_close(out.view(torch.int16).cpu().numpy().view(np.uint16), ref, bound)

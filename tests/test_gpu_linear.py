@@ -22,6 +22,7 @@ from oracle import formats as F
 from oracle import gemm as G
 from oracle import quantize as Q
 from oracle.rht import rht_cols
+from bf16_check import bf16_close
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -185,3 +186,44 @@ def test_backward_needs_forward():
     layer = QuantizedLinear(dev(inputs.weights((32, 32), cfg_seed=1)))
     with pytest.raises(RuntimeError):
         layer.backward(torch.zeros((16, 32), dtype=torch.bfloat16, device=DEV))
+
+
+@pytest.mark.parametrize("name,steps", [("nvfp4_rht", 2), ("ue5m3_periodic", 3)])
+def test_linear_autograd_bf16(name, steps):
+    """The layer under autograd with bf16 outputs (NVFP4 paper §4.1: FP4
+    inputs, BF16 outputs): y = layer(x); y.backward(dy) gives x.grad = dX and
+    accumulates dW into main_grad.  Y and dX are the oracle's fp32 values
+    rounded once to bf16 (within the GEMM bound plus half a bf16 ulp)."""
+    import dataclasses
+    r0, _ = RECIPES[name]
+    r = dataclasses.replace(r0, out_dtype="bf16")
+    tokens, d_in, d_out = 272, 128, 208
+    w = inputs.weights((d_out, d_in), cfg_seed=80)
+    layer = QuantizedLinear(dev(w), r)
+    dw_ref = np.zeros((d_out, d_in))
+    dw_bound = np.zeros((d_out, d_in))
+    amax = None
+    for s in range(steps):
+        x = inputs.activations((tokens, d_in), cfg_seed=91 + s)
+        dy = inputs.gradients((tokens, d_out), cfg_seed=91 + s)
+        if amax is None or s % r.amax_interval == 0:
+            amax = tensor_amaxes(x, w, dy, r)
+        xt = dev(x).view(torch.bfloat16).requires_grad_()
+        y = layer(xt)
+        assert y.dtype == torch.bfloat16 and y.requires_grad
+        y.backward(dev(dy).view(torch.bfloat16))
+        torch.cuda.synchronize()
+        ref, _ = oracle_step(x, w, dy, r, s, amax)
+        bf16_close(y.detach().view(torch.int16).cpu().numpy().view(np.uint16), *ref["y"])
+        assert xt.grad.dtype == torch.bfloat16
+        bf16_close(xt.grad.view(torch.int16).cpu().numpy().view(np.uint16), *ref["dx"])
+        dw_ref += ref["dw"][0]
+        dw_bound += ref["dw"][1]
+        check(layer.main_grad, (dw_ref, dw_bound))
+    assert layer.weight.grad is None and layer.step == steps
+
+
+def test_autograd_needs_bf16_output():
+    layer = QuantizedLinear(dev(inputs.weights((32, 32), cfg_seed=1)))
+    with pytest.raises(ValueError):
+        layer(torch.zeros((16, 32), dtype=torch.bfloat16, device=DEV))
