@@ -86,16 +86,33 @@ def parse():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn the counter CSVs of two --counters-run passes (FETCH_SIZE, "
                          "WRITE_SIZE) into the GEMM traffic summary")
+    ap.add_argument("--summarize-sq", nargs=2, metavar=("PASS_A_CSV", "PASS_B_CSV"),
+                    help="per-kernel SQ counter summary of two --counters-run passes (the "
+                         "counters of SQ_PASS_A and SQ_PASS_B); needs --ops-json")
+    ap.add_argument("--ops-json", metavar="PATH",
+                    help="--counters-run: write the step's ops in launch order here; "
+                         "--summarize-sq: read them")
     return ap.parse_args()
 
 
 CAL_BYTES = 512 << 20       # calibration kernel: reads and writes this many bytes
 
 
-def counters_run(ops):
+def counters_run(ops, host, ops_json=None):
     """One eager pass of the step's ops, then y = 2 x on CAL_BYTES of fp32
-    (a plain streaming kernel of known traffic) to calibrate the counters."""
+    (a plain streaming kernel of known traffic) to calibrate the counters.
+    ops_json: also write the ops in launch order (name, kind, algorithmic
+    units, elements of the tensor a quantization reads) for --summarize-sq."""
     import torch
+    if ops_json:
+        numel = {k: int(v.numel()) for k, v in host["device"].items()}
+        rows = []
+        for (name, kind, units, _) in ops:
+            tensor = next((t for t in ("dY", "X", "W") if (" " + t + " ") in (name + " ")), None)
+            rows.append({"name": name, "kind": kind, "units": units,
+                         "elements": numel.get(tensor) if not name.startswith("gemm") else None})
+        with open(ops_json, "w") as f:
+            json.dump(rows, f)
     for (_, _, _, f) in ops:
         f()
     x = torch.ones(CAL_BYTES // 4, dtype=torch.float32, device="cuda")
@@ -148,6 +165,63 @@ def summarize_pmc(fetch_csv, write_csv, cfg):
             gemm_tot.append(fb + wb)
         lines.append("%s %s fetch_bytes=%.0f write_bytes=%.0f" % (tag, n, fb, wb))
     lines.append("hbm_bytes_per_launch=%.0f" % float(np.mean(gemm_tot)))
+    print("\n".join(lines))
+
+
+# SQ counters of the two passes --summarize-sq reads (8 SQ counters each)
+SQ_PASS_A = ("SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
+             "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_WAIT_INST_ANY")
+SQ_PASS_B = ("SQ_ACTIVE_INST_LDS", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_ANY",
+             "SQ_WAIT_ANY", "SQ_INSTS_SALU", "SQ_ACTIVE_INST_VMEM", "SQ_INSTS_VMEM_RD")
+SQ_INSTANCES = 32      # SQ_BUSY_CYCLES sums the 32 shader engines (8 XCDs x 4)
+SIMDS = 1024           # 256 CUs x 4 SIMDs
+
+
+def summarize_sq(csv_a, csv_b, ops_json):
+    """Per-kernel SQ counter summary of one eager pass of the step (the
+    dispatches of --counters-run, matched to the ops in launch order).
+
+    clock_GHz      SQ_BUSY_CYCLES / 32 engines / kernel duration
+    valu_busy      SQ_INSTS_VALU x 4 cycles (a wave64 VALU op on a 16-lane
+                   SIMD) / (1024 SIMDs x busy cycles per engine)
+    mfma_busy      SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x busy cycles per engine)
+    valu_ops/elem  64 x SQ_INSTS_VALU / elements of the quantized tensor
+    wait_frac      SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (wave-cycles waiting on s_waitcnt)
+    lds_conflict   SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS
+    (durations are those of the profiled pass: counters slow kernels down)."""
+    import csv
+
+    def load(path):
+        d = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                key = int(r["Dispatch_Id"])
+                e = d.setdefault(key, {"name": r["Kernel_Name"],
+                                       "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+                e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        return [d[k] for k in sorted(d)]
+
+    def short(n):
+        n = n.replace("void ", "").replace("fp4gemm::", "").replace("(anonymous namespace)::", "")
+        return n.split("(")[0]
+    lib = lambda rows: [r for r in rows if any(k in r["name"] for k in ("k_quant", "k_gemm", "k_amax"))]
+    a, b = lib(load(csv_a)), lib(load(csv_b))
+    with open(ops_json) as f:
+        ops = json.load(f)
+    a, b = a[-len(ops):], b[-len(ops):]
+    lines = ["%-22s %-40s %8s %6s %6s %6s %9s %6s %6s" % (
+        "op", "kernel", "us", "GHz", "valu", "mfma", "valu/elem", "wait", "ldsbc")]
+    for op, ra, rb in zip(ops, a, b):
+        cyc = ra["SQ_BUSY_CYCLES"] / SQ_INSTANCES
+        valu = ra["SQ_INSTS_VALU"] * 4.0 / (SIMDS * cyc)
+        mfma = ra["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMDS * cyc)
+        per_elem = ("%9.1f" % (64.0 * ra["SQ_INSTS_VALU"] / op["elements"])
+                    if op["elements"] else "%9s" % "-")
+        wait = ra["SQ_WAIT_INST_ANY"] / max(ra["SQ_WAVE_CYCLES"], 1.0)
+        bc = rb["SQ_LDS_BANK_CONFLICT"] / max(rb["SQ_ACTIVE_INST_LDS"], 1.0)
+        lines.append("%-22s %-40s %8.1f %6.2f %6.3f %6.3f %s %6.3f %6.3f" % (
+            op["name"][:22], short(ra["name"])[:40], ra["ns"] / 1e3, cyc / ra["ns"], valu, mfma,
+            per_elem, wait, bc))
     print("\n".join(lines))
 
 
@@ -657,6 +731,9 @@ def main():
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.config)
         return
+    if args.summarize_sq:
+        summarize_sq(args.summarize_sq[0], args.summarize_sq[1], args.ops_json)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU (--gpus 1); runs on several GPUs are not "
               "part of this benchmark.", file=sys.stderr)
@@ -681,7 +758,7 @@ def main():
     cfg = args.config
     ops, cnt, host, fmt = build_step(cfg, dev, dual=not args.separate_quant)
     if args.counters_run:
-        counters_run(ops)
+        counters_run(ops, host, args.ops_json)
         return
 
     def run_step():
