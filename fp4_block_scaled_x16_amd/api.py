@@ -69,11 +69,14 @@ EXPORTS = ("fp4_amax", "fp4_quantize", "fp4_dequantize", "fp4_rht16", "fp4_gemm"
            "fp4_status_string", "fp4_last_error")
 
 
-def load_library(path=LIB_PATH):
-    """Load (once) and return the ctypes library; raises if it is not built."""
+def load_library(path=None):
+    """Load (once) and return the ctypes library; raises if it is not built.
+    The path defaults to $FP4_LIB if set (e.g. the sanitized host build of
+    the argument checks), else the in-tree library."""
     global _lib
     if _lib is not None:
         return _lib
+    path = path or os.environ.get("FP4_LIB") or LIB_PATH
     if not os.path.exists(path):
         raise Fp4Error(-1, "%s is missing: build it with __graft_entry__.build() "
                            "(python fp4_block_scaled_x16_amd/build.py)" % path)
@@ -90,8 +93,10 @@ def load_library(path=LIB_PATH):
                              i32, i64, i32, vp]
     lib.fp4_selftest_sweep.argtypes = [i32, vp, i32, vp, vp]
     lib.fp4_selftest_gemm_decode.argtypes = [i32, vp, vp]
+    lib.fp4_selftest_set_geometry.argtypes = [i32, i32]
     for f in ("fp4_amax", "fp4_quantize", "fp4_quantize_dual", "fp4_dequantize", "fp4_rht16",
-              "fp4_gemm", "fp4_selftest_sweep", "fp4_selftest_gemm_decode"):
+              "fp4_gemm", "fp4_selftest_sweep", "fp4_selftest_gemm_decode",
+              "fp4_selftest_set_geometry"):
         getattr(lib, f).restype = ctypes.c_int
     lib.fp4_status_string.argtypes = [ctypes.c_int]
     lib.fp4_status_string.restype = ctypes.c_char_p
@@ -379,3 +384,9 @@ def selftest_gemm_decode(fmt, device="cuda"):
     _check(lib.fp4_selftest_gemm_decode(_fmt(fmt), _ptr(out), _stream(out.device)),
            "fp4_selftest_gemm_decode")
     return out.cpu().numpy().view("uint16")
+
+
+def selftest_set_geometry(max_workgroups=0, gemm_tile_rows=0):
+    """Launch-geometry controls for race guards (0, 0: the defaults)."""
+    _check(load_library().fp4_selftest_set_geometry(int(max_workgroups), int(gemm_tile_rows)),
+           "fp4_selftest_set_geometry")

@@ -21,10 +21,12 @@ BUILD = os.path.join(ROOT, "_build")
 LIB_NAME = "libfp4_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-# (source, object name, extra flags): gemm_nv_dma.hip is built once per
-# block-scale format and tile height so the four kernel families compile in
-# parallel
-SOURCES = [("quant.hip", "quant", []), ("quant_rowscope.hip", "quant_rowscope", []), ("gemm.hip", "gemm", []), ("gemm_nv.hip", "gemm_nv", [])] + [
+# (source, object name, extra flags): gemm_nv.hip is built once per
+# block-scale format and gemm_nv_dma.hip once per format and tile height, so
+# the kernel families compile in parallel
+SOURCES = [("quant.hip", "quant", []), ("quant_rowscope.hip", "quant_rowscope", []),
+           ("gemm.hip", "gemm", [])] + [
+    ("gemm_nv.hip", "gemm_nv_%d" % f, ["-DFP4_NV_FMT=%d" % f]) for f in (0, 1)] + [
     ("gemm_nv_dma.hip", "gemm_nv_dma_%d_%d" % (f, mi), ["-DFP4_DMA_FMT=%d" % f, "-DFP4_DMA_MI=%d" % mi])
     for f in (0, 1) for mi in (4, 3)] + [
     ("gemm_mx.hip", "gemm_mx", []), ("gemm_mx_dma.hip", "gemm_mx_dma", []),
@@ -75,6 +77,40 @@ def build(verbose=False, incremental=False):
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
+
+
+CLANG = "/opt/rocm/llvm/bin/clang++"
+SANITIZED_LIB = os.path.join(BUILD, "sanitize", "libfp4_mi355x_sanitized.so")
+
+
+def build_sanitized():
+    """The C ABI's host code (fp4_api.cpp: every argument check) built as
+    plain host C++ with AddressSanitizer and UndefinedBehaviorSanitizer
+    (every UB report fatal), linked against host-only stand-ins for the
+    kernel launchers (csrc/sanitize_stubs.cpp).  Loaded in place of the real
+    library (FP4_LIB) by tests that never reach a device.  Returns the
+    library path."""
+    out_dir = os.path.dirname(SANITIZED_LIB)
+    os.makedirs(out_dir, exist_ok=True)
+    flags = ["-std=c++17", "-fPIC", "-O1", "-g", "-fno-omit-frame-pointer",
+             "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+             "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", "-I" + os.path.join(ROOT, "include")]
+    objs = []
+    for src in ("fp4_api.cpp", "sanitize_stubs.cpp"):
+        obj = os.path.join(out_dir, src.replace(".cpp", ".o"))
+        _run([CLANG] + flags + ["-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    _run([CLANG, "-shared", "-shared-libasan", "-fsanitize=address,undefined", "-o",
+          SANITIZED_LIB] + objs + ["-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"])
+    return SANITIZED_LIB
+
+
+def sanitizer_runtime():
+    """Path of clang's shared ASan runtime (to LD_PRELOAD into a process that
+    loads the sanitized library)."""
+    out = subprocess.run([CLANG, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                         capture_output=True, text=True, check=True).stdout.strip()
+    return out
 
 
 if __name__ == "__main__":

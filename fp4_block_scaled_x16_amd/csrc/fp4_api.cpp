@@ -462,6 +462,14 @@ FP4_EXPORT fp4_status fp4_gemm(const fp4_operand* A, const fp4_operand* B, int64
                        "fp4_gemm launch");
 }
 
+FP4_EXPORT fp4_status fp4_selftest_set_geometry(int max_workgroups, int gemm_tile_rows) {
+  if (max_workgroups < 0) return fail(FP4_ERR_ARG, "max_workgroups must be >= 0");
+  if (gemm_tile_rows != 0 && gemm_tile_rows != 192 && gemm_tile_rows != 256)
+    return fail(FP4_ERR_ARG, "gemm_tile_rows must be 0, 192 or 256");
+  fp4lib::set_launch_geometry(max_workgroups, gemm_tile_rows);
+  return ok();
+}
+
 FP4_EXPORT fp4_status fp4_selftest_sweep(int kind, const uint32_t* thresholds, int n,
                                          uint64_t* result, void* stream) {
   static const int kLen[3] = {7, 126, 255};

@@ -43,6 +43,12 @@ struct GemmOperand {
 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
+// Workgroups of a persistent grid of per_cu workgroups per CU, capped by the
+// launch-geometry control (fp4_selftest_set_geometry) when one is set.
+int64_t grid_cap(int per_cu);
+// Forced tile height of the two-level DMA GEMM (192 or 256), 0 if none.
+int gemm_tile_rows_forced();
+void set_launch_geometry(int max_workgroups, int gemm_tile_rows);
 
 // amax_plain (optional, rht with N = 16 along the columns only): also max |x|
 // from the same read.  along_rows: the rotation runs along the rows of x

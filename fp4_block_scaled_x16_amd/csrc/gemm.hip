@@ -145,13 +145,15 @@ hipError_t launch_gemm(int format, const GemmOperand& A, const GemmOperand& B, i
       const int64_t tiles = (M + bm - 1) / bm * p.tiles_n;
       return (tiles + cus - 1) / cus * bm;
     };
-    const int short_tile = cost(192) * 20 < cost(256) * 19 ? 1 : 0;
+    const int forced = gemm_tile_rows_forced();
+    const int short_tile = forced ? (forced == 192 ? 1 : 0) : (cost(192) * 20 < cost(256) * 19 ? 1 : 0);
     if (short_tile) p.tiles_m = static_cast<int>((M + 191) / 192);
     if (format == FP4_NVFP4)
       return short_tile ? launch_two_level_dma_0_3(scv, p, s) : launch_two_level_dma_0_4(scv, p, s);
     return short_tile ? launch_two_level_dma_1_3(scv, p, s) : launch_two_level_dma_1_4(scv, p, s);
   }
-  return launch_two_level(format, fast, scv, p, grid, s);
+  return format == FP4_NVFP4 ? launch_two_level_0(fast, scv, p, grid, s)
+                             : launch_two_level_1(fast, scv, p, grid, s);
 }
 
 }  // namespace fp4lib

@@ -390,8 +390,8 @@ hipError_t launch_with_lds(void (*kernel)(Params), size_t lds, int grid, hipStre
                            const Params& p);
 
 // Family launchers (one translation unit each).  `grid` = tiles_m * tiles_n.
-hipError_t launch_two_level(int format, bool fast, int scv, const Params& p, int grid,
-                            hipStream_t s);
+hipError_t launch_two_level_0(bool fast, int scv, const Params& p, int grid, hipStream_t s);
+hipError_t launch_two_level_1(bool fast, int scv, const Params& p, int grid, hipStream_t s);
 // gemm_nv_dma.hip, one object per format (0 NVFP4, 1 UE5M3) and tile height
 // (4: 256 rows, 3: 192 rows)
 hipError_t launch_two_level_dma_0_4(int scv, const Params& p, hipStream_t s);

@@ -1,5 +1,6 @@
 // NVFP4 / UE5M3 block-scaled GEMM with register-staged codes: the shapes the
-// DMA kernel does not take (ragged M, N and K tails masked).
+// DMA kernel does not take (ragged M, N and K tails masked).  Compiled once
+// per block-scale format (FP4_NV_FMT) so the two build in parallel.
 
 #include "gemm_common.hpp"
 
@@ -208,18 +209,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level(Params p) {
 
 }  // namespace
 
-hipError_t launch_two_level(int format, bool fast, int scv, const Params& p, int grid,
-                            hipStream_t s) {
-  void (*kern)(Params);
-  if (format == FP4_NVFP4) {
-    constexpr void (*nv[4])(Params) = {k_gemm_two_level<kNV, true, 0>, k_gemm_two_level<kNV, true, 1>,
-                                       k_gemm_two_level<kNV, true, 2>, k_gemm_two_level<kNV, true, 3>};
-    kern = fast ? nv[scv] : k_gemm_two_level<kNV, false, 0>;
-  } else {
-    constexpr void (*ue[4])(Params) = {k_gemm_two_level<kUE, true, 0>, k_gemm_two_level<kUE, true, 1>,
-                                       k_gemm_two_level<kUE, true, 2>, k_gemm_two_level<kUE, true, 3>};
-    kern = fast ? ue[scv] : k_gemm_two_level<kUE, false, 0>;
-  }
+#if !defined(FP4_NV_FMT)
+#error "compile with -DFP4_NV_FMT=0|1"
+#endif
+
+// This object's launcher, launch_two_level_<FMT> (0 NVFP4, 1 UE5M3): the
+// tile-aligned kernel for scale-loader variant `scv` when `fast`, else the
+// masked one.
+#define FP4_NV_NAME2(f) launch_two_level_##f
+#define FP4_NV_NAME(f) FP4_NV_NAME2(f)
+hipError_t FP4_NV_NAME(FP4_NV_FMT)(bool fast, int scv, const Params& p, int grid, hipStream_t s) {
+  constexpr int F = FP4_NV_FMT == 0 ? kNV : kUE;
+  constexpr void (*k[4])(Params) = {k_gemm_two_level<F, true, 0>, k_gemm_two_level<F, true, 1>,
+                                    k_gemm_two_level<F, true, 2>, k_gemm_two_level<F, true, 3>};
+  void (*kern)(Params) = fast ? k[scv] : k_gemm_two_level<F, false, 0>;
   return launch_with_lds(kern, 2 * sizeof(Stage2), grid, s, p);
 }
 

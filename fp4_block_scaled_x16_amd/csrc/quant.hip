@@ -12,6 +12,7 @@
 // tensor-scale prologue and the counter flush are paid once per workgroup.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <stdint.h>
 
@@ -753,6 +754,23 @@ int device_cu_count() {
   return cache[dev];
 }
 
+// Launch-geometry controls (fp4_selftest_set_geometry): results must not
+// depend on them; tests vary them to expose races between waves and tiles.
+static std::atomic<int> g_max_workgroups{0}, g_gemm_tile_rows{0};
+
+void set_launch_geometry(int max_workgroups, int gemm_tile_rows) {
+  g_max_workgroups.store(max_workgroups);
+  g_gemm_tile_rows.store(gemm_tile_rows);
+}
+
+int64_t grid_cap(int per_cu) {
+  const int64_t cap = static_cast<int64_t>(device_cu_count()) * per_cu;
+  const int m = g_max_workgroups.load();
+  return m > 0 && m < cap ? m : cap;
+}
+
+int gemm_tile_rows_forced() { return g_gemm_tile_rows.load(); }
+
 
 hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int rht,
                        int rht_n, const uint32_t (&signs)[4], float* amax, hipStream_t s,
@@ -775,7 +793,7 @@ hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld
     } else if (rht) {
       // the other sizes: the colwise quantizer's staging and rotation, amax only
       const int64_t tiles = ((rows + 127) / 128) * ((cols + 63) / 64);
-      const int64_t cap = static_cast<int64_t>(device_cu_count()) * kTileWgPerCu;
+      const int64_t cap = grid_cap(kTileWgPerCu);
       const int grid = static_cast<int>(tiles < cap ? tiles : cap);
       hipLaunchKernelGGL((k_quant_col<kNV, FP4_RNE, true, false, true>), dim3(grid),
                          dim3(kThreads), 0, s, x, rows, cols, ld, nullptr, nullptr, nullptr, 0.0f,
@@ -831,8 +849,7 @@ template <int FMT, int RND, bool RHT, bool CNT>
 static void col_launch(const QuantArgs& a, hipStream_t s) {
   constexpr int BS = FMT == kMX ? 32 : 16;
   const int64_t tiles = ((a.rows + 8 * BS - 1) / (8 * BS)) * ((a.cols + 63) / 64);
-  const int64_t cap = static_cast<int64_t>(device_cu_count()) *
-                      (RND == FP4_SR ? kColWgPerCuSR : kTileWgPerCu);
+  const int64_t cap = grid_cap(RND == FP4_SR ? kColWgPerCuSR : kTileWgPerCu);
   const int grid = static_cast<int>(tiles < cap ? (tiles > 0 ? tiles : 1) : cap);
   hipLaunchKernelGGL((k_quant_col<FMT, RND, RHT, CNT>), dim3(grid), dim3(kThreads), 0, s, a.x,
                      a.rows, a.cols, a.ld, a.codes, a.scales, a.amax, a.target, a.s_dec, a.seed,
@@ -873,8 +890,7 @@ template <int FMT, int RND, bool RHT, bool CNT, bool RRHT>
 static void dual_launch(const QuantArgs& a, const QuantArgs& b, hipStream_t s) {
   constexpr int BS = FMT == kMX ? 32 : 16;
   const int64_t tiles = ((a.rows + 8 * BS - 1) / (8 * BS)) * ((a.cols + 63) / 64);
-  const int64_t cap = static_cast<int64_t>(device_cu_count()) *
-                      (RND == FP4_SR ? kColWgPerCuSR : kTileWgPerCu);
+  const int64_t cap = grid_cap(RND == FP4_SR ? kColWgPerCuSR : kTileWgPerCu);
   const int grid = static_cast<int>(tiles < cap ? (tiles > 0 ? tiles : 1) : cap);
   hipLaunchKernelGGL((k_quant_dual<FMT, RND, RHT, CNT, RRHT>), dim3(grid), dim3(kThreads), 0, s,
                      a.x, a.rows, a.cols, a.ld, a.codes, a.scales, b.codes, b.scales, a.amax,
@@ -923,7 +939,7 @@ hipError_t launch_quant_dual(const QuantArgs& row, const QuantArgs& col, hipStre
 template <int FMT, int RND, bool CNT>
 static void q2d_launch(const QuantArgs& a, hipStream_t s) {
   const int64_t regions = ((a.rows + 63) / 64) * ((a.cols + 63) / 64);
-  const int64_t cap = static_cast<int64_t>(device_cu_count()) * kTileWgPerCu;
+  const int64_t cap = grid_cap(kTileWgPerCu);
   const int grid = static_cast<int>(regions < cap ? (regions > 0 ? regions : 1) : cap);
   hipLaunchKernelGGL((k_quant_2d<FMT, RND, CNT>), dim3(grid), dim3(kThreads), 0, s, a.x, a.rows,
                      a.cols, a.ld, a.codes, a.scales, a.emit_transpose ? a.codes_t : nullptr,

@@ -122,7 +122,7 @@ __device__ __forceinline__ uint32_t scale_for_block(float amax_b, float s_enc_g,
 // per_cu per CU.
 inline int grid_for(uint64_t work_items, int per_cu, int threads = 512) {
   const uint64_t want = (work_items + threads - 1) / threads;
-  const uint64_t cap = static_cast<uint64_t>(fp4lib::device_cu_count()) * per_cu;
+  const uint64_t cap = static_cast<uint64_t>(fp4lib::grid_cap(per_cu));
   const uint64_t g = want < cap ? want : cap;
   return static_cast<int>(g ? g : 1);
 }

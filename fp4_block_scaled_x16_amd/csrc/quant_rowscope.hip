@@ -248,7 +248,7 @@ void scoped_launch(const fp4lib::QuantArgs& a, const RhtN& r, hipStream_t s) {
   }
   const int64_t rows_per_wg = WAVE ? kRowThreads / 64 : 1;
   const int64_t want = (a.rows + rows_per_wg - 1) / rows_per_wg;
-  const int64_t cap = static_cast<int64_t>(fp4lib::device_cu_count()) * per_cu;
+  const int64_t cap = fp4lib::grid_cap(per_cu);
   const int grid = static_cast<int>(want < cap ? want : cap);
   hipLaunchKernelGGL(kernel, dim3(grid), dim3(kRowThreads), 0, s, a.x, a.rows, a.cols, a.ld,
                      a.codes, a.scales, const_cast<float*>(a.amax), a.amax_given, a.target,

@@ -39,6 +39,17 @@
 extern "C" {
 #endif
 
+/* Every enumeration of this interface is an int: in C++ its underlying type
+ * is fixed to int, so any int a caller passes is a value of the type and the
+ * argument checks can reject it (without a fixed type, C++ leaves loading a
+ * value outside the enumerators' range undefined); in C, an enum is an
+ * int-sized integer type already.  The layout is the same in both. */
+#ifdef __cplusplus
+#define FP4_ENUM_INT : int
+#else
+#define FP4_ENUM_INT
+#endif
+
 /* Element payload is always E2M1 (NVFP4 paper §3: values +-{0,.5,1,1.5,2,3,4,6}).
  * The block-scale format and block length differ:
  *   FP4_NVFP4  1x16 blocks, E4M3 scale (max 448), fp32 tensor scale  (§3, App. B)
@@ -46,20 +57,20 @@ extern "C" {
  *              max 122880), fp32 tensor scale with target T          (UE5M3 abstract)
  *   FP4_MXFP4  1x32 blocks, UE8M0 power-of-two scale rounded up, no tensor
  *              scale                                                  (§3, App. B.4) */
-typedef enum { FP4_NVFP4 = 0, FP4_UE5M3 = 1, FP4_MXFP4 = 2 } fp4_format;
+typedef enum fp4_format_e FP4_ENUM_INT { FP4_NVFP4 = 0, FP4_UE5M3 = 1, FP4_MXFP4 = 2 } fp4_format;
 
 /* Element rounding: nearest-even, or stochastic (NVFP4 paper §4.4). */
-typedef enum { FP4_RNE = 0, FP4_SR = 1 } fp4_round;
+typedef enum fp4_round_e FP4_ENUM_INT { FP4_RNE = 0, FP4_SR = 1 } fp4_round;
 
 /* Block-scale rounding for NVFP4 / UE5M3: to nearest (NVFP4 paper App. B.2),
  * or up -- the 2D-block FP4 page's truncation-free scaling: the block amax
  * times the encode scale then does not exceed 6, so no element is clipped
  * (up to fp32 rounding of the scale arithmetic).  MXFP4 scales are always
  * rounded up (App. B.4). */
-typedef enum { FP4_SCALE_RNE = 0, FP4_SCALE_UP = 1 } fp4_scale_round;
+typedef enum fp4_scale_round_e FP4_ENUM_INT { FP4_SCALE_RNE = 0, FP4_SCALE_UP = 1 } fp4_scale_round;
 
 /* 1D blocks along the blocked axis, or 16x16 tiles (NVFP4 paper §4.3). */
-typedef enum { FP4_BLOCK_1D = 0, FP4_BLOCK_2D16 = 1 } fp4_block;
+typedef enum fp4_block_e FP4_ENUM_INT { FP4_BLOCK_1D = 0, FP4_BLOCK_2D16 = 1 } fp4_block;
 
 /* Where the block scales of a 1D code matrix [R, C] (KB = C / BS blocks per
  * row) are stored.
@@ -73,12 +84,12 @@ typedef enum { FP4_BLOCK_1D = 0, FP4_BLOCK_2D16 = 1 } fp4_block;
  * TILED is a storage layout chosen for the GEMM: one 256-row output tile
  * reads the scales of 8 K-blocks as one contiguous 2 KiB run instead of 256
  * scattered pieces.  The scale values are the same in both layouts. */
-typedef enum { FP4_SCALES_ROWMAJOR = 0, FP4_SCALES_TILED = 1 } fp4_scale_layout;
+typedef enum fp4_scale_layout_e FP4_ENUM_INT { FP4_SCALES_ROWMAJOR = 0, FP4_SCALES_TILED = 1 } fp4_scale_layout;
 
 /* ROWWISE: blocks run along cols of X; output is [rows, cols] codes.
  * COLWISE: the matrix quantized is X^T; blocks run along rows of X and the
  * output is the [cols, rows] code matrix of X^T (Wgrad operands, §4.1). */
-typedef enum { FP4_ROWWISE = 0, FP4_COLWISE = 1 } fp4_orient;
+typedef enum fp4_orient_e FP4_ENUM_INT { FP4_ROWWISE = 0, FP4_COLWISE = 1 } fp4_orient;
 
 /* Span of the global (tensor-level) scale s_enc_G = 6 T / amax, s_dec_G =
  * 1 / s_enc_G (NVFP4 paper App. B.1).  TENSOR: one amax over the whole
@@ -90,9 +101,9 @@ typedef enum { FP4_ROWWISE = 0, FP4_COLWISE = 1 } fp4_orient;
  * GEMM applies s_dec_A[m] s_dec_B[n] to D[m, n].  (A COLWISE row is a
  * column of x spanning every token, which a one-read tile pass cannot see
  * whole before it encodes: COLWISE and 2D16 stay TENSOR.) */
-typedef enum { FP4_GLOBAL_TENSOR = 0, FP4_GLOBAL_ROW = 1 } fp4_global_scope;
+typedef enum fp4_global_scope_e FP4_ENUM_INT { FP4_GLOBAL_TENSOR = 0, FP4_GLOBAL_ROW = 1 } fp4_global_scope;
 
-typedef enum {
+typedef enum fp4_status_e FP4_ENUM_INT {
   FP4_OK = 0,
   FP4_ERR_ARG = 1,          /* null pointer, bad enum, misaligned or bad stride  */
   FP4_ERR_SHAPE = 2,        /* negative size, blocked axis not a block multiple  */
@@ -301,7 +312,7 @@ typedef struct {
 
 /* Element type of a GEMM output (NVFP4 paper §4.1: the GEMMs take FP4
  * inputs and write BF16 or FP32). */
-typedef enum { FP4_OUT_F32 = 0, FP4_OUT_BF16 = 1 } fp4_out_type;
+typedef enum fp4_out_type_e FP4_ENUM_INT { FP4_OUT_F32 = 0, FP4_OUT_BF16 = 1 } fp4_out_type;
 
 /*
  * fp4_gemm -- D[M, N] (+)= s_dec_A * s_dec_B * sum_k a[m, k] * b[n, k]

@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-typedef enum {
+typedef enum fp4_sweep_kind_e FP4_ENUM_INT {
   FP4_SWEEP_E2M1_RNE = 0,     /* every fp32 pattern except NaNs (2^32 - 2^24 + 2)   */
   FP4_SWEEP_E4M3_SCALE = 1,   /* every finite fp32 t >= 0 (patterns 0 .. 0x7F7FFFFF) */
   FP4_SWEEP_UE5M3_SCALE = 2   /* likewise                                            */
@@ -65,6 +65,21 @@ fp4_status fp4_selftest_sweep(int kind, const uint32_t* thresholds, int n,
  *           codes are written as 0.
  */
 fp4_status fp4_selftest_gemm_decode(fp4_format format, uint16_t* out, void* stream);
+
+/*
+ * fp4_selftest_set_geometry -- launch-geometry controls for race guards: no
+ * result of the library may depend on them, so a test runs the same work
+ * under different settings and requires bit-identical outputs.
+ *   max_workgroups  > 0: every persistent grid (amax, quantizers, dequantize,
+ *                   RHT) launches at most this many workgroups, each walking
+ *                   more of the work; 0: the default grids.
+ *   gemm_tile_rows  192 or 256: the NVFP4 / UE5M3 DMA GEMM uses this tile
+ *                   height; 0: chosen per shape.
+ * Process-wide, applied at the next launch; not synchronized with launches
+ * in flight on other host threads.  Rejects negative max_workgroups and
+ * other tile heights (FP4_ERR_ARG).
+ */
+fp4_status fp4_selftest_set_geometry(int max_workgroups, int gemm_tile_rows);
 
 #ifdef __cplusplus
 }

@@ -37,7 +37,8 @@ def test_header_declares_the_boundary():
 
 
 def test_exports_every_declared_symbol(lib):
-    out = subprocess.run(["nm", "-D", "--defined-only", api.LIB_PATH], capture_output=True,
+    path = os.environ.get("FP4_LIB") or api.LIB_PATH      # the library `lib` loaded
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True,
                          text=True, check=True).stdout
     exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
     for name in declared():
@@ -262,6 +263,13 @@ def test_gemm_rejects_output_type(lib):
     a, b = op(0), op(0)
     assert lib.fp4_gemm(ctypes.byref(a), ctypes.byref(b), 16, 16, 64, FAKE, 2, 16, 0, None) == 1
     assert "d_type" in _err(lib)
+
+
+def test_geometry_control_rejects(lib):
+    assert lib.fp4_selftest_set_geometry(-1, 0) == 1
+    assert lib.fp4_selftest_set_geometry(0, 128) == 1
+    assert lib.fp4_selftest_set_geometry(5, 192) == 0      # accepted: no device work
+    assert lib.fp4_selftest_set_geometry(0, 0) == 0
 
 
 def test_status_strings(lib):
