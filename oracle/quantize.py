@@ -16,6 +16,12 @@ page, so each is restated from its surrounding prose:
   B.3 (Eq. 4)  element code = Q(x * s_enc_L), Q = E2M1 conversion.
   B.4          MXFP4: power-of-two UE8M0 scale rounded up so the block amax
                never saturates; no tensor scale.
+  MXFP8        (2D-block FP4 page: the Q/K projections stay in MXFP8) E4M3
+               elements in 1x32 blocks with a UE8M0 scale, read as the OCP
+               MX format with B.4's round-up rule (B.4 names saturation as the
+               MXFP8 convergence problem it avoids): 2^e with e the smallest
+               integer such that 448 * 2^e >= amax_B; element code = sign bit
+               7 | E4M3 RNE code of |x * 2^-e|; one byte per element.
   B.1 (end)    the "global" scale may cover a smaller span than the tensor,
                a row for instance, so that no separate pass over memory is
                needed for the amax: scope="row" gives every row of the
@@ -63,8 +69,9 @@ from .rht import rht_cols
 
 FLT_MAX = np.float32(np.finfo(np.float32).max)
 
-FORMATS = ("nvfp4", "ue5m3", "mxfp4")
-BLOCK = {"nvfp4": 16, "ue5m3": 16, "mxfp4": 32}
+FORMATS = ("nvfp4", "ue5m3", "mxfp4", "mxfp8")
+BLOCK = {"nvfp4": 16, "ue5m3": 16, "mxfp4": 32, "mxfp8": 32}
+ELEM_MAX = {"mxfp4": 6.0, "mxfp8": 448.0}        # largest element magnitude of an MX format
 COUNTERS = ("scale_saturated", "scale_underflow", "scale_subnormal",
             "elem_saturated", "elem_underflow")
 
@@ -141,23 +148,24 @@ def block_scales_two_level(amax_b, s_enc_g, s_dec_g, fmt, scale_round="rne"):
 
 
 # ------------------------------------------------------------ B.4 -------
-def block_scales_mx(amax_b):
-    """UE8M0 codes and encode scales for MXFP4 blocks (App. B.4, §3).
+def block_scales_mx(amax_b, elem_max=6.0):
+    """UE8M0 codes and encode scales for MX blocks (App. B.4, §3).
 
-    The decode scale is the smallest power of two 2^e with 6 * 2^e >= amax_B
-    (rounded up so the block amax never saturates), e clamped to
-    [-127, 127]; an all-zero block takes e = -127.  Encode scale = 2^-e.
+    The decode scale is the smallest power of two 2^e with elem_max * 2^e >=
+    amax_B (rounded up so the block amax never saturates; elem_max = 6 for
+    MXFP4's E2M1, 448 for MXFP8's E4M3), e clamped to [-127, 127]; an
+    all-zero block takes e = -127.  Encode scale = 2^-e.
     """
     a = np.asarray(amax_b, dtype=np.float32).astype(np.float64)
     e = np.full(a.shape, -127, dtype=np.int64)
     nz = a > 0
     # exact search: start from a float estimate, then fix with exact tests
     est = np.zeros(a.shape, dtype=np.int64)
-    est[nz] = np.ceil(np.log2(a[nz] / 6.0)).astype(np.int64)
+    est[nz] = np.ceil(np.log2(a[nz] / elem_max)).astype(np.int64)
     for _ in range(3):
-        too_small = nz & (6.0 * np.ldexp(1.0, est) < a)
+        too_small = nz & (elem_max * np.ldexp(1.0, est) < a)
         est = np.where(too_small, est + 1, est)
-        can_lower = nz & (6.0 * np.ldexp(1.0, est - 1) >= a)
+        can_lower = nz & (elem_max * np.ldexp(1.0, est - 1) >= a)
         est = np.where(can_lower, est - 1, est)
     e[nz] = est[nz]
     e = np.clip(e, -127, 127)
@@ -200,6 +208,19 @@ def encode_elements(v, s_enc_l, rnd="rne", r16=None):
         raise ValueError(rnd)
     under = (v != 0) & ((code & 7) == 0)
     return code.astype(np.uint8), sat, under
+
+
+def encode_elements_e4m3(v, s_enc_l):
+    """MXFP8 element codes of v * s_enc_L: y = fp32(v * s), code = sign bit 7 |
+    E4M3 RNE code of |y| (saturating at 448, which the rounded-up block scale
+    never reaches).  Returns (codes uint8, elem_saturated, elem_underflow)."""
+    v = np.asarray(v, dtype=np.float32)
+    with np.errstate(over="ignore", invalid="ignore"):
+        y = (v * np.asarray(s_enc_l, dtype=np.float32)).astype(np.float32)
+    mag, sat = F.e4m3_rne_sat(np.abs(y))
+    code = mag.astype(np.uint8) | (np.signbit(y).astype(np.uint8) << 7)
+    under = (v != 0) & (mag == 0)
+    return code, sat, under
 
 
 def pack_codes(codes):
@@ -250,13 +271,16 @@ def quantize(x_bits, fmt="nvfp4", block="1d", orient="row", rnd="rne",
     """
     assert fmt in FORMATS and block in ("1d", "2d") and orient in ("row", "col")
     assert rnd in ("rne", "sr") and scope in ("tensor", "row")
-    assert scope == "tensor" or (fmt != "mxfp4" and block == "1d")
+    mx = fmt in ("mxfp4", "mxfp8")
+    assert scope == "tensor" or (not mx and block == "1d")
+    if fmt == "mxfp8":
+        assert block == "1d" and rnd == "rne" and not rht
     x = F.bf16_bits_to_f32(np.asarray(x_bits, dtype=np.uint16))
     assert x.ndim == 2
     R, C = x.shape
     bs = BLOCK[fmt]
     if block == "2d":
-        assert fmt != "mxfp4" and orient == "row" and not rht
+        assert not mx and orient == "row" and not rht
         assert R % 16 == 0 and C % 16 == 0
         bs = 16
     if rht:
@@ -270,8 +294,8 @@ def quantize(x_bits, fmt="nvfp4", block="1d", orient="row", rnd="rne",
     Ro, Co = v.shape
     assert Co % bs == 0, "block axis must be a multiple of the block size"
 
-    if fmt == "mxfp4":
-        assert amax is None, "MXFP4 has no tensor scale"
+    if mx:
+        assert amax is None, "MX formats have no tensor scale"
         amax_x, s_enc_g, s_dec_g = None, np.float32(1.0), np.float32(1.0)
     elif scope == "row":
         amax_x = (row_amax(v) if amax is None
@@ -293,8 +317,8 @@ def quantize(x_bits, fmt="nvfp4", block="1d", orient="row", rnd="rne",
         amax_b = (np.abs(vt).max(axis=(1, 3)) if Ro * Co
                   else np.zeros((Ro // 16, Co // 16), np.float32))
 
-    if fmt == "mxfp4":
-        scode, s_enc_l, sev = block_scales_mx(amax_b)
+    if mx:
+        scode, s_enc_l, sev = block_scales_mx(amax_b, ELEM_MAX[fmt])
     else:
         scode, s_enc_l, sev = block_scales_two_level(amax_b, s_enc_g, s_dec_g, fmt, scale_round)
 
@@ -309,7 +333,10 @@ def quantize(x_bits, fmt="nvfp4", block="1d", orient="row", rnd="rne",
         idx = (int(index_base) + np.arange(Ro, dtype=np.int64)[:, None] * Co
                + np.arange(Co, dtype=np.int64)[None, :])
         r16 = sr_random16(idx, seed, offset)
-    codes, esat, eund = encode_elements(v, s_el, rnd, r16)
+    if fmt == "mxfp8":
+        codes, esat, eund = encode_elements_e4m3(v, s_el)
+    else:
+        codes, esat, eund = encode_elements(v, s_el, rnd, r16)
 
     counters = {
         "scale_saturated": int(np.count_nonzero(sev["scale_saturated"])),
@@ -319,7 +346,7 @@ def quantize(x_bits, fmt="nvfp4", block="1d", orient="row", rnd="rne",
         "elem_underflow": int(np.count_nonzero(eund)),
     }
     out = {
-        "codes": pack_codes(codes),
+        "codes": codes if fmt == "mxfp8" else pack_codes(codes),   # MXFP8: a byte each
         "scales": scode.astype(np.uint8),
         "amax": (None if amax_x is None else
                  amax_x if scope == "row" else np.float32(amax_x)),
@@ -342,6 +369,16 @@ def scale_values(scodes, fmt):
     return F.ue8m0_value(scodes)
 
 
+def element_values(codes, fmt, R, C):
+    """Element values (float64, exact) of an [R, C] code matrix: packed E2M1
+    ([R, C/2] bytes) or MXFP8's E4M3 bytes ([R, C], sign in bit 7)."""
+    if fmt == "mxfp8":
+        c = np.asarray(codes, dtype=np.uint8).reshape(R, C).astype(np.int64)
+        mag = F.e4m3_value(c & 0x7F)
+        return np.where(c & 0x80, -mag, mag)
+    return F.e2m1_value(unpack_codes(np.asarray(codes, dtype=np.uint8).reshape(R, C // 2)))
+
+
 def element_scales(scodes, fmt, block, R, C):
     """Per-element block-scale values (float64) for an [R, C] code matrix."""
     sv = scale_values(scodes, fmt)
@@ -355,16 +392,16 @@ def dequantize(codes_packed, scodes, fmt, block, s_dec, R, C, out="f32"):
     """v = fp32(fp32(e2m1 * scale) * s_dec_G); bf16 output rounds v (RNE).
 
     The decode follows App. B.2-B.3 of the NVFP4 paper (the decode scales
-    undo the encode scales).  e2m1 * scale is exact in fp32.  MXFP4 has no
-    tensor scale (s_dec is taken as 1).  s_dec may be an array of R per-row
-    decode scales (scope="row").
+    undo the encode scales).  element * scale is exact in fp32 (E2M1, or
+    MXFP8's E4M3 times a power of two).  MX formats have no tensor scale
+    (s_dec is taken as 1).  s_dec may be an array of R per-row decode scales
+    (scope="row").
     """
-    codes = unpack_codes(np.asarray(codes_packed, dtype=np.uint8).reshape(R, C // 2))
-    e = F.e2m1_value(codes)
+    e = element_values(codes_packed, fmt, R, C)
     s = element_scales(scodes, fmt, block, R, C)
     with np.errstate(over="ignore"):
         prod = (e * s).astype(np.float32)
-        if fmt == "mxfp4":
+        if fmt in ("mxfp4", "mxfp8"):
             sd = np.float32(1.0)
         elif np.ndim(s_dec) == 0:
             sd = np.float32(s_dec)
@@ -379,5 +416,4 @@ def dequantize(codes_packed, scodes, fmt, block, s_dec, R, C, out="f32"):
 def operand_values(codes_packed, scodes, fmt, block, R, K):
     """Exact element values e2m1 * scale (float64) of a GEMM operand [R, K],
     without the tensor scale (it is applied after the GEMM, App. B.3)."""
-    codes = unpack_codes(np.asarray(codes_packed, dtype=np.uint8).reshape(R, K // 2))
-    return F.e2m1_value(codes) * element_scales(scodes, fmt, block, R, K)
+    return element_values(codes_packed, fmt, R, K) * element_scales(scodes, fmt, block, R, K)
