@@ -16,9 +16,9 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfp4_mi355x.so")
 
-NVFP4, UE5M3, MXFP4 = 0, 1, 2
-FORMATS = {"nvfp4": NVFP4, "ue5m3": UE5M3, "mxfp4": MXFP4}
-BLOCK_LEN = {NVFP4: 16, UE5M3: 16, MXFP4: 32}
+NVFP4, UE5M3, MXFP4, MXFP8 = 0, 1, 2, 3
+FORMATS = {"nvfp4": NVFP4, "ue5m3": UE5M3, "mxfp4": MXFP4, "mxfp8": MXFP8}
+BLOCK_LEN = {NVFP4: 16, UE5M3: 16, MXFP4: 32, MXFP8: 32}
 RNE, SR = 0, 1
 BLOCK_1D, BLOCK_2D16 = 0, 1
 ROWWISE, COLWISE = 0, 1
@@ -163,7 +163,7 @@ class Quantized:
     block: int
     rows: int               # rows of the code matrix
     cols: int               # cols of the code matrix (the blocked axis for 1D)
-    codes: torch.Tensor     # uint8 [rows, cols/2]
+    codes: torch.Tensor     # uint8 [rows, cols/2] (MXFP8: [rows, cols], a byte per element)
     scales: torch.Tensor    # uint8 1D: [rows, cols/BS] (TILED: flat, tiled_scale_bytes);
                             # 2D: [rows/16, cols/16]
     s_dec: torch.Tensor     # fp32 [1], or [rows] with per-row global scales
@@ -180,6 +180,8 @@ class Quantized:
         its tensors) alive for as long as the operand itself is referenced.
         """
         bs = BLOCK_LEN[self.fmt]
+        if self.fmt == MXFP8:
+            raise ValueError("no GEMM takes MXFP8 operands")
         if self.block == BLOCK_1D:
             assert not transposed
             op = Operand(self.fmt, self.codes.data_ptr(), self.cols // 2, self.scales.data_ptr(),
@@ -224,7 +226,8 @@ def quantize(x, fmt="nvfp4", block="1d", orient="row", rnd="rne", seed=0, offset
     rows, cols = (C, R) if col else (R, C)
     bs = 16 if blk == BLOCK_2D16 else BLOCK_LEN[f]
     dev = x.device
-    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+    code_cols = cols if f == MXFP8 else cols // 2
+    codes = torch.empty((rows, code_cols), dtype=torch.uint8, device=dev)
     layout = SCALE_LAYOUTS[scale_layout] if isinstance(scale_layout, str) else int(scale_layout)
     if blk == BLOCK_2D16:
         scales = torch.empty((rows // 16, cols // 16), dtype=torch.uint8, device=dev)

@@ -25,6 +25,7 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 # block-scale format and gemm_nv_dma.hip once per format and tile height, so
 # the kernel families compile in parallel
 SOURCES = [("quant.hip", "quant", []), ("quant_rowscope.hip", "quant_rowscope", []),
+           ("quant_mxfp8.hip", "quant_mxfp8", []),
            ("gemm.hip", "gemm", [])] + [
     ("gemm_nv.hip", "gemm_nv_%d" % f, ["-DFP4_NV_FMT=%d" % f]) for f in (0, 1)] + [
     ("gemm_nv_dma.hip", "gemm_nv_dma_%d_%d" % (f, mi), ["-DFP4_DMA_FMT=%d" % f, "-DFP4_DMA_MI=%d" % mi])

@@ -40,9 +40,14 @@ fp4_status device_status(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int block_len(fp4_format f) { return f == FP4_MXFP4 ? 32 : 16; }
+// MX formats: 1x32 blocks of power-of-two scales and no tensor scale.
+bool is_mx(fp4_format f) { return f == FP4_MXFP4 || f == FP4_MXFP8; }
 
-bool valid_format(int f) { return f == FP4_NVFP4 || f == FP4_UE5M3 || f == FP4_MXFP4; }
+int block_len(fp4_format f) { return is_mx(f) ? 32 : 16; }
+
+bool valid_format(int f) {
+  return f == FP4_NVFP4 || f == FP4_UE5M3 || f == FP4_MXFP4 || f == FP4_MXFP8;
+}
 
 int rht_size(const fp4_quant_desc* d) { return d->rht_n ? d->rht_n : 16; }
 
@@ -134,18 +139,20 @@ FP4_EXPORT fp4_status fp4_quantize(const fp4_quant_desc* d, const uint16_t* x, i
   if (d->round != FP4_RNE && d->round != FP4_SR) return fail(FP4_ERR_ARG, "bad round %d", (int)d->round);
   fp4_status st = check_bf16_input(x, rows, cols, ld);
   if (st) return st;
-  const bool two_level = d->format != FP4_MXFP4;
+  const bool two_level = !is_mx(d->format);
+  const bool mx8 = d->format == FP4_MXFP8;
   const bool is2d = d->block == FP4_BLOCK_2D16;
   const int bs = block_len(d->format);
-  if (is2d && d->format == FP4_MXFP4) return fail(FP4_ERR_UNSUPPORTED, "2D16 blocks need NVFP4 or UE5M3");
+  if (is2d && !two_level) return fail(FP4_ERR_UNSUPPORTED, "2D16 blocks need NVFP4 or UE5M3");
+  if (mx8 && d->round != FP4_RNE) return fail(FP4_ERR_UNSUPPORTED, "MXFP8 rounds to nearest even");
   if (is2d && d->orient != FP4_ROWWISE) return fail(FP4_ERR_UNSUPPORTED, "2D16 blocks are ROWWISE only");
   if (d->scale_round != FP4_SCALE_RNE && d->scale_round != FP4_SCALE_UP)
     return fail(FP4_ERR_ARG, "bad scale_round %d", (int)d->scale_round);
   if (d->rht && is2d) return fail(FP4_ERR_UNSUPPORTED, "RHT needs 1D blocks");
-  if (d->rht && d->format == FP4_MXFP4) return fail(FP4_ERR_UNSUPPORTED, "RHT needs NVFP4 or UE5M3");
+  if (d->rht && !two_level) return fail(FP4_ERR_UNSUPPORTED, "RHT needs NVFP4 or UE5M3");
   st = check_rht(d, "desc");
   if (st) return st;
-  if (d->amax_given && !two_level) return fail(FP4_ERR_UNSUPPORTED, "MXFP4 has no tensor amax");
+  if (d->amax_given && !two_level) return fail(FP4_ERR_UNSUPPORTED, "MX formats have no tensor amax");
   if (d->global_scope != FP4_GLOBAL_TENSOR && d->global_scope != FP4_GLOBAL_ROW)
     return fail(FP4_ERR_ARG, "bad global_scope %d", (int)d->global_scope);
   const bool row_scope = d->global_scope == FP4_GLOBAL_ROW;
@@ -215,7 +222,8 @@ FP4_EXPORT fp4_status fp4_quantize(const fp4_quant_desc* d, const uint16_t* x, i
   a.tiled = tiled ? 1 : 0;
   a.amax_given = d->amax_given ? 1 : 0;
   hipError_t e;
-  if (row_scope) e = fp4lib::launch_quant_row_scoped(a, s);
+  if (mx8) e = fp4lib::launch_quant_mx8(a, d->orient == FP4_COLWISE, s);
+  else if (row_scope) e = fp4lib::launch_quant_row_scoped(a, s);
   else if (is2d) e = fp4lib::launch_quant_2d(a, s);
   else if (d->orient == FP4_ROWWISE) e = fp4lib::launch_quant_row(a, s);
   else e = fp4lib::launch_quant_col(a, s);
@@ -234,6 +242,8 @@ FP4_EXPORT fp4_status fp4_quantize_dual(const fp4_quant_desc* rd, const fp4_quan
     const fp4_quant_desc* d = ds[i];
     const char* side = i ? "colwise" : "rowwise";
     if (!valid_format(d->format)) return fail(FP4_ERR_ARG, "%s: bad format %d", side, (int)d->format);
+    if (d->format == FP4_MXFP8)
+      return fail(FP4_ERR_UNSUPPORTED, "%s: dual quantization takes the FP4 formats", side);
     if (d->block != FP4_BLOCK_1D && d->block != FP4_BLOCK_2D16)
       return fail(FP4_ERR_ARG, "%s: bad block %d", side, (int)d->block);
     if (d->orient != FP4_ROWWISE && d->orient != FP4_COLWISE)
@@ -358,12 +368,12 @@ FP4_EXPORT fp4_status fp4_dequantize(fp4_format format, fp4_block block,
     return fail(FP4_ERR_ARG, "bad scale_layout %d", (int)scale_layout);
   const bool tiled = scale_layout == FP4_SCALES_TILED;
   if (tiled && block == FP4_BLOCK_2D16) return fail(FP4_ERR_UNSUPPORTED, "TILED scales are for 1D blocks");
-  if (block == FP4_BLOCK_2D16 && format == FP4_MXFP4)
+  if (block == FP4_BLOCK_2D16 && is_mx(format))
     return fail(FP4_ERR_UNSUPPORTED, "2D16 blocks need NVFP4 or UE5M3");
   if (s_dec_scope != FP4_GLOBAL_TENSOR && s_dec_scope != FP4_GLOBAL_ROW)
     return fail(FP4_ERR_ARG, "bad s_dec_scope %d", (int)s_dec_scope);
   const bool s_dec_rows = s_dec_scope == FP4_GLOBAL_ROW;
-  if (s_dec_rows && (format == FP4_MXFP4 || block != FP4_BLOCK_1D))
+  if (s_dec_rows && (is_mx(format) || block != FP4_BLOCK_1D))
     return fail(FP4_ERR_UNSUPPORTED, "per-row s_dec needs NVFP4 or UE5M3 and 1D blocks");
   if (rows < 0 || cols < 0) return fail(FP4_ERR_SHAPE, "negative size");
   const int bs = block_len(format);
@@ -373,9 +383,13 @@ FP4_EXPORT fp4_status fp4_dequantize(fp4_format format, fp4_block block,
     if (!codes || !scales || !out) return fail(FP4_ERR_ARG, "null pointer");
     if (!aligned16(codes) || !aligned16(out)) return fail(FP4_ERR_ARG, "codes/out must be 16-byte aligned");
     if (tiled && !aligned16(scales)) return fail(FP4_ERR_ARG, "TILED scales must be 16-byte aligned");
-    if (format != FP4_MXFP4 && !s_dec) return fail(FP4_ERR_ARG, "s_dec is null");
+    if (!is_mx(format) && !s_dec) return fail(FP4_ERR_ARG, "s_dec is null");
   }
   if (rows == 0 || cols == 0) return ok();
+  if (format == FP4_MXFP8)
+    return device_status(fp4lib::launch_dequant_mx8(tiled, codes, scales, rows, cols, out,
+                                                    out_fp32, static_cast<hipStream_t>(stream)),
+                         "fp4_dequantize launch");
   return device_status(fp4lib::launch_dequant(format, block == FP4_BLOCK_2D16, tiled, codes, scales,
                                               s_dec, s_dec_rows, rows, cols, out, out_fp32,
                                               static_cast<hipStream_t>(stream)),
@@ -413,6 +427,7 @@ FP4_EXPORT fp4_status fp4_gemm(const fp4_operand* A, const fp4_operand* B, int64
   if (!A || !B) return fail(FP4_ERR_ARG, "operand descriptor is null");
   if (!valid_format(A->format) || !valid_format(B->format)) return fail(FP4_ERR_ARG, "bad format");
   if (A->format != B->format) return fail(FP4_ERR_UNSUPPORTED, "A and B formats differ");
+  if (A->format == FP4_MXFP8) return fail(FP4_ERR_UNSUPPORTED, "no GEMM takes MXFP8 operands");
   if (M < 0 || N < 0 || K < 0) return fail(FP4_ERR_SHAPE, "negative size");
   const int bs = block_len(A->format);
   if (K % bs) return fail(FP4_ERR_SHAPE, "K=%lld must be a multiple of %d", (long long)K, bs);

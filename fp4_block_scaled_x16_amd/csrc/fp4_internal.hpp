@@ -61,6 +61,10 @@ hipError_t launch_quant_row(const QuantArgs& a, hipStream_t s);
 // amaxes (a.amax, float[rows]) come from the same read that quantizes.
 hipError_t launch_quant_row_scoped(const QuantArgs& a, hipStream_t s);
 hipError_t launch_quant_col(const QuantArgs& a, hipStream_t s);
+// MXFP8 (E4M3 elements, 1x32 blocks, UE8M0 scales), rowwise or colwise.
+hipError_t launch_quant_mx8(const QuantArgs& a, bool colwise, hipStream_t s);
+hipError_t launch_dequant_mx8(int tiled, const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                              int64_t cols, void* out, int out_fp32, hipStream_t s);
 hipError_t launch_quant_2d(const QuantArgs& a, hipStream_t s);
 // Rowwise (`row`) and colwise (`col`) 1D quantization of the same input in
 // one kernel: same format and rounding mode; RHT only on the colwise side.

@@ -1,0 +1,269 @@
+// MXFP8 quantization for the attention Q/K projections (the 2D-block FP4
+// training page keeps Q and K in MXFP8): E4M3 elements in 1x32 blocks, one
+// UE8M0 scale per block, no tensor scale.  The scale is 2^e with e the
+// smallest integer such that 448 * 2^e >= amax_B -- rounded up, as NVFP4
+// paper App. B.4 does for MX scales so that no element saturates (the page
+// ties saturation to MXFP8 convergence problems); element code = sign bit 7
+// | E4M3 RNE code of |x * 2^-e|; one byte per element.
+//
+//   k_quant_mx8_row  ROWWISE: one thread per block of 32 consecutive bf16
+//                    (four 16-byte loads), 32 code bytes as two 16-byte stores
+//   k_quant_mx8_col  COLWISE (codes of X^T): a 32 x 256 tile of X through
+//                    LDS, one thread per column: its 32 rows are one block,
+//                    written as 32 contiguous bytes of the X^T code row
+//   k_dequant_mx8    codes x 2^e, fp32 or bf16
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "fp4_device.hpp"
+#include "fp4_internal.hpp"
+#include "quant_common.hpp"
+
+using namespace fp4dev;
+using namespace fp4quant;
+
+namespace {
+
+constexpr int kBS = 32;
+constexpr int kMx8Threads = 256;
+constexpr int kMx8WgPerCu = 4;
+constexpr int kColTileCols = 256;          // colwise tile: 32 rows x 256 columns
+constexpr int kColLdsStride = 256 + 2;     // bf16 per LDS row (padded: rows start 1 bank apart)
+
+// UE8M0 code and encode scale of a block: 2^e, e = min{e : 448 * 2^e >=
+// amax} clamped to [-127, 127] (a zero block: e = -127).  With amax =
+// m * 2^k, 1 <= m < 2: 448 = 1.75 * 2^8 covers it at e = k - 8 iff
+// m <= 1.75, else at e = k - 7.
+__device__ __forceinline__ uint32_t block_scale_mx8(float amax_b, float& s_enc_l) {
+  int e = -127;
+  if (amax_b > 0.0f) {
+    const uint32_t b = __float_as_uint(amax_b);
+    const int E = static_cast<int>(b >> 23);
+    const uint32_t man = b & 0x7FFFFFu;
+    int k;
+    bool le;     // m <= 1.75
+    if (E == 0) {  // fp32 subnormal: amax = man * 2^-149
+      const int lead_pos = 31 - __clz(man);
+      k = lead_pos - 149;
+      const uint32_t lead = 1u << lead_pos;
+      le = man <= lead + (lead >> 1) + (lead >> 2);
+    } else {
+      k = E - 127;
+      le = man <= 0x600000u;
+    }
+    e = le ? k - 8 : k - 7;
+    e = e < -127 ? -127 : (e > 127 ? 127 : e);
+  }
+  const int ne = -e;
+  s_enc_l = ne >= -126 ? __uint_as_float(static_cast<uint32_t>(ne + 127) << 23)
+                       : __uint_as_float(0x00400000u);
+  return static_cast<uint32_t>(e + 127);
+}
+
+// Element code of v * s: sign bit 7 | E4M3 RNE magnitude (saturating at 448).
+// Counters: cnt[3] += |y| > 448; cnt[4] += (v != 0 and magnitude code 0).
+template <bool CNT>
+__device__ __forceinline__ uint32_t e4m3_code(float v, float s, uint32_t (&cnt)[5]) {
+  const float y = v * s;
+  const float t = fabsf(y);
+  const uint32_t mag = scale_m3_encode<7>(t, 448.0f, 0x7Eu);
+  if constexpr (CNT) {
+    cnt[3] += t > 448.0f ? 1u : 0u;
+    cnt[4] += (v != 0.0f && mag == 0u) ? 1u : 0u;
+  }
+  return mag | ((__float_as_uint(y) >> 24) & 0x80u);
+}
+
+template <bool CNT>
+__global__ __launch_bounds__(kMx8Threads) void k_quant_mx8_row(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, fp4_counters* __restrict__ counters,
+    int tiled) {
+  const uint64_t bpr = static_cast<uint64_t>(cols) / kBS;
+  const uint64_t n = static_cast<uint64_t>(rows) * bpr;
+  const uint64_t kg = (bpr + 7) >> 3;
+  uint32_t cnt[5] = {0, 0, 0, 0, 0};
+  for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kMx8Threads + threadIdx.x; i < n;
+       i += static_cast<uint64_t>(gridDim.x) * kMx8Threads) {
+    const uint64_t r = i / bpr, j = i - r * bpr;
+    const uint4* src = reinterpret_cast<const uint4*>(x + r * ld + j * kBS);
+    uint4 q[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) q[k] = src[k];
+    float v[kBS];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) unpack8(q[k], v + 8 * k);
+    float amax_b = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kBS; ++k) amax_b = fmaxf(amax_b, fabsf(v[k]));
+    float s;
+    const uint32_t sc = block_scale_mx8(amax_b, s);
+    uint32_t w[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      w[k] = e4m3_code<CNT>(v[4 * k], s, cnt) | (e4m3_code<CNT>(v[4 * k + 1], s, cnt) << 8) |
+             (e4m3_code<CNT>(v[4 * k + 2], s, cnt) << 16) |
+             (e4m3_code<CNT>(v[4 * k + 3], s, cnt) << 24);
+    }
+    uint4* dst = reinterpret_cast<uint4*>(codes + r * static_cast<uint64_t>(cols) + j * kBS);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    scales[tiled ? tiled_scale_offset(r, j, kg) : i] = static_cast<uint8_t>(sc);
+  }
+  if constexpr (CNT) flush_counters<kMx8Threads>(cnt, counters);
+}
+
+// COLWISE: tile (32 rows) x (256 columns) of X; thread t owns column t of
+// the tile, i.e. row c0 + t of X^T, block r0 / 32 of it.
+template <bool CNT>
+__global__ __launch_bounds__(kMx8Threads) void k_quant_mx8_col(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, fp4_counters* __restrict__ counters,
+    int tiled) {
+  __shared__ uint16_t tile[kBS * kColLdsStride];
+  const int64_t tiles_r = rows / kBS;
+  const int64_t tiles_c = (cols + kColTileCols - 1) / kColTileCols;
+  const uint64_t bpr_t = static_cast<uint64_t>(rows) / kBS;      // blocks per X^T row
+  const uint64_t kg = (bpr_t + 7) >> 3;
+  const int t = threadIdx.x;
+  uint32_t cnt[5] = {0, 0, 0, 0, 0};
+  for (int64_t tile_id = blockIdx.x; tile_id < tiles_r * tiles_c; tile_id += gridDim.x) {
+    const int64_t tr = tile_id / tiles_c, tc = tile_id - tr * tiles_c;
+    const int64_t r0 = tr * kBS, c0 = tc * kColTileCols;
+    // 32 rows x 256 columns = 1024 chunks of 8 bf16; chunk q: row q / 32,
+    // columns 8 (q % 32) ..; chunks beyond the last column load nothing
+    __syncthreads();     // the previous tile's LDS reads are done
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int q = t + k * kMx8Threads;
+      const int lr = q >> 5, lc = (q & 31) * 8;
+      if (c0 + lc < cols) {
+        const uint4 u = *reinterpret_cast<const uint4*>(x + (r0 + lr) * ld + c0 + lc);
+        uint32_t* d = reinterpret_cast<uint32_t*>(tile + lr * kColLdsStride + lc);
+        d[0] = u.x;
+        d[1] = u.y;
+        d[2] = u.z;
+        d[3] = u.w;
+      }
+    }
+    __syncthreads();
+    const int64_t c = c0 + t;
+    if (c < cols) {
+      float v[kBS];
+#pragma unroll
+      for (int k = 0; k < kBS; ++k) v[k] = bf16_to_f32(tile[k * kColLdsStride + t]);
+      float amax_b = 0.0f;
+#pragma unroll
+      for (int k = 0; k < kBS; ++k) amax_b = fmaxf(amax_b, fabsf(v[k]));
+      float s;
+      const uint32_t sc = block_scale_mx8(amax_b, s);
+      uint32_t w[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        w[k] = e4m3_code<CNT>(v[4 * k], s, cnt) | (e4m3_code<CNT>(v[4 * k + 1], s, cnt) << 8) |
+               (e4m3_code<CNT>(v[4 * k + 2], s, cnt) << 16) |
+               (e4m3_code<CNT>(v[4 * k + 3], s, cnt) << 24);
+      }
+      uint4* dst = reinterpret_cast<uint4*>(codes + c * static_cast<uint64_t>(rows) + r0);
+      dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+      dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+      const uint64_t j = static_cast<uint64_t>(tr);
+      scales[tiled ? tiled_scale_offset(static_cast<uint64_t>(c), j, kg)
+                   : static_cast<uint64_t>(c) * bpr_t + j] = static_cast<uint8_t>(sc);
+    }
+  }
+  if constexpr (CNT) flush_counters<kMx8Threads>(cnt, counters);
+}
+
+// v = fp32(e4m3 * 2^e) (exact), fp32 or bf16 (RNE) out; one thread per block.
+template <bool F32>
+__global__ __launch_bounds__(kMx8Threads) void k_dequant_mx8(const uint8_t* __restrict__ codes,
+                                                             const uint8_t* __restrict__ scales,
+                                                             int64_t rows, int64_t cols,
+                                                             void* __restrict__ out, int tiled) {
+  const uint64_t bpr = static_cast<uint64_t>(cols) / kBS;
+  const uint64_t n = static_cast<uint64_t>(rows) * bpr;
+  const uint64_t kg = (bpr + 7) >> 3;
+  for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kMx8Threads + threadIdx.x; i < n;
+       i += static_cast<uint64_t>(gridDim.x) * kMx8Threads) {
+    const uint64_t r = i / bpr, j = i - r * bpr;
+    const float s = ue8m0_decode(scales[tiled ? tiled_scale_offset(r, j, kg) : i]);
+    const uint4* src = reinterpret_cast<const uint4*>(codes + i * kBS);
+    const uint4 a = src[0], b = src[1];
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    float v[kBS];
+#pragma unroll
+    for (int k = 0; k < kBS; ++k) {
+      const uint32_t c = (w[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+      const float m = scale_m3_decode<7>(c & 0x7Fu) * s;
+      v[k] = (c & 0x80u) ? -m : m;
+    }
+    if constexpr (F32) {
+      float4* dst = reinterpret_cast<float4*>(static_cast<float*>(out) + i * kBS);
+#pragma unroll
+      for (int k = 0; k < kBS / 4; ++k)
+        dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+    } else {
+      uint32_t h[kBS / 2];
+#pragma unroll
+      for (int k = 0; k < kBS / 2; ++k) {
+        uint32_t lo = __float_as_uint(v[2 * k]), hi = __float_as_uint(v[2 * k + 1]);
+        lo = (lo + 0x7FFFu + ((lo >> 16) & 1u)) >> 16;
+        hi = (hi + 0x7FFFu + ((hi >> 16) & 1u)) >> 16;
+        h[k] = (lo & 0xFFFFu) | (hi << 16);
+      }
+      uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + i * kBS);
+#pragma unroll
+      for (int k = 0; k < kBS / 8; ++k)
+        dst[k] = make_uint4(h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]);
+    }
+  }
+}
+
+}  // namespace
+
+namespace fp4lib {
+
+hipError_t launch_quant_mx8(const QuantArgs& a, bool colwise, hipStream_t s) {
+  if (a.rows > 0 && a.cols > 0) {
+    if (colwise) {
+      const int64_t tiles = (a.rows / kBS) * ((a.cols + kColTileCols - 1) / kColTileCols);
+      const int64_t cap = grid_cap(kMx8WgPerCu);
+      const int grid = static_cast<int>(tiles < cap ? tiles : cap);
+      if (a.counters)
+        hipLaunchKernelGGL(k_quant_mx8_col<true>, dim3(grid), dim3(kMx8Threads), 0, s, a.x, a.rows,
+                           a.cols, a.ld, a.codes, a.scales, a.counters, a.tiled);
+      else
+        hipLaunchKernelGGL(k_quant_mx8_col<false>, dim3(grid), dim3(kMx8Threads), 0, s, a.x,
+                           a.rows, a.cols, a.ld, a.codes, a.scales, a.counters, a.tiled);
+    } else {
+      const uint64_t n = static_cast<uint64_t>(a.rows) * static_cast<uint64_t>(a.cols / kBS);
+      const int grid = grid_for(n, kMx8WgPerCu, kMx8Threads);
+      if (a.counters)
+        hipLaunchKernelGGL(k_quant_mx8_row<true>, dim3(grid), dim3(kMx8Threads), 0, s, a.x, a.rows,
+                           a.cols, a.ld, a.codes, a.scales, a.counters, a.tiled);
+      else
+        hipLaunchKernelGGL(k_quant_mx8_row<false>, dim3(grid), dim3(kMx8Threads), 0, s, a.x,
+                           a.rows, a.cols, a.ld, a.codes, a.scales, a.counters, a.tiled);
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_mx8(int tiled, const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                              int64_t cols, void* out, int out_fp32, hipStream_t s) {
+  if (rows > 0 && cols > 0) {
+    const uint64_t n = static_cast<uint64_t>(rows) * static_cast<uint64_t>(cols / kBS);
+    const int grid = grid_for(n, 2, kMx8Threads);
+    if (out_fp32)
+      hipLaunchKernelGGL(k_dequant_mx8<true>, dim3(grid), dim3(kMx8Threads), 0, s, codes, scales,
+                         rows, cols, out, tiled);
+    else
+      hipLaunchKernelGGL(k_dequant_mx8<false>, dim3(grid), dim3(kMx8Threads), 0, s, codes, scales,
+                         rows, cols, out, tiled);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fp4lib

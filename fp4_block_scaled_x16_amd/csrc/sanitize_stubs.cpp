@@ -22,6 +22,11 @@ hipError_t launch_quant_row(const QuantArgs&, hipStream_t) { return hipErrorNoDe
 hipError_t launch_quant_row_scoped(const QuantArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_quant_col(const QuantArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_quant_2d(const QuantArgs&, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_quant_mx8(const QuantArgs&, bool, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_dequant_mx8(int, const uint8_t*, const uint8_t*, int64_t, int64_t, void*, int,
+                              hipStream_t) {
+  return hipErrorNoDevice;
+}
 hipError_t launch_quant_dual(const QuantArgs&, const QuantArgs&, hipStream_t) {
   return hipErrorNoDevice;
 }

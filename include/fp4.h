@@ -50,14 +50,24 @@ extern "C" {
 #define FP4_ENUM_INT
 #endif
 
-/* Element payload is always E2M1 (NVFP4 paper §3: values +-{0,.5,1,1.5,2,3,4,6}).
- * The block-scale format and block length differ:
+/* The FP4 formats' element payload is E2M1 (NVFP4 paper §3: values
+ * +-{0,.5,1,1.5,2,3,4,6}), two codes per byte; their block-scale format and
+ * block length differ:
  *   FP4_NVFP4  1x16 blocks, E4M3 scale (max 448), fp32 tensor scale  (§3, App. B)
  *   FP4_UE5M3  1x16 blocks, unsigned E5M3 scale (bias 15, all codes finite,
  *              max 122880), fp32 tensor scale with target T          (UE5M3 abstract)
  *   FP4_MXFP4  1x32 blocks, UE8M0 power-of-two scale rounded up, no tensor
- *              scale                                                  (§3, App. B.4) */
-typedef enum fp4_format_e FP4_ENUM_INT { FP4_NVFP4 = 0, FP4_UE5M3 = 1, FP4_MXFP4 = 2 } fp4_format;
+ *              scale                                                  (§3, App. B.4)
+ * and one 8-bit format, for the attention Q/K projections that the 2D-block
+ * FP4 page keeps in MXFP8:
+ *   FP4_MXFP8  E4M3 elements (sign in bit 7, max 448), one byte each, in 1x32
+ *              blocks with a UE8M0 scale 2^e, e the smallest integer with
+ *              448 * 2^e >= amax_B (rounded up like MXFP4's, App. B.4), no
+ *              tensor scale; element code = E4M3 RNE of |x * 2^-e|.
+ *              Quantize (1D, RNE) and dequantize only: no GEMM takes it. */
+typedef enum fp4_format_e FP4_ENUM_INT {
+  FP4_NVFP4 = 0, FP4_UE5M3 = 1, FP4_MXFP4 = 2, FP4_MXFP8 = 3
+} fp4_format;
 
 /* Element rounding: nearest-even, or stochastic (NVFP4 paper §4.4). */
 typedef enum fp4_round_e FP4_ENUM_INT { FP4_RNE = 0, FP4_SR = 1 } fp4_round;
@@ -189,14 +199,15 @@ fp4_status fp4_amax(const fp4_quant_desc* desc /* host */, const uint16_t* x, in
  *   x       [rows, cols] bf16 (ld), device.
  *   codes   device, packed two codes per byte, element 2j in the low nibble
  *           of byte j.  ROWWISE: [rows, cols/2] bytes; COLWISE: [cols, rows/2].
+ *           MXFP8: one byte per element, [rows, cols] / [cols, rows].
  *   scales  device, one byte per block.  1D ROWWISE: [rows, cols/BS];
  *           1D COLWISE: [cols, rows/BS]; 2D16: [rows/16, cols/16]
- *           (BS = 16, or 32 for MXFP4).  1D scales follow desc->scale_layout
+ *           (BS = 16, or 32 for MXFP4 and MXFP8).  1D scales follow desc->scale_layout
  *           (TILED: 16-byte aligned, size as given with fp4_scale_layout).
  *   codes_t device, 2D16 with emit_transpose only: [cols, rows/2] codes of
  *           X^T quantized with the same tile scales (NULL otherwise).
  *   amax    device float.  NVFP4/UE5M3: written (amax_given = 0) or read
- *           (amax_given = 1).  MXFP4: unused, may be NULL.  global_scope
+ *           (amax_given = 1).  MXFP4, MXFP8: unused, may be NULL.  global_scope
  *           ROW: device float[rows], one amax per row, written or read
  *           likewise (written in the quantizing pass, no separate pass).
  *   s_dec   device float or NULL: receives s_dec_G = 1 / s_enc_G (1 for

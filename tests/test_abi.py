@@ -89,6 +89,13 @@ def quant(lib, d, rows=32, cols=64, ld=None, x=FAKE, codes=FAKE, scales=FAKE, co
     (dict(), -1, 64, 2),
     (dict(scale_layout=2), 32, 64, 1),
     (dict(block=1, scale_layout=1), 32, 64, 3),      # TILED scales are 1D only
+    (dict(format=3, round=1), 32, 64, 3),            # MXFP8 is RNE only
+    (dict(format=3, block=1), 32, 64, 3),            # MXFP8 is 1D
+    (dict(format=3, rht=1, orient=1), 32, 64, 3),    # no RHT for MXFP8
+    (dict(format=3, amax_given=1), 32, 64, 3),       # no tensor amax
+    (dict(format=3), 32, 48, 2),                     # cols % 32
+    (dict(format=3, orient=1), 48, 64, 2),           # rows % 32 (colwise)
+    (dict(global_scope=1, format=3), 32, 64, 3),     # no per-row scales
     (dict(global_scope=2), 32, 64, 1),               # bad global scope
     (dict(global_scope=1, format=2), 32, 64, 3),     # per-row scales: two-level formats
     (dict(global_scope=1, orient=1), 32, 64, 3),     # per-row scales: ROWWISE only
@@ -165,6 +172,7 @@ def dual(lib, rd, cd, rows=32, cols=64, x=FAKE, codes=FAKE, scales=FAKE, codes_t
     (dict(), dict(orient=1), 24, 64, 2),                      # rows % 16
     (dict(), dict(orient=1), 32, 40, 2),                      # cols % 16
     (dict(format=2), dict(orient=1, format=2), 48, 64, 2),    # rows % 32
+    (dict(format=3), dict(orient=1, format=3), 64, 64, 3),    # MXFP8: single quantizations
     (dict(global_scope=1), dict(orient=1), 32, 64, 3),        # per-row scales: fp4_quantize
     (dict(), dict(orient=1, global_scope=1), 32, 64, 3),
 ])
@@ -215,6 +223,10 @@ def test_other_entry_points_reject(lib):
     assert lib.fp4_dequantize(0, 0, 1, FAKE, ctypes.c_void_p(0x10008), FAKE, 0, 32, 64, FAKE, 1,
                               None) == 1
     assert lib.fp4_dequantize(0, 0, 0, FAKE, FAKE, FAKE, 2, 32, 64, FAKE, 1, None) == 1
+    assert lib.fp4_dequantize(3, 1, 0, FAKE, FAKE, None, 0, 32, 64, FAKE, 1, None) == 3
+    assert lib.fp4_dequantize(3, 0, 0, FAKE, FAKE, None, 1, 32, 64, FAKE, 1, None) == 3
+    assert lib.fp4_dequantize(3, 0, 0, FAKE, FAKE, None, 0, 32, 48, FAKE, 1, None) == 2
+    assert lib.fp4_dequantize(4, 0, 0, FAKE, FAKE, None, 0, 32, 64, FAKE, 1, None) == 1
     assert lib.fp4_dequantize(2, 0, 0, FAKE, FAKE, FAKE, 1, 32, 64, FAKE, 1, None) == 3
     assert lib.fp4_dequantize(0, 1, 0, FAKE, FAKE, FAKE, 1, 32, 64, FAKE, 1, None) == 3
     assert rht_call(lib, desc(orient=1), rows=40) == 2
@@ -242,6 +254,7 @@ def op(fmt=0, codes=0x10000, ld=32, rg=1, layout=0, scales=0x20000, s_dec=0x3000
     (op(0, layout=3), op(0), 16, 16, 64, 1),
     (op(0, layout=1, rg=16), op(0), 16, 16, 64, 3),          # TILED scales are 1D
     (op(2, layout=1, scales=0x20008), op(2), 16, 16, 64, 1),  # TILED misaligned
+    (op(3), op(3), 16, 16, 64, 3),                            # no MXFP8 GEMM
     (op(0, scope=2), op(0), 16, 16, 64, 1),                   # bad s_dec scope
     (op(2, scope=1), op(2), 16, 16, 64, 3),                   # per-row s_dec with MXFP4
     (op(0), op(0, scope=1, s_dec=0), 16, 16, 64, 3),          # per-row s_dec is required

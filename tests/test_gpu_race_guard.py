@@ -76,6 +76,13 @@ def test_quantize_1d(fmt, rnd, orient):
                                                   offset=1, counters=c, scale_layout="tiled"))
 
 
+@pytest.mark.parametrize("orient", ["row", "col"])
+def test_quantize_mxfp8(orient):
+    x = dev(X)
+    same_at_all_geometries(lambda c: api.quantize(x, "mxfp8", orient=orient, counters=c,
+                                                  scale_layout="tiled"))
+
+
 @pytest.mark.parametrize("rht_n", [16, 64])
 def test_quantize_col_rht(rht_n):
     x = dev(X)
