@@ -231,6 +231,33 @@ __global__ __launch_bounds__(kStream) void k_quant_row(
   if constexpr (CNT) flush_counters<kStream>(cnt, counters);
 }
 
+// ------------------------------------------- transposing LDS tile ------
+// The colwise and dual quantizers stage a tile of 8 BS rows x 64 bf16
+// columns of X in LDS: each row is eight 16-byte chunks, written by row
+// (one lane per chunk or block) and read by column (lane (grp, pair) reads
+// 32-bit word `pair` of rows grp * BS + k).  Chunk c of row r sits at
+//   r * 8 + (r / BS) * 8 + (c ^ f(r)),
+// f(r) = (r / BS) & 7 ^ (low bits of r): the XOR puts the eight row groups a
+// column read touches at once in eight different chunk columns, and the
+// rows that one 16-byte write instruction covers (2 or 4 consecutive rows)
+// in different chunk columns too; the one-chunk pad after each group of BS
+// rows alternates the group's 128-byte bank half, so neither pattern
+// conflicts with 32 or with 64 four-byte banks.
+template <int BS>
+__device__ __forceinline__ int tile_chunk(int r, int c) {
+  const int f = ((r / BS) & 7) ^ (BS == 16 ? ((r ^ (r >> 1)) & 1) : ((r ^ (r >> 2)) & 3));
+  return r * 8 + (r / BS) * 8 + (c ^ f);
+}
+
+template <int BS>
+constexpr int kTileChunks = 8 * BS * 8 + 8 * 8;
+
+// 32-bit word p (0..31: bf16 columns 2p, 2p + 1) of tile row r.
+template <int BS>
+__device__ __forceinline__ uint32_t tile_word(const uint4* tile, int r, int p) {
+  return reinterpret_cast<const uint32_t*>(tile)[tile_chunk<BS>(r, p >> 2) * 4 + (p & 3)];
+}
+
 // ------------------------------------------------------ colwise 1D ------
 // Quantizes X^T: blocks are BS consecutive rows of one column.  A workgroup
 // stages a (8 BS) x 64 tile of X in LDS (coalesced 16-byte row loads), then
@@ -251,8 +278,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
   constexpr int BS = FMT == kMX ? 32 : 16;
   constexpr int TR = 8 * BS;        // tile rows (8 groups)
   constexpr int TC = 64;            // tile columns
-  constexpr int LDW = TC / 2 + 1;   // LDS row pitch in 32-bit words (odd: spreads banks)
-  __shared__ uint32_t tile[TR * LDW];
+  __shared__ uint4 tile[kTileChunks<BS>];
 
   float s_enc_g = 1.0f, s_dec_g = 1.0f;
   if constexpr (FMT != kMX && !AMX) global_scales(*amax, target, s_enc_g, s_dec_g);
@@ -280,11 +306,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
       uint4 q = make_uint4(0, 0, 0, 0);
       if (r0 + lr < rows && c0 + lc < cols)
         q = *reinterpret_cast<const uint4*>(x + (r0 + lr) * ld + c0 + lc);
-      uint32_t* d = tile + lr * LDW + (lc >> 1);
-      d[0] = q.x;
-      d[1] = q.y;
-      d[2] = q.z;
-      d[3] = q.w;
+      tile[tile_chunk<BS>(lr, chunk & 7)] = q;
     }
     __syncthreads();
     const int64_t col = c0 + 2 * pair;
@@ -296,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
         float v[BS];
 #pragma unroll
         for (int k = 0; k < BS; ++k) {
-          const uint32_t w = tile[(grp * BS + k) * LDW + pair];
+          const uint32_t w = tile_word<BS>(tile, grp * BS + k, pair);
           v[k] = bf16_to_f32(h ? (w >> 16) : (w & 0xFFFFu));
         }
         if constexpr (RHT) rht_n(*reinterpret_cast<float(*)[16]>(v), rht, grp);
@@ -358,11 +380,10 @@ __attribute__((amdgpu_waves_per_eu(FMT == kMX ? 1 : 3))) void k_quant_dual(
   constexpr int BS = FMT == kMX ? 32 : 16;
   constexpr int TR = 8 * BS;        // tile rows (8 groups)
   constexpr int TC = 64;            // tile columns
-  constexpr int LDW = TC / 2 + 1;   // LDS row pitch in 32-bit words (odd: spreads banks)
   constexpr int BPR = TC / BS;      // rowwise blocks per tile row
   constexpr int NB = TR * BPR / kThreads;   // rowwise blocks per thread and tile (2)
   static_assert(NB * kThreads == TR * BPR, "tile must split evenly into blocks");
-  __shared__ uint32_t tile[TR * LDW];
+  __shared__ uint4 tile[kTileChunks<BS>];
 
   float s_enc_g = 1.0f, s_dec_g = 1.0f, s_enc_gt = 1.0f, s_dec_gt = 1.0f;
   if constexpr (FMT != kMX) {
@@ -414,14 +435,8 @@ __attribute__((amdgpu_waves_per_eu(FMT == kMX ? 1 : 3))) void k_quant_dual(
       const int b = t + k * kThreads;
       const int lr = b / BPR, lc = (b % BPR) * BS;
       const int64_t r = r0 + lr, c = c0 + lc;
-      uint32_t* d = tile + lr * LDW + (lc >> 1);
 #pragma unroll
-      for (int e = 0; e < BS / 8; ++e) {
-        d[4 * e] = q[k][e].x;
-        d[4 * e + 1] = q[k][e].y;
-        d[4 * e + 2] = q[k][e].z;
-        d[4 * e + 3] = q[k][e].w;
-      }
+      for (int e = 0; e < BS / 8; ++e) tile[tile_chunk<BS>(lr, lc / 8 + e)] = q[k][e];
       float v[BS];
 #pragma unroll
       for (int e = 0; e < BS / 8; ++e) unpack8(q[k][e], v + 8 * e);
@@ -465,7 +480,7 @@ __attribute__((amdgpu_waves_per_eu(FMT == kMX ? 1 : 3))) void k_quant_dual(
         float v[BS];
 #pragma unroll
         for (int k = 0; k < BS; ++k) {
-          const uint32_t w = tile[(grp * BS + k) * LDW + pair];
+          const uint32_t w = tile_word<BS>(tile, grp * BS + k, pair);
           v[k] = bf16_to_f32(h ? (w >> 16) : (w & 0xFFFFu));
         }
         if constexpr (RHT) rht_n(*reinterpret_cast<float(*)[16]>(v), rht, grp);
