@@ -25,6 +25,7 @@ ROWWISE, COLWISE = 0, 1
 SCALES_ROWMAJOR, SCALES_TILED = 0, 1
 SCALE_LAYOUTS = {"rowmajor": SCALES_ROWMAJOR, "tiled": SCALES_TILED}
 GLOBAL_TENSOR, GLOBAL_ROW = 0, 1
+COUNT_LEVELS = {"all": 0, "scales": 1}
 GLOBAL_SCOPES = {"tensor": GLOBAL_TENSOR, "row": GLOBAL_ROW}
 COUNTER_NAMES = ("scale_saturated", "scale_underflow", "scale_subnormal",
                  "elem_saturated", "elem_underflow")
@@ -43,7 +44,7 @@ class QuantDesc(ctypes.Structure):
                 ("amax_given", ctypes.c_int), ("emit_transpose", ctypes.c_int),
                 ("scale_layout", ctypes.c_int), ("rht_n", ctypes.c_int),
                 ("rht_signs_hi", ctypes.c_uint32 * 3), ("scale_round", ctypes.c_int),
-                ("global_scope", ctypes.c_int)]
+                ("global_scope", ctypes.c_int), ("count_level", ctypes.c_int)]
 
 
 SCALE_ROUND = {"rne": 0, "up": 1}
@@ -206,7 +207,8 @@ def tiled_scale_bytes(rows, blocks_per_row):
 
 def quantize(x, fmt="nvfp4", block="1d", orient="row", rnd="rne", seed=0, offset=0, rht=False,
              signs=0, target=448.0, amax_in=None, emit_transpose=False, counters=None,
-             scale_layout="rowmajor", rht_n=16, scale_round="rne", global_scope="tensor"):
+             scale_layout="rowmajor", rht_n=16, scale_round="rne", global_scope="tensor",
+             count="all"):
     """Quantize a bf16 [R, C] matrix.  orient="col" quantizes X^T ([C, R]).
     scale_layout: "rowmajor" or "tiled" (1D blocks only).  rht_n: size of
     the RHT (4, 16, 32, 64, 128); signs: its sign mask, up to 128 bits.
@@ -216,7 +218,8 @@ def quantize(x, fmt="nvfp4", block="1d", orient="row", rnd="rne", seed=0, offset
 
     amax_in: None -> computed on the device; else a device fp32 [1] tensor read
     as the (possibly stale) tensor amax ([R] per-row amaxes with "row").
-    counters: optional device uint64 [5] tensor, accumulated.
+    counters: optional device uint64 [5] tensor, accumulated; count: "all"
+    or "scales" (block-scale events only).
     """
     x = _as_bf16_bits(x)
     f = _fmt(fmt)
@@ -245,7 +248,7 @@ def quantize(x, fmt="nvfp4", block="1d", orient="row", rnd="rne", seed=0, offset
     desc = QuantDesc(f, blk, COLWISE if col else ROWWISE, SR if rnd == "sr" else RNE,
                      int(seed), int(offset), int(bool(rht)), s_lo, float(target),
                      int(amax_in is not None), int(bool(emit_transpose)), layout, int(rht_n), s_hi,
-                     SCALE_ROUND[scale_round], scope)
+                     SCALE_ROUND[scale_round], scope, COUNT_LEVELS[count])
     lib = load_library()
     _check(lib.fp4_quantize(ctypes.byref(desc), _ptr(x), R, C, x.stride(0), _ptr(codes),
                             _ptr(scales), _ptr(codes_t), _ptr(am), _ptr(s_dec), _ptr(counters),
@@ -262,7 +265,7 @@ def _scales_1d(rows, blocks, layout, dev):
 def quantize_dual(x, fmt="nvfp4", rnd="rne", seed=0, offset=0, offset_t=None, rht=False, signs=0,
                   target=448.0, amax_in=None, amax_t_in=None, counters=None,
                   scale_layout="rowmajor", scale_layout_t=None, rht_n=16, scale_round="rne",
-                  rht_row=False, signs_row=0, rht_n_row=16):
+                  rht_row=False, signs_row=0, rht_n_row=16, count="all"):
     """Rowwise and colwise 1D quantization of a bf16 [R, C] matrix from one
     read: returns (rowwise Quantized [R, C], colwise Quantized of X^T [C, R]).
 
@@ -271,7 +274,8 @@ def quantize_dual(x, fmt="nvfp4", rnd="rne", seed=0, offset=0, offset_t=None, rh
     scale_layout_t (default scale_layout); the rowwise side may rotate along
     the rows (rht_row/signs_row, rht_n_row 4 or 16).  amax_in / amax_t_in:
     None -> computed on the device, else device fp32 [1] tensors read as
-    the given amax of each side.
+    the given amax of each side.  count: "all" or "scales" (block-scale
+    events only).
     """
     x = _as_bf16_bits(x)
     f = _fmt(fmt)
@@ -295,12 +299,13 @@ def quantize_dual(x, fmt="nvfp4", rnd="rne", seed=0, offset=0, offset_t=None, rh
     s_lo, s_hi = _sign_words(signs)
     sr_mode = SCALE_ROUND[scale_round]
     r_lo, r_hi = _sign_words(signs_row)
+    cl = COUNT_LEVELS[count]
     d_row = QuantDesc(f, BLOCK_1D, ROWWISE, r, int(seed), int(offset), int(bool(rht_row)), r_lo,
                       float(target), int(amax_in is not None), 0, lay, int(rht_n_row), r_hi,
-                      sr_mode)
+                      sr_mode, GLOBAL_TENSOR, cl)
     d_col = QuantDesc(f, BLOCK_1D, COLWISE, r, int(seed), int(offset_t), int(bool(rht)), s_lo,
                       float(target), int(amax_t_in is not None), 0, lay_t, int(rht_n), s_hi,
-                      sr_mode)
+                      sr_mode, GLOBAL_TENSOR, cl)
     lib = load_library()
     _check(lib.fp4_quantize_dual(ctypes.byref(d_row), ctypes.byref(d_col), _ptr(x), R, C,
                                  x.stride(0), _ptr(codes), _ptr(scales), _ptr(codes_t),

@@ -155,6 +155,8 @@ FP4_EXPORT fp4_status fp4_quantize(const fp4_quant_desc* d, const uint16_t* x, i
   if (d->amax_given && !two_level) return fail(FP4_ERR_UNSUPPORTED, "MX formats have no tensor amax");
   if (d->global_scope != FP4_GLOBAL_TENSOR && d->global_scope != FP4_GLOBAL_ROW)
     return fail(FP4_ERR_ARG, "bad global_scope %d", (int)d->global_scope);
+  if (d->count_level != FP4_COUNT_ALL && d->count_level != FP4_COUNT_SCALES)
+    return fail(FP4_ERR_ARG, "bad count_level %d", (int)d->count_level);
   const bool row_scope = d->global_scope == FP4_GLOBAL_ROW;
   if (row_scope && (!two_level || is2d || d->orient != FP4_ROWWISE))
     return fail(FP4_ERR_UNSUPPORTED, "global_scope ROW needs NVFP4 or UE5M3, 1D, ROWWISE");
@@ -221,6 +223,7 @@ FP4_EXPORT fp4_status fp4_quantize(const fp4_quant_desc* d, const uint16_t* x, i
   a.emit_transpose = d->emit_transpose;
   a.tiled = tiled ? 1 : 0;
   a.amax_given = d->amax_given ? 1 : 0;
+  a.count_elems = d->count_level == FP4_COUNT_ALL ? 1 : 0;
   hipError_t e;
   if (mx8) e = fp4lib::launch_quant_mx8(a, d->orient == FP4_COLWISE, s);
   else if (row_scope) e = fp4lib::launch_quant_row_scoped(a, s);
@@ -263,7 +266,11 @@ FP4_EXPORT fp4_status fp4_quantize_dual(const fp4_quant_desc* rd, const fp4_quan
     if (d->global_scope != FP4_GLOBAL_TENSOR)
       return fail(FP4_ERR_UNSUPPORTED, "%s: dual quantization has tensor-scope global scales "
                                        "(per-row scales: fp4_quantize ROWWISE)", side);
+    if (d->count_level != FP4_COUNT_ALL && d->count_level != FP4_COUNT_SCALES)
+      return fail(FP4_ERR_ARG, "%s: bad count_level %d", side, (int)d->count_level);
   }
+  if (rd->count_level != cd->count_level)
+    return fail(FP4_ERR_UNSUPPORTED, "the two descs count different events");
   if (rd->orient != FP4_ROWWISE || cd->orient != FP4_COLWISE)
     return fail(FP4_ERR_UNSUPPORTED, "descs must be ROWWISE then COLWISE");
   if (rd->format != cd->format) return fail(FP4_ERR_UNSUPPORTED, "the two formats differ");
@@ -348,6 +355,7 @@ FP4_EXPORT fp4_status fp4_quantize_dual(const fp4_quant_desc* rd, const fp4_quan
     a[i].offset = ds[i]->offset;
     copy_signs(ds[i], a[i].rht_signs);
     a[i].rht_n = rht_size(ds[i]);
+    a[i].count_elems = ds[i]->count_level == FP4_COUNT_ALL ? 1 : 0;
     a[i].scale_up = ds[i]->format != FP4_MXFP4 && ds[i]->scale_round == FP4_SCALE_UP;
     a[i].format = ds[i]->format;
     a[i].round = ds[i]->round;

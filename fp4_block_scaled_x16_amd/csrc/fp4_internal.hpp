@@ -28,6 +28,7 @@ struct QuantArgs {
   int tiled;             // 1D scales in the TILED layout (2 KiB atoms of 256 rows x 8 blocks)
   int scale_up;          // block scales rounded up (truncation-free), two-level formats
   int amax_given;        // per-row scope: read amax[r] instead of computing it
+  int count_elems;       // with counters: element events too (else block-scale events only)
 };
 
 struct GemmOperand {

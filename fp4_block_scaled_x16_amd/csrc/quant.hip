@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kStream) void k_amax_rht(const uint16_t* __restrict
 // grid stride is a multiple of 64, so lane l handles blocks i = l mod 64,
 // and the N / 16 blocks of a group (cols % N == 0) sit on consecutive
 // lanes with the same bits above N / 16, which rht_n combines by shuffles.
-template <int FMT, int RND, bool CNT, bool RHT = false>
+template <int FMT, int RND, int CNT, bool RHT = false>
 __global__ __launch_bounds__(kStream) void k_quant_row(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, const float* __restrict__ amax,
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(kStream) void k_quant_row(
     float s_enc_l;
     const uint32_t sc = scale_for_block<FMT>(amax_b, s_enc_g, s_dec_g, s_enc_l, cnt, scale_up);
     uint32_t words[BS / 8];
-    encode_block<BS, RND, CNT>(v, s_enc_l, r_cur * static_cast<uint64_t>(cols) + j_cur * BS, seed,
+    encode_block<BS, RND, CNT == 2>(v, s_enc_l, r_cur * static_cast<uint64_t>(cols) + j_cur * BS, seed,
                                offset, words, cnt);
     uint8_t* dst = codes + r_cur * (static_cast<uint64_t>(cols) >> 1) + j_cur * (BS / 2);
     if constexpr (BS == 16) {
@@ -268,7 +268,7 @@ __device__ __forceinline__ uint32_t tile_word(const uint4* tile, int r, int p) {
 // AMX (amax only): the same staging and rotation, but instead of encoding,
 // the largest |value| is reduced into *amax_out (fp32 bits, atomic max):
 // the tensor amax in the rotated space for the N-point RHT variants.
-template <int FMT, int RND, bool RHT, bool CNT, bool AMX = false>
+template <int FMT, int RND, bool RHT, int CNT, bool AMX = false>
 __global__ __launch_bounds__(kThreads) void k_quant_col(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, const float* __restrict__ amax,
@@ -333,7 +333,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
         float s_enc_l;
         const uint32_t sc = scale_for_block<FMT>(amax_b, s_enc_g, s_dec_g, s_enc_l, cnt, scale_up);
         uint32_t words[BS / 8];
-        encode_block<BS, RND, CNT>(v, s_enc_l, static_cast<uint64_t>(c) * rows + row, seed,
+        encode_block<BS, RND, CNT == 2>(v, s_enc_l, static_cast<uint64_t>(c) * rows + row, seed,
                                    offset, words, cnt);
         uint8_t* dst = codes + c * (rows >> 1) + (row >> 1);
         if constexpr (BS == 16) {
@@ -366,7 +366,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
 // offset, and output layout.  RHT rotates the colwise side's N-row groups
 // (any N); RRHT rotates the rowwise side's blocks along the row (N = 4 or
 // 16, within a block: the Fprop / Dgrad operands, §4.2).
-template <int FMT, int RND, bool RHT, bool CNT, bool RRHT = false>
+template <int FMT, int RND, bool RHT, int CNT, bool RRHT = false>
 __global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(FMT == kMX ? 1 : 3))) void k_quant_dual(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
@@ -457,7 +457,7 @@ __attribute__((amdgpu_waves_per_eu(FMT == kMX ? 1 : 3))) void k_quant_dual(
       uint32_t words[BS / 8];
       // without the RHT both sides quantize the same values: the nonzero
       // inputs are counted here for both; a rotated side counts its own
-      encode_block<BS, RND, CNT, (RHT || RRHT) ? 1 : 2>(
+      encode_block<BS, RND, CNT == 2, (RHT || RRHT) ? 1 : 2>(
           v, s_enc_l, static_cast<uint64_t>(r) * cols + c, seed, offset, words, cnt);
       if (in) {
         uint8_t* dst = codes + r * (cols >> 1) + (c >> 1);
@@ -492,7 +492,7 @@ __attribute__((amdgpu_waves_per_eu(FMT == kMX ? 1 : 3))) void k_quant_dual(
         const uint32_t sc =
             scale_for_block<FMT>(amax_b, s_enc_gt, s_dec_gt, s_enc_l, cnt, scale_up_t);
         uint32_t words[BS / 8];
-        encode_block<BS, RND, CNT, (RHT || RRHT) ? 1 : 0>(
+        encode_block<BS, RND, CNT == 2, (RHT || RRHT) ? 1 : 0>(
             v, s_enc_l, static_cast<uint64_t>(c) * rows + row, seed_t, offset_t, words, cnt);
         uint8_t* dst = codes_t + c * (rows >> 1) + (row >> 1);
         if constexpr (BS == 16) {
@@ -524,7 +524,7 @@ __attribute__((amdgpu_waves_per_eu(FMT == kMX ? 1 : 3))) void k_quant_dual(
 // index r * cols + c, and the codes of W^T are the transposed codes of W,
 // so both orientations hold the same rounded values (the 2D-block FP4
 // page's transposition consistency, kept under SR).
-template <int FMT, int RND, bool CNT>
+template <int FMT, int RND, int CNT>
 __global__ __launch_bounds__(kThreads) void k_quant_2d(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, uint8_t* __restrict__ codes_t,
@@ -567,7 +567,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_2d(
     uint32_t tc5[5] = {0, 0, 0, 0, 0};
     const uint32_t sc = scale_for_block<FMT>(amax_t, s_enc_g, s_dec_g, s_enc_l, tc5, scale_up);
     uint32_t words[2];
-    encode_block<16, RND, CNT>(v, s_enc_l, static_cast<uint64_t>(row) * cols + col, seed, offset,
+    encode_block<16, RND, CNT == 2>(v, s_enc_l, static_cast<uint64_t>(row) * cols + col, seed, offset,
                                words, cnt);
     if (valid) {
       *reinterpret_cast<uint2*>(codes + row * (cols >> 1) + (col >> 1)) =
@@ -810,7 +810,7 @@ hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld
       const int64_t tiles = ((rows + 127) / 128) * ((cols + 63) / 64);
       const int64_t cap = grid_cap(kTileWgPerCu);
       const int grid = static_cast<int>(tiles < cap ? tiles : cap);
-      hipLaunchKernelGGL((k_quant_col<kNV, FP4_RNE, true, false, true>), dim3(grid),
+      hipLaunchKernelGGL((k_quant_col<kNV, FP4_RNE, true, 0, true>), dim3(grid),
                          dim3(kThreads), 0, s, x, rows, cols, ld, nullptr, nullptr, nullptr, 0.0f,
                          nullptr, uint64_t(0), uint64_t(0), r, nullptr, 0, out, 0);
     } else {
@@ -822,7 +822,7 @@ hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld
   return hipGetLastError();
 }
 
-template <int FMT, int RND, bool CNT>
+template <int FMT, int RND, int CNT>
 static void row_launch(const QuantArgs& a, hipStream_t s) {
   constexpr int BS = FMT == kMX ? 32 : 16;
   const uint64_t n = static_cast<uint64_t>(a.rows) * static_cast<uint64_t>(a.cols / BS);
@@ -843,8 +843,9 @@ static void row_launch(const QuantArgs& a, hipStream_t s) {
 
 template <int FMT, int RND>
 static void row_dispatch_cnt(const QuantArgs& a, hipStream_t s) {
-  if (a.counters) row_launch<FMT, RND, true>(a, s);
-  else row_launch<FMT, RND, false>(a, s);
+  if (a.counters && a.count_elems) row_launch<FMT, RND, 2>(a, s);
+  else if (a.counters) row_launch<FMT, RND, 1>(a, s);
+  else row_launch<FMT, RND, 0>(a, s);
 }
 
 template <int FMT>
@@ -860,7 +861,7 @@ hipError_t launch_quant_row(const QuantArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int FMT, int RND, bool RHT, bool CNT>
+template <int FMT, int RND, bool RHT, int CNT>
 static void col_launch(const QuantArgs& a, hipStream_t s) {
   constexpr int BS = FMT == kMX ? 32 : 16;
   const int64_t tiles = ((a.rows + 8 * BS - 1) / (8 * BS)) * ((a.cols + 63) / 64);
@@ -874,8 +875,9 @@ static void col_launch(const QuantArgs& a, hipStream_t s) {
 
 template <int FMT, int RND, bool RHT>
 static void col_dispatch_cnt(const QuantArgs& a, hipStream_t s) {
-  if (a.counters) col_launch<FMT, RND, RHT, true>(a, s);
-  else col_launch<FMT, RND, RHT, false>(a, s);
+  if (a.counters && a.count_elems) col_launch<FMT, RND, RHT, 2>(a, s);
+  else if (a.counters) col_launch<FMT, RND, RHT, 1>(a, s);
+  else col_launch<FMT, RND, RHT, 0>(a, s);
 }
 
 template <int FMT, int RND>
@@ -901,7 +903,7 @@ hipError_t launch_quant_col(const QuantArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int FMT, int RND, bool RHT, bool CNT, bool RRHT>
+template <int FMT, int RND, bool RHT, int CNT, bool RRHT>
 static void dual_launch(const QuantArgs& a, const QuantArgs& b, hipStream_t s) {
   constexpr int BS = FMT == kMX ? 32 : 16;
   const int64_t tiles = ((a.rows + 8 * BS - 1) / (8 * BS)) * ((a.cols + 63) / 64);
@@ -919,13 +921,15 @@ static void dual_dispatch_cnt(const QuantArgs& a, const QuantArgs& b, hipStream_
   // the rowwise side's RHT (a.rht) only with the two-level formats
   if constexpr (FMT != kMX) {
     if (a.rht) {
-      if (a.counters) dual_launch<FMT, RND, RHT, true, true>(a, b, s);
-      else dual_launch<FMT, RND, RHT, false, true>(a, b, s);
+      if (a.counters && a.count_elems) dual_launch<FMT, RND, RHT, 2, true>(a, b, s);
+      else if (a.counters) dual_launch<FMT, RND, RHT, 1, true>(a, b, s);
+      else dual_launch<FMT, RND, RHT, 0, true>(a, b, s);
       return;
     }
   }
-  if (a.counters) dual_launch<FMT, RND, RHT, true, false>(a, b, s);
-  else dual_launch<FMT, RND, RHT, false, false>(a, b, s);
+  if (a.counters && a.count_elems) dual_launch<FMT, RND, RHT, 2, false>(a, b, s);
+  else if (a.counters) dual_launch<FMT, RND, RHT, 1, false>(a, b, s);
+  else dual_launch<FMT, RND, RHT, 0, false>(a, b, s);
 }
 
 template <int FMT, int RND>
@@ -951,7 +955,7 @@ hipError_t launch_quant_dual(const QuantArgs& row, const QuantArgs& col, hipStre
   return hipGetLastError();
 }
 
-template <int FMT, int RND, bool CNT>
+template <int FMT, int RND, int CNT>
 static void q2d_launch(const QuantArgs& a, hipStream_t s) {
   const int64_t regions = ((a.rows + 63) / 64) * ((a.cols + 63) / 64);
   const int64_t cap = grid_cap(kTileWgPerCu);
@@ -964,11 +968,13 @@ static void q2d_launch(const QuantArgs& a, hipStream_t s) {
 template <int FMT>
 static void q2d_dispatch(const QuantArgs& a, hipStream_t s) {
   if (a.round == FP4_SR) {
-    if (a.counters) q2d_launch<FMT, FP4_SR, true>(a, s);
-    else q2d_launch<FMT, FP4_SR, false>(a, s);
+    if (a.counters && a.count_elems) q2d_launch<FMT, FP4_SR, 2>(a, s);
+    else if (a.counters) q2d_launch<FMT, FP4_SR, 1>(a, s);
+    else q2d_launch<FMT, FP4_SR, 0>(a, s);
   } else {
-    if (a.counters) q2d_launch<FMT, FP4_RNE, true>(a, s);
-    else q2d_launch<FMT, FP4_RNE, false>(a, s);
+    if (a.counters && a.count_elems) q2d_launch<FMT, FP4_RNE, 2>(a, s);
+    else if (a.counters) q2d_launch<FMT, FP4_RNE, 1>(a, s);
+    else q2d_launch<FMT, FP4_RNE, 0>(a, s);
   }
 }
 

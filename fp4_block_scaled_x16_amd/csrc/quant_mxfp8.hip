@@ -231,7 +231,7 @@ hipError_t launch_quant_mx8(const QuantArgs& a, bool colwise, hipStream_t s) {
       const int64_t tiles = (a.rows / kBS) * ((a.cols + kColTileCols - 1) / kColTileCols);
       const int64_t cap = grid_cap(kMx8WgPerCu);
       const int grid = static_cast<int>(tiles < cap ? tiles : cap);
-      if (a.counters)
+      if (a.counters && a.count_elems)
         hipLaunchKernelGGL(k_quant_mx8_col<true>, dim3(grid), dim3(kMx8Threads), 0, s, a.x, a.rows,
                            a.cols, a.ld, a.codes, a.scales, a.counters, a.tiled);
       else
@@ -240,7 +240,7 @@ hipError_t launch_quant_mx8(const QuantArgs& a, bool colwise, hipStream_t s) {
     } else {
       const uint64_t n = static_cast<uint64_t>(a.rows) * static_cast<uint64_t>(a.cols / kBS);
       const int grid = grid_for(n, kMx8WgPerCu, kMx8Threads);
-      if (a.counters)
+      if (a.counters && a.count_elems)
         hipLaunchKernelGGL(k_quant_mx8_row<true>, dim3(grid), dim3(kMx8Threads), 0, s, a.x, a.rows,
                            a.cols, a.ld, a.codes, a.scales, a.counters, a.tiled);
       else

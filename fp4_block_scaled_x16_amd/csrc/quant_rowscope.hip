@@ -60,7 +60,7 @@ __device__ __forceinline__ uint32_t block_amax_bits(const uint4 (&q)[2], const R
 
 // Quantize the BPT blocks a lane holds (block j = j0 + stride b of row r;
 // blocks at or beyond bpr are skipped) with the row's global scales.
-template <int FMT, int RND, bool CNT, bool RHT, int BPT>
+template <int FMT, int RND, int CNT, bool RHT, int BPT>
 __device__ __forceinline__ void encode_row_part(const uint4 (&q)[BPT][2], int64_t r, int64_t j0,
                                                 int stride, int64_t bpr, int64_t cols,
                                                 float s_enc_g, float s_dec_g, uint8_t* codes,
@@ -82,7 +82,7 @@ __device__ __forceinline__ void encode_row_part(const uint4 (&q)[BPT][2], int64_
     float s_enc_l;
     const uint32_t sc = scale_for_block<FMT>(amax_b, s_enc_g, s_dec_g, s_enc_l, cnt, scale_up);
     uint32_t words[BS / 8];
-    encode_block<BS, RND, CNT>(v, s_enc_l,
+    encode_block<BS, RND, CNT == 2>(v, s_enc_l,
                                static_cast<uint64_t>(r) * static_cast<uint64_t>(cols) +
                                    static_cast<uint64_t>(j) * BS,
                                seed, offset, words, cnt);
@@ -94,7 +94,7 @@ __device__ __forceinline__ void encode_row_part(const uint4 (&q)[BPT][2], int64_
 }
 
 // Wave per row (bpr <= 64 BPT).  Same arguments as k_quant_row_scoped.
-template <int FMT, int RND, bool CNT, bool RHT, int BPT>
+template <int FMT, int RND, int CNT, bool RHT, int BPT>
 __global__ __launch_bounds__(kRowThreads) void k_quant_row_scoped_wave(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ amax,
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(kRowThreads) void k_quant_row_scoped_wave(
 // Workgroup per row.  BPT: 16-element blocks per thread and sweep.  amax: float[rows], read
 // (amax_given) or written; s_dec_out: float[rows] or null.  The SR index of
 // element (r, c) is r * cols + c, as in the tensor-scope rowwise kernel.
-template <int FMT, int RND, bool CNT, bool RHT, int BPT>
+template <int FMT, int RND, int CNT, bool RHT, int BPT>
 __global__ __launch_bounds__(kRowThreads) void k_quant_row_scoped(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ amax,
@@ -234,7 +234,7 @@ __global__ __launch_bounds__(kRowThreads) void k_quant_row_scoped(
 // kernel's occupancy, queried once per kernel), capped by the rows, so a
 // wave (or workgroup) walks several rows and the wave kernel's next-row
 // loads overlap the current row's encode.
-template <int FMT, int RND, bool CNT, bool RHT, int BPT, bool WAVE>
+template <int FMT, int RND, int CNT, bool RHT, int BPT, bool WAVE>
 void scoped_launch(const fp4lib::QuantArgs& a, const RhtN& r, hipStream_t s) {
   auto kernel = WAVE ? k_quant_row_scoped_wave<FMT, RND, CNT, RHT, BPT>
                      : k_quant_row_scoped<FMT, RND, CNT, RHT, BPT>;
@@ -258,7 +258,7 @@ void scoped_launch(const fp4lib::QuantArgs& a, const RhtN& r, hipStream_t s) {
 // Rows of up to 256 blocks: a wave per row with the fewest of 1, 2, 4
 // blocks per lane that hold it; longer rows: a workgroup per row, 2, 4 or 8
 // blocks per thread (beyond 2048 blocks, in chunks of 2048).
-template <int FMT, int RND, bool CNT, bool RHT>
+template <int FMT, int RND, int CNT, bool RHT>
 void scoped_bpt(const fp4lib::QuantArgs& a, const RhtN& r, hipStream_t s) {
   const int64_t bpr = a.cols / 16;
   if (bpr <= 64) scoped_launch<FMT, RND, CNT, RHT, 1, true>(a, r, s);
@@ -269,7 +269,7 @@ void scoped_bpt(const fp4lib::QuantArgs& a, const RhtN& r, hipStream_t s) {
   else scoped_launch<FMT, RND, CNT, RHT, 8, false>(a, r, s);
 }
 
-template <int FMT, int RND, bool CNT>
+template <int FMT, int RND, int CNT>
 void scoped_rht(const fp4lib::QuantArgs& a, hipStream_t s) {
   const RhtN r = make_rht(a.rht_n, a.rht_signs);
   if (a.rht) scoped_bpt<FMT, RND, CNT, true>(a, r, s);
@@ -279,11 +279,13 @@ void scoped_rht(const fp4lib::QuantArgs& a, hipStream_t s) {
 template <int FMT>
 void scoped_dispatch(const fp4lib::QuantArgs& a, hipStream_t s) {
   if (a.round == FP4_SR) {
-    if (a.counters) scoped_rht<FMT, FP4_SR, true>(a, s);
-    else scoped_rht<FMT, FP4_SR, false>(a, s);
+    if (a.counters && a.count_elems) scoped_rht<FMT, FP4_SR, 2>(a, s);
+    else if (a.counters) scoped_rht<FMT, FP4_SR, 1>(a, s);
+    else scoped_rht<FMT, FP4_SR, 0>(a, s);
   } else {
-    if (a.counters) scoped_rht<FMT, FP4_RNE, true>(a, s);
-    else scoped_rht<FMT, FP4_RNE, false>(a, s);
+    if (a.counters && a.count_elems) scoped_rht<FMT, FP4_RNE, 2>(a, s);
+    else if (a.counters) scoped_rht<FMT, FP4_RNE, 1>(a, s);
+    else scoped_rht<FMT, FP4_RNE, 0>(a, s);
   }
 }
 

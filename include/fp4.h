@@ -113,6 +113,14 @@ typedef enum fp4_orient_e FP4_ENUM_INT { FP4_ROWWISE = 0, FP4_COLWISE = 1 } fp4_
  * whole before it encodes: COLWISE and 2D16 stay TENSOR.) */
 typedef enum fp4_global_scope_e FP4_ENUM_INT { FP4_GLOBAL_TENSOR = 0, FP4_GLOBAL_ROW = 1 } fp4_global_scope;
 
+/* Which events a quantization adds to its fp4_counters (when counters is
+ * not NULL).  ALL: every field.  SCALES: the block-scale events only
+ * (scale_saturated, scale_underflow, scale_subnormal -- what the UE5M3
+ * recipe monitors); the element fields are left unchanged, and the
+ * per-element tests, about a quarter of a quantizer's vector work, are
+ * skipped.  MX formats have no block-scale events. */
+typedef enum fp4_count_level_e FP4_ENUM_INT { FP4_COUNT_ALL = 0, FP4_COUNT_SCALES = 1 } fp4_count_level;
+
 typedef enum fp4_status_e FP4_ENUM_INT {
   FP4_OK = 0,
   FP4_ERR_ARG = 1,          /* null pointer, bad enum, misaligned or bad stride  */
@@ -173,6 +181,8 @@ typedef struct {
   fp4_global_scope global_scope;  /* TENSOR, or ROW (NVFP4/UE5M3, 1D ROWWISE,
                              fp4_quantize only): amax and s_dec are then
                              arrays of `rows` floats                          */
+  fp4_count_level count_level;    /* events counted into `counters` (the
+                             dual quantizer: the same on both sides)         */
 } fp4_quant_desc;
 
 /*

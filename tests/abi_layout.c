@@ -25,6 +25,7 @@ int main(void) {
   F(fp4_quant_desc, rht_signs_hi);
   F(fp4_quant_desc, scale_round);
   F(fp4_quant_desc, global_scope);
+  F(fp4_quant_desc, count_level);
   printf("fp4_operand.__size__ %zu\n", sizeof(fp4_operand));
   F(fp4_operand, format);
   F(fp4_operand, codes);

@@ -97,6 +97,7 @@ def quant(lib, d, rows=32, cols=64, ld=None, x=FAKE, codes=FAKE, scales=FAKE, co
     (dict(format=3, orient=1), 48, 64, 2),           # rows % 32 (colwise)
     (dict(global_scope=1, format=3), 32, 64, 3),     # no per-row scales
     (dict(global_scope=2), 32, 64, 1),               # bad global scope
+    (dict(count_level=2), 32, 64, 1),                # bad counting level
     (dict(global_scope=1, format=2), 32, 64, 3),     # per-row scales: two-level formats
     (dict(global_scope=1, orient=1), 32, 64, 3),     # per-row scales: ROWWISE only
     (dict(global_scope=1, block=1), 32, 64, 3),      # per-row scales: 1D only
@@ -173,6 +174,8 @@ def dual(lib, rd, cd, rows=32, cols=64, x=FAKE, codes=FAKE, scales=FAKE, codes_t
     (dict(), dict(orient=1), 32, 40, 2),                      # cols % 16
     (dict(format=2), dict(orient=1, format=2), 48, 64, 2),    # rows % 32
     (dict(format=3), dict(orient=1, format=3), 64, 64, 3),    # MXFP8: single quantizations
+    (dict(count_level=1), dict(orient=1), 32, 64, 3),         # both sides count the same
+    (dict(), dict(orient=1, count_level=5), 32, 64, 1),
     (dict(global_scope=1), dict(orient=1), 32, 64, 3),        # per-row scales: fp4_quantize
     (dict(), dict(orient=1, global_scope=1), 32, 64, 3),
 ])

@@ -522,3 +522,38 @@ def test_dual_rht_both_sides(n_row, n_col, rnd):
         assert f32_bits(q.s_dec.item()) == f32_bits(r["s_dec"])
     assert api.counters_dict(cnt) == {k: rr["counters"][k] + rc["counters"][k]
                                       for k in rr["counters"]}
+
+
+@pytest.mark.parametrize("kind", ["row", "col", "dual", "2d", "row_scope"])
+@pytest.mark.parametrize("fmt,rnd", [("nvfp4", "rne"), ("ue5m3", "sr")])
+def test_count_scales_only(kind, fmt, rnd):
+    """count="scales": the same codes and scales as counting everything, the
+    block-scale events equal to the oracle's, the element events untouched."""
+    x = inputs.gradients((288, 320), cfg_seed=44)
+    xd = dev(x)
+    kw = dict(rnd=rnd, seed=3)
+    names = ("scale_saturated", "scale_underflow", "scale_subnormal")
+    if kind == "dual":
+        oracle = [Q.quantize(x, fmt, orient="row", **kw),
+                  Q.quantize(x, fmt, orient="col", offset=1, **kw)]
+        run = lambda c, level: api.quantize_dual(xd, fmt, counters=c, count=level, offset=0, **kw)
+    else:
+        okw = dict(block="2d") if kind == "2d" else dict(scope="row") if kind == "row_scope" \
+            else dict(orient=kind)
+        gkw = dict(block="2d", emit_transpose=True) if kind == "2d" else \
+            dict(global_scope="row") if kind == "row_scope" else dict(orient=kind)
+        oracle = [Q.quantize(x, fmt, **okw, **kw)]
+        run = lambda c, level: api.quantize(xd, fmt, counters=c, count=level, **gkw, **kw)
+    c_all, c_sc = api.new_counters(), api.new_counters()
+    c_sc.fill_(7)                          # element fields must stay as they were
+    r_all, r_sc = run(c_all, "all"), run(c_sc, "scales")
+    torch.cuda.synchronize()
+    for a, b in zip(r_all if isinstance(r_all, tuple) else (r_all,),
+                    r_sc if isinstance(r_sc, tuple) else (r_sc,)):
+        assert torch.equal(a.codes, b.codes) and torch.equal(a.scales, b.scales)
+    got = api.counters_dict(c_sc)
+    for k in names:
+        assert got[k] == 7 + sum(o["counters"][k] for o in oracle), k
+    assert got["elem_saturated"] == 7 and got["elem_underflow"] == 7
+    assert api.counters_dict(c_all) == {k: sum(o["counters"][k] for o in oracle)
+                                        for k in api.COUNTER_NAMES}
