@@ -52,8 +52,9 @@ def sr_random16(idx, seed, offset):
 
     Philox4x32-10 with key = (seed low, seed high) and counter =
     (g low, g high, offset low, offset high), g = idx >> 3.  The 128 output
-    bits serve 8 consecutive indices: index j = idx & 7 takes the (j & 1)-th
-    16-bit half of output word j >> 1 (low half first).
+    bits serve 8 consecutive indices: index j = idx & 7 takes a 16-bit half
+    of output word j >> 1, the upper half for even j and the lower half for
+    odd j.
     """
     idx = np.asarray(idx, dtype=np.int64)
     g = (idx >> 3).astype(np.uint64)
@@ -65,5 +66,5 @@ def sr_random16(idx, seed, offset):
     w = np.stack(words, axis=-1)                      # [..., 4] uint32
     j = (idx & 7).astype(np.int64)
     word = np.take_along_axis(w.reshape(-1, 4), (j >> 1).reshape(-1, 1), axis=1).reshape(idx.shape)
-    return ((word >> ((j & 1) * 16).astype(np.uint32)) & 0xFFFF).astype(np.uint16)
+    return ((word >> ((1 - (j & 1)) * 16).astype(np.uint32)) & 0xFFFF).astype(np.uint16)
 

@@ -44,9 +44,12 @@ also listed in the design notes):
   * E2M1 conversion saturates |y| > 6 to 6, also under stochastic rounding.
   * The code's sign bit is the sign bit of y = x * s_enc_L.
   * Stochastic rounding: lo = largest E2M1 magnitude <= |y|, hi = the next
-    one; with 16 random bits r, round up iff r < 65536 * (|y| - lo)/(hi - lo).
-    Random bits come from ``philox.sr_random16`` keyed by the element's
-    index in the OUTPUT layout (r * C + c for the [R, C] code matrix).
+    one, f = (|y| - lo)/(hi - lo) in [0, 1); with 16 random bits r, round up
+    iff r + floor(65536 f) >= 65536, i.e. when the random bits, added to the
+    first 16 bits of the fraction f, carry.  This rounds up with probability
+    floor(65536 f) / 65536, within 2^-16 of f.  Random bits come from
+    ``philox.sr_random16`` keyed by the element's index in the OUTPUT layout
+    (r * C + c for the [R, C] code matrix).
   * Packing: byte j of a code row holds element 2j in its low nibble and
     element 2j + 1 in its high nibble.  Scales are row-major [R, C / BS];
     2D scales are [R / 16, C / 16]; colwise output is the transposed matrix.
@@ -201,7 +204,8 @@ def encode_elements(v, s_enc_l, rnd="rne", r16=None):
         # fp32 arithmetic, exact: (m - lo) by Sterbenz, division by a power of 2
         frac = ((mc.astype(np.float32) - lo_v.astype(np.float32))
                 / (hi_v - lo_v).astype(np.float32)).astype(np.float32)
-        up = r16.astype(np.float64) < frac.astype(np.float64) * 65536.0
+        lead16 = np.floor(frac.astype(np.float64) * 65536.0).astype(np.int64)
+        up = r16.astype(np.int64) + lead16 >= 65536
         mag = np.where(top, 7, lo_c + up.astype(np.int64))
         code = (mag.astype(np.uint8) | (np.signbit(y).astype(np.uint8) << 3))
     else:

@@ -54,7 +54,7 @@ def test_sr_stream_index_mapping(rocrand_ref):
     words = rocrand_ref(rows)
     for i in idx:
         w = int(words[i >> 3][(i & 7) >> 1])
-        assert r16[i] == ((w >> (16 * (i & 1))) & 0xFFFF)
+        assert r16[i] == ((w >> (16 * (1 - (i & 1)))) & 0xFFFF)   # even: upper half
 
 
 def test_sr_stream_uniform_and_seeded():

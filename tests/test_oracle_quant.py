@@ -233,12 +233,49 @@ def test_sr_matches_exact_expectation_and_keeps_grid_values():
     assert np.all((vals[:, keep] == lo[keep]) | (vals[:, keep] == hi[keep]) | (m[keep] == 6))
     # aggregate of (empirical mean - exact expectation) is ~ N(0, se)
     frac = (m - lo) / (hi - lo)
-    p_up = np.ceil(frac * 65536) / 65536
+    p_up = np.floor(frac * 65536) / 65536
     expect = lo + (hi - lo) * p_up
     var = (hi - lo) ** 2 * p_up * (1 - p_up)
     d = (vals[:, keep].mean(axis=0) - expect[keep])
     z = d.sum() / np.sqrt((var[keep] / codes.shape[0]).sum())
     assert abs(z) < 4
+
+
+def test_sr_rule_over_every_random_value():
+    # One element against all 65536 values of its 16 random bits: the draws
+    # that round up must be exactly the r with r + floor(65536 f) >= 65536,
+    # f the position of |y| between its E2M1 neighbours (found by search on
+    # the value set, NVFP4 paper §3), so that P(up) = floor(65536 f) / 65536;
+    # when 65536 f is an integer the mean over all r is |y| exactly (§4.4:
+    # unbiased).  Cases: each interval of the value set, fractions on and
+    # just off a multiple of 2^-16, tiny fractions, the top of [4, 6), 6 and
+    # beyond, and negative values.
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    ys = []
+    for lo, hi in zip(grid[:-1], grid[1:]):
+        for f in (0.0, 0.5, 0.25, 0.2, 1 / 3, 12345 / 65536, (12345 + 2 ** -6) / 65536,
+                  (12345 - 2 ** -6) / 65536, 2 ** -17, 2 ** -20, 1 - 2 ** -16, 1 - 2 ** -20):
+            ys.append(np.float32(lo + f * (hi - lo)))
+    ys += [np.float32(6.0), np.float32(7.5), np.float32(1e30)]
+    ys += [-y for y in ys[:40]]
+    r = np.arange(65536, dtype=np.uint16)
+    for y in ys:
+        v = np.full(65536, y, np.float32)
+        codes, _, _ = Q.encode_elements(v, np.float32(1.0), "sr", r)
+        assert np.all((codes >> 3) == (1 if np.signbit(y) else 0))
+        vals = np.abs(F.e2m1_value(codes))
+        m = abs(float(y))
+        if m >= 6:
+            assert np.all(vals == 6.0)
+            continue
+        k = np.searchsorted(grid, m, side="right") - 1
+        lo, hi = grid[k], grid[k + 1]
+        lead = int(np.floor((m - lo) / (hi - lo) * 65536))
+        up = vals == hi
+        assert np.all(up | (vals == lo))
+        assert np.array_equal(up, r.astype(np.int64) >= 65536 - lead), y
+        if ((m - lo) / (hi - lo) * 65536).is_integer():
+            assert vals.mean() == m
 
 
 def test_sr_keeps_on_grid_values():
