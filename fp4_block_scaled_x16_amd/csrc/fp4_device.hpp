@@ -175,32 +175,6 @@ __device__ __forceinline__ uint32_t nonzero_codes(uint32_t word) {
   return __builtin_popcount(((word & 0x77777777u) + 0x77777777u) & 0x88888888u);
 }
 
-// Stochastic E2M1 rounding (§4.4): lo = largest magnitude <= |y|, hi the
-// next; round up iff r16 < 65536 (|y| - lo) / (hi - lo), computed exactly
-// as (|y| - lo) * (65536 / (hi - lo)).  |y| >= 6 gives 6.
-__device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t r16) {
-  const uint32_t yb = __float_as_uint(y);
-  const uint32_t sign = (yb >> 28) & 8u;
-  const uint32_t b = yb & 0x7FFFFFFFu;
-  const float m = __uint_as_float(b);
-  uint32_t lo;
-  float lo_v, inv_gap;
-  if (m < 1.0f) {
-    lo = m >= 0.5f ? 1u : 0u;
-    lo_v = m >= 0.5f ? 0.5f : 0.0f;
-    inv_gap = 131072.0f;                             // 65536 / 0.5
-  } else {
-    lo = (b >> 22) - 252u;                          // truncation to one mantissa bit
-    lo_v = __uint_as_float(b & 0xFFC00000u);
-    const uint32_t E = b >> 23;                     // 127, 128 or 129 here
-    inv_gap = __uint_as_float((271u - E) << 23);    // 65536 / 2^(E - 128)
-  }
-  const float frac_s = (m - lo_v) * inv_gap;        // exact
-  uint32_t mag = lo + static_cast<uint32_t>(static_cast<float>(r16) < frac_s);
-  mag = m < 6.0f ? mag : 7u;
-  return sign | mag;
-}
-
 // -------------------------------------------------------------- Philox --
 // Philox4x32-10 (Salmon et al., SC'11): ten rounds of two 32x32->64
 // multiplies, key advanced by the Weyl constants between rounds.
@@ -209,6 +183,12 @@ struct U4 {
 };
 
 __device__ __forceinline__ U4 philox4x32_10(U4 c, uint32_t k0, uint32_t k1) {
+  // The key is uniform: left visible, the compiler hoists all ten round keys
+  // out of the kernels' loops and, short of scalar registers, parks them in
+  // vector-register lanes, paying a v_readlane (and its hazard wait) per key
+  // per round.  An empty asm makes the key opaque here, so the round keys are
+  // recomputed with scalar adds, which issue beside the vector work.
+  asm volatile("" : "+s"(k0), "+s"(k1));
 #pragma unroll
   for (int i = 0; i < 10; ++i) {
     if (i) {
@@ -231,9 +211,42 @@ __device__ __forceinline__ U4 sr_words(uint64_t g, uint64_t seed, uint64_t offse
                        static_cast<uint32_t>(seed), static_cast<uint32_t>(seed >> 32));
 }
 
-__device__ __forceinline__ uint32_t sr_bits(const U4& w, int j) {   // j = index & 7
-  const uint32_t word = (j >> 1) == 0 ? w.x : (j >> 1) == 1 ? w.y : (j >> 1) == 2 ? w.z : w.w;
-  return (j & 1) ? (word >> 16) : (word & 0xFFFFu);
+
+// Stochastic E2M1 rounding (§4.4) of y[0..7] into one code word (element i
+// in nibble i).  Element i takes 16 random bits u from word i >> 1 of w: the
+// upper half for even i, the lower half for odd i.  With lo the largest E2M1
+// magnitude <= |y|, hi the next and f = (|y| - lo) / (hi - lo), the code
+// rounds up iff u + floor(65536 f) >= 65536; |y| >= 6 gives 6 and the sign
+// bit copies y's.
+//
+// gfx950's stochastic packed FP4 convert takes two values and a 32-bit
+// random operand R; it adds bits 10..31 of R (first value) or bits 9..30
+// (second value) to the first 22 bits of f and rounds up on a carry.  With
+// u in the top 16 of those 22 bits and zeros below, the carry is exactly
+// the rule above.  Each pair goes through the convert twice, once with the
+// even element's bits placed for the first value (its code: the low nibble
+// of byte 0) and once with the odd element's bits placed for the second
+// value (the high nibble).  Only byte 0 of each result is used: the
+// instruction keeps the destination's other bytes, which the builtin does
+// not model.  A bitfield insert per pair and three byte permutes assemble
+// the word.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t e2m1_sr8(const float (&y)[8], const U4& w) {
+  const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+  uint32_t b[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const f32x2 p = {y[2 * k], y[2 * k + 1]};
+    const uint32_t ev = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p, wd[k] & 0xFFFF0000u, 1.0f, 0);
+    const uint32_t od = __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, p, wd[k] << 15, 1.0f, 0);
+    b[k] = (ev & 0x0Fu) | (od & 0xF0u);
+  }
+  // v_perm_b32: bytes 0-3 select from the second operand, 4-7 from the
+  // first, 0x0C gives a zero byte
+  const uint32_t b01 = __builtin_amdgcn_perm(b[1], b[0], 0x0C0C0400u);
+  const uint32_t b23 = __builtin_amdgcn_perm(b[3], b[2], 0x0C0C0400u);
+  return __builtin_amdgcn_perm(b23, b01, 0x05040100u);
 }
 
 // ----------------------------------------------------------------- RHT --

@@ -81,9 +81,7 @@ __device__ __forceinline__ void encode_block(const float* v, float s_enc_l, uint
     for (int i = 0; i < 8; ++i) y[i] = v[q * 8 + i] * s_enc_l;
     uint32_t word = 0;
     if constexpr (RND == FP4_SR) {
-      const U4 rw = sr_words((idx0 >> 3) + q, seed, offset);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) word |= e2m1_sr(y[i], sr_bits(rw, i)) << (4 * i);
+      word = e2m1_sr8(y, sr_words((idx0 >> 3) + q, seed, offset));
     } else {
       word = e2m1_rne_pair<0>(word, y[0], y[1]);
       word = e2m1_rne_pair<1>(word, y[2], y[3]);

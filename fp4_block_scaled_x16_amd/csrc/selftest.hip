@@ -6,6 +6,9 @@
 //   k_sweep_e2m1   fp32 -> E2M1 RNE through gfx950's packed FP4 convert, two
 //                  values per call into byte SEL of a word, as the quantizer
 //                  packs 8 codes (NVFP4 paper §3, App. B.3 Eq. 4)
+//   k_sweep_e2m1_sr  fp32 -> E2M1 by stochastic rounding (§4.4) through the
+//                  quantizers' 8-value helper, with the random bits on either
+//                  side of each input's carry threshold
 //   k_sweep_scale  fp32 -> E4M3 / UE5M3 block-scale codes (App. B.2 Eq. 3)
 //   k_gemm_decode  E2M1 x block scale -> fp16, the GEMM operand decode
 //                  (App. B.3)
@@ -98,6 +101,69 @@ __global__ __launch_bounds__(kSweepThreads) void k_sweep_e2m1(const uint32_t* __
   flush_sweep(bad, checked, first, res);
 }
 
+// Every non-NaN fp32 pattern through the stochastic-rounding helper the
+// quantizers call (e2m1_sr8).  thr holds the E2M1 magnitudes 0.5 .. 6 as fp32
+// patterns: an input of magnitude m lies in [lo, hi) with lo = thr[k-1] (0
+// for k = 0) and hi = thr[k], k = #(m >= thr); from the first 16 bits L of
+// f = (m - lo) / (hi - lo) (fp32 arithmetic, exact here: Sterbenz, then a
+// power of two) the random value 65535 - L must round down and 65536 - L
+// up.  Each group of 8 patterns is converted four times: both random values,
+// with the patterns in order and rotated by one place, so every pattern sits
+// once at an even and once at an odd position (the two take their random
+// bits from different halves of a word).  |y| >= 6 must give 6 for both.
+__global__ __launch_bounds__(kSweepThreads) void k_sweep_e2m1_sr(const uint32_t* __restrict__ thr,
+                                                                 unsigned long long* __restrict__ res) {
+  float t[7];
+#pragma unroll
+  for (int i = 0; i < 7; ++i) t[i] = __uint_as_float(thr[i]);
+  constexpr uint64_t kGroups = uint64_t(1) << 29;
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kSweepThreads;
+  uint64_t bad = 0, checked = 0, first = ~uint64_t(0);
+  for (uint64_t g = static_cast<uint64_t>(blockIdx.x) * kSweepThreads + threadIdx.x; g < kGroups;
+       g += stride) {
+    const uint32_t b0 = static_cast<uint32_t>(g << 3);
+#pragma unroll 1
+    for (int pass = 0; pass < 4; ++pass) {
+      const int rot = pass >> 1, up_side = pass & 1;
+      float y[8];
+      uint32_t pat[8], want[8], u[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pat[i] = b0 + static_cast<uint32_t>((i + rot) & 7);
+        y[i] = __uint_as_float(pat[i]);
+        const float m = __uint_as_float(pat[i] & 0x7FFFFFFFu);
+        uint32_t k = 0;
+#pragma unroll
+        for (int j = 0; j < 7; ++j) k += m >= t[j] ? 1u : 0u;
+        uint32_t mag = 7u;
+        u[i] = up_side ? 65535u : 0u;
+        if (k < 7u) {
+          const float lo = k ? t[k > 0 ? k - 1 : 0] : 0.0f;
+          const float hi = t[k];
+          const uint32_t lead = static_cast<uint32_t>((m - lo) / (hi - lo) * 65536.0f);
+          // lead = 0: no random value rounds up; test 65535 on both sides
+          u[i] = (up_side && lead) ? 65536u - lead : 65535u - (lead ? lead : 0u);
+          mag = k + ((u[i] + lead >= 65536u) ? 1u : 0u);
+        }
+        want[i] = ((pat[i] >> 28) & 8u) | mag;
+      }
+      const fp4dev::U4 w{(u[0] << 16) | u[1], (u[2] << 16) | u[3], (u[4] << 16) | u[5],
+                         (u[6] << 16) | u[7]};
+      const uint32_t word = fp4dev::e2m1_sr8(y, w);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if ((pat[i] & 0x7FFFFFFFu) > 0x7F800000u) continue;   // NaN: outside the contract
+        ++checked;
+        if (((word >> (4 * i)) & 0xFu) != want[i]) {
+          ++bad;
+          first = pat[i] < first ? pat[i] : first;
+        }
+      }
+    }
+  }
+  flush_sweep(bad, checked, first, res);
+}
+
 // Every finite fp32 t >= 0 through the block-scale encoder; the expected
 // code is the number of thresholds <= t (binary search over 256 entries,
 // padded with patterns above every input).
@@ -182,6 +248,8 @@ hipError_t launch_selftest_sweep(int kind, const uint32_t* thresholds, int n, ui
   const int grid = device_cu_count() * kSweepWgPerCu;
   if (kind == FP4_SWEEP_E2M1_RNE)
     hipLaunchKernelGGL(k_sweep_e2m1, dim3(grid), dim3(kSweepThreads), 0, s, thresholds, res);
+  else if (kind == FP4_SWEEP_E2M1_SR)
+    hipLaunchKernelGGL(k_sweep_e2m1_sr, dim3(grid), dim3(kSweepThreads), 0, s, thresholds, res);
   else if (kind == FP4_SWEEP_E4M3_SCALE)
     hipLaunchKernelGGL(k_sweep_scale<7>, dim3(grid), dim3(kSweepThreads), 0, s, thresholds, n, res);
   else

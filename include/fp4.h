@@ -228,8 +228,12 @@ fp4_status fp4_amax(const fp4_quant_desc* desc /* host */, const uint16_t* x, in
  *   multiple of BS; 2D16 needs rows and cols multiples of 16; RHT needs 1D
  *   blocks and the blocked axis a multiple of its size N (rht_n).
  *   SR random bits: element index i in the output code matrix ([R_out,
- *   C_out], i = r * C_out + c) takes 16 bits of Philox4x32-10(key = seed,
- *   counter = (i >> 3, offset)), half (i & 1) of output word (i & 7) >> 1.
+ *   C_out], i = r * C_out + c) takes 16 bits u of Philox4x32-10(key = seed,
+ *   counter = (i >> 3, offset)): output word (i & 7) >> 1, its upper half
+ *   for even i, its lower half for odd i.  With lo <= |y| < hi the
+ *   neighbouring E2M1 magnitudes and f = (|y| - lo) / (hi - lo), the code
+ *   rounds up iff u + floor(65536 f) >= 65536 (the random bits, added to
+ *   the first 16 bits of f, carry); |y| >= 6 gives 6.
  */
 fp4_status fp4_quantize(const fp4_quant_desc* desc /* host */,
                         const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,

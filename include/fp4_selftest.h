@@ -34,7 +34,8 @@ extern "C" {
 typedef enum fp4_sweep_kind_e FP4_ENUM_INT {
   FP4_SWEEP_E2M1_RNE = 0,     /* every fp32 pattern except NaNs (2^32 - 2^24 + 2)   */
   FP4_SWEEP_E4M3_SCALE = 1,   /* every finite fp32 t >= 0 (patterns 0 .. 0x7F7FFFFF) */
-  FP4_SWEEP_UE5M3_SCALE = 2   /* likewise                                            */
+  FP4_SWEEP_UE5M3_SCALE = 2,  /* likewise                                            */
+  FP4_SWEEP_E2M1_SR = 3       /* every fp32 pattern except NaNs, four draws each     */
 } fp4_sweep_kind;
 
 /*
@@ -49,6 +50,13 @@ typedef enum fp4_sweep_kind_e FP4_ENUM_INT {
  *   result      device uint64[3], overwritten: [0] inputs whose code differs,
  *               [1] the smallest differing input pattern (all ones if none),
  *               [2] inputs checked.
+ * FP4_SWEEP_E2M1_SR checks stochastic rounding (NVFP4 paper §4.4, the rule
+ * in fp4.h under fp4_quantize) through the quantizers' 8-value helper: the
+ * 7 thresholds are the E2M1 magnitudes 0.5, 1, ..., 6 (the smallest
+ * magnitude whose round-down code is i + 1); each input is converted at an
+ * even and at an odd element position with the random value just below and
+ * at its carry threshold (16 random bits u round up iff u + floor(65536 f)
+ * >= 65536), so every input counts four times in [2].
  */
 fp4_status fp4_selftest_sweep(int kind, const uint32_t* thresholds, int n,
                               uint64_t* result, void* stream);

@@ -288,6 +288,16 @@ def test_geometry_control_rejects(lib):
     assert lib.fp4_selftest_set_geometry(0, 0) == 0
 
 
+def test_selftest_sweep_rejects(lib):
+    # validation happens on the host before any device work
+    assert lib.fp4_selftest_sweep(4, FAKE, 7, FAKE, None) == 1
+    assert lib.fp4_selftest_sweep(-1, FAKE, 7, FAKE, None) == 1
+    assert lib.fp4_selftest_sweep(3, FAKE, 6, FAKE, None) == 1      # E2M1 SR takes 7
+    assert "7 thresholds" in _err(lib)
+    assert lib.fp4_selftest_sweep(3, None, 7, FAKE, None) == 1
+    assert lib.fp4_selftest_sweep(3, FAKE, 7, None, None) == 1
+
+
 def test_status_strings(lib):
     assert lib.fp4_status_string(0) == b"ok"
     assert lib.fp4_status_string(3) == b"unsupported combination"

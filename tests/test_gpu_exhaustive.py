@@ -9,6 +9,12 @@ elements; the UE5M3 abstract for the unsigned E5M3 scale).
   byte 0..3 of a word); the expected code is the oracle's rule, evaluated on
   the device as a table of the 7 boundaries between codes, found here by
   bisecting the oracle's encoder over fp32 patterns.
+* fp32 -> E2M1 by stochastic rounding (§4.4): every fp32 pattern except
+  NaNs through the quantizers' 8-value helper, at an even and an odd
+  position, with the 16 random bits just below and at the input's carry
+  threshold, against the oracle's rule (round up iff u + floor(65536 f) >=
+  65536, f the position between the E2M1 neighbours, which are found by
+  bisecting the oracle's round-down code).
 * fp32 -> E4M3 / UE5M3 block-scale code: every finite t >= 0 through the
   quantizer's scale encoder, against the 126 / 255 boundaries of the
   oracle's encoders.
@@ -57,6 +63,18 @@ def test_e2m1_rne_convert_exhaustive():
     assert np.array_equal(_as_f32(thr), want)
     bad, first, checked = api.selftest_sweep("e2m1_rne", thr)
     assert checked == 2 ** 32 - (2 ** 24 - 2)
+    assert bad == 0, "%d mismatches, first at 0x%08x" % (bad, first)
+
+
+def test_e2m1_sr_exhaustive():
+    # the round-down code steps at the E2M1 magnitudes themselves (§3)
+    thr = _boundaries(lambda b: F.e2m1_floor_code(np.abs(_as_f32(b))), 8, 0x7F800000)
+    assert np.array_equal(_as_f32(thr), np.array([0.5, 1, 1.5, 2, 3, 4, 6], np.float32))
+    # every input, at an even and an odd element position, with the random
+    # value just below and at its carry threshold (the rule of the oracle's
+    # stochastic rounding: u + floor(65536 f) >= 65536)
+    bad, first, checked = api.selftest_sweep("e2m1_sr", thr)
+    assert checked == 4 * (2 ** 32 - (2 ** 24 - 2))
     assert bad == 0, "%d mismatches, first at 0x%08x" % (bad, first)
 
 
