@@ -14,7 +14,7 @@ already resident in HBM.  A step runs:
 quantizes each orientation with its own read.)  Event counters are kept on
 every quantization.  The step is captured once as a HIP graph and replayed
 (after a bitwise check of replays against the eager step).  Per-kernel
-durations come from graphs that run each op after a 512 MiB write (which
+durations come from graphs that run each op after a 512 MiB read (which
 evicts the 256 MB Infinity Cache), minus the same graph without the op,
 timed with events on the launch stream.  Printed: one JSON line whose
 `value` is the step's GEMM throughput (3 x 2MNK / step time, TFLOP/s),
@@ -41,7 +41,7 @@ PEAK_TFLOPS = {"fp16": 2500.0, "fp4": 10100.0}   # dense MFMA, MI355X
 # rocprofv3 counter summaries of the dominant (GEMM) kernel, per workload
 PROFILE_TRAFFIC = {2: os.path.join(ROOT, "profiles", "traffic_gemm_nvfp4_1.2b_ffn.txt"),
                    4: os.path.join(ROOT, "profiles", "traffic_gemm_ue5m3_8b_ffn.txt")}
-FLUSH_BYTES = 512 << 20     # written before each timed op: more than the 256 MB Infinity Cache
+FLUSH_BYTES = 512 << 20     # read before each timed op: more than the 256 MB Infinity Cache
 
 # algorithmic bytes per element
 B_AMAX = 2.0
@@ -671,7 +671,7 @@ def format_comparison(dev):
     return out
 
 
-def row_scope_parts(fmt, host, graph_ms, flush_buf, R=10):
+def row_scope_parts(fmt, host, graph_ms, flush, R=10):
     """The per-row global scale (NVFP4 paper App. B.1, closing remark) on the
     rowwise operands of Fprop and Dgrad, cache-flushed like `parts`: for X,
     W (RNE) and dY (SR), the tensor-scope route -- an amax pass, then the
@@ -683,18 +683,19 @@ def row_scope_parts(fmt, host, graph_ms, flush_buf, R=10):
     from fp4_block_scaled_x16_amd import api
 
     dev_t, tg = host["device"], host["targets"]
-    cnt = api.new_counters(flush_buf.device)
-    buf = torch.empty(1, dtype=torch.float32, device=flush_buf.device)
+    dev = host["fprop_out"].device
+    cnt = api.new_counters(dev)
+    buf = torch.empty(1, dtype=torch.float32, device=dev)
 
     def cold_ms(f):
         def body():
             for _ in range(R):
-                flush_buf.fill_(1.0)
+                flush()
                 f()
 
         def flush_only():
             for _ in range(R):
-                flush_buf.fill_(1.0)
+                flush()
         return max(graph_ms(body) - graph_ms(flush_only), 0.0) / R
 
     res = {}
@@ -839,11 +840,20 @@ def main():
     counters = api.counters_dict(cnt)
 
     # Per-kernel durations, timed with events on the stream the kernels run
-    # on: a graph of R x (512 MiB write, op) minus a graph of R x (512 MiB
-    # write), so every op starts with the Infinity Cache holding none of its
-    # inputs; and (`parts_warm`) a graph of R back-to-back launches.
+    # on: a graph of R x (512 MiB read, op) minus a graph of R x (512 MiB
+    # read), so every op starts with the Infinity Cache holding none of its
+    # inputs and no dirty lines of other work (a write flush would leave
+    # 256 MB of them for the op to write back); the op's own output lines
+    # are written back under the next flush, which the difference charges
+    # to the op.  `parts_warm`: a graph of R back-to-back launches.
     R = 10
     flush_buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    flush_buf.fill_(1.0)
+    flush_bits = flush_buf.view(torch.int16).view(16384, -1)
+    flush_out = torch.empty(1, dtype=torch.float32, device=dev)
+
+    def flush():
+        api.amax(flush_bits, out=flush_out)     # reads the 512 MiB buffer
 
     def graph_ms(body, reps=3):
         g = torch.cuda.CUDAGraph()
@@ -862,13 +872,13 @@ def main():
 
     def flushes():
         for _ in range(R):
-            flush_buf.fill_(1.0)
+            flush()
 
     op_ms, op_ms_warm = [], []
     for (_, _, _, f) in ops:
         def cold():
             for _ in range(R):
-                flush_buf.fill_(1.0)
+                flush()
                 f()
 
         def warm():
@@ -895,7 +905,7 @@ def main():
     parts, parts_warm = rates(op_ms), rates(op_ms_warm)
     row_scope = None
     if fmt != "mxfp4":
-        row_scope = row_scope_parts(fmt, host, graph_ms, flush_buf)
+        row_scope = row_scope_parts(fmt, host, graph_ms, flush)
     q_bytes = sum(u for (_, k, u, _) in ops if k == "hbm")
     q_ms = sum(parts[n]["ms"] for (n, k, u, _) in ops if k == "hbm" and u > 0)
     g_flops = sum(u for (_, k, u, _) in ops if k == "mfma")
@@ -945,7 +955,7 @@ def main():
     }
     if row_scope is not None:
         out["row_scope"] = row_scope
-    del flush_buf
+    del flush_buf, flush_bits
     if cfg == 5:
         out["format_comparison"] = format_comparison(dev)
     if pool is not None:

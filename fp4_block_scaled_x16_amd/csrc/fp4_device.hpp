@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "exact_div.hpp"
+
 namespace fp4dev {
 
 constexpr float kFltMax = 3.40282346638528859812e+38f;
@@ -78,34 +80,49 @@ struct ScaleEvents {
   uint32_t sat, under, sub;
 };
 
+// Local encode scale of a block-scale code (Eq. 3's reciprocal):
+// 1 / (s_hat * s_dec_G), clamped to FLT_MAX; 0 for the zero code.
+template <int FMT>
+__device__ __forceinline__ float enc_scale_of_code(uint32_t code, float s_dec_g) {
+  const float s_hat = FMT == kNV ? scale_m3_decode<7>(code) : scale_m3_decode<15>(code);
+  const float p = s_hat * s_dec_g;
+  const float inv = fminf(1.0f / p, kFltMax);
+  return code ? inv : 0.0f;
+}
+
 // Two-level block scale (Eqs. 2-3) -> scale code; s_enc_l receives the
-// local encode scale (0 for a zero code, reciprocal clamped to FLT_MAX).
+// local encode scale (0 for a zero code, reciprocal clamped to FLT_MAX),
+// read from `enc_tab` (enc_scale_of_code of every code for this s_dec_G)
+// when the caller holds one, else computed.
 template <int FMT>
 // up: round the scale up instead of to nearest (truncation-free scaling,
 // 2D-block FP4 page): the nearest code, moved one code up when its value is
 // below t (the codes of both formats are ascending in value).
 __device__ __forceinline__ uint32_t block_scale_two_level(float amax_b, float s_enc_g,
                                                           float s_dec_g, float& s_enc_l,
-                                                          ScaleEvents& ev, bool up = false) {
-  const float s_dec_l = amax_b / 6.0f;
+                                                          ScaleEvents& ev, bool up = false,
+                                                          const float* enc_tab = nullptr) {
+  // amax_B / 6 rounded as fp32 division rounds it; the multiply-and-correct
+  // form holds on [2^-125, FLT_MAX] (every input checked on the host), a
+  // branch divides below it and for inf / NaN (blocks that small are rare)
+  float s_dec_l;
+  if (amax_b >= fp4exact::kDiv6Lo && amax_b <= fp4exact::kDiv6Hi) [[likely]]
+    s_dec_l = fp4exact::div6_normal(amax_b);
+  else
+    s_dec_l = amax_b / 6.0f;
   float t = s_dec_l * s_enc_g;
   if (!(t <= kFltMax)) t = kFltMax;
   uint32_t code;
-  float s_hat;
   if constexpr (FMT == kNV) {
     ev.sat += (t > 448.0f);
     code = scale_m3_encode<7>(t, 448.0f, 0x7Eu);
-    s_hat = scale_m3_decode<7>(code);
-    if (up && code < 0x7Eu && s_hat < t) s_hat = scale_m3_decode<7>(++code);
+    if (up && code < 0x7Eu && scale_m3_decode<7>(code) < t) ++code;
   } else {
     ev.sat += (t > 122880.0f);
     code = scale_m3_encode<15>(t, 122880.0f, 0xFFu);
-    s_hat = scale_m3_decode<15>(code);
-    if (up && code < 0xFFu && s_hat < t) s_hat = scale_m3_decode<15>(++code);
+    if (up && code < 0xFFu && scale_m3_decode<15>(code) < t) ++code;
   }
-  const float p = s_hat * s_dec_g;
-  const float inv = fminf(1.0f / p, kFltMax);
-  s_enc_l = code ? inv : 0.0f;
+  s_enc_l = enc_tab ? enc_tab[code] : enc_scale_of_code<FMT>(code, s_dec_g);
   ev.under += (amax_b > 0.0f) & (code == 0u);
   ev.sub += (code >= 1u) & (code <= 7u);
   return code;

@@ -174,6 +174,9 @@ __global__ __launch_bounds__(kStream) void k_quant_row(
   float s_enc_g = 1.0f, s_dec_g = 1.0f;
   if constexpr (FMT != kMX) global_scales(*amax, target, s_enc_g, s_dec_g);
   if (s_dec_out && blockIdx.x == 0 && threadIdx.x == 0) *s_dec_out = s_dec_g;
+  __shared__ float enc_tab[FMT == kMX ? 1 : 256];
+  fill_enc_table<FMT, kStream>(enc_tab, s_dec_g);
+  if constexpr (FMT != kMX) __syncthreads();
 
   const uint64_t bpr = static_cast<uint64_t>(cols) / BS;
   const uint64_t n = static_cast<uint64_t>(rows) * bpr;
@@ -213,7 +216,8 @@ __global__ __launch_bounds__(kStream) void k_quant_row(
 #pragma unroll
     for (int k = 0; k < BS; ++k) amax_b = fmaxf(amax_b, fabsf(v[k]));
     float s_enc_l;
-    const uint32_t sc = scale_for_block<FMT>(amax_b, s_enc_g, s_dec_g, s_enc_l, cnt, scale_up);
+    const uint32_t sc =
+        scale_for_block<FMT>(amax_b, s_enc_g, s_dec_g, s_enc_l, cnt, scale_up, enc_tab);
     uint32_t words[BS / 8];
     encode_block<BS, RND, CNT == 2>(v, s_enc_l, r_cur * static_cast<uint64_t>(cols) + j_cur * BS, seed,
                                offset, words, cnt);
@@ -283,6 +287,9 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
   float s_enc_g = 1.0f, s_dec_g = 1.0f;
   if constexpr (FMT != kMX && !AMX) global_scales(*amax, target, s_enc_g, s_dec_g);
   if (s_dec_out && blockIdx.x == 0 && threadIdx.x == 0) *s_dec_out = s_dec_g;
+  // read after the first tile's barrier
+  __shared__ float enc_tab[FMT == kMX || AMX ? 1 : 256];
+  if constexpr (!AMX) fill_enc_table<FMT, kThreads>(enc_tab, s_dec_g);
 
   // tile counts fit in 32 bits (the host keeps rows, cols below 2^31)
   const uint32_t tiles_c = static_cast<uint32_t>((cols + TC - 1) / TC);
@@ -331,7 +338,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_col(
           continue;
         }
         float s_enc_l;
-        const uint32_t sc = scale_for_block<FMT>(amax_b, s_enc_g, s_dec_g, s_enc_l, cnt, scale_up);
+        const uint32_t sc =
+            scale_for_block<FMT>(amax_b, s_enc_g, s_dec_g, s_enc_l, cnt, scale_up, enc_tab);
         uint32_t words[BS / 8];
         encode_block<BS, RND, CNT == 2>(v, s_enc_l, static_cast<uint64_t>(c) * rows + row, seed,
                                    offset, words, cnt);
@@ -394,6 +402,10 @@ __attribute__((amdgpu_waves_per_eu(FMT == kMX ? 1 : 3))) void k_quant_dual(
     if (s_dec_out) *s_dec_out = s_dec_g;
     if (s_dec_t_out) *s_dec_t_out = s_dec_gt;
   }
+  __shared__ float enc_tab[2][FMT == kMX ? 1 : 256];   // rowwise, colwise side
+  fill_enc_table<FMT, kThreads>(enc_tab[0], s_dec_g);
+  fill_enc_table<FMT, kThreads>(enc_tab[1], s_dec_gt);
+  if constexpr (FMT != kMX) __syncthreads();
 
   // tile counts fit in 32 bits (the host keeps rows, cols below 2^31)
   const uint32_t tiles_c = static_cast<uint32_t>((cols + TC - 1) / TC);
@@ -448,7 +460,7 @@ __attribute__((amdgpu_waves_per_eu(FMT == kMX ? 1 : 3))) void k_quant_dual(
       const bool in = r < rows && c < cols;
       uint32_t sc_cnt[5] = {0, 0, 0, 0, 0};
       const uint32_t sc =
-          scale_for_block<FMT>(amax_b, s_enc_g, s_dec_g, s_enc_l, sc_cnt, scale_up);
+          scale_for_block<FMT>(amax_b, s_enc_g, s_dec_g, s_enc_l, sc_cnt, scale_up, enc_tab[0]);
       if (in) {
         cnt[0] += sc_cnt[0];
         cnt[1] += sc_cnt[1];
@@ -490,7 +502,7 @@ __attribute__((amdgpu_waves_per_eu(FMT == kMX ? 1 : 3))) void k_quant_dual(
         for (int k = 0; k < BS; ++k) amax_b = fmaxf(amax_b, fabsf(v[k]));
         float s_enc_l;
         const uint32_t sc =
-            scale_for_block<FMT>(amax_b, s_enc_gt, s_dec_gt, s_enc_l, cnt, scale_up_t);
+            scale_for_block<FMT>(amax_b, s_enc_gt, s_dec_gt, s_enc_l, cnt, scale_up_t, enc_tab[1]);
         uint32_t words[BS / 8];
         encode_block<BS, RND, CNT == 2, (RHT || RRHT) ? 1 : 0>(
             v, s_enc_l, static_cast<uint64_t>(c) * rows + row, seed_t, offset_t, words, cnt);
@@ -542,20 +554,34 @@ __global__ __launch_bounds__(kThreads) void k_quant_2d(
   const int t = threadIdx.x;
   const int lr = t >> 2, tcol = t & 3;
   uint32_t cnt[5] = {0, 0, 0, 0, 0};
+  // this thread's 16 elements of region `reg` (zeros outside W or past the
+  // last region: whole 16x16 tiles are in or out)
+  auto load = [&](uint32_t reg, uint4 (&q)[2]) {
+    const uint32_t rr = reg / reg_c, rc = reg - rr * reg_c;
+    const int64_t row = static_cast<int64_t>(rr) * 64 + lr;
+    const int64_t col = static_cast<int64_t>(rc) * 64 + tcol * 16;
+    if (reg < nreg && row < rows && col < cols) {
+      const uint4* src = reinterpret_cast<const uint4*>(x + row * ld + col);
+      q[0] = src[0];
+      q[1] = src[1];
+    } else {
+      q[0] = make_uint4(0, 0, 0, 0);
+      q[1] = make_uint4(0, 0, 0, 0);
+    }
+  };
+  uint4 q[2];
+  load(blockIdx.x, q);
   for (uint32_t reg = blockIdx.x; reg < nreg; reg += gridDim.x) {
     const uint32_t rr = reg / reg_c, rc = reg - rr * reg_c;
     const int64_t r0 = static_cast<int64_t>(rr) * 64, c0 = static_cast<int64_t>(rc) * 64;
     const int64_t row = r0 + lr, col = c0 + tcol * 16;
-    const bool valid = row < rows && col < cols;   // whole 16x16 tiles are in or out
+    const bool valid = row < rows && col < cols;
+    // the next region's loads are in flight while this one is encoded
+    uint4 nq[2];
+    load(reg + gridDim.x, nq);
     float v[16];
-    if (valid) {
-      const uint4* src = reinterpret_cast<const uint4*>(x + row * ld + col);
-      unpack8(src[0], v);
-      unpack8(src[1], v + 8);
-    } else {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) v[k] = 0.0f;
-    }
+    unpack8(q[0], v);
+    unpack8(q[1], v + 8);
     float am = 0.0f;
 #pragma unroll
     for (int k = 0; k < 16; ++k) am = fmaxf(am, fabsf(v[k]));
@@ -565,6 +591,9 @@ __global__ __launch_bounds__(kThreads) void k_quant_2d(
     const float amax_t = __uint_as_float(amb);
     float s_enc_l;
     uint32_t tc5[5] = {0, 0, 0, 0, 0};
+    // the reciprocal is computed here, not read from a per-code table: with
+    // one block per thread the table read's latency sits on the path to
+    // the transposing barrier (measured slower)
     const uint32_t sc = scale_for_block<FMT>(amax_t, s_enc_g, s_dec_g, s_enc_l, tc5, scale_up);
     uint32_t words[2];
     encode_block<16, RND, CNT == 2>(v, s_enc_l, static_cast<uint64_t>(row) * cols + col, seed, offset,
@@ -601,6 +630,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_2d(
       }
       __syncthreads();
     }
+    q[0] = nq[0];
+    q[1] = nq[1];
   }
   if constexpr (CNT) flush_counters<kThreads>(cnt, counters);
 }

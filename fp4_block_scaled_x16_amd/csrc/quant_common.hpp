@@ -103,16 +103,29 @@ __device__ __forceinline__ void encode_block(const float* v, float s_enc_l, uint
 template <int FMT>
 __device__ __forceinline__ uint32_t scale_for_block(float amax_b, float s_enc_g, float s_dec_g,
                                                     float& s_enc_l, uint32_t (&cnt)[5],
-                                                    bool up) {
+                                                    bool up, const float* enc_tab = nullptr) {
   if constexpr (FMT == kMX) {
     return block_scale_mx(amax_b, s_enc_l);
   } else {
     ScaleEvents ev{0, 0, 0};
-    const uint32_t sc = block_scale_two_level<FMT>(amax_b, s_enc_g, s_dec_g, s_enc_l, ev, up);
+    const uint32_t sc =
+        block_scale_two_level<FMT>(amax_b, s_enc_g, s_dec_g, s_enc_l, ev, up, enc_tab);
     cnt[0] += ev.sat;
     cnt[1] += ev.under;
     cnt[2] += ev.sub;
     return sc;
+  }
+}
+
+// The local encode scale of every block-scale code for one tensor scale,
+// computed once per workgroup into LDS (thread c, c + NT, ...: code c);
+// the caller synchronizes the workgroup before the first lookup.  Each
+// block then reads its s_enc_L instead of dividing (the same value:
+// enc_scale_of_code is block_scale_two_level's own arithmetic).
+template <int FMT, int NT>
+__device__ __forceinline__ void fill_enc_table(float* tab, float s_dec_g) {
+  if constexpr (FMT != kMX) {
+    for (int c = threadIdx.x; c < 256; c += NT) tab[c] = enc_scale_of_code<FMT>(c, s_dec_g);
   }
 }
 
