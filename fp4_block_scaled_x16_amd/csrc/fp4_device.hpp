@@ -216,7 +216,9 @@ __device__ __forceinline__ U4 philox4x32_10(U4 c, uint32_t k0, uint32_t k1) {
     const uint64_t p1 = static_cast<uint64_t>(0xCD9E8D57u) * c.z;
     const uint32_t hi0 = static_cast<uint32_t>(p0 >> 32), lo0 = static_cast<uint32_t>(p0);
     const uint32_t hi1 = static_cast<uint32_t>(p1 >> 32), lo1 = static_cast<uint32_t>(p1);
-    c = U4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+    // three-way xors as one gfx950 bitop3 each (0x96: the parity table)
+    c = U4{static_cast<uint32_t>(__builtin_amdgcn_bitop3_b32(hi1, c.y, k0, 0x96)), lo1,
+           static_cast<uint32_t>(__builtin_amdgcn_bitop3_b32(hi0, c.w, k1, 0x96)), lo0};
   }
   return c;
 }
