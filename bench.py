@@ -590,29 +590,48 @@ OP_TIMING_LAUNCHES = 40     # per op and graph: R = 10 launches, replayed 1 + 3 
 
 def summarize_trace(path):
     """Average duration of each library kernel over all its launches, and
-    over its last 2 x OP_TIMING_LAUNCHES launches: those of the per-op timing
-    graphs (each kernel alone on the GPU; first after a cache-evicting write,
-    `parts`, then back to back, `parts_warm`), as opposed to the step
-    replays, where independent kernels run side by side."""
+    over the per-op timing graphs (each kernel alone on the GPU): the first
+    OP_TIMING_LAUNCHES launches of the kernel after the first cache flush
+    (torch's row-wise max over the 512 MiB buffer), each after a flush
+    (`parts`), and the next OP_TIMING_LAUNCHES, back to back (`parts_warm`);
+    as opposed to the step replays before them, where independent kernels
+    run side by side.  A kernel that several ops launch (k_amax in a
+    current-amax step) reports the graphs of the first of them; kernels the
+    step does not launch (the per-row-scale comparison's, the stale amaxes'
+    setup) get no per-op columns."""
     import csv
     import collections
     by = collections.defaultdict(list)
+    flush_t = []
     with open(path) as f:
         for r in csv.DictReader(f):
+            t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+            if "reduce_kernel" in r["Kernel_Name"] and "MaxNanFunctor" in r["Kernel_Name"]:
+                flush_t.append(t0)
+                continue
             n = r["Kernel_Name"].replace("void ", "").replace("fp4gemm::", "")
             n = n.replace("(anonymous namespace)::", "").split("(")[0]
             if n.startswith(("k_gemm", "k_quant", "k_amax")):
-                t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
                 by[n].append((t0, (t1 - t0) / 1e3))
+    if not flush_t:
+        raise SystemExit("no cache-flush launches in %s" % path)
+    first_flush = min(flush_t)
     L = OP_TIMING_LAUNCHES
     print("| kernel | calls | avg us, all | avg us, alone after a cache flush | avg us, alone back to back |")
     print("|---|---:|---:|---:|---:|")
     for n, v in by.items():
-        d = [x[1] for x in sorted(v)]
-        cold, warm = d[-2 * L:-L], d[-L:]
-        print("| %s | %d | %.1f | %.1f | %.1f |" % (n, len(d), sum(d) / len(d),
-                                                   sum(cold) / max(len(cold), 1),
-                                                   sum(warm) / max(len(warm), 1)))
+        v = sorted(v)
+        d = [x[1] for x in v]
+        after = [x[1] for x in v if x[0] >= first_flush]
+        # the step ran it: an eager warmup, two checked replays and the timed
+        # ones, so at least 4 launches before the flushes (the three amax
+        # launches that set up stale amaxes do not count)
+        if len(d) - len(after) >= 4 and len(after) >= 2 * L:
+            cold, warm = after[:L], after[L:2 * L]
+            cols = "%.1f | %.1f" % (sum(cold) / L, sum(warm) / L)
+        else:
+            cols = "- | -"
+        print("| %s | %d | %.1f | %s |" % (n, len(d), sum(d) / len(d), cols))
 
 
 def format_comparison(dev):
@@ -849,11 +868,13 @@ def main():
     R = 10
     flush_buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
     flush_buf.fill_(1.0)
-    flush_bits = flush_buf.view(torch.int16).view(16384, -1)
-    flush_out = torch.empty(1, dtype=torch.float32, device=dev)
+    flush_rows = flush_buf.view(-1, 4096)
+    flush_out = torch.empty(flush_rows.shape[0], dtype=torch.float32, device=dev)
 
     def flush():
-        api.amax(flush_bits, out=flush_out)     # reads the 512 MiB buffer
+        # reads the 512 MiB buffer (a row-wise max: one small output, and a
+        # kernel of torch's own, so kernel traces tell it from the library's)
+        torch.amax(flush_rows, dim=1, out=flush_out)
 
     def graph_ms(body, reps=3):
         g = torch.cuda.CUDAGraph()
@@ -903,9 +924,12 @@ def main():
             out[name] = p
         return out
     parts, parts_warm = rates(op_ms), rates(op_ms_warm)
+    # side measurements after the per-op graphs, whose launches come first
+    # after the step's (what --summarize-trace reads)
     row_scope = None
     if fmt != "mxfp4":
         row_scope = row_scope_parts(fmt, host, graph_ms, flush)
+    fmt_cmp = format_comparison(dev) if cfg == 5 else None
     q_bytes = sum(u for (_, k, u, _) in ops if k == "hbm")
     q_ms = sum(parts[n]["ms"] for (n, k, u, _) in ops if k == "hbm" and u > 0)
     g_flops = sum(u for (_, k, u, _) in ops if k == "mfma")
@@ -955,9 +979,9 @@ def main():
     }
     if row_scope is not None:
         out["row_scope"] = row_scope
-    del flush_buf, flush_bits
-    if cfg == 5:
-        out["format_comparison"] = format_comparison(dev)
+    del flush_buf, flush_rows, flush_out
+    if fmt_cmp is not None:
+        out["format_comparison"] = fmt_cmp
     if pool is not None:
         out["cpu_baseline"] = cpu_baseline(cfg, host, fmt, args.cpu_tokens, pool)
         pool.close()
