@@ -164,6 +164,60 @@ def test_scale_underflow_block(fmt):
     assert c["scale_underflow"] > 0
 
 
+def _tiny_tiles(rows, cols, seed=5):
+    """bf16 bits of a tensor of tiny values whose 16x16 tiles have the block
+    amaxes in TINY_AMAX (each reached on the tile's diagonal, so every 1x16
+    and 16x1 block of a tile has that amax), the tensor amax 2^-110."""
+    rng = np.random.default_rng(seed)
+    x = np.zeros((rows, cols), np.float32)
+    k = 0
+    for r0 in range(0, rows, 16):
+        for c0 in range(0, cols, 16):
+            a = TINY_AMAX[k % len(TINY_AMAX)]
+            k += 1
+            t = (a * rng.uniform(-1, 1, (16, 16))).astype(np.float32)
+            t[np.arange(16), np.arange(16)] = a * rng.choice([-1.0, 1.0], 16)
+            x[r0:r0 + 16, c0:c0 + 16] = t
+    return _bits(x)
+
+
+# Block amaxes around 2^-125, where the quantizers' amax_B / 6 switches
+# from the multiply-and-correct form to a division, down to the smallest
+# bf16 subnormal and zero; 2^-110 sets a tensor scale that brings them into
+# the scale formats' normal and subnormal ranges.
+TINY_AMAX = [2.0 ** -110, 2.0 ** -120, 2.0 ** -125 * 1.0078125, 2.0 ** -125,
+             2.0 ** -125 * 0.99609375, 2.0 ** -126, 2.0 ** -129, 2.0 ** -133, 0.0]
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "ue5m3"])
+@pytest.mark.parametrize("rnd", ["rne", "sr"])
+@pytest.mark.parametrize("kind", ["row", "col", "2d", "dual"])
+def test_tiny_block_amaxes(kind, fmt, rnd):
+    xb = _tiny_tiles(128, 96)
+    assert np.abs(F.bf16_bits_to_f32(xb)).max() == np.float32(2.0 ** -110)
+    if kind == "dual":
+        cnt = api.new_counters()
+        qr, qc = api.quantize_dual(dev(xb), fmt, rnd=rnd, seed=3, offset=0, offset_t=1,
+                                   counters=cnt)
+        torch.cuda.synchronize()
+        rr = Q.quantize(xb, fmt, orient="row", rnd=rnd, seed=3, offset=0)
+        rc = Q.quantize(xb, fmt, orient="col", rnd=rnd, seed=3, offset=1)
+        for q, r in ((qr, rr), (qc, rc)):
+            assert np.array_equal(q.codes.cpu().numpy(), r["codes"]), "codes differ"
+            assert np.array_equal(gpu_scales(q), r["scales"]), "scales differ"
+            assert f32_bits(q.s_dec.item()) == f32_bits(r["s_dec"]), "s_dec differs"
+        assert api.counters_dict(cnt) == {k: rr["counters"][k] + rc["counters"][k]
+                                          for k in rr["counters"]}
+        return
+    block, orient = ("2d", "row") if kind == "2d" else ("1d", kind)
+    q, r, c = run_both(xb, fmt, block=block, orient=orient, rnd=rnd,
+                       emit_transpose=kind == "2d")
+    assert_same(q, r, c)
+    # the mix reaches the subnormal scale codes, and (E4M3) the underflow to
+    # code 0
+    assert c["scale_subnormal"] > 0 and (fmt != "nvfp4" or c["scale_underflow"] > 0)
+
+
 def test_hand_example():
     b0 = [6, -0.5, 1, 1.5, 2, 3, 4, -6, 0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5]
     x = _bits([b0 + [10.5] + [1.75] * 15])
