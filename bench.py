@@ -747,6 +747,55 @@ def row_scope_parts(fmt, host, graph_ms, flush, R=10):
     return res
 
 
+def other_kernels(fmt, host, graph_ms, flush, R=10):
+    """The hot path's kernels that the step does not launch, cold like
+    `parts`, against HBM with their algorithmic bytes per element: the
+    dequantization of X's rowwise codes to bf16 (2.5625 B) and fp32
+    (4.5625 B; NVFP4 paper App. B.3), the RHT alone on X along tokens, 16-
+    and 64-point (bf16 in, fp32 out: 6 B; §4.2), and MXFP8 quantization of
+    an X-sized input rowwise and colwise (3.03125 B; 2D-block FP4 page, the
+    Q/K projections).  Two-level workloads dequantize their own format; the
+    MXFP4 workload dequantizes NVFP4 codes of X."""
+    import torch
+    from fp4_block_scaled_x16_amd import api, inputs
+
+    X = host["device"]["X"]
+    dev = X.device
+    n = X.numel()
+    signs = inputs.rht_sign_mask()
+    qx = api.quantize(X, fmt if fmt != "mxfp4" else "nvfp4")
+    out_bf = torch.empty(X.shape, dtype=torch.bfloat16, device=dev)
+    out_f = torch.empty(X.shape, dtype=torch.float32, device=dev)
+    work = [("dequantize X to bf16", 2.5625, lambda: api.dequantize(qx, torch.bfloat16, out=out_bf)),
+            ("dequantize X to fp32", 4.5625, lambda: api.dequantize(qx, torch.float32, out=out_f)),
+            ("rht X 16-point", 6.0, lambda: api.rht16(X, signs, out=out_f)),
+            ("rht X 64-point", 6.0, lambda: api.rht16(X, signs, rht_n=64, out=out_f)),
+            ("mxfp8 X rowwise", 3.03125, lambda: api.quantize(X, "mxfp8")),
+            ("mxfp8 X colwise", 3.03125, lambda: api.quantize(X, "mxfp8", orient="col"))]
+
+    def flush_only():
+        for _ in range(R):
+            flush()
+    t_flush = graph_ms(flush_only)
+    res = {}
+    for name, bpe, f in work:
+        def body():
+            for _ in range(R):
+                flush()
+                f()
+
+        def warm():
+            for _ in range(R):
+                f()
+        ms = max(graph_ms(body) - t_flush, 0.0) / R
+        gbs = bpe * n / (ms * 1e-3) / 1e9
+        res[name] = {"ms": round(ms, 4), "GBps": round(gbs, 1),
+                     "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                     "ms_warm": round(graph_ms(warm) / R, 4)}
+    res["elements"] = n
+    return res
+
+
 def main():
     args = parse()
     if args.summarize_trace:
@@ -930,6 +979,7 @@ def main():
     if fmt != "mxfp4":
         row_scope = row_scope_parts(fmt, host, graph_ms, flush)
     fmt_cmp = format_comparison(dev) if cfg == 5 else None
+    others = other_kernels(fmt, host, graph_ms, flush)
     q_bytes = sum(u for (_, k, u, _) in ops if k == "hbm")
     q_ms = sum(parts[n]["ms"] for (n, k, u, _) in ops if k == "hbm" and u > 0)
     g_flops = sum(u for (_, k, u, _) in ops if k == "mfma")
@@ -980,6 +1030,7 @@ def main():
     if row_scope is not None:
         out["row_scope"] = row_scope
     del flush_buf, flush_rows, flush_out
+    out["other_kernels"] = others
     if fmt_cmp is not None:
         out["format_comparison"] = fmt_cmp
     if pool is not None:

@@ -324,8 +324,15 @@ def counters_dict(c):
 
 
 # ------------------------------------------------------------ dequantize --
-def dequantize(q: Quantized, out_dtype=torch.float32):
-    out = torch.empty((q.rows, q.cols), dtype=out_dtype, device=q.codes.device)
+def dequantize(q: Quantized, out_dtype=torch.float32, out=None):
+    """Values of a quantized matrix as fp32 or bf16 [rows, cols] (into `out`,
+    a contiguous tensor of that shape and dtype, when given)."""
+    if out is None:
+        out = torch.empty((q.rows, q.cols), dtype=out_dtype, device=q.codes.device)
+    elif (out.dtype != out_dtype or tuple(out.shape) != (q.rows, q.cols)
+          or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous %s tensor of shape (%d, %d)"
+                         % (out_dtype, q.rows, q.cols))
     lib = load_library()
     _check(lib.fp4_dequantize(q.fmt, q.block, q.scale_layout, _ptr(q.codes), _ptr(q.scales),
                               _ptr(q.s_dec), q.scope,
@@ -335,10 +342,16 @@ def dequantize(q: Quantized, out_dtype=torch.float32):
 
 
 # ------------------------------------------------------------------- RHT --
-def rht16(x, signs, rht_n=16, orient="col"):
-    """The RHT alone (fp32 [R, C]) along the blocked axis of `orient`."""
+def rht16(x, signs, rht_n=16, orient="col", out=None):
+    """The RHT alone (fp32 [R, C]) along the blocked axis of `orient` (into
+    `out`, a contiguous fp32 tensor of x's shape, when given)."""
     x = _as_bf16_bits(x)
-    y = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    if out is None:
+        y = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    elif out.dtype != torch.float32 or out.shape != x.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous fp32 tensor of the input's shape")
+    else:
+        y = out
     desc = _rht_desc(orient, True, signs, rht_n)
     lib = load_library()
     _check(lib.fp4_rht16(ctypes.byref(desc), _ptr(x), x.shape[0], x.shape[1], x.stride(0),

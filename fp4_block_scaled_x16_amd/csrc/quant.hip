@@ -637,8 +637,22 @@ __global__ __launch_bounds__(kThreads) void k_quant_2d(
 }
 
 // ---------------------------------------------------------- dequantize --
-// One thread per block of BS codes of a [rows, cols] code matrix.
-// sd_rows: s_dec holds one decode scale per row (per-row global scale).
+// One thread per block of BS codes of a [rows, cols] code matrix, kDqUnroll
+// blocks (one grid stride apart, so every wave access stays contiguous)
+// loaded before any is decoded.  sd_rows: s_dec holds one decode scale per
+// row (per-row global scale).  E2M1 codes are decoded by gfx950's packed
+// FP4 -> fp32 convert with a unit scale (exact: every E2M1 value is an fp32
+// value; the sign bit gives -0 for code 8), then v = (e * s_hat) * s_dec.
+constexpr int kDqUnroll = 4;
+
+// The two E2M1 values of byte B of w, exact in fp32 (low nibble first).
+template <int B>
+__device__ __forceinline__ void e2m1_byte_f32(uint32_t w, float s_hat, float sd, float* v) {
+  const auto e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, B);
+  v[2 * B] = (e[0] * s_hat) * sd;
+  v[2 * B + 1] = (e[1] * s_hat) * sd;
+}
+
 template <int FMT, bool B2D, bool F32>
 __global__ __launch_bounds__(kStream) void k_dequant(const uint8_t* __restrict__ codes,
                                                       const uint8_t* __restrict__ scales,
@@ -650,60 +664,68 @@ __global__ __launch_bounds__(kStream) void k_dequant(const uint8_t* __restrict__
   const uint64_t bpr = static_cast<uint64_t>(cols) / BS;
   const uint64_t n = static_cast<uint64_t>(rows) * bpr;
   const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kStream;
-  for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kStream + threadIdx.x; i < n;
-       i += stride) {
-    const uint64_t r = i / bpr, j = i - r * bpr;
-    const float sd = (FMT != kMX && sd_rows) ? s_dec[r] : sd_tensor;
-    const uint32_t sc = B2D     ? scales[(r >> 4) * bpr + j]
-                        : tiled ? scales[tiled_scale_offset(r, j, (bpr + 7) >> 3)]
-                                : scales[i];
-    float s_hat;
-    if constexpr (FMT == kNV) s_hat = scale_m3_decode<7>(sc);
-    else if constexpr (FMT == kUE) s_hat = scale_m3_decode<15>(sc);
-    else s_hat = ue8m0_decode(sc);
-    uint32_t words[BS / 8];
-    const uint8_t* src = codes + i * (BS / 2);
-    if constexpr (BS == 16) {
-      const uint2 q = *reinterpret_cast<const uint2*>(src);
-      words[0] = q.x;
-      words[1] = q.y;
-    } else {
-      const uint4 q = *reinterpret_cast<const uint4*>(src);
-      words[0] = q.x;
-      words[1] = q.y;
-      words[2] = q.z;
-      words[3] = q.w;
-    }
-    float v[BS];
+  for (uint64_t i0 = static_cast<uint64_t>(blockIdx.x) * kStream + threadIdx.x; i0 < n;
+       i0 += kDqUnroll * stride) {
+    uint32_t words[kDqUnroll][BS / 8];
+    uint32_t sc[kDqUnroll];
+    float sd[kDqUnroll];
 #pragma unroll
-    for (int k = 0; k < BS; ++k) {
-      const uint32_t c = (words[k >> 3] >> (4 * (k & 7))) & 0xFu;
-      const uint32_t m = c & 7u;
-      // E2M1 magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6
-      const float mag = m < 4u ? 0.5f * static_cast<float>(m)
-                               : static_cast<float>((m & 1u) ? 3u << ((m - 4u) >> 1)
-                                                             : 2u << ((m - 4u) >> 1));
-      const float e = (c & 8u) ? -mag : mag;
-      v[k] = (e * s_hat) * sd;
-    }
-    if constexpr (F32) {
-      float4* dst = reinterpret_cast<float4*>(static_cast<float*>(out) + i * BS);
-#pragma unroll
-      for (int k = 0; k < BS / 4; ++k)
-        dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
-    } else {
-      uint32_t h[BS / 2];
-#pragma unroll
-      for (int k = 0; k < BS / 2; ++k) {
-        uint32_t lo = __float_as_uint(v[2 * k]), hi = __float_as_uint(v[2 * k + 1]);
-        lo = (lo + 0x7FFFu + ((lo >> 16) & 1u)) >> 16;
-        hi = (hi + 0x7FFFu + ((hi >> 16) & 1u)) >> 16;
-        h[k] = (lo & 0xFFFFu) | (hi << 16);
+    for (int u = 0; u < kDqUnroll; ++u) {
+      const uint64_t i = i0 + u * stride;
+      if (i >= n) continue;
+      const uint64_t r = i / bpr, j = i - r * bpr;
+      sd[u] = (FMT != kMX && sd_rows) ? s_dec[r] : sd_tensor;
+      sc[u] = B2D     ? scales[(r >> 4) * bpr + j]
+              : tiled ? scales[tiled_scale_offset(r, j, (bpr + 7) >> 3)]
+                      : scales[i];
+      const uint8_t* src = codes + i * (BS / 2);
+      if constexpr (BS == 16) {
+        const uint2 q = *reinterpret_cast<const uint2*>(src);
+        words[u][0] = q.x;
+        words[u][1] = q.y;
+      } else {
+        const uint4 q = *reinterpret_cast<const uint4*>(src);
+        words[u][0] = q.x;
+        words[u][1] = q.y;
+        words[u][2] = q.z;
+        words[u][3] = q.w;
       }
-      uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + i * BS);
+    }
 #pragma unroll
-      for (int k = 0; k < BS / 8; ++k)
-        dst[k] = make_uint4(h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]);
+    for (int u = 0; u < kDqUnroll; ++u) {
+      const uint64_t i = i0 + u * stride;
+      if (i >= n) continue;
+      float s_hat;
+      if constexpr (FMT == kNV) s_hat = scale_m3_decode<7>(sc[u]);
+      else if constexpr (FMT == kUE) s_hat = scale_m3_decode<15>(sc[u]);
+      else s_hat = ue8m0_decode(sc[u]);
+      float v[BS];
+#pragma unroll
+      for (int w = 0; w < BS / 8; ++w) {
+        e2m1_byte_f32<0>(words[u][w], s_hat, sd[u], v + 8 * w);
+        e2m1_byte_f32<1>(words[u][w], s_hat, sd[u], v + 8 * w);
+        e2m1_byte_f32<2>(words[u][w], s_hat, sd[u], v + 8 * w);
+        e2m1_byte_f32<3>(words[u][w], s_hat, sd[u], v + 8 * w);
+      }
+      if constexpr (F32) {
+        float4* dst = reinterpret_cast<float4*>(static_cast<float*>(out) + i * BS);
+#pragma unroll
+        for (int k = 0; k < BS / 4; ++k)
+          dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+      } else {
+        uint32_t h[BS / 2];
+#pragma unroll
+        for (int k = 0; k < BS / 2; ++k) {
+          uint32_t lo = __float_as_uint(v[2 * k]), hi = __float_as_uint(v[2 * k + 1]);
+          lo = (lo + 0x7FFFu + ((lo >> 16) & 1u)) >> 16;
+          hi = (hi + 0x7FFFu + ((hi >> 16) & 1u)) >> 16;
+          h[k] = (lo & 0xFFFFu) | (hi << 16);
+        }
+        uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + i * BS);
+#pragma unroll
+        for (int k = 0; k < BS / 8; ++k)
+          dst[k] = make_uint4(h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]);
+      }
     }
   }
 }
@@ -736,51 +758,108 @@ __global__ __launch_bounds__(kStream) void k_rht16(const uint16_t* __restrict__ 
 }
 
 // ------------------------------------------------ RHT of size N, alone --
-// fl32(1/sqrt(N)) D_r H_N on every N-element group along the rows of x
-// (ROW: N consecutive columns of a row) or along its columns (COL: N
-// consecutive rows of a column), as the quantizers apply it.  One thread
-// per 16-element segment; the N / 16 segments of a group are consecutive
-// segments of one line, on consecutive lanes (segment s on lane s mod 64:
-// the grid stride is a multiple of 64), combined by rht_n's shuffles.
-// AMX: the largest |value| goes to *amax_out (fp32 bits, atomic max), else
-// the values are written to y ([rows, cols] fp32, row-major).
-template <bool ROW, bool AMX>
-__global__ __launch_bounds__(kStream) void k_rht_gen(const uint16_t* __restrict__ x, int64_t rows,
-                                                     int64_t cols, int64_t ld, RhtN rht,
-                                                     float* __restrict__ y,
-                                                     uint32_t* __restrict__ amax_out) {
-  const uint64_t seg_per_line = static_cast<uint64_t>(ROW ? cols : rows) >> 4;
-  const uint64_t nseg = seg_per_line * static_cast<uint64_t>(ROW ? rows : cols);
+// fl32(1/sqrt(N)) D_r H_N on every N-element group along the rows of x (N
+// consecutive columns of a row), as the rowwise quantizers apply it.  One
+// thread per 16-element segment; the N / 16 segments of a group are
+// consecutive segments of one row, on consecutive lanes (segment s on lane
+// s mod 64: the grid stride is a multiple of 64), combined by rht_n's
+// shuffles.  AMX: the largest |value| goes to *amax_out (fp32 bits, atomic
+// max), else the values are written to y ([rows, cols] fp32, row-major).
+template <bool AMX>
+__global__ __launch_bounds__(kStream) void k_rht_rows(const uint16_t* __restrict__ x, int64_t rows,
+                                                      int64_t cols, int64_t ld, RhtN rht,
+                                                      float* __restrict__ y,
+                                                      uint32_t* __restrict__ amax_out) {
+  const uint64_t seg_per_line = static_cast<uint64_t>(cols) >> 4;
+  const uint64_t nseg = seg_per_line * static_cast<uint64_t>(rows);
   const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kStream;
   float m = 0.0f;
   for (uint64_t sg = static_cast<uint64_t>(blockIdx.x) * kStream + threadIdx.x; sg < nseg;
        sg += stride) {
     const uint64_t line = sg / seg_per_line, j = sg - line * seg_per_line;
     float v[16];
-    if constexpr (ROW) {
-      const uint4* src = reinterpret_cast<const uint4*>(x + line * ld + 16 * j);
-      unpack8(src[0], v);
-      unpack8(src[1], v + 8);
-    } else {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) v[k] = bf16_to_f32(x[(16 * j + k) * ld + line]);
-    }
+    const uint4* src = reinterpret_cast<const uint4*>(x + line * ld + 16 * j);
+    unpack8(src[0], v);
+    unpack8(src[1], v + 8);
     rht_n(v, rht, static_cast<int>(threadIdx.x & 7));
     if constexpr (AMX) {
 #pragma unroll
       for (int k = 0; k < 16; ++k) m = fmaxf(m, fabsf(v[k]));
-    } else if constexpr (ROW) {
+    } else {
       float4* dst = reinterpret_cast<float4*>(y + line * static_cast<uint64_t>(cols) + 16 * j);
 #pragma unroll
       for (int k = 0; k < 4; ++k) dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
-    } else {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) y[(16 * j + k) * static_cast<uint64_t>(cols) + line] = v[k];
     }
   }
   if constexpr (AMX) flush_max<kStream>(__float_as_uint(m), amax_out);
 }
 
+// The RHT alone along the columns (N-row groups of each column, any N up
+// to 128), written as fp32 [rows, cols].  The colwise quantizer's staging:
+// a 128 x 64 tile of X goes into LDS with coalesced 16-byte row loads, each
+// thread rotates one column pair of one 16-row segment (rht_n combines the
+// N / 16 segments of a group across the lanes that hold them), and the
+// rotated tile goes back through LDS so that every store writes whole rows.
+// The row count is a multiple of N, and N divides the 128-row tile, so a
+// group lies wholly inside or wholly outside the tensor.
+__global__ __launch_bounds__(kThreads) void k_rht_col_tiled(const uint16_t* __restrict__ x,
+                                                            int64_t rows, int64_t cols, int64_t ld,
+                                                            RhtN rht, float* __restrict__ y) {
+  constexpr int TR = 128, TC = 64;
+  __shared__ uint4 tile[kTileChunks<16>];
+  __shared__ float out_t[TR][TC + 1];
+  const uint32_t tiles_c = static_cast<uint32_t>((cols + TC - 1) / TC);
+  const uint32_t tiles_r = static_cast<uint32_t>((rows + TR - 1) / TR);
+  const uint32_t ntiles = tiles_c * tiles_r;
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int grp = lane & 7;                  // 16-row segment of the tile
+  const int pair = wave * 8 + (lane >> 3);   // column pair (0..31)
+  for (uint32_t tile_id = blockIdx.x; tile_id < ntiles; tile_id += gridDim.x) {
+    const uint32_t tr = tile_id / tiles_c, tc = tile_id - tr * tiles_c;
+    const int64_t r0 = static_cast<int64_t>(tr) * TR, c0 = static_cast<int64_t>(tc) * TC;
+#pragma unroll
+    for (int k = 0; k < TR * 8 / kThreads; ++k) {
+      const int chunk = t + k * kThreads;
+      const int lr = chunk >> 3, lc = (chunk & 7) * 8;
+      uint4 q = make_uint4(0, 0, 0, 0);
+      if (r0 + lr < rows && c0 + lc < cols)
+        q = *reinterpret_cast<const uint4*>(x + (r0 + lr) * ld + c0 + lc);
+      tile[tile_chunk<16>(lr, chunk & 7)] = q;
+    }
+    __syncthreads();
+    if (c0 + 2 * pair < cols && r0 + grp * 16 < rows) {
+#pragma unroll 1
+      for (int h = 0; h < 2; ++h) {
+        float v[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const uint32_t w = tile_word<16>(tile, grp * 16 + k, pair);
+          v[k] = bf16_to_f32(h ? (w >> 16) : (w & 0xFFFFu));
+        }
+        rht_n(v, rht, grp);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) out_t[grp * 16 + k][2 * pair + h] = v[k];
+      }
+    }
+    __syncthreads();
+    // two threads per tile row, 32 consecutive columns each
+    const int orow = t >> 1, ocol = (t & 1) * 32;
+    const int64_t gr = r0 + orow;
+    if (gr < rows) {
+      float* dst = y + gr * cols + c0 + ocol;
+      if (c0 + ocol + 32 <= cols && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          reinterpret_cast<float4*>(dst)[q] =
+              make_float4(out_t[orow][ocol + 4 * q], out_t[orow][ocol + 4 * q + 1],
+                          out_t[orow][ocol + 4 * q + 2], out_t[orow][ocol + 4 * q + 3]);
+      } else {
+        for (int q = 0; q < 32 && c0 + ocol + q < cols; ++q) dst[q] = out_t[orow][ocol + q];
+      }
+    }
+  }
+}
 
 }  // namespace
 
@@ -830,7 +909,7 @@ hipError_t launch_amax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld
     if (rht && along_rows) {
       // rotation along the rows (rowwise quantization): the generic kernel
       const uint64_t n = static_cast<uint64_t>(rows) * static_cast<uint64_t>(cols / 16);
-      hipLaunchKernelGGL((k_rht_gen<true, true>), dim3(grid_for(n, kAmaxWgPerCu)), dim3(kStream),
+      hipLaunchKernelGGL((k_rht_rows<true>), dim3(grid_for(n, kAmaxWgPerCu)), dim3(kStream),
                          0, s, x, rows, cols, ld, r, nullptr, out);
     } else if (rht && r.n == 16) {
       const uint64_t n = static_cast<uint64_t>(rows / 16) * static_cast<uint64_t>(cols / 2);
@@ -1059,12 +1138,16 @@ hipError_t launch_rht(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
     } else {
       const uint64_t n = static_cast<uint64_t>(along_rows ? rows : cols) *
                          static_cast<uint64_t>((along_rows ? cols : rows) / 16);
-      if (along_rows)
-        hipLaunchKernelGGL((k_rht_gen<true, false>), dim3(grid_for(n, 2)), dim3(kStream), 0, s, x,
+      if (along_rows) {
+        hipLaunchKernelGGL((k_rht_rows<false>), dim3(grid_for(n, 2)), dim3(kStream), 0, s, x,
                            rows, cols, ld, r, y, nullptr);
-      else
-        hipLaunchKernelGGL((k_rht_gen<false, false>), dim3(grid_for(n, 2)), dim3(kStream), 0, s,
-                           x, rows, cols, ld, r, y, nullptr);
+      } else {
+        const int64_t tiles = ((rows + 127) / 128) * ((cols + 63) / 64);
+        const int64_t cap = grid_cap(kTileWgPerCu);
+        const int grid = static_cast<int>(tiles < cap ? tiles : cap);
+        hipLaunchKernelGGL(k_rht_col_tiled, dim3(grid), dim3(kThreads), 0, s, x, rows, cols, ld,
+                           r, y);
+      }
     }
   }
   return hipGetLastError();
