@@ -31,7 +31,7 @@ constexpr int kStream = 512;        // streaming kernels (amax, rowwise, dequant
 // MI355X: more waves let the VALU-heavy stochastic-rounding kernels overlap
 // their LDS and memory latency; the RNE tile kernels prefer fewer).
 constexpr int kRowWgPerCu = 2;      // rowwise, RNE and SR
-constexpr int kColWgPerCuSR = 4;    // colwise with stochastic rounding
+constexpr int kColWgPerCuSR = 6;    // colwise and dual with stochastic rounding
 constexpr int kTileWgPerCu = 3;     // colwise / dual RNE, 2D
 constexpr int kAmaxWgPerCu = 1;     // tensor amax (plain and 16-point RHT)
 
