@@ -378,7 +378,7 @@ def gemm(a: Operand, b: Operand, M, N, K, out=None, accumulate=False, device=Non
 
 
 # ------------------------------------------------------------- self-test --
-SWEEPS = {"e2m1_rne": 0, "e4m3_scale": 1, "ue5m3_scale": 2, "e2m1_sr": 3}
+SWEEPS = {"e2m1_rne": 0, "e4m3_scale": 1, "ue5m3_scale": 2, "e2m1_sr": 3, "e4m3_elem": 4}
 
 
 def selftest_sweep(kind, thresholds, device="cuda"):

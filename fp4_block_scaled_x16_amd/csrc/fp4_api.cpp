@@ -495,8 +495,8 @@ FP4_EXPORT fp4_status fp4_selftest_set_geometry(int max_workgroups, int gemm_til
 
 FP4_EXPORT fp4_status fp4_selftest_sweep(int kind, const uint32_t* thresholds, int n,
                                          uint64_t* result, void* stream) {
-  static const int kLen[4] = {7, 126, 255, 7};
-  if (kind < FP4_SWEEP_E2M1_RNE || kind > FP4_SWEEP_E2M1_SR)
+  static const int kLen[5] = {7, 126, 255, 7, 126};
+  if (kind < FP4_SWEEP_E2M1_RNE || kind > FP4_SWEEP_E4M3_ELEM)
     return fail(FP4_ERR_ARG, "bad sweep kind %d", kind);
   if (n != kLen[kind])
     return fail(FP4_ERR_ARG, "sweep kind %d needs %d thresholds (got %d)", kind, kLen[kind], n);

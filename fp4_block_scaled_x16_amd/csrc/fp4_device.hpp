@@ -52,6 +52,23 @@ __device__ __forceinline__ uint32_t scale_m3_encode(float t, float tmax, uint32_
   return (r >> 20) - ((127u - BIAS) << 3);
 }
 
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// Four E4M3 element codes in one word, byte k = sign of y_k | E4M3 code of
+// |y_k| rounded to nearest even (the grid scale_m3_encode<7> encodes:
+// subnormal step 2^-9, largest value 448), through gfx950's packed FP8
+// convert at unit scale.  Defined for |y_k| <= 448 only, where it agrees
+// with scale_m3_encode<7> on every fp32 magnitude; callers scale a block so
+// that no element exceeds 448.  Each convert fills the low half of a fresh
+// word and the two halves are merged by a byte permute.
+__device__ __forceinline__ uint32_t e4m3_pack4(float y0, float y1, float y2, float y3) {
+  const s16x2 z = {0, 0};
+  const s16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, y0, y1, 1.0f, false);
+  const s16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, y2, y3, 1.0f, false);
+  return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo),
+                               0x05040100u);
+}
+
 template <int BIAS>
 __device__ __forceinline__ float scale_m3_decode(uint32_t code) {
   constexpr float kSubStep = (BIAS == 7) ? 0x1p-9f : 0x1p-17f;

@@ -4,10 +4,13 @@
 // smallest integer such that 448 * 2^e >= amax_B -- rounded up, as NVFP4
 // paper App. B.4 does for MX scales so that no element saturates (the page
 // ties saturation to MXFP8 convergence problems); element code = sign bit 7
-// | E4M3 RNE code of |x * 2^-e|; one byte per element.
+// | E4M3 RNE code of |x * 2^-e|, four at a time through gfx950's packed
+// FP8 convert (e4m3_pack4); one byte per element.
 //
 //   k_quant_mx8_row  ROWWISE: one thread per block of 32 consecutive bf16
-//                    (four 16-byte loads), 32 code bytes as two 16-byte stores
+//                    (four 16-byte loads, the next block's issued before the
+//                    current one is encoded), 32 code bytes as two 16-byte
+//                    stores
 //   k_quant_mx8_col  COLWISE (codes of X^T): a 32 x 256 tile of X through
 //                    LDS, one thread per column: its 32 rows are one block,
 //                    written as 32 contiguous bytes of the X^T code row
@@ -61,20 +64,32 @@ __device__ __forceinline__ uint32_t block_scale_mx8(float amax_b, float& s_enc_l
   return static_cast<uint32_t>(e + 127);
 }
 
-// Element code of v * s: sign bit 7 | E4M3 RNE magnitude (saturating at 448).
-// Counters: cnt[3] += |y| > 448; cnt[4] += (v != 0 and magnitude code 0).
+// Codes of a 32-element block, w[k] = elements 4k .. 4k + 3 in memory
+// order; element code = sign bit 7 | E4M3 RNE magnitude of v * s.  The
+// block scale 2^-e has 448 * 2^e >= amax, so |v * s| <= 448: the range in
+// which the hardware convert of e4m3_pack4 is the format's RNE encoder.
+// Counters: cnt[3] += |v * s| > 448 (kept for the counter contract; the
+// bound makes it 0); cnt[4] += (v != 0 and magnitude code 0).
 template <bool CNT>
-__device__ __forceinline__ uint32_t e4m3_code(float v, float s, uint32_t (&cnt)[5]) {
-  const float y = v * s;
-  const float t = fabsf(y);
-  const uint32_t mag = scale_m3_encode<7>(t, 448.0f, 0x7Eu);
-  if constexpr (CNT) {
-    cnt[3] += t > 448.0f ? 1u : 0u;
-    cnt[4] += (v != 0.0f && mag == 0u) ? 1u : 0u;
+__device__ __forceinline__ void encode_mx8(const float (&v)[kBS], float s, uint32_t (&w)[8],
+                                           uint32_t (&cnt)[5]) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float y[4] = {v[4 * k] * s, v[4 * k + 1] * s, v[4 * k + 2] * s, v[4 * k + 3] * s};
+    w[k] = e4m3_pack4(y[0], y[1], y[2], y[3]);
+    if constexpr (CNT) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        cnt[3] += fabsf(y[e]) > 448.0f ? 1u : 0u;
+        cnt[4] += (v[4 * k + e] != 0.0f && ((w[k] >> (8 * e)) & 0x7Fu) == 0u) ? 1u : 0u;
+      }
+    }
   }
-  return mag | ((__float_as_uint(y) >> 24) & 0x80u);
 }
 
+// ROWWISE: a grid-stride loop over blocks; the next block's loads are
+// issued before the current block is encoded (past the end they re-read
+// the current block, so no branch guards them).
 template <bool CNT>
 __global__ __launch_bounds__(kMx8Threads) void k_quant_mx8_row(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
@@ -83,14 +98,32 @@ __global__ __launch_bounds__(kMx8Threads) void k_quant_mx8_row(
   const uint64_t bpr = static_cast<uint64_t>(cols) / kBS;
   const uint64_t n = static_cast<uint64_t>(rows) * bpr;
   const uint64_t kg = (bpr + 7) >> 3;
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kMx8Threads;
+  uint64_t i = static_cast<uint64_t>(blockIdx.x) * kMx8Threads + threadIdx.x;
+  uint64_t r = bpr ? i / bpr : 0, j = bpr ? i - r * bpr : 0;
+  const uint64_t sr = bpr ? stride / bpr : 0, sj = bpr ? stride - sr * bpr : 0;
   uint32_t cnt[5] = {0, 0, 0, 0, 0};
-  for (uint64_t i = static_cast<uint64_t>(blockIdx.x) * kMx8Threads + threadIdx.x; i < n;
-       i += static_cast<uint64_t>(gridDim.x) * kMx8Threads) {
-    const uint64_t r = i / bpr, j = i - r * bpr;
+  uint4 q[4];
+  if (i < n) {
     const uint4* src = reinterpret_cast<const uint4*>(x + r * ld + j * kBS);
-    uint4 q[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) q[k] = src[k];
+  }
+  for (; i < n; i += stride) {
+    const uint64_t r_cur = r, j_cur = j;
+    r += sr;
+    j += sj;
+    if (j >= bpr) {
+      j -= bpr;
+      ++r;
+    }
+    const bool has_next = i + stride < n;
+    const uint4* nsrc = reinterpret_cast<const uint4*>(x + (has_next ? r : r_cur) * ld +
+                                                       (has_next ? j : j_cur) * kBS);
+    uint4 nq[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) nq[k] = nsrc[k];
+
     float v[kBS];
 #pragma unroll
     for (int k = 0; k < 4; ++k) unpack8(q[k], v + 8 * k);
@@ -100,16 +133,14 @@ __global__ __launch_bounds__(kMx8Threads) void k_quant_mx8_row(
     float s;
     const uint32_t sc = block_scale_mx8(amax_b, s);
     uint32_t w[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      w[k] = e4m3_code<CNT>(v[4 * k], s, cnt) | (e4m3_code<CNT>(v[4 * k + 1], s, cnt) << 8) |
-             (e4m3_code<CNT>(v[4 * k + 2], s, cnt) << 16) |
-             (e4m3_code<CNT>(v[4 * k + 3], s, cnt) << 24);
-    }
-    uint4* dst = reinterpret_cast<uint4*>(codes + r * static_cast<uint64_t>(cols) + j * kBS);
+    encode_mx8<CNT>(v, s, w, cnt);
+    uint4* dst = reinterpret_cast<uint4*>(codes + r_cur * static_cast<uint64_t>(cols) + j_cur * kBS);
     dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
     dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-    scales[tiled ? tiled_scale_offset(r, j, kg) : i] = static_cast<uint8_t>(sc);
+    scales[tiled ? tiled_scale_offset(r_cur, j_cur, kg) : r_cur * bpr + j_cur] =
+        static_cast<uint8_t>(sc);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) q[k] = nq[k];
   }
   if constexpr (CNT) flush_counters<kMx8Threads>(cnt, counters);
 }
@@ -128,26 +159,41 @@ __global__ __launch_bounds__(kMx8Threads) void k_quant_mx8_col(
   const uint64_t kg = (bpr_t + 7) >> 3;
   const int t = threadIdx.x;
   uint32_t cnt[5] = {0, 0, 0, 0, 0};
-  for (int64_t tile_id = blockIdx.x; tile_id < tiles_r * tiles_c; tile_id += gridDim.x) {
+  const int64_t n_tiles = tiles_r * tiles_c;
+  // 32 rows x 256 columns = 1024 chunks of 8 bf16; chunk q = t + 256 k:
+  // row q / 32, columns 8 (q % 32) ..; chunks beyond the last column are
+  // neither loaded nor staged.  The next tile's chunks are loaded into
+  // registers while the current tile is encoded from LDS.
+  uint4 u[4];
+  auto load = [&](int64_t id) {
+    const int64_t lr0 = id / tiles_c;
+    const int64_t r0 = lr0 * kBS, c0 = (id - lr0 * tiles_c) * kColTileCols;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int q = t + k * kMx8Threads;
+      const int lr = q >> 5, lc = (q & 31) * 8;
+      if (c0 + lc < cols) u[k] = *reinterpret_cast<const uint4*>(x + (r0 + lr) * ld + c0 + lc);
+    }
+  };
+  if (blockIdx.x < n_tiles) load(blockIdx.x);
+  for (int64_t tile_id = blockIdx.x; tile_id < n_tiles; tile_id += gridDim.x) {
     const int64_t tr = tile_id / tiles_c, tc = tile_id - tr * tiles_c;
     const int64_t r0 = tr * kBS, c0 = tc * kColTileCols;
-    // 32 rows x 256 columns = 1024 chunks of 8 bf16; chunk q: row q / 32,
-    // columns 8 (q % 32) ..; chunks beyond the last column load nothing
     __syncthreads();     // the previous tile's LDS reads are done
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int q = t + k * kMx8Threads;
       const int lr = q >> 5, lc = (q & 31) * 8;
       if (c0 + lc < cols) {
-        const uint4 u = *reinterpret_cast<const uint4*>(x + (r0 + lr) * ld + c0 + lc);
         uint32_t* d = reinterpret_cast<uint32_t*>(tile + lr * kColLdsStride + lc);
-        d[0] = u.x;
-        d[1] = u.y;
-        d[2] = u.z;
-        d[3] = u.w;
+        d[0] = u[k].x;
+        d[1] = u[k].y;
+        d[2] = u[k].z;
+        d[3] = u[k].w;
       }
     }
     __syncthreads();
+    if (tile_id + gridDim.x < n_tiles) load(tile_id + gridDim.x);
     const int64_t c = c0 + t;
     if (c < cols) {
       float v[kBS];
@@ -159,12 +205,7 @@ __global__ __launch_bounds__(kMx8Threads) void k_quant_mx8_col(
       float s;
       const uint32_t sc = block_scale_mx8(amax_b, s);
       uint32_t w[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        w[k] = e4m3_code<CNT>(v[4 * k], s, cnt) | (e4m3_code<CNT>(v[4 * k + 1], s, cnt) << 8) |
-               (e4m3_code<CNT>(v[4 * k + 2], s, cnt) << 16) |
-               (e4m3_code<CNT>(v[4 * k + 3], s, cnt) << 24);
-      }
+      encode_mx8<CNT>(v, s, w, cnt);
       uint4* dst = reinterpret_cast<uint4*>(codes + c * static_cast<uint64_t>(rows) + r0);
       dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
       dst[1] = make_uint4(w[4], w[5], w[6], w[7]);

@@ -10,6 +10,9 @@
 //                  quantizers' 8-value helper, with the random bits on either
 //                  side of each input's carry threshold
 //   k_sweep_scale  fp32 -> E4M3 / UE5M3 block-scale codes (App. B.2 Eq. 3)
+//   k_sweep_e4m3_elem  fp32 -> E4M3 element codes of MXFP8 through the
+//                  hardware FP8 convert, four signed values per word as the
+//                  MXFP8 quantizer packs them
 //   k_gemm_decode  E2M1 x block scale -> fp16, the GEMM operand decode
 //                  (App. B.3)
 #include <hip/hip_runtime.h>
@@ -195,6 +198,39 @@ __global__ __launch_bounds__(kSweepThreads) void k_sweep_scale(const uint32_t* _
   flush_sweep(bad, checked, first, res);
 }
 
+// Every fp32 magnitude t in [0, 448] through the MXFP8 element packer, as
+// (t, -t, -t, t) and (-t, t, t, -t): each byte position with either sign.
+// Expected magnitude code: the number of thresholds <= t, sign in bit 7.
+__global__ __launch_bounds__(kSweepThreads) void k_sweep_e4m3_elem(const uint32_t* __restrict__ thr,
+                                                                   int n,
+                                                                   unsigned long long* __restrict__ res) {
+  __shared__ uint32_t t[256];
+  t[threadIdx.x] = static_cast<int>(threadIdx.x) < n ? thr[threadIdx.x] : 0xFFFFFFFFu;
+  __syncthreads();
+  constexpr uint64_t kEnd = 0x43E00001ull;   // one past 448.0f
+  const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kSweepThreads;
+  uint64_t bad = 0, checked = 0, first = ~uint64_t(0);
+  for (uint64_t b = static_cast<uint64_t>(blockIdx.x) * kSweepThreads + threadIdx.x; b < kEnd;
+       b += stride) {
+    const float tv = __uint_as_float(static_cast<uint32_t>(b));
+    const uint32_t w0 = fp4dev::e4m3_pack4(tv, -tv, -tv, tv);
+    const uint32_t w1 = fp4dev::e4m3_pack4(-tv, tv, tv, -tv);
+    uint32_t pos = 0;
+#pragma unroll
+    for (uint32_t s = 128; s >= 1; s >>= 1)
+      if (t[pos + s - 1] <= static_cast<uint32_t>(b)) pos += s;
+    const uint32_t ng = pos | 0x80u;
+    const uint32_t e0 = pos | (ng << 8) | (ng << 16) | (pos << 24);
+    const uint32_t e1 = ng | (pos << 8) | (pos << 16) | (ng << 24);
+    ++checked;
+    if (w0 != e0 || w1 != e1) {
+      ++bad;
+      first = b < first ? b : first;
+    }
+  }
+  flush_sweep(bad, checked, first, res);
+}
+
 // One thread per block-scale code s: the 16 E2M1 codes times s, with s in
 // the low and then in the high half of the scale pair, the pair taken from
 // bytes 0-1 and then from bytes 2-3 of a word.
@@ -252,6 +288,9 @@ hipError_t launch_selftest_sweep(int kind, const uint32_t* thresholds, int n, ui
     hipLaunchKernelGGL(k_sweep_e2m1_sr, dim3(grid), dim3(kSweepThreads), 0, s, thresholds, res);
   else if (kind == FP4_SWEEP_E4M3_SCALE)
     hipLaunchKernelGGL(k_sweep_scale<7>, dim3(grid), dim3(kSweepThreads), 0, s, thresholds, n, res);
+  else if (kind == FP4_SWEEP_E4M3_ELEM)
+    hipLaunchKernelGGL(k_sweep_e4m3_elem, dim3(grid), dim3(kSweepThreads), 0, s, thresholds, n,
+                       res);
   else
     hipLaunchKernelGGL(k_sweep_scale<15>, dim3(grid), dim3(kSweepThreads), 0, s, thresholds, n,
                        res);

@@ -35,7 +35,8 @@ typedef enum fp4_sweep_kind_e FP4_ENUM_INT {
   FP4_SWEEP_E2M1_RNE = 0,     /* every fp32 pattern except NaNs (2^32 - 2^24 + 2)   */
   FP4_SWEEP_E4M3_SCALE = 1,   /* every finite fp32 t >= 0 (patterns 0 .. 0x7F7FFFFF) */
   FP4_SWEEP_UE5M3_SCALE = 2,  /* likewise                                            */
-  FP4_SWEEP_E2M1_SR = 3       /* every fp32 pattern except NaNs, four draws each     */
+  FP4_SWEEP_E2M1_SR = 3,      /* every fp32 pattern except NaNs, four draws each     */
+  FP4_SWEEP_E4M3_ELEM = 4     /* every fp32 magnitude 0 .. 448 (0 .. 0x43E00000)    */
 } fp4_sweep_kind;
 
 /*
@@ -46,7 +47,8 @@ typedef enum fp4_sweep_kind_e FP4_ENUM_INT {
  * the code copies the input's sign bit.
  *   thresholds  device uint32 array, ascending fp32 bit patterns: entry i is
  *               the smallest magnitude whose code is i + 1.  Length n:
- *               7 (E2M1), 126 (E4M3, codes 1 .. 0x7E), 255 (UE5M3).
+ *               7 (E2M1), 126 (E4M3, codes 1 .. 0x7E; also for
+ *               FP4_SWEEP_E4M3_ELEM), 255 (UE5M3).
  *   result      device uint64[3], overwritten: [0] inputs whose code differs,
  *               [1] the smallest differing input pattern (all ones if none),
  *               [2] inputs checked.
@@ -57,6 +59,12 @@ typedef enum fp4_sweep_kind_e FP4_ENUM_INT {
  * even and at an odd element position with the random value just below and
  * at its carry threshold (16 random bits u round up iff u + floor(65536 f)
  * >= 65536), so every input counts four times in [2].
+ * FP4_SWEEP_E4M3_ELEM checks the MXFP8 element encoder (E4M3 round to
+ * nearest even of the scaled element, MXFP8 row of fp4.h's format list):
+ * the hardware FP8 convert the quantizer packs four elements with, over
+ * the magnitudes the block scale lets through (|v * 2^-e| <= 448); each
+ * input t is packed as (t, -t, -t, t) and (-t, t, t, -t), the sign going
+ * to bit 7 of its byte, and counts once in [2].
  */
 fp4_status fp4_selftest_sweep(int kind, const uint32_t* thresholds, int n,
                               uint64_t* result, void* stream);

@@ -290,7 +290,9 @@ def test_geometry_control_rejects(lib):
 
 def test_selftest_sweep_rejects(lib):
     # validation happens on the host before any device work
-    assert lib.fp4_selftest_sweep(4, FAKE, 7, FAKE, None) == 1
+    assert lib.fp4_selftest_sweep(5, FAKE, 7, FAKE, None) == 1
+    assert lib.fp4_selftest_sweep(4, FAKE, 7, FAKE, None) == 1      # E4M3 elements take 126
+    assert "126 thresholds" in _err(lib)
     assert lib.fp4_selftest_sweep(-1, FAKE, 7, FAKE, None) == 1
     assert lib.fp4_selftest_sweep(3, FAKE, 6, FAKE, None) == 1      # E2M1 SR takes 7
     assert "7 thresholds" in _err(lib)

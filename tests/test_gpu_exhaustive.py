@@ -18,6 +18,10 @@ elements; the UE5M3 abstract for the unsigned E5M3 scale).
 * fp32 -> E4M3 / UE5M3 block-scale code: every finite t >= 0 through the
   quantizer's scale encoder, against the 126 / 255 boundaries of the
   oracle's encoders.
+* fp32 -> E4M3 MXFP8 element code: every magnitude 0 .. 448 (all that the
+  MXFP8 block scale lets through) with both signs at each byte position of
+  the hardware FP8 convert's packed word, against the same 126 boundaries
+  (the oracle encodes MXFP8 elements with its E4M3 RNE encoder).
 * E2M1 x scale -> fp16 (the GEMM operand decode): all 16 codes times every
   E4M3 scale code (the FP4 and FP8 hardware converts, then the packed
   multiply) and every UE5M3 scale code (its packed integer / fp16 decode),
@@ -90,6 +94,20 @@ def test_scale_encoder_exhaustive(kind, encode, n_codes, vmax):
     assert _as_f32(thr[-1]) <= vmax
     bad, first, checked = api.selftest_sweep(kind, thr)
     assert checked == 0x7F800000
+    assert bad == 0, "%d mismatches, first at 0x%08x" % (bad, first)
+
+
+def test_mxfp8_element_encoder_exhaustive():
+    thr = _boundaries(lambda b: F.e4m3_rne_sat(_as_f32(b))[0].astype(np.int64), 0x7F, 0x7F7FFFFF)
+    # code k begins at the midpoint between values k-1 and k, a tie going
+    # to the even code: at the midpoint for even k, just above it for odd k
+    vals = F.E4M3_VALUES[:0x7F].astype(np.float64)
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)      # exact: 4 mantissa bits
+    k = np.arange(1, 0x7F)
+    want = np.where(k % 2 == 0, mids, np.nextafter(mids, np.float32(np.inf)))
+    assert np.array_equal(_as_f32(thr), want)
+    bad, first, checked = api.selftest_sweep("e4m3_elem", thr)
+    assert checked == 0x43E00001                      # every pattern 0 .. 448.0f
     assert bad == 0, "%d mismatches, first at 0x%08x" % (bad, first)
 
 
