@@ -146,6 +146,69 @@ __device__ __forceinline__ void epilogue_bf16(const Params& p, floatx16 (&acc)[M
   }
 }
 
+// Epilogue through LDS, for a wave whose whole 128 x 128 (MI * 32 x 128)
+// part of the tile lies inside an fp32 D with 16-byte aligned rows, with
+// no accumulation and no per-row decode scales.  Each 32 x 32 block goes
+// through a per-wave LDS buffer of 32 rows x kEpiPitch floats: the
+// accumulators go in by output row (lane (i, h): row i, columns 8g + 4h ..
+// + 3, g = 0..3) and come out so that 8 consecutive lanes hold one row's 32
+// columns, so each of the four 16-byte stores writes 8 whole 128-byte row
+// segments instead of a quarter of 32 (4x fewer memory requests; the fp32
+// D write was the larger part of the epilogue).  The pitch of 36 floats
+// puts the 16 rows one write pass covers, and the 2 rows one read pass
+// covers, on different banks.  Values are (acc * pre) * scale, the same two
+// roundings as multiplying the accumulators by `pre` and then calling
+// `epilogue` with `scale`.
+constexpr int kEpiPitch = 36;
+constexpr int kEpiBufFloats = 32 * kEpiPitch;
+
+template <int MI>
+__device__ __forceinline__ bool epilogue_lds_ok(const Params& p, int64_t m0, int64_t n0, int wm,
+                                                int wn) {
+  return !p.d_bf16 && !p.accumulate && !p.s_dec_rows[0] && !p.s_dec_rows[1] &&
+         (p.ldd & 3) == 0 && (reinterpret_cast<uintptr_t>(p.D) & 15) == 0 &&
+         m0 + wm * (MI * 32) + MI * 32 <= p.M && n0 + wn * 128 + 128 <= p.N;
+}
+
+// lds_t: this wave's BUFS * kEpiBufFloats floats (with 2, blocks alternate
+// halves).
+template <int MI, int BUFS = 2>
+__device__ __forceinline__ void epilogue_lds(const Params& p, floatx16 (&acc)[MI][4], float pre,
+                                             float scale, int64_t m0, int64_t n0, int wm, int wn,
+                                             int lane, float* lds_t) {
+  const int i = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      float* buf = lds_t + (BUFS == 2 ? ((mi * 4 + ni) & 1) * kEpiBufFloats : 0);
+      // the accumulators go out unscaled (straight from their registers);
+      // the scaling is per element, so it is applied after the transpose
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<float4*>(buf + i * kEpiPitch + 8 * g + 4 * h) =
+            make_float4(acc[mi][ni][4 * g], acc[mi][ni][4 * g + 1], acc[mi][ni][4 * g + 2],
+                        acc[mi][ni][4 * g + 3]);
+      // the other lanes' writes are read next: order them within the wave
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      float4 v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        v[r] = *reinterpret_cast<const float4*>(buf + (8 * r + (lane >> 3)) * kEpiPitch +
+                                                4 * (lane & 7));
+      // and these reads precede the next writes into the buffer
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      const int64_t row0 = m0 + wm * (MI * 32) + mi * 32, col0 = n0 + wn * 128 + ni * 32;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        *reinterpret_cast<float4*>(p.D + (row0 + 8 * r + (lane >> 3)) * p.ldd + col0 +
+                                   4 * (lane & 7)) =
+            make_float4((v[r].x * pre) * scale, (v[r].y * pre) * scale, (v[r].z * pre) * scale,
+                        (v[r].w * pre) * scale);
+    }
+  }
+}
+
 // `scale` is the tensor-level s_dec_B (1 when B has per-row scales).  Per-row
 // decode scales (s_dec_A[m], s_dec_B[n]) are multiplied into the
 // accumulators before the first store: either read from LDS copies of the

@@ -180,7 +180,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx_ring(Params p) {
   ring_step<false, false, kDmaPerStep>(st1, st2, acc, f0, f1, a_sc, b_sc, src, 0, wave, wm, wn, i, h);
   ring_step<false, false, 0>(st2, st3, acc, f0, f1, a_sc, b_sc, src, 0, wave, wm, wn, i, h);
   ring_step<true, false, 0>(st3, st0, acc, f0, f1, a_sc, b_sc, src, 0, wave, wm, wn, i, h);
-  epilogue(p, acc, 1.0f, m0, n0, wm, wn, lane);
+  // every wave is past its last stage read and its DMAs have landed: stage
+  // 0 holds the epilogue's per-wave transpose buffers (one each: a stage is
+  // 34 KiB)
+  ring_barrier();
+  static_assert(sizeof(StageD) >= 4 * kEpiBufFloats * sizeof(float), "epilogue buffers");
+  if (epilogue_lds_ok<4>(p, m0, n0, wm, wn))
+    epilogue_lds<4, 1>(p, acc, 1.0f, 1.0f, m0, n0, wm, wn, lane,
+                       reinterpret_cast<float*>(&st0) + wave * kEpiBufFloats);
+  else
+    epilogue(p, acc, 1.0f, m0, n0, wm, wn, lane);
 }
 
 
@@ -362,7 +371,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx_tiled(Params p) {
   }
   v_step<false, false>(sv0, sv1, acc, fa, fb, a_sc, b_sc, src, 0, wave, wm, wn, i, h);
   v_step<true, false>(sv1, sv0, acc, fa, fb, a_sc, b_sc, src, 0, wave, wm, wn, i, h);
-  epilogue(p, acc, 1.0f, m0, n0, wm, wn, lane);
+  // every wave is past its last stage read and its DMAs have landed: stage
+  // 0 holds the epilogue's per-wave transpose buffers
+  ring_barrier();
+  static_assert(sizeof(StageV) >= 4 * 2 * kEpiBufFloats * sizeof(float), "epilogue buffers");
+  if (epilogue_lds_ok<4>(p, m0, n0, wm, wn))
+    epilogue_lds<4, 2>(p, acc, 1.0f, 1.0f, m0, n0, wm, wn, lane,
+                       reinterpret_cast<float*>(&sv0) + wave * 2 * kEpiBufFloats);
+  else
+    epilogue(p, acc, 1.0f, m0, n0, wm, wn, lane);
 }
 
 }  // namespace

@@ -72,6 +72,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level_dma(Params p) {
   // per-row decode scales of the tile's A rows and B rows (per-row global
   // scales only): loaded with the first K step's scales, read by the epilogue
   __shared__ __attribute__((aligned(16))) float srow[2][256];
+  __shared__ __attribute__((aligned(16))) float ept[4][2 * kEpiBufFloats];
   int tm, tn;
   tile_coords(p, tm, tn);
   const int64_t m0 = static_cast<int64_t>(tm) * BM, n0 = static_cast<int64_t>(tn) * kBN;
@@ -270,11 +271,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level_dma(Params p) {
   float scale = FMT == kUE ? 1024.0f : 1.0f;   // undo the two 2^-5 scale shifts
   if (p.s_dec[0] && !p.s_dec_rows[0]) scale *= *p.s_dec[0];
   const float sb = p.s_dec[1] && !p.s_dec_rows[1] ? *p.s_dec[1] : 1.0f;
+  if (epilogue_lds_ok<MI>(p, m0, n0, wm, wn)) {
+    epilogue_lds<MI>(p, acc, scale, sb, m0, n0, wm, wn, lane, ept[wave]);
+  } else {
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] *= scale;
-  epilogue(p, acc, sb, m0, n0, wm, wn, lane, srow[0], srow[1]);
+      for (int ni = 0; ni < 4; ++ni) acc[mi][ni] *= scale;
+    epilogue(p, acc, sb, m0, n0, wm, wn, lane, srow[0], srow[1]);
+  }
 }
 
 }  // namespace
