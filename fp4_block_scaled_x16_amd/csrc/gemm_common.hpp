@@ -146,65 +146,132 @@ __device__ __forceinline__ void epilogue_bf16(const Params& p, floatx16 (&acc)[M
   }
 }
 
-// Epilogue through LDS, for a wave whose whole 128 x 128 (MI * 32 x 128)
-// part of the tile lies inside an fp32 D with 16-byte aligned rows, with
-// no accumulation and no per-row decode scales.  Each 32 x 32 block goes
-// through a per-wave LDS buffer of 32 rows x kEpiPitch floats: the
-// accumulators go in by output row (lane (i, h): row i, columns 8g + 4h ..
-// + 3, g = 0..3) and come out so that 8 consecutive lanes hold one row's 32
-// columns, so each of the four 16-byte stores writes 8 whole 128-byte row
-// segments instead of a quarter of 32 (4x fewer memory requests; the fp32
-// D write was the larger part of the epilogue).  The pitch of 36 floats
-// puts the 16 rows one write pass covers, and the 2 rows one read pass
-// covers, on different banks.  Values are (acc * pre) * scale, the same two
-// roundings as multiplying the accumulators by `pre` and then calling
-// `epilogue` with `scale`.
+// Epilogue through LDS, for a wave whose whole MI * 32 x 128 part of the
+// tile lies inside D, with no per-row decode scales.  In the MFMA output
+// layout lane (i, h) holds row i, columns 8g + 4h .. + 3 (g = 0..3) of a
+// 32 x 32 block, so a plain 16-byte store covers 32 rows with 32 bytes
+// each (and a bf16 one 32 rows with 16 bytes).  Here each block goes
+// through a per-wave LDS buffer of 32 rows x kEpiPitch floats and comes out
+// with 8 consecutive lanes holding one row's 32 values, so every store
+// writes 8 whole 128-byte row segments (a bf16 D: 8 rows x 64 bytes) -- 4x
+// fewer memory requests; the D write was the larger part of the epilogue.
+// The pitch of 36 floats puts the rows one write pass covers, and the 2
+// rows one read pass covers, on different banks.  Values are (acc * pre) *
+// scale in fp32 -- the same two roundings as multiplying the accumulators
+// by `pre` and calling `epilogue` with `scale` -- plus the old D (fp32,
+// accumulate), or rounded once to bf16 (no accumulation).  ALL: also the
+// accumulate and bf16 cases; without it only a plain fp32 D (the 256-row
+// kernels have no registers to spare for the other two: with them the
+// compiler spilled values of every path, the plain one included).
 constexpr int kEpiPitch = 36;
 constexpr int kEpiBufFloats = 32 * kEpiPitch;
 
-template <int MI>
+template <int MI, bool ALL>
 __device__ __forceinline__ bool epilogue_lds_ok(const Params& p, int64_t m0, int64_t n0, int wm,
                                                 int wn) {
-  return !p.d_bf16 && !p.accumulate && !p.s_dec_rows[0] && !p.s_dec_rows[1] &&
+  if (!ALL && (p.d_bf16 || p.accumulate)) return false;
+  // rows of D 16-byte (fp32) or 8-byte (bf16) aligned
+  return !p.s_dec_rows[0] && !p.s_dec_rows[1] && !(p.d_bf16 && p.accumulate) &&
          (p.ldd & 3) == 0 && (reinterpret_cast<uintptr_t>(p.D) & 15) == 0 &&
          m0 + wm * (MI * 32) + MI * 32 <= p.M && n0 + wn * 128 + 128 <= p.N;
 }
 
-// lds_t: this wave's BUFS * kEpiBufFloats floats (with 2, blocks alternate
-// halves).
-template <int MI, int BUFS = 2>
+// 32 x 32 fp32 block through `buf`: v[r] = this lane's 4 values of row
+// 8r + lane / 8, columns 4 (lane % 8) .. + 3, unscaled (the accumulators go
+// out straight from their registers; the scaling is per element, so the
+// caller applies it after the transpose).
+__device__ __forceinline__ void lds_transpose_f32(const floatx16& a, float* buf, int lane,
+                                                  float4 (&v)[4]) {
+  const int i = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+    *reinterpret_cast<float4*>(buf + i * kEpiPitch + 8 * g + 4 * h) =
+        make_float4(a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]);
+  // the other lanes' writes are read next: order them within the wave
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    v[r] = *reinterpret_cast<const float4*>(buf + (8 * r + (lane >> 3)) * kEpiPitch +
+                                            4 * (lane & 7));
+  // and these reads precede the next writes into the buffer
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+}
+
+__device__ __forceinline__ float4 scale4(const float4& v, float pre, float scale) {
+  return make_float4((v.x * pre) * scale, (v.y * pre) * scale, (v.z * pre) * scale,
+                     (v.w * pre) * scale);
+}
+
+// lds_t: this wave's BUFS * kEpiBufFloats words (with 2, consecutive blocks
+// alternate halves).
+template <int MI, int BUFS, bool ALL>
 __device__ __forceinline__ void epilogue_lds(const Params& p, floatx16 (&acc)[MI][4], float pre,
                                              float scale, int64_t m0, int64_t n0, int wm, int wn,
                                              int lane, float* lds_t) {
-  const int i = lane & 31, h = lane >> 5;
+  const int lr = lane >> 3, lc = lane & 7;    // row within 8, 16-byte chunk within 128 bytes
+  const int64_t wr0 = m0 + wm * (MI * 32), wc0 = n0 + wn * 128;
+  // one straight-line loop per case (a branch per block on the case costs
+  // the plain fp32 loop measurably)
+  if (ALL && p.accumulate) {
+    // the old D of a block is loaded ahead of its LDS round trip, in the
+    // same coalesced layout as the stores
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+        const int64_t row0 = wr0 + mi * 32, col0 = wc0 + ni * 32;
+        float4 old[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          old[r] = *reinterpret_cast<const float4*>(p.D + (row0 + 8 * r + lr) * p.ldd + col0 +
+                                                    4 * lc);
+        float4 v[4];
+        lds_transpose_f32(acc[mi][ni],
+                          lds_t + (BUFS == 2 ? ((mi * 4 + ni) & 1) * kEpiBufFloats : 0), lane, v);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float4 y = scale4(v[r], pre, scale);
+          *reinterpret_cast<float4*>(p.D + (row0 + 8 * r + lr) * p.ldd + col0 + 4 * lc) =
+              make_float4(y.x + old[r].x, y.y + old[r].y, y.z + old[r].z, y.w + old[r].w);
+        }
+      }
+    }
+    return;
+  }
+  if (ALL && p.d_bf16) {
+    // 8 lanes write a row's 64 bytes
+    uint16_t* d16 = reinterpret_cast<uint16_t*>(p.D);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+        const int64_t row0 = wr0 + mi * 32, col0 = wc0 + ni * 32;
+        float4 v[4];
+        lds_transpose_f32(acc[mi][ni],
+                          lds_t + (BUFS == 2 ? ((mi * 4 + ni) & 1) * kEpiBufFloats : 0), lane, v);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float4 y = scale4(v[r], pre, scale);
+          *reinterpret_cast<uint2*>(d16 + (row0 + 8 * r + lr) * p.ldd + col0 + 4 * lc) =
+              make_uint2(f32_to_bf16_rne(y.x) | (f32_to_bf16_rne(y.y) << 16),
+                         f32_to_bf16_rne(y.z) | (f32_to_bf16_rne(y.w) << 16));
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) {
-      float* buf = lds_t + (BUFS == 2 ? ((mi * 4 + ni) & 1) * kEpiBufFloats : 0);
-      // the accumulators go out unscaled (straight from their registers);
-      // the scaling is per element, so it is applied after the transpose
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *reinterpret_cast<float4*>(buf + i * kEpiPitch + 8 * g + 4 * h) =
-            make_float4(acc[mi][ni][4 * g], acc[mi][ni][4 * g + 1], acc[mi][ni][4 * g + 2],
-                        acc[mi][ni][4 * g + 3]);
-      // the other lanes' writes are read next: order them within the wave
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      const int64_t row0 = wr0 + mi * 32, col0 = wc0 + ni * 32;
       float4 v[4];
+      lds_transpose_f32(acc[mi][ni],
+                        lds_t + (BUFS == 2 ? ((mi * 4 + ni) & 1) * kEpiBufFloats : 0), lane, v);
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        v[r] = *reinterpret_cast<const float4*>(buf + (8 * r + (lane >> 3)) * kEpiPitch +
-                                                4 * (lane & 7));
-      // and these reads precede the next writes into the buffer
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      const int64_t row0 = m0 + wm * (MI * 32) + mi * 32, col0 = n0 + wn * 128 + ni * 32;
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        *reinterpret_cast<float4*>(p.D + (row0 + 8 * r + (lane >> 3)) * p.ldd + col0 +
-                                   4 * (lane & 7)) =
-            make_float4((v[r].x * pre) * scale, (v[r].y * pre) * scale, (v[r].z * pre) * scale,
-                        (v[r].w * pre) * scale);
+        *reinterpret_cast<float4*>(p.D + (row0 + 8 * r + lr) * p.ldd + col0 + 4 * lc) =
+            scale4(v[r], pre, scale);
     }
   }
 }

@@ -185,8 +185,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx_ring(Params p) {
   // 34 KiB)
   ring_barrier();
   static_assert(sizeof(StageD) >= 4 * kEpiBufFloats * sizeof(float), "epilogue buffers");
-  if (epilogue_lds_ok<4>(p, m0, n0, wm, wn))
-    epilogue_lds<4, 1>(p, acc, 1.0f, 1.0f, m0, n0, wm, wn, lane,
+  if (epilogue_lds_ok<4, false>(p, m0, n0, wm, wn))
+    epilogue_lds<4, 1, false>(p, acc, 1.0f, 1.0f, m0, n0, wm, wn, lane,
                        reinterpret_cast<float*>(&st0) + wave * kEpiBufFloats);
   else
     epilogue(p, acc, 1.0f, m0, n0, wm, wn, lane);
@@ -375,8 +375,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_mx_tiled(Params p) {
   // 0 holds the epilogue's per-wave transpose buffers
   ring_barrier();
   static_assert(sizeof(StageV) >= 4 * 2 * kEpiBufFloats * sizeof(float), "epilogue buffers");
-  if (epilogue_lds_ok<4>(p, m0, n0, wm, wn))
-    epilogue_lds<4, 2>(p, acc, 1.0f, 1.0f, m0, n0, wm, wn, lane,
+  if (epilogue_lds_ok<4, false>(p, m0, n0, wm, wn))
+    epilogue_lds<4, 2, false>(p, acc, 1.0f, 1.0f, m0, n0, wm, wn, lane,
                        reinterpret_cast<float*>(&sv0) + wave * 2 * kEpiBufFloats);
   else
     epilogue(p, acc, 1.0f, m0, n0, wm, wn, lane);

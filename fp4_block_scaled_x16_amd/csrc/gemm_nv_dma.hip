@@ -271,8 +271,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_two_level_dma(Params p) {
   float scale = FMT == kUE ? 1024.0f : 1.0f;   // undo the two 2^-5 scale shifts
   if (p.s_dec[0] && !p.s_dec_rows[0]) scale *= *p.s_dec[0];
   const float sb = p.s_dec[1] && !p.s_dec_rows[1] ? *p.s_dec[1] : 1.0f;
-  if (epilogue_lds_ok<MI>(p, m0, n0, wm, wn)) {
-    epilogue_lds<MI>(p, acc, scale, sb, m0, n0, wm, wn, lane, ept[wave]);
+  if (epilogue_lds_ok<MI, MI == 3>(p, m0, n0, wm, wn)) {
+    epilogue_lds<MI, 2, MI == 3>(p, acc, scale, sb, m0, n0, wm, wn, lane, ept[wave]);
   } else {
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
