@@ -170,6 +170,50 @@ def test_gemm_accumulate_and_ldd(fmt, K):
     assert torch.equal(big[:, 8 + N:].cpu(), init[:, 8 + N:].cpu())
 
 
+@pytest.mark.parametrize("view", ["aligned", "odd_pitch", "misaligned"])
+@pytest.mark.parametrize("kind", ["fp32", "bf16", "fp32_accumulate"])
+@pytest.mark.parametrize("tile_rows", [192, 256])
+def test_gemm_epilogue_layouts(tile_rows, kind, view):
+    """The DMA GEMM's epilogue stages whole 32 x 32 blocks through LDS when a
+    wave's part of the tile lies inside D with aligned rows (a plain fp32 D;
+    on 192-row tiles also a bf16 D and accumulation), else it stores lane by
+    lane.  Output views with aligned rows, with an odd row pitch, and
+    starting one element past an aligned address, on both tile heights
+    (some waves of the ragged last tiles outside D), against the oracle;
+    the memory around the view is untouched."""
+    fmt, M, N, K = "nvfp4", 400, 384, 256
+    a_bits = inputs.activations((M, K), cfg_seed=81)
+    b_bits = inputs.weights((N, K), cfg_seed=82)
+    qa, qb = gpu_quant(a_bits, fmt, "row"), gpu_quant(b_bits, fmt, "row")
+    av, sa = oracle_operand(a_bits, fmt, "row")
+    bv, sb = oracle_operand(b_bits, fmt, "row")
+    ref = G.gemm_ref(av, bv, sa, sb).astype(np.float64)
+    bound = G.gemm_abs_bound(av, bv, sa, sb)
+    dt = torch.bfloat16 if kind == "bf16" else torch.float32
+    pitch = N + (9 if view == "odd_pitch" else 32)            # 393: odd
+    off = 1 if view == "misaligned" else 8          # 8 elements: 16- (bf16) or 32-byte offset
+    big = torch.randn((M, pitch), dtype=torch.float32, device=DEV).to(dt)
+    init = big.clone()
+    out = big[:, off:off + N]
+    accumulate = kind == "fp32_accumulate"
+    api.selftest_set_geometry(0, tile_rows)
+    try:
+        api.gemm(qa.operand(), qb.operand(), M, N, K, out=out, accumulate=accumulate)
+        torch.cuda.synchronize()
+    finally:
+        api.selftest_set_geometry(0, 0)
+    if kind == "bf16":
+        bf16_close(out.contiguous().view(torch.int16).cpu().numpy().view(np.uint16), ref, bound)
+    else:
+        got = out.cpu().numpy()
+        if accumulate:
+            d0 = init[:, off:off + N].cpu().numpy().astype(np.float64)
+            ref, bound = ref + d0, bound + np.abs(d0)
+        check(got, ref, bound)
+    assert torch.equal(big[:, :off].cpu(), init[:, :off].cpu())
+    assert torch.equal(big[:, off + N:].cpu(), init[:, off + N:].cpu())
+
+
 def test_gemm_k_zero():
     a = api.quantize(dev(inputs.activations((64, 32), cfg_seed=52)), "nvfp4")
     b = api.quantize(dev(inputs.weights((48, 32), cfg_seed=52)), "nvfp4")
