@@ -11,9 +11,11 @@
 //                    (four 16-byte loads, the next block's issued before the
 //                    current one is encoded), 32 code bytes as two 16-byte
 //                    stores
-//   k_quant_mx8_col  COLWISE (codes of X^T): a 32 x 256 tile of X through
-//                    LDS, one thread per column: its 32 rows are one block,
-//                    written as 32 contiguous bytes of the X^T code row
+//   k_quant_mx8_col  COLWISE (codes of X^T): a 128 x 64 tile of X through
+//                    LDS; a thread takes 16 rows of a column pair (half of
+//                    a block of each column, the block amax completed with
+//                    its neighbour lane), so the 8 lanes of a column write
+//                    128 contiguous bytes of the X^T code row
 //   k_dequant_mx8    codes x 2^e, fp32 or bf16
 #include <hip/hip_runtime.h>
 
@@ -31,8 +33,14 @@ namespace {
 constexpr int kBS = 32;
 constexpr int kMx8Threads = 256;
 constexpr int kMx8WgPerCu = 4;
-constexpr int kColTileCols = 256;          // colwise tile: 32 rows x 256 columns
-constexpr int kColLdsStride = 256 + 2;     // bf16 per LDS row (padded: rows start 1 bank apart)
+constexpr int kColTileRows = 128;          // colwise tile: 128 rows (4 blocks) x 64 columns
+constexpr int kColTileCols = 64;
+// LDS words (bf16 pairs) of tile row r: r * 33 + (r / 16) * 8 -- rows one
+// bank apart, and the 8 row groups of 16 that a column read touches at once
+// start 24 banks apart, so the reads of a wave (8 column pairs x 8 groups)
+// hit 64 distinct banks
+__device__ __forceinline__ int col_tile_word(int r) { return r * 33 + (r >> 4) * 8; }
+constexpr int kColTileWords = kColTileRows * 33 + 8 * 8;
 
 // UE8M0 code and encode scale of a block: 2^e, e = min{e : 448 * 2^e >=
 // amax} clamped to [-127, 127] (a zero block: e = -127).  With amax =
@@ -75,6 +83,24 @@ __device__ __forceinline__ void encode_mx8(const float (&v)[kBS], float s, uint3
                                            uint32_t (&cnt)[5]) {
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
+    const float y[4] = {v[4 * k] * s, v[4 * k + 1] * s, v[4 * k + 2] * s, v[4 * k + 3] * s};
+    w[k] = e4m3_pack4(y[0], y[1], y[2], y[3]);
+    if constexpr (CNT) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        cnt[3] += fabsf(y[e]) > 448.0f ? 1u : 0u;
+        cnt[4] += (v[4 * k + e] != 0.0f && ((w[k] >> (8 * e)) & 0x7Fu) == 0u) ? 1u : 0u;
+      }
+    }
+  }
+}
+
+// The same for 16 elements (half a block), w[k] = elements 4k .. 4k + 3.
+template <bool CNT>
+__device__ __forceinline__ void encode_mx8_16(const float (&v)[16], float s, uint32_t (&w)[4],
+                                              uint32_t (&cnt)[5]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
     const float y[4] = {v[4 * k] * s, v[4 * k + 1] * s, v[4 * k + 2] * s, v[4 * k + 3] * s};
     w[k] = e4m3_pack4(y[0], y[1], y[2], y[3]);
     if constexpr (CNT) {
@@ -145,47 +171,54 @@ __global__ __launch_bounds__(kMx8Threads) void k_quant_mx8_row(
   if constexpr (CNT) flush_counters<kMx8Threads>(cnt, counters);
 }
 
-// COLWISE: tile (32 rows) x (256 columns) of X; thread t owns column t of
-// the tile, i.e. row c0 + t of X^T, block r0 / 32 of it.
+// COLWISE: tiles of 128 rows (4 blocks) x 64 columns of X.  Thread t =
+// 8 p + h takes rows 16 h .. 16 h + 15 of columns 2p, 2p + 1 (one 32-bit
+// LDS word per row holds both): half of block h / 2 of rows c0 + 2p and
+// c0 + 2p + 1 of X^T; lanes t and t ^ 1 hold the two halves of a block and
+// exchange their amaxes, and lanes 8p .. 8p + 7 write 128 contiguous code
+// bytes of each of the two X^T rows.  Rows beyond X are whole blocks
+// (rows % 32 == 0): both halves of a block are in or out together.
 template <bool CNT>
 __global__ __launch_bounds__(kMx8Threads) void k_quant_mx8_col(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, fp4_counters* __restrict__ counters,
     int tiled) {
-  __shared__ uint16_t tile[kBS * kColLdsStride];
-  const int64_t tiles_r = rows / kBS;
+  __shared__ uint32_t tile[kColTileWords];
+  const int64_t tiles_r = (rows + kColTileRows - 1) / kColTileRows;
   const int64_t tiles_c = (cols + kColTileCols - 1) / kColTileCols;
   const uint64_t bpr_t = static_cast<uint64_t>(rows) / kBS;      // blocks per X^T row
   const uint64_t kg = (bpr_t + 7) >> 3;
   const int t = threadIdx.x;
+  const int p = t >> 3, h = t & 7;
   uint32_t cnt[5] = {0, 0, 0, 0, 0};
   const int64_t n_tiles = tiles_r * tiles_c;
-  // 32 rows x 256 columns = 1024 chunks of 8 bf16; chunk q = t + 256 k:
-  // row q / 32, columns 8 (q % 32) ..; chunks beyond the last column are
-  // neither loaded nor staged.  The next tile's chunks are loaded into
-  // registers while the current tile is encoded from LDS.
+  // 128 rows x 64 columns = 1024 chunks of 8 bf16; chunk q = t + 256 k:
+  // row q / 8, columns 8 (q % 8) ..; chunks outside X are neither loaded
+  // nor staged.  The next tile's chunks are loaded into registers while the
+  // current tile is encoded from LDS.
   uint4 u[4];
   auto load = [&](int64_t id) {
-    const int64_t lr0 = id / tiles_c;
-    const int64_t r0 = lr0 * kBS, c0 = (id - lr0 * tiles_c) * kColTileCols;
+    const int64_t tr = id / tiles_c;
+    const int64_t r0 = tr * kColTileRows, c0 = (id - tr * tiles_c) * kColTileCols;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int q = t + k * kMx8Threads;
-      const int lr = q >> 5, lc = (q & 31) * 8;
-      if (c0 + lc < cols) u[k] = *reinterpret_cast<const uint4*>(x + (r0 + lr) * ld + c0 + lc);
+      const int lr = q >> 3, lc = (q & 7) * 8;
+      if (r0 + lr < rows && c0 + lc < cols)
+        u[k] = *reinterpret_cast<const uint4*>(x + (r0 + lr) * ld + c0 + lc);
     }
   };
   if (blockIdx.x < n_tiles) load(blockIdx.x);
   for (int64_t tile_id = blockIdx.x; tile_id < n_tiles; tile_id += gridDim.x) {
     const int64_t tr = tile_id / tiles_c, tc = tile_id - tr * tiles_c;
-    const int64_t r0 = tr * kBS, c0 = tc * kColTileCols;
+    const int64_t r0 = tr * kColTileRows, c0 = tc * kColTileCols;
     __syncthreads();     // the previous tile's LDS reads are done
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int q = t + k * kMx8Threads;
-      const int lr = q >> 5, lc = (q & 31) * 8;
-      if (c0 + lc < cols) {
-        uint32_t* d = reinterpret_cast<uint32_t*>(tile + lr * kColLdsStride + lc);
+      const int lr = q >> 3, lc = (q & 7) * 8;
+      if (r0 + lr < rows && c0 + lc < cols) {
+        uint32_t* d = tile + col_tile_word(lr) + (lc >> 1);
         d[0] = u[k].x;
         d[1] = u[k].y;
         d[2] = u[k].z;
@@ -194,24 +227,40 @@ __global__ __launch_bounds__(kMx8Threads) void k_quant_mx8_col(
     }
     __syncthreads();
     if (tile_id + gridDim.x < n_tiles) load(tile_id + gridDim.x);
-    const int64_t c = c0 + t;
-    if (c < cols) {
-      float v[kBS];
+    const int64_t row = r0 + 16 * h;          // first row of this thread's half block
+    const bool rows_in = row < rows;          // the partner lane agrees (whole blocks)
+    float v0[16], v1[16];
+    float a0 = 0.0f, a1 = 0.0f;
+    if (rows_in) {
 #pragma unroll
-      for (int k = 0; k < kBS; ++k) v[k] = bf16_to_f32(tile[k * kColLdsStride + t]);
-      float amax_b = 0.0f;
+      for (int k = 0; k < 16; ++k) {
+        const uint32_t w = tile[col_tile_word(16 * h + k) + p];
+        v0[k] = bf16_to_f32(w & 0xFFFFu);
+        v1[k] = bf16_to_f32(w >> 16);
+        a0 = fmaxf(a0, fabsf(v0[k]));
+        a1 = fmaxf(a1, fabsf(v1[k]));
+      }
+    }
+    // the block amax: this half's and the neighbour lane's (max is exact)
+    a0 = fmaxf(a0, __shfl_xor(a0, 1, 64));
+    a1 = fmaxf(a1, __shfl_xor(a1, 1, 64));
+    if (rows_in) {
+      const uint64_t j = static_cast<uint64_t>(row) / kBS;
 #pragma unroll
-      for (int k = 0; k < kBS; ++k) amax_b = fmaxf(amax_b, fabsf(v[k]));
-      float s;
-      const uint32_t sc = block_scale_mx8(amax_b, s);
-      uint32_t w[8];
-      encode_mx8<CNT>(v, s, w, cnt);
-      uint4* dst = reinterpret_cast<uint4*>(codes + c * static_cast<uint64_t>(rows) + r0);
-      dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-      dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-      const uint64_t j = static_cast<uint64_t>(tr);
-      scales[tiled ? tiled_scale_offset(static_cast<uint64_t>(c), j, kg)
-                   : static_cast<uint64_t>(c) * bpr_t + j] = static_cast<uint8_t>(sc);
+      for (int e = 0; e < 2; ++e) {
+        const int64_t c = c0 + 2 * p + e;
+        if (c < cols) {
+          float s;
+          const uint32_t sc = block_scale_mx8(e ? a1 : a0, s);
+          uint32_t w[4];
+          encode_mx8_16<CNT>(e ? v1 : v0, s, w, cnt);
+          *reinterpret_cast<uint4*>(codes + c * static_cast<uint64_t>(rows) + row) =
+              make_uint4(w[0], w[1], w[2], w[3]);
+          if ((h & 1) == 0)
+            scales[tiled ? tiled_scale_offset(static_cast<uint64_t>(c), j, kg)
+                         : static_cast<uint64_t>(c) * bpr_t + j] = static_cast<uint8_t>(sc);
+        }
+      }
     }
   }
   if constexpr (CNT) flush_counters<kMx8Threads>(cnt, counters);
@@ -269,7 +318,8 @@ namespace fp4lib {
 hipError_t launch_quant_mx8(const QuantArgs& a, bool colwise, hipStream_t s) {
   if (a.rows > 0 && a.cols > 0) {
     if (colwise) {
-      const int64_t tiles = (a.rows / kBS) * ((a.cols + kColTileCols - 1) / kColTileCols);
+      const int64_t tiles = ((a.rows + kColTileRows - 1) / kColTileRows) *
+                            ((a.cols + kColTileCols - 1) / kColTileCols);
       const int64_t cap = grid_cap(kMx8WgPerCu);
       const int grid = static_cast<int>(tiles < cap ? tiles : cap);
       if (a.counters && a.count_elems)
