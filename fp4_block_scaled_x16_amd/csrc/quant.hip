@@ -637,13 +637,18 @@ __global__ __launch_bounds__(kThreads) void k_quant_2d(
 }
 
 // ---------------------------------------------------------- dequantize --
-// One thread per block of BS codes of a [rows, cols] code matrix, kDqUnroll
-// blocks (one grid stride apart, so every wave access stays contiguous)
-// loaded before any is decoded.  sd_rows: s_dec holds one decode scale per
-// row (per-row global scale).  E2M1 codes are decoded by gfx950's packed
-// FP4 -> fp32 convert with a unit scale (exact: every E2M1 value is an fp32
-// value; the sign bit gives -0 for code 8), then v = (e * s_hat) * s_dec.
-constexpr int kDqUnroll = 4;
+// One thread per DQ_E consecutive values of a row of the [rows, cols] code
+// matrix -- exactly one 16-byte store (8 bf16 or 4 fp32) -- so a wave's
+// stores cover 1 KiB of contiguous output; kDqUnroll of them, one grid
+// stride apart, are loaded before any is decoded.  The 2 (or 4, 8) threads
+// of a block each read its scale byte.  sd_rows: s_dec holds one decode
+// scale per row (per-row global scale).  E2M1 codes are decoded by gfx950's
+// packed FP4 -> fp32 convert with a unit scale (exact: every E2M1 value is
+// an fp32 value; the sign bit gives -0 for code 8), then v = (e * s_hat) *
+// s_dec.
+constexpr int kDqUnroll = 8;
+template <bool F32>
+constexpr int kDqE = F32 ? 4 : 8;
 
 // The two E2M1 values of byte B of w, exact in fp32 (low nibble first).
 template <int B>
@@ -660,36 +665,31 @@ __global__ __launch_bounds__(kStream) void k_dequant(const uint8_t* __restrict__
                                                       int sd_rows, int64_t rows, int64_t cols,
                                                       void* __restrict__ out, int tiled) {
   constexpr int BS = FMT == kMX ? 32 : 16;
+  constexpr int E = kDqE<F32>;                 // values per thread item
   const float sd_tensor = (FMT == kMX || sd_rows) ? 1.0f : *s_dec;
+  const uint64_t ipr = static_cast<uint64_t>(cols) / E;    // items per row (cols % BS == 0)
   const uint64_t bpr = static_cast<uint64_t>(cols) / BS;
-  const uint64_t n = static_cast<uint64_t>(rows) * bpr;
+  const uint64_t n = static_cast<uint64_t>(rows) * ipr;
   const uint64_t stride = static_cast<uint64_t>(gridDim.x) * kStream;
   for (uint64_t i0 = static_cast<uint64_t>(blockIdx.x) * kStream + threadIdx.x; i0 < n;
        i0 += kDqUnroll * stride) {
-    uint32_t words[kDqUnroll][BS / 8];
+    uint32_t word[kDqUnroll];
     uint32_t sc[kDqUnroll];
     float sd[kDqUnroll];
 #pragma unroll
     for (int u = 0; u < kDqUnroll; ++u) {
       const uint64_t i = i0 + u * stride;
       if (i >= n) continue;
-      const uint64_t r = i / bpr, j = i - r * bpr;
+      const uint64_t r = i / ipr, j = (i - r * ipr) / (BS / E);
       sd[u] = (FMT != kMX && sd_rows) ? s_dec[r] : sd_tensor;
       sc[u] = B2D     ? scales[(r >> 4) * bpr + j]
               : tiled ? scales[tiled_scale_offset(r, j, (bpr + 7) >> 3)]
-                      : scales[i];
-      const uint8_t* src = codes + i * (BS / 2);
-      if constexpr (BS == 16) {
-        const uint2 q = *reinterpret_cast<const uint2*>(src);
-        words[u][0] = q.x;
-        words[u][1] = q.y;
-      } else {
-        const uint4 q = *reinterpret_cast<const uint4*>(src);
-        words[u][0] = q.x;
-        words[u][1] = q.y;
-        words[u][2] = q.z;
-        words[u][3] = q.w;
-      }
+                      : scales[r * bpr + j];
+      // item i's codes: bytes i * E / 2 ..
+      if constexpr (F32)
+        word[u] = *reinterpret_cast<const uint16_t*>(codes + i * 2);
+      else
+        word[u] = *reinterpret_cast<const uint32_t*>(codes + i * 4);
     }
 #pragma unroll
     for (int u = 0; u < kDqUnroll; ++u) {
@@ -699,32 +699,25 @@ __global__ __launch_bounds__(kStream) void k_dequant(const uint8_t* __restrict__
       if constexpr (FMT == kNV) s_hat = scale_m3_decode<7>(sc[u]);
       else if constexpr (FMT == kUE) s_hat = scale_m3_decode<15>(sc[u]);
       else s_hat = ue8m0_decode(sc[u]);
-      float v[BS];
-#pragma unroll
-      for (int w = 0; w < BS / 8; ++w) {
-        e2m1_byte_f32<0>(words[u][w], s_hat, sd[u], v + 8 * w);
-        e2m1_byte_f32<1>(words[u][w], s_hat, sd[u], v + 8 * w);
-        e2m1_byte_f32<2>(words[u][w], s_hat, sd[u], v + 8 * w);
-        e2m1_byte_f32<3>(words[u][w], s_hat, sd[u], v + 8 * w);
-      }
+      float v[E];
+      e2m1_byte_f32<0>(word[u], s_hat, sd[u], v);
+      e2m1_byte_f32<1>(word[u], s_hat, sd[u], v);
       if constexpr (F32) {
-        float4* dst = reinterpret_cast<float4*>(static_cast<float*>(out) + i * BS);
-#pragma unroll
-        for (int k = 0; k < BS / 4; ++k)
-          dst[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+        *reinterpret_cast<float4*>(static_cast<float*>(out) + i * E) =
+            make_float4(v[0], v[1], v[2], v[3]);
       } else {
-        uint32_t h[BS / 2];
+        e2m1_byte_f32<2>(word[u], s_hat, sd[u], v);
+        e2m1_byte_f32<3>(word[u], s_hat, sd[u], v);
+        uint32_t hw[4];
 #pragma unroll
-        for (int k = 0; k < BS / 2; ++k) {
+        for (int k = 0; k < 4; ++k) {
           uint32_t lo = __float_as_uint(v[2 * k]), hi = __float_as_uint(v[2 * k + 1]);
           lo = (lo + 0x7FFFu + ((lo >> 16) & 1u)) >> 16;
           hi = (hi + 0x7FFFu + ((hi >> 16) & 1u)) >> 16;
-          h[k] = (lo & 0xFFFFu) | (hi << 16);
+          hw[k] = (lo & 0xFFFFu) | (hi << 16);
         }
-        uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + i * BS);
-#pragma unroll
-        for (int k = 0; k < BS / 8; ++k)
-          dst[k] = make_uint4(h[4 * k], h[4 * k + 1], h[4 * k + 2], h[4 * k + 3]);
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + i * E) =
+            make_uint4(hw[0], hw[1], hw[2], hw[3]);
       }
     }
   }
@@ -1098,8 +1091,8 @@ template <int FMT, bool B2D>
 static void dq_launch(int tiled, const uint8_t* codes, const uint8_t* scales, const float* s_dec,
                       int sd_rows, int64_t rows, int64_t cols, void* out, int out_fp32,
                       hipStream_t s) {
-  constexpr int BS = FMT == kMX ? 32 : 16;
-  const uint64_t n = static_cast<uint64_t>(rows) * static_cast<uint64_t>(cols / BS);
+  const int E = out_fp32 ? kDqE<true> : kDqE<false>;
+  const uint64_t n = static_cast<uint64_t>(rows) * static_cast<uint64_t>(cols / E);
   const int grid = grid_for(n, 2);
   if (out_fp32)
     hipLaunchKernelGGL((k_dequant<FMT, B2D, true>), dim3(grid), dim3(kStream), 0, s, codes,
