@@ -836,19 +836,21 @@ __global__ __launch_bounds__(kThreads) void k_rht_col_tiled(const uint16_t* __re
       }
     }
     __syncthreads();
-    // two threads per tile row, 32 consecutive columns each
-    const int orow = t >> 1, ocol = (t & 1) * 32;
-    const int64_t gr = r0 + orow;
-    if (gr < rows) {
-      float* dst = y + gr * cols + c0 + ocol;
-      if (c0 + ocol + 32 <= cols && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+    // 16 threads per 64-column tile row, 4 floats each, 16 rows per pass:
+    // every store instruction writes 4 whole 256-byte row segments (the
+    // LDS reads of a pass hit 64 distinct banks: rows are 65 floats apart)
+    const int oc = 4 * (t & 15);
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
-          reinterpret_cast<float4*>(dst)[q] =
-              make_float4(out_t[orow][ocol + 4 * q], out_t[orow][ocol + 4 * q + 1],
-                          out_t[orow][ocol + 4 * q + 2], out_t[orow][ocol + 4 * q + 3]);
+    for (int pass = 0; pass < TR / 16; ++pass) {
+      const int orow = pass * 16 + (t >> 4);
+      const int64_t gr = r0 + orow;
+      if (gr >= rows) continue;
+      float* dst = y + gr * cols + c0 + oc;
+      if (c0 + oc + 4 <= cols && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+        *reinterpret_cast<float4*>(dst) = make_float4(out_t[orow][oc], out_t[orow][oc + 1],
+                                                      out_t[orow][oc + 2], out_t[orow][oc + 3]);
       } else {
-        for (int q = 0; q < 32 && c0 + ocol + q < cols; ++q) dst[q] = out_t[orow][ocol + q];
+        for (int e = 0; e < 4 && c0 + oc + e < cols; ++e) dst[e] = out_t[orow][oc + e];
       }
     }
   }
