@@ -553,6 +553,22 @@ def test_rht_alone_and_rotated_amax(n, orient):
     assert f32_bits(a.item()) == f32_bits(Q.tensor_amax(want))
 
 
+@pytest.mark.parametrize("n", [16, 64])
+def test_rht_alone_rows_ragged(n):
+    """The RHT along rows alone when the last wave of 16-element segments is
+    partial (37 x 384: 888 segments, 13.875 waves of 64): every value bit
+    for bit as the oracle's, and nothing written past the output (a guard
+    row after it stays untouched)."""
+    x = inputs.activations((37, 384), cfg_seed=64)
+    signs = inputs.rht_sign_bits(n)
+    guard = torch.full((38, 384), 7.0, dtype=torch.float32, device=DEV)
+    y = api.rht16(dev(x), signs, rht_n=n, orient="row", out=guard[:37])
+    torch.cuda.synchronize()
+    want = _rot(F.bf16_bits_to_f32(x), signs, n, "row")
+    assert np.array_equal(y.cpu().numpy().view(np.uint32), want.view(np.uint32))
+    assert torch.equal(guard[37].cpu(), torch.full((384,), 7.0))
+
+
 @pytest.mark.parametrize("n_row,n_col,rnd", [(16, 16, "rne"), (4, 64, "sr"), (16, 128, "sr")])
 def test_dual_rht_both_sides(n_row, n_col, rnd):
     """The dual quantizer with the rowwise side rotated along the rows and
