@@ -754,8 +754,9 @@ def other_kernels(fmt, host, graph_ms, flush, R=10):
     (4.5625 B; NVFP4 paper App. B.3), the RHT alone on X along tokens, 16-
     and 64-point (bf16 in, fp32 out: 6 B; §4.2), and MXFP8 quantization of
     an X-sized input rowwise and colwise (3.03125 B; 2D-block FP4 page, the
-    Q/K projections).  Two-level workloads dequantize their own format; the
-    MXFP4 workload dequantizes NVFP4 codes of X."""
+    Q/K projections) and the dequantization of its rowwise codes to bf16
+    (3.03125 B) and fp32 (5.03125 B).  Two-level workloads dequantize their
+    own format; the MXFP4 workload dequantizes NVFP4 codes of X."""
     import torch
     from fp4_block_scaled_x16_amd import api, inputs
 
@@ -764,6 +765,7 @@ def other_kernels(fmt, host, graph_ms, flush, R=10):
     n = X.numel()
     signs = inputs.rht_sign_mask()
     qx = api.quantize(X, fmt if fmt != "mxfp4" else "nvfp4")
+    qm = api.quantize(X, "mxfp8")
     out_bf = torch.empty(X.shape, dtype=torch.bfloat16, device=dev)
     out_f = torch.empty(X.shape, dtype=torch.float32, device=dev)
     work = [("dequantize X to bf16", 2.5625, lambda: api.dequantize(qx, torch.bfloat16, out=out_bf)),
@@ -771,7 +773,9 @@ def other_kernels(fmt, host, graph_ms, flush, R=10):
             ("rht X 16-point", 6.0, lambda: api.rht16(X, signs, out=out_f)),
             ("rht X 64-point", 6.0, lambda: api.rht16(X, signs, rht_n=64, out=out_f)),
             ("mxfp8 X rowwise", 3.03125, lambda: api.quantize(X, "mxfp8")),
-            ("mxfp8 X colwise", 3.03125, lambda: api.quantize(X, "mxfp8", orient="col"))]
+            ("mxfp8 X colwise", 3.03125, lambda: api.quantize(X, "mxfp8", orient="col")),
+            ("mxfp8 dequantize X to bf16", 3.03125, lambda: api.dequantize(qm, torch.bfloat16, out=out_bf)),
+            ("mxfp8 dequantize X to fp32", 5.03125, lambda: api.dequantize(qm, torch.float32, out=out_f))]
 
     def flush_only():
         for _ in range(R):

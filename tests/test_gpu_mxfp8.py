@@ -54,14 +54,21 @@ def test_mxfp8_quantize(orient, layout, R, C):
 
 
 @pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
-def test_mxfp8_dequantize(out):
-    x = qk_like((96, 256), 5)
-    q, r = check(x, "row", "tiled")
+@pytest.mark.parametrize("orient,layout,R,C", [("row", "tiled", 96, 256), ("row", "rowmajor", 96, 544),
+                                               ("col", "tiled", 320, 1032), ("col", "rowmajor", 64, 96)])
+def test_mxfp8_dequantize(out, orient, layout, R, C):
+    """Dequantized values bit for bit (fp32, and bf16 rounded once) for
+    rowwise and colwise codes in both scale layouts; the shapes leave the
+    last grid stride of 16-byte stores partial."""
+    x = qk_like((R, C), R + C + 5)
+    q, r = check(x, orient, layout)
     d = api.dequantize(q, out)
     torch.cuda.synchronize()
-    want = Q.dequantize(r["codes"], r["scales"], "mxfp8", "1d", 1.0, 96, 256,
+    Rq, Cq = (R, C) if orient == "row" else (C, R)
+    want = Q.dequantize(r["codes"], r["scales"], "mxfp8", "1d", 1.0, Rq, Cq,
                         out="f32" if out == torch.float32 else "bf16")
     got = d.cpu()
+    assert tuple(got.shape) == (Rq, Cq)
     if out == torch.float32:
         assert np.array_equal(got.numpy().view(np.uint32), want.view(np.uint32))
     else:
